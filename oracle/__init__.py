@@ -1,0 +1,122 @@
+"""fp64 CPU oracle of the Mamba-3 trapezoidal selective scan.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the smoke check and the
+bench's CPU-baseline leg, never by the library.  It shares no code with the
+HIP path.  The arithmetic lives in ``m3_oracle.c`` (plain C, double
+precision, one sequential token loop per (batch, head)); this module only
+marshals numpy arrays into it.  See the header of ``m3_oracle.c`` for what is
+computed and which passage of the pages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "m3_oracle.c")
+_LIB = os.path.join(_HERE, "_m3_oracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+        ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
+        ("bcnorm", ctypes.c_int32), ("eps", ctypes.c_double),
+        ("x", _dp), ("Bm", _dp), ("Cm", _dp), ("dt", _dp), ("lam", _dp), ("theta", _dp),
+        ("A", _dp), ("D", _dp),
+        ("b_norm_w", _dp), ("c_norm_w", _dp), ("b_bias", _dp), ("c_bias", _dp),
+        ("h0", _dp), ("pB0", _dp), ("px0", _dp), ("ang0", _dp),
+        ("y", _dp), ("h1", _dp), ("pB1", _dp), ("px1", _dp), ("ang1", _dp),
+        ("mutation", ctypes.c_int32), ("nthreads", ctypes.c_int32),
+    ]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        _lib.m3o_scan.argtypes = [ctypes.POINTER(_Args)]
+        _lib.m3o_scan.restype = ctypes.c_int
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_dp) if a is not None else None
+
+
+def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
+         b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None,
+         init=None, nthreads=None, mutation=0):
+    """Run the sequential fp64 loop.
+
+    Shapes: x [Bt,T,H,P] (or [Bt,T,H,P,R]), B/C [Bt,T,H,N] (or [...,N,R]),
+    dt/lam [Bt,T,H], theta [Bt,T,H,N/2], A/D [H]; optional gains [N] and
+    biases [H,R,N]; ``init`` a dict with any of h [Bt,H,N,P], prev_B
+    [Bt,H,N,R], prev_x [Bt,H,P,R], angle [Bt,H,N/2].
+
+    Returns (y, final) with y shaped like x (float64) and final a dict of
+    float64 arrays h, prev_B, prev_x, angle (angle is the unreduced running
+    sum).
+    """
+    x = _f64(x)
+    mimo = x.ndim == 5
+    Bsz, T, H, P = x.shape[:4]
+    R = x.shape[4] if mimo else 1
+    Bm, Cm = _f64(B), _f64(C)
+    N = Bm.shape[3]
+    keep = [x, Bm, Cm]
+    a = _Args()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.rank = Bsz, T, H, P, N, R
+    a.bcnorm, a.eps = int(bool(bcnorm)), float(eps)
+
+    def put(name, arr):
+        arr = _f64(arr)
+        keep.append(arr)
+        setattr(a, name, _ptr(arr))
+        return arr
+
+    a.x, a.Bm, a.Cm = _ptr(x), _ptr(Bm), _ptr(Cm)
+    for name, arr in (("dt", dt), ("lam", lam), ("theta", theta), ("A", A), ("D", D),
+                      ("b_norm_w", b_norm_w), ("c_norm_w", c_norm_w),
+                      ("b_bias", b_bias), ("c_bias", c_bias)):
+        put(name, arr)
+    init = init or {}
+    for name, key in (("h0", "h"), ("pB0", "prev_B"), ("px0", "prev_x"), ("ang0", "angle")):
+        put(name, init.get(key))
+    y = np.zeros(x.shape, dtype=np.float64)
+    fin = dict(h=np.zeros((Bsz, H, N, P)), prev_B=np.zeros((Bsz, H, N, R)),
+               prev_x=np.zeros((Bsz, H, P, R)), angle=np.zeros((Bsz, H, N // 2)))
+    a.y = _ptr(y)
+    a.h1, a.pB1, a.px1, a.ang1 = (_ptr(fin["h"]), _ptr(fin["prev_B"]),
+                                  _ptr(fin["prev_x"]), _ptr(fin["angle"]))
+    a.mutation = int(mutation)
+    a.nthreads = int(nthreads or os.cpu_count() or 1)
+    rc = _load().m3o_scan(ctypes.byref(a))
+    if rc != 0:
+        raise ValueError("oracle: unsupported sizes")
+    return y, fin

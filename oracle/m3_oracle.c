@@ -1,0 +1,200 @@
+/*
+ * m3_oracle.c -- plain fp64 CPU reference of the Mamba-3 trapezoidal selective
+ * scan (SISO and rank-R MIMO, complex state as data-dependent RoPE on B/C).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * bench's CPU-baseline leg may load this.  It shares no code with the HIP
+ * library and is deliberately slow: one sequential loop over tokens per
+ * (batch, head) sequence, everything in double precision.
+ *
+ * What it computes (sources, by page and section):
+ *  - Recurrence  h_t = alpha_t h_{t-1} + beta_t B_{t-1} x_{t-1}^T + gamma_t B_t x_t^T,
+ *    output y_t = C_t^T h_t (+ D x_t):  torchmamba README, "Models" table
+ *    (Mamba-3 SISO row: 3-term trapezoid) and "Math notes" (M3 SISO:
+ *    exponential-trapezoidal recurrence with data-dependent lambda).
+ *  - alpha = exp(dt*A) (exponential-Euler): torchmamba "Math notes", M1.
+ *    beta = alpha*dt*(1-lambda), gamma = lambda*dt: not printed on any page.
+ *    Reading taken: the deferred boundary term of the dotLLM streaming fix
+ *    ("Mamba-3 streaming decode" comment, PR #136) adds dt_0*(1-lambda_0)*
+ *    k_state*v_state to the state *before* the scan decays it, and the
+ *    scan's per-token scale is gamma + dt_{t+1}(1-lambda_{t+1}); both hold
+ *    only if beta carries the factor alpha.  lambda = 1 then gives the
+ *    Mamba-2 update h = alpha h + dt B x^T (torchmamba "Models",
+ *    reductions paragraph).
+ *  - lambda per token and head; theta per token, head and rotation pair:
+ *    dotLLM PR #136, "Key findings / design decisions".
+ *  - BC norm (RMSNorm over N), then the per-head bias, then the rotation:
+ *    dotLLM PR #136, "Summary" (Mamba3QkNorm, Mamba3DataRoPE) and "Key
+ *    findings" (bias after the norm, before RoPE).
+ *  - Complex state as accumulated data-dependent pairwise rotations of B
+ *    and C: torchmamba "Math notes" (M3 SISO, RoPE trick).  The angle is the
+ *    inclusive running sum of theta (the cumulative angle carried in the
+ *    decode state, dotLLM "Mamba3State persistent state buffers").  Pair i
+ *    is the components (2i, 2i+1); the rotation is the standard
+ *    (u, v) -> (u cos a - v sin a, u sin a + v cos a).
+ *  - MIMO: rank-R update on a shared (N, P) state; B, C, x carry the rank
+ *    axis, theta/dt/lambda/A/D do not (torchmamba "Models" MIMO row,
+ *    "API reference" cache note: the state has no R axis).
+ *  - Carried state (h, previous rotated B, previous x, cumulative angle):
+ *    torchmamba "API reference" (Mamba3SisoCache(angle, ssm, x_prev,
+ *    b_prev)); dotLLM "Mamba3State" / k_state, v_state.
+ *
+ * Layouts (row-major, last index fastest):
+ *   x, y  [B, T, H, P, R]     B, C [B, T, H, N, R]     dt, lam [B, T, H]
+ *   theta [B, T, H, N/2]      A, D [H]                 norm gains [N]
+ *   biases [H, R, N]          h [B, H, N, P]           prev_B [B, H, N, R]
+ *   prev_x [B, H, P, R]       angle [B, H, N/2]
+ * SISO is R = 1 (the trailing unit axis is simply absent in memory).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    int64_t batch, seqlen;
+    int32_t nheads, headdim, dstate, rank;
+    int32_t bcnorm;       /* 1: RMSNorm over N on B and C before the bias */
+    double eps;           /* RMSNorm epsilon */
+    /* inputs (NULL where optional) */
+    const double *x, *Bm, *Cm, *dt, *lam, *theta, *A, *D;
+    const double *b_norm_w, *c_norm_w;   /* [N] or NULL (= 1) */
+    const double *b_bias, *c_bias;       /* [H, R, N] or NULL (= 0) */
+    const double *h0, *pB0, *px0, *ang0; /* initial state or NULL (= 0) */
+    /* outputs */
+    double *y;                            /* [B, T, H, P, R] */
+    double *h1, *pB1, *px1, *ang1;        /* final state or NULL */
+    /* Test hook: a nonzero value plants one deliberate mistake so that the
+     * pin tests can show they catch it.  0 in every real use. */
+    int32_t mutation;
+    int32_t nthreads;
+} m3o_args;
+
+/* normalise + bias + rotate one raw vector v[N] (stride `stride`) */
+static void prep_vec(const m3o_args *a, const double *v, int64_t stride, const double *gain,
+                     const double *bias, const double *ang, double *out) {
+    const int N = a->dstate;
+    double s = 1.0;
+    if (a->bcnorm) {
+        double ms = 0.0;
+        for (int n = 0; n < N; ++n) ms += v[n * stride] * v[n * stride];
+        ms /= (double)N;
+        s = 1.0 / sqrt(ms + a->eps);
+    }
+    double hat[256];
+    for (int n = 0; n < N; ++n) {
+        double g = (a->bcnorm && gain) ? gain[n] : 1.0;
+        hat[n] = (a->bcnorm ? g * v[n * stride] * s : v[n * stride]) + (bias ? bias[n] : 0.0);
+    }
+    for (int i = 0; i < N / 2; ++i) {
+        double c = cos(ang[i]), sn = sin(ang[i]);
+        if (a->mutation == 3) sn = -sn; /* planted: rotation in the other direction for B and C */
+        double u = hat[2 * i], w = hat[2 * i + 1];
+        out[2 * i] = u * c - w * sn;
+        out[2 * i + 1] = u * sn + w * c;
+    }
+}
+
+static void run_sequence(const m3o_args *a, int64_t b, int h) {
+    const int64_t T = a->seqlen;
+    const int H = a->nheads, P = a->headdim, N = a->dstate, R = a->rank, N2 = N / 2;
+    double *st = calloc((size_t)N * P, sizeof(double));       /* h          [N][P] */
+    double *pB = calloc((size_t)N * R, sizeof(double));       /* prev B~    [N][R] */
+    double *px = calloc((size_t)P * R, sizeof(double));       /* prev x     [P][R] */
+    double *Bt = calloc((size_t)N * R, sizeof(double));       /* B~_t       [N][R] */
+    double *Ct = calloc((size_t)N * R, sizeof(double));       /* C~_t       [N][R] */
+    double *ang = calloc((size_t)(N2 > 0 ? N2 : 1), sizeof(double));
+    double *col = calloc((size_t)N, sizeof(double));
+    const int64_t bh = b * H + h;
+    if (a->h0) memcpy(st, a->h0 + bh * N * P, sizeof(double) * N * P);
+    if (a->pB0) memcpy(pB, a->pB0 + bh * N * R, sizeof(double) * N * R);
+    if (a->px0) memcpy(px, a->px0 + bh * P * R, sizeof(double) * P * R);
+    if (a->ang0) memcpy(ang, a->ang0 + bh * N2, sizeof(double) * N2);
+
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t bth = (b * T + t) * H + h; /* index of (b, t, h) */
+        /* cumulative angle, inclusive of this token */
+        double ang_used[128];
+        for (int i = 0; i < N2; ++i) {
+            ang[i] += a->theta[bth * N2 + i];
+            ang_used[i] = ang[i];
+            if (a->mutation == 2) ang_used[i] -= a->theta[bth * N2 + i]; /* planted: exclusive sum */
+        }
+        for (int r = 0; r < R; ++r) {
+            const double *bb = a->b_bias ? a->b_bias + ((int64_t)h * R + r) * N : NULL;
+            const double *cb = a->c_bias ? a->c_bias + ((int64_t)h * R + r) * N : NULL;
+            prep_vec(a, a->Bm + bth * N * R + r, R, a->b_norm_w, bb, ang_used, col);
+            for (int n = 0; n < N; ++n) Bt[n * R + r] = col[n];
+            prep_vec(a, a->Cm + bth * N * R + r, R, a->c_norm_w, cb, ang_used, col);
+            for (int n = 0; n < N; ++n) Ct[n * R + r] = col[n];
+        }
+        const double dt = a->dt[bth], lam = a->lam[bth];
+        const double alpha = exp(dt * a->A[h]);
+        double beta = alpha * dt * (1.0 - lam);
+        double gamma = lam * dt;
+        if (a->mutation == 1) beta = dt * (1.0 - lam); /* planted: beta without alpha */
+        if (a->mutation == 5) { double tmp = beta; beta = gamma; gamma = tmp; } /* planted: swapped */
+        const double *xt = a->x + bth * P * R;
+        /* state update */
+        for (int n = 0; n < N; ++n) {
+            for (int p = 0; p < P; ++p) {
+                double prev_term = 0.0, cur_term = 0.0;
+                for (int r = 0; r < R; ++r) {
+                    /* planted (mutation 4): pair the previous x with the current B~ */
+                    const double *pb = (a->mutation == 4) ? Bt : pB;
+                    prev_term += pb[n * R + r] * px[p * R + r];
+                    cur_term += Bt[n * R + r] * xt[p * R + r];
+                }
+                st[n * P + p] = alpha * st[n * P + p] + beta * prev_term + gamma * cur_term;
+            }
+        }
+        /* output: y_t[:, r] = h^T C~_t[:, r] + D x_t[:, r] */
+        double *yt = a->y + bth * P * R;
+        for (int p = 0; p < P; ++p) {
+            for (int r = 0; r < R; ++r) {
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n) acc += st[n * P + p] * Ct[n * R + r];
+                yt[p * R + r] = acc + a->D[h] * xt[p * R + r];
+            }
+        }
+        memcpy(pB, Bt, sizeof(double) * N * R);
+        for (int i = 0; i < P * R; ++i) px[i] = xt[i];
+    }
+    if (a->h1) memcpy(a->h1 + bh * N * P, st, sizeof(double) * N * P);
+    if (a->pB1) memcpy(a->pB1 + bh * N * R, pB, sizeof(double) * N * R);
+    if (a->px1) memcpy(a->px1 + bh * P * R, px, sizeof(double) * P * R);
+    if (a->ang1) memcpy(a->ang1 + bh * N2, ang, sizeof(double) * N2);
+    free(st); free(pB); free(px); free(Bt); free(Ct); free(ang); free(col);
+}
+
+typedef struct { const m3o_args *a; int64_t begin, end; } work_t;
+
+static void *worker(void *p) {
+    work_t *w = (work_t *)p;
+    for (int64_t s = w->begin; s < w->end; ++s)
+        run_sequence(w->a, s / w->a->nheads, (int)(s % w->a->nheads));
+    return NULL;
+}
+
+/* Returns 0 on success, -1 on unsupported sizes. */
+int m3o_scan(const m3o_args *a) {
+    if (a->dstate <= 0 || (a->dstate & 1) || a->dstate > 256 || a->rank < 1 || a->headdim <= 0 ||
+        a->nheads <= 0 || a->batch < 0 || a->seqlen < 0)
+        return -1;
+    const int64_t nseq = a->batch * a->nheads;
+    int nt = a->nthreads > 0 ? a->nthreads : 1;
+    if (nt > nseq) nt = (int)(nseq > 0 ? nseq : 1);
+    pthread_t th[256];
+    work_t w[256];
+    if (nt > 256) nt = 256;
+    for (int i = 0; i < nt; ++i) {
+        w[i].a = a;
+        w[i].begin = nseq * i / nt;
+        w[i].end = nseq * (i + 1) / nt;
+    }
+    for (int i = 1; i < nt; ++i) pthread_create(&th[i], NULL, worker, &w[i]);
+    worker(&w[0]);
+    for (int i = 1; i < nt; ++i) pthread_join(th[i], NULL);
+    return 0;
+}
