@@ -1,0 +1,157 @@
+/*
+ * libmamba3 -- the Mamba-3 sequence-mixer scan on AMD MI355X (gfx950).
+ *
+ * The operation (sources are the pages' titles and sections):
+ *
+ *   Per batch b and head h, over tokens t = 0 .. T-1:
+ *     Theta_t = Theta_{t-1} + theta_t                    cumulative data-dependent angle, per pair
+ *     B^_t    = g_B * B_t / sqrt(mean_n B_t^2 + eps) + bias_B      (C^_t likewise)
+ *     B~_t    = Rot(Theta_t) B^_t,  C~_t = Rot(Theta_t) C^_t          pair i = components (2i, 2i+1)
+ *     alpha_t = exp(dt_t A),  beta_t = alpha_t dt_t (1 - lambda_t),  gamma_t = lambda_t dt_t
+ *     h_t     = alpha_t h_{t-1} + beta_t B~_{t-1} x_{t-1}^T + gamma_t B~_t x_t^T
+ *     y_t     = C~_t^T h_t + D x_t
+ *
+ *   - The three-term exponential-trapezoidal recurrence: torchmamba README,
+ *     "Models" table (Mamba-3 SISO row) and "Math notes" (M3 SISO).
+ *   - alpha from exponential-Euler: same page, "Math notes" (M1).  beta and
+ *     gamma are not printed on the pages; the form above is the one under
+ *     which the dotLLM streaming fix (PR #136, comment "Mamba-3 streaming
+ *     decode") folds the trapezoid into one scan with per-token scale
+ *     gamma_t + dt_{t+1}(1 - lambda_{t+1}).
+ *   - BC norm, then bias, then rotation; lambda per (token, head); theta per
+ *     (token, head, pair): dotLLM PR #136, "Summary" and "Key findings /
+ *     design decisions".
+ *   - Complex state as accumulated data-dependent rotations of B and C:
+ *     torchmamba "Math notes" (M3 SISO, RoPE trick).
+ *   - MIMO: B, C and x carry a rank axis R; the (N, P) state is shared and
+ *     has no rank axis; every output rank r reads C~_t[:, r]:  torchmamba
+ *     "Models" (MIMO row) and "API reference" (cache note).
+ *   - The carried decode state (h, previous rotated B, previous x, angle):
+ *     torchmamba "API reference" (Mamba3SisoCache(angle, ssm, x_prev,
+ *     b_prev)); dotLLM PR #136 "Mamba3State" and k_state / v_state.
+ *
+ * Layouts: row-major, contiguous, last index fastest.
+ *   x, y    [B, T, H, P]        MIMO: [B, T, H, P, R]       io dtype
+ *   Bm, Cm  [B, T, H, N]        MIMO: [B, T, H, N, R]       io dtype, raw (before the norm)
+ *   dt, lam [B, T, H]           float32 (dt > 0 already activated, lam in [0, 1])
+ *   theta   [B, T, H, N/2]      float32 per-step angle of pair i
+ *   A, D    [H]                 float32 (A < 0)
+ *   b_norm_w, c_norm_w [N]      float32 or NULL (gain 1)
+ *   b_bias, c_bias     [H, R, N] float32 or NULL (bias 0)
+ *   state: h [B, H, N, P], prev_B [B, H, N, R], prev_x [B, H, P, R], angle [B, H, N/2], float32
+ *
+ * Memory: every pointer is a DEVICE pointer owned by the caller.  The
+ * library allocates nothing; the scans take a caller-provided workspace of
+ * m3_scan_workspace_bytes() bytes.  All calls are asynchronous on the given
+ * HIP stream (a hipStream_t passed as void*; NULL = the null stream) and do
+ * not synchronise.  The library keeps no global mutable state, so calls on
+ * different streams with different workspaces may run concurrently.
+ *
+ * Errors: arguments are checked on the host before any launch.  NULL
+ * required pointers, bad sizes, odd N, R < 1 or pointers that are not 16-byte
+ * aligned give M3_EINVAL; sizes outside the supported range give
+ * M3_EUNSUPPORTED; a short workspace gives M3_EWORKSPACE; a failed launch
+ * gives M3_EHIP.  Values are not checked on the device (NaN propagates).
+ */
+#ifndef LIBMAMBA3_H
+#define LIBMAMBA3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    M3_OK = 0,
+    M3_EINVAL = 1,
+    M3_EUNSUPPORTED = 2,
+    M3_EWORKSPACE = 3,
+    M3_EHIP = 4
+} m3_status;
+
+typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype; /* dtype of x, B, C and y */
+
+enum { M3_FLAG_BCNORM = 1u << 0 }; /* apply the RMSNorm over N to B and C */
+
+typedef struct {
+    int64_t batch;   /* B >= 0 */
+    int64_t seqlen;  /* T >= 0 (m3_step: must be 1) */
+    int32_t nheads;  /* H >= 1 */
+    int32_t headdim; /* P, 1 .. 128 */
+    int32_t dstate;  /* N, even, 2 .. 128 */
+    int32_t rank;    /* R, 1 .. 8 (1 for m3_scan_siso) */
+    int32_t chunk;   /* tokens per chunk, one of 16, 32, 64, 128 (the result does not depend on it);
+                        for rank R the chunk holds chunk*R (token, rank) rows, at most 128 */
+    int32_t io;      /* m3_dtype */
+    uint32_t flags;  /* M3_FLAG_* */
+    float norm_eps;  /* RMSNorm epsilon (1e-5 is the usual value) */
+} m3_shape;
+
+typedef struct {
+    const void *x;                    /* [B, T, H, P(, R)]  io dtype */
+    const void *Bm, *Cm;              /* [B, T, H, N(, R)]  io dtype */
+    const float *dt, *lam;            /* [B, T, H] */
+    const float *theta;               /* [B, T, H, N/2] */
+    const float *A, *D;               /* [H] */
+    const float *b_norm_w, *c_norm_w; /* [N] or NULL */
+    const float *b_bias, *c_bias;     /* [H, R, N] or NULL */
+} m3_inputs;
+
+typedef struct {
+    float *h;      /* [B, H, N, P] state after the last token, in the rotated frame of Theta */
+    float *prev_B; /* [B, H, N, R] B~ of the last token (normalised, biased, rotated; not scaled) */
+    float *prev_x; /* [B, H, P, R] x of the last token */
+    float *angle;  /* [B, H, N/2] cumulative angle Theta of the last token, kept in [0, 2 pi) */
+} m3_state;
+
+/* Bytes of workspace m3_scan_siso / m3_scan_mimo need for this shape (0 when T == 0). */
+size_t m3_scan_workspace_bytes(const m3_shape *shape);
+
+/*
+ * Chunked scan over T tokens (SISO: rank must be 1).
+ *   y:     [B, T, H, P] output, io dtype (bf16 rounded to nearest even).
+ *   init:  carried state to start from, or NULL for zeros (all four arrays must be set).
+ *   final: where to write the state after the last token, or NULL.  May be the
+ *          same arrays as init (in-place streaming).  With T == 0, final = init.
+ *   ws:    device workspace of at least m3_scan_workspace_bytes(shape) bytes,
+ *          owned by the caller; its contents on entry do not matter.  Calls that
+ *          share a workspace must be ordered on one stream.
+ * Chunk-parallel SSD form: an intra-chunk quadratic part on the matrix
+ * cores and a sequential pass over chunk states (torchmamba "Math notes", M2:
+ * chunkwise SSD with a factored inter-chunk carry).
+ */
+m3_status m3_scan_siso(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,
+                       m3_state *final, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Rank-R MIMO scan: same contract as m3_scan_siso with rank R >= 1 and the
+ * rank-axis layouts; x, y [B, T, H, P, R], Bm, Cm [B, T, H, N, R].  Every
+ * (token, rank) pair is a row of the chunk (chunk * R rows, at most 128).
+ * torchmamba "Models" (MIMO row) and "Math notes" (MIMO: rank-R update on a
+ * shared state; a chunk of C_SISO / R tokens).
+ */
+m3_status m3_scan_mimo(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,
+                       m3_state *final, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One decode step (seqlen must be 1) for any rank R: reads and updates
+ * `state` in place (all four arrays required) and writes y [B, 1, H, P(, R)].
+ * torchmamba "Quickstart"/"API reference" (step(u_t, cache)); dotLLM PR #136
+ * "Mamba-3 streaming decode" (the carried previous B~ and x).
+ */
+m3_status m3_step(const m3_shape *shape, const m3_inputs *in, void *y, m3_state *state,
+                  void *stream);
+
+/* Static description of a status code. */
+const char *m3_status_str(m3_status status);
+
+/* Library version, e.g. "0.1.0". */
+const char *m3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMAMBA3_H */

@@ -1,0 +1,227 @@
+"""Python binding of libmamba3 (Mamba-3 trapezoidal selective scan on MI355X).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``libmamba3.so``; this module checks tensor dtypes/devices/contiguity, builds
+the C structs, allocates outputs and workspace with torch, and passes raw
+device pointers and the current HIP stream to the C ABI
+(``include/libmamba3.h``).  The functions carry the C names:
+
+    m3_scan_siso, m3_scan_mimo, m3_step, m3_scan_workspace_bytes, m3_status_str
+
+There is no fallback: if the library is missing or a call fails, a
+RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["m3_scan_siso", "m3_scan_mimo", "m3_step", "m3_scan_workspace_bytes",
+           "m3_status_str", "Shape", "M3_F32", "M3_BF16", "M3_FLAG_BCNORM", "lib_path", "load"]
+
+M3_F32, M3_BF16 = 0, 1
+M3_FLAG_BCNORM = 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libmamba3.so")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("io", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float)]
+
+
+class _Inputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("x", "Bm", "Cm", "dt", "lam", "theta", "A", "D",
+                 "b_norm_w", "c_norm_w", "b_bias", "c_bias")]
+
+
+class _State(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("h", "prev_B", "prev_x", "angle")]
+
+
+_lib = None
+
+
+def load():
+    """Load libmamba3.so (built in-tree by ``mamba_selective_scan_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"libmamba3.so not built ({lib_path}); run "
+                               "`python -m mamba_selective_scan_amd.build`")
+        lib = ctypes.CDLL(lib_path)
+        P = ctypes.POINTER
+        lib.m3_scan_workspace_bytes.argtypes = [P(Shape)]
+        lib.m3_scan_workspace_bytes.restype = ctypes.c_size_t
+        for name in ("m3_scan_siso", "m3_scan_mimo"):
+            f = getattr(lib, name)
+            f.argtypes = [P(Shape), P(_Inputs), ctypes.c_void_p, P(_State), P(_State),
+                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+            f.restype = ctypes.c_int
+        lib.m3_step.argtypes = [P(Shape), P(_Inputs), ctypes.c_void_p, P(_State), ctypes.c_void_p]
+        lib.m3_step.restype = ctypes.c_int
+        lib.m3_status_str.argtypes = [ctypes.c_int]
+        lib.m3_status_str.restype = ctypes.c_char_p
+        lib.m3_version.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def m3_status_str(code: int) -> str:
+    return load().m3_status_str(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise RuntimeError(f"{what}: {m3_status_str(code)}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, device, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape_of(x, B, chunk, bcnorm, eps, mimo):
+    io = {torch.float32: M3_F32, torch.bfloat16: M3_BF16}.get(x.dtype)
+    if io is None:
+        raise TypeError("x must be float32 or bfloat16")
+    if mimo:
+        if x.dim() != 5:
+            raise ValueError("MIMO x must be [B, T, H, P, R]")
+        Bsz, T, H, P, R = x.shape
+        N = B.shape[3]
+    else:
+        if x.dim() != 4:
+            raise ValueError("SISO x must be [B, T, H, P]")
+        Bsz, T, H, P = x.shape
+        R = 1
+        N = B.shape[3]
+    return Shape(Bsz, T, H, P, N, R, int(chunk), io, M3_FLAG_BCNORM if bcnorm else 0, float(eps))
+
+
+def _inputs(s: Shape, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo):
+    dev, io_t = x.device, x.dtype
+    f32 = torch.float32
+    bs = (s.batch, s.seqlen, s.nheads, s.dstate) + ((s.rank,) if mimo else ())
+    _need(B, "B", io_t, dev, bs)
+    _need(C, "C", io_t, dev, bs)
+    _need(dt, "dt", f32, dev, (s.batch, s.seqlen, s.nheads))
+    _need(lam, "lam", f32, dev, (s.batch, s.seqlen, s.nheads))
+    _need(theta, "theta", f32, dev, (s.batch, s.seqlen, s.nheads, s.dstate // 2))
+    _need(A, "A", f32, dev, (s.nheads,))
+    _need(D, "D", f32, dev, (s.nheads,))
+    _need(b_norm_w, "b_norm_w", f32, dev, (s.dstate,))
+    _need(c_norm_w, "c_norm_w", f32, dev, (s.dstate,))
+    _need(b_bias, "b_bias", f32, dev, (s.nheads, s.rank, s.dstate))
+    _need(c_bias, "c_bias", f32, dev, (s.nheads, s.rank, s.dstate))
+    return _Inputs(*(_ptr(t) for t in (x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w,
+                                        b_bias, c_bias)))
+
+
+def new_state(batch, nheads, headdim, dstate, rank=1, device="cuda"):
+    """Zero carried state (h, prev_B, prev_x, angle) as float32 device tensors."""
+    z = lambda *sh: torch.zeros(sh, dtype=torch.float32, device=device)
+    return dict(h=z(batch, nheads, dstate, headdim), prev_B=z(batch, nheads, dstate, rank),
+                prev_x=z(batch, nheads, headdim, rank), angle=z(batch, nheads, dstate // 2))
+
+
+def _state(s: Shape, st, dev, name):
+    if st is None:
+        return None
+    _need(st["h"], f"{name}.h", torch.float32, dev, (s.batch, s.nheads, s.dstate, s.headdim))
+    _need(st["prev_B"], f"{name}.prev_B", torch.float32, dev, (s.batch, s.nheads, s.dstate, s.rank))
+    _need(st["prev_x"], f"{name}.prev_x", torch.float32, dev, (s.batch, s.nheads, s.headdim, s.rank))
+    _need(st["angle"], f"{name}.angle", torch.float32, dev, (s.batch, s.nheads, s.dstate // 2))
+    return _State(*(_ptr(st[k]) for k in ("h", "prev_B", "prev_x", "angle")))
+
+
+def m3_scan_workspace_bytes(shape: Shape) -> int:
+    return int(load().m3_scan_workspace_bytes(ctypes.byref(shape)))
+
+
+def _scan(mimo, x, B, C, dt, lam, theta, A, D, *, chunk=64, bcnorm=True, eps=1e-5,
+          b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, init=None, final=None,
+          y=None, workspace=None, stream=None):
+    lib = load()
+    s = _shape_of(x, B, chunk, bcnorm, eps, mimo)
+    _need(x, "x", x.dtype, x.device)
+    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, x.device, tuple(x.shape))
+    if final is True:
+        final = new_state(s.batch, s.nheads, s.headdim, s.dstate, s.rank, x.device)
+    st_in = _state(s, init, x.device, "init")
+    st_out = _state(s, final, x.device, "final")
+    need = int(lib.m3_scan_workspace_bytes(ctypes.byref(s)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, x.device)
+    f = lib.m3_scan_mimo if mimo else lib.m3_scan_siso
+    rc = f(ctypes.byref(s), ctypes.byref(inp), _ptr(y),
+           ctypes.byref(st_in) if st_in is not None else None,
+           ctypes.byref(st_out) if st_out is not None else None,
+           _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+    _check(rc, "m3_scan_mimo" if mimo else "m3_scan_siso")
+    return (y, final) if final is not None else y
+
+
+def m3_scan_siso(x, B, C, dt, lam, theta, A, D, **kw):
+    """SISO chunked scan.  x [B,T,H,P], B/C [B,T,H,N] (float32 or bfloat16); dt/lam [B,T,H],
+    theta [B,T,H,N/2], A/D [H] float32.  ``final=True`` returns (y, final_state)."""
+    return _scan(False, x, B, C, dt, lam, theta, A, D, **kw)
+
+
+def m3_scan_mimo(x, B, C, dt, lam, theta, A, D, **kw):
+    """Rank-R MIMO chunked scan.  x [B,T,H,P,R], B/C [B,T,H,N,R]; ``chunk`` counts tokens."""
+    return _scan(True, x, B, C, dt, lam, theta, A, D, **kw)
+
+
+def m3_step(x, B, C, dt, lam, theta, A, D, state, *, bcnorm=True, eps=1e-5, b_norm_w=None,
+            c_norm_w=None, b_bias=None, c_bias=None, y=None, stream=None):
+    """One decode step (T == 1) that updates ``state`` in place; returns y.
+
+    x [B,1,H,P] (or [B,1,H,P,R]), B/C [B,1,H,N(,R)], dt/lam [B,1,H], theta [B,1,H,N/2]."""
+    lib = load()
+    mimo = x.dim() == 5
+    s = _shape_of(x, B, 16, bcnorm, eps, mimo)
+    if s.seqlen != 1:
+        raise ValueError("m3_step takes exactly one token (T == 1)")
+    _need(x, "x", x.dtype, x.device)
+    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, x.device, tuple(x.shape))
+    st = _state(s, state, x.device, "state")
+    rc = lib.m3_step(ctypes.byref(s), ctypes.byref(inp), _ptr(y), ctypes.byref(st), _stream(stream))
+    _check(rc, "m3_step")
+    return y

@@ -1,0 +1,251 @@
+// m3_api.cpp -- the C ABI of libmamba3: argument checks, workspace layout and
+// kernel dispatch.  Every check happens on the host before the first launch;
+// nothing here allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/libmamba3.h"
+#include "m3_internal.hpp"
+
+namespace {
+
+using m3::ScanParams;
+using m3::StepParams;
+using m3::TileShape;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int pow2_at_least(int v, int lo) {
+    int r = lo;
+    while (r < v) r <<= 1;
+    return r;
+}
+
+// Shape checks common to the scans and the step.  Returns M3_OK or an error.
+m3_status check_shape(const m3_shape *s, bool step) {
+    if (!s) return M3_EINVAL;
+    if (s->batch < 0 || s->seqlen < 0 || s->nheads < 1 || s->headdim < 1 || s->dstate < 2 ||
+        (s->dstate & 1) || s->rank < 1)
+        return M3_EINVAL;
+    if (s->io != M3_F32 && s->io != M3_BF16) return M3_EINVAL;
+    if ((s->flags & ~(uint32_t)M3_FLAG_BCNORM) != 0) return M3_EINVAL;
+    if ((s->flags & M3_FLAG_BCNORM) && !(s->norm_eps >= 0.f)) return M3_EINVAL;
+    if (step && s->seqlen != 1) return M3_EINVAL;
+    if (s->dstate > 128 || s->headdim > 128 || s->rank > 8) return M3_EUNSUPPORTED;
+    if (s->nheads > 65535 || s->batch > 65535) return M3_EUNSUPPORTED;
+    if (!step) {
+        if (s->chunk != 16 && s->chunk != 32 && s->chunk != 64 && s->chunk != 128) return M3_EUNSUPPORTED;
+        if ((int64_t)s->chunk * s->rank > 128) return M3_EUNSUPPORTED;
+    }
+    return M3_OK;
+}
+
+m3_status check_inputs(const m3_inputs *in, bool need_data) {
+    if (!in) return M3_EINVAL;
+    if (need_data) {
+        if (!in->x || !in->Bm || !in->Cm || !in->dt || !in->lam || !in->theta || !in->A || !in->D)
+            return M3_EINVAL;
+    } else if (!in->A || !in->D) {
+        return M3_EINVAL;
+    }
+    const void *ptrs[] = {in->x, in->Bm, in->Cm, in->dt, in->lam, in->theta, in->A, in->D,
+                          in->b_norm_w, in->c_norm_w, in->b_bias, in->c_bias};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return M3_EINVAL;
+    return M3_OK;
+}
+
+m3_status check_state(const m3_state *st, bool required) {
+    if (!st) return required ? M3_EINVAL : M3_OK;
+    if (!st->h || !st->prev_B || !st->prev_x || !st->angle) return M3_EINVAL;
+    if (!aligned16(st->h) || !aligned16(st->prev_B) || !aligned16(st->prev_x) || !aligned16(st->angle))
+        return M3_EINVAL;
+    return M3_OK;
+}
+
+struct WsLayout {
+    size_t S, decay, phi, cphi, sphi, thfin, total;
+};
+
+WsLayout ws_layout(const m3_shape *s) {
+    WsLayout w{};
+    const int64_t T = s->seqlen;
+    const int64_t C = T > 0 ? (T + s->chunk - 1) / s->chunk : 0;
+    const int64_t BH = s->batch * (int64_t)s->nheads;
+    const int64_t N2 = s->dstate / 2;
+    size_t off = 0;
+    w.S = off;     off = align_up(off + sizeof(float) * (size_t)(BH * C * s->headdim * s->dstate));
+    w.decay = off; off = align_up(off + sizeof(float) * (size_t)(BH * C));
+    w.phi = off;   off = align_up(off + sizeof(float) * (size_t)(BH * C * N2));
+    w.cphi = off;  off = align_up(off + sizeof(float) * (size_t)(BH * C * N2));
+    w.sphi = off;  off = align_up(off + sizeof(float) * (size_t)(BH * C * N2));
+    w.thfin = off; off = align_up(off + sizeof(float) * (size_t)(BH * N2));
+    w.total = (C == 0 || BH == 0) ? 0 : off;
+    return w;
+}
+
+TileShape tile_of(const m3_shape *s) {
+    TileShape ts;
+    ts.rows = pow2_at_least(s->chunk * s->rank, 32);
+    ts.np = pow2_at_least(s->dstate, 32);
+    ts.pp = pow2_at_least(s->headdim, 32);
+    return ts;
+}
+
+m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_state *init,
+                    m3_state *fin, void *ws, size_t ws_bytes, void *stream, bool mimo) {
+    m3_status rc = check_shape(s, false);
+    if (rc != M3_OK) return rc;
+    if (!mimo && s->rank != 1) return M3_EINVAL;
+    rc = check_inputs(in, s->seqlen > 0 && s->batch > 0);
+    if (rc != M3_OK) return rc;
+    if ((rc = check_state(init, false)) != M3_OK) return rc;
+    if ((rc = check_state(fin, false)) != M3_OK) return rc;
+    if (s->seqlen > 0 && s->batch > 0 && !y) return M3_EINVAL;
+    if (!aligned16(y)) return M3_EINVAL;
+    const TileShape ts = tile_of(s);
+    const bool bf = s->io == M3_BF16;
+    if (m3::chunk_kernel_lds_bytes(m3::MODE_OUTPUT, bf, ts) > 160 * 1024 ||
+        m3::chunk_kernel_lds_bytes(m3::MODE_STATE, bf, ts) > 160 * 1024)
+        return M3_EUNSUPPORTED;
+    const WsLayout wl = ws_layout(s);
+    if (wl.total > 0 && (!ws || ws_bytes < wl.total)) return M3_EWORKSPACE;
+    if (!aligned16(ws)) return M3_EINVAL;
+
+    ScanParams p;
+    std::memset(&p, 0, sizeof p);
+    p.B = s->batch;
+    p.T = s->seqlen;
+    p.H = s->nheads;
+    p.P = s->headdim;
+    p.N = s->dstate;
+    p.R = s->rank;
+    p.Q = s->chunk;
+    p.nchunks = (int)(s->seqlen > 0 ? (s->seqlen + s->chunk - 1) / s->chunk : 0);
+    p.flags = s->flags;
+    p.eps = s->norm_eps;
+    p.x = in->x;
+    p.Bm = in->Bm;
+    p.Cm = in->Cm;
+    p.dt = in->dt;
+    p.lam = in->lam;
+    p.theta = in->theta;
+    p.A = in->A;
+    p.D = in->D;
+    p.bnw = in->b_norm_w;
+    p.cnw = in->c_norm_w;
+    p.bbias = in->b_bias;
+    p.cbias = in->c_bias;
+    p.y = y;
+    if (init) {
+        p.h0 = init->h;
+        p.pB0 = init->prev_B;
+        p.px0 = init->prev_x;
+        p.ang0 = init->angle;
+    }
+    if (fin) {
+        p.h1 = fin->h;
+        p.pB1 = fin->prev_B;
+        p.px1 = fin->prev_x;
+        p.ang1 = fin->angle;
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (p.B == 0) return M3_OK;
+    if (p.T == 0) {
+        if (!fin) return M3_OK;
+        return m3::launch_fill_state(p, st) == hipSuccess ? M3_OK : M3_EHIP;
+    }
+    if (p.nchunks > 65535) return M3_EUNSUPPORTED;
+    char *base = static_cast<char *>(ws);
+    p.S = reinterpret_cast<float *>(base + wl.S);
+    p.decay = reinterpret_cast<float *>(base + wl.decay);
+    p.phi = reinterpret_cast<float *>(base + wl.phi);
+    p.cphi = reinterpret_cast<float *>(base + wl.cphi);
+    p.sphi = reinterpret_cast<float *>(base + wl.sphi);
+    p.thfin = reinterpret_cast<float *>(base + wl.thfin);
+
+    if (m3::launch_chunk_kernel(m3::MODE_STATE, bf, ts, p, st) != hipSuccess) return M3_EHIP;
+    if (m3::launch_state_pass(p, st) != hipSuccess) return M3_EHIP;
+    if (m3::launch_chunk_kernel(m3::MODE_OUTPUT, bf, ts, p, st) != hipSuccess) return M3_EHIP;
+    return M3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t m3_scan_workspace_bytes(const m3_shape *shape) {
+    if (!shape || shape->chunk < 1 || shape->seqlen < 0 || shape->batch < 0 || shape->nheads < 1 ||
+        shape->headdim < 1 || shape->dstate < 2)
+        return 0;
+    return ws_layout(shape).total;
+}
+
+m3_status m3_scan_siso(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,
+                       m3_state *final, void *ws, size_t ws_bytes, void *stream) {
+    return scan_impl(shape, in, y, init, final, ws, ws_bytes, stream, false);
+}
+
+m3_status m3_scan_mimo(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,
+                       m3_state *final, void *ws, size_t ws_bytes, void *stream) {
+    return scan_impl(shape, in, y, init, final, ws, ws_bytes, stream, true);
+}
+
+m3_status m3_step(const m3_shape *s, const m3_inputs *in, void *y, m3_state *state, void *stream) {
+    m3_status rc = check_shape(s, true);
+    if (rc != M3_OK) return rc;
+    if ((rc = check_inputs(in, s->batch > 0)) != M3_OK) return rc;
+    if ((rc = check_state(state, true)) != M3_OK) return rc;
+    if (s->batch > 0 && !y) return M3_EINVAL;
+    if (!aligned16(y)) return M3_EINVAL;
+    if (s->batch == 0) return M3_OK;
+    StepParams p;
+    std::memset(&p, 0, sizeof p);
+    p.B = s->batch;
+    p.H = s->nheads;
+    p.P = s->headdim;
+    p.N = s->dstate;
+    p.R = s->rank;
+    p.flags = s->flags;
+    p.eps = s->norm_eps;
+    p.x = in->x;
+    p.Bm = in->Bm;
+    p.Cm = in->Cm;
+    p.dt = in->dt;
+    p.lam = in->lam;
+    p.theta = in->theta;
+    p.A = in->A;
+    p.D = in->D;
+    p.bnw = in->b_norm_w;
+    p.cnw = in->c_norm_w;
+    p.bbias = in->b_bias;
+    p.cbias = in->c_bias;
+    p.y = y;
+    p.h = state->h;
+    p.pB = state->prev_B;
+    p.px = state->prev_x;
+    p.ang = state->angle;
+    return m3::launch_step(s->io == M3_BF16, p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? M3_OK
+               : M3_EHIP;
+}
+
+const char *m3_status_str(m3_status status) {
+    switch (status) {
+        case M3_OK: return "M3_OK: success";
+        case M3_EINVAL: return "M3_EINVAL: invalid argument (NULL pointer, bad size, odd N, rank < 1 or misaligned pointer)";
+        case M3_EUNSUPPORTED: return "M3_EUNSUPPORTED: size outside the supported range (N, P <= 128, R <= 8, chunk in {16,32,64,128}, chunk*R <= 128)";
+        case M3_EWORKSPACE: return "M3_EWORKSPACE: workspace missing or smaller than m3_scan_workspace_bytes()";
+        case M3_EHIP: return "M3_EHIP: a HIP launch failed";
+    }
+    return "unknown m3_status";
+}
+
+const char *m3_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// m3_device.hpp -- device-side helpers for the gfx950 Mamba-3 kernels:
+// bf16 rounding, hi/lo operand splitting, MFMA wrappers, angle reduction.
+//
+// Matrix-core conventions used everywhere (checked on gfx950 hardware):
+//   v_mfma_f32_16x16x32_bf16: lane l, slot j (0..7) of A holds A[l%16][8*(l/16)+j],
+//     slot j of B holds B[8*(l/16)+j][l%16]; result slot i (0..3) is C[4*(l/16)+i][l%16].
+//   v_mfma_f32_16x16x4_f32:  lane l of A holds A[l%16][l/16], of B holds B[l/16][l%16].
+// A "fragment" here is 8 values per lane along the contraction index k; the
+// only requirement is that A and B agree on which logical k each (lane group,
+// slot) carries.  For the fp32 path a fragment feeds 8 consecutive 16x16x4
+// MFMAs (slot j -> instruction j).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ uint32_t f2bf(float f) {  // round to nearest, ties to even
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// split v into hi + lo, both bf16 (hi = rne(v), lo = rne(v - hi)); |v - hi - lo| <= 2^-17 |v|
+__device__ __forceinline__ void split_hl(float v, uint32_t &hi, uint32_t &lo) {
+    hi = f2bf(v);
+    lo = f2bf(v - bf2f(hi));
+}
+__device__ __forceinline__ uint32_t pack2(uint32_t a, uint32_t b) { return a | (b << 16); }
+
+// ---------------------------------------------------------------- io types
+struct IoF32 {
+    typedef float T;
+    static constexpr int bytes = 4;
+    __device__ __forceinline__ static float ld(const float *p) { return *p; }
+    __device__ __forceinline__ static void st(float *p, float v) { *p = v; }
+};
+struct IoBF16 {
+    typedef uint16_t T;
+    static constexpr int bytes = 2;
+    __device__ __forceinline__ static float ld(const uint16_t *p) { return bf2f(*p); }
+    __device__ __forceinline__ static void st(uint16_t *p, float v) { *p = (uint16_t)f2bf(v); }
+};
+
+// ---------------------------------------------------------------- operand fragments
+// Hi/lo bf16 operand (3-product emulation of an fp32 operand) or an fp32 operand.
+struct FragHL { u32x4_t hi, lo; };
+struct FragF { float v[8]; };
+
+__device__ __forceinline__ f32x4_t mfma_bf(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc += A * B, both split:  hi*hi + hi*lo + lo*hi  (the lo*lo term is below fp32 rounding of the sum)
+__device__ __forceinline__ f32x4_t mma(const FragHL &a, const FragHL &b, f32x4_t c) {
+    c = mfma_bf(a.lo, b.hi, c);
+    c = mfma_bf(a.hi, b.lo, c);
+    c = mfma_bf(a.hi, b.hi, c);
+    return c;
+}
+// acc += A * B with B exact in bf16
+__device__ __forceinline__ f32x4_t mma(const FragHL &a, const u32x4_t &b, f32x4_t c) {
+    c = mfma_bf(a.lo, b, c);
+    c = mfma_bf(a.hi, b, c);
+    return c;
+}
+__device__ __forceinline__ f32x4_t mma(const u32x4_t &a, const FragHL &b, f32x4_t c) {
+    c = mfma_bf(a, b.lo, c);
+    c = mfma_bf(a, b.hi, c);
+    return c;
+}
+__device__ __forceinline__ f32x4_t mma(const FragF &a, const FragF &b, f32x4_t c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = mfma_f(a.v[j], b.v[j], c);
+    return c;
+}
+
+// build a hi/lo fragment from 8 floats
+__device__ __forceinline__ FragHL make_hl(const float (&v)[8]) {
+    FragHL f;
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) split_hl(v[j], h[j], l[j]);
+    f.hi = u32x4_t{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+    f.lo = u32x4_t{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+    return f;
+}
+__device__ __forceinline__ FragF make_f(const float (&v)[8]) {
+    FragF f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = v[j];
+    return f;
+}
+
+// ---------------------------------------------------------------- angles
+// Reduce an angle to [0, 2 pi) in double precision (exact enough for any float input).
+__device__ __forceinline__ double wrap_2pi(double a) {
+    const double two_pi = 6.283185307179586476925286766559;
+    double k = floor(a / two_pi);
+    double r = a - k * two_pi;
+    if (r < 0.0) r += two_pi;
+    if (r >= two_pi) r -= two_pi;
+    return r;
+}
+
+}  // namespace m3

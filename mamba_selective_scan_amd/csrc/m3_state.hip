@@ -1,0 +1,285 @@
+// m3_state.hip -- the sequential pass over chunk states, the empty-call state
+// copy, and the single-token decode step.
+#include <type_traits>
+
+#include "m3_device.hpp"
+#include "m3_internal.hpp"
+
+namespace m3 {
+
+// ---------------------------------------------------------------- state pass
+// One thread per (batch, head, p, rotation pair i), pairs fastest.  Walks the
+// chunks in order:
+//     H_0     = Rot(-Theta_init) (h_init + eta_{-1} sum_r prev_B[:, r] prev_x[:, r]^T),
+//               eta_{-1} = dt_0 (1 - lambda_0)   (the deferred boundary term of the
+//               previous call; dotLLM PR #136, "Mamba-3 streaming decode")
+//     H_{c+1} = Rot(-Phi_c) (decay_c H_c + S_c)
+// and overwrites S_c with H_c (the state entering chunk c, in chunk c's frame).
+// The final state is Rot(Theta_final) H_C with Theta_final = Theta_init + sum_c Phi_c
+// (accumulated in double, reduced to [0, 2 pi)).
+__global__ __launch_bounds__(256) void state_pass_kernel(ScanParams p) {
+    const int N2 = p.N / 2, P = p.P, R = p.R, N = p.N;
+    const int64_t per_bh = (int64_t)P * N2;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t bh = gid / per_bh;
+    if (bh >= p.B * p.H) return;
+    const int64_t rem = gid - bh * per_bh;
+    const int pp = (int)(rem / N2), i = (int)(rem - (int64_t)pp * N2);
+    const int64_t b = bh / p.H;
+    const int h = (int)(bh - b * p.H);
+    const int C = p.nchunks;
+
+    float u = 0.f, v = 0.f;  // (H[pp][2i], H[pp][2i+1])
+    double th = 0.0;
+    if (p.h0) {
+        u = p.h0[(bh * N + 2 * i) * P + pp];
+        v = p.h0[(bh * N + 2 * i + 1) * P + pp];
+    }
+    if (p.pB0 && p.px0) {
+        const int64_t g0 = (b * p.T) * p.H + h;  // token 0
+        const float eta = p.dt[g0] * (1.f - p.lam[g0]);
+        float su = 0.f, sv = 0.f;
+        for (int r = 0; r < R; ++r) {
+            const float xr = p.px0[(bh * P + pp) * R + r];
+            su += p.pB0[(bh * N + 2 * i) * R + r] * xr;
+            sv += p.pB0[(bh * N + 2 * i + 1) * R + r] * xr;
+        }
+        u += eta * su;
+        v += eta * sv;
+    }
+    if (p.ang0) {
+        th = (double)p.ang0[bh * N2 + i];
+        float sn, cn;
+        sincosf((float)wrap_2pi(th), &sn, &cn);
+        const float nu = u * cn + v * sn, nv = -u * sn + v * cn;
+        u = nu;
+        v = nv;
+    }
+    float *Sb = p.S + bh * (int64_t)C * P * N + (int64_t)pp * N + 2 * i;
+    const int64_t sstride = (int64_t)P * N;
+    const float *dec = p.decay + bh * C;
+    const int64_t ab = bh * (int64_t)C * N2 + i;
+    // software pipeline: prefetch the next chunk's inputs
+    f32x2_t s_nx = *(const f32x2_t *)Sb;
+    float d_nx = dec[0], c_nx = p.cphi[ab], sn_nx = p.sphi[ab], ph_nx = p.phi[ab];
+    for (int c = 0; c < C; ++c) {
+        const f32x2_t s = s_nx;
+        const float d = d_nx, cp = c_nx, sp = sn_nx, ph = ph_nx;
+        if (c + 1 < C) {
+            s_nx = *(const f32x2_t *)(Sb + (c + 1) * sstride);
+            d_nx = dec[c + 1];
+            c_nx = p.cphi[ab + (int64_t)(c + 1) * N2];
+            sn_nx = p.sphi[ab + (int64_t)(c + 1) * N2];
+            ph_nx = p.phi[ab + (int64_t)(c + 1) * N2];
+        }
+        *(f32x2_t *)(Sb + c * sstride) = f32x2_t{u, v};
+        const float a0 = d * u + s[0], a1 = d * v + s[1];
+        u = a0 * cp + a1 * sp;
+        v = -a0 * sp + a1 * cp;
+        th += (double)ph;
+    }
+    const double thr = wrap_2pi(th);
+    if (p.h1) {
+        float sn, cn;
+        sincosf((float)thr, &sn, &cn);
+        p.h1[(bh * N + 2 * i) * P + pp] = u * cn - v * sn;
+        p.h1[(bh * N + 2 * i + 1) * P + pp] = u * sn + v * cn;
+    }
+    if (pp == 0) p.thfin[bh * N2 + i] = (float)thr;
+}
+
+hipError_t launch_state_pass(const ScanParams &p, hipStream_t stream) {
+    const int64_t total = p.B * p.H * (int64_t)p.P * (p.N / 2);
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(state_pass_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- empty call
+// T == 0: the final state is the initial state (zeros when there is none);
+// the angle is reduced to [0, 2 pi).
+__global__ __launch_bounds__(256) void fill_state_kernel(ScanParams p) {
+    const int64_t nbh = p.B * p.H;
+    const int64_t nh = nbh * p.N * p.P, nb = nbh * p.N * p.R, nx = nbh * p.P * p.R, na = nbh * (p.N / 2);
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool have = p.h0 && p.pB0 && p.px0 && p.ang0;
+    if (gid < nh) p.h1[gid] = have ? p.h0[gid] : 0.f;
+    if (gid < nb) p.pB1[gid] = have ? p.pB0[gid] : 0.f;
+    if (gid < nx) p.px1[gid] = have ? p.px0[gid] : 0.f;
+    if (gid < na) p.ang1[gid] = have ? (float)wrap_2pi((double)p.ang0[gid]) : 0.f;
+}
+
+hipError_t launch_fill_state(const ScanParams &p, hipStream_t stream) {
+    const int64_t nbh = p.B * p.H;
+    int64_t m = nbh * p.N * p.P;
+    if (nbh * p.N * p.R > m) m = nbh * p.N * p.R;
+    if (nbh * p.P * p.R > m) m = nbh * p.P * p.R;
+    if (m == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_state_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- decode step
+// One workgroup per (head, batch).  The step is the recurrence itself for one
+// token (torchmamba "Quickstart": step(u_t, cache)):
+//     Theta <- Theta + theta;  B~, C~ = Rot(Theta)(norm(B) + bias), ...
+//     h <- alpha h + beta sum_r prevB_r prevx_r^T + gamma sum_r B~_r x_r^T
+//     y_r = h^T C~_r + D x_r;  prev_B <- B~;  prev_x <- x
+// Memory-bound: h is read once and written once with 16-byte accesses.
+template <class Io, int VEC>
+__global__ __launch_bounds__(256) void step_kernel(StepParams p) {
+    using ET = typename Io::T;
+    const int h = blockIdx.x;
+    const int64_t b = blockIdx.y;
+    const int N = p.N, P = p.P, R = p.R, N2 = N / 2;
+    const int64_t bh = b * p.H + h;  // == (b, t=0, h) since T = 1
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    float *s_bt = sm;              // [N][R] new B~ (raw B first)
+    float *s_ct = s_bt + N * R;    // [N][R] new C~ (raw C first)
+    float *s_pb = s_ct + N * R;    // [N][R] previous B~
+    float *s_px = s_pb + N * R;    // [P][R] previous x
+    float *s_x = s_px + P * R;     // [P][R] x
+    float *s_cos = s_x + P * R;    // [N/2]
+    float *s_sin = s_cos + N2;     // [N/2]
+    float *s_rs = s_sin + N2;      // [2][R] norm factors (B then C)
+    float *s_red = s_rs + 2 * R;   // [NG][P][R] partial outputs
+
+    const ET *xg = (const ET *)p.x + bh * P * R;
+    const ET *bg = (const ET *)p.Bm + bh * N * R;
+    const ET *cg = (const ET *)p.Cm + bh * N * R;
+    float *hst = p.h + bh * (int64_t)N * P;
+    for (int e = tid; e < N * R; e += 256) {
+        s_bt[e] = Io::ld(bg + e);
+        s_ct[e] = Io::ld(cg + e);
+        s_pb[e] = p.pB[bh * N * R + e];
+    }
+    for (int e = tid; e < P * R; e += 256) {
+        s_x[e] = Io::ld(xg + e);
+        s_px[e] = p.px[bh * P * R + e];
+    }
+    for (int i = tid; i < N2; i += 256) {
+        const double th = wrap_2pi((double)p.ang[bh * N2 + i] + (double)p.theta[bh * N2 + i]);
+        float sn, cn;
+        sincosf((float)th, &sn, &cn);
+        s_cos[i] = cn;
+        s_sin[i] = sn;
+        p.ang[bh * N2 + i] = (float)th;
+    }
+    __syncthreads();
+    // RMS over N per (B or C, rank): one wave per combination
+    const bool bcnorm = (p.flags & 1u) != 0;
+    for (int cb = wave; cb < 2 * R; cb += 4) {
+        const float *src = cb < R ? s_bt : s_ct;
+        const int r = cb < R ? cb : cb - R;
+        float ss = 0.f;
+        for (int n = lane; n < N; n += 64) ss += src[n * R + r] * src[n * R + r];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if (lane == 0) s_rs[cb] = bcnorm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
+    }
+    __syncthreads();
+    // norm, gain, bias, rotation: one thread per (pair, rank)
+    for (int e = tid; e < N2 * R; e += 256) {
+        const int i = e / R, r = e - i * R, n = 2 * i;
+        const float rb = s_rs[r], rc = s_rs[R + r];
+        float gb0 = 1.f, gb1 = 1.f, gc0 = 1.f, gc1 = 1.f;
+        if (bcnorm && p.bnw) { gb0 = p.bnw[n]; gb1 = p.bnw[n + 1]; }
+        if (bcnorm && p.cnw) { gc0 = p.cnw[n]; gc1 = p.cnw[n + 1]; }
+        float u = s_bt[n * R + r] * rb * gb0, w = s_bt[(n + 1) * R + r] * rb * gb1;
+        float uc = s_ct[n * R + r] * rc * gc0, wc = s_ct[(n + 1) * R + r] * rc * gc1;
+        if (p.bbias) {
+            u += p.bbias[((int64_t)h * R + r) * N + n];
+            w += p.bbias[((int64_t)h * R + r) * N + n + 1];
+        }
+        if (p.cbias) {
+            uc += p.cbias[((int64_t)h * R + r) * N + n];
+            wc += p.cbias[((int64_t)h * R + r) * N + n + 1];
+        }
+        const float cn = s_cos[i], sn = s_sin[i];
+        s_bt[n * R + r] = u * cn - w * sn;
+        s_bt[(n + 1) * R + r] = u * sn + w * cn;
+        s_ct[n * R + r] = uc * cn - wc * sn;
+        s_ct[(n + 1) * R + r] = uc * sn + wc * cn;
+    }
+    __syncthreads();
+    for (int e = tid; e < N * R; e += 256) p.pB[bh * N * R + e] = s_bt[e];
+    for (int e = tid; e < P * R; e += 256) p.px[bh * P * R + e] = s_x[e];
+
+    const float dtv = p.dt[bh], lmv = p.lam[bh];
+    const float alpha = __expf(dtv * p.A[h]);
+    const float beta = alpha * dtv * (1.f - lmv), gamma = lmv * dtv;
+
+    // state update and partial outputs; thread = (p group of VEC, n group)
+    const int PG = P / VEC;
+    const int NG = 256 / PG;
+    const int pg = tid % PG, ng = tid / PG;
+    float acc[VEC][8];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[j][r] = 0.f;
+    if (ng < NG) {
+        for (int n = ng; n < N; n += NG) {
+            float hv[VEC];
+            if (VEC == 4) {
+                const f32x4_t v4 = *(const f32x4_t *)(hst + (int64_t)n * P + pg * 4);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) hv[j] = v4[j];
+            } else {
+                hv[0] = hst[(int64_t)n * P + pg];
+            }
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const int pc = pg * VEC + j;
+                float prev = 0.f, cur = 0.f;
+                for (int r = 0; r < R; ++r) {
+                    prev += s_pb[n * R + r] * s_px[pc * R + r];
+                    cur += s_bt[n * R + r] * s_x[pc * R + r];
+                }
+                hv[j] = alpha * hv[j] + beta * prev + gamma * cur;
+                for (int r = 0; r < R && r < 8; ++r) acc[j][r] += hv[j] * s_ct[n * R + r];
+            }
+            if (VEC == 4) {
+                *(f32x4_t *)(hst + (int64_t)n * P + pg * 4) = f32x4_t{hv[0], hv[VEC > 1 ? 1 : 0],
+                                                                       hv[VEC > 2 ? 2 : 0], hv[VEC > 3 ? 3 : 0]};
+            } else {
+                hst[(int64_t)n * P + pg] = hv[0];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            for (int r = 0; r < R; ++r) s_red[(ng * P + pg * VEC + j) * R + r] = acc[j][r];
+    }
+    __syncthreads();
+    ET *yg = (ET *)p.y + bh * P * R;
+    const float Dh = p.D[h];
+    for (int e = tid; e < P * R; e += 256) {
+        float s = 0.f;
+        for (int k = 0; k < NG; ++k) s += s_red[k * P * R + e];
+        Io::st(yg + e, s + Dh * s_x[e]);
+    }
+    (void)lane;
+}
+
+static size_t step_lds_bytes(const StepParams &p, int vec) {
+    const int NG = 256 / (p.P / vec);
+    return sizeof(float) * (size_t)(3 * p.N * p.R + 2 * p.P * p.R + p.N + 2 * p.R + NG * p.P * p.R);
+}
+
+hipError_t launch_step(bool bf16, const StepParams &p, hipStream_t stream) {
+    const int vec = (p.P % 4 == 0) ? 4 : 1;
+    const size_t lds = step_lds_bytes(p, vec);
+    dim3 grid((unsigned)p.H, (unsigned)p.B);
+    if (bf16) {
+        if (vec == 4) hipLaunchKernelGGL((step_kernel<IoBF16, 4>), grid, dim3(256), lds, stream, p);
+        else hipLaunchKernelGGL((step_kernel<IoBF16, 1>), grid, dim3(256), lds, stream, p);
+    } else {
+        if (vec == 4) hipLaunchKernelGGL((step_kernel<IoF32, 4>), grid, dim3(256), lds, stream, p);
+        else hipLaunchKernelGGL((step_kernel<IoF32, 1>), grid, dim3(256), lds, stream, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace m3

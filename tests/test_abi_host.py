@@ -1,0 +1,139 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, sizes the workspace, and rejects bad arguments before any HIP call.
+No kernel is launched here (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmamba3.h")
+
+
+def _lib():
+    import mamba_selective_scan_amd as m3
+    if not os.path.exists(m3.lib_path):
+        from mamba_selective_scan_amd import build
+        build.build(verbose=False)
+    return m3, m3.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(m3_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    m3, lib = _lib()
+    names = declared_functions()
+    assert set(names) >= {"m3_scan_siso", "m3_scan_mimo", "m3_step", "m3_scan_workspace_bytes",
+                          "m3_status_str", "m3_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.m3_version().decode().count(".") == 2
+
+
+def _shape(m3, **kw):
+    base = dict(batch=4, seqlen=2048, nheads=16, headdim=64, dstate=64, rank=1, chunk=64,
+                io=m3.M3_BF16, flags=m3.M3_FLAG_BCNORM, norm_eps=1e-5)
+    base.update(kw)
+    return m3.Shape(**base)
+
+
+def test_workspace_bytes():
+    m3, lib = _lib()
+    s = _shape(m3)
+    ws = m3.m3_scan_workspace_bytes(s)
+    # chunk states dominate: B*H*C*P*N floats
+    assert ws >= 4 * 16 * 32 * 64 * 64 * 4
+    assert ws < 4 * 16 * 32 * 64 * 64 * 4 * 1.1
+    assert m3.m3_scan_workspace_bytes(_shape(m3, seqlen=0)) == 0
+    # the chunk size changes the number of chunk states
+    assert m3.m3_scan_workspace_bytes(_shape(m3, chunk=128)) < ws
+
+
+def _fake_inputs(m3):
+    # host addresses that are 16-byte aligned; never dereferenced (calls fail validation first)
+    buf = ctypes.create_string_buffer(4096)
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    ptrs = {n: ctypes.c_void_p(base) for n in ("x", "Bm", "Cm", "dt", "lam", "theta", "A", "D")}
+    return buf, ptrs
+
+
+def _call_scan(m3, lib, s, inp_over=None, y=True, ws_bytes=None, init=None, fin=None, mimo=False):
+    buf, ptrs = _fake_inputs(m3)
+    if inp_over:
+        ptrs.update(inp_over)
+    inp = m3._Inputs(**ptrs)
+    ws = ctypes.c_void_p(ptrs["x"].value)
+    nbytes = ws_bytes if ws_bytes is not None else m3.m3_scan_workspace_bytes(s) + 1024
+    f = lib.m3_scan_mimo if mimo else lib.m3_scan_siso
+    rc = f(ctypes.byref(s), ctypes.byref(inp), ptrs["x"] if y else None,
+           ctypes.byref(init) if init is not None else None,
+           ctypes.byref(fin) if fin is not None else None, ws, ctypes.c_size_t(nbytes), None)
+    return rc
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dstate=63), 1),          # odd N
+    (dict(dstate=0), 1),
+    (dict(rank=0), 1),
+    (dict(nheads=0), 1),
+    (dict(headdim=0), 1),
+    (dict(batch=-1), 1),
+    (dict(seqlen=-5), 1),
+    (dict(io=7), 1),
+    (dict(flags=0x10), 1),
+    (dict(rank=2), 1),             # SISO call with rank 2
+    (dict(dstate=130), 2),         # N > 128
+    (dict(headdim=129), 2),
+    (dict(chunk=48), 2),
+    (dict(chunk=8), 2),
+])
+def test_invalid_shapes(kw, code):
+    m3, lib = _lib()
+    s = _shape(m3, **kw)
+    assert _call_scan(m3, lib, s) == code
+
+
+def test_invalid_pointers_and_workspace():
+    m3, lib = _lib()
+    s = _shape(m3)
+    assert _call_scan(m3, lib, s, inp_over={"dt": None}) == 1
+    assert _call_scan(m3, lib, s, inp_over={"theta": None}) == 1
+    _, ptrs = _fake_inputs(m3)
+    mis = ctypes.c_void_p(ptrs["x"].value + 2)
+    assert _call_scan(m3, lib, s, inp_over={"Bm": mis}) == 1     # misaligned
+    assert _call_scan(m3, lib, s, y=False) == 1                  # no output
+    assert _call_scan(m3, lib, s, ws_bytes=100) == 3             # short workspace
+    half = m3._State(h=ptrs["x"], prev_B=None, prev_x=ptrs["x"], angle=ptrs["x"])
+    assert _call_scan(m3, lib, s, init=half) == 1                # incomplete state
+
+
+def test_mimo_limits():
+    m3, lib = _lib()
+    assert _call_scan(m3, lib, _shape(m3, rank=9, chunk=16), mimo=True) == 2   # R > 8
+    assert _call_scan(m3, lib, _shape(m3, rank=4, chunk=64), mimo=True) == 2   # 256 rows
+    assert _call_scan(m3, lib, _shape(m3, rank=0, chunk=16), mimo=True) == 1
+
+
+def test_step_validation():
+    m3, lib = _lib()
+    _, ptrs = _fake_inputs(m3)
+    inp = m3._Inputs(**ptrs)
+    st = m3._State(h=ptrs["x"], prev_B=ptrs["x"], prev_x=ptrs["x"], angle=ptrs["x"])
+    s = _shape(m3, seqlen=2)
+    assert lib.m3_step(ctypes.byref(s), ctypes.byref(inp), ptrs["x"], ctypes.byref(st), None) == 1
+    s = _shape(m3, seqlen=1)
+    assert lib.m3_step(ctypes.byref(s), ctypes.byref(inp), ptrs["x"], None, None) == 1
+    s = _shape(m3, seqlen=1, dstate=5)
+    assert lib.m3_step(ctypes.byref(s), ctypes.byref(inp), ptrs["x"], ctypes.byref(st), None) == 1
+
+
+def test_status_strings():
+    m3, lib = _lib()
+    for code, tag in ((0, "M3_OK"), (1, "M3_EINVAL"), (2, "M3_EUNSUPPORTED"), (3, "M3_EWORKSPACE"),
+                      (4, "M3_EHIP")):
+        assert m3.m3_status_str(code).startswith(tag)
+    assert "unknown" in m3.m3_status_str(99)
