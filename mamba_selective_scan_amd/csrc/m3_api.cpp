@@ -68,33 +68,55 @@ m3_status check_state(const m3_state *st, bool required) {
     return M3_OK;
 }
 
-struct WsLayout {
-    size_t S, decay, phi, cphi, sphi, thfin, total;
+// Blocks, segments and workspace of one scan.
+struct Plan {
+    int TB, nblk, nseg, bps, ncg;
+    size_t Sagg, lseg, pseg, cseg, sseg, total;
 };
-
-WsLayout ws_layout(const m3_shape *s) {
-    WsLayout w{};
-    const int64_t T = s->seqlen;
-    const int64_t C = T > 0 ? (T + s->chunk - 1) / s->chunk : 0;
-    const int64_t BH = s->batch * (int64_t)s->nheads;
-    const int64_t N2 = s->dstate / 2;
-    size_t off = 0;
-    w.S = off;     off = align_up(off + sizeof(float) * (size_t)(BH * C * s->headdim * s->dstate));
-    w.decay = off; off = align_up(off + sizeof(float) * (size_t)(BH * C));
-    w.phi = off;   off = align_up(off + sizeof(float) * (size_t)(BH * C * N2));
-    w.cphi = off;  off = align_up(off + sizeof(float) * (size_t)(BH * C * N2));
-    w.sphi = off;  off = align_up(off + sizeof(float) * (size_t)(BH * C * N2));
-    w.thfin = off; off = align_up(off + sizeof(float) * (size_t)(BH * N2));
-    w.total = (C == 0 || BH == 0) ? 0 : off;
-    return w;
-}
 
 TileShape tile_of(const m3_shape *s) {
     TileShape ts;
-    ts.rows = pow2_at_least(s->chunk * s->rank, 32);
     ts.np = pow2_at_least(s->dstate, 32);
-    ts.pp = pow2_at_least(s->headdim, 32);
+    ts.pp = pow2_at_least(s->headdim < 64 ? s->headdim : 64, 32);
+    ts.vec = s->rank == 1 && (s->dstate % 8) == 0 && (s->headdim % 8) == 0;
     return ts;
+}
+
+Plan plan_of(const m3_shape *s) {
+    Plan pl{};
+    const int64_t T = s->seqlen;
+    const TileShape ts0 = tile_of(s);
+    pl.ncg = (s->headdim + ts0.pp - 1) / ts0.pp;
+    const int64_t BH = s->batch * (int64_t)s->nheads * pl.ncg;  // independent (sequence, column group) pairs
+    // tokens per 64-row block: the chunk, capped so chunk * rank fits the block
+    const int cap = m3::kBlockRows / s->rank;
+    pl.TB = s->chunk < cap ? s->chunk : cap;
+    if (pl.TB < 1) pl.TB = 1;
+    pl.nblk = (int)(T > 0 ? (T + pl.TB - 1) / pl.TB : 0);
+    // segments: enough workgroups to fill the 256 compute units at the LDS occupancy
+    const TileShape ts = tile_of(s);
+    const size_t lds = m3::seg_kernel_lds_bytes(true, s->io == M3_BF16, ts);
+    int per_cu = lds ? (int)((160 * 1024) / lds) : 1;
+    if (per_cu < 1) per_cu = 1;
+    if (per_cu > 4) per_cu = 4;
+    const int64_t target = 256LL * per_cu;
+    int64_t nseg = BH > 0 ? (target + BH - 1) / BH : 1;
+    if (nseg > 16) nseg = 16;  // the output kernel folds earlier segments: cost grows as nseg^2
+    if (nseg > pl.nblk) nseg = pl.nblk;
+    if (nseg < 1) nseg = 1;
+    pl.bps = (int)((pl.nblk + nseg - 1) / nseg);
+    if (pl.bps < 1) pl.bps = 1;
+    pl.nseg = pl.nblk > 0 ? (pl.nblk + pl.bps - 1) / pl.bps : 1;
+    const int64_t NS = (BH / pl.ncg) * pl.nseg;
+    const int64_t N2 = s->dstate / 2;
+    size_t off = 0;
+    pl.Sagg = off; off = align_up(off + sizeof(float) * (size_t)(NS * s->headdim * s->dstate));
+    pl.lseg = off; off = align_up(off + sizeof(float) * (size_t)NS);
+    pl.pseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * N2));
+    pl.cseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * N2));
+    pl.sseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * N2));
+    pl.total = (pl.nblk == 0 || BH == 0) ? 0 : off;
+    return pl;
 }
 
 m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_state *init,
@@ -110,11 +132,10 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     if (!aligned16(y)) return M3_EINVAL;
     const TileShape ts = tile_of(s);
     const bool bf = s->io == M3_BF16;
-    if (m3::chunk_kernel_lds_bytes(m3::MODE_OUTPUT, bf, ts) > 160 * 1024 ||
-        m3::chunk_kernel_lds_bytes(m3::MODE_STATE, bf, ts) > 160 * 1024)
+    if (m3::seg_kernel_lds_bytes(true, bf, ts) > 160 * 1024 || m3::seg_kernel_lds_bytes(false, bf, ts) > 160 * 1024)
         return M3_EUNSUPPORTED;
-    const WsLayout wl = ws_layout(s);
-    if (wl.total > 0 && (!ws || ws_bytes < wl.total)) return M3_EWORKSPACE;
+    const Plan pl = plan_of(s);
+    if (pl.total > 0 && (!ws || ws_bytes < pl.total)) return M3_EWORKSPACE;
     if (!aligned16(ws)) return M3_EINVAL;
 
     ScanParams p;
@@ -125,8 +146,11 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     p.P = s->headdim;
     p.N = s->dstate;
     p.R = s->rank;
-    p.Q = s->chunk;
-    p.nchunks = (int)(s->seqlen > 0 ? (s->seqlen + s->chunk - 1) / s->chunk : 0);
+    p.TB = pl.TB;
+    p.nblk = pl.nblk;
+    p.nseg = pl.nseg;
+    p.bps = pl.bps;
+    p.ncg = pl.ncg;
     p.flags = s->flags;
     p.eps = s->norm_eps;
     p.x = in->x;
@@ -160,18 +184,14 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
         if (!fin) return M3_OK;
         return m3::launch_fill_state(p, st) == hipSuccess ? M3_OK : M3_EHIP;
     }
-    if (p.nchunks > 65535) return M3_EUNSUPPORTED;
     char *base = static_cast<char *>(ws);
-    p.S = reinterpret_cast<float *>(base + wl.S);
-    p.decay = reinterpret_cast<float *>(base + wl.decay);
-    p.phi = reinterpret_cast<float *>(base + wl.phi);
-    p.cphi = reinterpret_cast<float *>(base + wl.cphi);
-    p.sphi = reinterpret_cast<float *>(base + wl.sphi);
-    p.thfin = reinterpret_cast<float *>(base + wl.thfin);
-
-    if (m3::launch_chunk_kernel(m3::MODE_STATE, bf, ts, p, st) != hipSuccess) return M3_EHIP;
-    if (m3::launch_state_pass(p, st) != hipSuccess) return M3_EHIP;
-    if (m3::launch_chunk_kernel(m3::MODE_OUTPUT, bf, ts, p, st) != hipSuccess) return M3_EHIP;
+    p.Sagg = reinterpret_cast<float *>(base + pl.Sagg);
+    p.lseg = reinterpret_cast<float *>(base + pl.lseg);
+    p.pseg = reinterpret_cast<float *>(base + pl.pseg);
+    p.cseg = reinterpret_cast<float *>(base + pl.cseg);
+    p.sseg = reinterpret_cast<float *>(base + pl.sseg);
+    if (p.nseg > 1 && m3::launch_seg_state(bf, ts, p, st) != hipSuccess) return M3_EHIP;
+    if (m3::launch_seg_output(bf, ts, p, st) != hipSuccess) return M3_EHIP;
     return M3_OK;
 }
 
@@ -183,7 +203,9 @@ size_t m3_scan_workspace_bytes(const m3_shape *shape) {
     if (!shape || shape->chunk < 1 || shape->seqlen < 0 || shape->batch < 0 || shape->nheads < 1 ||
         shape->headdim < 1 || shape->dstate < 2)
         return 0;
-    return ws_layout(shape).total;
+    if (shape->rank < 1 || shape->rank > 8 || (shape->dstate & 1) || shape->dstate > 128 || shape->headdim > 128)
+        return 0;
+    return plan_of(shape).total;
 }
 
 m3_status m3_scan_siso(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,

@@ -87,14 +87,27 @@ __device__ __forceinline__ f32x4_t mma(const FragF &a, const FragF &b, f32x4_t c
     return c;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 words hi = rne(v), lo = rne(v - hi) (one v_cvt_pk_bf16_f32 each)
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    const uint32_t hu = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+    const float ha = __uint_as_float(hu << 16), hb = __uint_as_float(hu & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a - ha, b - hb}, bf16x2_t));
+    hi = hu;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // build a hi/lo fragment from 8 floats
 __device__ __forceinline__ FragHL make_hl(const float (&v)[8]) {
     FragHL f;
-    uint32_t h[8], l[8];
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) split_hl(v[j], h[j], l[j]);
-    f.hi = u32x4_t{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-    f.lo = u32x4_t{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+    for (int j = 0; j < 4; ++j) split2(v[2 * j], v[2 * j + 1], h[j], l[j]);
+    f.hi = u32x4_t{h[0], h[1], h[2], h[3]};
+    f.lo = u32x4_t{l[0], l[1], l[2], l[3]};
     return f;
 }
 __device__ __forceinline__ FragF make_f(const float (&v)[8]) {
@@ -108,7 +121,8 @@ __device__ __forceinline__ FragF make_f(const float (&v)[8]) {
 // Reduce an angle to [0, 2 pi) in double precision (exact enough for any float input).
 __device__ __forceinline__ double wrap_2pi(double a) {
     const double two_pi = 6.283185307179586476925286766559;
-    double k = floor(a / two_pi);
+    const double inv_two_pi = 0.15915494309189533576888376337251;
+    double k = floor(a * inv_two_pi);
     double r = a - k * two_pi;
     if (r < 0.0) r += two_pi;
     if (r >= two_pi) r -= two_pi;

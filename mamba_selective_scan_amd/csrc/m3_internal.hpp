@@ -1,4 +1,4 @@
-// m3_internal.hpp -- parameter block and launcher declarations shared by the
+// m3_internal.hpp -- parameter blocks and launcher declarations shared by the
 // host dispatch (m3_api.cpp) and the kernel translation units.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -7,11 +7,18 @@
 
 namespace m3 {
 
+// Rows of one matrix-core block: (token, rank) pairs, rank fastest.
+constexpr int kBlockRows = 64;
+
 struct ScanParams {
     // sizes
     int64_t B, T;
-    int H, P, N, R, Q;  // Q = tokens per chunk
-    int nchunks;
+    int H, P, N, R;
+    int TB;    // tokens per block (TB * R <= kBlockRows)
+    int nblk;  // blocks per (batch, head) sequence
+    int nseg;  // segments per sequence (a workgroup walks one segment's blocks in order)
+    int bps;   // blocks per segment
+    int ncg;   // column groups: P is split across workgroups in groups of at most 64 columns
     uint32_t flags;
     float eps;
     // inputs
@@ -22,13 +29,12 @@ struct ScanParams {
     // carried state
     const float *h0, *pB0, *px0, *ang0;  // initial (NULL = zeros)
     float *h1, *pB1, *px1, *ang1;        // final (NULL = not requested)
-    // workspace
-    float *S;      // [B][H][C][P][N]  chunk states (in place: states entering each chunk)
-    float *decay;  // [B][H][C]        exp(sum of log alpha over the chunk)
-    float *phi;    // [B][H][C][N/2]   chunk angle totals
-    float *cphi;   // [B][H][C][N/2]   cos of phi
-    float *sphi;   // [B][H][C][N/2]   sin of phi
-    float *thfin;  // [B][H][N/2]      final cumulative angle, in [0, 2 pi)
+    // workspace: per-segment aggregates written by the state kernel
+    float *Sagg;  // [B*H][nseg][P][N]  state contributed by the segment, from zero, in its end frame
+    float *lseg;  // [B*H][nseg]        sum of dt*A over the segment
+    float *pseg;  // [B*H][nseg][N/2]   segment angle total reduced to [0, 2 pi)
+    float *cseg;  // [B*H][nseg][N/2]   cos of the segment angle total
+    float *sseg;  // [B*H][nseg][N/2]   sin of the segment angle total
 };
 
 struct StepParams {
@@ -43,18 +49,16 @@ struct StepParams {
     float *h, *pB, *px, *ang;
 };
 
-enum { MODE_STATE = 0, MODE_OUTPUT = 1 };
-
-// Tile shape chosen by the host: rows per chunk (Q*R padded), padded N, padded P.
+// Tile variant chosen by the host.
 struct TileShape {
-    int rows, np, pp;
+    int np;    // N padded: 32, 64 or 128
+    int pp;    // columns per workgroup, padded: 32 or 64
+    bool vec;  // SISO with N % 8 == 0 and P % 8 == 0: 16-byte global accesses
 };
 
-// Launchers (return hipSuccess or the launch error).  Defined in the kernel TUs.
-hipError_t launch_chunk_kernel(int mode, bool bf16, const TileShape &ts, const ScanParams &p,
-                               hipStream_t stream);
-size_t chunk_kernel_lds_bytes(int mode, bool bf16, const TileShape &ts);
-hipError_t launch_state_pass(const ScanParams &p, hipStream_t stream);
+hipError_t launch_seg_state(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t stream);
+hipError_t launch_seg_output(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t stream);
+size_t seg_kernel_lds_bytes(bool output, bool bf16, const TileShape &ts);
 hipError_t launch_fill_state(const ScanParams &p, hipStream_t stream);
 hipError_t launch_step(bool bf16, const StepParams &p, hipStream_t stream);
 

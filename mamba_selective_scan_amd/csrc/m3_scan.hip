@@ -1,0 +1,33 @@
+// m3_scan.hip -- choice of the scan kernel variant (io type x load path).
+#include "m3_internal.hpp"
+
+namespace m3 {
+
+#define M3_DECLARE(NAME)                                                                              \
+    hipError_t NAME##_launch(bool output, const TileShape &ts, const ScanParams &p, hipStream_t st); \
+    size_t NAME##_bytes(bool output, const TileShape &ts);
+M3_DECLARE(scan_bf16_vec)
+M3_DECLARE(scan_bf16_gen)
+M3_DECLARE(scan_f32_vec)
+M3_DECLARE(scan_f32_gen)
+#undef M3_DECLARE
+
+size_t seg_kernel_lds_bytes(bool output, bool bf16, const TileShape &ts) {
+    if (bf16) return ts.vec ? scan_bf16_vec_bytes(output, ts) : scan_bf16_gen_bytes(output, ts);
+    return ts.vec ? scan_f32_vec_bytes(output, ts) : scan_f32_gen_bytes(output, ts);
+}
+
+static hipError_t launch(bool output, bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t st) {
+    if (bf16) return ts.vec ? scan_bf16_vec_launch(output, ts, p, st) : scan_bf16_gen_launch(output, ts, p, st);
+    return ts.vec ? scan_f32_vec_launch(output, ts, p, st) : scan_f32_gen_launch(output, ts, p, st);
+}
+
+hipError_t launch_seg_state(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t st) {
+    return launch(false, bf16, ts, p, st);
+}
+
+hipError_t launch_seg_output(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t st) {
+    return launch(true, bf16, ts, p, st);
+}
+
+}  // namespace m3

@@ -1,0 +1,6 @@
+// m3_scan_f32_vec.hip -- kernel instances for one (io type, load path) pair.
+#include "m3_scan_impl.hpp"
+
+namespace m3 {
+M3_DEFINE_VARIANT(scan_f32_vec, IoF32, true)
+}  // namespace m3

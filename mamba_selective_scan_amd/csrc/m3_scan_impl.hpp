@@ -1,0 +1,1212 @@
+// m3_scan_impl.hpp -- the chunked Mamba-3 scan on gfx950 (kernel templates).
+//
+// Method.  Chunkwise SSD (torchmamba README, "Math notes", M2: an intra-chunk
+// quadratic part plus a factored state carry between chunks) applied to the
+// Mamba-3 trapezoid in its single-scan form (dotLLM PR #136, comment
+// "Mamba-3 streaming decode": per-token scale gamma_t + eta_t with the
+// one-token lookahead eta_t = dt_{t+1}(1 - lambda_{t+1}), which crosses block
+// edges).  With the shifted state h'_t = h_t + eta_t B~_t x_t^T:
+//     h'_t = alpha_t h'_{t-1} + (gamma_t + eta_t) B~_t x_t^T
+//     y_t  = C~_t^T h'_t - eta_t (C~_t . B~_t) x_t + D x_t
+// so inside a block the mask is
+//     L[t, s] = exp(cs_t - cs_s) * (s < t ? scale_s : s == t ? gamma_t : 0)
+// with cs the running sum of dt*A inside the block.  Rotations use
+// block-local angles (running sum of theta from the block start); a carried
+// state lives in the frame of the block it enters:
+//     H_next = Rot(-Phi_end) (exp(cs_end) H + S),   S = sum_s exp(cs_end - cs_s) scale_s B~_s x_s^T.
+//
+// Work split.  A block is 64 rows ((token, rank) pairs, rank fastest).  The
+// blocks of one (batch, head) sequence are cut into segments, and the head
+// dimension P into column groups of at most 64; a workgroup walks the blocks
+// of one segment in order for one column group, carrying the state in
+// registers:
+//   seg_state_kernel : per segment, the state it contributes starting from zero
+//                      (to the workspace; not run for the last segment).
+//   seg_output_kernel: per segment, the incoming state (initial state folded
+//                      through the earlier segments' contributions), then for
+//                      each block the outputs and the state update.
+// No workgroup waits for another: the output kernel reads only what the state
+// kernel, launched before it on the same stream, wrote.
+//
+// Matrix cores.  Wave w owns rows 16w..16w+15 of a block.
+//   G^T tiles  = B~[s rows] C~[t rows]^T    (A: B~ from LDS, B: C~ in registers)
+//   Y_intra   += (G o L) X                  (the G^T result fragments are the A operand)
+//   Y_inter    = C~ H                       (B: H^T from LDS)
+//   S          = (w B~)^T X                 (A: (w B~)^T, B: X^T, both from LDS)
+// The state fragments hold S[n = 4g + i][p = l16] per 16x16 tile, so the two
+// components of a rotation pair sit in one lane.
+// bf16 I/O: every inexact operand is split into hi + lo bf16 and multiplied
+// as hi*hi + hi*lo + lo*hi (x itself is exact); fp32 I/O uses the fp32 MFMA.
+#pragma once
+#include <type_traits>
+
+#include "m3_device.hpp"
+#include "m3_internal.hpp"
+
+namespace m3 {
+
+// sin and cos of an angle: reduce to [-pi, pi] with a two-constant 2 pi (hi + lo,
+// both fused multiply-adds), then the hardware sin/cos units, which take the
+// argument in revolutions.
+__device__ __forceinline__ void fast_sincos(float a, float &s, float &c) {
+    const float two_pi_hi = 6.28318548202514648f;      // float nearest to 2 pi
+    const float two_pi_lo = -1.7484555314695172e-07f;  // 2 pi - two_pi_hi
+    const float inv_two_pi = 0.15915494309189535f;
+    const float k = rintf(a * inv_two_pi);
+    float r = fmaf(-k, two_pi_hi, a);
+    r = fmaf(-k, two_pi_lo, r);
+    const float rev = r * inv_two_pi;
+    s = __builtin_amdgcn_sinf(rev);
+    c = __builtin_amdgcn_cosf(rev);
+}
+__device__ __forceinline__ f32x2_t sincos_acc(float a) {
+    float s, c;
+    fast_sincos(a, s, c);
+    return f32x2_t{s, c};
+}
+
+// v + (value of the lane K to the left inside its row of 16 lanes, or 0)
+template <int K>
+__device__ __forceinline__ float add_row_shr(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + K, 0xF, 0xF, true));
+}
+// inclusive add-scan over the 16 lanes of each DPP row
+__device__ __forceinline__ float row_incl_scan(float v) {
+    v = add_row_shr<1>(v);
+    v = add_row_shr<2>(v);
+    v = add_row_shr<4>(v);
+    v = add_row_shr<8>(v);
+    return v;
+}
+
+// inclusive add-scan of 64 lanes (every lane of the wave must be active)
+__device__ __forceinline__ float wave_incl_scan(float v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// LDS-only workgroup barrier (global memory needs no ordering between the waves here)
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <class Io, int NP_, int PP_, bool VEC_>
+struct SegCfg {
+    using ET = typename Io::T;
+    static constexpr bool BF = std::is_same<Io, IoBF16>::value;
+    static constexpr bool VEC = VEC_;
+    static constexpr int NP = NP_, PP = PP_;
+    static constexpr int ROWS = kBlockRows;
+    static constexpr int KS = NP / 32;  // 32-wide k steps over n
+    static constexpr int PT = PP / 16;  // p tiles
+    static constexpr int NT = NP / 16;  // n tiles
+    static constexpr int TPW = (PT * NT + 3) / 4;  // state tiles per wave
+    static constexpr int ES = BF ? 2 : 4;          // bytes per operand element per plane
+    static constexpr int NPL = BF ? 2 : 1;         // planes: (hi, lo) or (fp32)
+    static constexpr int PADE = BF ? 8 : 4;        // 16 bytes of padding per row
+    static constexpr int OPP = NP + PADE;          // pitch of [row][n] and [p][n]
+    static constexpr int RPP = ROWS + PADE;        // pitch of [p][row] and [n][row]
+    static constexpr int PHP = NP / 2;             // pitch of the angle table [token][pair]
+    static constexpr int XW = BF ? 8 : 4;          // io elements per 16-byte vector
+    // per-thread raw counts
+    static constexpr int XN = VEC ? (ROWS * PP / XW / 256) * 4 : ROWS * PP / 256;  // x words / elements
+    static constexpr int TN = VEC ? 4 * KS : ROWS * (NP / 2) / 256;               // theta floats
+    static constexpr int BWV = BF ? 4 : 8;  // words per 8 B/C elements when VEC
+
+    static constexpr size_t al(size_t v) { return (v + 15) / 16 * 16; }
+    static constexpr size_t BT_PLANE = (size_t)ROWS * OPP;  // elements per plane
+    static constexpr size_t WB_PLANE = (size_t)NP * RPP;
+    static constexpr size_t HT_PLANE = (size_t)PP * OPP;
+    static constexpr size_t L_BT = al(BT_PLANE * ES * NPL);
+    static constexpr size_t L_WB = al(WB_PLANE * ES * NPL);
+    static constexpr size_t L_XT = al((size_t)PP * RPP * ES);
+    static constexpr size_t L_HT = al(HT_PLANE * ES * NPL);
+    static constexpr size_t L_Y = al((size_t)ROWS * PP * sizeof(ET));
+    // angles: the general path keeps a table [token][pair]; the SISO path only tile totals [4][pair]
+    static constexpr size_t L_PHI = al(VEC ? (size_t)4 * (NP / 2) * 4 : (size_t)ROWS * PHP * 4);
+    // scalars: cs, scale, gamma, w, exp(cs) [ROWS]; scan scratch [256 + 8];
+    // per pair: block angle total, its cos and sin; per pair (double): running angle base
+    static constexpr size_t L_SC0 = al((5 * ROWS + 264 + 3 * (NP / 2)) * 4);
+    static constexpr size_t L_SC = L_SC0 + (size_t)(NP / 2) * 8;
+    static constexpr size_t STATE_BYTES = L_WB + L_XT + L_PHI + L_SC;
+    static constexpr size_t OUTPUT_BYTES = L_BT + L_WB + L_XT + L_HT + L_Y + L_PHI + L_SC;
+};
+
+// Raw inputs of one block, prefetched into registers.  With VEC the words are
+// the unconverted 16-byte loads; otherwise they are float bits.
+template <class Cfg, bool WANT_C>
+struct RawBlock {
+    static constexpr int BW = (Cfg::VEC && Cfg::BF) ? 4 : 8;  // words per 8 values
+    uint32_t b[Cfg::KS][BW];
+    uint32_t c[WANT_C ? Cfg::KS : 1][BW];
+    uint32_t x[Cfg::XN];
+    float th[Cfg::TN];
+    float dt, lam, dtn, lamn;
+};
+
+struct BlockGeo {
+    int64_t t0;  // first token
+    int Tv;      // valid tokens
+};
+
+__device__ __forceinline__ BlockGeo block_geo(const ScanParams &p, int blk) {
+    BlockGeo g;
+    g.t0 = (int64_t)blk * p.TB;
+    const int64_t rem = p.T - g.t0;
+    g.Tv = (int)(rem < (int64_t)p.TB ? rem : (int64_t)p.TB);
+    return g;
+}
+
+// LDS carve-up
+template <class Cfg, bool OUT>
+struct Smem {
+    unsigned char *bt, *wb, *xt, *ht, *ys, *phi;
+    float *cs, *scale, *gam, *w, *ecs, *tmp, *pend, *cph, *sph;
+    double *base;
+    __device__ __forceinline__ explicit Smem(unsigned char *s) {
+        unsigned char *q = s;
+        if (OUT) { bt = q; q += Cfg::L_BT; } else { bt = nullptr; }
+        wb = q; q += Cfg::L_WB;
+        xt = q; q += Cfg::L_XT;
+        if (OUT) { ht = q; q += Cfg::L_HT; ys = q; q += Cfg::L_Y; } else { ht = nullptr; ys = nullptr; }
+        phi = q; q += Cfg::L_PHI;
+        float *f = (float *)q;
+        cs = f; scale = cs + Cfg::ROWS; gam = scale + Cfg::ROWS; w = gam + Cfg::ROWS; ecs = w + Cfg::ROWS;
+        tmp = ecs + Cfg::ROWS;
+        pend = tmp + 264; cph = pend + Cfg::NP / 2; sph = cph + Cfg::NP / 2;
+        base = (double *)(q + Cfg::L_SC0);
+    }
+};
+
+// Per-workgroup constants: the sequence's base pointers and token strides.
+struct WgCtx {
+    int64_t b, bh;
+    int h, cg, seg, p0, Pw, blk0, blk1;
+    int R;      // rank (compile-time 1 on the SISO path)
+    float invR; // 1 / R, to turn rows into tokens without an integer divide
+    const void *xb, *Bb, *Cb;  // x, B, C at (b, token 0, h) (x offset by the column group)
+    const float *thb, *dtb, *lamb;
+    void *yb;
+    int sx, sbc, sth, sdt;     // token strides in elements: H*P*R, H*N*R, H*N/2, H
+    float invN, eps;
+    bool bcnorm, affine;
+};
+
+__device__ __forceinline__ int tok_of(int row, const WgCtx &c) {
+    return (int)(((float)row + 0.5f) * c.invR);
+}
+
+// Issue the global loads of one block (nothing is converted so the loads stay in flight).
+template <class Io, class Cfg, bool WANT_C>
+__device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const ScanParams &p, const WgCtx &c,
+                                           const BlockGeo &g) {
+    using ET = typename Io::T;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, gq = lane >> 4;
+    const int64_t T = p.T, H = p.H;
+    const int N = p.N, P = p.P, N2 = p.N / 2;
+    const int row = wave * 16 + l16;
+    const int64_t b = c.b;
+    const int h = c.h;
+    if constexpr (Cfg::VEC) {
+        // SISO, N and P multiples of 8: row == token, 8 consecutive n per (lane, k step).
+        // Uniform 64-bit block bases plus 32-bit per-lane byte offsets.
+        const bool rv = row < g.Tv;
+        const char *bbase = (const char *)c.Bb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
+        const char *cbase = (const char *)c.Cb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
+        const char *tbase = (const char *)c.thb + (int64_t)g.t0 * c.sth * 4;
+        const uint32_t boff = (uint32_t)row * (uint32_t)(c.sbc * sizeof(ET)) + (uint32_t)(8 * gq * sizeof(ET));
+        const uint32_t toff = (uint32_t)row * (uint32_t)(c.sth * 4) + (uint32_t)(16 * gq);
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KS; ++kk) {
+            const bool ok = rv && kk * 32 + 8 * gq < N;
+#pragma unroll
+            for (int q = 0; q < Cfg::BWV / 4; ++q) {
+                u32x4_t vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
+                const uint32_t o = boff + (uint32_t)((kk * 32 + q * Cfg::XW) * sizeof(ET));
+                if (ok) {
+                    vb = *(const u32x4_t *)(bbase + o);
+                    if constexpr (WANT_C) vc = *(const u32x4_t *)(cbase + o);
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    rb.b[kk][q * 4 + k] = vb[k];
+                    if constexpr (WANT_C) rb.c[kk][q * 4 + k] = vc[k];
+                }
+            }
+            // angles of this lane's pairs: kk*16 + 4g + 0..3
+            f32x4_t tv = {0.f, 0.f, 0.f, 0.f};
+            if (ok) tv = *(const f32x4_t *)(tbase + toff + kk * 64);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rb.th[kk * 4 + k] = tv[k];
+        }
+        const char *xbase = (const char *)c.xb + (int64_t)g.t0 * c.sx * (int64_t)sizeof(ET);
+#pragma unroll
+        for (int m = 0; m < Cfg::XN / 4; ++m) {
+            const int e = tid + 256 * m;
+            const int xr = e / (Cfg::PP / Cfg::XW), pc = (e % (Cfg::PP / Cfg::XW)) * Cfg::XW;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            const uint32_t o = (uint32_t)xr * (uint32_t)(c.sx * sizeof(ET)) + (uint32_t)(pc * sizeof(ET));
+            if (xr < g.Tv && pc < c.Pw) v = *(const u32x4_t *)(xbase + o);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rb.x[m * 4 + k] = v[k];
+        }
+    } else {
+        // general layout (rank R, any even N, any P): element loads
+        const int R = c.R;
+        const int tok = tok_of(row, c), r = row - tok * R;
+        const bool rv = tok < g.Tv;
+        const int64_t base = ((b * T + g.t0 + tok) * H + h) * (int64_t)N * R + r;
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KS; ++kk) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int n = kk * 32 + 8 * gq + j;
+                const bool ok = rv && n < N;
+                rb.b[kk][j] = __float_as_uint(ok ? Io::ld((const ET *)p.Bm + base + (int64_t)n * R) : 0.f);
+                if constexpr (WANT_C)
+                    rb.c[kk][j] = __float_as_uint(ok ? Io::ld((const ET *)p.Cm + base + (int64_t)n * R) : 0.f);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < Cfg::XN; ++m) {
+            const int e = tid + 256 * m;
+            const int xrow = e / Cfg::PP, pc = e - xrow * Cfg::PP;
+            const int xt = tok_of(xrow, c), xrk = xrow - xt * R;
+            float v = 0.f;
+            if (xt < g.Tv && pc < c.Pw)
+                v = Io::ld((const ET *)p.x + ((b * T + g.t0 + xt) * H + h) * (int64_t)P * R + (int64_t)(c.p0 + pc) * R + xrk);
+            rb.x[m] = __float_as_uint(v);
+        }
+#pragma unroll
+        for (int m = 0; m < Cfg::TN; ++m) {
+            const int e = tid + 256 * m;
+            const int tr = e / (Cfg::NP / 2), pc = e - tr * (Cfg::NP / 2);
+            rb.th[m] = (tr < g.Tv && pc < N2) ? p.theta[((b * T + g.t0 + tr) * H + h) * (int64_t)N2 + pc] : 0.f;
+        }
+    }
+    if (wave == 0) {
+        rb.dt = rb.lam = rb.dtn = rb.lamn = 0.f;
+        const float *db = c.dtb + (int64_t)g.t0 * c.sdt, *lb = c.lamb + (int64_t)g.t0 * c.sdt;
+        const uint32_t o = (uint32_t)lane * (uint32_t)c.sdt;
+        if (lane < g.Tv) {
+            rb.dt = db[o];
+            rb.lam = lb[o];
+            if (g.t0 + lane + 1 < T) {
+                rb.dtn = db[o + c.sdt];
+                rb.lamn = lb[o + c.sdt];
+            }
+        }
+    }
+    (void)b;
+    (void)h;
+    (void)H;
+    (void)P;
+}
+
+// decode the 8 B or C values of one k step
+template <class Cfg, int BW>
+__device__ __forceinline__ void raw8(const uint32_t (&w)[BW], float (&v)[8]) {
+    if constexpr (Cfg::VEC && Cfg::BF) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(w[k]);
+    }
+}
+
+// Stage 1 of a block: per-token scalars, angle partial sums and X^T into LDS.
+// SISO: the angle running sum inside each wave's 16 rows is taken in
+// registers (returned in `phi`); the 16-row totals go to LDS.  Ends with a barrier.
+template <class Io, class Cfg, bool WANT_C, class Sm>
+__device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const Sm &sm, const ScanParams &p,
+                                                const WgCtx &c, const BlockGeo &g) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15;
+    if (wave == 0) {
+        // log alpha, gamma, eta (next token's dt (1 - lambda); 0 after the last token), scale
+        const float la = rb.dt * p.A[c.h];
+        const float ga = rb.lam * rb.dt;
+        const float sc = ga + rb.dtn * (1.f - rb.lamn);
+        const float cs = wave_incl_scan(la);
+        const float cs_end = __shfl(cs, 63, 64);
+        sm.cs[lane] = cs;
+        sm.scale[lane] = sc;
+        sm.gam[lane] = ga;
+        sm.ecs[lane] = __expf(cs);
+        sm.w[lane] = __expf(cs_end - cs) * sc;
+    }
+    if constexpr (Cfg::VEC) {
+        float *tt = (float *)sm.phi;  // [4 tiles][NP/2]
+#pragma unroll
+        for (int k = 0; k < Cfg::TN; ++k) rb.th[k] = row_incl_scan(rb.th[k]);
+        if (l16 == 15) {
+            const int gq = lane >> 4;
+#pragma unroll
+            for (int kk = 0; kk < Cfg::KS; ++kk)
+                *(f32x4_t *)(tt + wave * (Cfg::NP / 2) + kk * 16 + 4 * gq) =
+                    f32x4_t{rb.th[kk * 4], rb.th[kk * 4 + 1], rb.th[kk * 4 + 2], rb.th[kk * 4 + 3]};
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < Cfg::TN; ++m) {
+            const int e = tid + 256 * m;
+            const int tr = e / (Cfg::NP / 2), pc = e - tr * (Cfg::NP / 2);
+            ((float *)sm.phi)[tr * Cfg::PHP + pc] = rb.th[m];
+        }
+    }
+    // x -> X^T [p][row]
+    if constexpr (Cfg::VEC) {
+#pragma unroll
+        for (int m = 0; m < Cfg::XN / 4; ++m) {
+            const int e = tid + 256 * m;
+            const int xr = e / (Cfg::PP / Cfg::XW), pc = (e % (Cfg::PP / Cfg::XW)) * Cfg::XW;
+            if constexpr (Cfg::BF) {
+                uint16_t *xt = (uint16_t *)sm.xt;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    xt[(pc + 2 * k) * Cfg::RPP + xr] = (uint16_t)(rb.x[m * 4 + k] & 0xffffu);
+                    xt[(pc + 2 * k + 1) * Cfg::RPP + xr] = (uint16_t)(rb.x[m * 4 + k] >> 16);
+                }
+            } else {
+                float *xt = (float *)sm.xt;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) xt[(pc + k) * Cfg::RPP + xr] = __uint_as_float(rb.x[m * 4 + k]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < Cfg::XN; ++m) {
+            const int e = tid + 256 * m;
+            const int xrow = e / Cfg::PP, pc = e - xrow * Cfg::PP;
+            const float v = __uint_as_float(rb.x[m]);
+            if constexpr (Cfg::BF) ((uint16_t *)sm.xt)[pc * Cfg::RPP + xrow] = (uint16_t)f2bf(v);
+            else ((float *)sm.xt)[pc * Cfg::RPP + xrow] = v;
+        }
+    }
+    lds_barrier();
+}
+
+// Stage 2 (general path only): running angle over the table (segmented scan per pair).  Ends with a barrier.
+template <class Cfg, class Sm>
+__device__ __forceinline__ void stage_angles_table(const Sm &sm, const ScanParams &p, const BlockGeo &g) {
+    const int tid = threadIdx.x;
+    const int N2 = p.N / 2;
+    const int Tv = g.Tv;
+    float *phi = (float *)sm.phi;
+    int nseg = 256 / N2;
+    if (nseg > Tv) nseg = Tv;
+    if (nseg < 1) nseg = 1;
+    const int seglen = (Tv + nseg - 1) / nseg;
+    const int i = tid % N2, sg = tid / N2;
+    if (sg < nseg) {
+        const int ta = sg * seglen, tb = min(Tv, ta + seglen);
+        float acc = 0.f;
+        for (int t = ta; t < tb; ++t) {
+            acc += phi[t * Cfg::PHP + i];
+            phi[t * Cfg::PHP + i] = acc;
+        }
+        sm.tmp[sg * N2 + i] = acc;
+    }
+    lds_barrier();
+    if (sg < nseg && sg > 0) {
+        float off = 0.f;
+        for (int k = 0; k < sg; ++k) off += sm.tmp[k * N2 + i];
+        const int ta = sg * seglen, tb = min(Tv, ta + seglen);
+        for (int t = ta; t < tb; ++t) phi[t * Cfg::PHP + i] += off;
+    }
+    lds_barrier();
+}
+
+// Block angle totals per pair (and their cos/sin) for the carry.  Reads the
+// angle data of stage 1/2; the results are consumed after a later barrier.
+template <class Cfg, class Sm>
+__device__ __forceinline__ void block_angle_totals(const Sm &sm, const ScanParams &p, const BlockGeo &g) {
+    const int tid = threadIdx.x;
+    const int N2 = p.N / 2;
+    if (tid < N2) {
+        float a;
+        if constexpr (Cfg::VEC) {
+            const float *tt = (const float *)sm.phi;
+            a = tt[tid] + tt[Cfg::NP / 2 + tid] + tt[2 * (Cfg::NP / 2) + tid] + tt[3 * (Cfg::NP / 2) + tid];
+        } else {
+            a = ((const float *)sm.phi)[(g.Tv - 1) * Cfg::PHP + tid];
+        }
+        float s, c;
+        { const f32x2_t sc_ = sincos_acc(a); s = sc_[0]; c = sc_[1]; }
+        sm.pend[tid] = a;
+        sm.cph[tid] = c;
+        sm.sph[tid] = s;
+    }
+}
+
+// Stage 3: B~ (and C~) for the rows this lane owns.  Writes B~ [row][n] (output
+// mode) and (w B~)^T [n][row] planes to LDS; returns C~ fragments.
+template <class Io, class Cfg, bool WANT_C, class Frag, class Sm>
+__device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, const Sm &sm, const ScanParams &p,
+                                               const WgCtx &c, const BlockGeo &g, Frag (&ct)[Cfg::KS]) {
+    constexpr int KS = Cfg::KS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, gq = lane >> 4;
+    const int N = p.N;
+    const int R = Cfg::VEC ? 1 : c.R;
+    const int row = wave * 16 + l16;
+    const int tok = Cfg::VEC ? row : tok_of(row, c);
+    const int r = row - tok * R;
+    const bool rv = tok < g.Tv;
+    float ssb = 0.f, ssc = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        float vb[8], vc[8];
+        raw8<Cfg>(rb.b[kk], vb);
+        if constexpr (WANT_C) raw8<Cfg>(rb.c[kk], vc);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            ssb = fmaf(vb[j], vb[j], ssb);
+            if constexpr (WANT_C) ssc = fmaf(vc[j], vc[j], ssc);
+        }
+    }
+    ssb += __shfl_xor(ssb, 16, 64);
+    ssb += __shfl_xor(ssb, 32, 64);
+    if constexpr (WANT_C) {
+        ssc += __shfl_xor(ssc, 16, 64);
+        ssc += __shfl_xor(ssc, 32, 64);
+    }
+    // norm factors; rows past the block end are zero
+    const float rsb = rv ? (c.bcnorm ? __builtin_amdgcn_rsqf(fmaf(ssb, c.invN, c.eps)) : 1.f) : 0.f;
+    const float rsc = rv ? (c.bcnorm ? __builtin_amdgcn_rsqf(fmaf(ssc, c.invN, c.eps)) : 1.f) : 0.f;
+    const float wt = sm.w[tok];  // zero past the block end
+    // angle offsets of the earlier 16-row tiles (SISO path)
+    f32x4_t phoff[KS];
+    if constexpr (Cfg::VEC) {
+        const float *tt = (const float *)sm.phi;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w2 = 0; w2 < 3; ++w2) {
+                const f32x4_t t4 = *(const f32x4_t *)(tt + w2 * (Cfg::NP / 2) + kk * 16 + 4 * gq);
+                if (w2 < wave) o += t4;
+            }
+            phoff[kk] = o;
+        }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        float vb[8], vc[8];
+        raw8<Cfg>(rb.b[kk], vb);
+        if constexpr (WANT_C) raw8<Cfg>(rb.c[kk], vc);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            vb[j] *= rsb;
+            if constexpr (WANT_C) vc[j] *= rsc;
+        }
+        if (c.affine && rv) {
+            // gains (with the norm) and per-(head, rank) biases
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int n = kk * 32 + 8 * gq + j;
+                if (n < N) {
+                    if (c.bcnorm && p.bnw) vb[j] *= p.bnw[n];
+                    if (p.bbias) vb[j] += p.bbias[((int64_t)c.h * R + r) * N + n];
+                    if constexpr (WANT_C) {
+                        if (c.bcnorm && p.cnw) vc[j] *= p.cnw[n];
+                        if (p.cbias) vc[j] += p.cbias[((int64_t)c.h * R + r) * N + n];
+                    }
+                }
+            }
+        }
+        float ob[8], oc[8];
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+            const int n = kk * 32 + 8 * gq + 2 * jp;
+            float ang;
+            if constexpr (Cfg::VEC) ang = rb.th[kk * 4 + jp] + phoff[kk][jp];
+            else ang = (rv && n < N) ? ((const float *)sm.phi)[tok * Cfg::PHP + n / 2] : 0.f;
+            float sn, cn;
+            fast_sincos(ang, sn, cn);
+            const float u = vb[2 * jp], v = vb[2 * jp + 1];
+            ob[2 * jp] = u * cn - v * sn;
+            ob[2 * jp + 1] = u * sn + v * cn;
+            if constexpr (WANT_C) {
+                const float uc = vc[2 * jp], vcc = vc[2 * jp + 1];
+                oc[2 * jp] = uc * cn - vcc * sn;
+                oc[2 * jp + 1] = uc * sn + vcc * cn;
+            }
+        }
+        if constexpr (Cfg::BF) {
+            uint32_t wh[4], wl[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) split2(ob[2 * k] * wt, ob[2 * k + 1] * wt, wh[k], wl[k]);
+            if constexpr (WANT_C) {
+                uint32_t bh_[4], bl_[4], ch[4], cl[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    split2(ob[2 * k], ob[2 * k + 1], bh_[k], bl_[k]);
+                    split2(oc[2 * k], oc[2 * k + 1], ch[k], cl[k]);
+                }
+                const int off = row * Cfg::OPP + kk * 32 + 8 * gq;
+                uint16_t *bt = (uint16_t *)sm.bt;
+                *(u32x4_t *)(bt + off) = u32x4_t{bh_[0], bh_[1], bh_[2], bh_[3]};
+                *(u32x4_t *)(bt + Cfg::BT_PLANE + off) = u32x4_t{bl_[0], bl_[1], bl_[2], bl_[3]};
+                ct[kk].hi = u32x4_t{ch[0], ch[1], ch[2], ch[3]};
+                ct[kk].lo = u32x4_t{cl[0], cl[1], cl[2], cl[3]};
+            }
+            uint16_t *wb = (uint16_t *)sm.wb;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int n = kk * 32 + 8 * gq + 2 * k;
+                wb[n * Cfg::RPP + row] = (uint16_t)(wh[k] & 0xffffu);
+                wb[(n + 1) * Cfg::RPP + row] = (uint16_t)(wh[k] >> 16);
+                wb[Cfg::WB_PLANE + n * Cfg::RPP + row] = (uint16_t)(wl[k] & 0xffffu);
+                wb[Cfg::WB_PLANE + (n + 1) * Cfg::RPP + row] = (uint16_t)(wl[k] >> 16);
+            }
+        } else {
+            if constexpr (WANT_C) {
+                const int off = row * Cfg::OPP + kk * 32 + 8 * gq;
+                float *bt = (float *)sm.bt;
+                *(f32x4_t *)(bt + off) = f32x4_t{ob[0], ob[1], ob[2], ob[3]};
+                *(f32x4_t *)(bt + off + 4) = f32x4_t{ob[4], ob[5], ob[6], ob[7]};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ct[kk].v[j] = oc[j];
+            }
+            float *wb = (float *)sm.wb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) wb[(kk * 32 + 8 * gq + j) * Cfg::RPP + row] = ob[j] * wt;
+        }
+    }
+}
+
+// Carried B~ of the call's last token: read back from the B~ plane of the last
+// block and rotated from the block frame to the global frame (block base angle).
+template <class Cfg, class Sm>
+__device__ __forceinline__ void write_final_prev_b(const Sm &sm, const ScanParams &p, const WgCtx &c,
+                                                   const BlockGeo &g) {
+    const int N = p.N, N2 = p.N / 2, R = c.R;
+    const int lrow0 = (g.Tv - 1) * R;
+    for (int e = threadIdx.x; e < N2 * R; e += 256) {
+        const int i = e / R, r = e - i * R, n = 2 * i;
+        const int off = (lrow0 + r) * Cfg::OPP + n;
+        float u, v;
+        if constexpr (Cfg::BF) {
+            const uint16_t *bt = (const uint16_t *)sm.bt;
+            u = bf2f(bt[off]) + bf2f(bt[Cfg::BT_PLANE + off]);
+            v = bf2f(bt[off + 1]) + bf2f(bt[Cfg::BT_PLANE + off + 1]);
+        } else {
+            u = ((const float *)sm.bt)[off];
+            v = ((const float *)sm.bt)[off + 1];
+        }
+        float sn, cn;
+        fast_sincos((float)wrap_2pi(sm.base[i]), sn, cn);
+        p.pB1[(c.bh * N + n) * R + r] = u * cn - v * sn;
+        p.pB1[(c.bh * N + n + 1) * R + r] = u * sn + v * cn;
+    }
+}
+
+// State tiles of this wave: tile e = wave + 4m -> (nt = e / PT, pt = e % PT);
+// fragment slot i of lane l holds element (n = nt*16 + 4(l/16) + i, p = pt*16 + l%16).
+template <class Cfg>
+__device__ __forceinline__ bool state_tile(int m, int &nt, int &pt) {
+    const int e = (threadIdx.x >> 6) + 4 * m;
+    nt = e / Cfg::PT;
+    pt = e - nt * Cfg::PT;
+    return e < Cfg::PT * Cfg::NT;
+}
+
+// acc += (w B~)^T X for this wave's state tiles
+template <class Cfg, class Sm>
+__device__ __forceinline__ void mfma_state(const Sm &sm, f32x4_t (&acc)[Cfg::TPW]) {
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < Cfg::TPW; ++m) {
+        int nt, pt;
+        if (!state_tile<Cfg>(m, nt, pt)) continue;
+#pragma unroll
+        for (int kk = 0; kk < Cfg::ROWS / 32; ++kk) {
+            const int wo = (nt * 16 + l16) * Cfg::RPP + kk * 32 + 8 * gq;
+            const int xo = (pt * 16 + l16) * Cfg::RPP + kk * 32 + 8 * gq;
+            if constexpr (Cfg::BF) {
+                FragHL wf;
+                wf.hi = *(const u32x4_t *)((const uint16_t *)sm.wb + wo);
+                wf.lo = *(const u32x4_t *)((const uint16_t *)sm.wb + Cfg::WB_PLANE + wo);
+                const u32x4_t xb = *(const u32x4_t *)((const uint16_t *)sm.xt + xo);
+                acc[m] = mma(wf, xb, acc[m]);
+            } else {
+                FragF wf, xb;
+                const float *wp = (const float *)sm.wb + wo, *xp = (const float *)sm.xt + xo;
+                const f32x4_t w0 = *(const f32x4_t *)wp, w1 = *(const f32x4_t *)(wp + 4);
+                const f32x4_t x0 = *(const f32x4_t *)xp, x1 = *(const f32x4_t *)(xp + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    wf.v[j] = w0[j]; wf.v[j + 4] = w1[j];
+                    xb.v[j] = x0[j]; xb.v[j + 4] = x1[j];
+                }
+                acc[m] = mma(wf, xb, acc[m]);
+            }
+        }
+    }
+}
+
+// rotate the pairs (slot 0, 1) and (slot 2, 3) of a state fragment by -angle (cos c, sin s)
+__device__ __forceinline__ void rot_neg(f32x4_t &v, float c0, float s0, float c1, float s1) {
+    const float u0 = v[0], v0 = v[1], u1 = v[2], v1 = v[3];
+    v[0] = u0 * c0 + v0 * s0;
+    v[1] = -u0 * s0 + v0 * c0;
+    v[2] = u1 * c1 + v1 * s1;
+    v[3] = -u1 * s1 + v1 * c1;
+}
+
+// Carry update:  H <- Rot(-Phi) (decay H + S), with the matrix cores adding S
+// into the decayed state in place.
+template <class Cfg, class Sm>
+__device__ __forceinline__ void carry_block(const Sm &sm, f32x4_t (&hs)[Cfg::TPW], float decay, int N2) {
+    const int gq = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int m = 0; m < Cfg::TPW; ++m) hs[m] *= decay;
+    mfma_state<Cfg>(sm, hs);
+#pragma unroll
+    for (int m = 0; m < Cfg::TPW; ++m) {
+        int nt, pt;
+        if (!state_tile<Cfg>(m, nt, pt)) continue;
+        const int pr = (nt * 16 + 4 * gq) >> 1;  // pairs pr, pr + 1
+        // padded pairs (n >= N) carry zeros; their angle entries are never written
+        const float c0 = pr < N2 ? sm.cph[pr] : 1.f, s0 = pr < N2 ? sm.sph[pr] : 0.f;
+        const float c1 = pr + 1 < N2 ? sm.cph[pr + 1] : 1.f, s1 = pr + 1 < N2 ? sm.sph[pr + 1] : 0.f;
+        rot_neg(hs[m], c0, s0, c1, s1);
+    }
+}
+
+// H fragments -> H^T [p][n] planes in LDS (hi/lo or fp32); 4 consecutive n per lane
+template <class Cfg, class Sm>
+__device__ __forceinline__ void write_ht(const Sm &sm, const f32x4_t (&hs)[Cfg::TPW]) {
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < Cfg::TPW; ++m) {
+        int nt, pt;
+        if (!state_tile<Cfg>(m, nt, pt)) continue;
+        const int off = (pt * 16 + l16) * Cfg::OPP + nt * 16 + 4 * gq;
+        if constexpr (Cfg::BF) {
+            uint32_t h0, l0, h1, l1;
+            split2(hs[m][0], hs[m][1], h0, l0);
+            split2(hs[m][2], hs[m][3], h1, l1);
+            *(u32x2_t *)((uint16_t *)sm.ht + off) = u32x2_t{h0, h1};
+            *(u32x2_t *)((uint16_t *)sm.ht + Cfg::HT_PLANE + off) = u32x2_t{l0, l1};
+        } else {
+            *(f32x4_t *)((float *)sm.ht + off) = hs[m];
+        }
+    }
+}
+
+// workgroup -> (sequence, column group, segment); the segments of one
+// (sequence, column group) share an XCD when the count allows it
+__device__ __forceinline__ void wg_map(int64_t nbh, int ncg, int nsegk, int64_t &bh, int &cg, int &seg) {
+    const int64_t bid = blockIdx.x;
+    const int64_t nq = nbh * ncg;
+    int64_t q;
+    if ((nq & 7) == 0) {
+        const int64_t xcd = bid & 7, k = bid >> 3;
+        q = xcd + 8 * (k / nsegk);
+        seg = (int)(k % nsegk);
+    } else {
+        q = bid / nsegk;
+        seg = (int)(bid % nsegk);
+    }
+    bh = q / ncg;
+    cg = (int)(q - bh * ncg);
+}
+
+template <class Cfg>
+__device__ __forceinline__ WgCtx make_ctx(const ScanParams &p, int nsegk) {
+    WgCtx c;
+    wg_map(p.B * p.H, p.ncg, nsegk, c.bh, c.cg, c.seg);
+    c.b = c.bh / p.H;
+    c.h = (int)(c.bh - c.b * p.H);
+    c.p0 = c.cg * Cfg::PP;
+    c.Pw = min(Cfg::PP, p.P - c.p0);
+    c.blk0 = c.seg * p.bps;
+    c.blk1 = min(p.nblk, c.blk0 + p.bps);
+    c.R = Cfg::VEC ? 1 : p.R;
+    c.invR = 1.f / (float)c.R;
+    using ET = typename Cfg::ET;
+    const int64_t tok0 = c.b * p.T * p.H + c.h;  // (b, token 0, h)
+    c.sx = p.H * p.P * c.R;
+    c.sbc = p.H * p.N * c.R;
+    c.sth = p.H * (p.N / 2);
+    c.sdt = p.H;
+    c.xb = (const ET *)p.x + tok0 * p.P * c.R + (int64_t)c.p0 * c.R;
+    c.Bb = (const ET *)p.Bm + tok0 * p.N * c.R;
+    c.Cb = (const ET *)p.Cm + tok0 * p.N * c.R;
+    c.thb = p.theta + tok0 * (p.N / 2);
+    c.dtb = p.dt + tok0;
+    c.lamb = p.lam + tok0;
+    c.yb = (ET *)p.y + tok0 * p.P * c.R + (int64_t)c.p0 * c.R;
+    c.invN = 1.f / (float)p.N;
+    c.eps = p.eps;
+    c.bcnorm = (p.flags & 1u) != 0;
+    c.affine = (c.bcnorm && (p.bnw || p.cnw)) || p.bbias || p.cbias;
+    return c;
+}
+
+// ============================================================ state kernel
+template <class Io, int NP, int PP, bool VEC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) void seg_state_kernel(ScanParams p) {
+    using Cfg = SegCfg<Io, NP, PP, VEC>;
+    using Frag = typename std::conditional<Cfg::BF, FragHL, FragF>::type;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const Smem<Cfg, false> sm(smem);
+    const WgCtx c = make_ctx<Cfg>(p, p.nseg - 1);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int l16 = lane & 15, gq = lane >> 4;
+    const int N2 = p.N / 2;
+
+    f32x4_t sagg[Cfg::TPW];
+#pragma unroll
+    for (int m = 0; m < Cfg::TPW; ++m) sagg[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (tid < N2) sm.base[tid] = 0.0;
+    float lsum = 0.f;
+    Frag ct_unused[Cfg::KS];
+
+    RawBlock<Cfg, false> rb;
+    BlockGeo g = block_geo(p, c.blk0);
+    load_block<Io>(rb, p, c, g);
+    for (int blk = c.blk0; blk < c.blk1; ++blk) {
+        lds_barrier();  // previous block's readers of the LDS planes are done
+        stage_scalars_x<Io>(rb, sm, p, c, g);
+        if constexpr (!VEC) stage_angles_table<Cfg>(sm, p, g);
+        block_angle_totals<Cfg>(sm, p, g);
+        stage_prologue<Io>(rb, sm, p, c, g, ct_unused);
+        const BlockGeo gn = block_geo(p, blk + 1);
+        if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
+        lds_barrier();
+        const float cs_end = sm.cs[Cfg::ROWS - 1];
+        carry_block<Cfg>(sm, sagg, __expf(cs_end), N2);
+        lsum += cs_end;
+        if (tid < N2) sm.base[tid] += (double)sm.pend[tid];
+        g = gn;
+    }
+    // segment aggregate -> workspace [n][p]
+    const int64_t bs = c.bh * p.nseg + c.seg;
+    float *Sg = p.Sagg + bs * (int64_t)p.P * p.N;
+#pragma unroll
+    for (int m = 0; m < Cfg::TPW; ++m) {
+        int nt, pt;
+        if (!state_tile<Cfg>(m, nt, pt)) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int nn = nt * 16 + 4 * gq + i, pp = pt * 16 + l16;
+            if (pp < c.Pw && nn < p.N) Sg[(int64_t)nn * p.P + c.p0 + pp] = sagg[m][i];
+        }
+    }
+    if (c.cg != 0) return;  // the segment's decay and angle are the same for every column group
+    if (tid == 0) p.lseg[bs] = lsum;
+    lds_barrier();
+    if (tid < N2) {
+        const double a = wrap_2pi(sm.base[tid]);
+        float s, cc;
+        { const f32x2_t sc_ = sincos_acc((float)a); s = sc_[0]; cc = sc_[1]; }
+        p.pseg[bs * N2 + tid] = (float)a;
+        p.cseg[bs * N2 + tid] = cc;
+        p.sseg[bs * N2 + tid] = s;
+    }
+}
+
+// ============================================================ output kernel
+template <class Io, int NP, int PP, bool VEC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg_output_kernel(ScanParams p) {
+    using Cfg = SegCfg<Io, NP, PP, VEC>;
+    using ET = typename Io::T;
+    using Frag = typename std::conditional<Cfg::BF, FragHL, FragF>::type;
+    constexpr int KS = Cfg::KS, PT = Cfg::PT, TPW = Cfg::TPW;
+    constexpr int OPP = Cfg::OPP, RPP = Cfg::RPP;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const Smem<Cfg, true> sm(smem);
+    const WgCtx c = make_ctx<Cfg>(p, p.nseg);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, gq = lane >> 4;
+    const int N = p.N, P = p.P, N2 = N / 2;
+    const int R = VEC ? 1 : c.R;
+    const int64_t bh = c.bh;
+    const bool want_final = (c.seg == p.nseg - 1) && (p.h1 != nullptr);
+
+    // prefetch the first block while the incoming state is assembled
+    RawBlock<Cfg, true> rb;
+    BlockGeo g = block_geo(p, c.blk0);
+    load_block<Io>(rb, p, c, g);
+
+    // ---- incoming state H (this wave's state fragments) and the base angle per pair
+    f32x4_t hs[TPW];
+    {
+        const int64_t g0 = (c.b * p.T) * p.H + c.h;  // token 0 of the call
+        const float eta0 = (p.pB0 && p.px0) ? p.dt[g0] * (1.f - p.lam[g0]) : 0.f;
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            hs[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            int nt, pt;
+            if (!state_tile<Cfg>(m, nt, pt)) continue;
+            const int pp = pt * 16 + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int nn = nt * 16 + 4 * gq + i;
+                float v = 0.f;
+                if (pp < c.Pw && nn < N) {
+                    if (p.h0) v = p.h0[(bh * N + nn) * P + c.p0 + pp];
+                    if (p.pB0 && p.px0) {
+                        float acc = 0.f;
+                        for (int r = 0; r < R; ++r)
+                            acc += p.pB0[(bh * N + nn) * R + r] * p.px0[(bh * P + c.p0 + pp) * R + r];
+                        v += eta0 * acc;
+                    }
+                }
+                hs[m][i] = v;
+            }
+            if (p.ang0) {
+                // rotate by -Theta_init
+                const int pr = (nt * 16 + 4 * gq) >> 1;
+                float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
+                if (pr < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr])); s0 = sc_[0]; c0 = sc_[1]; }
+                if (pr + 1 < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
+                rot_neg(hs[m], c0, s0, c1, s1);
+            }
+        }
+        // fold the earlier segments: H <- Rot(-Phi_s) (exp(l_s) H) + S_s
+        for (int s2 = 0; s2 < c.seg; ++s2) {
+            const int64_t bs = bh * p.nseg + s2;
+            const float dec = __expf(p.lseg[bs]);
+            const float *Sg = p.Sagg + bs * (int64_t)P * N;
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+                int nt, pt;
+                if (!state_tile<Cfg>(m, nt, pt)) continue;
+                const int pp = pt * 16 + l16;
+                const int pr = (nt * 16 + 4 * gq) >> 1;
+                const float c0 = pr < N2 ? p.cseg[bs * N2 + pr] : 1.f, s0 = pr < N2 ? p.sseg[bs * N2 + pr] : 0.f;
+                const float c1 = pr + 1 < N2 ? p.cseg[bs * N2 + pr + 1] : 1.f;
+                const float s1 = pr + 1 < N2 ? p.sseg[bs * N2 + pr + 1] : 0.f;
+                f32x4_t a = dec * hs[m];
+                rot_neg(a, c0, s0, c1, s1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int nn = nt * 16 + 4 * gq + i;
+                    // the aggregate is already in the segment's end frame
+                    if (pp < c.Pw && nn < N) a[i] += Sg[(int64_t)nn * P + c.p0 + pp];
+                }
+                hs[m] = a;
+            }
+        }
+        if (tid < N2) {
+            double a = p.ang0 ? (double)p.ang0[bh * N2 + tid] : 0.0;
+            for (int s2 = 0; s2 < c.seg; ++s2) a += (double)p.pseg[(bh * p.nseg + s2) * N2 + tid];
+            sm.base[tid] = a;
+        }
+        write_ht<Cfg>(sm, hs);
+    }
+
+    Frag ct[KS];
+    for (int blk = c.blk0; blk < c.blk1; ++blk) {
+        lds_barrier();  // previous block's LDS readers are done; H^T written
+        stage_scalars_x<Io>(rb, sm, p, c, g);
+        if constexpr (!VEC) stage_angles_table<Cfg>(sm, p, g);
+        block_angle_totals<Cfg>(sm, p, g);
+        const bool last_blk = want_final && (blk == p.nblk - 1);
+        stage_prologue<Io>(rb, sm, p, c, g, ct);
+        const BlockGeo gn = block_geo(p, blk + 1);
+        if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
+        lds_barrier();
+        if (last_blk && c.cg == 0) write_final_prev_b<Cfg>(sm, p, c, g);
+
+        // ---- outputs for this wave's 16 rows
+        const int tt = wave;
+        const int row0 = tt * 16 + 4 * gq;  // result rows row0 .. row0 + 3 of this lane
+        f32x4_t yacc[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) yacc[pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // Y_inter = C~ H first, then scaled by exp(cs_t) per row; Y_intra accumulates on top
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const int ho = (pt * 16 + l16) * OPP + kk * 32 + 8 * gq;
+                if constexpr (Cfg::BF) {
+                    FragHL hf;
+                    hf.hi = *(const u32x4_t *)((const uint16_t *)sm.ht + ho);
+                    hf.lo = *(const u32x4_t *)((const uint16_t *)sm.ht + Cfg::HT_PLANE + ho);
+                    yacc[pt] = mma(ct[kk], hf, yacc[pt]);
+                } else {
+                    FragF hf;
+                    const f32x4_t v0 = *(const f32x4_t *)((const float *)sm.ht + ho);
+                    const f32x4_t v1 = *(const f32x4_t *)((const float *)sm.ht + ho + 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { hf.v[j] = v0[j]; hf.v[j + 4] = v1[j]; }
+                    yacc[pt] = mma(ct[kk], hf, yacc[pt]);
+                }
+            }
+        }
+        {
+            f32x4_t ecs4;
+            if constexpr (VEC) {
+                ecs4 = *(const f32x4_t *)(sm.ecs + row0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ecs4[i] = sm.ecs[tok_of(row0 + i, c)];
+            }
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) yacc[pt] *= ecs4;
+        }
+        const int trow = tt * 16 + l16;  // this lane's t-row in the G^T fragments
+        const int ttok = VEC ? trow : tok_of(trow, c);
+        const float cs_t = sm.cs[ttok], g_t = sm.gam[ttok];
+        int smax = tt;
+        if constexpr (!VEC) {
+            // with R not dividing 16 the rows of the tile's last token may spill into the next tile
+            smax = ((tok_of(tt * 16 + 15, c)) * R + R - 1) >> 4;
+            if (smax > Cfg::ROWS / 16 - 1) smax = Cfg::ROWS / 16 - 1;
+        }
+        for (int sp = 0; sp <= smax / 2; ++sp) {
+            const int st0 = 2 * sp, st1 = 2 * sp + 1;
+            const bool has1 = st1 <= smax;
+            f32x4_t g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const int o0 = (st0 * 16 + l16) * OPP + kk * 32 + 8 * gq;
+                const int o1 = (st1 * 16 + l16) * OPP + kk * 32 + 8 * gq;
+                if constexpr (Cfg::BF) {
+                    const uint16_t *bt = (const uint16_t *)sm.bt;
+                    FragHL a0;
+                    a0.hi = *(const u32x4_t *)(bt + o0);
+                    a0.lo = *(const u32x4_t *)(bt + Cfg::BT_PLANE + o0);
+                    g0 = mma(a0, ct[kk], g0);
+                    if (has1) {
+                        FragHL a1;
+                        a1.hi = *(const u32x4_t *)(bt + o1);
+                        a1.lo = *(const u32x4_t *)(bt + Cfg::BT_PLANE + o1);
+                        g1 = mma(a1, ct[kk], g1);
+                    }
+                } else {
+                    const float *bt = (const float *)sm.bt;
+                    FragF a0;
+                    const f32x4_t u0 = *(const f32x4_t *)(bt + o0), u1 = *(const f32x4_t *)(bt + o0 + 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { a0.v[j] = u0[j]; a0.v[j + 4] = u1[j]; }
+                    g0 = mma(a0, ct[kk], g0);
+                    if (has1) {
+                        FragF a1;
+                        const f32x4_t v0 = *(const f32x4_t *)(bt + o1), v1 = *(const f32x4_t *)(bt + o1 + 4);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) { a1.v[j] = v0[j]; a1.v[j + 4] = v1[j]; }
+                        g1 = mma(a1, ct[kk], g1);
+                    }
+                }
+            }
+            // mask: slot i of g0 is G[t = trow][s = st0*16 + 4g + i]
+            float mv[8];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int sb = (half ? st1 : st0) * 16 + 4 * gq;
+                const f32x4_t gv = half ? g1 : g0;
+                if (half && !has1) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mv[4 + i] = 0.f;
+                    continue;
+                }
+                if constexpr (VEC) {
+                    const f32x4_t css = *(const f32x4_t *)(sm.cs + sb);
+                    const f32x4_t scs = *(const f32x4_t *)(sm.scale + sb);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int s = sb + i;
+                        const float L = s < trow ? __expf(cs_t - css[i]) * scs[i] : (s == trow ? g_t : 0.f);
+                        mv[half * 4 + i] = gv[i] * L;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int stok = tok_of(sb + i, c);
+                        const float L = stok < ttok ? __expf(cs_t - sm.cs[stok]) * sm.scale[stok]
+                                                    : (stok == ttok ? g_t : 0.f);
+                        mv[half * 4 + i] = gv[i] * L;
+                    }
+                }
+            }
+            Frag mf;
+            if constexpr (Cfg::BF) mf = make_hl(mv);
+            else mf = make_f(mv);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const int xo0 = (pt * 16 + l16) * RPP + st0 * 16 + 4 * gq;
+                const int xo1 = (pt * 16 + l16) * RPP + st1 * 16 + 4 * gq;
+                if constexpr (Cfg::BF) {
+                    const u32x2_t x0 = *(const u32x2_t *)((const uint16_t *)sm.xt + xo0);
+                    u32x2_t x1 = {0u, 0u};
+                    if (has1) x1 = *(const u32x2_t *)((const uint16_t *)sm.xt + xo1);
+                    const u32x4_t xb = {x0[0], x0[1], x1[0], x1[1]};
+                    yacc[pt] = mma(mf, xb, yacc[pt]);
+                } else {
+                    FragF xb;
+                    const f32x4_t x0 = *(const f32x4_t *)((const float *)sm.xt + xo0);
+                    f32x4_t x1 = {0.f, 0.f, 0.f, 0.f};
+                    if (has1) x1 = *(const f32x4_t *)((const float *)sm.xt + xo1);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { xb.v[j] = x0[j]; xb.v[j + 4] = x1[j]; }
+                    yacc[pt] = mma(mf, xb, yacc[pt]);
+                }
+            }
+        }
+
+        // ---- epilogue: y = exp(cs_t) Y_inter + Y_intra + D x  -> staging (own rows)
+        {
+            ET *ys = (ET *)sm.ys;
+            const float Dh = p.D[c.h];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const int pc = pt * 16 + l16;
+                float xv[4];
+                if constexpr (Cfg::BF) {
+                    const u32x2_t x2 = *(const u32x2_t *)((const uint16_t *)sm.xt + pc * RPP + row0);
+                    xv[0] = __uint_as_float(x2[0] << 16);
+                    xv[1] = __uint_as_float(x2[0] & 0xffff0000u);
+                    xv[2] = __uint_as_float(x2[1] << 16);
+                    xv[3] = __uint_as_float(x2[1] & 0xffff0000u);
+                } else {
+                    const f32x4_t x4 = *(const f32x4_t *)((const float *)sm.xt + pc * RPP + row0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xv[i] = x4[i];
+                }
+                float yv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) yv[i] = yacc[pt][i] + Dh * xv[i];
+                if constexpr (Cfg::BF) {
+                    const uint32_t w01 = pack_bf16(yv[0], yv[1]), w23 = pack_bf16(yv[2], yv[3]);
+                    ys[(row0 + 0) * PP + pc] = (uint16_t)(w01 & 0xffffu);
+                    ys[(row0 + 1) * PP + pc] = (uint16_t)(w01 >> 16);
+                    ys[(row0 + 2) * PP + pc] = (uint16_t)(w23 & 0xffffu);
+                    ys[(row0 + 3) * PP + pc] = (uint16_t)(w23 >> 16);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ys[(row0 + i) * PP + pc] = yv[i];
+                }
+            }
+        }
+        const float cs_end = sm.cs[Cfg::ROWS - 1];
+        lds_barrier();  // staging complete; all waves done reading H^T and the planes
+        {
+            const ET *ys = (const ET *)sm.ys;
+            const int Rv = g.Tv * R;
+            if constexpr (VEC) {
+#pragma unroll
+                for (int m = 0; m < Cfg::ROWS * PP / Cfg::XW / 256; ++m) {
+                    const int e = tid + 256 * m;
+                    const int yr = e / (PP / Cfg::XW), pc = (e % (PP / Cfg::XW)) * Cfg::XW;
+                    if (yr < Rv && pc < c.Pw)
+                        *(u32x4_t *)((ET *)c.yb + (g.t0 + yr) * c.sx + pc) = *(const u32x4_t *)(ys + yr * PP + pc);
+                }
+            } else {
+                for (int e = tid; e < Rv * PP; e += 256) {
+                    const int yr = e / PP, pc = e - yr * PP;
+                    if (pc >= c.Pw) continue;
+                    const int tok = tok_of(yr, c), r = yr - tok * R;
+                    ((ET *)c.yb)[(g.t0 + tok) * c.sx + (int64_t)pc * R + r] = ys[yr * PP + pc];
+                }
+            }
+        }
+        // ---- carry to the next block
+        carry_block<Cfg>(sm, hs, __expf(cs_end), N2);
+        write_ht<Cfg>(sm, hs);
+        if (last_blk) {
+            // carried x of the last token
+            const int lrow0 = (g.Tv - 1) * R;
+            for (int e = tid; e < c.Pw * R; e += 256) {
+                const int pc = e / R, r = e - pc * R;
+                float xv;
+                if constexpr (Cfg::BF) xv = bf2f(((const uint16_t *)sm.xt)[pc * RPP + lrow0 + r]);
+                else xv = ((const float *)sm.xt)[pc * RPP + lrow0 + r];
+                p.px1[(bh * P + c.p0 + pc) * R + r] = xv;
+            }
+        }
+        if (tid < N2) sm.base[tid] += (double)sm.pend[tid];
+        g = gn;
+    }
+    if (want_final) {
+        lds_barrier();  // final base angles visible
+        // final state in the global frame: Rot(Theta_final) H
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            int nt, pt;
+            if (!state_tile<Cfg>(m, nt, pt)) continue;
+            const int pp = pt * 16 + l16;
+            const int pr = (nt * 16 + 4 * gq) >> 1;
+            float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
+            if (pr < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi(sm.base[pr])); s0 = sc_[0]; c0 = sc_[1]; }
+            if (pr + 1 < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi(sm.base[pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
+            f32x4_t a = hs[m];
+            rot_neg(a, c0, -s0, c1, -s1);  // rotation by +Theta
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int nn = nt * 16 + 4 * gq + i;
+                if (pp < c.Pw && nn < N) p.h1[(bh * N + nn) * P + c.p0 + pp] = a[i];
+            }
+        }
+        if (c.cg == 0 && tid < N2) p.ang1[bh * N2 + tid] = (float)wrap_2pi(sm.base[tid]);
+    }
+}
+
+// ---------------------------------------------------------------- launch helpers
+template <class K>
+static hipError_t set_lds(K kern, size_t bytes) {
+    if (bytes > 65536)
+        return hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    return hipSuccess;
+}
+
+template <class Io, int NP, int PP, bool VEC>
+static hipError_t launch_seg_t(bool output, const ScanParams &p, hipStream_t st) {
+    using Cfg = SegCfg<Io, NP, PP, VEC>;
+    if (output) {
+        auto kern = seg_output_kernel<Io, NP, PP, VEC>;
+        hipError_t e = set_lds(kern, Cfg::OUTPUT_BYTES);
+        if (e != hipSuccess) return e;
+        const int64_t nwg = p.B * p.H * (int64_t)p.ncg * p.nseg;
+        hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), Cfg::OUTPUT_BYTES, st, p);
+    } else {
+        auto kern = seg_state_kernel<Io, NP, PP, VEC>;
+        hipError_t e = set_lds(kern, Cfg::STATE_BYTES);
+        if (e != hipSuccess) return e;
+        const int64_t nwg = p.B * p.H * (int64_t)p.ncg * (p.nseg - 1);
+        if (nwg <= 0) return hipSuccess;
+        hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), Cfg::STATE_BYTES, st, p);
+    }
+    return hipGetLastError();
+}
+
+#define M3_SHAPES(X, Io, VEC) \
+    X(Io, 32, 32, VEC) X(Io, 32, 64, VEC) X(Io, 64, 32, VEC) X(Io, 64, 64, VEC) X(Io, 128, 32, VEC) X(Io, 128, 64, VEC)
+
+// Instantiate the launcher and LDS query of one (io type, load path) pair.
+#define M3_DEFINE_VARIANT(NAME, Io, VEC)                                                               \
+    hipError_t NAME##_launch(bool output, const TileShape &ts, const ScanParams &p, hipStream_t st) {  \
+        M3_SHAPES(M3_LAUNCH_CASE, Io, VEC)                                                            \
+        return hipErrorInvalidValue;                                                                  \
+    }                                                                                                 \
+    size_t NAME##_bytes(bool output, const TileShape &ts) {                                           \
+        M3_SHAPES(M3_BYTES_CASE, Io, VEC)                                                             \
+        return 0;                                                                                     \
+    }
+#define M3_LAUNCH_CASE(IoT, NPV, PPV, V) \
+    if (ts.np == NPV && ts.pp == PPV) return launch_seg_t<IoT, NPV, PPV, V>(output, p, st);
+#define M3_BYTES_CASE(IoT, NPV, PPV, V)                                                                 \
+    if (ts.np == NPV && ts.pp == PPV)                                                                   \
+        return output ? SegCfg<IoT, NPV, PPV, V>::OUTPUT_BYTES : SegCfg<IoT, NPV, PPV, V>::STATE_BYTES;
+
+}  // namespace m3

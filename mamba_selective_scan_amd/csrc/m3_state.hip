@@ -1,99 +1,10 @@
-// m3_state.hip -- the sequential pass over chunk states, the empty-call state
-// copy, and the single-token decode step.
+// m3_state.hip -- the empty-call state copy and the single-token decode step.
 #include <type_traits>
 
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
 
 namespace m3 {
-
-// ---------------------------------------------------------------- state pass
-// One thread per (batch, head, p, rotation pair i), pairs fastest.  Walks the
-// chunks in order:
-//     H_0     = Rot(-Theta_init) (h_init + eta_{-1} sum_r prev_B[:, r] prev_x[:, r]^T),
-//               eta_{-1} = dt_0 (1 - lambda_0)   (the deferred boundary term of the
-//               previous call; dotLLM PR #136, "Mamba-3 streaming decode")
-//     H_{c+1} = Rot(-Phi_c) (decay_c H_c + S_c)
-// and overwrites S_c with H_c (the state entering chunk c, in chunk c's frame).
-// The final state is Rot(Theta_final) H_C with Theta_final = Theta_init + sum_c Phi_c
-// (accumulated in double, reduced to [0, 2 pi)).
-__global__ __launch_bounds__(256) void state_pass_kernel(ScanParams p) {
-    const int N2 = p.N / 2, P = p.P, R = p.R, N = p.N;
-    const int64_t per_bh = (int64_t)P * N2;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t bh = gid / per_bh;
-    if (bh >= p.B * p.H) return;
-    const int64_t rem = gid - bh * per_bh;
-    const int pp = (int)(rem / N2), i = (int)(rem - (int64_t)pp * N2);
-    const int64_t b = bh / p.H;
-    const int h = (int)(bh - b * p.H);
-    const int C = p.nchunks;
-
-    float u = 0.f, v = 0.f;  // (H[pp][2i], H[pp][2i+1])
-    double th = 0.0;
-    if (p.h0) {
-        u = p.h0[(bh * N + 2 * i) * P + pp];
-        v = p.h0[(bh * N + 2 * i + 1) * P + pp];
-    }
-    if (p.pB0 && p.px0) {
-        const int64_t g0 = (b * p.T) * p.H + h;  // token 0
-        const float eta = p.dt[g0] * (1.f - p.lam[g0]);
-        float su = 0.f, sv = 0.f;
-        for (int r = 0; r < R; ++r) {
-            const float xr = p.px0[(bh * P + pp) * R + r];
-            su += p.pB0[(bh * N + 2 * i) * R + r] * xr;
-            sv += p.pB0[(bh * N + 2 * i + 1) * R + r] * xr;
-        }
-        u += eta * su;
-        v += eta * sv;
-    }
-    if (p.ang0) {
-        th = (double)p.ang0[bh * N2 + i];
-        float sn, cn;
-        sincosf((float)wrap_2pi(th), &sn, &cn);
-        const float nu = u * cn + v * sn, nv = -u * sn + v * cn;
-        u = nu;
-        v = nv;
-    }
-    float *Sb = p.S + bh * (int64_t)C * P * N + (int64_t)pp * N + 2 * i;
-    const int64_t sstride = (int64_t)P * N;
-    const float *dec = p.decay + bh * C;
-    const int64_t ab = bh * (int64_t)C * N2 + i;
-    // software pipeline: prefetch the next chunk's inputs
-    f32x2_t s_nx = *(const f32x2_t *)Sb;
-    float d_nx = dec[0], c_nx = p.cphi[ab], sn_nx = p.sphi[ab], ph_nx = p.phi[ab];
-    for (int c = 0; c < C; ++c) {
-        const f32x2_t s = s_nx;
-        const float d = d_nx, cp = c_nx, sp = sn_nx, ph = ph_nx;
-        if (c + 1 < C) {
-            s_nx = *(const f32x2_t *)(Sb + (c + 1) * sstride);
-            d_nx = dec[c + 1];
-            c_nx = p.cphi[ab + (int64_t)(c + 1) * N2];
-            sn_nx = p.sphi[ab + (int64_t)(c + 1) * N2];
-            ph_nx = p.phi[ab + (int64_t)(c + 1) * N2];
-        }
-        *(f32x2_t *)(Sb + c * sstride) = f32x2_t{u, v};
-        const float a0 = d * u + s[0], a1 = d * v + s[1];
-        u = a0 * cp + a1 * sp;
-        v = -a0 * sp + a1 * cp;
-        th += (double)ph;
-    }
-    const double thr = wrap_2pi(th);
-    if (p.h1) {
-        float sn, cn;
-        sincosf((float)thr, &sn, &cn);
-        p.h1[(bh * N + 2 * i) * P + pp] = u * cn - v * sn;
-        p.h1[(bh * N + 2 * i + 1) * P + pp] = u * sn + v * cn;
-    }
-    if (pp == 0) p.thfin[bh * N2 + i] = (float)thr;
-}
-
-hipError_t launch_state_pass(const ScanParams &p, hipStream_t stream) {
-    const int64_t total = p.B * p.H * (int64_t)p.P * (p.N / 2);
-    const int64_t blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(state_pass_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-    return hipGetLastError();
-}
 
 // ---------------------------------------------------------------- empty call
 // T == 0: the final state is the initial state (zeros when there is none);

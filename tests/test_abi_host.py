@@ -45,12 +45,14 @@ def test_workspace_bytes():
     m3, lib = _lib()
     s = _shape(m3)
     ws = m3.m3_scan_workspace_bytes(s)
-    # chunk states dominate: B*H*C*P*N floats
-    assert ws >= 4 * 16 * 32 * 64 * 64 * 4
-    assert ws < 4 * 16 * 32 * 64 * 64 * 4 * 1.1
+    state = 16 * 64 * 64 * 4  # one (N x P) fp32 state per head
+    # one state per (batch, head, segment); between 1 and 16 segments per sequence
+    assert 4 * state <= ws <= 4 * 16 * state * 1.1
     assert m3.m3_scan_workspace_bytes(_shape(m3, seqlen=0)) == 0
-    # the chunk size changes the number of chunk states
-    assert m3.m3_scan_workspace_bytes(_shape(m3, chunk=128)) < ws
+    assert m3.m3_scan_workspace_bytes(_shape(m3, dstate=63)) == 0
+    # a single block needs a single segment per sequence
+    one = m3.m3_scan_workspace_bytes(_shape(m3, seqlen=10))
+    assert 4 * state <= one < 4 * state * 1.1
 
 
 def _fake_inputs(m3):
