@@ -71,7 +71,7 @@ m3_status check_state(const m3_state *st, bool required) {
 // Blocks, segments and workspace of one scan.
 struct Plan {
     int TB, nblk, nseg, bps, ncg;
-    size_t Sagg, lseg, pseg, cseg, sseg, total;
+    size_t Sagg, lseg, pseg, cseg, total;
 };
 
 TileShape tile_of(const m3_shape *s) {
@@ -101,20 +101,19 @@ Plan plan_of(const m3_shape *s) {
     if (per_cu > 4) per_cu = 4;
     const int64_t target = 256LL * per_cu;
     int64_t nseg = BH > 0 ? (target + BH - 1) / BH : 1;
-    if (nseg > 16) nseg = 16;  // the output kernel folds earlier segments: cost grows as nseg^2
+    if (nseg > 16) nseg = 16;  // the output kernel folds every earlier segment's aggregate
     if (nseg > pl.nblk) nseg = pl.nblk;
     if (nseg < 1) nseg = 1;
     pl.bps = (int)((pl.nblk + nseg - 1) / nseg);
     if (pl.bps < 1) pl.bps = 1;
     pl.nseg = pl.nblk > 0 ? (pl.nblk + pl.bps - 1) / pl.bps : 1;
     const int64_t NS = (BH / pl.ncg) * pl.nseg;
-    const int64_t N2 = s->dstate / 2;
+    const int64_t np2 = ts.np / 2;
     size_t off = 0;
-    pl.Sagg = off; off = align_up(off + sizeof(float) * (size_t)(NS * s->headdim * s->dstate));
+    pl.Sagg = off; off = align_up(off + sizeof(float) * (size_t)(BH * pl.nseg * ts.np * ts.pp));
     pl.lseg = off; off = align_up(off + sizeof(float) * (size_t)NS);
-    pl.pseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * N2));
-    pl.cseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * N2));
-    pl.sseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * N2));
+    pl.pseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * np2));
+    pl.cseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * np2 * 2));
     pl.total = (pl.nblk == 0 || BH == 0) ? 0 : off;
     return pl;
 }
@@ -189,7 +188,7 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     p.lseg = reinterpret_cast<float *>(base + pl.lseg);
     p.pseg = reinterpret_cast<float *>(base + pl.pseg);
     p.cseg = reinterpret_cast<float *>(base + pl.cseg);
-    p.sseg = reinterpret_cast<float *>(base + pl.sseg);
+    p.np2 = ts.np / 2;
     if (p.nseg > 1 && m3::launch_seg_state(bf, ts, p, st) != hipSuccess) return M3_EHIP;
     if (m3::launch_seg_output(bf, ts, p, st) != hipSuccess) return M3_EHIP;
     return M3_OK;

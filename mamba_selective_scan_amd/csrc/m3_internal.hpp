@@ -30,11 +30,12 @@ struct ScanParams {
     const float *h0, *pB0, *px0, *ang0;  // initial (NULL = zeros)
     float *h1, *pB1, *px1, *ang1;        // final (NULL = not requested)
     // workspace: per-segment aggregates written by the state kernel
-    float *Sagg;  // [B*H][nseg][P][N]  state contributed by the segment, from zero, in its end frame
-    float *lseg;  // [B*H][nseg]        sum of dt*A over the segment
-    float *pseg;  // [B*H][nseg][N/2]   segment angle total reduced to [0, 2 pi)
-    float *cseg;  // [B*H][nseg][N/2]   cos of the segment angle total
-    float *sseg;  // [B*H][nseg][N/2]   sin of the segment angle total
+    int np2;      // pairs padded to the tile height (NP / 2): pitch of pseg and cseg
+    float *Sagg;  // [B*H*ncg][nseg][NP*PP] state contributed by the segment, from zero, in its
+                  //   end frame, stored in matrix-core fragment order (tile, lane, slot)
+    float *lseg;  // [B*H][nseg]         sum of dt*A over the segment
+    float *pseg;  // [B*H][nseg][np2]    segment angle total reduced to [0, 2 pi); padded pairs 0
+    float *cseg;  // [B*H][nseg][np2][2] (cos, sin) of the segment angle total; padded pairs (1, 0)
 };
 
 struct StepParams {

@@ -797,29 +797,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
         if (tid < N2) sm.base[tid] += (double)sm.pend[tid];
         g = gn;
     }
-    // segment aggregate -> workspace [n][p]
+    // segment aggregate -> workspace, in fragment order (one 16-byte store per tile and lane)
+    const int wave = tid >> 6;
     const int64_t bs = c.bh * p.nseg + c.seg;
-    float *Sg = p.Sagg + bs * (int64_t)p.P * p.N;
+    float *Sg = p.Sagg + ((c.bh * p.ncg + c.cg) * p.nseg + c.seg) * (int64_t)(NP * PP);
 #pragma unroll
     for (int m = 0; m < Cfg::TPW; ++m) {
         int nt, pt;
         if (!state_tile<Cfg>(m, nt, pt)) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int nn = nt * 16 + 4 * gq + i, pp = pt * 16 + l16;
-            if (pp < c.Pw && nn < p.N) Sg[(int64_t)nn * p.P + c.p0 + pp] = sagg[m][i];
-        }
+        *(f32x4_t *)(Sg + ((size_t)(wave + 4 * m) * 64 + lane) * 4) = sagg[m];
     }
     if (c.cg != 0) return;  // the segment's decay and angle are the same for every column group
     if (tid == 0) p.lseg[bs] = lsum;
     lds_barrier();
-    if (tid < N2) {
-        const double a = wrap_2pi(sm.base[tid]);
-        float s, cc;
-        { const f32x2_t sc_ = sincos_acc((float)a); s = sc_[0]; cc = sc_[1]; }
-        p.pseg[bs * N2 + tid] = (float)a;
-        p.cseg[bs * N2 + tid] = cc;
-        p.sseg[bs * N2 + tid] = s;
+    if (tid < NP / 2) {
+        const double a = tid < N2 ? wrap_2pi(sm.base[tid]) : 0.0;
+        const f32x2_t sc_ = sincos_acc((float)a);
+        p.pseg[bs * p.np2 + tid] = (float)a;
+        *(f32x2_t *)(p.cseg + (bs * p.np2 + tid) * 2) = f32x2_t{sc_[1], sc_[0]};
     }
 }
 
@@ -881,34 +876,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 rot_neg(hs[m], c0, s0, c1, s1);
             }
         }
-        // fold the earlier segments: H <- Rot(-Phi_s) (exp(l_s) H) + S_s
-        for (int s2 = 0; s2 < c.seg; ++s2) {
-            const int64_t bs = bh * p.nseg + s2;
-            const float dec = __expf(p.lseg[bs]);
-            const float *Sg = p.Sagg + bs * (int64_t)P * N;
+        // fold the earlier segments: H <- Rot(-Phi_s) (exp(l_s) H) + S_s (the aggregate is
+        // already in its segment's end frame).  FB segments at a time, so that their loads are
+        // in flight together; slots past the last segment reload it and are not applied.
+        constexpr int FB = 4;
+        const int64_t q = bh * p.ncg + c.cg;
+        for (int s0 = 0; s0 < c.seg; s0 += FB) {
+            f32x4_t sv[FB][TPW], cs[FB][TPW];
+            float lg[FB];
 #pragma unroll
-            for (int m = 0; m < TPW; ++m) {
-                int nt, pt;
-                if (!state_tile<Cfg>(m, nt, pt)) continue;
-                const int pp = pt * 16 + l16;
-                const int pr = (nt * 16 + 4 * gq) >> 1;
-                const float c0 = pr < N2 ? p.cseg[bs * N2 + pr] : 1.f, s0 = pr < N2 ? p.sseg[bs * N2 + pr] : 0.f;
-                const float c1 = pr + 1 < N2 ? p.cseg[bs * N2 + pr + 1] : 1.f;
-                const float s1 = pr + 1 < N2 ? p.sseg[bs * N2 + pr + 1] : 0.f;
-                f32x4_t a = dec * hs[m];
-                rot_neg(a, c0, s0, c1, s1);
+            for (int k = 0; k < FB; ++k) {
+                const int s2 = min(s0 + k, c.seg - 1);
+                const int64_t bs = bh * p.nseg + s2;
+                lg[k] = p.lseg[bs];
+                const float *Sg = p.Sagg + (q * p.nseg + s2) * (int64_t)(NP * PP);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int nn = nt * 16 + 4 * gq + i;
-                    // the aggregate is already in the segment's end frame
-                    if (pp < c.Pw && nn < N) a[i] += Sg[(int64_t)nn * P + c.p0 + pp];
+                for (int m = 0; m < TPW; ++m) {
+                    int nt, pt;
+                    if (!state_tile<Cfg>(m, nt, pt)) continue;
+                    sv[k][m] = *(const f32x4_t *)(Sg + ((size_t)(wave + 4 * m) * 64 + lane) * 4);
+                    // (cos, sin) of pairs nt*8 + 2*gq and the next one
+                    cs[k][m] = *(const f32x4_t *)(p.cseg + (bs * p.np2 + nt * 8 + 2 * gq) * 2);
                 }
-                hs[m] = a;
+            }
+#pragma unroll
+            for (int k = 0; k < FB; ++k) {
+                if (s0 + k >= c.seg) break;
+                const float dec = __expf(lg[k]);
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) {
+                    int nt, pt;
+                    if (!state_tile<Cfg>(m, nt, pt)) continue;
+                    f32x4_t a = dec * hs[m];
+                    rot_neg(a, cs[k][m][0], cs[k][m][1], cs[k][m][2], cs[k][m][3]);
+                    hs[m] = a + sv[k][m];
+                }
             }
         }
         if (tid < N2) {
             double a = p.ang0 ? (double)p.ang0[bh * N2 + tid] : 0.0;
-            for (int s2 = 0; s2 < c.seg; ++s2) a += (double)p.pseg[(bh * p.nseg + s2) * N2 + tid];
+            for (int s0 = 0; s0 < c.seg; s0 += FB) {
+                float v[FB];
+#pragma unroll
+                for (int k = 0; k < FB; ++k) v[k] = p.pseg[(bh * p.nseg + min(s0 + k, c.seg - 1)) * p.np2 + tid];
+#pragma unroll
+                for (int k = 0; k < FB; ++k)
+                    if (s0 + k < c.seg) a += (double)v[k];
+            }
             sm.base[tid] = a;
         }
         write_ht<Cfg>(sm, hs);
