@@ -135,6 +135,10 @@ struct SegCfg {
     // per pair: block angle total, its cos and sin; per pair (double): running angle base
     static constexpr size_t L_SC0 = al((5 * ROWS + 264 + 3 * (NP / 2)) * 4);
     static constexpr size_t L_SC = L_SC0 + (size_t)(NP / 2) * 8;
+    // The output kernel prefetches the next block's raw inputs right after the prologue
+    // when that fits the register file next to the matrix-core fragments; otherwise it
+    // issues them once the block's outputs are staged (overlapping the stores and the carry).
+    static constexpr bool EARLY_PF = VEC && NP <= 64;
     static constexpr size_t STATE_BYTES = L_WB + L_XT + L_PHI + L_SC;
     static constexpr size_t OUTPUT_BYTES = L_BT + L_WB + L_XT + L_HT + L_Y + L_PHI + L_SC;
 };
@@ -879,7 +883,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // fold the earlier segments: H <- Rot(-Phi_s) (exp(l_s) H) + S_s (the aggregate is
         // already in its segment's end frame).  FB segments at a time, so that their loads are
         // in flight together; slots past the last segment reload it and are not applied.
-        constexpr int FB = 4;
+        constexpr int FB = TPW <= 2 ? 4 : (TPW <= 4 ? 2 : 1);
         const int64_t q = bh * p.ncg + c.cg;
         for (int s0 = 0; s0 < c.seg; s0 += FB) {
             f32x4_t sv[FB][TPW], cs[FB][TPW];
@@ -937,7 +941,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const bool last_blk = want_final && (blk == p.nblk - 1);
         stage_prologue<Io>(rb, sm, p, c, g, ct);
         const BlockGeo gn = block_geo(p, blk + 1);
-        if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
+        if constexpr (Cfg::EARLY_PF) {
+            if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
+        }
         lds_barrier();
         if (last_blk && c.cg == 0) write_final_prev_b<Cfg>(sm, p, c, g);
 
@@ -1115,6 +1121,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         const float cs_end = sm.cs[Cfg::ROWS - 1];
         lds_barrier();  // staging complete; all waves done reading H^T and the planes
+        if constexpr (!Cfg::EARLY_PF) {
+            if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
+        }
         {
             const ET *ys = (const ET *)sm.ys;
             const int Rv = g.Tv * R;
