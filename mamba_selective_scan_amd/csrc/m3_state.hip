@@ -36,15 +36,42 @@ hipError_t launch_fill_state(const ScanParams &p, hipStream_t stream) {
 //     Theta <- Theta + theta;  B~, C~ = Rot(Theta)(norm(B) + bias), ...
 //     h <- alpha h + beta sum_r prevB_r prevx_r^T + gamma sum_r B~_r x_r^T
 //     y_r = h^T C~_r + D x_r;  prev_B <- B~;  prev_x <- x
-// Memory-bound: h is read once and written once with 16-byte accesses.
-template <class Io, int VEC>
+// Memory-bound: h is read once and written once with 16-byte accesses; the
+// first U rows of h per thread are requested before the prologue so that their
+// latency overlaps the norm and rotation.
+template <class Io, int VEC, int RMAX>
 __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     using ET = typename Io::T;
+    constexpr int U = 4;  // h rows in flight per thread
     const int h = blockIdx.x;
     const int64_t b = blockIdx.y;
-    const int N = p.N, P = p.P, R = p.R, N2 = N / 2;
+    const int N = p.N, P = p.P, R = RMAX == 1 ? 1 : p.R, N2 = N / 2;
     const int64_t bh = b * p.H + h;  // == (b, t=0, h) since T = 1
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // state update mapping: thread = (group of VEC columns, n group)
+    const int PG = P / VEC;
+    const int NG = 256 / PG;
+    const int pg = tid % PG, ng = tid / PG;
+    const bool upd = ng < NG;
+    float *hst = p.h + bh * (int64_t)N * P;
+    float hv[U][VEC];
+    auto load_rows = [&](int n0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int n = n0 + u * NG;
+            if (upd && n < N) {
+                if constexpr (VEC == 4) {
+                    const f32x4_t v4 = *(const f32x4_t *)(hst + (int64_t)n * P + pg * 4);
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) hv[u][j] = v4[j];
+                } else {
+                    hv[u][0] = hst[(int64_t)n * P + pg];
+                }
+            }
+        }
+    };
+    load_rows(ng);
 
     extern __shared__ __attribute__((aligned(16))) float sm[];
     float *s_bt = sm;              // [N][R] new B~ (raw B first)
@@ -60,7 +87,6 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     const ET *xg = (const ET *)p.x + bh * P * R;
     const ET *bg = (const ET *)p.Bm + bh * N * R;
     const ET *cg = (const ET *)p.Cm + bh * N * R;
-    float *hst = p.h + bh * (int64_t)N * P;
     for (int e = tid; e < N * R; e += 256) {
         s_bt[e] = Io::ld(bg + e);
         s_ct[e] = Io::ld(cg + e);
@@ -122,46 +148,45 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     const float alpha = __expf(dtv * p.A[h]);
     const float beta = alpha * dtv * (1.f - lmv), gamma = lmv * dtv;
 
-    // state update and partial outputs; thread = (p group of VEC, n group)
-    const int PG = P / VEC;
-    const int NG = 256 / PG;
-    const int pg = tid % PG, ng = tid / PG;
-    float acc[VEC][8];
+    float acc[VEC][RMAX];
 #pragma unroll
     for (int j = 0; j < VEC; ++j)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) acc[j][r] = 0.f;
-    if (ng < NG) {
-        for (int n = ng; n < N; n += NG) {
-            float hv[VEC];
-            if (VEC == 4) {
-                const f32x4_t v4 = *(const f32x4_t *)(hst + (int64_t)n * P + pg * 4);
+        for (int r = 0; r < RMAX; ++r) acc[j][r] = 0.f;
+    if (upd) {
+        for (int n0 = ng; n0 < N; n0 += U * NG) {
+            if (n0 != ng) load_rows(n0);
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) hv[j] = v4[j];
-            } else {
-                hv[0] = hst[(int64_t)n * P + pg];
-            }
+            for (int u = 0; u < U; ++u) {
+                const int n = n0 + u * NG;
+                if (n >= N) break;
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                const int pc = pg * VEC + j;
-                float prev = 0.f, cur = 0.f;
-                for (int r = 0; r < R; ++r) {
-                    prev += s_pb[n * R + r] * s_px[pc * R + r];
-                    cur += s_bt[n * R + r] * s_x[pc * R + r];
+                for (int j = 0; j < VEC; ++j) {
+                    const int pc = pg * VEC + j;
+                    float prev = 0.f, cur = 0.f;
+                    for (int r = 0; r < R; ++r) {
+                        prev += s_pb[n * R + r] * s_px[pc * R + r];
+                        cur += s_bt[n * R + r] * s_x[pc * R + r];
+                    }
+                    const float hn = alpha * hv[u][j] + beta * prev + gamma * cur;
+                    hv[u][j] = hn;
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r)
+                        if (r < R) acc[j][r] += hn * s_ct[n * R + r];
                 }
-                hv[j] = alpha * hv[j] + beta * prev + gamma * cur;
-                for (int r = 0; r < R && r < 8; ++r) acc[j][r] += hv[j] * s_ct[n * R + r];
-            }
-            if (VEC == 4) {
-                *(f32x4_t *)(hst + (int64_t)n * P + pg * 4) = f32x4_t{hv[0], hv[VEC > 1 ? 1 : 0],
-                                                                       hv[VEC > 2 ? 2 : 0], hv[VEC > 3 ? 3 : 0]};
-            } else {
-                hst[(int64_t)n * P + pg] = hv[0];
+                if constexpr (VEC == 4) {
+                    *(f32x4_t *)(hst + (int64_t)n * P + pg * 4) = f32x4_t{hv[u][0], hv[u][VEC > 1 ? 1 : 0],
+                                                                          hv[u][VEC > 2 ? 2 : 0], hv[u][VEC > 3 ? 3 : 0]};
+                } else {
+                    hst[(int64_t)n * P + pg] = hv[u][0];
+                }
             }
         }
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
-            for (int r = 0; r < R; ++r) s_red[(ng * P + pg * VEC + j) * R + r] = acc[j][r];
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r)
+                if (r < R) s_red[(ng * P + pg * VEC + j) * R + r] = acc[j][r];
     }
     __syncthreads();
     ET *yg = (ET *)p.y + bh * P * R;
@@ -183,13 +208,15 @@ hipError_t launch_step(bool bf16, const StepParams &p, hipStream_t stream) {
     const int vec = (p.P % 4 == 0) ? 4 : 1;
     const size_t lds = step_lds_bytes(p, vec);
     dim3 grid((unsigned)p.H, (unsigned)p.B);
+#define M3_STEP_LAUNCH(IO, V, RM) hipLaunchKernelGGL((step_kernel<IO, V, RM>), grid, dim3(256), lds, stream, p)
     if (bf16) {
-        if (vec == 4) hipLaunchKernelGGL((step_kernel<IoBF16, 4>), grid, dim3(256), lds, stream, p);
-        else hipLaunchKernelGGL((step_kernel<IoBF16, 1>), grid, dim3(256), lds, stream, p);
+        if (p.R == 1) { if (vec == 4) M3_STEP_LAUNCH(IoBF16, 4, 1); else M3_STEP_LAUNCH(IoBF16, 1, 1); }
+        else { if (vec == 4) M3_STEP_LAUNCH(IoBF16, 4, 8); else M3_STEP_LAUNCH(IoBF16, 1, 8); }
     } else {
-        if (vec == 4) hipLaunchKernelGGL((step_kernel<IoF32, 4>), grid, dim3(256), lds, stream, p);
-        else hipLaunchKernelGGL((step_kernel<IoF32, 1>), grid, dim3(256), lds, stream, p);
+        if (p.R == 1) { if (vec == 4) M3_STEP_LAUNCH(IoF32, 4, 1); else M3_STEP_LAUNCH(IoF32, 1, 1); }
+        else { if (vec == 4) M3_STEP_LAUNCH(IoF32, 4, 8); else M3_STEP_LAUNCH(IoF32, 1, 8); }
     }
+#undef M3_STEP_LAUNCH
     return hipGetLastError();
 }
 
