@@ -30,8 +30,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-result", "-munsafe-fp-atomics"]
 
-SOURCES = ["m3_scan_bf16_vec.hip", "m3_scan_bf16_gen.hip", "m3_scan_f32_vec.hip", "m3_scan_f32_gen.hip",
-           "m3_scan.hip", "m3_state.hip", "m3_api.cpp"]
+SOURCES = ["m3_scan_bf16_vec.hip", "m3_scan_bf16_gen.hip", "m3_scan_bf16_mimo.hip", "m3_scan_f32_vec.hip",
+           "m3_scan_f32_gen.hip", "m3_scan.hip", "m3_state.hip", "m3_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -78,7 +78,10 @@ TileShape tile_of(const m3_shape *s) {
     TileShape ts;
     ts.np = pow2_at_least(s->dstate, 32);
     ts.pp = pow2_at_least(s->headdim < 64 ? s->headdim : 64, 32);
-    ts.vec = s->rank == 1 && (s->dstate % 8) == 0 && (s->headdim % 8) == 0;
+    const bool v8 = (s->dstate % 8) == 0 && (s->headdim % 8) == 0;
+    ts.mode = m3::kTileGen;
+    if (v8 && s->rank == 1) ts.mode = m3::kTileVec;
+    else if (v8 && s->io == M3_BF16 && (s->rank == 2 || s->rank == 4 || s->rank == 8)) ts.mode = m3::kTileMimo;
     return ts;
 }
 

@@ -51,10 +51,13 @@ struct StepParams {
 };
 
 // Tile variant chosen by the host.
+enum TileMode { kTileGen = 0, kTileVec = 1, kTileMimo = 2 };
 struct TileShape {
     int np;    // N padded: 32, 64 or 128
     int pp;    // columns per workgroup, padded: 32 or 64
-    bool vec;  // SISO with N % 8 == 0 and P % 8 == 0: 16-byte global accesses
+    int mode;  // kTileVec: rank 1 with N % 8 == 0 and P % 8 == 0 (16-byte accesses);
+               // kTileMimo: bf16, rank 2, 4 or 8, N % 8 == 0, P % 8 == 0 (16-byte accesses);
+               // kTileGen: anything else (element accesses)
 };
 
 hipError_t launch_seg_state(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t stream);

@@ -10,16 +10,25 @@ M3_DECLARE(scan_bf16_vec)
 M3_DECLARE(scan_bf16_gen)
 M3_DECLARE(scan_f32_vec)
 M3_DECLARE(scan_f32_gen)
+M3_DECLARE(scan_bf16_mimo)
 #undef M3_DECLARE
 
 size_t seg_kernel_lds_bytes(bool output, bool bf16, const TileShape &ts) {
-    if (bf16) return ts.vec ? scan_bf16_vec_bytes(output, ts) : scan_bf16_gen_bytes(output, ts);
-    return ts.vec ? scan_f32_vec_bytes(output, ts) : scan_f32_gen_bytes(output, ts);
+    if (bf16) {
+        if (ts.mode == kTileVec) return scan_bf16_vec_bytes(output, ts);
+        if (ts.mode == kTileMimo) return scan_bf16_mimo_bytes(output, ts);
+        return scan_bf16_gen_bytes(output, ts);
+    }
+    return ts.mode == kTileVec ? scan_f32_vec_bytes(output, ts) : scan_f32_gen_bytes(output, ts);
 }
 
 static hipError_t launch(bool output, bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t st) {
-    if (bf16) return ts.vec ? scan_bf16_vec_launch(output, ts, p, st) : scan_bf16_gen_launch(output, ts, p, st);
-    return ts.vec ? scan_f32_vec_launch(output, ts, p, st) : scan_f32_gen_launch(output, ts, p, st);
+    if (bf16) {
+        if (ts.mode == kTileVec) return scan_bf16_vec_launch(output, ts, p, st);
+        if (ts.mode == kTileMimo) return scan_bf16_mimo_launch(output, ts, p, st);
+        return scan_bf16_gen_launch(output, ts, p, st);
+    }
+    return ts.mode == kTileVec ? scan_f32_vec_launch(output, ts, p, st) : scan_f32_gen_launch(output, ts, p, st);
 }
 
 hipError_t launch_seg_state(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t st) {

@@ -2,5 +2,5 @@
 #include "m3_scan_impl.hpp"
 
 namespace m3 {
-M3_DEFINE_VARIANT(scan_bf16_gen, IoBF16, false)
+M3_DEFINE_VARIANT(scan_bf16_gen, IoBF16, kModeGen)
 }  // namespace m3

@@ -2,5 +2,5 @@
 #include "m3_scan_impl.hpp"
 
 namespace m3 {
-M3_DEFINE_VARIANT(scan_bf16_vec, IoBF16, true)
+M3_DEFINE_VARIANT(scan_bf16_vec, IoBF16, kModeVec)
 }  // namespace m3

@@ -2,5 +2,5 @@
 #include "m3_scan_impl.hpp"
 
 namespace m3 {
-M3_DEFINE_VARIANT(scan_f32_gen, IoF32, false)
+M3_DEFINE_VARIANT(scan_f32_gen, IoF32, kModeGen)
 }  // namespace m3

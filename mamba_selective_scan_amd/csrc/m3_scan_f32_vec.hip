@@ -2,5 +2,5 @@
 #include "m3_scan_impl.hpp"
 
 namespace m3 {
-M3_DEFINE_VARIANT(scan_f32_vec, IoF32, true)
+M3_DEFINE_VARIANT(scan_f32_vec, IoF32, kModeVec)
 }  // namespace m3

@@ -97,11 +97,22 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <class Io, int NP_, int PP_, bool VEC_>
+// Load paths (the MODE of a kernel variant):
+//   kModeGen : any rank, any even N, any P; element loads.
+//   kModeVec : rank 1 with N and P multiples of 8; 16-byte loads straight into the
+//              operand registers, angle running sums in registers.
+//   kModeMimo: bf16, rank 2, 4 or 8 with N and P multiples of 8; 16-byte loads of the
+//              (n, rank) / (p, rank) interleaved rows, regrouped per rank through LDS.
+constexpr int kModeGen = 0, kModeVec = 1, kModeMimo = 2;
+
+template <class Io, int NP_, int PP_, int MODE_>
 struct SegCfg {
     using ET = typename Io::T;
     static constexpr bool BF = std::is_same<Io, IoBF16>::value;
-    static constexpr bool VEC = VEC_;
+    static constexpr bool VEC = MODE_ == kModeVec;
+    static constexpr bool MV = MODE_ == kModeMimo;
+    static_assert(!MV || BF, "the interleaved-rank load path is bf16 only");
+    static constexpr bool PACKED = (VEC || MV) && BF;  // raw B/C held as packed bf16 words
     static constexpr int NP = NP_, PP = PP_;
     static constexpr int ROWS = kBlockRows;
     static constexpr int KS = NP / 32;  // 32-wide k steps over n
@@ -119,6 +130,9 @@ struct SegCfg {
     static constexpr int XN = VEC ? (ROWS * PP / XW / 256) * 4 : ROWS * PP / 256;  // x words / elements
     static constexpr int TN = VEC ? 4 * KS : ROWS * (NP / 2) / 256;               // theta floats
     static constexpr int BWV = BF ? 4 : 8;  // words per 8 B/C elements when VEC
+    // MV: 16-byte vectors per thread for a block's B (or C) and x
+    static constexpr int NBV = (ROWS * NP / 8 + 255) / 256;
+    static constexpr int NXV = (ROWS * PP / 8 + 255) / 256;
 
     static constexpr size_t al(size_t v) { return (v + 15) / 16 * 16; }
     static constexpr size_t BT_PLANE = (size_t)ROWS * OPP;  // elements per plane
@@ -138,8 +152,10 @@ struct SegCfg {
     // The output kernel prefetches the next block's raw inputs right after the prologue
     // when that fits the register file next to the matrix-core fragments; otherwise it
     // issues them once the block's outputs are staged (overlapping the stores and the carry).
-    static constexpr bool EARLY_PF = VEC && NP <= 64;
-    static constexpr size_t STATE_BYTES = L_WB + L_XT + L_PHI + L_SC;
+    static constexpr bool EARLY_PF = (VEC || MV) && NP <= 64;
+    // MV state kernel: raw B regrouped per rank, [row][n] (the output kernel uses the B~ planes)
+    static constexpr size_t L_RAW = MV ? al((size_t)ROWS * OPP * 2) : 0;
+    static constexpr size_t STATE_BYTES = L_WB + L_XT + L_PHI + L_SC + L_RAW;
     static constexpr size_t OUTPUT_BYTES = L_BT + L_WB + L_XT + L_HT + L_Y + L_PHI + L_SC;
 };
 
@@ -147,10 +163,11 @@ struct SegCfg {
 // the unconverted 16-byte loads; otherwise they are float bits.
 template <class Cfg, bool WANT_C>
 struct RawBlock {
-    static constexpr int BW = (Cfg::VEC && Cfg::BF) ? 4 : 8;  // words per 8 values
-    uint32_t b[Cfg::KS][BW];
-    uint32_t c[WANT_C ? Cfg::KS : 1][BW];
-    uint32_t x[Cfg::XN];
+    static constexpr int BW = Cfg::PACKED ? 4 : 8;  // words per 8 values
+    static constexpr int NB = Cfg::MV ? Cfg::NBV : Cfg::KS;
+    uint32_t b[NB][BW];  // MV: 16-byte vectors in memory order
+    uint32_t c[WANT_C ? NB : 1][BW];
+    uint32_t x[Cfg::MV ? Cfg::NXV * 4 : Cfg::XN];
     float th[Cfg::TN];
     float dt, lam, dtn, lamn;
 };
@@ -171,7 +188,7 @@ __device__ __forceinline__ BlockGeo block_geo(const ScanParams &p, int blk) {
 // LDS carve-up
 template <class Cfg, bool OUT>
 struct Smem {
-    unsigned char *bt, *wb, *xt, *ht, *ys, *phi;
+    unsigned char *bt, *wb, *xt, *ht, *ys, *phi, *raw;
     float *cs, *scale, *gam, *w, *ecs, *tmp, *pend, *cph, *sph;
     double *base;
     __device__ __forceinline__ explicit Smem(unsigned char *s) {
@@ -181,6 +198,8 @@ struct Smem {
         xt = q; q += Cfg::L_XT;
         if (OUT) { ht = q; q += Cfg::L_HT; ys = q; q += Cfg::L_Y; } else { ht = nullptr; ys = nullptr; }
         phi = q; q += Cfg::L_PHI;
+        raw = nullptr;
+        if (!OUT && Cfg::MV) { raw = q; q += Cfg::L_RAW; }
         float *f = (float *)q;
         cs = f; scale = cs + Cfg::ROWS; gam = scale + Cfg::ROWS; w = gam + Cfg::ROWS; ecs = w + Cfg::ROWS;
         tmp = ecs + Cfg::ROWS;
@@ -262,6 +281,49 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
 #pragma unroll
             for (int k = 0; k < 4; ++k) rb.x[m * 4 + k] = v[k];
         }
+    } else if constexpr (Cfg::MV) {
+        // rank R in {2, 4, 8}: one token's B (C) is N*R contiguous values, n major, rank
+        // minor; x is P*R.  16-byte vectors over every (token, vector) slot of the block;
+        // slots past the block end or the padded n / p range load zeros.
+        const int R = c.R;
+        const int Tv = g.Tv;
+        const int vpt = (Cfg::NP * R) >> 3, xvpt = (Cfg::PP * R) >> 3;
+        const float ivpt = 1.f / (float)vpt, ixvpt = 1.f / (float)xvpt;
+        const char *bbase = (const char *)c.Bb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
+        const char *cbase = (const char *)c.Cb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
+#pragma unroll
+        for (int m = 0; m < Cfg::NBV; ++m) {
+            const int v = tid + 256 * m;
+            const int tok = (int)(((float)v + 0.5f) * ivpt), o = v - tok * vpt;
+            u32x4_t vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
+            if (tok < Tv && o * 8 < N * R) {
+                const uint32_t off = (uint32_t)tok * (uint32_t)(c.sbc * sizeof(ET)) + (uint32_t)(o * 16);
+                vb = *(const u32x4_t *)(bbase + off);
+                if constexpr (WANT_C) vc = *(const u32x4_t *)(cbase + off);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                rb.b[m][k] = vb[k];
+                if constexpr (WANT_C) rb.c[m][k] = vc[k];
+            }
+        }
+        const char *xbase = (const char *)c.xb + (int64_t)g.t0 * c.sx * (int64_t)sizeof(ET);
+#pragma unroll
+        for (int m = 0; m < Cfg::NXV; ++m) {
+            const int v = tid + 256 * m;
+            const int tok = (int)(((float)v + 0.5f) * ixvpt), o = v - tok * xvpt;
+            u32x4_t vx = {0u, 0u, 0u, 0u};
+            if (tok < Tv && o * 8 < c.Pw * R)
+                vx = *(const u32x4_t *)(xbase + (uint32_t)tok * (uint32_t)(c.sx * sizeof(ET)) + (uint32_t)(o * 16));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rb.x[m * 4 + k] = vx[k];
+        }
+#pragma unroll
+        for (int m = 0; m < Cfg::TN; ++m) {
+            const int e = tid + 256 * m;
+            const int tr = e / (Cfg::NP / 2), pc = e - tr * (Cfg::NP / 2);
+            rb.th[m] = (tr < Tv && pc < N2) ? p.theta[((b * T + g.t0 + tr) * H + h) * (int64_t)N2 + pc] : 0.f;
+        }
     } else {
         // general layout (rank R, any even N, any P): element loads
         const int R = c.R;
@@ -318,7 +380,7 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
 // decode the 8 B or C values of one k step
 template <class Cfg, int BW>
 __device__ __forceinline__ void raw8(const uint32_t (&w)[BW], float (&v)[8]) {
-    if constexpr (Cfg::VEC && Cfg::BF) {
+    if constexpr (Cfg::PACKED) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             v[2 * k] = __uint_as_float(w[k] << 16);
@@ -327,6 +389,53 @@ __device__ __forceinline__ void raw8(const uint32_t (&w)[BW], float (&v)[8]) {
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(w[k]);
+    }
+}
+
+// two bf16 halves (half h of a and of b) -> one word, a's in the low half
+__device__ __forceinline__ uint32_t pick_halves(uint32_t a, uint32_t b, int h) {
+    return h ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+}
+
+// Interleaved-rank path: regroup a block's raw B (and C) vectors per rank into
+// [row][n] bf16 planes (pitch OPP), row = token * R + rank.  Every slot of the
+// block is written (zeros past the block end and in the padded n range).
+template <class Cfg, bool WANT_C>
+__device__ __forceinline__ void stage_raw_bc(const RawBlock<Cfg, WANT_C> &rb, uint16_t *pb, uint16_t *pcp,
+                                             const WgCtx &c) {
+    const int tid = threadIdx.x;
+    const int R = c.R;
+    const int vpt = (Cfg::NP * R) >> 3;
+    const float ivpt = 1.f / (float)vpt;
+#pragma unroll
+    for (int m = 0; m < Cfg::NBV; ++m) {
+        const int v = tid + 256 * m;
+        const int tok = (int)(((float)v + 0.5f) * ivpt), o = v - tok * vpt;
+        if (tok * R >= Cfg::ROWS) continue;
+        const int n0 = (o * 8) / R, row0 = tok * R;
+        if (R == 2) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int off = (row0 + r) * Cfg::OPP + n0;
+                *(u32x2_t *)(pb + off) = u32x2_t{pick_halves(rb.b[m][0], rb.b[m][1], r), pick_halves(rb.b[m][2], rb.b[m][3], r)};
+                if constexpr (WANT_C)
+                    *(u32x2_t *)(pcp + off) = u32x2_t{pick_halves(rb.c[m][0], rb.c[m][1], r), pick_halves(rb.c[m][2], rb.c[m][3], r)};
+            }
+        } else if (R == 4) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int off = (row0 + r) * Cfg::OPP + n0;
+                *(uint32_t *)(pb + off) = pick_halves(rb.b[m][r >> 1], rb.b[m][(r >> 1) + 2], r & 1);
+                if constexpr (WANT_C) *(uint32_t *)(pcp + off) = pick_halves(rb.c[m][r >> 1], rb.c[m][(r >> 1) + 2], r & 1);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int off = (row0 + r) * Cfg::OPP + n0;
+                pb[off] = (uint16_t)((r & 1) ? (rb.b[m][r >> 1] >> 16) : (rb.b[m][r >> 1] & 0xffffu));
+                if constexpr (WANT_C) pcp[off] = (uint16_t)((r & 1) ? (rb.c[m][r >> 1] >> 16) : (rb.c[m][r >> 1] & 0xffffu));
+            }
+        }
     }
 }
 
@@ -371,7 +480,30 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
         }
     }
     // x -> X^T [p][row]
-    if constexpr (Cfg::VEC) {
+    if constexpr (Cfg::MV) {
+        // one vector holds 8 / R columns x R ranks: R consecutive rows of each column
+        const int R = c.R;
+        const int xvpt = (Cfg::PP * R) >> 3;
+        const float ixvpt = 1.f / (float)xvpt;
+        uint16_t *xt = (uint16_t *)sm.xt;
+#pragma unroll
+        for (int m = 0; m < Cfg::NXV; ++m) {
+            const int v = tid + 256 * m;
+            const int tok = (int)(((float)v + 0.5f) * ixvpt), o = v - tok * xvpt;
+            if (tok * R >= Cfg::ROWS) continue;
+            const int p0 = (o * 8) / R, row0 = tok * R;
+            if (R == 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *(uint32_t *)(xt + (p0 + i) * Cfg::RPP + row0) = rb.x[m * 4 + i];
+            } else if (R == 4) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    *(u32x2_t *)(xt + (p0 + i) * Cfg::RPP + row0) = u32x2_t{rb.x[m * 4 + 2 * i], rb.x[m * 4 + 2 * i + 1]};
+            } else {
+                *(u32x4_t *)(xt + p0 * Cfg::RPP + row0) = u32x4_t{rb.x[m * 4], rb.x[m * 4 + 1], rb.x[m * 4 + 2], rb.x[m * 4 + 3]};
+            }
+        }
+    } else if constexpr (Cfg::VEC) {
 #pragma unroll
         for (int m = 0; m < Cfg::XN / 4; ++m) {
             const int e = tid + 256 * m;
@@ -469,12 +601,38 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
     const int tok = Cfg::VEC ? row : tok_of(row, c);
     const int r = row - tok * R;
     const bool rv = tok < g.Tv;
+    // raw B / C words of this lane's row: registers, or (interleaved ranks) the regrouped planes
+    using RB = RawBlock<Cfg, WANT_C>;
+    uint32_t bw[KS][RB::BW], cw[WANT_C ? KS : 1][RB::BW];
+    if constexpr (Cfg::MV) {
+        const uint16_t *pb = WANT_C ? (const uint16_t *)sm.bt : (const uint16_t *)sm.raw;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const int off = row * Cfg::OPP + kk * 32 + 8 * gq;
+            const u32x4_t v = *(const u32x4_t *)(pb + off);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) bw[kk][k] = v[k];
+            if constexpr (WANT_C) {
+                const u32x4_t u = *(const u32x4_t *)((const uint16_t *)sm.bt + Cfg::BT_PLANE + off);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) cw[kk][k] = u[k];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int k = 0; k < RB::BW; ++k) {
+                bw[kk][k] = rb.b[kk][k];
+                if constexpr (WANT_C) cw[kk][k] = rb.c[kk][k];
+            }
+    }
     float ssb = 0.f, ssc = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
         float vb[8], vc[8];
-        raw8<Cfg>(rb.b[kk], vb);
-        if constexpr (WANT_C) raw8<Cfg>(rb.c[kk], vc);
+        raw8<Cfg>(bw[kk], vb);
+        if constexpr (WANT_C) raw8<Cfg>(cw[kk], vc);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             ssb = fmaf(vb[j], vb[j], ssb);
@@ -509,8 +667,8 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
         float vb[8], vc[8];
-        raw8<Cfg>(rb.b[kk], vb);
-        if constexpr (WANT_C) raw8<Cfg>(rb.c[kk], vc);
+        raw8<Cfg>(bw[kk], vb);
+        if constexpr (WANT_C) raw8<Cfg>(cw[kk], vc);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             vb[j] *= rsb;
@@ -765,9 +923,10 @@ __device__ __forceinline__ WgCtx make_ctx(const ScanParams &p, int nsegk) {
 }
 
 // ============================================================ state kernel
-template <class Io, int NP, int PP, bool VEC>
+template <class Io, int NP, int PP, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) void seg_state_kernel(ScanParams p) {
-    using Cfg = SegCfg<Io, NP, PP, VEC>;
+    using Cfg = SegCfg<Io, NP, PP, MODE>;
+    constexpr bool VEC = Cfg::VEC;
     using Frag = typename std::conditional<Cfg::BF, FragHL, FragF>::type;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Smem<Cfg, false> sm(smem);
@@ -786,6 +945,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
     RawBlock<Cfg, false> rb;
     BlockGeo g = block_geo(p, c.blk0);
     load_block<Io>(rb, p, c, g);
+    if constexpr (Cfg::MV) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.raw, nullptr, c);
     for (int blk = c.blk0; blk < c.blk1; ++blk) {
         lds_barrier();  // previous block's readers of the LDS planes are done
         stage_scalars_x<Io>(rb, sm, p, c, g);
@@ -797,6 +957,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
         lds_barrier();
         const float cs_end = sm.cs[Cfg::ROWS - 1];
         carry_block<Cfg>(sm, sagg, __expf(cs_end), N2);
+        if constexpr (Cfg::MV) {
+            if (blk + 1 < c.blk1) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.raw, nullptr, c);
+        }
         lsum += cs_end;
         if (tid < N2) sm.base[tid] += (double)sm.pend[tid];
         g = gn;
@@ -823,9 +986,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
 }
 
 // ============================================================ output kernel
-template <class Io, int NP, int PP, bool VEC>
+template <class Io, int NP, int PP, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg_output_kernel(ScanParams p) {
-    using Cfg = SegCfg<Io, NP, PP, VEC>;
+    using Cfg = SegCfg<Io, NP, PP, MODE>;
+    constexpr bool VEC = Cfg::VEC;
     using ET = typename Io::T;
     using Frag = typename std::conditional<Cfg::BF, FragHL, FragF>::type;
     constexpr int KS = Cfg::KS, PT = Cfg::PT, TPW = Cfg::TPW;
@@ -931,6 +1095,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         write_ht<Cfg>(sm, hs);
     }
+    if constexpr (Cfg::MV) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.bt, (uint16_t *)sm.bt + Cfg::BT_PLANE, c);
 
     Frag ct[KS];
     for (int blk = c.blk0; blk < c.blk1; ++blk) {
@@ -1107,7 +1272,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 float yv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) yv[i] = yacc[pt][i] + Dh * xv[i];
-                if constexpr (Cfg::BF) {
+                if constexpr (Cfg::MV) {
+                    // staged in the global order [token][p][rank]
+                    const uint32_t w01 = pack_bf16(yv[0], yv[1]), w23 = pack_bf16(yv[2], yv[3]);
+                    if (R == 2) {
+                        const int tk = row0 >> 1;
+                        *(uint32_t *)(ys + (tk * PP + pc) * 2) = w01;
+                        *(uint32_t *)(ys + ((tk + 1) * PP + pc) * 2) = w23;
+                    } else {
+                        const int tk = tok_of(row0, c), r0 = row0 - tk * R;
+                        *(u32x2_t *)(ys + (tk * PP + pc) * R + r0) = u32x2_t{w01, w23};
+                    }
+                } else if constexpr (Cfg::BF) {
                     const uint32_t w01 = pack_bf16(yv[0], yv[1]), w23 = pack_bf16(yv[2], yv[3]);
                     ys[(row0 + 0) * PP + pc] = (uint16_t)(w01 & 0xffffu);
                     ys[(row0 + 1) * PP + pc] = (uint16_t)(w01 >> 16);
@@ -1124,10 +1300,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (!Cfg::EARLY_PF) {
             if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
         }
+        if constexpr (Cfg::MV) {
+            // every wave is past its last read of the B~ planes: regroup the next block there
+            if (blk + 1 < c.blk1) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.bt, (uint16_t *)sm.bt + Cfg::BT_PLANE, c);
+        }
         {
             const ET *ys = (const ET *)sm.ys;
             const int Rv = g.Tv * R;
-            if constexpr (VEC) {
+            if constexpr (Cfg::MV) {
+                const int yvpt = (PP * R) >> 3;
+                const float iy = 1.f / (float)yvpt;
+#pragma unroll
+                for (int m = 0; m < Cfg::NXV; ++m) {
+                    const int e = tid + 256 * m;
+                    const int tk = (int)(((float)e + 0.5f) * iy), o = e - tk * yvpt;
+                    if (tk < g.Tv && o * 8 < c.Pw * R)
+                        *(u32x4_t *)((ET *)c.yb + (g.t0 + tk) * c.sx + o * 8) = *(const u32x4_t *)(ys + tk * PP * R + o * 8);
+                }
+            } else if constexpr (VEC) {
 #pragma unroll
                 for (int m = 0; m < Cfg::ROWS * PP / Cfg::XW / 256; ++m) {
                     const int e = tid + 256 * m;
@@ -1193,17 +1383,17 @@ static hipError_t set_lds(K kern, size_t bytes) {
     return hipSuccess;
 }
 
-template <class Io, int NP, int PP, bool VEC>
+template <class Io, int NP, int PP, int MODE>
 static hipError_t launch_seg_t(bool output, const ScanParams &p, hipStream_t st) {
-    using Cfg = SegCfg<Io, NP, PP, VEC>;
+    using Cfg = SegCfg<Io, NP, PP, MODE>;
     if (output) {
-        auto kern = seg_output_kernel<Io, NP, PP, VEC>;
+        auto kern = seg_output_kernel<Io, NP, PP, MODE>;
         hipError_t e = set_lds(kern, Cfg::OUTPUT_BYTES);
         if (e != hipSuccess) return e;
         const int64_t nwg = p.B * p.H * (int64_t)p.ncg * p.nseg;
         hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), Cfg::OUTPUT_BYTES, st, p);
     } else {
-        auto kern = seg_state_kernel<Io, NP, PP, VEC>;
+        auto kern = seg_state_kernel<Io, NP, PP, MODE>;
         hipError_t e = set_lds(kern, Cfg::STATE_BYTES);
         if (e != hipSuccess) return e;
         const int64_t nwg = p.B * p.H * (int64_t)p.ncg * (p.nseg - 1);
@@ -1213,17 +1403,17 @@ static hipError_t launch_seg_t(bool output, const ScanParams &p, hipStream_t st)
     return hipGetLastError();
 }
 
-#define M3_SHAPES(X, Io, VEC) \
-    X(Io, 32, 32, VEC) X(Io, 32, 64, VEC) X(Io, 64, 32, VEC) X(Io, 64, 64, VEC) X(Io, 128, 32, VEC) X(Io, 128, 64, VEC)
+#define M3_SHAPES(X, Io, MODE) \
+    X(Io, 32, 32, MODE) X(Io, 32, 64, MODE) X(Io, 64, 32, MODE) X(Io, 64, 64, MODE) X(Io, 128, 32, MODE) X(Io, 128, 64, MODE)
 
 // Instantiate the launcher and LDS query of one (io type, load path) pair.
-#define M3_DEFINE_VARIANT(NAME, Io, VEC)                                                               \
+#define M3_DEFINE_VARIANT(NAME, Io, MODE)                                                              \
     hipError_t NAME##_launch(bool output, const TileShape &ts, const ScanParams &p, hipStream_t st) {  \
-        M3_SHAPES(M3_LAUNCH_CASE, Io, VEC)                                                            \
+        M3_SHAPES(M3_LAUNCH_CASE, Io, MODE)                                                           \
         return hipErrorInvalidValue;                                                                  \
     }                                                                                                 \
     size_t NAME##_bytes(bool output, const TileShape &ts) {                                           \
-        M3_SHAPES(M3_BYTES_CASE, Io, VEC)                                                             \
+        M3_SHAPES(M3_BYTES_CASE, Io, MODE)                                                            \
         return 0;                                                                                     \
     }
 #define M3_LAUNCH_CASE(IoT, NPV, PPV, V) \
