@@ -986,8 +986,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
 }
 
 // ============================================================ output kernel
+// With N above 64 the LDS planes allow one workgroup per compute unit (one wave per
+// SIMD), so such variants may use the whole register file.
 template <class Io, int NP, int PP, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg_output_kernel(ScanParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1 : 2, NP > 64 ? 1 : 2))) void seg_output_kernel(ScanParams p) {
     using Cfg = SegCfg<Io, NP, PP, MODE>;
     constexpr bool VEC = Cfg::VEC;
     using ET = typename Io::T;
