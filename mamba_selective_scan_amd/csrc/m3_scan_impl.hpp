@@ -97,6 +97,9 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The 16-row tile of a block that this wave owns.
+__device__ __forceinline__ int row_tile() { return threadIdx.x >> 6; }
+
 // Load paths (the MODE of a kernel variant):
 //   kModeGen : any rank, any even N, any P; element loads.
 //   kModeVec : rank 1 with N and P multiples of 8; 16-byte loads straight into the
@@ -235,7 +238,7 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
     const int l16 = lane & 15, gq = lane >> 4;
     const int64_t T = p.T, H = p.H;
     const int N = p.N, P = p.P, N2 = p.N / 2;
-    const int row = wave * 16 + l16;
+    const int row = row_tile() * 16 + l16;
     const int64_t b = c.b;
     const int h = c.h;
     if constexpr (Cfg::VEC) {
@@ -468,7 +471,7 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
             const int gq = lane >> 4;
 #pragma unroll
             for (int kk = 0; kk < Cfg::KS; ++kk)
-                *(f32x4_t *)(tt + wave * (Cfg::NP / 2) + kk * 16 + 4 * gq) =
+                *(f32x4_t *)(tt + row_tile() * (Cfg::NP / 2) + kk * 16 + 4 * gq) =
                     f32x4_t{rb.th[kk * 4], rb.th[kk * 4 + 1], rb.th[kk * 4 + 2], rb.th[kk * 4 + 3]};
         }
     } else {
@@ -597,7 +600,7 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
     const int l16 = lane & 15, gq = lane >> 4;
     const int N = p.N;
     const int R = Cfg::VEC ? 1 : c.R;
-    const int row = wave * 16 + l16;
+    const int row = row_tile() * 16 + l16;
     const int tok = Cfg::VEC ? row : tok_of(row, c);
     const int r = row - tok * R;
     const bool rv = tok < g.Tv;
@@ -653,13 +656,14 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
     f32x4_t phoff[KS];
     if constexpr (Cfg::VEC) {
         const float *tt = (const float *)sm.phi;
+        const int rtile = row_tile();
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w2 = 0; w2 < 3; ++w2) {
                 const f32x4_t t4 = *(const f32x4_t *)(tt + w2 * (Cfg::NP / 2) + kk * 16 + 4 * gq);
-                if (w2 < wave) o += t4;
+                if (w2 < rtile) o += t4;
             }
             phoff[kk] = o;
         }
@@ -1095,13 +1099,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             }
             sm.base[tid] = a;
         }
-        write_ht<Cfg>(sm, hs);
     }
-    if constexpr (Cfg::MV) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.bt, (uint16_t *)sm.bt + Cfg::BT_PLANE, c);
 
     Frag ct[KS];
     for (int blk = c.blk0; blk < c.blk1; ++blk) {
-        lds_barrier();  // previous block's LDS readers are done; H^T written
+        lds_barrier();  // every wave is done with the previous block's LDS planes
+        write_ht<Cfg>(sm, hs);  // the state entering this block (read after two more barriers)
+        if constexpr (Cfg::MV) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.bt, (uint16_t *)sm.bt + Cfg::BT_PLANE, c);
         stage_scalars_x<Io>(rb, sm, p, c, g);
         if constexpr (!VEC) stage_angles_table<Cfg>(sm, p, g);
         block_angle_totals<Cfg>(sm, p, g);
@@ -1115,7 +1119,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         if (last_blk && c.cg == 0) write_final_prev_b<Cfg>(sm, p, c, g);
 
         // ---- outputs for this wave's 16 rows
-        const int tt = wave;
+        const int tt = row_tile();
         const int row0 = tt * 16 + 4 * gq;  // result rows row0 .. row0 + 3 of this lane
         f32x4_t yacc[PT];
 #pragma unroll
@@ -1298,47 +1302,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             }
         }
         const float cs_end = sm.cs[Cfg::ROWS - 1];
-        lds_barrier();  // staging complete; all waves done reading H^T and the planes
         if constexpr (!Cfg::EARLY_PF) {
             if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
         }
-        if constexpr (Cfg::MV) {
-            // every wave is past its last read of the B~ planes: regroup the next block there
-            if (blk + 1 < c.blk1) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.bt, (uint16_t *)sm.bt + Cfg::BT_PLANE, c);
-        }
+        // ---- y: this wave's rows, staged in its own part of the staging area (LDS
+        // operations of one wave complete in order), stored as 16-byte vectors
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
         {
             const ET *ys = (const ET *)sm.ys;
             const int Rv = g.Tv * R;
             if constexpr (Cfg::MV) {
                 const int yvpt = (PP * R) >> 3;
                 const float iy = 1.f / (float)yvpt;
+                const int tk0 = (tt * 16) / R;
 #pragma unroll
-                for (int m = 0; m < Cfg::NXV; ++m) {
-                    const int e = tid + 256 * m;
-                    const int tk = (int)(((float)e + 0.5f) * iy), o = e - tk * yvpt;
+                for (int m = 0; m < 16 * PP / 8 / 64; ++m) {
+                    const int e = lane + 64 * m;
+                    const int tk = tk0 + (int)(((float)e + 0.5f) * iy), o = e - (tk - tk0) * yvpt;
                     if (tk < g.Tv && o * 8 < c.Pw * R)
                         *(u32x4_t *)((ET *)c.yb + (g.t0 + tk) * c.sx + o * 8) = *(const u32x4_t *)(ys + tk * PP * R + o * 8);
                 }
             } else if constexpr (VEC) {
 #pragma unroll
-                for (int m = 0; m < Cfg::ROWS * PP / Cfg::XW / 256; ++m) {
-                    const int e = tid + 256 * m;
-                    const int yr = e / (PP / Cfg::XW), pc = (e % (PP / Cfg::XW)) * Cfg::XW;
+                for (int m = 0; m < 16 * PP / Cfg::XW / 64; ++m) {
+                    const int e = lane + 64 * m;
+                    const int yr = tt * 16 + e / (PP / Cfg::XW), pc = (e % (PP / Cfg::XW)) * Cfg::XW;
                     if (yr < Rv && pc < c.Pw)
                         *(u32x4_t *)((ET *)c.yb + (g.t0 + yr) * c.sx + pc) = *(const u32x4_t *)(ys + yr * PP + pc);
                 }
             } else {
-                for (int e = tid; e < Rv * PP; e += 256) {
-                    const int yr = e / PP, pc = e - yr * PP;
-                    if (pc >= c.Pw) continue;
+                for (int e = lane; e < 16 * PP; e += 64) {
+                    const int yr = tt * 16 + e / PP, pc = e - (e / PP) * PP;
+                    if (yr >= Rv || pc >= c.Pw) continue;
                     const int tok = tok_of(yr, c), r = yr - tok * R;
                     ((ET *)c.yb)[(g.t0 + tok) * c.sx + (int64_t)pc * R + r] = ys[yr * PP + pc];
                 }
             }
         }
-        // ---- carry to the next block
+        // ---- carry to the next block (H^T is rewritten after the next top barrier)
         carry_block<Cfg>(sm, hs, __expf(cs_end), N2);
-        write_ht<Cfg>(sm, hs);
         if (last_blk) {
             // carried x of the last token
             const int lrow0 = (g.Tv - 1) * R;
