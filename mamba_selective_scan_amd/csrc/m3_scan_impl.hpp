@@ -45,17 +45,13 @@
 
 namespace m3 {
 
-// sin and cos of an angle: reduce to [-pi, pi] with a two-constant 2 pi (hi + lo,
-// both fused multiply-adds), then the hardware sin/cos units, which take the
-// argument in revolutions.
+// sin and cos of an angle with the hardware sin/cos units, which take the
+// argument in revolutions: the angle is scaled by 1 / (2 pi) and its fractional
+// part taken.  The scaling rounds to 2^-24 of the angle, below the float
+// resolution of the angle itself; callers pass block-local running sums or
+// angles already reduced to [0, 2 pi).
 __device__ __forceinline__ void fast_sincos(float a, float &s, float &c) {
-    const float two_pi_hi = 6.28318548202514648f;      // float nearest to 2 pi
-    const float two_pi_lo = -1.7484555314695172e-07f;  // 2 pi - two_pi_hi
-    const float inv_two_pi = 0.15915494309189535f;
-    const float k = rintf(a * inv_two_pi);
-    float r = fmaf(-k, two_pi_hi, a);
-    r = fmaf(-k, two_pi_lo, r);
-    const float rev = r * inv_two_pi;
+    const float rev = __builtin_amdgcn_fractf(a * 0.15915494309189535f);
     s = __builtin_amdgcn_sinf(rev);
     c = __builtin_amdgcn_cosf(rev);
 }
@@ -79,14 +75,13 @@ __device__ __forceinline__ float row_incl_scan(float v) {
     return v;
 }
 
-// inclusive add-scan of 64 lanes (every lane of the wave must be active)
+// inclusive add-scan of 64 lanes (every lane of the wave must be active): scans
+// inside the rows of 16, then row 0's total is broadcast into row 1 (and row 2's
+// into row 3), then row 1's running total into rows 2 and 3
 __device__ __forceinline__ float wave_incl_scan(float v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
-    }
+    v = row_incl_scan(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
     return v;
 }
 
@@ -456,7 +451,7 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
         const float ga = rb.lam * rb.dt;
         const float sc = ga + rb.dtn * (1.f - rb.lamn);
         const float cs = wave_incl_scan(la);
-        const float cs_end = __shfl(cs, 63, 64);
+        const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
         sm.cs[lane] = cs;
         sm.scale[lane] = sc;
         sm.gam[lane] = ga;
