@@ -126,7 +126,9 @@ struct SegCfg {
     static constexpr int XW = BF ? 8 : 4;          // io elements per 16-byte vector
     // per-thread raw counts
     static constexpr int XN = VEC ? (ROWS * PP / XW / 256) * 4 : ROWS * PP / 256;  // x words / elements
-    static constexpr int TN = VEC ? 4 * KS : ROWS * (NP / 2) / 256;               // theta floats
+    // tokens per block: 64 for ranks 1 and 3..7 of the general path; at most 32 with MV (rank >= 2)
+    static constexpr int TOKS = MV ? ROWS / 2 : ROWS;
+    static constexpr int TN = VEC ? 4 * KS : TOKS * (NP / 2) / 256;               // theta floats
     static constexpr int BWV = BF ? 4 : 8;  // words per 8 B/C elements when VEC
     // MV: 16-byte vectors per thread for a block's B (or C) and x
     static constexpr int NBV = (ROWS * NP / 8 + 255) / 256;
@@ -142,7 +144,7 @@ struct SegCfg {
     static constexpr size_t L_HT = al(HT_PLANE * ES * NPL);
     static constexpr size_t L_Y = al((size_t)ROWS * PP * sizeof(ET));
     // angles: the general path keeps a table [token][pair]; the SISO path only tile totals [4][pair]
-    static constexpr size_t L_PHI = al(VEC ? (size_t)4 * (NP / 2) * 4 : (size_t)ROWS * PHP * 4);
+    static constexpr size_t L_PHI = al(VEC ? (size_t)4 * (NP / 2) * 4 : (size_t)TOKS * PHP * 4);
     // scalars: cs, scale, gamma, w, exp(cs) [ROWS]; scan scratch [256 + 8];
     // per pair: block angle total, its cos and sin; per pair (double): running angle base
     static constexpr size_t L_SC0 = al((5 * ROWS + 264 + 3 * (NP / 2)) * 4);
@@ -153,8 +155,10 @@ struct SegCfg {
     static constexpr bool EARLY_PF = (VEC || MV) && NP <= 64;
     // MV state kernel: raw B regrouped per rank, [row][n] (the output kernel uses the B~ planes)
     static constexpr size_t L_RAW = MV ? al((size_t)ROWS * OPP * 2) : 0;
-    static constexpr size_t STATE_BYTES = L_WB + L_XT + L_PHI + L_SC + L_RAW;
-    static constexpr size_t OUTPUT_BYTES = L_BT + L_WB + L_XT + L_HT + L_Y + L_PHI + L_SC;
+    // rank-1 path: norm gains and this head's biases for B and C, [4][NP] (1 and 0 when absent)
+    static constexpr size_t L_AFF = VEC ? al((size_t)4 * NP * 4) : 0;
+    static constexpr size_t STATE_BYTES = L_WB + L_XT + L_PHI + L_SC + L_RAW + L_AFF;
+    static constexpr size_t OUTPUT_BYTES = L_BT + L_WB + L_XT + L_HT + L_Y + L_PHI + L_SC + L_AFF;
 };
 
 // Raw inputs of one block, prefetched into registers.  With VEC the words are
@@ -187,7 +191,7 @@ __device__ __forceinline__ BlockGeo block_geo(const ScanParams &p, int blk) {
 template <class Cfg, bool OUT>
 struct Smem {
     unsigned char *bt, *wb, *xt, *ht, *ys, *phi, *raw;
-    float *cs, *scale, *gam, *w, *ecs, *tmp, *pend, *cph, *sph;
+    float *cs, *scale, *gam, *w, *ecs, *tmp, *pend, *cph, *sph, *aff;
     double *base;
     __device__ __forceinline__ explicit Smem(unsigned char *s) {
         unsigned char *q = s;
@@ -203,6 +207,7 @@ struct Smem {
         tmp = ecs + Cfg::ROWS;
         pend = tmp + 264; cph = pend + Cfg::NP / 2; sph = cph + Cfg::NP / 2;
         base = (double *)(q + Cfg::L_SC0);
+        aff = (float *)(q + Cfg::L_SC);
     }
 };
 
@@ -474,7 +479,7 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
         for (int m = 0; m < Cfg::TN; ++m) {
             const int e = tid + 256 * m;
             const int tr = e / (Cfg::NP / 2), pc = e - tr * (Cfg::NP / 2);
-            ((float *)sm.phi)[tr * Cfg::PHP + pc] = rb.th[m];
+            if (tr < Cfg::TOKS) ((float *)sm.phi)[tr * Cfg::PHP + pc] = rb.th[m];
         }
     }
     // x -> X^T [p][row]
@@ -673,7 +678,30 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
             vb[j] *= rsb;
             if constexpr (WANT_C) vc[j] *= rsc;
         }
-        if (c.affine && rv) {
+        if constexpr (Cfg::VEC) {
+            if (c.affine && rv) {
+                // gains (with the norm) and this head's biases, staged in LDS at kernel start
+                const int n0 = kk * 32 + 8 * gq;
+                const f32x4_t g0 = *(const f32x4_t *)(sm.aff + n0), g1 = *(const f32x4_t *)(sm.aff + n0 + 4);
+                const f32x4_t b0 = *(const f32x4_t *)(sm.aff + 2 * Cfg::NP + n0);
+                const f32x4_t b1 = *(const f32x4_t *)(sm.aff + 2 * Cfg::NP + n0 + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    vb[j] = fmaf(vb[j], g0[j], b0[j]);
+                    vb[j + 4] = fmaf(vb[j + 4], g1[j], b1[j]);
+                }
+                if constexpr (WANT_C) {
+                    const f32x4_t h0 = *(const f32x4_t *)(sm.aff + Cfg::NP + n0), h1 = *(const f32x4_t *)(sm.aff + Cfg::NP + n0 + 4);
+                    const f32x4_t d0 = *(const f32x4_t *)(sm.aff + 3 * Cfg::NP + n0);
+                    const f32x4_t d1 = *(const f32x4_t *)(sm.aff + 3 * Cfg::NP + n0 + 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        vc[j] = fmaf(vc[j], h0[j], d0[j]);
+                        vc[j + 4] = fmaf(vc[j + 4], h1[j], d1[j]);
+                    }
+                }
+            }
+        } else if (c.affine && rv) {
             // gains (with the norm) and per-(head, rank) biases
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -921,6 +949,24 @@ __device__ __forceinline__ WgCtx make_ctx(const ScanParams &p, int nsegk) {
     return c;
 }
 
+// Rank-1 path: gains and this head's biases into LDS ([4][NP]; 1 and 0 when absent
+// or past N).  Read after the next barrier.
+template <class Cfg, class Sm>
+__device__ __forceinline__ void stage_affine(const Sm &sm, const ScanParams &p, const WgCtx &c) {
+    if constexpr (Cfg::VEC) {
+        const int tid = threadIdx.x;
+        if (tid < Cfg::NP) {
+            const int n = tid;
+            const bool in = n < p.N;
+            const bool g = c.bcnorm;  // gains apply only together with the norm
+            sm.aff[n] = (in && g && p.bnw) ? p.bnw[n] : 1.f;
+            sm.aff[Cfg::NP + n] = (in && g && p.cnw) ? p.cnw[n] : 1.f;
+            sm.aff[2 * Cfg::NP + n] = (in && p.bbias) ? p.bbias[(int64_t)c.h * p.N + n] : 0.f;
+            sm.aff[3 * Cfg::NP + n] = (in && p.cbias) ? p.cbias[(int64_t)c.h * p.N + n] : 0.f;
+        }
+    }
+}
+
 // ============================================================ state kernel
 template <class Io, int NP, int PP, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) void seg_state_kernel(ScanParams p) {
@@ -941,6 +987,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
     float lsum = 0.f;
     Frag ct_unused[Cfg::KS];
 
+    stage_affine<Cfg>(sm, p, c);
     RawBlock<Cfg, false> rb;
     BlockGeo g = block_geo(p, c.blk0);
     load_block<Io>(rb, p, c, g);
@@ -1006,6 +1053,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     const bool want_final = (c.seg == p.nseg - 1) && (p.h1 != nullptr);
 
     // prefetch the first block while the incoming state is assembled
+    stage_affine<Cfg>(sm, p, c);
     RawBlock<Cfg, true> rb;
     BlockGeo g = block_geo(p, c.blk0);
     load_block<Io>(rb, p, c, g);
@@ -1104,14 +1152,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         stage_scalars_x<Io>(rb, sm, p, c, g);
         if constexpr (!VEC) stage_angles_table<Cfg>(sm, p, g);
         block_angle_totals<Cfg>(sm, p, g);
-        const bool last_blk = want_final && (blk == p.nblk - 1);
         stage_prologue<Io>(rb, sm, p, c, g, ct);
         const BlockGeo gn = block_geo(p, blk + 1);
         if constexpr (Cfg::EARLY_PF) {
             if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
         }
         lds_barrier();
-        if (last_blk && c.cg == 0) write_final_prev_b<Cfg>(sm, p, c, g);
 
         // ---- outputs for this wave's 16 rows
         const int tt = row_tile();
@@ -1337,9 +1383,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         }
         // ---- carry to the next block (H^T is rewritten after the next top barrier)
         carry_block<Cfg>(sm, hs, __expf(cs_end), N2);
-        if (last_blk) {
+        // running angle at the next block's start (the last block's start angle is kept
+        // for the carried B~ below)
+        if (tid < N2 && blk + 1 < c.blk1) sm.base[tid] += (double)sm.pend[tid];
+        g = gn;
+    }
+    if (want_final) {
+        // The last block's B~ (B~ planes), x (X^T plane) and angle total are still in LDS.
+        const BlockGeo gl = block_geo(p, c.blk1 - 1);
+        lds_barrier();
+        if (c.cg == 0) write_final_prev_b<Cfg>(sm, p, c, gl);
+        {
             // carried x of the last token
-            const int lrow0 = (g.Tv - 1) * R;
+            const int lrow0 = (gl.Tv - 1) * R;
             for (int e = tid; e < c.Pw * R; e += 256) {
                 const int pc = e / R, r = e - pc * R;
                 float xv;
@@ -1348,10 +1404,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 p.px1[(bh * P + c.p0 + pc) * R + r] = xv;
             }
         }
+        lds_barrier();  // every read of the last block's start angle is done
         if (tid < N2) sm.base[tid] += (double)sm.pend[tid];
-        g = gn;
-    }
-    if (want_final) {
         lds_barrier();  // final base angles visible
         // final state in the global frame: Rot(Theta_final) H
 #pragma unroll

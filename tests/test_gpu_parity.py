@@ -188,14 +188,16 @@ def test_shapes(T, P, N, R, Q, io):
     check_state(fin, f_ref, io)
 
 
-@pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_norm_off_and_nonzero_init(io):
+@pytest.mark.parametrize("io,with_params", [("f32", False), ("bf16", False), ("f32", True), ("bf16", True)])
+def test_norm_off_and_nonzero_init(io, with_params):
+    """Norm off (gains then have no effect, biases still apply) with a carried initial state."""
     w = custom(batch=2, seqlen=150, nheads=2, headdim=32, dstate=32, chunk=32, io=io, seed=99)
-    log(f"case norm off + init {w}")
+    log(f"case norm off + init {w} params={with_params}")
     inp = make_inputs(w)
     st = make_state(w, scale=0.5)
-    y_ref, f_ref = oracle.scan(*oracle_args(inp), bcnorm=False, init=st)
-    y, fin = run_gpu(w, inp, init=st, final=True, bcnorm=False)
+    npar = make_norm_params(w) if with_params else {}
+    y_ref, f_ref = oracle.scan(*oracle_args(inp), bcnorm=False, init=st, **npar)
+    y, fin = run_gpu(w, inp, init=st, final=True, bcnorm=False, npar=npar or None)
     check("y", y, y_ref, io)
     check_state(fin, f_ref, io)
 
