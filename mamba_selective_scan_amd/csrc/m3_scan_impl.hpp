@@ -174,6 +174,21 @@ struct RawBlock {
     float dt, lam, dtn, lamn;
 };
 
+// Offset of (col, row) in a [col][row] plane of pitch RPP, the row index XOR-swizzled
+// by bits 3..5 of col.  Writes of one row to 8 columns then spread over the LDS
+// banks, and every aligned group of 8 rows stays contiguous for the 16-byte reads.
+template <class Cfg>
+__device__ __forceinline__ int tr_off(int col, int row) {
+    return col * Cfg::RPP + (row ^ (((col >> 3) & 7) << 3));
+}
+// Offset of (row, col) in the y staging plane [row][PP] (rank-1 and general paths):
+// columns XOR-swizzled in groups of 16 by bits 2.. of the row, so that the four
+// 4-row groups written by one instruction use different banks.
+template <class Cfg>
+__device__ __forceinline__ int ys_off(int row, int col) {
+    return row * Cfg::PP + (col ^ (((row >> 2) & (Cfg::PP / 16 - 1)) << 4));
+}
+
 struct BlockGeo {
     int64_t t0;  // first token
     int Tv;      // valid tokens
@@ -497,13 +512,13 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
             const int p0 = (o * 8) / R, row0 = tok * R;
             if (R == 2) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) *(uint32_t *)(xt + (p0 + i) * Cfg::RPP + row0) = rb.x[m * 4 + i];
+                for (int i = 0; i < 4; ++i) *(uint32_t *)(xt + tr_off<Cfg>(p0 + i, row0)) = rb.x[m * 4 + i];
             } else if (R == 4) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    *(u32x2_t *)(xt + (p0 + i) * Cfg::RPP + row0) = u32x2_t{rb.x[m * 4 + 2 * i], rb.x[m * 4 + 2 * i + 1]};
+                    *(u32x2_t *)(xt + tr_off<Cfg>(p0 + i, row0)) = u32x2_t{rb.x[m * 4 + 2 * i], rb.x[m * 4 + 2 * i + 1]};
             } else {
-                *(u32x4_t *)(xt + p0 * Cfg::RPP + row0) = u32x4_t{rb.x[m * 4], rb.x[m * 4 + 1], rb.x[m * 4 + 2], rb.x[m * 4 + 3]};
+                *(u32x4_t *)(xt + tr_off<Cfg>(p0, row0)) = u32x4_t{rb.x[m * 4], rb.x[m * 4 + 1], rb.x[m * 4 + 2], rb.x[m * 4 + 3]};
             }
         }
     } else if constexpr (Cfg::VEC) {
@@ -515,13 +530,13 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
                 uint16_t *xt = (uint16_t *)sm.xt;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    xt[(pc + 2 * k) * Cfg::RPP + xr] = (uint16_t)(rb.x[m * 4 + k] & 0xffffu);
-                    xt[(pc + 2 * k + 1) * Cfg::RPP + xr] = (uint16_t)(rb.x[m * 4 + k] >> 16);
+                    xt[tr_off<Cfg>(pc + 2 * k, xr)] = (uint16_t)(rb.x[m * 4 + k] & 0xffffu);
+                    xt[tr_off<Cfg>(pc + 2 * k + 1, xr)] = (uint16_t)(rb.x[m * 4 + k] >> 16);
                 }
             } else {
                 float *xt = (float *)sm.xt;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) xt[(pc + k) * Cfg::RPP + xr] = __uint_as_float(rb.x[m * 4 + k]);
+                for (int k = 0; k < 4; ++k) xt[tr_off<Cfg>(pc + k, xr)] = __uint_as_float(rb.x[m * 4 + k]);
             }
         }
     } else {
@@ -530,8 +545,8 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
             const int e = tid + 256 * m;
             const int xrow = e / Cfg::PP, pc = e - xrow * Cfg::PP;
             const float v = __uint_as_float(rb.x[m]);
-            if constexpr (Cfg::BF) ((uint16_t *)sm.xt)[pc * Cfg::RPP + xrow] = (uint16_t)f2bf(v);
-            else ((float *)sm.xt)[pc * Cfg::RPP + xrow] = v;
+            if constexpr (Cfg::BF) ((uint16_t *)sm.xt)[tr_off<Cfg>(pc, xrow)] = (uint16_t)f2bf(v);
+            else ((float *)sm.xt)[tr_off<Cfg>(pc, xrow)] = v;
         }
     }
     lds_barrier();
@@ -756,10 +771,10 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int n = kk * 32 + 8 * gq + 2 * k;
-                wb[n * Cfg::RPP + row] = (uint16_t)(wh[k] & 0xffffu);
-                wb[(n + 1) * Cfg::RPP + row] = (uint16_t)(wh[k] >> 16);
-                wb[Cfg::WB_PLANE + n * Cfg::RPP + row] = (uint16_t)(wl[k] & 0xffffu);
-                wb[Cfg::WB_PLANE + (n + 1) * Cfg::RPP + row] = (uint16_t)(wl[k] >> 16);
+                wb[tr_off<Cfg>(n, row)] = (uint16_t)(wh[k] & 0xffffu);
+                wb[tr_off<Cfg>(n + 1, row)] = (uint16_t)(wh[k] >> 16);
+                wb[Cfg::WB_PLANE + tr_off<Cfg>(n, row)] = (uint16_t)(wl[k] & 0xffffu);
+                wb[Cfg::WB_PLANE + tr_off<Cfg>(n + 1, row)] = (uint16_t)(wl[k] >> 16);
             }
         } else {
             if constexpr (WANT_C) {
@@ -772,7 +787,7 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
             }
             float *wb = (float *)sm.wb;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wb[(kk * 32 + 8 * gq + j) * Cfg::RPP + row] = ob[j] * wt;
+            for (int j = 0; j < 8; ++j) wb[tr_off<Cfg>(kk * 32 + 8 * gq + j, row)] = ob[j] * wt;
         }
     }
 }
@@ -824,8 +839,8 @@ __device__ __forceinline__ void mfma_state(const Sm &sm, f32x4_t (&acc)[Cfg::TPW
         if (!state_tile<Cfg>(m, nt, pt)) continue;
 #pragma unroll
         for (int kk = 0; kk < Cfg::ROWS / 32; ++kk) {
-            const int wo = (nt * 16 + l16) * Cfg::RPP + kk * 32 + 8 * gq;
-            const int xo = (pt * 16 + l16) * Cfg::RPP + kk * 32 + 8 * gq;
+            const int wo = tr_off<Cfg>(nt * 16 + l16, kk * 32 + 8 * gq);
+            const int xo = tr_off<Cfg>(pt * 16 + l16, kk * 32 + 8 * gq);
             if constexpr (Cfg::BF) {
                 FragHL wf;
                 wf.hi = *(const u32x4_t *)((const uint16_t *)sm.wb + wo);
@@ -1277,8 +1292,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             else mf = make_f(mv);
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const int xo0 = (pt * 16 + l16) * RPP + st0 * 16 + 4 * gq;
-                const int xo1 = (pt * 16 + l16) * RPP + st1 * 16 + 4 * gq;
+                const int xo0 = tr_off<Cfg>(pt * 16 + l16, st0 * 16 + 4 * gq);
+                const int xo1 = tr_off<Cfg>(pt * 16 + l16, st1 * 16 + 4 * gq);
                 if constexpr (Cfg::BF) {
                     const u32x2_t x0 = *(const u32x2_t *)((const uint16_t *)sm.xt + xo0);
                     u32x2_t x1 = {0u, 0u};
@@ -1306,13 +1321,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 const int pc = pt * 16 + l16;
                 float xv[4];
                 if constexpr (Cfg::BF) {
-                    const u32x2_t x2 = *(const u32x2_t *)((const uint16_t *)sm.xt + pc * RPP + row0);
+                    const u32x2_t x2 = *(const u32x2_t *)((const uint16_t *)sm.xt + tr_off<Cfg>(pc, row0));
                     xv[0] = __uint_as_float(x2[0] << 16);
                     xv[1] = __uint_as_float(x2[0] & 0xffff0000u);
                     xv[2] = __uint_as_float(x2[1] << 16);
                     xv[3] = __uint_as_float(x2[1] & 0xffff0000u);
                 } else {
-                    const f32x4_t x4 = *(const f32x4_t *)((const float *)sm.xt + pc * RPP + row0);
+                    const f32x4_t x4 = *(const f32x4_t *)((const float *)sm.xt + tr_off<Cfg>(pc, row0));
 #pragma unroll
                     for (int i = 0; i < 4; ++i) xv[i] = x4[i];
                 }
@@ -1332,13 +1347,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                     }
                 } else if constexpr (Cfg::BF) {
                     const uint32_t w01 = pack_bf16(yv[0], yv[1]), w23 = pack_bf16(yv[2], yv[3]);
-                    ys[(row0 + 0) * PP + pc] = (uint16_t)(w01 & 0xffffu);
-                    ys[(row0 + 1) * PP + pc] = (uint16_t)(w01 >> 16);
-                    ys[(row0 + 2) * PP + pc] = (uint16_t)(w23 & 0xffffu);
-                    ys[(row0 + 3) * PP + pc] = (uint16_t)(w23 >> 16);
+                    ys[ys_off<Cfg>(row0 + 0, pc)] = (uint16_t)(w01 & 0xffffu);
+                    ys[ys_off<Cfg>(row0 + 1, pc)] = (uint16_t)(w01 >> 16);
+                    ys[ys_off<Cfg>(row0 + 2, pc)] = (uint16_t)(w23 & 0xffffu);
+                    ys[ys_off<Cfg>(row0 + 3, pc)] = (uint16_t)(w23 >> 16);
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) ys[(row0 + i) * PP + pc] = yv[i];
+                    for (int i = 0; i < 4; ++i) ys[ys_off<Cfg>(row0 + i, pc)] = yv[i];
                 }
             }
         }
@@ -1370,14 +1385,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                     const int e = lane + 64 * m;
                     const int yr = tt * 16 + e / (PP / Cfg::XW), pc = (e % (PP / Cfg::XW)) * Cfg::XW;
                     if (yr < Rv && pc < c.Pw)
-                        *(u32x4_t *)((ET *)c.yb + (g.t0 + yr) * c.sx + pc) = *(const u32x4_t *)(ys + yr * PP + pc);
+                        *(u32x4_t *)((ET *)c.yb + (g.t0 + yr) * c.sx + pc) = *(const u32x4_t *)(ys + ys_off<Cfg>(yr, pc));
                 }
             } else {
                 for (int e = lane; e < 16 * PP; e += 64) {
                     const int yr = tt * 16 + e / PP, pc = e - (e / PP) * PP;
                     if (yr >= Rv || pc >= c.Pw) continue;
                     const int tok = tok_of(yr, c), r = yr - tok * R;
-                    ((ET *)c.yb)[(g.t0 + tok) * c.sx + (int64_t)pc * R + r] = ys[yr * PP + pc];
+                    ((ET *)c.yb)[(g.t0 + tok) * c.sx + (int64_t)pc * R + r] = ys[ys_off<Cfg>(yr, pc)];
                 }
             }
         }
@@ -1399,8 +1414,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             for (int e = tid; e < c.Pw * R; e += 256) {
                 const int pc = e / R, r = e - pc * R;
                 float xv;
-                if constexpr (Cfg::BF) xv = bf2f(((const uint16_t *)sm.xt)[pc * RPP + lrow0 + r]);
-                else xv = ((const float *)sm.xt)[pc * RPP + lrow0 + r];
+                if constexpr (Cfg::BF) xv = bf2f(((const uint16_t *)sm.xt)[tr_off<Cfg>(pc, lrow0 + r)]);
+                else xv = ((const float *)sm.xt)[tr_off<Cfg>(pc, lrow0 + r)];
                 p.px1[(bh * P + c.p0 + pc) * R + r] = xv;
             }
         }
