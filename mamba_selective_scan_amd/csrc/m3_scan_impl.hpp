@@ -174,9 +174,10 @@ struct RawBlock {
     float dt, lam, dtn, lamn;
 };
 
-// Offset of (col, row) in a [col][row] plane of pitch RPP, the row index XOR-swizzled
-// by bits 3..5 of col.  Writes of one row to 8 columns then spread over the LDS
-// banks, and every aligned group of 8 rows stays contiguous for the 16-byte reads.
+// Offset of (col, row) in the (w B~)^T plane [n][row] (pitch RPP), the row index
+// XOR-swizzled by bits 3..5 of n.  The prologue writes one row into n, n + 8, ...
+// at once; the swizzle spreads those writes over the LDS banks, and every aligned
+// group of 8 rows stays contiguous for the 16-byte operand reads.
 template <class Cfg>
 __device__ __forceinline__ int tr_off(int col, int row) {
     return col * Cfg::RPP + (row ^ (((col >> 3) & 7) << 3));
@@ -184,6 +185,9 @@ __device__ __forceinline__ int tr_off(int col, int row) {
 // Offset of (row, col) in the y staging plane [row][PP] (rank-1 and general paths):
 // columns XOR-swizzled in groups of 16 by bits 2.. of the row, so that the four
 // 4-row groups written by one instruction use different banks.
+// Offset of (p, row) in the X^T plane [p][row] (pitch RPP).
+template <class Cfg>
+__device__ __forceinline__ int xt_off(int col, int row) { return col * Cfg::RPP + row; }
 template <class Cfg>
 __device__ __forceinline__ int ys_off(int row, int col) {
     return row * Cfg::PP + (col ^ (((row >> 2) & (Cfg::PP / 16 - 1)) << 4));
@@ -512,13 +516,13 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
             const int p0 = (o * 8) / R, row0 = tok * R;
             if (R == 2) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) *(uint32_t *)(xt + tr_off<Cfg>(p0 + i, row0)) = rb.x[m * 4 + i];
+                for (int i = 0; i < 4; ++i) *(uint32_t *)(xt + xt_off<Cfg>(p0 + i, row0)) = rb.x[m * 4 + i];
             } else if (R == 4) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    *(u32x2_t *)(xt + tr_off<Cfg>(p0 + i, row0)) = u32x2_t{rb.x[m * 4 + 2 * i], rb.x[m * 4 + 2 * i + 1]};
+                    *(u32x2_t *)(xt + xt_off<Cfg>(p0 + i, row0)) = u32x2_t{rb.x[m * 4 + 2 * i], rb.x[m * 4 + 2 * i + 1]};
             } else {
-                *(u32x4_t *)(xt + tr_off<Cfg>(p0, row0)) = u32x4_t{rb.x[m * 4], rb.x[m * 4 + 1], rb.x[m * 4 + 2], rb.x[m * 4 + 3]};
+                *(u32x4_t *)(xt + xt_off<Cfg>(p0, row0)) = u32x4_t{rb.x[m * 4], rb.x[m * 4 + 1], rb.x[m * 4 + 2], rb.x[m * 4 + 3]};
             }
         }
     } else if constexpr (Cfg::VEC) {
@@ -530,13 +534,13 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
                 uint16_t *xt = (uint16_t *)sm.xt;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    xt[tr_off<Cfg>(pc + 2 * k, xr)] = (uint16_t)(rb.x[m * 4 + k] & 0xffffu);
-                    xt[tr_off<Cfg>(pc + 2 * k + 1, xr)] = (uint16_t)(rb.x[m * 4 + k] >> 16);
+                    xt[xt_off<Cfg>(pc + 2 * k, xr)] = (uint16_t)(rb.x[m * 4 + k] & 0xffffu);
+                    xt[xt_off<Cfg>(pc + 2 * k + 1, xr)] = (uint16_t)(rb.x[m * 4 + k] >> 16);
                 }
             } else {
                 float *xt = (float *)sm.xt;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) xt[tr_off<Cfg>(pc + k, xr)] = __uint_as_float(rb.x[m * 4 + k]);
+                for (int k = 0; k < 4; ++k) xt[xt_off<Cfg>(pc + k, xr)] = __uint_as_float(rb.x[m * 4 + k]);
             }
         }
     } else {
@@ -545,8 +549,8 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
             const int e = tid + 256 * m;
             const int xrow = e / Cfg::PP, pc = e - xrow * Cfg::PP;
             const float v = __uint_as_float(rb.x[m]);
-            if constexpr (Cfg::BF) ((uint16_t *)sm.xt)[tr_off<Cfg>(pc, xrow)] = (uint16_t)f2bf(v);
-            else ((float *)sm.xt)[tr_off<Cfg>(pc, xrow)] = v;
+            if constexpr (Cfg::BF) ((uint16_t *)sm.xt)[xt_off<Cfg>(pc, xrow)] = (uint16_t)f2bf(v);
+            else ((float *)sm.xt)[xt_off<Cfg>(pc, xrow)] = v;
         }
     }
     lds_barrier();
@@ -840,7 +844,7 @@ __device__ __forceinline__ void mfma_state(const Sm &sm, f32x4_t (&acc)[Cfg::TPW
 #pragma unroll
         for (int kk = 0; kk < Cfg::ROWS / 32; ++kk) {
             const int wo = tr_off<Cfg>(nt * 16 + l16, kk * 32 + 8 * gq);
-            const int xo = tr_off<Cfg>(pt * 16 + l16, kk * 32 + 8 * gq);
+            const int xo = xt_off<Cfg>(pt * 16 + l16, kk * 32 + 8 * gq);
             if constexpr (Cfg::BF) {
                 FragHL wf;
                 wf.hi = *(const u32x4_t *)((const uint16_t *)sm.wb + wo);
@@ -1292,8 +1296,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             else mf = make_f(mv);
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const int xo0 = tr_off<Cfg>(pt * 16 + l16, st0 * 16 + 4 * gq);
-                const int xo1 = tr_off<Cfg>(pt * 16 + l16, st1 * 16 + 4 * gq);
+                const int xo0 = xt_off<Cfg>(pt * 16 + l16, st0 * 16 + 4 * gq);
+                const int xo1 = xt_off<Cfg>(pt * 16 + l16, st1 * 16 + 4 * gq);
                 if constexpr (Cfg::BF) {
                     const u32x2_t x0 = *(const u32x2_t *)((const uint16_t *)sm.xt + xo0);
                     u32x2_t x1 = {0u, 0u};
@@ -1321,13 +1325,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 const int pc = pt * 16 + l16;
                 float xv[4];
                 if constexpr (Cfg::BF) {
-                    const u32x2_t x2 = *(const u32x2_t *)((const uint16_t *)sm.xt + tr_off<Cfg>(pc, row0));
+                    const u32x2_t x2 = *(const u32x2_t *)((const uint16_t *)sm.xt + xt_off<Cfg>(pc, row0));
                     xv[0] = __uint_as_float(x2[0] << 16);
                     xv[1] = __uint_as_float(x2[0] & 0xffff0000u);
                     xv[2] = __uint_as_float(x2[1] << 16);
                     xv[3] = __uint_as_float(x2[1] & 0xffff0000u);
                 } else {
-                    const f32x4_t x4 = *(const f32x4_t *)((const float *)sm.xt + tr_off<Cfg>(pc, row0));
+                    const f32x4_t x4 = *(const f32x4_t *)((const float *)sm.xt + xt_off<Cfg>(pc, row0));
 #pragma unroll
                     for (int i = 0; i < 4; ++i) xv[i] = x4[i];
                 }
@@ -1414,8 +1418,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             for (int e = tid; e < c.Pw * R; e += 256) {
                 const int pc = e / R, r = e - pc * R;
                 float xv;
-                if constexpr (Cfg::BF) xv = bf2f(((const uint16_t *)sm.xt)[tr_off<Cfg>(pc, lrow0 + r)]);
-                else xv = ((const float *)sm.xt)[tr_off<Cfg>(pc, lrow0 + r)];
+                if constexpr (Cfg::BF) xv = bf2f(((const uint16_t *)sm.xt)[xt_off<Cfg>(pc, lrow0 + r)]);
+                else xv = ((const float *)sm.xt)[xt_off<Cfg>(pc, lrow0 + r)];
                 p.px1[(bh * P + c.p0 + pc) * R + r] = xv;
             }
         }
