@@ -173,6 +173,9 @@ def test_chunk_size_invariance(io):
     (50, 1, 2, 1, 16, "f32"),          # smallest sizes
     (130, 128, 128, 1, 64, "bf16"),    # largest P and N
     (97, 64, 64, 2, 32, "bf16"),       # MIMO R=2, ragged
+    (70, 64, 64, 4, 16, "bf16"),       # MIMO R=4 (16-byte interleaved-rank loads), ragged
+    (45, 40, 48, 8, 16, "bf16"),       # MIMO R=8, N and P not powers of two
+    (60, 128, 128, 4, 16, "bf16"),     # MIMO R=4 at the largest N and P
     (40, 32, 16, 3, 16, "f32"),        # MIMO R=3 (48 rows -> 64 padded)
     (33, 16, 32, 8, 16, "f32"),        # MIMO R=8, 128 rows
 ])
