@@ -70,8 +70,8 @@ m3_status check_state(const m3_state *st, bool required) {
 
 // Blocks, segments and workspace of one scan.
 struct Plan {
-    int TB, nblk, nseg, bps, ncg;
-    size_t Sagg, lseg, pseg, cseg, total;
+    int TB, nblk, nseg, bps, ncg, nsub, sbps;
+    size_t Sagg, lseg, pseg, cseg, Hin, bseg, total;
 };
 
 TileShape tile_of(const m3_shape *s) {
@@ -104,19 +104,32 @@ Plan plan_of(const m3_shape *s) {
     if (per_cu > 4) per_cu = 4;
     const int64_t target = 256LL * per_cu;
     int64_t nseg = BH > 0 ? (target + BH - 1) / BH : 1;
-    if (nseg > 16) nseg = 16;  // the output kernel folds every earlier segment's aggregate
+    if (nseg > 16) nseg = 16;
     if (nseg > pl.nblk) nseg = pl.nblk;
     if (nseg < 1) nseg = 1;
     pl.bps = (int)((pl.nblk + nseg - 1) / nseg);
     if (pl.bps < 1) pl.bps = 1;
     pl.nseg = pl.nblk > 0 ? (pl.nblk + pl.bps - 1) / pl.bps : 1;
-    const int64_t NS = (BH / pl.ncg) * pl.nseg;
+    // state sub-segments over the blocks of segments 0 .. nseg-2: halve them (while the
+    // length stays a whole number of blocks) until about three state workgroups per unit
+    // (only with long segments: splitting then pays for the extra prefix launch; otherwise
+    // one sub-segment per segment and the output kernel folds the aggregates itself)
+    pl.sbps = pl.bps;
+    if (pl.bps >= 8)
+        while ((pl.sbps % 2) == 0 && BH * (pl.nseg - 1) * (pl.bps / pl.sbps) < 768 &&
+               (pl.nseg - 1) * (pl.bps / pl.sbps) < 32)
+            pl.sbps /= 2;
+    pl.nsub = (pl.nseg - 1) * (pl.bps / pl.sbps);
+    const int64_t BHs = BH / pl.ncg;  // (batch, head) sequences
+    const int64_t NSUB = BHs * (pl.nsub > 0 ? pl.nsub : 1);
     const int64_t np2 = ts.np / 2;
     size_t off = 0;
-    pl.Sagg = off; off = align_up(off + sizeof(float) * (size_t)(BH * pl.nseg * ts.np * ts.pp));
-    pl.lseg = off; off = align_up(off + sizeof(float) * (size_t)NS);
-    pl.pseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * np2));
-    pl.cseg = off; off = align_up(off + sizeof(float) * (size_t)(NS * np2 * 2));
+    pl.Sagg = off; off = align_up(off + sizeof(float) * (size_t)(BH * (pl.nsub > 0 ? pl.nsub : 1) * ts.np * ts.pp));
+    pl.lseg = off; off = align_up(off + sizeof(float) * (size_t)NSUB);
+    pl.pseg = off; off = align_up(off + sizeof(float) * (size_t)(NSUB * np2));
+    pl.cseg = off; off = align_up(off + sizeof(float) * (size_t)(NSUB * np2 * 2));
+    pl.Hin = off; off = align_up(off + sizeof(float) * (size_t)(BH * pl.nseg * ts.np * ts.pp));
+    pl.bseg = off; off = align_up(off + sizeof(float) * (size_t)(BHs * pl.nseg * np2));
     pl.total = (pl.nblk == 0 || BH == 0) ? 0 : off;
     return pl;
 }
@@ -152,6 +165,8 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     p.nblk = pl.nblk;
     p.nseg = pl.nseg;
     p.bps = pl.bps;
+    p.nsub = pl.nsub;
+    p.sbps = pl.sbps;
     p.ncg = pl.ncg;
     p.flags = s->flags;
     p.eps = s->norm_eps;
@@ -192,7 +207,14 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     p.pseg = reinterpret_cast<float *>(base + pl.pseg);
     p.cseg = reinterpret_cast<float *>(base + pl.cseg);
     p.np2 = ts.np / 2;
-    if (p.nseg > 1 && m3::launch_seg_state(bf, ts, p, st) != hipSuccess) return M3_EHIP;
+    p.pp = ts.pp;
+    // incoming states per segment from the prefix kernel when the state is split finer than
+    // the segments; otherwise the output kernel assembles them itself
+    const bool prefix = p.sbps < p.bps;
+    p.Hin = prefix ? reinterpret_cast<float *>(base + pl.Hin) : nullptr;
+    p.bseg = prefix ? reinterpret_cast<float *>(base + pl.bseg) : nullptr;
+    if (p.nsub > 0 && m3::launch_seg_state(bf, ts, p, st) != hipSuccess) return M3_EHIP;
+    if (prefix && m3::launch_seg_prefix(ts, p, st) != hipSuccess) return M3_EHIP;
     if (m3::launch_seg_output(bf, ts, p, st) != hipSuccess) return M3_EHIP;
     return M3_OK;
 }

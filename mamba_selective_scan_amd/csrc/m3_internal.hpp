@@ -16,8 +16,10 @@ struct ScanParams {
     int H, P, N, R;
     int TB;    // tokens per block (TB * R <= kBlockRows)
     int nblk;  // blocks per (batch, head) sequence
-    int nseg;  // segments per sequence (a workgroup walks one segment's blocks in order)
-    int bps;   // blocks per segment
+    int nseg;  // output segments per sequence (a workgroup walks one segment's blocks in order)
+    int bps;   // blocks per output segment
+    int nsub;  // state sub-segments per sequence, covering the blocks of segments 0 .. nseg-2
+    int sbps;  // blocks per state sub-segment (divides bps)
     int ncg;   // column groups: P is split across workgroups in groups of at most 64 columns
     uint32_t flags;
     float eps;
@@ -29,13 +31,19 @@ struct ScanParams {
     // carried state
     const float *h0, *pB0, *px0, *ang0;  // initial (NULL = zeros)
     float *h1, *pB1, *px1, *ang1;        // final (NULL = not requested)
-    // workspace: per-segment aggregates written by the state kernel
-    int np2;      // pairs padded to the tile height (NP / 2): pitch of pseg and cseg
-    float *Sagg;  // [B*H*ncg][nseg][NP*PP] state contributed by the segment, from zero, in its
-                  //   end frame, stored in matrix-core fragment order (tile, lane, slot)
-    float *lseg;  // [B*H][nseg]         sum of dt*A over the segment
-    float *pseg;  // [B*H][nseg][np2]    segment angle total reduced to [0, 2 pi); padded pairs 0
-    float *cseg;  // [B*H][nseg][np2][2] (cos, sin) of the segment angle total; padded pairs (1, 0)
+    // workspace
+    int np2;      // pairs padded to the tile height (NP / 2): pitch of pseg, cseg and bseg
+    int pp;       // columns per workgroup, padded (PP)
+    // per state sub-segment, written by the state kernel:
+    float *Sagg;  // [B*H*ncg][nsub][NP*PP] state contributed by the sub-segment, from zero, in
+                  //   its end frame, stored in matrix-core fragment order (tile, lane, slot)
+    float *lseg;  // [B*H][nsub]         sum of dt*A over the sub-segment
+    float *pseg;  // [B*H][nsub][np2]    sub-segment angle total reduced to [0, 2 pi); padded pairs 0
+    float *cseg;  // [B*H][nsub][np2][2] (cos, sin) of that angle; padded pairs (1, 0)
+    // per output segment, written by the prefix kernel (NULL when it does not run):
+    float *Hin;   // [B*H*ncg][nseg][NP*PP] incoming state in the frame of the segment's first
+                  //   block, fragment order
+    float *bseg;  // [B*H][nseg][np2]    global angle at the segment's start, reduced to [0, 2 pi)
 };
 
 struct StepParams {
@@ -61,6 +69,7 @@ struct TileShape {
 };
 
 hipError_t launch_seg_state(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t stream);
+hipError_t launch_seg_prefix(const TileShape &ts, const ScanParams &p, hipStream_t stream);
 hipError_t launch_seg_output(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t stream);
 size_t seg_kernel_lds_bytes(bool output, bool bf16, const TileShape &ts);
 hipError_t launch_fill_state(const ScanParams &p, hipStream_t stream);

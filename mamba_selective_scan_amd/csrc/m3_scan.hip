@@ -1,5 +1,7 @@
-// m3_scan.hip -- choice of the scan kernel variant (io type x load path).
-#include "m3_internal.hpp"
+// m3_scan.hip -- choice of the scan kernel variant (io type x load path) and the
+// segment prefix kernel.
+#define M3_WITH_PREFIX_KERNEL
+#include "m3_scan_impl.hpp"
 
 namespace m3 {
 
@@ -33,6 +35,14 @@ static hipError_t launch(bool output, bool bf16, const TileShape &ts, const Scan
 
 hipError_t launch_seg_state(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t st) {
     return launch(false, bf16, ts, p, st);
+}
+
+hipError_t launch_seg_prefix(const TileShape &ts, const ScanParams &p, hipStream_t st) {
+    const int per_q = ts.np * ts.pp / 4;
+    const int64_t nwg = p.B * p.H * (int64_t)p.ncg * ((per_q + 255) / 256);
+    if (nwg <= 0) return hipSuccess;
+    hipLaunchKernelGGL(seg_prefix_kernel, dim3((unsigned)nwg), dim3(256), 0, st, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_seg_output(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t st) {

@@ -937,15 +937,15 @@ __device__ __forceinline__ void wg_map(int64_t nbh, int ncg, int nsegk, int64_t 
 }
 
 template <class Cfg>
-__device__ __forceinline__ WgCtx make_ctx(const ScanParams &p, int nsegk) {
+__device__ __forceinline__ WgCtx make_ctx(const ScanParams &p, int nsegk, int bpu) {
     WgCtx c;
     wg_map(p.B * p.H, p.ncg, nsegk, c.bh, c.cg, c.seg);
     c.b = c.bh / p.H;
     c.h = (int)(c.bh - c.b * p.H);
     c.p0 = c.cg * Cfg::PP;
     c.Pw = min(Cfg::PP, p.P - c.p0);
-    c.blk0 = c.seg * p.bps;
-    c.blk1 = min(p.nblk, c.blk0 + p.bps);
+    c.blk0 = c.seg * bpu;
+    c.blk1 = min(p.nblk, c.blk0 + bpu);
     c.R = Cfg::VEC ? 1 : p.R;
     c.invR = 1.f / (float)c.R;
     using ET = typename Cfg::ET;
@@ -994,7 +994,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
     using Frag = typename std::conditional<Cfg::BF, FragHL, FragF>::type;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Smem<Cfg, false> sm(smem);
-    const WgCtx c = make_ctx<Cfg>(p, p.nseg - 1);
+    const WgCtx c = make_ctx<Cfg>(p, p.nsub, p.sbps);  // c.seg: the state sub-segment
     const int tid = threadIdx.x, lane = tid & 63;
     const int l16 = lane & 15, gq = lane >> 4;
     const int N2 = p.N / 2;
@@ -1031,8 +1031,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
     }
     // segment aggregate -> workspace, in fragment order (one 16-byte store per tile and lane)
     const int wave = tid >> 6;
-    const int64_t bs = c.bh * p.nseg + c.seg;
-    float *Sg = p.Sagg + ((c.bh * p.ncg + c.cg) * p.nseg + c.seg) * (int64_t)(NP * PP);
+    const int64_t bs = c.bh * p.nsub + c.seg;
+    float *Sg = p.Sagg + ((c.bh * p.ncg + c.cg) * p.nsub + c.seg) * (int64_t)(NP * PP);
 #pragma unroll
     for (int m = 0; m < Cfg::TPW; ++m) {
         int nt, pt;
@@ -1063,7 +1063,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     constexpr int OPP = Cfg::OPP, RPP = Cfg::RPP;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Smem<Cfg, true> sm(smem);
-    const WgCtx c = make_ctx<Cfg>(p, p.nseg);
+    const WgCtx c = make_ctx<Cfg>(p, p.nseg, p.bps);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, gq = lane >> 4;
     const int N = p.N, P = p.P, N2 = N / 2;
@@ -1077,89 +1077,103 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     BlockGeo g = block_geo(p, c.blk0);
     load_block<Io>(rb, p, c, g);
 
-    // ---- incoming state H (this wave's state fragments) and the base angle per pair
+    // ---- incoming state H (this wave's state fragments) and, for the final state, the
+    // global angle at the segment's start: from the prefix kernel when it ran, otherwise
+    // assembled here from the initial state and the earlier segments' aggregates (then one
+    // state sub-segment per output segment)
     f32x4_t hs[TPW];
-    {
-        const int64_t g0 = (c.b * p.T) * p.H + c.h;  // token 0 of the call
-        const float eta0 = (p.pB0 && p.px0) ? p.dt[g0] * (1.f - p.lam[g0]) : 0.f;
+    if (p.Hin) {
+        const float *Hg = p.Hin + ((bh * p.ncg + c.cg) * p.nseg + c.seg) * (int64_t)(NP * PP);
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             hs[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             int nt, pt;
-            if (!state_tile<Cfg>(m, nt, pt)) continue;
-            const int pp = pt * 16 + l16;
+            if (state_tile<Cfg>(m, nt, pt)) hs[m] = *(const f32x4_t *)(Hg + ((size_t)(wave + 4 * m) * 64 + lane) * 4);
+        }
+        if (want_final && tid < N2) sm.base[tid] = (double)p.bseg[(bh * p.nseg + c.seg) * p.np2 + tid];
+    } else {
+        {
+            const int64_t g0 = (c.b * p.T) * p.H + c.h;  // token 0 of the call
+            const float eta0 = (p.pB0 && p.px0) ? p.dt[g0] * (1.f - p.lam[g0]) : 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int nn = nt * 16 + 4 * gq + i;
-                float v = 0.f;
-                if (pp < c.Pw && nn < N) {
-                    if (p.h0) v = p.h0[(bh * N + nn) * P + c.p0 + pp];
-                    if (p.pB0 && p.px0) {
-                        float acc = 0.f;
-                        for (int r = 0; r < R; ++r)
-                            acc += p.pB0[(bh * N + nn) * R + r] * p.px0[(bh * P + c.p0 + pp) * R + r];
-                        v += eta0 * acc;
+            for (int m = 0; m < TPW; ++m) {
+                hs[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                int nt, pt;
+                if (!state_tile<Cfg>(m, nt, pt)) continue;
+                const int pp = pt * 16 + l16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int nn = nt * 16 + 4 * gq + i;
+                    float v = 0.f;
+                    if (pp < c.Pw && nn < N) {
+                        if (p.h0) v = p.h0[(bh * N + nn) * P + c.p0 + pp];
+                        if (p.pB0 && p.px0) {
+                            float acc = 0.f;
+                            for (int r = 0; r < R; ++r)
+                                acc += p.pB0[(bh * N + nn) * R + r] * p.px0[(bh * P + c.p0 + pp) * R + r];
+                            v += eta0 * acc;
+                        }
+                    }
+                    hs[m][i] = v;
+                }
+                if (p.ang0) {
+                    // rotate by -Theta_init
+                    const int pr = (nt * 16 + 4 * gq) >> 1;
+                    float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
+                    if (pr < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr])); s0 = sc_[0]; c0 = sc_[1]; }
+                    if (pr + 1 < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
+                    rot_neg(hs[m], c0, s0, c1, s1);
+                }
+            }
+            // fold the earlier segments: H <- Rot(-Phi_s) (exp(l_s) H) + S_s (the aggregate is
+            // already in its segment's end frame).  FB segments at a time, so that their loads are
+            // in flight together; slots past the last segment reload it and are not applied.
+            constexpr int FB = TPW <= 2 ? 4 : (TPW <= 4 ? 2 : 1);
+            const int64_t q = bh * p.ncg + c.cg;
+            for (int s0 = 0; s0 < c.seg; s0 += FB) {
+                f32x4_t sv[FB][TPW], cs[FB][TPW];
+                float lg[FB];
+#pragma unroll
+                for (int k = 0; k < FB; ++k) {
+                    const int s2 = min(s0 + k, c.seg - 1);
+                    const int64_t bs = bh * p.nsub + s2;
+                    lg[k] = p.lseg[bs];
+                    const float *Sg = p.Sagg + (q * p.nsub + s2) * (int64_t)(NP * PP);
+#pragma unroll
+                    for (int m = 0; m < TPW; ++m) {
+                        int nt, pt;
+                        if (!state_tile<Cfg>(m, nt, pt)) continue;
+                        sv[k][m] = *(const f32x4_t *)(Sg + ((size_t)(wave + 4 * m) * 64 + lane) * 4);
+                        // (cos, sin) of pairs nt*8 + 2*gq and the next one
+                        cs[k][m] = *(const f32x4_t *)(p.cseg + (bs * p.np2 + nt * 8 + 2 * gq) * 2);
                     }
                 }
-                hs[m][i] = v;
-            }
-            if (p.ang0) {
-                // rotate by -Theta_init
-                const int pr = (nt * 16 + 4 * gq) >> 1;
-                float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
-                if (pr < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr])); s0 = sc_[0]; c0 = sc_[1]; }
-                if (pr + 1 < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
-                rot_neg(hs[m], c0, s0, c1, s1);
-            }
-        }
-        // fold the earlier segments: H <- Rot(-Phi_s) (exp(l_s) H) + S_s (the aggregate is
-        // already in its segment's end frame).  FB segments at a time, so that their loads are
-        // in flight together; slots past the last segment reload it and are not applied.
-        constexpr int FB = TPW <= 2 ? 4 : (TPW <= 4 ? 2 : 1);
-        const int64_t q = bh * p.ncg + c.cg;
-        for (int s0 = 0; s0 < c.seg; s0 += FB) {
-            f32x4_t sv[FB][TPW], cs[FB][TPW];
-            float lg[FB];
 #pragma unroll
-            for (int k = 0; k < FB; ++k) {
-                const int s2 = min(s0 + k, c.seg - 1);
-                const int64_t bs = bh * p.nseg + s2;
-                lg[k] = p.lseg[bs];
-                const float *Sg = p.Sagg + (q * p.nseg + s2) * (int64_t)(NP * PP);
+                for (int k = 0; k < FB; ++k) {
+                    if (s0 + k >= c.seg) break;
+                    const float dec = __expf(lg[k]);
 #pragma unroll
-                for (int m = 0; m < TPW; ++m) {
-                    int nt, pt;
-                    if (!state_tile<Cfg>(m, nt, pt)) continue;
-                    sv[k][m] = *(const f32x4_t *)(Sg + ((size_t)(wave + 4 * m) * 64 + lane) * 4);
-                    // (cos, sin) of pairs nt*8 + 2*gq and the next one
-                    cs[k][m] = *(const f32x4_t *)(p.cseg + (bs * p.np2 + nt * 8 + 2 * gq) * 2);
+                    for (int m = 0; m < TPW; ++m) {
+                        int nt, pt;
+                        if (!state_tile<Cfg>(m, nt, pt)) continue;
+                        f32x4_t a = dec * hs[m];
+                        rot_neg(a, cs[k][m][0], cs[k][m][1], cs[k][m][2], cs[k][m][3]);
+                        hs[m] = a + sv[k][m];
+                    }
                 }
             }
+            if (tid < N2) {
+                double a = p.ang0 ? (double)p.ang0[bh * N2 + tid] : 0.0;
+                for (int s0 = 0; s0 < c.seg; s0 += FB) {
+                    float v[FB];
 #pragma unroll
-            for (int k = 0; k < FB; ++k) {
-                if (s0 + k >= c.seg) break;
-                const float dec = __expf(lg[k]);
+                    for (int k = 0; k < FB; ++k) v[k] = p.pseg[(bh * p.nsub + min(s0 + k, c.seg - 1)) * p.np2 + tid];
 #pragma unroll
-                for (int m = 0; m < TPW; ++m) {
-                    int nt, pt;
-                    if (!state_tile<Cfg>(m, nt, pt)) continue;
-                    f32x4_t a = dec * hs[m];
-                    rot_neg(a, cs[k][m][0], cs[k][m][1], cs[k][m][2], cs[k][m][3]);
-                    hs[m] = a + sv[k][m];
+                    for (int k = 0; k < FB; ++k)
+                        if (s0 + k < c.seg) a += (double)v[k];
                 }
+                sm.base[tid] = a;
             }
-        }
-        if (tid < N2) {
-            double a = p.ang0 ? (double)p.ang0[bh * N2 + tid] : 0.0;
-            for (int s0 = 0; s0 < c.seg; s0 += FB) {
-                float v[FB];
-#pragma unroll
-                for (int k = 0; k < FB; ++k) v[k] = p.pseg[(bh * p.nseg + min(s0 + k, c.seg - 1)) * p.np2 + tid];
-#pragma unroll
-                for (int k = 0; k < FB; ++k)
-                    if (s0 + k < c.seg) a += (double)v[k];
-            }
-            sm.base[tid] = a;
         }
     }
 
@@ -1448,6 +1462,104 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     }
 }
 
+#ifdef M3_WITH_PREFIX_KERNEL
+// ============================================================ prefix kernel
+// Incoming state of every output segment: the initial state (h + eta_{-1} prev_B prev_x^T,
+// rotated by -Theta_init into the frame of block 0) folded through the state sub-segments,
+//     H <- Rot(-Phi_sub) (exp(l_sub) H) + S_sub,
+// written at each output segment's start.  One thread per (sequence and column group,
+// fragment float4 of the state); the sub-segment aggregates are loaded 16 at a time.
+// Also the global angle at each segment's start (for the carried final state).
+__global__ __launch_bounds__(256) void seg_prefix_kernel(ScanParams p) {
+    const int NP = 2 * p.np2, PP = p.pp, PT = PP / 16;
+    const int per_q = NP * PP / 4;
+    const int nwg_q = (per_q + 255) / 256;
+    const int64_t q = blockIdx.x / nwg_q;
+    const int idx = (int)(blockIdx.x - q * nwg_q) * 256 + (int)threadIdx.x;
+    const int64_t bh = q / p.ncg;
+    const int cg = (int)(q - bh * p.ncg);
+    const int64_t b = bh / p.H;
+    const int h = (int)(bh - b * p.H);
+    const int N = p.N, P = p.P, N2 = N / 2, R = p.R;
+    const int p0 = cg * PP, Pw = min(PP, P - p0);
+    const int kps = p.bps / p.sbps;  // state sub-segments per output segment
+    if (idx < per_q) {
+        const int e = idx >> 6, lane = idx & 63;
+        const int nt = e / PT, pt = e - nt * PT, gq = lane >> 4, l16 = lane & 15;
+        const int pp = pt * 16 + l16;
+        f32x4_t H = {0.f, 0.f, 0.f, 0.f};
+        if (p.h0 || (p.pB0 && p.px0)) {
+            const int64_t g0 = (b * p.T) * p.H + h;  // token 0 of the call
+            const float eta0 = (p.pB0 && p.px0) ? p.dt[g0] * (1.f - p.lam[g0]) : 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int nn = nt * 16 + 4 * gq + i;
+                float v = 0.f;
+                if (pp < Pw && nn < N) {
+                    if (p.h0) v = p.h0[(bh * N + nn) * P + p0 + pp];
+                    if (p.pB0 && p.px0) {
+                        float acc = 0.f;
+                        for (int r = 0; r < R; ++r)
+                            acc += p.pB0[(bh * N + nn) * R + r] * p.px0[(bh * P + p0 + pp) * R + r];
+                        v += eta0 * acc;
+                    }
+                }
+                H[i] = v;
+            }
+        }
+        if (p.ang0) {
+            // rotate by -Theta_init
+            const int pr = (nt * 16 + 4 * gq) >> 1;
+            float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
+            if (pr < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr])); s0 = sc_[0]; c0 = sc_[1]; }
+            if (pr + 1 < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
+            rot_neg(H, c0, s0, c1, s1);
+        }
+        float *Ho = p.Hin + q * p.nseg * (int64_t)(NP * PP) + (size_t)idx * 4;
+        *(f32x4_t *)Ho = H;
+        constexpr int KB = 16;
+        for (int j0 = 0; j0 < p.nsub; j0 += KB) {
+            f32x4_t sv[KB], cs[KB];
+            float lg[KB];
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int j = min(j0 + k, p.nsub - 1);
+                const int64_t bs = bh * p.nsub + j;
+                lg[k] = p.lseg[bs];
+                sv[k] = *(const f32x4_t *)(p.Sagg + (q * p.nsub + j) * (int64_t)(NP * PP) + (size_t)idx * 4);
+                cs[k] = *(const f32x4_t *)(p.cseg + (bs * p.np2 + nt * 8 + 2 * gq) * 2);
+            }
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int j = j0 + k;
+                if (j >= p.nsub) break;
+                f32x4_t a = __expf(lg[k]) * H;
+                rot_neg(a, cs[k][0], cs[k][1], cs[k][2], cs[k][3]);
+                H = a + sv[k];
+                if ((j + 1) % kps == 0) *(f32x4_t *)(Ho + (int64_t)((j + 1) / kps) * (NP * PP)) = H;
+            }
+        }
+    }
+    if (cg == 0 && idx < p.np2) {
+        double a = (idx < N2 && p.ang0) ? (double)p.ang0[bh * N2 + idx] : 0.0;
+        p.bseg[(bh * p.nseg) * p.np2 + idx] = (float)wrap_2pi(a);
+        constexpr int KB = 16;
+        for (int j0 = 0; j0 < p.nsub; j0 += KB) {
+            float v[KB];
+#pragma unroll
+            for (int k = 0; k < KB; ++k) v[k] = p.pseg[(bh * p.nsub + min(j0 + k, p.nsub - 1)) * p.np2 + idx];
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int j = j0 + k;
+                if (j >= p.nsub) break;
+                a += (double)v[k];
+                if ((j + 1) % kps == 0) p.bseg[(bh * p.nseg + (j + 1) / kps) * p.np2 + idx] = (float)wrap_2pi(a);
+            }
+        }
+    }
+}
+#endif  // M3_WITH_PREFIX_KERNEL
+
 // ---------------------------------------------------------------- launch helpers
 template <class K>
 static hipError_t set_lds(K kern, size_t bytes) {
@@ -1469,7 +1581,7 @@ static hipError_t launch_seg_t(bool output, const ScanParams &p, hipStream_t st)
         auto kern = seg_state_kernel<Io, NP, PP, MODE>;
         hipError_t e = set_lds(kern, Cfg::STATE_BYTES);
         if (e != hipSuccess) return e;
-        const int64_t nwg = p.B * p.H * (int64_t)p.ncg * (p.nseg - 1);
+        const int64_t nwg = p.B * p.H * (int64_t)p.ncg * p.nsub;
         if (nwg <= 0) return hipSuccess;
         hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), Cfg::STATE_BYTES, st, p);
     }

@@ -205,6 +205,22 @@ def test_norm_off_and_nonzero_init(io, with_params):
     check_state(fin, f_ref, io)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_long_segments_with_state(io):
+    """Few sequences and many blocks: the state is aggregated over sub-segments shorter than
+    the output segments and a prefix pass assembles every segment's incoming state,
+    including the initial state."""
+    w = custom(batch=1, seqlen=2048, nheads=2, headdim=32, dstate=32, chunk=16, io=io, seed=2048)
+    log(f"case long segments + init {w}")
+    inp = make_inputs(w)
+    st = make_state(w, scale=0.5)
+    npar = make_norm_params(w)
+    y_ref, f_ref = oracle.scan(*oracle_args(inp), init=st, **npar)
+    y, fin = run_gpu(w, inp, init=st, final=True, npar=npar)
+    check("y", y, y_ref, io)
+    check_state(fin, f_ref, io)
+
+
 def test_empty_sequence_copies_state():
     import torch
     m3 = _m3()
