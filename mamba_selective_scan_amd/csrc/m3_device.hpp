@@ -129,4 +129,20 @@ __device__ __forceinline__ double wrap_2pi(double a) {
     return r;
 }
 
+// sin and cos of an angle with the hardware sin/cos units, which take the
+// argument in revolutions: the angle is scaled by 1 / (2 pi) and its fractional
+// part taken.  The scaling rounds to 2^-24 of the angle, below the float
+// resolution of the angle itself; callers pass block-local running sums or
+// angles already reduced to [0, 2 pi).
+__device__ __forceinline__ void fast_sincos(float a, float &s, float &c) {
+    const float rev = __builtin_amdgcn_fractf(a * 0.15915494309189535f);
+    s = __builtin_amdgcn_sinf(rev);
+    c = __builtin_amdgcn_cosf(rev);
+}
+__device__ __forceinline__ f32x2_t sincos_acc(float a) {
+    float s, c;
+    fast_sincos(a, s, c);
+    return f32x2_t{s, c};
+}
+
 }  // namespace m3

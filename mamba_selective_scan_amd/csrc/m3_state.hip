@@ -199,12 +199,142 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     (void)lane;
 }
 
+// Rank-1 decode step (P a multiple of 4).  B~ and C~ are formed by one wave each (lane n
+// holds component n, and n + 64 when N > 64): a wave reduction for the norm and a swap
+// between neighbouring lanes for the rotation of pair (2i, 2i + 1).  A third wave stages
+// x and the carried x.  The step then needs two workgroup barriers, and each thread's rows
+// of h are requested before anything else.
+template <class Io>
+__global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
+    using ET = typename Io::T;
+    constexpr int U = 4;  // h rows in flight per thread
+    const int h = blockIdx.x;
+    const int64_t b = blockIdx.y;
+    const int N = p.N, P = p.P, N2 = N / 2;
+    const int64_t bh = b * p.H + h;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int PG = P / 4, NG = 256 / PG;
+    const int pg = tid % PG, ng = tid / PG;
+    const bool upd = ng < NG;
+    float *hst = p.h + bh * (int64_t)N * P;
+    f32x4_t hv[U];
+    auto load_rows = [&](int n0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int n = n0 + u * NG;
+            if (upd && n < N) hv[u] = *(const f32x4_t *)(hst + (int64_t)n * P + pg * 4);
+        }
+    };
+    load_rows(ng);
+
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    const int NA = (N + 3) & ~3, PA = (P + 3) & ~3, N2A = (N2 + 3) & ~3;  // 16-byte aligned parts
+    float *s_bt = sm;             // [N] B~
+    float *s_ct = s_bt + NA;      // [N] C~
+    float *s_pb = s_ct + NA;      // [N] previous B~
+    float *s_x = s_pb + NA;       // [P] x
+    float *s_px = s_x + PA;       // [P] previous x
+    float *s_ang = s_px + PA;     // [N/2] new angle
+    float *s_red = s_ang + N2A;   // [NG][P] partial outputs
+    const bool bcnorm = (p.flags & 1u) != 0;
+    if (wave < 2) {
+        const ET *src = (const ET *)(wave == 0 ? p.Bm : p.Cm) + bh * N;
+        const float *gain = wave == 0 ? p.bnw : p.cnw;
+        const float *bias = wave == 0 ? p.bbias : p.cbias;
+        float v[2], ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int n = lane + 64 * k;
+            v[k] = n < N ? Io::ld(src + n) : 0.f;
+            ss += v[k] * v[k];
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        const float rs = bcnorm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int n = lane + 64 * k;
+            const bool in = n < N;
+            float u = v[k] * rs;
+            if (in && bcnorm && gain) u *= gain[n];
+            if (in && bias) u += bias[(int64_t)h * N + n];
+            // the pair's angle Theta + theta (the stored angle is kept in [0, 2 pi))
+            const int i = n >> 1;
+            const double a = in ? wrap_2pi((double)p.ang[bh * N2 + i] + (double)p.theta[bh * N2 + i]) : 0.0;
+            const f32x2_t sc = sincos_acc((float)a);  // (sin, cos)
+            const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(u), 0xB1, 0xF, 0xF, false));
+            const float out = (n & 1) ? other * sc[0] + u * sc[1] : u * sc[1] - other * sc[0];
+            if (!in) continue;
+            if (wave == 0) {
+                s_pb[n] = p.pB[bh * N + n];
+                p.pB[bh * N + n] = out;
+                s_bt[n] = out;
+                if ((n & 1) == 0) s_ang[i] = (float)a;
+            } else {
+                s_ct[n] = out;
+            }
+        }
+    } else if (wave == 2) {
+        const ET *xg = (const ET *)p.x + bh * P;
+        for (int pc = lane; pc < P; pc += 64) {
+            const float xv = Io::ld(xg + pc);
+            s_x[pc] = xv;
+            s_px[pc] = p.px[bh * P + pc];
+            p.px[bh * P + pc] = xv;
+        }
+    }
+    __syncthreads();
+    if (tid < N2) p.ang[bh * N2 + tid] = s_ang[tid];
+
+    const float dtv = p.dt[bh], lmv = p.lam[bh];
+    const float alpha = __expf(dtv * p.A[h]);
+    const float beta = alpha * dtv * (1.f - lmv), gamma = lmv * dtv;
+    if (upd) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t xv4 = *(const f32x4_t *)(s_x + pg * 4), pxv4 = *(const f32x4_t *)(s_px + pg * 4);
+        for (int n0 = ng; n0 < N; n0 += U * NG) {
+            if (n0 != ng) load_rows(n0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int n = n0 + u * NG;
+                if (n >= N) break;
+                const float pb = beta * s_pb[n], bt = gamma * s_bt[n], ct = s_ct[n];
+                f32x4_t hn;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    hn[j] = alpha * hv[u][j] + pb * pxv4[j] + bt * xv4[j];
+                    acc[j] += hn[j] * ct;
+                }
+                *(f32x4_t *)(hst + (int64_t)n * P + pg * 4) = hn;
+            }
+        }
+        *(f32x4_t *)(s_red + ng * P + pg * 4) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+    }
+    __syncthreads();
+    ET *yg = (ET *)p.y + bh * P;
+    const float Dh = p.D[h];
+    for (int e = tid; e < P; e += 256) {
+        float sacc = 0.f;
+        for (int k2 = 0; k2 < NG; ++k2) sacc += s_red[k2 * P + e];
+        Io::st(yg + e, sacc + Dh * s_x[e]);
+    }
+}
+
 static size_t step_lds_bytes(const StepParams &p, int vec) {
     const int NG = 256 / (p.P / vec);
     return sizeof(float) * (size_t)(3 * p.N * p.R + 2 * p.P * p.R + p.N + 2 * p.R + NG * p.P * p.R);
 }
 
 hipError_t launch_step(bool bf16, const StepParams &p, hipStream_t stream) {
+    if (p.R == 1 && p.P % 4 == 0) {
+        const int NG = 256 / (p.P / 4);
+        const int NA = (p.N + 3) & ~3, PA = (p.P + 3) & ~3, N2A = (p.N / 2 + 3) & ~3;
+        const size_t lds = sizeof(float) * (size_t)(3 * NA + 2 * PA + N2A + NG * p.P);
+        dim3 grid((unsigned)p.H, (unsigned)p.B);
+        if (bf16) hipLaunchKernelGGL((step_kernel_r1<IoBF16>), grid, dim3(256), lds, stream, p);
+        else hipLaunchKernelGGL((step_kernel_r1<IoF32>), grid, dim3(256), lds, stream, p);
+        return hipGetLastError();
+    }
     const int vec = (p.P % 4 == 0) ? 4 : 1;
     const size_t lds = step_lds_bytes(p, vec);
     dim3 grid((unsigned)p.H, (unsigned)p.B);

@@ -320,6 +320,31 @@ def test_step_matches_scan_mimo_f32():
     check_state(state, f_ref, "f32")
 
 
+@pytest.mark.parametrize("N,P,io", [(6, 12, "f32"), (6, 5, "f32"), (128, 128, "bf16"), (64, 64, "bf16")])
+def test_step_rank1_shapes(N, P, io):
+    """Rank-1 steps (norm gains and biases, initial state) vs the oracle's scan over the same
+    tokens: odd pair counts, P not a multiple of 4 (element path), the largest N and P."""
+    import torch
+    m3 = _m3()
+    w = custom(batch=3, seqlen=12, nheads=2, headdim=P, dstate=N, chunk=16, io=io, seed=N + P)
+    log(f"case step rank 1 {w}")
+    inp = make_inputs(w)
+    npar = make_norm_params(w)
+    st0 = make_state(w, scale=0.4)
+    y_ref, f_ref = oracle.scan(*oracle_args(inp), init=st0, **npar)
+    d = to_dev(inp, io)
+    pd = {k: torch.from_numpy(v).cuda() for k, v in npar.items()}
+    state = state_to_dev(st0)
+    ys = []
+    for t in range(w.seqlen):
+        one = {k: (v[:, t:t + 1].contiguous() if k not in ("A", "D") else v) for k, v in d.items()}
+        ys.append(m3.m3_step(one["x"], one["B"], one["C"], one["dt"], one["lam"], one["theta"],
+                             one["A"], one["D"], state, **pd))
+    torch.cuda.synchronize()
+    check("y", torch.cat(ys, 1), y_ref, io)
+    check_state(state, f_ref, io)
+
+
 def test_errors_raise():
     import torch
     m3 = _m3()
