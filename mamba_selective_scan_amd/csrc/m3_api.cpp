@@ -71,7 +71,7 @@ m3_status check_state(const m3_state *st, bool required) {
 // Blocks, segments and workspace of one scan.
 struct Plan {
     int TB, nblk, nseg, bps, ncg, nsub, sbps;
-    size_t Sagg, lseg, pseg, cseg, Hin, bseg, total;
+    size_t Sagg, lseg, pseg, cseg, Hin, total;
 };
 
 TileShape tile_of(const m3_shape *s) {
@@ -115,7 +115,7 @@ Plan plan_of(const m3_shape *s) {
     // (only with long segments: splitting then pays for the extra prefix launch; otherwise
     // one sub-segment per segment and the output kernel folds the aggregates itself)
     pl.sbps = pl.bps;
-    if (pl.bps >= 8)
+    if (pl.bps >= 8 && pl.nseg > 1)
         while ((pl.sbps % 2) == 0 && BH * (pl.nseg - 1) * (pl.bps / pl.sbps) < 768 &&
                (pl.nseg - 1) * (pl.bps / pl.sbps) < 32)
             pl.sbps /= 2;
@@ -129,7 +129,6 @@ Plan plan_of(const m3_shape *s) {
     pl.pseg = off; off = align_up(off + sizeof(float) * (size_t)(NSUB * np2));
     pl.cseg = off; off = align_up(off + sizeof(float) * (size_t)(NSUB * np2 * 2));
     pl.Hin = off; off = align_up(off + sizeof(float) * (size_t)(BH * pl.nseg * ts.np * ts.pp));
-    pl.bseg = off; off = align_up(off + sizeof(float) * (size_t)(BHs * pl.nseg * np2));
     pl.total = (pl.nblk == 0 || BH == 0) ? 0 : off;
     return pl;
 }
@@ -212,7 +211,6 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     // the segments; otherwise the output kernel assembles them itself
     const bool prefix = p.sbps < p.bps;
     p.Hin = prefix ? reinterpret_cast<float *>(base + pl.Hin) : nullptr;
-    p.bseg = prefix ? reinterpret_cast<float *>(base + pl.bseg) : nullptr;
     if (p.nsub > 0 && m3::launch_seg_state(bf, ts, p, st) != hipSuccess) return M3_EHIP;
     if (prefix && m3::launch_seg_prefix(ts, p, st) != hipSuccess) return M3_EHIP;
     if (m3::launch_seg_output(bf, ts, p, st) != hipSuccess) return M3_EHIP;

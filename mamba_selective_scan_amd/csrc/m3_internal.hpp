@@ -32,7 +32,7 @@ struct ScanParams {
     const float *h0, *pB0, *px0, *ang0;  // initial (NULL = zeros)
     float *h1, *pB1, *px1, *ang1;        // final (NULL = not requested)
     // workspace
-    int np2;      // pairs padded to the tile height (NP / 2): pitch of pseg, cseg and bseg
+    int np2;      // pairs padded to the tile height (NP / 2): pitch of pseg and cseg
     int pp;       // columns per workgroup, padded (PP)
     // per state sub-segment, written by the state kernel:
     float *Sagg;  // [B*H*ncg][nsub][NP*PP] state contributed by the sub-segment, from zero, in
@@ -43,7 +43,6 @@ struct ScanParams {
     // per output segment, written by the prefix kernel (NULL when it does not run):
     float *Hin;   // [B*H*ncg][nseg][NP*PP] incoming state in the frame of the segment's first
                   //   block, fragment order
-    float *bseg;  // [B*H][nseg][np2]    global angle at the segment's start, reduced to [0, 2 pi)
 };
 
 struct StepParams {

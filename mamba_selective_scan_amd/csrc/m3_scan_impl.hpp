@@ -1074,7 +1074,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             int nt, pt;
             if (state_tile<Cfg>(m, nt, pt)) hs[m] = *(const f32x4_t *)(Hg + ((size_t)(wave + 4 * m) * 64 + lane) * 4);
         }
-        if (want_final && tid < N2) sm.base[tid] = (double)p.bseg[(bh * p.nseg + c.seg) * p.np2 + tid];
+        if (want_final && tid < N2) {
+            // global angle at this (last) segment's start: the initial angle plus every
+            // state sub-segment's angle total
+            double a = p.ang0 ? (double)p.ang0[bh * N2 + tid] : 0.0;
+            constexpr int KB = 16;
+            for (int j0 = 0; j0 < p.nsub; j0 += KB) {
+                float v[KB];
+#pragma unroll
+                for (int k = 0; k < KB; ++k) v[k] = p.pseg[(bh * p.nsub + min(j0 + k, p.nsub - 1)) * p.np2 + tid];
+#pragma unroll
+                for (int k = 0; k < KB; ++k)
+                    if (j0 + k < p.nsub) a += (double)v[k];
+            }
+            sm.base[tid] = a;
+        }
     } else {
         {
             const int64_t g0 = (c.b * p.T) * p.H + c.h;  // token 0 of the call
@@ -1453,7 +1467,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
 //     H <- Rot(-Phi_sub) (exp(l_sub) H) + S_sub,
 // written at each output segment's start.  One thread per (sequence and column group,
 // fragment float4 of the state); the sub-segment aggregates are loaded 16 at a time.
-// Also the global angle at each segment's start (for the carried final state).
 __global__ __launch_bounds__(256) void seg_prefix_kernel(ScanParams p) {
     const int NP = 2 * p.np2, PP = p.pp, PT = PP / 16;
     const int per_q = NP * PP / 4;
@@ -1521,23 +1534,6 @@ __global__ __launch_bounds__(256) void seg_prefix_kernel(ScanParams p) {
                 rot_neg(a, cs[k][0], cs[k][1], cs[k][2], cs[k][3]);
                 H = a + sv[k];
                 if ((j + 1) % kps == 0) *(f32x4_t *)(Ho + (int64_t)((j + 1) / kps) * (NP * PP)) = H;
-            }
-        }
-    }
-    if (cg == 0 && idx < p.np2) {
-        double a = (idx < N2 && p.ang0) ? (double)p.ang0[bh * N2 + idx] : 0.0;
-        p.bseg[(bh * p.nseg) * p.np2 + idx] = (float)wrap_2pi(a);
-        constexpr int KB = 16;
-        for (int j0 = 0; j0 < p.nsub; j0 += KB) {
-            float v[KB];
-#pragma unroll
-            for (int k = 0; k < KB; ++k) v[k] = p.pseg[(bh * p.nsub + min(j0 + k, p.nsub - 1)) * p.np2 + idx];
-#pragma unroll
-            for (int k = 0; k < KB; ++k) {
-                const int j = j0 + k;
-                if (j >= p.nsub) break;
-                a += (double)v[k];
-                if ((j + 1) % kps == 0) p.bseg[(bh * p.nseg + (j + 1) / kps) * p.np2 + idx] = (float)wrap_2pi(a);
             }
         }
     }
