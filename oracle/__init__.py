@@ -34,6 +34,9 @@ class _Args(ctypes.Structure):
         ("h0", _dp), ("pB0", _dp), ("px0", _dp), ("ang0", _dp),
         ("y", _dp), ("h1", _dp), ("pB1", _dp), ("px1", _dp), ("ang1", _dp),
         ("mutation", ctypes.c_int32), ("nthreads", ctypes.c_int32),
+        ("rope_pairs", ctypes.c_int32), ("a_per_token", ctypes.c_int32),
+        ("dt_softplus", ctypes.c_int32), ("lam_sigmoid", ctypes.c_int32),
+        ("dt_bias", _dp), ("z", _dp),
     ]
 
 
@@ -71,13 +74,18 @@ def _ptr(a):
 
 def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
          b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None,
-         init=None, nthreads=None, mutation=0):
+         init=None, nthreads=None, mutation=0, rope_pairs=None,
+         dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None):
     """Run the sequential fp64 loop.
 
     Shapes: x [Bt,T,H,P] (or [Bt,T,H,P,R]), B/C [Bt,T,H,N] (or [...,N,R]),
-    dt/lam [Bt,T,H], theta [Bt,T,H,N/2], A/D [H]; optional gains [N] and
-    biases [H,R,N]; ``init`` a dict with any of h [Bt,H,N,P], prev_B
-    [Bt,H,N,R], prev_x [Bt,H,P,R], angle [Bt,H,N/2].
+    dt/lam [Bt,T,H], theta [Bt,T,H,NR], A [H] or [Bt,T,H] (a per-token decay
+    rate, recognised by its shape), D [H]; optional gains [N] and biases
+    [H,R,N]; ``init`` a dict with any of h [Bt,H,N,P], prev_B [Bt,H,N,R],
+    prev_x [Bt,H,P,R], angle [Bt,H,NR].  NR = ``rope_pairs`` (default N/2:
+    every pair rotates).  ``dt_softplus``/``dt_bias`` and ``lam_sigmoid``
+    take dt and lam as raw values; ``z`` (shaped like x) gates the output
+    with silu(z).
 
     Returns (y, final) with y shaped like x (float64) and final a dict of
     float64 arrays h, prev_B, prev_x, angle (angle is the unreduced running
@@ -101,16 +109,27 @@ def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
         return arr
 
     a.x, a.Bm, a.Cm = _ptr(x), _ptr(Bm), _ptr(Cm)
-    for name, arr in (("dt", dt), ("lam", lam), ("theta", theta), ("A", A), ("D", D),
-                      ("b_norm_w", b_norm_w), ("c_norm_w", c_norm_w),
-                      ("b_bias", b_bias), ("c_bias", c_bias)):
+    NR = N // 2 if rope_pairs is None else int(rope_pairs)
+    a.rope_pairs = NR
+    A = _f64(A)
+    a.a_per_token = int(A.ndim == 3)
+    if A.ndim == 3 and A.shape != (Bsz, T, H):
+        raise ValueError("oracle: a per-token A must be [B, T, H]")
+    a.dt_softplus, a.lam_sigmoid = int(bool(dt_softplus)), int(bool(lam_sigmoid))
+    if NR > 0 and np.shape(theta)[-1] != NR:
+        raise ValueError("oracle: theta must hold rope_pairs angles per token")
+    if z is not None and np.shape(z) != x.shape:
+        raise ValueError("oracle: z must be shaped like x")
+    for name, arr in (("dt", dt), ("lam", lam), ("theta", theta if NR > 0 else None), ("A", A),
+                      ("D", D), ("b_norm_w", b_norm_w), ("c_norm_w", c_norm_w),
+                      ("b_bias", b_bias), ("c_bias", c_bias), ("dt_bias", dt_bias), ("z", z)):
         put(name, arr)
     init = init or {}
     for name, key in (("h0", "h"), ("pB0", "prev_B"), ("px0", "prev_x"), ("ang0", "angle")):
         put(name, init.get(key))
     y = np.zeros(x.shape, dtype=np.float64)
     fin = dict(h=np.zeros((Bsz, H, N, P)), prev_B=np.zeros((Bsz, H, N, R)),
-               prev_x=np.zeros((Bsz, H, P, R)), angle=np.zeros((Bsz, H, N // 2)))
+               prev_x=np.zeros((Bsz, H, P, R)), angle=np.zeros((Bsz, H, NR)))
     a.y = _ptr(y)
     a.h1, a.pB1, a.px1, a.ang1 = (_ptr(fin["h"]), _ptr(fin["prev_B"]),
                                   _ptr(fin["prev_x"]), _ptr(fin["angle"]))

@@ -39,11 +39,33 @@
  *    torchmamba "API reference" (Mamba3SisoCache(angle, ssm, x_prev,
  *    b_prev)); dotLLM "Mamba3State" / k_state, v_state.
  *
+ * Options of the canonical block (all off by default):
+ *  - Partial rotation: only pairs 0 .. rope_pairs-1 rotate; theta and the
+ *    carried angle hold rope_pairs values per (token, head) and the other
+ *    pairs pass through unrotated.  dotLLM PR #136, real-weight validation
+ *    comment (rope_fraction 0.5 -> num_rope_angles 32 of d_state 128) and
+ *    "Mamba3State persistent state buffers" (cum_angle [n_head,
+ *    num_rope_angles]).  Which pairs rotate is not printed; reading taken:
+ *    the leading ones.
+ *  - Per-token decay rate: A indexed per (batch, token, head) instead of per
+ *    head, alpha_t = exp(dt_t A_t).  dotLLM PR #136, Stage D3 comment
+ *    (per-(T,H) ADT from dd_A).
+ *  - Input activations: dt_t = softplus(dt_raw + dt_bias[h]) and
+ *    lambda_t = sigmoid(lambda_raw), applied to every token the recurrence
+ *    reads (the current, the next one through beta, and token 0 of a
+ *    continued call).  dotLLM PR #136, "Stage C" (in_proj split ->
+ *    softplus/sigmoid -> Discretize).  The bias inside the softplus is the
+ *    usual Mamba dt bias; the pages name the activation only.
+ *  - Output gate: y_t = (C_t^T h_t + D x_t) * silu(z_t), silu(v) = v sigmoid(v),
+ *    z laid out like y.  dotLLM PR #136, "Stage C" (SelectiveScan -> D skip
+ *    -> silu(z) gate).
+ *
  * Layouts (row-major, last index fastest):
- *   x, y  [B, T, H, P, R]     B, C [B, T, H, N, R]     dt, lam [B, T, H]
- *   theta [B, T, H, N/2]      A, D [H]                 norm gains [N]
- *   biases [H, R, N]          h [B, H, N, P]           prev_B [B, H, N, R]
- *   prev_x [B, H, P, R]       angle [B, H, N/2]
+ *   x, y, z [B, T, H, P, R]   B, C [B, T, H, N, R]     dt, lam [B, T, H]
+ *   theta [B, T, H, NR]       A [H] (per token: [B, T, H])   D, dt_bias [H]
+ *   norm gains [N]            biases [H, R, N]         h [B, H, N, P]
+ *   prev_B [B, H, N, R]       prev_x [B, H, P, R]      angle [B, H, NR]
+ * with NR = rope_pairs (N/2 unless the rotation is partial).
  * SISO is R = 1 (the trailing unit axis is simply absent in memory).
  */
 #include <math.h>
@@ -69,7 +91,29 @@ typedef struct {
      * pin tests can show they catch it.  0 in every real use. */
     int32_t mutation;
     int32_t nthreads;
+    /* canonical-block options */
+    int32_t rope_pairs;   /* rotated pairs (0 .. N/2); theta [B,T,H,rope_pairs], angle [B,H,rope_pairs] */
+    int32_t a_per_token;  /* 1: A is [B, T, H] */
+    int32_t dt_softplus;  /* 1: dt holds raw values; dt = softplus(dt + dt_bias[h]) */
+    int32_t lam_sigmoid;  /* 1: lam holds raw values; lambda = sigmoid(lam) */
+    const double *dt_bias; /* [H] or NULL (= 0) */
+    const double *z;       /* gate input laid out like y, or NULL (no gate) */
 } m3o_args;
+
+static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+/* dt and lambda of token index `bth` = (b, t, h) after the optional activations */
+static double dt_of(const m3o_args *a, int64_t bth, int h) {
+    double v = a->dt[bth];
+    if (a->dt_softplus) v = softplus(v + (a->dt_bias ? a->dt_bias[h] : 0.0));
+    return v;
+}
+static double lam_of(const m3o_args *a, int64_t bth) {
+    double v = a->lam[bth];
+    if (a->lam_sigmoid) v = sigmoid(v);
+    return v;
+}
 
 /* normalise + bias + rotate one raw vector v[N] (stride `stride`) */
 static void prep_vec(const m3o_args *a, const double *v, int64_t stride, const double *gain,
@@ -104,22 +148,30 @@ static void run_sequence(const m3o_args *a, int64_t b, int h) {
     double *px = calloc((size_t)P * R, sizeof(double));       /* prev x     [P][R] */
     double *Bt = calloc((size_t)N * R, sizeof(double));       /* B~_t       [N][R] */
     double *Ct = calloc((size_t)N * R, sizeof(double));       /* C~_t       [N][R] */
-    double *ang = calloc((size_t)(N2 > 0 ? N2 : 1), sizeof(double));
+    const int NR = a->rope_pairs; /* rotated pairs */
+    double *ang = calloc((size_t)(N2 > 0 ? N2 : 1), sizeof(double)); /* pairs >= NR stay 0 */
     double *col = calloc((size_t)N, sizeof(double));
     const int64_t bh = b * H + h;
     if (a->h0) memcpy(st, a->h0 + bh * N * P, sizeof(double) * N * P);
     if (a->pB0) memcpy(pB, a->pB0 + bh * N * R, sizeof(double) * N * R);
     if (a->px0) memcpy(px, a->px0 + bh * P * R, sizeof(double) * P * R);
-    if (a->ang0) memcpy(ang, a->ang0 + bh * N2, sizeof(double) * N2);
+    if (a->ang0) memcpy(ang, a->ang0 + bh * NR, sizeof(double) * NR);
 
     for (int64_t t = 0; t < T; ++t) {
         const int64_t bth = (b * T + t) * H + h; /* index of (b, t, h) */
         /* cumulative angle, inclusive of this token */
         double ang_used[128];
         for (int i = 0; i < N2; ++i) {
-            ang[i] += a->theta[bth * N2 + i];
-            ang_used[i] = ang[i];
-            if (a->mutation == 2) ang_used[i] -= a->theta[bth * N2 + i]; /* planted: exclusive sum */
+            if (i < NR) {
+                ang[i] += a->theta[bth * NR + i];
+                ang_used[i] = ang[i];
+                if (a->mutation == 2) ang_used[i] -= a->theta[bth * NR + i]; /* planted: exclusive sum */
+            } else {
+                ang_used[i] = 0.0;
+            }
+        }
+        if (a->mutation == 7 && NR > 0 && NR < N2) { /* planted: the trailing pairs rotate instead */
+            for (int i = N2 - 1; i >= 0; --i) ang_used[i] = i >= N2 - NR ? ang_used[i - (N2 - NR)] : 0.0;
         }
         for (int r = 0; r < R; ++r) {
             const double *bb = a->b_bias ? a->b_bias + ((int64_t)h * R + r) * N : NULL;
@@ -129,8 +181,10 @@ static void run_sequence(const m3o_args *a, int64_t b, int h) {
             prep_vec(a, a->Cm + bth * N * R + r, R, a->c_norm_w, cb, ang_used, col);
             for (int n = 0; n < N; ++n) Ct[n * R + r] = col[n];
         }
-        const double dt = a->dt[bth], lam = a->lam[bth];
-        const double alpha = exp(dt * a->A[h]);
+        const double dt = dt_of(a, bth, h), lam = lam_of(a, bth);
+        double Av = a->a_per_token ? a->A[bth] : a->A[h];
+        if (a->mutation == 6 && a->a_per_token && t > 0) Av = a->A[bth - H]; /* planted: previous token's A */
+        const double alpha = exp(dt * Av);
         double beta = alpha * dt * (1.0 - lam);
         double gamma = lam * dt;
         if (a->mutation == 1) beta = dt * (1.0 - lam); /* planted: beta without alpha */
@@ -155,7 +209,12 @@ static void run_sequence(const m3o_args *a, int64_t b, int h) {
             for (int r = 0; r < R; ++r) {
                 double acc = 0.0;
                 for (int n = 0; n < N; ++n) acc += st[n * P + p] * Ct[n * R + r];
-                yt[p * R + r] = acc + a->D[h] * xt[p * R + r];
+                double v = acc + a->D[h] * xt[p * R + r];
+                if (a->z) {
+                    const double zv = a->z[bth * P * R + p * R + r];
+                    v *= a->mutation == 8 ? sigmoid(zv) : zv * sigmoid(zv); /* planted (8): sigmoid gate */
+                }
+                yt[p * R + r] = v;
             }
         }
         memcpy(pB, Bt, sizeof(double) * N * R);
@@ -164,7 +223,7 @@ static void run_sequence(const m3o_args *a, int64_t b, int h) {
     if (a->h1) memcpy(a->h1 + bh * N * P, st, sizeof(double) * N * P);
     if (a->pB1) memcpy(a->pB1 + bh * N * R, pB, sizeof(double) * N * R);
     if (a->px1) memcpy(a->px1 + bh * P * R, px, sizeof(double) * P * R);
-    if (a->ang1) memcpy(a->ang1 + bh * N2, ang, sizeof(double) * N2);
+    if (a->ang1) memcpy(a->ang1 + bh * NR, ang, sizeof(double) * NR);
     free(st); free(pB); free(px); free(Bt); free(Ct); free(ang); free(col);
 }
 
@@ -180,7 +239,7 @@ static void *worker(void *p) {
 /* Returns 0 on success, -1 on unsupported sizes. */
 int m3o_scan(const m3o_args *a) {
     if (a->dstate <= 0 || (a->dstate & 1) || a->dstate > 256 || a->rank < 1 || a->headdim <= 0 ||
-        a->nheads <= 0 || a->batch < 0 || a->seqlen < 0)
+        a->nheads <= 0 || a->batch < 0 || a->seqlen < 0 || a->rope_pairs < 0 || a->rope_pairs > a->dstate / 2)
         return -1;
     const int64_t nseq = a->batch * a->nheads;
     int nt = a->nthreads > 0 ? a->nthreads : 1;

@@ -112,15 +112,18 @@ def make_inputs(w: Workload, *, batch: int | None = None, seqlen: int | None = N
 
 
 def make_state(w: Workload, *, batch: int | None = None, seed: int = 1234,
-               scale: float = 1.0) -> dict:
-    """A random carried state (h, prev_B, prev_x, angle) for streaming tests."""
+               scale: float = 1.0, rope_pairs: int | None = None) -> dict:
+    """A random carried state (h, prev_B, prev_x, angle) for streaming tests.
+
+    ``angle`` holds ``rope_pairs`` angles per (batch, head) (default N/2)."""
     Bsz = w.batch if batch is None else batch
     H, P, N, R = w.nheads, w.headdim, w.dstate, w.rank
     rng = np.random.default_rng(seed)
     h = (scale * rng.standard_normal((Bsz, H, N, P))).astype(np.float32)
     pB = rng.standard_normal((Bsz, H, N, R)).astype(np.float32)
     px = rng.standard_normal((Bsz, H, P, R)).astype(np.float32)
-    ang = rng.uniform(0.0, 2 * math.pi, (Bsz, H, N // 2)).astype(np.float32)
+    nr = N // 2 if rope_pairs is None else rope_pairs
+    ang = rng.uniform(0.0, 2 * math.pi, (Bsz, H, nr)).astype(np.float32)
     return dict(h=h, prev_B=pB, prev_x=px, angle=ang)
 
 
@@ -141,3 +144,33 @@ def custom(name="custom", **kw) -> Workload:
     base = dict(batch=1, seqlen=64, nheads=2, headdim=4, dstate=4, rank=1, chunk=16, io="f32")
     base.update(kw)
     return Workload(name, **base)
+
+
+def make_block_inputs(w: Workload, *, rope_pairs: int | None = None, batch: int | None = None,
+                      seqlen: int | None = None, seed: int | None = None) -> dict:
+    """Inputs of the canonical-block options, drawn after ``make_inputs``' recipe.
+
+    One more ``default_rng(seed + 7919)`` stream, in this order:
+
+        dt_raw  = N(0, 1) - dt_shift          [B, T, H]   (the scan applies softplus(dt_raw + dt_bias))
+        dt_bias ~ N(0, 0.25^2)                [H]
+        lam_raw ~ N(0, 1)                     [B, T, H]   (the scan applies the sigmoid)
+        A_tok   = -exp(U(0, ln 16))           [B, T, H]   per-token decay rate
+        z       ~ N(0, 1)                     like x      (gate input; bf16-rounded for bf16 io)
+        theta_p ~ U(0, pi/8)                  [B, T, H, rope_pairs]  (rope_pairs = N/4 by default)
+    """
+    Bsz = w.batch if batch is None else batch
+    T = w.seqlen if seqlen is None else seqlen
+    H, P, N, R = w.nheads, w.headdim, w.dstate, w.rank
+    nr = N // 4 if rope_pairs is None else rope_pairs
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 7919)
+    xs = (Bsz, T, H, P) if R == 1 else (Bsz, T, H, P, R)
+    dt_raw = (rng.standard_normal((Bsz, T, H)) - w.dt_shift).astype(np.float32)
+    dt_bias = (0.25 * rng.standard_normal(H)).astype(np.float32)
+    lam_raw = rng.standard_normal((Bsz, T, H)).astype(np.float32)
+    A_tok = (-np.exp(rng.uniform(0.0, math.log(16.0), (Bsz, T, H)))).astype(np.float32)
+    z = rng.standard_normal(xs, dtype=np.float32)
+    theta_p = rng.uniform(0.0, math.pi / 8, (Bsz, T, H, nr)).astype(np.float32)
+    if w.io == "bf16":
+        z = bf16_round(z)
+    return dict(dt_raw=dt_raw, dt_bias=dt_bias, lam_raw=lam_raw, A_tok=A_tok, z=z, theta_p=theta_p)

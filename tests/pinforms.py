@@ -56,16 +56,20 @@ def quadratic(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
     """
     x, B, C, siso = _as_mimo(x, B, C)
     Bsz, T, H, P, R = x.shape
+    N = B.shape[3]
     assert T <= 16, "quadratic form is for short sequences"
     y = np.zeros((Bsz, T, H, P, R))
     for b in range(Bsz):
         for h in range(H):
-            ang = np.cumsum(theta[b, :, h, :].astype(np.float64), axis=0)  # inclusive
+            ang = np.zeros((T, N // 2))
+            NR = np.shape(theta)[-1]  # rotated pairs: the leading NR (all N/2 by default)
+            ang[:, :NR] = np.cumsum(np.asarray(theta, np.float64)[b, :, h, :], axis=0)  # inclusive
             Bt = rotate(prep_hat(B[b, :, h], gains[0], biases[0], h, bcnorm, eps), ang)
             Ct = rotate(prep_hat(C[b, :, h], gains[1], biases[1], h, bcnorm, eps), ang)
             d = dt[b, :, h].astype(np.float64)
             la = lam[b, :, h].astype(np.float64)
-            al = np.exp(d * float(A[h]))
+            Ah = np.asarray(A, np.float64)
+            al = np.exp(d * (Ah[b, :, h] if Ah.ndim == 3 else Ah[h]))  # A per token or per head
             be = al * d * (1.0 - la)
             ga = la * d
             S = np.zeros((T, T))
@@ -108,14 +112,18 @@ def complex_state_loop(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
             Cc = Ch[:, 0::2, :] + 1j * Ch[:, 1::2, :]
             g = np.zeros((N // 2, P), dtype=np.complex128)
             prev = np.zeros((N // 2, P), dtype=np.complex128)
+            Ah = np.asarray(A, np.float64)
+            NR = np.shape(theta)[-1]  # pairs past NR do not rotate
             for t in range(T):
                 d = float(dt[b, t, h]); la = float(lam[b, t, h])
-                al = np.exp(d * float(A[h]))
+                al = np.exp(d * (Ah[b, t, h] if Ah.ndim == 3 else Ah[h]))
                 be = al * d * (1.0 - la)
                 ga = la * d
                 xt = x[b, t, h].astype(np.float64)  # [P, R]
                 cur = Bc[t] @ xt.T                    # sum_r B^[:,r] x[:,r]^T  -> [N/2, P]
-                rot = np.exp(-1j * theta[b, t, h].astype(np.float64))[:, None]
+                th = np.zeros(N // 2)
+                th[:NR] = np.asarray(theta, np.float64)[b, t, h]
+                rot = np.exp(-1j * th)[:, None]
                 g = rot * (al * g + be * prev) + ga * cur
                 prev = cur
                 # real dot product of 2-vectors: Re(conj(c) * g)
