@@ -30,15 +30,30 @@
  *     torchmamba "API reference" (Mamba3SisoCache(angle, ssm, x_prev,
  *     b_prev)); dotLLM PR #136 "Mamba3State" and k_state / v_state.
  *
+ * Options of the canonical Mamba-3 block (m3_shape.flags; all off by default):
+ *   M3_FLAG_PARTIAL_ROPE  only pairs 0 .. rope_pairs-1 rotate, the others pass through;
+ *                         theta and the carried angle hold rope_pairs values (NR below).
+ *                         dotLLM PR #136, real-weight validation comment (rope_fraction 0.5:
+ *                         32 rotated pairs of d_state 128) and "Mamba3State" (cum_angle
+ *                         [n_head, num_rope_angles]).
+ *   M3_FLAG_A_PER_TOKEN   A is a per-(batch, token, head) decay rate [B, T, H]:
+ *                         alpha_t = exp(dt_t A_t).  dotLLM PR #136, Stage D3 (per-(T,H) ADT).
+ *   M3_FLAG_DT_SOFTPLUS   dt holds raw values; the scan uses softplus(dt + dt_bias[h]).
+ *   M3_FLAG_LAM_SIGMOID   lam holds raw values; the scan uses sigmoid(lam).
+ *                         Both: dotLLM PR #136, "Stage C" (in_proj split -> softplus/sigmoid).
+ *   z != NULL             gated output y = (C~^T h + D x) * silu(z), silu(v) = v sigmoid(v).
+ *                         dotLLM PR #136, "Stage C" (D skip -> silu(z) gate).
+ *
  * Layouts: row-major, contiguous, last index fastest.
- *   x, y    [B, T, H, P]        MIMO: [B, T, H, P, R]       io dtype
+ *   x, y, z [B, T, H, P]        MIMO: [B, T, H, P, R]       io dtype
  *   Bm, Cm  [B, T, H, N]        MIMO: [B, T, H, N, R]       io dtype, raw (before the norm)
- *   dt, lam [B, T, H]           float32 (dt > 0 already activated, lam in [0, 1])
- *   theta   [B, T, H, N/2]      float32 per-step angle of pair i
- *   A, D    [H]                 float32 (A < 0)
+ *   dt, lam [B, T, H]           float32 (activated: dt > 0, lam in [0, 1]; raw with the flags)
+ *   theta   [B, T, H, NR]       float32 per-step angle of pair i (NR = N/2, or rope_pairs)
+ *   A       [H]                 float32 (A < 0); [B, T, H] with M3_FLAG_A_PER_TOKEN
+ *   D, dt_bias [H]              float32 (dt_bias may be NULL: 0)
  *   b_norm_w, c_norm_w [N]      float32 or NULL (gain 1)
  *   b_bias, c_bias     [H, R, N] float32 or NULL (bias 0)
- *   state: h [B, H, N, P], prev_B [B, H, N, R], prev_x [B, H, P, R], angle [B, H, N/2], float32
+ *   state: h [B, H, N, P], prev_B [B, H, N, R], prev_x [B, H, P, R], angle [B, H, NR], float32
  *
  * Memory: every pointer is a DEVICE pointer owned by the caller.  The
  * library allocates nothing; the scans take a caller-provided workspace of
@@ -48,8 +63,9 @@
  * different streams with different workspaces may run concurrently.
  *
  * Errors: arguments are checked on the host before any launch.  NULL
- * required pointers, bad sizes, odd N, R < 1 or pointers that are not 16-byte
- * aligned give M3_EINVAL; sizes outside the supported range give
+ * required pointers, bad sizes, odd N, R < 1, unknown flags, rope_pairs
+ * outside 0 .. N/2 or pointers that are not 16-byte aligned give M3_EINVAL;
+ * sizes outside the supported range give
  * M3_EUNSUPPORTED; a short workspace gives M3_EWORKSPACE; a failed launch
  * gives M3_EHIP.  Values are not checked on the device (NaN propagates).
  */
@@ -73,7 +89,13 @@ typedef enum {
 
 typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype; /* dtype of x, B, C and y */
 
-enum { M3_FLAG_BCNORM = 1u << 0 }; /* apply the RMSNorm over N to B and C */
+enum {
+    M3_FLAG_BCNORM = 1u << 0,       /* apply the RMSNorm over N to B and C */
+    M3_FLAG_PARTIAL_ROPE = 1u << 1, /* rotate only the leading rope_pairs pairs */
+    M3_FLAG_A_PER_TOKEN = 1u << 2,  /* A is [B, T, H] */
+    M3_FLAG_DT_SOFTPLUS = 1u << 3,  /* dt is raw: use softplus(dt + dt_bias[h]) */
+    M3_FLAG_LAM_SIGMOID = 1u << 4   /* lam is raw: use sigmoid(lam) */
+};
 
 typedef struct {
     int64_t batch;   /* B >= 0 */
@@ -87,23 +109,27 @@ typedef struct {
     int32_t io;      /* m3_dtype */
     uint32_t flags;  /* M3_FLAG_* */
     float norm_eps;  /* RMSNorm epsilon (1e-5 is the usual value) */
+    int32_t rope_pairs; /* with M3_FLAG_PARTIAL_ROPE: rotated pairs, 0 .. N/2 (ignored otherwise) */
 } m3_shape;
 
 typedef struct {
     const void *x;                    /* [B, T, H, P(, R)]  io dtype */
     const void *Bm, *Cm;              /* [B, T, H, N(, R)]  io dtype */
     const float *dt, *lam;            /* [B, T, H] */
-    const float *theta;               /* [B, T, H, N/2] */
-    const float *A, *D;               /* [H] */
+    const float *theta;               /* [B, T, H, NR]; may be NULL when NR == 0 */
+    const float *A;                   /* [H], or [B, T, H] with M3_FLAG_A_PER_TOKEN */
+    const float *D;                   /* [H] */
     const float *b_norm_w, *c_norm_w; /* [N] or NULL */
     const float *b_bias, *c_bias;     /* [H, R, N] or NULL */
+    const float *dt_bias;             /* [H] or NULL; read only with M3_FLAG_DT_SOFTPLUS */
+    const void *z;                    /* gate input laid out like y (io dtype), or NULL: no gate */
 } m3_inputs;
 
 typedef struct {
     float *h;      /* [B, H, N, P] state after the last token, in the rotated frame of Theta */
     float *prev_B; /* [B, H, N, R] B~ of the last token (normalised, biased, rotated; not scaled) */
     float *prev_x; /* [B, H, P, R] x of the last token */
-    float *angle;  /* [B, H, N/2] cumulative angle Theta of the last token, kept in [0, 2 pi) */
+    float *angle;  /* [B, H, NR] cumulative angle Theta of the last token, kept in [0, 2 pi) */
 } m3_state;
 
 /* Bytes of workspace m3_scan_siso / m3_scan_mimo need for this shape (0 when T == 0). */
@@ -147,7 +173,7 @@ m3_status m3_step(const m3_shape *shape, const m3_inputs *in, void *y, m3_state 
 /* Static description of a status code. */
 const char *m3_status_str(m3_status status);
 
-/* Library version, e.g. "0.1.0". */
+/* Library version, e.g. "0.2.0". */
 const char *m3_version(void);
 
 #ifdef __cplusplus

@@ -19,10 +19,15 @@ import os
 import torch
 
 __all__ = ["m3_scan_siso", "m3_scan_mimo", "m3_step", "m3_scan_workspace_bytes",
-           "m3_status_str", "Shape", "M3_F32", "M3_BF16", "M3_FLAG_BCNORM", "lib_path", "load"]
+           "m3_status_str", "Shape", "M3_F32", "M3_BF16", "M3_FLAG_BCNORM", "M3_FLAG_PARTIAL_ROPE",
+           "M3_FLAG_A_PER_TOKEN", "M3_FLAG_DT_SOFTPLUS", "M3_FLAG_LAM_SIGMOID", "lib_path", "load"]
 
 M3_F32, M3_BF16 = 0, 1
-M3_FLAG_BCNORM = 1
+M3_FLAG_BCNORM = 1 << 0
+M3_FLAG_PARTIAL_ROPE = 1 << 1
+M3_FLAG_A_PER_TOKEN = 1 << 2
+M3_FLAG_DT_SOFTPLUS = 1 << 3
+M3_FLAG_LAM_SIGMOID = 1 << 4
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmamba3.so")
 
@@ -32,13 +37,14 @@ class Shape(ctypes.Structure):
                 ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
                 ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("io", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float)]
+                ("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float),
+                ("rope_pairs", ctypes.c_int32)]
 
 
 class _Inputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("x", "Bm", "Cm", "dt", "lam", "theta", "A", "D",
-                 "b_norm_w", "c_norm_w", "b_bias", "c_bias")]
+                 "b_norm_w", "c_norm_w", "b_bias", "c_bias", "dt_bias", "z")]
 
 
 class _State(ctypes.Structure):
@@ -108,7 +114,7 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _shape_of(x, B, chunk, bcnorm, eps, mimo):
+def _shape_of(x, B, chunk, bcnorm, eps, mimo, opts):
     io = {torch.float32: M3_F32, torch.bfloat16: M3_BF16}.get(x.dtype)
     if io is None:
         raise TypeError("x must be float32 or bfloat16")
@@ -123,10 +129,26 @@ def _shape_of(x, B, chunk, bcnorm, eps, mimo):
         Bsz, T, H, P = x.shape
         R = 1
         N = B.shape[3]
-    return Shape(Bsz, T, H, P, N, R, int(chunk), io, M3_FLAG_BCNORM if bcnorm else 0, float(eps))
+    flags = M3_FLAG_BCNORM if bcnorm else 0
+    nr = opts.get("rope_pairs")
+    if nr is not None:
+        flags |= M3_FLAG_PARTIAL_ROPE
+    A = opts.get("A")
+    if A is not None and A.dim() == 3:
+        flags |= M3_FLAG_A_PER_TOKEN
+    if opts.get("dt_softplus"):
+        flags |= M3_FLAG_DT_SOFTPLUS
+    if opts.get("lam_sigmoid"):
+        flags |= M3_FLAG_LAM_SIGMOID
+    return Shape(Bsz, T, H, P, N, R, int(chunk), io, flags, float(eps), int(nr or 0))
 
 
-def _inputs(s: Shape, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo):
+def _rotated(s: Shape) -> int:
+    return s.rope_pairs if s.flags & M3_FLAG_PARTIAL_ROPE else s.dstate // 2
+
+
+def _inputs(s: Shape, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
+            dt_bias=None, z=None):
     dev, io_t = x.device, x.dtype
     f32 = torch.float32
     bs = (s.batch, s.seqlen, s.nheads, s.dstate) + ((s.rank,) if mimo else ())
@@ -134,22 +156,30 @@ def _inputs(s: Shape, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias,
     _need(C, "C", io_t, dev, bs)
     _need(dt, "dt", f32, dev, (s.batch, s.seqlen, s.nheads))
     _need(lam, "lam", f32, dev, (s.batch, s.seqlen, s.nheads))
-    _need(theta, "theta", f32, dev, (s.batch, s.seqlen, s.nheads, s.dstate // 2))
-    _need(A, "A", f32, dev, (s.nheads,))
+    _need(theta, "theta", f32, dev, (s.batch, s.seqlen, s.nheads, _rotated(s)))
+    if s.flags & M3_FLAG_A_PER_TOKEN:
+        _need(A, "A", f32, dev, (s.batch, s.seqlen, s.nheads))
+    else:
+        _need(A, "A", f32, dev, (s.nheads,))
     _need(D, "D", f32, dev, (s.nheads,))
+    _need(dt_bias, "dt_bias", f32, dev, (s.nheads,))
+    _need(z, "z", io_t, dev, tuple(x.shape))
     _need(b_norm_w, "b_norm_w", f32, dev, (s.dstate,))
     _need(c_norm_w, "c_norm_w", f32, dev, (s.dstate,))
     _need(b_bias, "b_bias", f32, dev, (s.nheads, s.rank, s.dstate))
     _need(c_bias, "c_bias", f32, dev, (s.nheads, s.rank, s.dstate))
     return _Inputs(*(_ptr(t) for t in (x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w,
-                                        b_bias, c_bias)))
+                                        b_bias, c_bias, dt_bias, z)))
 
 
-def new_state(batch, nheads, headdim, dstate, rank=1, device="cuda"):
-    """Zero carried state (h, prev_B, prev_x, angle) as float32 device tensors."""
+def new_state(batch, nheads, headdim, dstate, rank=1, device="cuda", rope_pairs=None):
+    """Zero carried state (h, prev_B, prev_x, angle) as float32 device tensors.
+
+    ``angle`` holds ``rope_pairs`` angles per (batch, head) (default N/2)."""
     z = lambda *sh: torch.zeros(sh, dtype=torch.float32, device=device)
+    nr = dstate // 2 if rope_pairs is None else rope_pairs
     return dict(h=z(batch, nheads, dstate, headdim), prev_B=z(batch, nheads, dstate, rank),
-                prev_x=z(batch, nheads, headdim, rank), angle=z(batch, nheads, dstate // 2))
+                prev_x=z(batch, nheads, headdim, rank), angle=z(batch, nheads, nr))
 
 
 def _state(s: Shape, st, dev, name):
@@ -158,7 +188,7 @@ def _state(s: Shape, st, dev, name):
     _need(st["h"], f"{name}.h", torch.float32, dev, (s.batch, s.nheads, s.dstate, s.headdim))
     _need(st["prev_B"], f"{name}.prev_B", torch.float32, dev, (s.batch, s.nheads, s.dstate, s.rank))
     _need(st["prev_x"], f"{name}.prev_x", torch.float32, dev, (s.batch, s.nheads, s.headdim, s.rank))
-    _need(st["angle"], f"{name}.angle", torch.float32, dev, (s.batch, s.nheads, s.dstate // 2))
+    _need(st["angle"], f"{name}.angle", torch.float32, dev, (s.batch, s.nheads, _rotated(s)))
     return _State(*(_ptr(st[k]) for k in ("h", "prev_B", "prev_x", "angle")))
 
 
@@ -168,17 +198,20 @@ def m3_scan_workspace_bytes(shape: Shape) -> int:
 
 def _scan(mimo, x, B, C, dt, lam, theta, A, D, *, chunk=64, bcnorm=True, eps=1e-5,
           b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, init=None, final=None,
-          y=None, workspace=None, stream=None):
+          y=None, workspace=None, stream=None, rope_pairs=None, dt_softplus=False, dt_bias=None,
+          lam_sigmoid=False, z=None):
     lib = load()
-    s = _shape_of(x, B, chunk, bcnorm, eps, mimo)
+    s = _shape_of(x, B, chunk, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A,
+                                                        dt_softplus=dt_softplus, lam_sigmoid=lam_sigmoid))
     _need(x, "x", x.dtype, x.device)
-    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo)
+    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
+                  dt_bias, z)
     if y is None:
         y = torch.empty_like(x)
     else:
         _need(y, "y", x.dtype, x.device, tuple(x.shape))
     if final is True:
-        final = new_state(s.batch, s.nheads, s.headdim, s.dstate, s.rank, x.device)
+        final = new_state(s.batch, s.nheads, s.headdim, s.dstate, s.rank, x.device, _rotated(s))
     st_in = _state(s, init, x.device, "init")
     st_out = _state(s, final, x.device, "final")
     need = int(lib.m3_scan_workspace_bytes(ctypes.byref(s)))
@@ -196,7 +229,11 @@ def _scan(mimo, x, B, C, dt, lam, theta, A, D, *, chunk=64, bcnorm=True, eps=1e-
 
 def m3_scan_siso(x, B, C, dt, lam, theta, A, D, **kw):
     """SISO chunked scan.  x [B,T,H,P], B/C [B,T,H,N] (float32 or bfloat16); dt/lam [B,T,H],
-    theta [B,T,H,N/2], A/D [H] float32.  ``final=True`` returns (y, final_state)."""
+    theta [B,T,H,N/2], A/D [H] float32.  ``final=True`` returns (y, final_state).
+
+    Canonical-block options: ``rope_pairs`` (rotate only the leading pairs; theta and the
+    state angle then hold that many), A of shape [B,T,H] (per-token decay rate),
+    ``dt_softplus`` / ``dt_bias`` and ``lam_sigmoid`` (raw dt / lam), ``z`` (silu gate)."""
     return _scan(False, x, B, C, dt, lam, theta, A, D, **kw)
 
 
@@ -206,17 +243,21 @@ def m3_scan_mimo(x, B, C, dt, lam, theta, A, D, **kw):
 
 
 def m3_step(x, B, C, dt, lam, theta, A, D, state, *, bcnorm=True, eps=1e-5, b_norm_w=None,
-            c_norm_w=None, b_bias=None, c_bias=None, y=None, stream=None):
+            c_norm_w=None, b_bias=None, c_bias=None, y=None, stream=None, rope_pairs=None,
+            dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None):
     """One decode step (T == 1) that updates ``state`` in place; returns y.
 
-    x [B,1,H,P] (or [B,1,H,P,R]), B/C [B,1,H,N(,R)], dt/lam [B,1,H], theta [B,1,H,N/2]."""
+    x [B,1,H,P] (or [B,1,H,P,R]), B/C [B,1,H,N(,R)], dt/lam [B,1,H], theta [B,1,H,N/2]
+    (the same options as the scans; a per-token A is [B,1,H])."""
     lib = load()
     mimo = x.dim() == 5
-    s = _shape_of(x, B, 16, bcnorm, eps, mimo)
+    s = _shape_of(x, B, 16, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A,
+                                                     dt_softplus=dt_softplus, lam_sigmoid=lam_sigmoid))
     if s.seqlen != 1:
         raise ValueError("m3_step takes exactly one token (T == 1)")
     _need(x, "x", x.dtype, x.device)
-    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo)
+    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
+                  dt_bias, z)
     if y is None:
         y = torch.empty_like(x)
     else:

@@ -20,6 +20,18 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+static_assert(M3_FLAG_BCNORM == m3::kFlagNorm && M3_FLAG_PARTIAL_ROPE == m3::kFlagPartialRope &&
+                  M3_FLAG_A_PER_TOKEN == m3::kFlagAPerToken && M3_FLAG_DT_SOFTPLUS == m3::kFlagDtSoftplus &&
+                  M3_FLAG_LAM_SIGMOID == m3::kFlagLamSigmoid,
+              "flag values of the C ABI and the kernels differ");
+constexpr uint32_t kAllFlags = M3_FLAG_BCNORM | M3_FLAG_PARTIAL_ROPE | M3_FLAG_A_PER_TOKEN | M3_FLAG_DT_SOFTPLUS |
+                               M3_FLAG_LAM_SIGMOID;
+
+// Rotated pairs: rope_pairs with M3_FLAG_PARTIAL_ROPE, otherwise all N/2.
+int rotated_pairs(const m3_shape *s) {
+    return (s->flags & M3_FLAG_PARTIAL_ROPE) ? s->rope_pairs : s->dstate / 2;
+}
+
 int pow2_at_least(int v, int lo) {
     int r = lo;
     while (r < v) r <<= 1;
@@ -33,7 +45,8 @@ m3_status check_shape(const m3_shape *s, bool step) {
         (s->dstate & 1) || s->rank < 1)
         return M3_EINVAL;
     if (s->io != M3_F32 && s->io != M3_BF16) return M3_EINVAL;
-    if ((s->flags & ~(uint32_t)M3_FLAG_BCNORM) != 0) return M3_EINVAL;
+    if ((s->flags & ~kAllFlags) != 0) return M3_EINVAL;
+    if ((s->flags & M3_FLAG_PARTIAL_ROPE) && (s->rope_pairs < 0 || s->rope_pairs > s->dstate / 2)) return M3_EINVAL;
     if ((s->flags & M3_FLAG_BCNORM) && !(s->norm_eps >= 0.f)) return M3_EINVAL;
     if (step && s->seqlen != 1) return M3_EINVAL;
     if (s->dstate > 128 || s->headdim > 128 || s->rank > 8) return M3_EUNSUPPORTED;
@@ -45,24 +58,25 @@ m3_status check_shape(const m3_shape *s, bool step) {
     return M3_OK;
 }
 
-m3_status check_inputs(const m3_inputs *in, bool need_data) {
+m3_status check_inputs(const m3_inputs *in, bool need_data, int nr) {
     if (!in) return M3_EINVAL;
     if (need_data) {
-        if (!in->x || !in->Bm || !in->Cm || !in->dt || !in->lam || !in->theta || !in->A || !in->D)
+        if (!in->x || !in->Bm || !in->Cm || !in->dt || !in->lam || (nr > 0 && !in->theta) || !in->A || !in->D)
             return M3_EINVAL;
     } else if (!in->A || !in->D) {
         return M3_EINVAL;
     }
     const void *ptrs[] = {in->x, in->Bm, in->Cm, in->dt, in->lam, in->theta, in->A, in->D,
-                          in->b_norm_w, in->c_norm_w, in->b_bias, in->c_bias};
+                          in->b_norm_w, in->c_norm_w, in->b_bias, in->c_bias, in->dt_bias, in->z};
     for (const void *p : ptrs)
         if (!aligned16(p)) return M3_EINVAL;
     return M3_OK;
 }
 
-m3_status check_state(const m3_state *st, bool required) {
+// The angle array may be NULL when no pair rotates (it then holds nothing).
+m3_status check_state(const m3_state *st, bool required, int nr) {
     if (!st) return required ? M3_EINVAL : M3_OK;
-    if (!st->h || !st->prev_B || !st->prev_x || !st->angle) return M3_EINVAL;
+    if (!st->h || !st->prev_B || !st->prev_x || (nr > 0 && !st->angle)) return M3_EINVAL;
     if (!aligned16(st->h) || !aligned16(st->prev_B) || !aligned16(st->prev_x) || !aligned16(st->angle))
         return M3_EINVAL;
     return M3_OK;
@@ -80,7 +94,8 @@ TileShape tile_of(const m3_shape *s) {
     ts.pp = pow2_at_least(s->headdim < 64 ? s->headdim : 64, 32);
     const bool v8 = (s->dstate % 8) == 0 && (s->headdim % 8) == 0;
     ts.mode = m3::kTileGen;
-    if (v8 && s->rank == 1) ts.mode = m3::kTileVec;
+    // the rank-1 path loads the angles of four pairs per 16-byte access
+    if (v8 && s->rank == 1 && rotated_pairs(s) % 4 == 0) ts.mode = m3::kTileVec;
     else if (v8 && s->io == M3_BF16 && (s->rank == 2 || s->rank == 4 || s->rank == 8)) ts.mode = m3::kTileMimo;
     return ts;
 }
@@ -138,10 +153,10 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     m3_status rc = check_shape(s, false);
     if (rc != M3_OK) return rc;
     if (!mimo && s->rank != 1) return M3_EINVAL;
-    rc = check_inputs(in, s->seqlen > 0 && s->batch > 0);
+    rc = check_inputs(in, s->seqlen > 0 && s->batch > 0, rotated_pairs(s));
     if (rc != M3_OK) return rc;
-    if ((rc = check_state(init, false)) != M3_OK) return rc;
-    if ((rc = check_state(fin, false)) != M3_OK) return rc;
+    if ((rc = check_state(init, false, rotated_pairs(s))) != M3_OK) return rc;
+    if ((rc = check_state(fin, false, rotated_pairs(s))) != M3_OK) return rc;
     if (s->seqlen > 0 && s->batch > 0 && !y) return M3_EINVAL;
     if (!aligned16(y)) return M3_EINVAL;
     const TileShape ts = tile_of(s);
@@ -169,6 +184,9 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     p.ncg = pl.ncg;
     p.flags = s->flags;
     p.eps = s->norm_eps;
+    p.nr = rotated_pairs(s);
+    p.dtbias = in->dt_bias;
+    p.z = in->z;
     p.x = in->x;
     p.Bm = in->Bm;
     p.Cm = in->Cm;
@@ -243,8 +261,8 @@ m3_status m3_scan_mimo(const m3_shape *shape, const m3_inputs *in, void *y, cons
 m3_status m3_step(const m3_shape *s, const m3_inputs *in, void *y, m3_state *state, void *stream) {
     m3_status rc = check_shape(s, true);
     if (rc != M3_OK) return rc;
-    if ((rc = check_inputs(in, s->batch > 0)) != M3_OK) return rc;
-    if ((rc = check_state(state, true)) != M3_OK) return rc;
+    if ((rc = check_inputs(in, s->batch > 0, rotated_pairs(s))) != M3_OK) return rc;
+    if ((rc = check_state(state, true, rotated_pairs(s))) != M3_OK) return rc;
     if (s->batch > 0 && !y) return M3_EINVAL;
     if (!aligned16(y)) return M3_EINVAL;
     if (s->batch == 0) return M3_OK;
@@ -257,6 +275,9 @@ m3_status m3_step(const m3_shape *s, const m3_inputs *in, void *y, m3_state *sta
     p.R = s->rank;
     p.flags = s->flags;
     p.eps = s->norm_eps;
+    p.nr = rotated_pairs(s);
+    p.dtbias = in->dt_bias;
+    p.z = in->z;
     p.x = in->x;
     p.Bm = in->Bm;
     p.Cm = in->Cm;
@@ -282,7 +303,7 @@ m3_status m3_step(const m3_shape *s, const m3_inputs *in, void *y, m3_state *sta
 const char *m3_status_str(m3_status status) {
     switch (status) {
         case M3_OK: return "M3_OK: success";
-        case M3_EINVAL: return "M3_EINVAL: invalid argument (NULL pointer, bad size, odd N, rank < 1 or misaligned pointer)";
+        case M3_EINVAL: return "M3_EINVAL: invalid argument (NULL pointer, bad size, odd N, rank < 1, unknown flag, rope_pairs outside 0..N/2 or misaligned pointer)";
         case M3_EUNSUPPORTED: return "M3_EUNSUPPORTED: size outside the supported range (N, P <= 128, R <= 8, chunk in {16,32,64,128}, chunk*R <= 128)";
         case M3_EWORKSPACE: return "M3_EWORKSPACE: workspace missing or smaller than m3_scan_workspace_bytes()";
         case M3_EHIP: return "M3_EHIP: a HIP launch failed";
@@ -290,6 +311,6 @@ const char *m3_status_str(m3_status status) {
     return "unknown m3_status";
 }
 
-const char *m3_version(void) { return "0.1.0"; }
+const char *m3_version(void) { return "0.2.0"; }
 
 }  // extern "C"

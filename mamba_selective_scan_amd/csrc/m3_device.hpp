@@ -145,4 +145,13 @@ __device__ __forceinline__ f32x2_t sincos_acc(float a) {
     return f32x2_t{s, c};
 }
 
+// ---------------------------------------------------------------- block activations
+// Input activations of the canonical block: dt = softplus(raw + bias) in the
+// overflow-safe form max(v, 0) + log1p(exp(-|v|)); lambda = sigmoid(raw) (reciprocal
+// to 1 ulp; exp overflow at raw << 0 gives 0, the limit).
+__device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v))); }
+__device__ __forceinline__ float sigmoid_f(float v) { return __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
+// Output gate silu(z) = z sigmoid(z) (exp overflow at z << 0 gives -0, the limit).
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+
 }  // namespace m3

@@ -10,6 +10,10 @@ namespace m3 {
 // Rows of one matrix-core block: (token, rank) pairs, rank fastest.
 constexpr int kBlockRows = 64;
 
+// Option bits of ScanParams::flags / StepParams::flags (the values of the public M3_FLAG_*).
+constexpr uint32_t kFlagNorm = 1u << 0, kFlagPartialRope = 1u << 1, kFlagAPerToken = 1u << 2,
+                   kFlagDtSoftplus = 1u << 3, kFlagLamSigmoid = 1u << 4;
+
 struct ScanParams {
     // sizes
     int64_t B, T;
@@ -23,10 +27,13 @@ struct ScanParams {
     int ncg;   // column groups: P is split across workgroups in groups of at most 64 columns
     uint32_t flags;
     float eps;
+    int nr;  // rotated pairs (N/2 unless the rotation is partial): theta and angle hold nr per token / sequence
     // inputs
     const void *x, *Bm, *Cm;
-    const float *dt, *lam, *theta, *A, *D;
+    const float *dt, *lam, *theta, *A, *D;  // A: [H], or [B, T, H] with kFlagAPerToken
     const float *bnw, *cnw, *bbias, *cbias;
+    const float *dtbias;  // [H] or NULL (read with kFlagDtSoftplus)
+    const void *z;        // gate input laid out like y, or NULL
     void *y;
     // carried state
     const float *h0, *pB0, *px0, *ang0;  // initial (NULL = zeros)
@@ -50,9 +57,12 @@ struct StepParams {
     int H, P, N, R;
     uint32_t flags;
     float eps;
+    int nr;  // rotated pairs
     const void *x, *Bm, *Cm;
-    const float *dt, *lam, *theta, *A, *D;
+    const float *dt, *lam, *theta, *A, *D;  // A: [H], or [B, H] (one token) with kFlagAPerToken
     const float *bnw, *cnw, *bbias, *cbias;
+    const float *dtbias;
+    const void *z;
     void *y;
     float *h, *pB, *px, *ang;
 };

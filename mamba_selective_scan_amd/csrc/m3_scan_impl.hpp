@@ -155,7 +155,14 @@ struct RawBlock {
     uint32_t c[WANT_C ? NB : 1][BW];
     uint32_t x[Cfg::MV ? Cfg::NXV * 4 : Cfg::XN];
     float th[Cfg::TN];
-    float dt, lam, dtn, lamn;
+    float dt, lam, dtn, lamn;  // raw dt, lambda of the lane's token and the next one (wave 0)
+    float av;                  // per-token decay rate of the lane's token (wave 0, kFlagAPerToken)
+};
+
+// Gate input z of one block, prefetched into registers with the same element mapping as x.
+template <class Cfg>
+struct RawZ {
+    uint32_t w[Cfg::MV ? Cfg::NXV * 4 : Cfg::XN];
 };
 
 // Offset of (col, row) in the (w B~)^T plane [n][row] (pitch RPP), the row index
@@ -214,6 +221,19 @@ struct Smem {
     }
 };
 
+// eta_{-1} = dt_0 (1 - lambda_0) of the call's first token (index g0 of [B, T, H]) after the
+// optional input activations: the weight of the carried previous B~ x^T in the first state.
+__device__ __forceinline__ float eta_first(const ScanParams &p, int64_t g0, int h) {
+    float dt = p.dt[g0], lam = p.lam[g0];
+    if (p.flags & kFlagDtSoftplus) dt = softplus_f(dt + (p.dtbias ? p.dtbias[h] : 0.f));
+    if (p.flags & kFlagLamSigmoid) lam = sigmoid_f(lam);
+    return dt * (1.f - lam);
+}
+// Carried angle of pair i at the call's start (0 without a state or for a pair that does not rotate).
+__device__ __forceinline__ double init_angle(const ScanParams &p, int64_t bh, int i) {
+    return (p.ang0 && i < p.nr) ? (double)p.ang0[bh * p.nr + i] : 0.0;
+}
+
 // Per-workgroup constants: the sequence's base pointers and token strides.
 struct WgCtx {
     int64_t b, bh;
@@ -223,7 +243,7 @@ struct WgCtx {
     const void *xb, *Bb, *Cb;  // x, B, C at (b, token 0, h) (x offset by the column group)
     const float *thb, *dtb, *lamb;
     void *yb;
-    int sx, sbc, sth, sdt;     // token strides in elements: H*P*R, H*N*R, H*N/2, H
+    int sx, sbc, sth, sdt;     // token strides in elements: H*P*R, H*N*R, H*nr, H
     float invN, eps;
     bool bcnorm, affine;
 };
@@ -270,9 +290,9 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
                     if constexpr (WANT_C) rb.c[kk][q * 4 + k] = vc[k];
                 }
             }
-            // angles of this lane's pairs: kk*16 + 4g + 0..3
+            // angles of this lane's pairs: kk*16 + 4g + 0..3 (all four rotate or none: nr % 4 == 0)
             f32x4_t tv = {0.f, 0.f, 0.f, 0.f};
-            if (ok) tv = *(const f32x4_t *)(tbase + toff + kk * 64);
+            if (ok && kk * 16 + 4 * gq < p.nr) tv = *(const f32x4_t *)(tbase + toff + kk * 64);
 #pragma unroll
             for (int k = 0; k < 4; ++k) rb.th[kk * 4 + k] = tv[k];
         }
@@ -328,7 +348,7 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
         for (int m = 0; m < Cfg::TN; ++m) {
             const int e = tid + 256 * m;
             const int tr = e / (Cfg::NP / 2), pc = e - tr * (Cfg::NP / 2);
-            rb.th[m] = (tr < Tv && pc < N2) ? p.theta[((b * T + g.t0 + tr) * H + h) * (int64_t)N2 + pc] : 0.f;
+            rb.th[m] = (tr < Tv && pc < p.nr) ? p.theta[((b * T + g.t0 + tr) * H + h) * (int64_t)p.nr + pc] : 0.f;
         }
     } else {
         // general layout (rank R, any even N, any P): element loads
@@ -361,16 +381,17 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
         for (int m = 0; m < Cfg::TN; ++m) {
             const int e = tid + 256 * m;
             const int tr = e / (Cfg::NP / 2), pc = e - tr * (Cfg::NP / 2);
-            rb.th[m] = (tr < g.Tv && pc < N2) ? p.theta[((b * T + g.t0 + tr) * H + h) * (int64_t)N2 + pc] : 0.f;
+            rb.th[m] = (tr < g.Tv && pc < p.nr) ? p.theta[((b * T + g.t0 + tr) * H + h) * (int64_t)p.nr + pc] : 0.f;
         }
     }
     if (wave == 0) {
-        rb.dt = rb.lam = rb.dtn = rb.lamn = 0.f;
+        rb.dt = rb.lam = rb.dtn = rb.lamn = rb.av = 0.f;
         const float *db = c.dtb + (int64_t)g.t0 * c.sdt, *lb = c.lamb + (int64_t)g.t0 * c.sdt;
         const uint32_t o = (uint32_t)lane * (uint32_t)c.sdt;
         if (lane < g.Tv) {
             rb.dt = db[o];
             rb.lam = lb[o];
+            if (p.flags & kFlagAPerToken) rb.av = (p.A + (c.b * T + g.t0) * H + h)[o];
             if (g.t0 + lane + 1 < T) {
                 rb.dtn = db[o + c.sdt];
                 rb.lamn = lb[o + c.sdt];
@@ -381,6 +402,85 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
     (void)h;
     (void)H;
     (void)P;
+}
+
+// Issue the loads of one block's gate input z (laid out like x and y).
+template <class Io, class Cfg>
+__device__ __forceinline__ void load_z(RawZ<Cfg> &rz, const ScanParams &p, const WgCtx &c, const BlockGeo &g) {
+    using ET = typename Io::T;
+    const int tid = threadIdx.x;
+    const int R = c.R;
+    // z at (b, token t0, h), offset by the column group like x
+    const ET *zb = (const ET *)p.z + ((c.b * p.T + g.t0) * p.H + c.h) * (int64_t)p.P * R + (int64_t)c.p0 * R;
+    if constexpr (Cfg::VEC) {
+#pragma unroll
+        for (int m = 0; m < Cfg::XN / 4; ++m) {
+            const int e = tid + 256 * m;
+            const int zr = e / (Cfg::PP / Cfg::XW), pc = (e % (Cfg::PP / Cfg::XW)) * Cfg::XW;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (zr < g.Tv && pc < c.Pw) v = *(const u32x4_t *)(zb + (int64_t)zr * c.sx + pc);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rz.w[m * 4 + k] = v[k];
+        }
+    } else if constexpr (Cfg::MV) {
+        const int xvpt = (Cfg::PP * R) >> 3;
+        const float ixvpt = 1.f / (float)xvpt;
+#pragma unroll
+        for (int m = 0; m < Cfg::NXV; ++m) {
+            const int v = tid + 256 * m;
+            const int tok = (int)(((float)v + 0.5f) * ixvpt), o = v - tok * xvpt;
+            u32x4_t vz = {0u, 0u, 0u, 0u};
+            if (tok < g.Tv && o * 8 < c.Pw * R) vz = *(const u32x4_t *)(zb + (int64_t)tok * c.sx + o * 8);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rz.w[m * 4 + k] = vz[k];
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < Cfg::XN; ++m) {
+            const int e = tid + 256 * m;
+            const int zrow = e / Cfg::PP, pc = e - zrow * Cfg::PP;
+            const int zt = tok_of(zrow, c), zrk = zrow - zt * R;
+            float v = 0.f;
+            if (zt < g.Tv && pc < c.Pw) v = Io::ld(zb + (int64_t)zt * c.sx + (int64_t)pc * R + zrk);
+            rz.w[m] = __float_as_uint(v);
+        }
+    }
+}
+
+// Write the prefetched z into the y staging area at the positions the block's y values
+// take (read back by the epilogue after two barriers; the area is free after the top one).
+template <class Cfg, class Sm>
+__device__ __forceinline__ void stage_z(const RawZ<Cfg> &rz, const Sm &sm, const WgCtx &c) {
+    using ET = typename Cfg::ET;
+    const int tid = threadIdx.x;
+    ET *ys = (ET *)sm.ys;
+    if constexpr (Cfg::VEC) {
+#pragma unroll
+        for (int m = 0; m < Cfg::XN / 4; ++m) {
+            const int e = tid + 256 * m;
+            const int zr = e / (Cfg::PP / Cfg::XW), pc = (e % (Cfg::PP / Cfg::XW)) * Cfg::XW;
+            *(u32x4_t *)(ys + ys_off<Cfg>(zr, pc)) = u32x4_t{rz.w[m * 4], rz.w[m * 4 + 1], rz.w[m * 4 + 2], rz.w[m * 4 + 3]};
+        }
+    } else if constexpr (Cfg::MV) {
+        const int R = c.R;
+        const int xvpt = (Cfg::PP * R) >> 3;
+        const float ixvpt = 1.f / (float)xvpt;
+#pragma unroll
+        for (int m = 0; m < Cfg::NXV; ++m) {
+            const int v = tid + 256 * m;
+            const int tok = (int)(((float)v + 0.5f) * ixvpt), o = v - tok * xvpt;
+            if (tok * R >= Cfg::ROWS) continue;
+            *(u32x4_t *)(ys + tok * Cfg::PP * R + o * 8) = u32x4_t{rz.w[m * 4], rz.w[m * 4 + 1], rz.w[m * 4 + 2], rz.w[m * 4 + 3]};
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < Cfg::XN; ++m) {
+            const int e = tid + 256 * m;
+            const int zrow = e / Cfg::PP, pc = e - zrow * Cfg::PP;
+            if constexpr (Cfg::BF) ys[ys_off<Cfg>(zrow, pc)] = (uint16_t)f2bf(__uint_as_float(rz.w[m]));
+            else ys[ys_off<Cfg>(zrow, pc)] = __uint_as_float(rz.w[m]);
+        }
+    }
 }
 
 // decode the 8 B or C values of one k step
@@ -454,10 +554,24 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15;
     if (wave == 0) {
-        // log alpha, gamma, eta (next token's dt (1 - lambda); 0 after the last token), scale
-        const float la = rb.dt * p.A[c.h];
-        const float ga = rb.lam * rb.dt;
-        const float sc = ga + rb.dtn * (1.f - rb.lamn);
+        // log alpha, gamma, eta (next token's dt (1 - lambda); 0 after the last token), scale;
+        // dt and lambda through the optional input activations, tokens past the end stay 0
+        float dt = rb.dt, lam = rb.lam, dtn = rb.dtn, lamn = rb.lamn;
+        if (p.flags & (kFlagDtSoftplus | kFlagLamSigmoid)) {
+            const bool cur = lane < g.Tv, nxt = cur && g.t0 + lane + 1 < p.T;
+            if (p.flags & kFlagDtSoftplus) {
+                const float bias = p.dtbias ? p.dtbias[c.h] : 0.f;
+                dt = cur ? softplus_f(dt + bias) : 0.f;
+                dtn = nxt ? softplus_f(dtn + bias) : 0.f;
+            }
+            if (p.flags & kFlagLamSigmoid) {
+                lam = cur ? sigmoid_f(lam) : 0.f;
+                lamn = nxt ? sigmoid_f(lamn) : 0.f;
+            }
+        }
+        const float la = dt * ((p.flags & kFlagAPerToken) ? rb.av : p.A[c.h]);
+        const float ga = lam * dt;
+        const float sc = ga + dtn * (1.f - lamn);
         const float cs = wave_incl_scan(la);
         const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
         sm.cs[lane] = cs;
@@ -936,18 +1050,18 @@ __device__ __forceinline__ WgCtx make_ctx(const ScanParams &p, int nsegk, int bp
     const int64_t tok0 = c.b * p.T * p.H + c.h;  // (b, token 0, h)
     c.sx = p.H * p.P * c.R;
     c.sbc = p.H * p.N * c.R;
-    c.sth = p.H * (p.N / 2);
+    c.sth = p.H * p.nr;
     c.sdt = p.H;
     c.xb = (const ET *)p.x + tok0 * p.P * c.R + (int64_t)c.p0 * c.R;
     c.Bb = (const ET *)p.Bm + tok0 * p.N * c.R;
     c.Cb = (const ET *)p.Cm + tok0 * p.N * c.R;
-    c.thb = p.theta + tok0 * (p.N / 2);
+    c.thb = p.theta + tok0 * p.nr;
     c.dtb = p.dt + tok0;
     c.lamb = p.lam + tok0;
     c.yb = (ET *)p.y + tok0 * p.P * c.R + (int64_t)c.p0 * c.R;
     c.invN = 1.f / (float)p.N;
     c.eps = p.eps;
-    c.bcnorm = (p.flags & 1u) != 0;
+    c.bcnorm = (p.flags & kFlagNorm) != 0;
     c.affine = (c.bcnorm && (p.bnw || p.cnw)) || p.bbias || p.cbias;
     return c;
 }
@@ -1037,13 +1151,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
 // ============================================================ output kernel
 // With N above 64 the LDS planes allow one workgroup per compute unit (one wave per
 // SIMD), so such variants may use the whole register file.
-template <class Io, int NP, int PP, int MODE>
+template <class Io, int NP, int PP, int MODE, bool GATE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1 : 2, NP > 64 ? 1 : 2))) void seg_output_kernel(ScanParams p) {
     using Cfg = SegCfg<Io, NP, PP, MODE>;
     constexpr bool VEC = Cfg::VEC;
     using ET = typename Io::T;
     using Frag = typename std::conditional<Cfg::BF, FragHL, FragF>::type;
     constexpr int KS = Cfg::KS, PT = Cfg::PT, TPW = Cfg::TPW;
+    // The gated variant loads z in the epilogue, so it prefetches the next block late
+    // (after the stores): the prefetched inputs then do not share the registers with z.
+    constexpr bool EARLY_PF = Cfg::EARLY_PF && !GATE;
     constexpr int OPP = Cfg::OPP, RPP = Cfg::RPP;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Smem<Cfg, true> sm(smem);
@@ -1058,7 +1175,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     // prefetch the first block while the incoming state is assembled
     stage_affine<Cfg>(sm, p, c);
     RawBlock<Cfg, true> rb;
+    RawZ<Cfg> rz;
     BlockGeo g = block_geo(p, c.blk0);
+    if constexpr (GATE) load_z<Io>(rz, p, c, g);
     load_block<Io>(rb, p, c, g);
 
     // ---- incoming state H (this wave's state fragments) and, for the final state, the
@@ -1077,7 +1196,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         if (want_final && tid < N2) {
             // global angle at this (last) segment's start: the initial angle plus every
             // state sub-segment's angle total
-            double a = p.ang0 ? (double)p.ang0[bh * N2 + tid] : 0.0;
+            double a = init_angle(p, bh, tid);
             constexpr int KB = 16;
             for (int j0 = 0; j0 < p.nsub; j0 += KB) {
                 float v[KB];
@@ -1092,7 +1211,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     } else {
         {
             const int64_t g0 = (c.b * p.T) * p.H + c.h;  // token 0 of the call
-            const float eta0 = (p.pB0 && p.px0) ? p.dt[g0] * (1.f - p.lam[g0]) : 0.f;
+            const float eta0 = (p.pB0 && p.px0) ? eta_first(p, g0, c.h) : 0.f;
 #pragma unroll
             for (int m = 0; m < TPW; ++m) {
                 hs[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1118,8 +1237,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                     // rotate by -Theta_init
                     const int pr = (nt * 16 + 4 * gq) >> 1;
                     float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
-                    if (pr < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr])); s0 = sc_[0]; c0 = sc_[1]; }
-                    if (pr + 1 < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
+                    if (pr < p.nr) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * p.nr + pr])); s0 = sc_[0]; c0 = sc_[1]; }
+                    if (pr + 1 < p.nr) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * p.nr + pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
                     rot_neg(hs[m], c0, s0, c1, s1);
                 }
             }
@@ -1161,7 +1280,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 }
             }
             if (tid < N2) {
-                double a = p.ang0 ? (double)p.ang0[bh * N2 + tid] : 0.0;
+                double a = init_angle(p, bh, tid);
                 for (int s0 = 0; s0 < c.seg; s0 += FB) {
                     float v[FB];
 #pragma unroll
@@ -1178,6 +1297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     Frag ct[KS];
     for (int blk = c.blk0; blk < c.blk1; ++blk) {
         lds_barrier();  // every wave is done with the previous block's LDS planes
+        if constexpr (GATE) stage_z<Cfg>(rz, sm, c);  // read by the epilogue after two more barriers
         write_ht<Cfg>(sm, hs);  // the state entering this block (read after two more barriers)
         if constexpr (Cfg::MV) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.bt, (uint16_t *)sm.bt + Cfg::BT_PLANE, c);
         stage_scalars_x<Io>(rb, sm, p, c, g);
@@ -1185,7 +1305,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         block_angle_totals<Cfg>(sm, p, g);
         stage_prologue<Io>(rb, sm, p, c, g, ct);
         const BlockGeo gn = block_geo(p, blk + 1);
-        if constexpr (Cfg::EARLY_PF) {
+        if constexpr (EARLY_PF) {
             if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
         }
         lds_barrier();
@@ -1328,7 +1448,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             }
         }
 
-        // ---- epilogue: y = exp(cs_t) Y_inter + Y_intra + D x  -> staging (own rows)
+        // ---- epilogue: y = exp(cs_t) Y_inter + Y_intra + D x, times silu(z) with the gate,
+        // rounded once -> staging (own rows)
         {
             ET *ys = (ET *)sm.ys;
             const float Dh = p.D[c.h];
@@ -1350,6 +1471,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 float yv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) yv[i] = yacc[pt][i] + Dh * xv[i];
+                if constexpr (GATE) {
+                    // z of these outputs, staged at the positions their y values take
+                    float zv[4];
+                    if constexpr (Cfg::MV) {
+                        u32x2_t zw;
+                        if (R == 2) {
+                            const int tk = row0 >> 1;
+                            zw[0] = *(const uint32_t *)(ys + (tk * PP + pc) * 2);
+                            zw[1] = *(const uint32_t *)(ys + ((tk + 1) * PP + pc) * 2);
+                        } else {
+                            const int tk = tok_of(row0, c), r0 = row0 - tk * R;
+                            zw = *(const u32x2_t *)(ys + (tk * PP + pc) * R + r0);
+                        }
+                        zv[0] = __uint_as_float(zw[0] << 16);
+                        zv[1] = __uint_as_float(zw[0] & 0xffff0000u);
+                        zv[2] = __uint_as_float(zw[1] << 16);
+                        zv[3] = __uint_as_float(zw[1] & 0xffff0000u);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) zv[i] = Io::ld(ys + ys_off<Cfg>(row0 + i, pc));
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) yv[i] *= silu_f(zv[i]);
+                }
                 if constexpr (Cfg::MV) {
                     // staged in the global order [token][p][rank]
                     const uint32_t w01 = pack_bf16(yv[0], yv[1]), w23 = pack_bf16(yv[2], yv[3]);
@@ -1374,8 +1519,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             }
         }
         const float cs_end = sm.cs[Cfg::ROWS - 1];
-        if constexpr (!Cfg::EARLY_PF) {
-            if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
+        if constexpr (!EARLY_PF) {
+            if (blk + 1 < c.blk1) {
+                if constexpr (GATE) load_z<Io>(rz, p, c, gn);
+                load_block<Io>(rb, p, c, gn);
+            }
         }
         // ---- y: this wave's rows, staged in its own part of the staging area (LDS
         // operations of one wave complete in order), stored as 16-byte vectors
@@ -1456,7 +1604,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 if (pp < c.Pw && nn < N) p.h1[(bh * N + nn) * P + c.p0 + pp] = a[i];
             }
         }
-        if (c.cg == 0 && tid < N2) p.ang1[bh * N2 + tid] = (float)wrap_2pi(sm.base[tid]);
+        if (c.cg == 0 && tid < p.nr) p.ang1[bh * p.nr + tid] = (float)wrap_2pi(sm.base[tid]);
     }
 }
 
@@ -1487,7 +1635,7 @@ __global__ __launch_bounds__(256) void seg_prefix_kernel(ScanParams p) {
         f32x4_t H = {0.f, 0.f, 0.f, 0.f};
         if (p.h0 || (p.pB0 && p.px0)) {
             const int64_t g0 = (b * p.T) * p.H + h;  // token 0 of the call
-            const float eta0 = (p.pB0 && p.px0) ? p.dt[g0] * (1.f - p.lam[g0]) : 0.f;
+            const float eta0 = (p.pB0 && p.px0) ? eta_first(p, g0, h) : 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int nn = nt * 16 + 4 * gq + i;
@@ -1508,8 +1656,8 @@ __global__ __launch_bounds__(256) void seg_prefix_kernel(ScanParams p) {
             // rotate by -Theta_init
             const int pr = (nt * 16 + 4 * gq) >> 1;
             float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
-            if (pr < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr])); s0 = sc_[0]; c0 = sc_[1]; }
-            if (pr + 1 < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * N2 + pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
+            if (pr < p.nr) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * p.nr + pr])); s0 = sc_[0]; c0 = sc_[1]; }
+            if (pr + 1 < p.nr) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * p.nr + pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
             rot_neg(H, c0, s0, c1, s1);
         }
         float *Ho = p.Hin + q * p.nseg * (int64_t)(NP * PP) + (size_t)idx * 4;
@@ -1552,7 +1700,8 @@ template <class Io, int NP, int PP, int MODE>
 static hipError_t launch_seg_t(bool output, const ScanParams &p, hipStream_t st) {
     using Cfg = SegCfg<Io, NP, PP, MODE>;
     if (output) {
-        auto kern = seg_output_kernel<Io, NP, PP, MODE>;
+        // variant with the silu(z) output gate when z is given
+        auto kern = p.z ? seg_output_kernel<Io, NP, PP, MODE, true> : seg_output_kernel<Io, NP, PP, MODE, false>;
         hipError_t e = set_lds(kern, Cfg::OUTPUT_BYTES);
         if (e != hipSuccess) return e;
         const int64_t nwg = p.B * p.H * (int64_t)p.ncg * p.nseg;

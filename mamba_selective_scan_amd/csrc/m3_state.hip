@@ -11,9 +11,9 @@ namespace m3 {
 // the angle is reduced to [0, 2 pi).
 __global__ __launch_bounds__(256) void fill_state_kernel(ScanParams p) {
     const int64_t nbh = p.B * p.H;
-    const int64_t nh = nbh * p.N * p.P, nb = nbh * p.N * p.R, nx = nbh * p.P * p.R, na = nbh * (p.N / 2);
+    const int64_t nh = nbh * p.N * p.P, nb = nbh * p.N * p.R, nx = nbh * p.P * p.R, na = nbh * p.nr;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool have = p.h0 && p.pB0 && p.px0 && p.ang0;
+    const bool have = p.h0 && p.pB0 && p.px0 && (p.ang0 || p.nr == 0);
     if (gid < nh) p.h1[gid] = have ? p.h0[gid] : 0.f;
     if (gid < nb) p.pB1[gid] = have ? p.pB0[gid] : 0.f;
     if (gid < nx) p.px1[gid] = have ? p.px0[gid] : 0.f;
@@ -31,6 +31,26 @@ hipError_t launch_fill_state(const ScanParams &p, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------- decode step
+// alpha, beta, gamma of the step's token: dt and lambda through the optional input
+// activations, A per head or (one token) per (batch, head).
+__device__ __forceinline__ void step_coeffs(const StepParams &p, int64_t bh, int h, float &alpha, float &beta,
+                                            float &gamma) {
+    float dt = p.dt[bh], lam = p.lam[bh];
+    if (p.flags & kFlagDtSoftplus) dt = softplus_f(dt + (p.dtbias ? p.dtbias[h] : 0.f));
+    if (p.flags & kFlagLamSigmoid) lam = sigmoid_f(lam);
+    const float A = (p.flags & kFlagAPerToken) ? p.A[bh] : p.A[h];
+    alpha = __expf(dt * A);
+    beta = alpha * dt * (1.f - lam);
+    gamma = lam * dt;
+}
+
+// y of one output element with the optional gate y * silu(z).
+template <class Io>
+__device__ __forceinline__ void store_y(const StepParams &p, int64_t off, float v) {
+    using ET = typename Io::T;
+    if (p.z) v *= silu_f(Io::ld((const ET *)p.z + off));
+    Io::st((ET *)p.y + off, v);
+}
 // One workgroup per (head, batch).  The step is the recurrence itself for one
 // token (torchmamba "Quickstart": step(u_t, cache)):
 //     Theta <- Theta + theta;  B~, C~ = Rot(Theta)(norm(B) + bias), ...
@@ -97,16 +117,18 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
         s_px[e] = p.px[bh * P * R + e];
     }
     for (int i = tid; i < N2; i += 256) {
-        const double th = wrap_2pi((double)p.ang[bh * N2 + i] + (double)p.theta[bh * N2 + i]);
-        float sn, cn;
-        sincosf((float)th, &sn, &cn);
+        float sn = 0.f, cn = 1.f;  // pairs past nr do not rotate
+        if (i < p.nr) {
+            const double th = wrap_2pi((double)p.ang[bh * p.nr + i] + (double)p.theta[bh * p.nr + i]);
+            sincosf((float)th, &sn, &cn);
+            p.ang[bh * p.nr + i] = (float)th;
+        }
         s_cos[i] = cn;
         s_sin[i] = sn;
-        p.ang[bh * N2 + i] = (float)th;
     }
     __syncthreads();
     // RMS over N per (B or C, rank): one wave per combination
-    const bool bcnorm = (p.flags & 1u) != 0;
+    const bool bcnorm = (p.flags & kFlagNorm) != 0;
     for (int cb = wave; cb < 2 * R; cb += 4) {
         const float *src = cb < R ? s_bt : s_ct;
         const int r = cb < R ? cb : cb - R;
@@ -144,9 +166,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     for (int e = tid; e < N * R; e += 256) p.pB[bh * N * R + e] = s_bt[e];
     for (int e = tid; e < P * R; e += 256) p.px[bh * P * R + e] = s_x[e];
 
-    const float dtv = p.dt[bh], lmv = p.lam[bh];
-    const float alpha = __expf(dtv * p.A[h]);
-    const float beta = alpha * dtv * (1.f - lmv), gamma = lmv * dtv;
+    float alpha, beta, gamma;
+    step_coeffs(p, bh, h, alpha, beta, gamma);
 
     float acc[VEC][RMAX];
 #pragma unroll
@@ -189,12 +210,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
                 if (r < R) s_red[(ng * P + pg * VEC + j) * R + r] = acc[j][r];
     }
     __syncthreads();
-    ET *yg = (ET *)p.y + bh * P * R;
     const float Dh = p.D[h];
     for (int e = tid; e < P * R; e += 256) {
         float s = 0.f;
         for (int k = 0; k < NG; ++k) s += s_red[k * P * R + e];
-        Io::st(yg + e, s + Dh * s_x[e]);
+        store_y<Io>(p, bh * P * R + e, s + Dh * s_x[e]);
     }
     (void)lane;
 }
@@ -236,7 +256,7 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
     float *s_px = s_x + PA;       // [P] previous x
     float *s_ang = s_px + PA;     // [N/2] new angle
     float *s_red = s_ang + N2A;   // [NG][P] partial outputs
-    const bool bcnorm = (p.flags & 1u) != 0;
+    const bool bcnorm = (p.flags & kFlagNorm) != 0;
     if (wave < 2) {
         const ET *src = (const ET *)(wave == 0 ? p.Bm : p.Cm) + bh * N;
         const float *gain = wave == 0 ? p.bnw : p.cnw;
@@ -260,7 +280,7 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
             if (in && bias) u += bias[(int64_t)h * N + n];
             // the pair's angle Theta + theta (the stored angle is kept in [0, 2 pi))
             const int i = n >> 1;
-            const double a = in ? wrap_2pi((double)p.ang[bh * N2 + i] + (double)p.theta[bh * N2 + i]) : 0.0;
+            const double a = (in && i < p.nr) ? wrap_2pi((double)p.ang[bh * p.nr + i] + (double)p.theta[bh * p.nr + i]) : 0.0;
             const f32x2_t sc = sincos_acc((float)a);  // (sin, cos)
             const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(u), 0xB1, 0xF, 0xF, false));
             const float out = (n & 1) ? other * sc[0] + u * sc[1] : u * sc[1] - other * sc[0];
@@ -284,11 +304,10 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
         }
     }
     __syncthreads();
-    if (tid < N2) p.ang[bh * N2 + tid] = s_ang[tid];
+    if (tid < p.nr) p.ang[bh * p.nr + tid] = s_ang[tid];
 
-    const float dtv = p.dt[bh], lmv = p.lam[bh];
-    const float alpha = __expf(dtv * p.A[h]);
-    const float beta = alpha * dtv * (1.f - lmv), gamma = lmv * dtv;
+    float alpha, beta, gamma;
+    step_coeffs(p, bh, h, alpha, beta, gamma);
     if (upd) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         f32x4_t xv4 = *(const f32x4_t *)(s_x + pg * 4), pxv4 = *(const f32x4_t *)(s_px + pg * 4);
@@ -311,12 +330,11 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
         *(f32x4_t *)(s_red + ng * P + pg * 4) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
     }
     __syncthreads();
-    ET *yg = (ET *)p.y + bh * P;
     const float Dh = p.D[h];
     for (int e = tid; e < P; e += 256) {
         float sacc = 0.f;
         for (int k2 = 0; k2 < NG; ++k2) sacc += s_red[k2 * P + e];
-        Io::st(yg + e, sacc + Dh * s_x[e]);
+        store_y<Io>(p, bh * P + e, sacc + Dh * s_x[e]);
     }
 }
 

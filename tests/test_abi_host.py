@@ -87,7 +87,10 @@ def _call_scan(m3, lib, s, inp_over=None, y=True, ws_bytes=None, init=None, fin=
     (dict(batch=-1), 1),
     (dict(seqlen=-5), 1),
     (dict(io=7), 1),
-    (dict(flags=0x10), 1),
+    (dict(flags=0x20), 1),         # unknown flag
+    (dict(flags=0x80000001), 1),
+    (dict(flags=3, rope_pairs=33), 1),   # more rotated pairs than N/2
+    (dict(flags=3, rope_pairs=-1), 1),
     (dict(rank=2), 1),             # SISO call with rank 2
     (dict(dstate=130), 2),         # N > 128
     (dict(headdim=129), 2),
@@ -112,6 +115,23 @@ def test_invalid_pointers_and_workspace():
     assert _call_scan(m3, lib, s, ws_bytes=100) == 3             # short workspace
     half = m3._State(h=ptrs["x"], prev_B=None, prev_x=ptrs["x"], angle=ptrs["x"])
     assert _call_scan(m3, lib, s, init=half) == 1                # incomplete state
+
+
+def test_option_pointers():
+    m3, lib = _lib()
+    _, ptrs = _fake_inputs(m3)
+    mis = ctypes.c_void_p(ptrs["x"].value + 4)
+    s = _shape(m3, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_DT_SOFTPLUS)
+    assert _call_scan(m3, lib, s, inp_over={"dt_bias": mis}) == 1   # misaligned dt bias
+    assert _call_scan(m3, lib, s, inp_over={"z": mis}) == 1         # misaligned gate input
+    # no rotated pair: theta and the state's angle may be NULL (the call then stops at the
+    # short workspace, after every pointer check)
+    s0 = _shape(m3, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_PARTIAL_ROPE, rope_pairs=0)
+    st = m3._State(h=ptrs["x"], prev_B=ptrs["x"], prev_x=ptrs["x"], angle=None)
+    assert _call_scan(m3, lib, s0, inp_over={"theta": None}, init=st, ws_bytes=100) == 3
+    s1 = _shape(m3, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_PARTIAL_ROPE, rope_pairs=1)
+    assert _call_scan(m3, lib, s1, inp_over={"theta": None}, ws_bytes=100) == 1
+    assert _call_scan(m3, lib, s1, init=st, ws_bytes=100) == 1
 
 
 def test_mimo_limits():
