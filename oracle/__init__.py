@@ -17,6 +17,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "m3_oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "m3_oracle_bwd.c"), os.path.join(_HERE, "m3_oracle.h")]
 _LIB = os.path.join(_HERE, "_m3_oracle.so")
 
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -40,12 +41,25 @@ class _Args(ctypes.Structure):
     ]
 
 
+class _BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("f", ctypes.POINTER(_Args)),
+        ("dy", _dp), ("dh1", _dp), ("dpB1", _dp), ("dpx1", _dp), ("dang1", _dp),
+        ("dx", _dp), ("dB", _dp), ("dC", _dp), ("ddt", _dp), ("dlam", _dp), ("dtheta", _dp),
+        ("dA", _dp), ("dz", _dp),
+        ("dD", _dp), ("dbnw", _dp), ("dcnw", _dp), ("dbb", _dp), ("dcb", _dp), ("ddtb", _dp),
+        ("dh0", _dp), ("dpB0", _dp), ("dpx0", _dp), ("dang0", _dp),
+        ("mutation", ctypes.c_int32),
+    ]
+
+
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (plain C, -O2, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    newest = max(os.path.getmtime(f) for f in _SRCS)
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-                               "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+                               "-fno-fast-math", *[f for f in _SRCS if f.endswith(".c")], "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -59,6 +73,8 @@ def _load():
         _lib = ctypes.CDLL(build())
         _lib.m3o_scan.argtypes = [ctypes.POINTER(_Args)]
         _lib.m3o_scan.restype = ctypes.c_int
+        _lib.m3o_scan_bwd.argtypes = [ctypes.POINTER(_BwdArgs)]
+        _lib.m3o_scan_bwd.restype = ctypes.c_int
     return _lib
 
 
@@ -139,3 +155,89 @@ def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
     if rc != 0:
         raise ValueError("oracle: unsupported sizes")
     return y, fin
+
+
+def _prepare(x, B, C, dt, lam, theta, A, D, bcnorm, eps, b_norm_w, c_norm_w, b_bias, c_bias, init,
+             nthreads, mutation, rope_pairs, dt_softplus, dt_bias, lam_sigmoid, z):
+    """The forward argument block (and the arrays it points into) for a call."""
+    x = _f64(x)
+    mimo = x.ndim == 5
+    Bsz, T, H, P = x.shape[:4]
+    R = x.shape[4] if mimo else 1
+    Bm, Cm = _f64(B), _f64(C)
+    N = Bm.shape[3]
+    keep = [x, Bm, Cm]
+    a = _Args()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.rank = Bsz, T, H, P, N, R
+    a.bcnorm, a.eps = int(bool(bcnorm)), float(eps)
+
+    def put(name, arr):
+        arr = _f64(arr)
+        keep.append(arr)
+        setattr(a, name, _ptr(arr))
+        return arr
+
+    a.x, a.Bm, a.Cm = _ptr(x), _ptr(Bm), _ptr(Cm)
+    NR = N // 2 if rope_pairs is None else int(rope_pairs)
+    a.rope_pairs = NR
+    A = _f64(A)
+    a.a_per_token = int(A.ndim == 3)
+    a.dt_softplus, a.lam_sigmoid = int(bool(dt_softplus)), int(bool(lam_sigmoid))
+    for name, arr in (("dt", dt), ("lam", lam), ("theta", theta if NR > 0 else None), ("A", A),
+                      ("D", D), ("b_norm_w", b_norm_w), ("c_norm_w", c_norm_w),
+                      ("b_bias", b_bias), ("c_bias", c_bias), ("dt_bias", dt_bias), ("z", z)):
+        put(name, arr)
+    init = init or {}
+    for name, key in (("h0", "h"), ("pB0", "prev_B"), ("px0", "prev_x"), ("ang0", "angle")):
+        put(name, init.get(key))
+    a.mutation = int(mutation)
+    a.nthreads = int(nthreads or os.cpu_count() or 1)
+    return a, keep, (Bsz, T, H, P, N, R, NR)
+
+
+def scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5,
+             b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, init=None, dfinal=None,
+             nthreads=None, mutation=0, rope_pairs=None, dt_softplus=False, dt_bias=None,
+             lam_sigmoid=False, z=None):
+    """Gradients of the scan by the fp64 reverse sweep (m3_oracle_bwd.c).
+
+    Same inputs and options as ``scan``; ``dy`` is the gradient of y (shaped like x) and
+    ``dfinal`` an optional dict of gradients of the final state (h, prev_B, prev_x, angle).
+    Returns a dict of float64 gradients, each shaped like its input: x, B, C, dt, lam,
+    theta, A (per head, or per token when A is), D, b_norm_w, c_norm_w, b_bias, c_bias
+    ([H, R, N]), dt_bias, z (when gated), and init (a dict h, prev_B, prev_x, angle).
+    Gradients of raw dt / lam when the activations are on.
+    """
+    a, keep, (Bsz, T, H, P, N, R, NR) = _prepare(
+        x, B, C, dt, lam, theta, A, D, bcnorm, eps, b_norm_w, c_norm_w, b_bias, c_bias, init,
+        nthreads, 0, rope_pairs, dt_softplus, dt_bias, lam_sigmoid, z)
+    g = _BwdArgs()
+    g.f = ctypes.pointer(a)
+    dyv = _f64(dy)
+    keep.append(dyv)
+    g.dy = _ptr(dyv)
+    dfinal = dfinal or {}
+    for name, key in (("dh1", "h"), ("dpB1", "prev_B"), ("dpx1", "prev_x"), ("dang1", "angle")):
+        arr = _f64(dfinal.get(key))
+        keep.append(arr)
+        setattr(g, name, _ptr(arr))
+    xs = np.shape(x)
+    out = dict(x=np.zeros(xs), B=np.zeros(np.shape(B)), C=np.zeros(np.shape(C)),
+               dt=np.zeros((Bsz, T, H)), lam=np.zeros((Bsz, T, H)), theta=np.zeros((Bsz, T, H, NR)),
+               A=np.zeros(np.shape(A)), D=np.zeros(H), b_norm_w=np.zeros(N), c_norm_w=np.zeros(N),
+               b_bias=np.zeros((H, R, N)), c_bias=np.zeros((H, R, N)), dt_bias=np.zeros(H),
+               z=np.zeros(xs) if z is not None else None)
+    ini = dict(h=np.zeros((Bsz, H, N, P)), prev_B=np.zeros((Bsz, H, N, R)),
+               prev_x=np.zeros((Bsz, H, P, R)), angle=np.zeros((Bsz, H, NR)))
+    for name, key in (("dx", "x"), ("dB", "B"), ("dC", "C"), ("ddt", "dt"), ("dlam", "lam"),
+                      ("dtheta", "theta"), ("dA", "A"), ("dz", "z"), ("dD", "D"), ("dbnw", "b_norm_w"),
+                      ("dcnw", "c_norm_w"), ("dbb", "b_bias"), ("dcb", "c_bias"), ("ddtb", "dt_bias")):
+        setattr(g, name, _ptr(out[key]))
+    for name, key in (("dh0", "h"), ("dpB0", "prev_B"), ("dpx0", "prev_x"), ("dang0", "angle")):
+        setattr(g, name, _ptr(ini[key]))
+    g.mutation = int(mutation)
+    rc = _load().m3o_scan_bwd(ctypes.byref(g))
+    if rc != 0:
+        raise ValueError("oracle: unsupported sizes")
+    out["init"] = ini
+    return out
