@@ -170,6 +170,43 @@ m3_status m3_scan_mimo(const m3_shape *shape, const m3_inputs *in, void *y, cons
 m3_status m3_step(const m3_shape *shape, const m3_inputs *in, void *y, m3_state *state,
                   void *stream);
 
+/* Gradients of a scan (every pointer a device pointer owned by the caller; NULL = not
+ * wanted).  Per-element gradients have the shape and layout of their inputs: dx, dB, dC,
+ * dz in the io dtype, the rest float32.  ddt and dlam are gradients of dt and lam as
+ * passed (of the raw values when M3_FLAG_DT_SOFTPLUS / M3_FLAG_LAM_SIGMOID are set).  dA
+ * is [H], or [B, T, H] with M3_FLAG_A_PER_TOKEN.  Parameter gradients (dA per head, dD,
+ * d_dt_bias, the gains [N] and biases [H, R, N]) are sums over batch and tokens (and over
+ * heads for the gains); they are overwritten, not accumulated. */
+typedef struct {
+    void *dx, *dB, *dC;
+    float *ddt, *dlam, *dtheta;
+    float *dA, *dD;
+    float *db_norm_w, *dc_norm_w;
+    float *db_bias, *dc_bias;
+    float *ddt_bias;
+    void *dz; /* required when the forward call was gated (in->z != NULL) */
+} m3_grads;
+
+/* Bytes of workspace m3_scan_bwd needs for this shape (0 when T == 0). */
+size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape);
+
+/*
+ * Reverse-mode gradients of m3_scan_siso / m3_scan_mimo (any rank R; the same shape,
+ * inputs and options as the forward call).
+ *   dy:     [B, T, H, P(, R)] gradient of y, io dtype.
+ *   init:   the forward call's initial state, or NULL (zeros).
+ *   dfinal: gradients of the forward call's final state, or NULL (zeros).
+ *   dinit:  where to write the gradients of the initial state, or NULL.
+ * The pages ask for a differentiable scan (torchmamba "Verification": fp64 gradchecks;
+ * dotLLM PR #136: a trainable block) but print no backward; this is the adjoint of the
+ * recurrence, recomputing the forward states (no forward activations are stored).
+ * One workgroup per (batch, head) sequence.  Sizes whose staging does not fit the
+ * compute unit's local memory give M3_EUNSUPPORTED.
+ */
+m3_status m3_scan_bwd(const m3_shape *shape, const m3_inputs *in, const void *dy, const m3_state *init,
+                      const m3_state *dfinal, m3_grads *grads, m3_state *dinit, void *ws, size_t ws_bytes,
+                      void *stream);
+
 /* Static description of a status code. */
 const char *m3_status_str(m3_status status);
 

@@ -18,7 +18,8 @@ import os
 
 import torch
 
-__all__ = ["m3_scan_siso", "m3_scan_mimo", "m3_step", "m3_scan_workspace_bytes",
+__all__ = ["m3_scan_siso", "m3_scan_mimo", "m3_step", "m3_scan_bwd", "m3_scan_workspace_bytes",
+           "m3_scan_bwd_workspace_bytes",
            "m3_status_str", "Shape", "M3_F32", "M3_BF16", "M3_FLAG_BCNORM", "M3_FLAG_PARTIAL_ROPE",
            "M3_FLAG_A_PER_TOKEN", "M3_FLAG_DT_SOFTPLUS", "M3_FLAG_LAM_SIGMOID", "lib_path", "load"]
 
@@ -51,6 +52,12 @@ class _State(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("h", "prev_B", "prev_x", "angle")]
 
 
+class _Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dB", "dC", "ddt", "dlam", "dtheta", "dA", "dD", "db_norm_w", "dc_norm_w",
+                 "db_bias", "dc_bias", "ddt_bias", "dz")]
+
+
 _lib = None
 
 
@@ -72,6 +79,11 @@ def load():
             f.restype = ctypes.c_int
         lib.m3_step.argtypes = [P(Shape), P(_Inputs), ctypes.c_void_p, P(_State), ctypes.c_void_p]
         lib.m3_step.restype = ctypes.c_int
+        lib.m3_scan_bwd_workspace_bytes.argtypes = [P(Shape)]
+        lib.m3_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.m3_scan_bwd.argtypes = [P(Shape), P(_Inputs), ctypes.c_void_p, P(_State), P(_State), P(_Grads),
+                                    P(_State), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.m3_scan_bwd.restype = ctypes.c_int
         lib.m3_status_str.argtypes = [ctypes.c_int]
         lib.m3_status_str.restype = ctypes.c_char_p
         lib.m3_version.restype = ctypes.c_char_p
@@ -266,3 +278,57 @@ def m3_step(x, B, C, dt, lam, theta, A, D, state, *, bcnorm=True, eps=1e-5, b_no
     rc = lib.m3_step(ctypes.byref(s), ctypes.byref(inp), _ptr(y), ctypes.byref(st), _stream(stream))
     _check(rc, "m3_step")
     return y
+
+
+def m3_scan_bwd_workspace_bytes(shape: Shape) -> int:
+    return int(load().m3_scan_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def m3_scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5, b_norm_w=None,
+                c_norm_w=None, b_bias=None, c_bias=None, init=None, dfinal=None, rope_pairs=None,
+                dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None, workspace=None,
+                stream=None):
+    """Gradients of m3_scan_siso / m3_scan_mimo (SISO when x is 4-D) given ``dy``.
+
+    ``init`` is the forward call's initial state and ``dfinal`` the gradients of its final
+    state (dicts h, prev_B, prev_x, angle; either may be None).  Returns a dict of tensors
+    shaped like the inputs: x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias
+    ([H, R, N]), c_bias, dt_bias, z (gated calls) and init (a dict of the initial state's
+    gradients).  Parameter gradients are sums over batch and tokens.
+    """
+    lib = load()
+    mimo = x.dim() == 5
+    s = _shape_of(x, B, 16, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A,
+                                                     dt_softplus=dt_softplus, lam_sigmoid=lam_sigmoid))
+    _need(x, "x", x.dtype, x.device)
+    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
+                  dt_bias, z)
+    _need(dy, "dy", x.dtype, x.device, tuple(x.shape))
+    dev, f32 = x.device, torch.float32
+    H, N, R = s.nheads, s.dstate, s.rank
+    g = dict(x=torch.empty_like(x), B=torch.empty_like(B), C=torch.empty_like(C),
+             dt=torch.empty_like(dt), lam=torch.empty_like(lam), theta=torch.empty_like(theta),
+             A=torch.empty_like(A), D=torch.empty_like(D),
+             b_norm_w=torch.empty(N, dtype=f32, device=dev), c_norm_w=torch.empty(N, dtype=f32, device=dev),
+             b_bias=torch.empty((H, R, N), dtype=f32, device=dev),
+             c_bias=torch.empty((H, R, N), dtype=f32, device=dev),
+             dt_bias=torch.empty(H, dtype=f32, device=dev),
+             z=torch.empty_like(z) if z is not None else None)
+    gr = _Grads(*(_ptr(g[k]) for k in ("x", "B", "C", "dt", "lam", "theta", "A", "D", "b_norm_w",
+                                         "c_norm_w", "b_bias", "c_bias", "dt_bias", "z")))
+    st_in = _state(s, init, dev, "init")
+    st_df = _state(s, dfinal, dev, "dfinal")
+    dinit = new_state(s.batch, s.nheads, s.headdim, s.dstate, s.rank, dev, _rotated(s))
+    st_di = _state(s, dinit, dev, "dinit")
+    need = int(lib.m3_scan_bwd_workspace_bytes(ctypes.byref(s)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    rc = lib.m3_scan_bwd(ctypes.byref(s), ctypes.byref(inp), _ptr(dy),
+                         ctypes.byref(st_in) if st_in is not None else None,
+                         ctypes.byref(st_df) if st_df is not None else None,
+                         ctypes.byref(gr), ctypes.byref(st_di), _ptr(workspace),
+                         ctypes.c_size_t(workspace.numel()), _stream(stream))
+    _check(rc, "m3_scan_bwd")
+    g["init"] = dinit
+    return g

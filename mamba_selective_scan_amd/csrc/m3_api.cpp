@@ -235,9 +235,130 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     return M3_OK;
 }
 
+struct BwdPlan {
+    size_t cbar, part, total;
+    int pw;
+};
+
+BwdPlan bwd_plan_of(const m3_shape *s) {
+    BwdPlan pl{};
+    const int64_t BH = s->batch * (int64_t)s->nheads;
+    pl.pw = 3 + 2 * s->dstate + 2 * s->rank * s->dstate;
+    size_t off = 0;
+    pl.cbar = off; off = align_up(off + sizeof(float) * (size_t)(BH * s->seqlen * s->dstate * s->rank));
+    pl.part = off; off = align_up(off + sizeof(float) * (size_t)(BH * pl.pw));
+    pl.total = (s->seqlen == 0 || BH == 0) ? 0 : off;
+    return pl;
+}
+
+m3_status bwd_impl(const m3_shape *s, const m3_inputs *in, const void *dy, const m3_state *init,
+                   const m3_state *dfin, m3_grads *g, m3_state *dinit, void *ws, size_t ws_bytes, void *stream) {
+    m3_status rc = check_shape(s, false);
+    if (rc != M3_OK) return rc;
+    const int nr = rotated_pairs(s);
+    const bool data = s->seqlen > 0 && s->batch > 0;
+    if ((rc = check_inputs(in, data, nr)) != M3_OK) return rc;
+    if ((rc = check_state(init, false, nr)) != M3_OK) return rc;
+    if ((rc = check_state(dfin, false, nr)) != M3_OK) return rc;
+    if ((rc = check_state(dinit, false, nr)) != M3_OK) return rc;
+    if (!g) return M3_EINVAL;
+    if (data && !dy) return M3_EINVAL;
+    if (in->z && data && !g->dz) return M3_EINVAL;
+    const void *ptrs[] = {dy, g->dx, g->dB, g->dC, g->ddt, g->dlam, g->dtheta, g->dA, g->dD, g->db_norm_w,
+                          g->dc_norm_w, g->db_bias, g->dc_bias, g->ddt_bias, g->dz};
+    for (const void *q : ptrs)
+        if (!aligned16(q)) return M3_EINVAL;
+    if (m3::bwd_lds_bytes(s->dstate, s->headdim, s->rank) > 160 * 1024) return M3_EUNSUPPORTED;
+    const BwdPlan pl = bwd_plan_of(s);
+    if (pl.total > 0 && (!ws || ws_bytes < pl.total)) return M3_EWORKSPACE;
+    if (!aligned16(ws)) return M3_EINVAL;
+    if (s->batch == 0) return M3_OK;
+    m3::BwdParams p;
+    std::memset(&p, 0, sizeof p);
+    p.B = s->batch;
+    p.T = s->seqlen;
+    p.H = s->nheads;
+    p.P = s->headdim;
+    p.N = s->dstate;
+    p.R = s->rank;
+    p.flags = s->flags;
+    p.eps = s->norm_eps;
+    p.nr = nr;
+    p.x = in->x;
+    p.Bm = in->Bm;
+    p.Cm = in->Cm;
+    p.dt = in->dt;
+    p.lam = in->lam;
+    p.theta = in->theta;
+    p.A = in->A;
+    p.D = in->D;
+    p.bnw = in->b_norm_w;
+    p.cnw = in->c_norm_w;
+    p.bbias = in->b_bias;
+    p.cbias = in->c_bias;
+    p.dtbias = in->dt_bias;
+    p.z = in->z;
+    if (init) {
+        p.h0 = init->h;
+        p.pB0 = init->prev_B;
+        p.px0 = init->prev_x;
+        p.ang0 = init->angle;
+    }
+    p.dy = dy;
+    if (dfin) {
+        p.dh1 = dfin->h;
+        p.dpB1 = dfin->prev_B;
+        p.dpx1 = dfin->prev_x;
+        p.dang1 = dfin->angle;
+    }
+    p.dx = g->dx;
+    p.dB = g->dB;
+    p.dC = g->dC;
+    p.dz = g->dz;
+    p.ddt = g->ddt;
+    p.dlam = g->dlam;
+    p.dtheta = g->dtheta;
+    const bool atok = (s->flags & M3_FLAG_A_PER_TOKEN) != 0;
+    p.dAt = atok ? g->dA : nullptr;
+    p.dA = atok ? nullptr : g->dA;
+    p.dD = g->dD;
+    p.dbnw = g->db_norm_w;
+    p.dcnw = g->dc_norm_w;
+    p.dbb = g->db_bias;
+    p.dcb = g->dc_bias;
+    p.ddtb = g->ddt_bias;
+    if (dinit) {
+        p.dh0 = dinit->h;
+        p.dpB0 = dinit->prev_B;
+        p.dpx0 = dinit->prev_x;
+        p.dang0 = dinit->angle;
+    }
+    char *base = static_cast<char *>(ws);
+    p.cbar = pl.total ? reinterpret_cast<float *>(base + pl.cbar) : nullptr;
+    p.part = pl.total ? reinterpret_cast<float *>(base + pl.part) : nullptr;
+    p.pw = pl.pw;
+    return m3::launch_bwd(s->io == M3_BF16, p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? M3_OK
+                                                                                                     : M3_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape) {
+    if (!shape || shape->seqlen < 0 || shape->batch < 0 || shape->nheads < 1 || shape->headdim < 1 ||
+        shape->dstate < 2 || shape->rank < 1 || shape->rank > 8 || (shape->dstate & 1) || shape->dstate > 128 ||
+        shape->headdim > 128)
+        return 0;
+    return bwd_plan_of(shape).total;
+}
+
+m3_status m3_scan_bwd(const m3_shape *shape, const m3_inputs *in, const void *dy, const m3_state *init,
+                      const m3_state *dfinal, m3_grads *grads, m3_state *dinit, void *ws, size_t ws_bytes,
+                      void *stream) {
+    return bwd_impl(shape, in, dy, init, dfinal, grads, dinit, ws, ws_bytes, stream);
+}
+
 
 size_t m3_scan_workspace_bytes(const m3_shape *shape) {
     if (!shape || shape->chunk < 1 || shape->seqlen < 0 || shape->batch < 0 || shape->nheads < 1 ||

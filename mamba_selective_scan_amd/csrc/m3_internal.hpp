@@ -67,6 +67,36 @@ struct StepParams {
     float *h, *pB, *px, *ang;
 };
 
+// Gradients of a scan (reverse-mode), one workgroup per (batch, head) sequence.
+struct BwdParams {
+    int64_t B, T;
+    int H, P, N, R;
+    uint32_t flags;
+    float eps;
+    int nr;
+    // forward inputs (as for ScanParams)
+    const void *x, *Bm, *Cm;
+    const float *dt, *lam, *theta, *A, *D;
+    const float *bnw, *cnw, *bbias, *cbias, *dtbias;
+    const void *z;
+    const float *h0, *pB0, *px0, *ang0;      // initial state or NULL
+    // upstream gradients
+    const void *dy;                           // like y
+    const float *dh1, *dpB1, *dpx1, *dang1;  // of the final state, or NULL
+    // per-element gradients
+    void *dx, *dB, *dC, *dz;                  // io dtype
+    float *ddt, *dlam, *dtheta, *dAt;         // dAt: per-token A gradient (kFlagAPerToken) or NULL
+    float *dh0, *dpB0, *dpx0, *dang0;         // or NULL
+    // parameter gradients, summed over sequences by bwd_reduce_kernel (each may be NULL)
+    float *dA, *dD, *dbnw, *dcnw, *dbb, *dcb, *ddtb;
+    // workspace
+    float *cbar;  // [B*H][T][N][R] gradient of the normalised C (forward sweep -> reverse sweep)
+    float *part;  // [B*H][pw] per-sequence partial sums of the parameter gradients
+    int pw;
+};
+size_t bwd_lds_bytes(int N, int P, int R);
+hipError_t launch_bwd(bool bf16, const BwdParams &p, hipStream_t stream);
+
 // Tile variant chosen by the host.
 enum TileMode { kTileGen = 0, kTileVec = 1, kTileMimo = 2 };
 struct TileShape {
