@@ -199,9 +199,8 @@ size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape);
  *   dinit:  where to write the gradients of the initial state, or NULL.
  * The pages ask for a differentiable scan (torchmamba "Verification": fp64 gradchecks;
  * dotLLM PR #136: a trainable block) but print no backward; this is the adjoint of the
- * recurrence, recomputing the forward states (no forward activations are stored).
- * One workgroup per (batch, head) sequence.  Sizes whose staging does not fit the
- * compute unit's local memory give M3_EUNSUPPORTED.
+ * recurrence, recomputing the forward states (no forward activations are stored);
+ * the workspace holds per-segment states and per-token partial sums.
  */
 m3_status m3_scan_bwd(const m3_shape *shape, const m3_inputs *in, const void *dy, const m3_state *init,
                       const m3_state *dfinal, m3_grads *grads, m3_state *dinit, void *ws, size_t ws_bytes,

@@ -7,27 +7,36 @@
 // RoPE trick): per pair i the state g_t = Rot(-Theta_t) h_t evolves as
 //     g_t = Q_t (alpha_t g_{t-1} + beta_t b_{t-1} x_{t-1}^T) + gamma_t b_t x_t^T,
 //     y_t = sum_i c_t^T g_t + D x_t,        Q_t = Rot(-theta_t),
-// with b, c the normalised, biased and *unrotated* B and C, so no cumulative
-// angle enters the sweeps.  One workgroup walks one (batch, head) sequence:
-//
-//   forward sweep  recomputes g_t and emits dc_t = g_t dy_t (the gradient of c)
-//                  (and, with the gate, the ungated output for dz);
-//   reverse sweep  runs the adjoint  G_{t-1} = alpha_t Q_t^T G_t + c_{t-1} dy_{t-1}^T
-//                  and emits db_t, dx_t and the per-token scalars.
-//
-// The gradients of alpha_t and of the per-step angle need <G_t, g_{t-1}>-type
-// inner products; instead of the forward states the reverse sweep carries, per
-// pair, the 2x2 matrix K_t = sum_p G_t[:, p] g_t[:, p]^T, which obeys
+// with b, c the normalised, biased and unrotated B and C, so no cumulative
+// angle enters the sweeps.  The adjoint is
+//     G_{t-1} = alpha_t Q_t^T G_t + c_{t-1} dy_{t-1}^T,
+// and the decay and angle gradients, which need <G_t, g_{t-1}>-type inner
+// products, come from the per-pair 2x2 matrix K_t = sum_p G_t[:, p] g_t[:, p]^T:
 //     K_{t-1} = Q_t^T E_t + c_{t-1} dc_{t-1}^T,
 //     E_t     = (K_t - gamma_t u_t b_t^T) Q_t - beta_t v_t b_{t-1}^T,
-//     u_t = G_t x_t,  v_t = G_t x_{t-1}   (sums over p),
-// and gives  d log alpha_t = sum_i trace(Q_t^T E_t)  and the local angle
-// gradient  F01 - F10  of  F = K_t - gamma_t u_t b_t^T.
+//     u_t = G_t x_t,  v_t = G_t x_{t-1},  dc_t = g_t dy_t   (sums over the columns p),
+//     d log alpha_t = sum_i trace(Q_t^T E_t),  local angle gradient = F01 - F10 of
+//     F = K_t - gamma_t u_t b_t^T.
 //
-// Lane layout: lane (wave w, row rho, column cc) owns pairs grp*npl .. of the
-// state (grp = 4 w + rho) and columns cc*cpl .. ; sums over columns are row
-// all-reduces (DPP), sums over pairs go through per-wave partials in LDS that
-// are added once per block of 16 (token, rank) rows.
+// Every quantity above is linear in the per-column contributions, and the
+// state columns evolve independently, so a workgroup handles one group of 16
+// columns of one time segment of one (batch, head) sequence; partial sums over
+// the column groups are added by the final per-token kernel.  Segments are
+// chained like the forward's: forward aggregates from zero, a fold that turns
+// them into segment start states; reverse aggregates of the adjoint from zero,
+// a fold that turns them into segment end adjoints.  Kernels, in launch order:
+//   bwd_sweep_kernel (mode 0)  forward aggregate of each segment
+//   bwd_ffold_kernel           segment start states, final angle
+//   bwd_sweep_kernel (mode 1)  adjoint aggregate of each segment
+//   bwd_rfold_kernel           segment end adjoints, gradient of the initial h
+//   bwd_sweep_kernel (mode 2)  both sweeps of each segment: column-group shares
+//   bwd_final_kernel           per-token sums, norm backward, boundary terms
+//   bwd_reduce_kernel          parameter gradients
+//
+// Lane layout of a sweep: lane (wave w, row rho, column cc) owns pairs
+// (4 w + rho) * NPL + j of the state and column cc of the group; sums over
+// columns are row all-reduces (DPP), sums over pairs go through per-wave
+// partials in LDS added once per block of 16 (token, rank) rows.
 #include <type_traits>
 
 #include "m3_device.hpp"
@@ -38,6 +47,7 @@ namespace m3 {
 namespace {
 
 constexpr int kRows = 16;  // (token, rank) rows per staged block
+constexpr int kCW = 16;    // state columns per workgroup
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -57,46 +67,10 @@ __device__ __forceinline__ float rows_sum4(float v) {
     v += __shfl_xor(v, 32, 64);
     return v;
 }
+__device__ __forceinline__ float wave_sum(float v) { return rows_sum4(row_sum16(v)); }
 
-struct BwdLds {
-    float *sb, *sx, *sc, *sy, *scb, *sbb, *scs, *sth, *sxg, *sxb, *ssc, *ssp, *srn, *spend, *sred, *sthf;
-    __device__ BwdLds(float *s, int N, int P) {
-        const int RW = kRows + 8;
-        sb = s;                  // [RW][N]  b rows; rows 0..R-1 hold the previous token
-        sx = sb + RW * N;        // [RW][P]  x rows; rows 0..R-1 hold the previous token
-        sc = sx + RW * P;        // [16][N]  c rows
-        sy = sc + kRows * N;     // [16][P]  gated dy rows
-        scb = sy + kRows * P;    // [16][N]  gradient of c
-        sbb = scb + kRows * N;   // [16][N]  gradient of b
-        scs = sbb + kRows * N;   // [16][N/2][2] (cos, sin) of the token's angle step
-        sth = scs + kRows * N;   // [16][N/2] local angle gradient
-        sxg = sth + kRows * (N / 2);  // [4][16][P] per-wave partials (forward: ungated y; reverse: gamma part of dx)
-        sxb = sxg + 4 * kRows * P;    // [4][16][P] reverse: beta part of dx of the previous token
-        ssc = sxb + 4 * kRows * P;    // [16][8] per token: alpha, beta, gamma, dt, lambda, A, dsoftplus, dsigmoid
-        ssp = ssc + kRows * 8;        // [16][4][4] per-wave partial scalars: dlog(alpha), beta grad, gamma grad
-        srn = ssp + kRows * 16;       // [16][2] norm factors (b, c) of the rows
-        spend = srn + kRows * 2;      // [8][P] dx pending for the previous block's last token (beta part)
-        sred = spend + 8 * P;         // [4][2][N] cross-wave sums of the gain gradients
-        sthf = sred + 8 * N;          // [N/2] gradient of the final angle
-    }
-    static __host__ __device__ size_t floats(int N, int P) {
-        const int RW = kRows + 8;
-        return (size_t)RW * N + (size_t)RW * P + 4 * kRows * N + kRows * N / 2 + 2 * kRows * P +
-               8 * kRows * P + kRows * 8 + kRows * 16 + kRows * 2 + 8 * P + 8 * N + N / 2 + 4;
-    }
-};
-
-}  // namespace
-
-size_t bwd_lds_bytes(int N, int P, int R) {
-    (void)R;
-    return sizeof(float) * BwdLds::floats(N, P);
-}
-
-namespace {
-
-// Normalised (gain, bias) row of raw B or C: one wave, lanes over n.  Returns the
-// norm factor; writes the row to dst[N].
+// Normalised (gain, bias) row of raw B or C: one wave, lanes over n.  Returns the norm
+// factor; writes the row to dst[N] (when dst is not NULL).
 template <class Io>
 __device__ __forceinline__ float norm_row(const BwdParams &p, const typename Io::T *raw, int R, const float *gain,
                                           const float *bias, float *dst) {
@@ -109,51 +83,23 @@ __device__ __forceinline__ float norm_row(const BwdParams &p, const typename Io:
         v[k] = n < N ? Io::ld(raw + (int64_t)n * R) : 0.f;
         ss += v[k] * v[k];
     }
-    ss = rows_sum4(row_sum16(ss));
+    ss = wave_sum(ss);
     const float rs = norm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
+    if (dst) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int n = lane + 64 * k;
-        if (n < N) {
-            float u = norm ? v[k] * rs * (gain ? gain[n] : 1.f) : v[k];
-            if (bias) u += bias[n];
-            dst[n] = u;
+        for (int k = 0; k < 2; ++k) {
+            const int n = lane + 64 * k;
+            if (n < N) {
+                float u = norm ? v[k] * rs * (gain ? gain[n] : 1.f) : v[k];
+                if (bias) u += bias[n];
+                dst[n] = u;
+            }
         }
     }
     return rs;
 }
 
-// Gradient of a raw B or C row from the gradient of its normalised row (one wave,
-// lanes over n); accumulates the gain and bias gradients of this lane's n.
-template <class Io>
-__device__ __forceinline__ void norm_row_bwd(const BwdParams &p, const typename Io::T *raw, int R, const float *gain,
-                                             float rs, const float *grad, typename Io::T *out, float (&again)[2],
-                                             float (&abias)[2]) {
-    const int lane = threadIdx.x & 63, N = p.N;
-    const bool norm = (p.flags & kFlagNorm) != 0;
-    float v[2], gv[2], dot = 0.f;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int n = lane + 64 * k;
-        v[k] = n < N ? Io::ld(raw + (int64_t)n * R) : 0.f;
-        gv[k] = n < N ? grad[n] : 0.f;
-        const float gn = (n < N && gain) ? gain[n] : 1.f;
-        dot += gv[k] * gn * v[k];
-        abias[k] += gv[k];
-        if (norm) again[k] += gv[k] * v[k] * rs;
-    }
-    dot = rows_sum4(row_sum16(dot));
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int n = lane + 64 * k;
-        if (n >= N) continue;
-        const float gn = gain ? gain[n] : 1.f;
-        const float d = norm ? gv[k] * gn * rs - dot * rs * rs * rs * v[k] / (float)N : gv[k];
-        if (out) Io::st(out + (int64_t)n * R, d);
-    }
-}
-
-// dt and lambda after the optional activations, with the derivatives of the activations
+// dt and lambda after the optional activations, with the activations' derivatives
 __device__ __forceinline__ void act_scalars(const BwdParams &p, int64_t bth, int h, float &dt, float &lam,
                                             float &ddt_draw, float &dlam_draw) {
     dt = p.dt[bth];
@@ -171,379 +117,428 @@ __device__ __forceinline__ void act_scalars(const BwdParams &p, int64_t bth, int
     }
 }
 
-// Stage tokens t0 .. t0+Tv-1 (and the previous token's b and x rows).
-template <class Io>
-__device__ void stage_block(const BwdParams &p, const BwdLds &L, int64_t b, int h, int64_t t0, int Tv, bool want_cb) {
+// Complex-form b of the carried previous token: Rot(-Theta_init) prev_B (pair i, rank r)
+__device__ __forceinline__ void init_b(const BwdParams &p, int64_t bh, int i, int r, float &u, float &v) {
+    const int N = p.N, R = p.R;
+    u = v = 0.f;
+    if (p.pB0) {
+        u = p.pB0[(bh * N + 2 * i) * R + r];
+        v = p.pB0[(bh * N + 2 * i + 1) * R + r];
+    }
+    if (p.ang0 && i < p.nr) {
+        float s, c;
+        fast_sincos((float)wrap_2pi((double)p.ang0[bh * p.nr + i]), s, c);
+        const float u2 = c * u + s * v, v2 = -s * u + c * v;
+        u = u2;
+        v = v2;
+    }
+}
+
+// LDS layout of the sweep kernel (floats)
+template <int NPAD>
+struct SweepLds {
+    static constexpr int RW = kRows + 8;                // rows incl. the previous token's (R <= 8)
+    static constexpr int SB = 0;                        // [RW][NPAD] b rows (rows 0..R-1: previous token)
+    static constexpr int SX = SB + RW * NPAD;           // [RW][16]   x rows (own columns)
+    static constexpr int SC = SX + RW * kCW;            // [16][NPAD] c rows
+    static constexpr int SY = SC + kRows * NPAD;        // [16][16]   gated dy rows
+    static constexpr int SCB = SY + kRows * kCW;        // [16][NPAD] gradient of c (share)
+    static constexpr int SCS = SCB + kRows * NPAD;      // [16][NPAD/2][2] (cos, sin) of the angle steps
+    static constexpr int SXG = SCS + kRows * NPAD;      // [4][16][16] per-wave partials (ungated y / gamma part of dx)
+    static constexpr int SXB = SXG + 4 * kRows * kCW;   // [4][16][16] beta part of dx of the previous token
+    static constexpr int SSC = SXB + 4 * kRows * kCW;   // [16][8] alpha, beta, gamma, dt, lambda, A, -, -
+    static constexpr int SSP = SSC + kRows * 8;         // [16][4][4] per-wave partial scalars
+    static constexpr int SPN = SSP + kRows * 16;        // [8][16] dx pending for the previous block's last token
+    static constexpr int SRD = SPN + 8 * kCW;           // [8] reductions
+    static constexpr int TOTAL = SRD + 8;
+};
+
+// Stage tokens t0 .. t0+Tv-1 of one sequence (b and x rows of the previous token too).
+// Every global load of the block is issued before the first use, so the block pays
+// the memory latency once.
+template <class Io, int NPAD>
+__device__ void stage(const BwdParams &p, float *sm, int64_t b, int h, int cg, int64_t t0, int Tv, bool want_c,
+                      bool want_cb) {
     using ET = typename Io::T;
+    using L = SweepLds<NPAD>;
+    constexpr int MB = (kRows + 8) / 4, MC = kRows / 4, MT = kRows * (NPAD / 2) / 256 > 0 ? kRows * (NPAD / 2) / 256 : 1;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int N = p.N, P = p.P, R = p.R, N2 = N / 2, NR = p.nr;
     const int64_t T = p.T, H = p.H;
     const int64_t bh = b * H + h;
-    // b and x rows, previous token included (rows 0 .. R-1)
-    for (int row = w; row < (Tv + 1) * R; row += 4) {
+    const int p0 = cg * kCW;
+    const bool norm = (p.flags & kFlagNorm) != 0;
+    const int nbr = (Tv + 1) * R, ncr = Tv * R;
+    // ---- loads
+    float bv[MB][2], xv[MB], cvv[MC][2], yv[MC], zv[MC], cb[MC][2];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+        const int row = w + 4 * m;
+        bv[m][0] = bv[m][1] = xv[m] = 0.f;
         const int64_t t = t0 - 1 + row / R;
-        const int r = row % R;
-        float *db = L.sb + row * N, *dx = L.sx + row * P;
-        if (t >= 0) {
+        if (row < nbr && t >= 0) {
+            const int r = row % R;
             const int64_t bth = (b * T + t) * H + h;
-            const float rs = norm_row<Io>(p, (const ET *)p.Bm + bth * N * R + r, R, p.bnw,
-                                          p.bbias ? p.bbias + ((int64_t)h * R + r) * N : nullptr, db);
-            if (row >= R && lane == 0) L.srn[(row - R) * 2 + 0] = rs;
-            for (int pc = lane; pc < P; pc += 64) dx[pc] = Io::ld((const ET *)p.x + bth * P * R + (int64_t)pc * R + r);
-        } else {
-            // the carried previous token: b = Rot(-Theta_init) prev_B, x = prev_x
-            for (int i = lane; i < N2; i += 64) {
-                float u = 0.f, v = 0.f;
-                if (p.pB0) {
-                    u = p.pB0[(bh * N + 2 * i) * R + r];
-                    v = p.pB0[(bh * N + 2 * i + 1) * R + r];
-                }
-                if (p.ang0 && i < NR) {
-                    float s, c;
-                    fast_sincos((float)wrap_2pi((double)p.ang0[bh * NR + i]), s, c);
-                    const float u2 = c * u + s * v, v2 = -s * u + c * v;
-                    u = u2;
-                    v = v2;
-                }
-                db[2 * i] = u;
-                db[2 * i + 1] = v;
+            const ET *raw = (const ET *)p.Bm + bth * N * R + r;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int n = lane + 64 * k;
+                if (n < N) bv[m][k] = Io::ld(raw + (int64_t)n * R);
             }
-            for (int pc = lane; pc < P; pc += 64) dx[pc] = p.px0 ? p.px0[(bh * P + pc) * R + r] : 0.f;
+            if (lane < kCW && p0 + lane < P) xv[m] = Io::ld((const ET *)p.x + bth * P * R + (int64_t)(p0 + lane) * R + r);
         }
     }
-    // c rows, gated dy rows, gradient-of-c rows (reverse sweep)
-    for (int q = w; q < Tv * R; q += 4) {
-        const int64_t t = t0 + q / R;
-        const int r = q % R;
-        const int64_t bth = (b * T + t) * H + h;
-        const float rs = norm_row<Io>(p, (const ET *)p.Cm + bth * N * R + r, R, p.cnw,
-                                      p.cbias ? p.cbias + ((int64_t)h * R + r) * N : nullptr, L.sc + q * N);
-        if (lane == 0) L.srn[q * 2 + 1] = rs;
-        for (int pc = lane; pc < P; pc += 64) {
-            const int64_t o = bth * P * R + (int64_t)pc * R + r;
-            float g = Io::ld((const ET *)p.dy + o);
-            if (p.z) g *= silu_f(Io::ld((const ET *)p.z + o));
-            L.sy[q * P + pc] = g;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+        const int q = w + 4 * m;
+        cvv[m][0] = cvv[m][1] = yv[m] = cb[m][0] = cb[m][1] = 0.f;
+        zv[m] = 1.f;
+        if (want_c && q < ncr) {
+            const int64_t t = t0 + q / R;
+            const int r = q % R;
+            const int64_t bth = (b * T + t) * H + h;
+            const ET *raw = (const ET *)p.Cm + bth * N * R + r;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int n = lane + 64 * k;
+                if (n < N) cvv[m][k] = Io::ld(raw + (int64_t)n * R);
+                if (want_cb && n < N) cb[m][k] = p.cbar[((cg * (p.B * H) + bh) * T + t) * (int64_t)N * R + n * R + r];
+            }
+            if (lane < kCW && p0 + lane < P) {
+                const int64_t o = bth * P * R + (int64_t)(p0 + lane) * R + r;
+                yv[m] = Io::ld((const ET *)p.dy + o);
+                if (p.z) zv[m] = Io::ld((const ET *)p.z + o);
+            }
         }
-        if (want_cb)
-            for (int n = lane; n < N; n += 64) L.scb[q * N + n] = p.cbar[((bh * T + t) * N + n) * R + r];
     }
-    // per-token scalars and angle steps
+    float sdt = 0.f, slam = 0.f, sA = 0.f;
     if (tid < Tv) {
         const int64_t bth = (b * T + t0 + tid) * H + h;
-        float dt, lam, dsp, dsg;
-        act_scalars(p, bth, h, dt, lam, dsp, dsg);
-        const float A = (p.flags & kFlagAPerToken) ? p.A[bth] : p.A[h];
-        const float al = __expf(dt * A);
-        float *s = L.ssc + tid * 8;
+        sdt = p.dt[bth];
+        slam = p.lam[bth];
+        sA = (p.flags & kFlagAPerToken) ? p.A[bth] : p.A[h];
+    }
+    float th[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int e = tid + 256 * m;
+        const int k = e / N2, i = e - k * N2;
+        th[m] = 0.f;
+        if (k < Tv && i < NR) th[m] = p.theta[((b * T + t0 + k) * H + h) * (int64_t)NR + i];
+    }
+    // ---- normalised rows and the rest
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+        const int row = w + 4 * m;
+        if (row >= nbr) continue;  // uniform per wave
+        const int64_t t = t0 - 1 + row / R;
+        const int r = row % R;
+        float *db = sm + L::SB + row * NPAD;
+        if (t >= 0) {
+            const float ss = wave_sum(bv[m][0] * bv[m][0] + bv[m][1] * bv[m][1]);
+            const float rs = norm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
+            const float *bias = p.bbias ? p.bbias + ((int64_t)h * R + r) * N : nullptr;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int n = lane + 64 * k;
+                if (n < N) {
+                    float u = norm ? bv[m][k] * rs * (p.bnw ? p.bnw[n] : 1.f) : bv[m][k];
+                    if (bias) u += bias[n];
+                    db[n] = u;
+                }
+            }
+            if (lane < kCW) sm[L::SX + row * kCW + lane] = xv[m];
+        } else {
+            for (int i = lane; i < N2; i += 64) init_b(p, bh, i, r, db[2 * i], db[2 * i + 1]);
+            if (lane < kCW) sm[L::SX + row * kCW + lane] = (p.px0 && p0 + lane < P) ? p.px0[(bh * P + p0 + lane) * R + r] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+        const int q = w + 4 * m;
+        if (!want_c || q >= ncr) continue;  // uniform per wave
+        const int r = q % R;
+        const float ss = wave_sum(cvv[m][0] * cvv[m][0] + cvv[m][1] * cvv[m][1]);
+        const float rs = norm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
+        const float *bias = p.cbias ? p.cbias + ((int64_t)h * R + r) * N : nullptr;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int n = lane + 64 * k;
+            if (n < N) {
+                float u = norm ? cvv[m][k] * rs * (p.cnw ? p.cnw[n] : 1.f) : cvv[m][k];
+                if (bias) u += bias[n];
+                sm[L::SC + q * NPAD + n] = u;
+                if (want_cb) sm[L::SCB + q * NPAD + n] = cb[m][k];
+            }
+        }
+        if (lane < kCW) sm[L::SY + q * kCW + lane] = p.z ? yv[m] * silu_f(zv[m]) : yv[m];
+    }
+    if (tid < Tv) {
+        float dt = sdt, lam = slam;
+        if (p.flags & kFlagDtSoftplus) dt = softplus_f(dt + (p.dtbias ? p.dtbias[h] : 0.f));
+        if (p.flags & kFlagLamSigmoid) lam = sigmoid_f(lam);
+        const float al = __expf(dt * sA);
+        float *s = sm + L::SSC + tid * 8;
         s[0] = al;
         s[1] = al * dt * (1.f - lam);
         s[2] = lam * dt;
         s[3] = dt;
         s[4] = lam;
-        s[5] = A;
-        s[6] = dsp;
-        s[7] = dsg;
+        s[5] = sA;
     }
-    for (int e = tid; e < Tv * N2; e += 256) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int e = tid + 256 * m;
         const int k = e / N2, i = e - k * N2;
-        float s = 0.f, c = 1.f;
-        if (i < NR) {
-            const float th = p.theta[((b * T + t0 + k) * H + h) * (int64_t)NR + i];
-            s = __sinf(th);
-            c = __cosf(th);
-        }
-        L.scs[e * 2 + 0] = c;
-        L.scs[e * 2 + 1] = s;
+        if (k >= Tv) continue;
+        sm[L::SCS + (k * (NPAD / 2) + i) * 2 + 0] = i < NR ? __cosf(th[m]) : 1.f;
+        sm[L::SCS + (k * (NPAD / 2) + i) * 2 + 1] = i < NR ? __sinf(th[m]) : 0.f;
     }
 }
 
 }  // namespace
 
-template <class Io, int NPLM, int CPLM, int RMAX>
-__global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p) {
+// mode 0: forward aggregate; 1: adjoint aggregate; 2: both sweeps with the shares
+template <class Io, int NPAD, int RMAX>
+__global__ __launch_bounds__(256) void bwd_sweep_kernel(BwdParams p, int mode) {
     using ET = typename Io::T;
-    extern __shared__ __attribute__((aligned(16))) float smem_f[];
+    using L = SweepLds<NPAD>;
+    constexpr int N2P = NPAD / 2;
+    constexpr int NPL = N2P >= 16 ? N2P / 16 : 1;
+    __shared__ __attribute__((aligned(16))) float sm[L::TOTAL];
     const int N = p.N, P = p.P, R = RMAX == 1 ? 1 : p.R, N2 = N / 2, NR = p.nr;
-    const BwdLds L(smem_f, N, P);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int rho = lane >> 4, cc = lane & 15, grp = w * 4 + rho;
-    const int64_t bh = blockIdx.x;
+    const int64_t bid = blockIdx.x;
+    const int seg = (int)(bid % p.nseg);
+    const int64_t q1 = bid / p.nseg;
+    const int cg = (int)(q1 % p.ncg);
+    const int64_t bh = q1 / p.ncg;
     const int64_t b = bh / p.H;
     const int h = (int)(bh - b * p.H);
-    const int64_t T = p.T, H = p.H;
-    const int npl = (N2 + 15) / 16, cpl = (P + 15) / 16;
+    const int64_t T = p.T, H = p.H, BH = p.B * p.H;
     const int TBt = kRows / R;
-    const int nblk = (int)((T + TBt - 1) / TBt);
-    const float Dh = p.D[h];
+    const int64_t ts = (int64_t)seg * p.segT, te = min(T, ts + (int64_t)p.segT);
+    const int nblk = (int)((te - ts + TBt - 1) / TBt);
+    const int pc = cg * kCW + cc;  // this lane's column
+    const bool cv = pc < P;
+    const int64_t sidx = (bh * p.ncg + cg) * p.nseg + seg;  // (sequence, group, segment)
+    const int i0 = grp * NPL;
+    auto piv = [&](int j) { return i0 + j < N2; };
+    auto CS = [&](int k, int i, int c) { return sm[L::SCS + (k * N2P + i) * 2 + c]; };
+    auto SB = [&](int row, int n) { return sm[L::SB + row * NPAD + n]; };
+    auto SX = [&](int row) { return sm[L::SX + row * kCW + cc]; };
 
-    // per-lane accumulators of parameter gradients
-    float aD = 0.f, aA = 0.f, aDtb = 0.f;
-    float gB[2] = {0.f, 0.f}, gC[2] = {0.f, 0.f};       // gain gradients, n = lane, lane + 64
-    float bB[2][2] = {{0.f, 0.f}, {0.f, 0.f}};           // bias gradients of ranks w, w + 4
-    float bC[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-
-    // ---------------------------------------------------------------- forward sweep
-    float G[NPLM][2][CPLM];
-    double th_run[NPLM];  // global angle of this lane's pairs (final angle after the sweep)
+    float G[NPL][2];
 #pragma unroll
-    for (int j = 0; j < NPLM; ++j) {
-        const int i = grp * npl + j;
-        th_run[j] = (p.ang0 && j < npl && i < NR) ? (double)p.ang0[bh * NR + i] : 0.0;
-        float s0 = 0.f, c0 = 1.f;
-        if (th_run[j] != 0.0) fast_sincos((float)wrap_2pi(th_run[j]), s0, c0);
+    for (int j = 0; j < NPL; ++j) G[j][0] = G[j][1] = 0.f;
+    // ---------------------------------------------------------------- forward sweep (modes 0, 2)
+    if (mode != 1) {
+        float lsum = 0.f;
 #pragma unroll
-        for (int q = 0; q < CPLM; ++q) {
-            const int pc = cc * cpl + q;
-            float u = 0.f, v = 0.f;
-            if (j < npl && q < cpl && i < N2 && pc < P && p.h0) {
-                u = p.h0[(bh * N + 2 * i) * P + pc];
-                v = p.h0[(bh * N + 2 * i + 1) * P + pc];
+        for (int j = 0; j < NPL; ++j) {
+            const int i = i0 + j;
+            G[j][0] = G[j][1] = 0.f;
+            if (mode == 2 && piv(j)) {
+                G[j][0] = p.Gagg[(sidx * N + 2 * i) * kCW + cc];
+                G[j][1] = p.Gagg[(sidx * N + 2 * i + 1) * kCW + cc];
             }
-            G[j][0][q] = c0 * u + s0 * v;  // g = Rot(-Theta_init) h0
-            G[j][1][q] = -s0 * u + c0 * v;
         }
-    }
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int64_t t0 = (int64_t)blk * TBt;
-        const int Tv = (int)min((int64_t)TBt, T - t0);
-        __syncthreads();
-        stage_block<Io>(p, L, b, h, t0, Tv, false);
-        __syncthreads();
-        for (int k = 0; k < Tv; ++k) {
-            const float al = L.ssc[k * 8 + 0], be = L.ssc[k * 8 + 1], ga = L.ssc[k * 8 + 2];
+        for (int blk = 0; blk < nblk; ++blk) {
+            const int64_t t0 = ts + (int64_t)blk * TBt;
+            const int Tv = (int)min((int64_t)TBt, te - t0);
+            __syncthreads();
+            stage<Io, NPAD>(p, sm, b, h, cg, t0, Tv, mode == 2, false);
+            __syncthreads();
+            if (mode == 0) {
+                // segment totals of log alpha and of the angle steps (one group writes them)
+                if (cg == 0 && tid == 0)
+                    for (int k = 0; k < Tv; ++k) lsum += sm[L::SSC + k * 8 + 3] * sm[L::SSC + k * 8 + 5];
+            }
+            for (int k = 0; k < Tv; ++k) {
+                const float al = sm[L::SSC + k * 8 + 0], be = sm[L::SSC + k * 8 + 1], ga = sm[L::SSC + k * 8 + 2];
 #pragma unroll
-            for (int j = 0; j < NPLM; ++j) {
-                if (j >= npl) break;
-                const int i = grp * npl + j;
-                const bool iv = i < N2;
-                const float c = iv ? L.scs[(k * N2 + i) * 2] : 1.f, s = iv ? L.scs[(k * N2 + i) * 2 + 1] : 0.f;
-                if (iv && i < NR) th_run[j] += (double)p.theta[((b * T + t0 + k) * H + h) * (int64_t)NR + i];
-#pragma unroll
-                for (int q = 0; q < CPLM; ++q) {
-                    if (q >= cpl) break;
-                    const int pc = cc * cpl + q;
-                    const bool ok = iv && pc < P;
-                    float m0 = al * G[j][0][q], m1 = al * G[j][1][q];
-                    float a0 = 0.f, a1 = 0.f;
+                for (int j = 0; j < NPL; ++j) {
+                    const int i = i0 + j;
+                    if (!piv(j)) continue;
+                    const float c = CS(k, i, 0), s = CS(k, i, 1);
+                    float m0 = al * G[j][0], m1 = al * G[j][1], a0 = 0.f, a1 = 0.f;
 #pragma unroll
                     for (int r = 0; r < RMAX; ++r) {
                         if (r >= R) break;
-                        if (ok) {
-                            const float xp = L.sx[(k * R + r) * P + pc], xc = L.sx[(R + k * R + r) * P + pc];
-                            m0 += be * L.sb[(k * R + r) * N + 2 * i] * xp;
-                            m1 += be * L.sb[(k * R + r) * N + 2 * i + 1] * xp;
-                            a0 += L.sb[(R + k * R + r) * N + 2 * i] * xc;
-                            a1 += L.sb[(R + k * R + r) * N + 2 * i + 1] * xc;
+                        const float xp = SX(k * R + r), xc = SX(R + k * R + r);
+                        m0 += be * SB(k * R + r, 2 * i) * xp;
+                        m1 += be * SB(k * R + r, 2 * i + 1) * xp;
+                        a0 += SB(R + k * R + r, 2 * i) * xc;
+                        a1 += SB(R + k * R + r, 2 * i + 1) * xc;
+                    }
+                    G[j][0] = c * m0 + s * m1 + ga * a0;
+                    G[j][1] = -s * m0 + c * m1 + ga * a1;
+                }
+                if (mode == 2) {
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r) {
+                        if (r >= R) break;
+                        const int q_ = k * R + r;
+                        const float yv = sm[L::SY + q_ * kCW + cc];
+                        float yt = 0.f;
+#pragma unroll
+                        for (int j = 0; j < NPL; ++j) {
+                            const int i = i0 + j;
+                            const float c0 = row_sum16(G[j][0] * yv), c1 = row_sum16(G[j][1] * yv);
+                            if (cc == 0 && piv(j)) {
+                                sm[L::SCB + q_ * NPAD + 2 * i] = c0;
+                                sm[L::SCB + q_ * NPAD + 2 * i + 1] = c1;
+                            }
+                            if (piv(j)) yt += sm[L::SC + q_ * NPAD + 2 * i] * G[j][0] + sm[L::SC + q_ * NPAD + 2 * i + 1] * G[j][1];
+                        }
+                        if (p.z) {
+                            yt = rows_sum4(yt);
+                            if (rho == 0) sm[L::SXG + (w * kRows + q_) * kCW + cc] = yt;
                         }
                     }
-                    G[j][0][q] = c * m0 + s * m1 + ga * a0;
-                    G[j][1][q] = -s * m0 + c * m1 + ga * a1;
                 }
             }
-            // gradient of c (sum over columns) and, with the gate, the ungated output (sum over pairs)
-#pragma unroll
-            for (int r = 0; r < RMAX; ++r) {
-                if (r >= R) break;
-                const int q_ = k * R + r;
-#pragma unroll
-                for (int j = 0; j < NPLM; ++j) {
-                    if (j >= npl) break;
-                    const int i = grp * npl + j;
-                    float c0 = 0.f, c1 = 0.f;
-#pragma unroll
-                    for (int q = 0; q < CPLM; ++q) {
-                        if (q >= cpl) break;
-                        const int pc = cc * cpl + q;
-                        const float yv = pc < P ? L.sy[q_ * P + pc] : 0.f;
-                        c0 += G[j][0][q] * yv;
-                        c1 += G[j][1][q] * yv;
-                    }
-                    c0 = row_sum16(c0);
-                    c1 = row_sum16(c1);
-                    if (cc == 0 && i < N2) {
-                        L.scb[q_ * N + 2 * i] = c0;
-                        L.scb[q_ * N + 2 * i + 1] = c1;
-                    }
+            if (mode == 2) {
+                __syncthreads();
+                // the gradient of c (this group's share) for the reverse sweep and the final kernel
+                for (int e = tid; e < Tv * R * N; e += 256) {
+                    const int q_ = e / N, n = e - q_ * N;
+                    const int64_t t = t0 + q_ / R;
+                    p.cbar[((cg * BH + bh) * T + t) * (int64_t)N * R + n * R + q_ % R] = sm[L::SCB + q_ * NPAD + n];
                 }
-                if (p.z) {
+                if (p.z && p.dz) {
+                    for (int e = tid; e < Tv * R * kCW; e += 256) {
+                        const int q_ = e / kCW, c2 = e - q_ * kCW;
+                        if (cg * kCW + c2 >= P) continue;
+                        const int64_t t = t0 + q_ / R;
+                        const int64_t o = ((b * T + t) * H + h) * P * R + (int64_t)(cg * kCW + c2) * R + q_ % R;
+                        float yf = p.D[h] * sm[L::SX + (R + q_) * kCW + c2];
 #pragma unroll
-                    for (int q = 0; q < CPLM; ++q) {
-                        if (q >= cpl) break;
-                        const int pc = cc * cpl + q;
-                        float acc = 0.f;
-#pragma unroll
-                        for (int j = 0; j < NPLM; ++j) {
-                            if (j >= npl) break;
-                            const int i = grp * npl + j;
-                            if (i < N2) acc += L.sc[q_ * N + 2 * i] * G[j][0][q] + L.sc[q_ * N + 2 * i + 1] * G[j][1][q];
-                        }
-                        acc = rows_sum4(acc);
-                        if (rho == 0 && pc < P) L.sxg[(w * kRows + q_) * P + pc] = acc;
+                        for (int ww = 0; ww < 4; ++ww) yf += sm[L::SXG + (ww * kRows + q_) * kCW + c2];
+                        const float zv = Io::ld((const ET *)p.z + o), sgz = sigmoid_f(zv);
+                        Io::st((ET *)p.dz + o, Io::ld((const ET *)p.dy + o) * yf * sgz * (1.f + zv * (1.f - sgz)));
                     }
                 }
             }
-        }
-        __syncthreads();
-        // the gradient of c is complete: keep it for the reverse sweep, and turn it into dC
-        for (int e = tid; e < Tv * R * N; e += 256) {
-            const int q_ = e / N, n = e - q_ * N;
-            const int64_t t = t0 + q_ / R;
-            p.cbar[((bh * T + t) * N + n) * R + q_ % R] = L.scb[q_ * N + n];
-        }
-        for (int r = w, sl = 0; r < R; r += 4, ++sl) {
-            for (int k = 0; k < Tv; ++k) {
-                const int q_ = k * R + r;
-                const int64_t bth = (b * T + t0 + k) * H + h;
-                norm_row_bwd<Io>(p, (const ET *)p.Cm + bth * N * R + r, R, p.cnw, L.srn[q_ * 2 + 1], L.scb + q_ * N,
-                                 p.dC ? (ET *)p.dC + bth * N * R + r : nullptr, gC, bC[sl]);
+            if (mode == 0 && cg == 0) {
+                // angle totals of the segment, per pair
+                for (int i = tid; i < N2; i += 256) {
+                    float a = blk == 0 ? 0.f : p.pseg[(bh * p.nseg + seg) * N2 + i];
+                    if (i < NR)
+                        for (int k = 0; k < Tv; ++k) a += p.theta[((b * T + t0 + k) * H + h) * (int64_t)NR + i];
+                    p.pseg[(bh * p.nseg + seg) * N2 + i] = a;
+                }
             }
         }
-        if (p.z && p.dz) {
-            for (int e = tid; e < Tv * R * P; e += 256) {
-                const int q_ = e / P, pc = e - q_ * P;
-                const int64_t t = t0 + q_ / R;
-                const int r = q_ % R;
-                const int64_t o = ((b * T + t) * H + h) * P * R + (int64_t)pc * R + r;
-                const float yf = L.sxg[(0 * kRows + q_) * P + pc] + L.sxg[(1 * kRows + q_) * P + pc] +
-                                 L.sxg[(2 * kRows + q_) * P + pc] + L.sxg[(3 * kRows + q_) * P + pc] +
-                                 Dh * L.sx[(R + q_) * P + pc];
-                const float zv = Io::ld((const ET *)p.z + o), sgz = sigmoid_f(zv);
-                Io::st((ET *)p.dz + o, Io::ld((const ET *)p.dy + o) * yf * sgz * (1.f + zv * (1.f - sgz)));
+        if (mode == 0) {
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) {
+                const int i = i0 + j;
+                if (!piv(j)) continue;
+                p.Gagg[(sidx * N + 2 * i) * kCW + cc] = G[j][0];
+                p.Gagg[(sidx * N + 2 * i + 1) * kCW + cc] = G[j][1];
             }
+            if (cg == 0 && tid == 0) p.lseg[bh * p.nseg + seg] = lsum;
+            return;
         }
     }
 
-    // ---------------------------------------------------------------- final state
-    // b of the last token (complex form) is in the last staged block: rows R + (Tv-1) R + r
-    const int TvL = T > 0 ? (int)(T - (int64_t)(nblk - 1) * TBt) : 0;
-    float Gb[NPLM][2][CPLM];
-    float K[NPLM][2][2];
-    float bpend[RMAX][NPLM][2];
-    float thf[NPLM];  // gradient of the final angle
+    // ---------------------------------------------------------------- reverse sweep (modes 1, 2)
+    float Gb[NPL][2], K[NPL][2][2], bpend[RMAX][NPL][2];
 #pragma unroll
-    for (int j = 0; j < NPLM; ++j) {
-        const int i = grp * npl + j;
-        const bool iv = j < npl && i < N2;
-        float s0 = 0.f, c0 = 1.f;
-        if (iv && i < NR && th_run[j] != 0.0) fast_sincos((float)wrap_2pi(th_run[j]), s0, c0);
-        float tj = 0.f, k00 = 0.f, k01 = 0.f, k10 = 0.f, k11 = 0.f;
+    for (int j = 0; j < NPL; ++j) {
+        const int i = i0 + j;
+        Gb[j][0] = Gb[j][1] = 0.f;
+        if (mode == 2 && piv(j)) {
+            Gb[j][0] = p.Ragg[(sidx * N + 2 * i) * kCW + cc];
+            Gb[j][1] = p.Ragg[(sidx * N + 2 * i + 1) * kCW + cc];
+        }
 #pragma unroll
-        for (int q = 0; q < CPLM; ++q) {
-            const int pc = cc * cpl + q;
+        for (int r = 0; r < RMAX; ++r) bpend[r][j][0] = bpend[r][j][1] = 0.f;
+        // K at the segment end: sum over the columns of G_end g_end^T
+        K[j][0][0] = row_sum16(Gb[j][0] * G[j][0]);
+        K[j][0][1] = row_sum16(Gb[j][0] * G[j][1]);
+        K[j][1][0] = row_sum16(Gb[j][1] * G[j][0]);
+        K[j][1][1] = row_sum16(Gb[j][1] * G[j][1]);
+        if (mode == 2 && seg == p.nseg - 1) {
+            // share of the final-angle gradient: <dh_final, J h_final>, h_final = Rot(Theta_final) g
+            float s0 = 0.f, c0 = 1.f;
+            if (piv(j) && i < NR) fast_sincos((float)wrap_2pi((double)p.thfin[bh * N2 + i]), s0, c0);
             float a = 0.f, bq = 0.f;
-            if (iv && q < cpl && pc < P && p.dh1) {
+            if (piv(j) && cv && p.dh1) {
                 a = p.dh1[(bh * N + 2 * i) * P + pc];
                 bq = p.dh1[(bh * N + 2 * i + 1) * P + pc];
             }
-            const float g0 = (q < cpl) ? G[j][0][q] : 0.f, g1 = (q < cpl) ? G[j][1][q] : 0.f;
-            // h_final = Rot(Theta_final) g ; <dh, J h_final>
-            const float hf0 = c0 * g0 - s0 * g1, hf1 = s0 * g0 + c0 * g1;
-            tj += -a * hf1 + bq * hf0;
-            // gradient of g_final: Rot(-Theta_final) dh
-            const float u0 = c0 * a + s0 * bq, u1 = -s0 * a + c0 * bq;
-            Gb[j][0][q] = u0;
-            Gb[j][1][q] = u1;
-            k00 += u0 * g0;
-            k01 += u0 * g1;
-            k10 += u1 * g0;
-            k11 += u1 * g1;
+            const float hf0 = c0 * G[j][0] - s0 * G[j][1], hf1 = s0 * G[j][0] + c0 * G[j][1];
+            const float tj = row_sum16(-a * hf1 + bq * hf0);
+            if (cc == 0 && piv(j)) p.thfp[(bh * p.ncg + cg) * N2 + i] = i < NR ? tj : 0.f;
         }
-        K[j][0][0] = row_sum16(k00);
-        K[j][0][1] = row_sum16(k01);
-        K[j][1][0] = row_sum16(k10);
-        K[j][1][1] = row_sum16(k11);
-        tj = row_sum16(tj);
-        // prev_B of the final state = Rot(Theta_final) b_{T-1}
-#pragma unroll
-        for (int r = 0; r < RMAX; ++r) {
-            float u = 0.f, v = 0.f;
-            if (r < R && iv && p.dpB1) {
-                u = p.dpB1[(bh * N + 2 * i) * R + r];
-                v = p.dpB1[(bh * N + 2 * i + 1) * R + r];
-            }
-            float bl0 = 0.f, bl1 = 0.f;
-            if (r < R && iv) {
-                bl0 = L.sb[(R + (TvL - 1) * R + r) * N + 2 * i];
-                bl1 = L.sb[(R + (TvL - 1) * R + r) * N + 2 * i + 1];
-            }
-            const float pb0 = c0 * bl0 - s0 * bl1, pb1 = s0 * bl0 + c0 * bl1;
-            tj += -u * pb1 + v * pb0;
-            bpend[r][j][0] = c0 * u + s0 * v;
-            bpend[r][j][1] = -s0 * u + c0 * v;
-        }
-        if (iv && i < NR && p.dang1) tj += p.dang1[bh * NR + i];
-        thf[j] = (iv && i < NR) ? tj : 0.f;
-        if (cc == 0 && rho >= 0 && iv) L.sthf[i] = thf[j];
     }
-    // dx pending of the last token: the final state's prev_x gradient
-    __syncthreads();
-    for (int e = tid; e < R * P; e += 256) {
-        const int r = e / P, pc = e - r * P;
-        L.spend[r * P + pc] = p.dpx1 ? p.dpx1[(bh * P + pc) * R + r] : 0.f;
-    }
-
-    // ---------------------------------------------------------------- reverse sweep
-    for (int blk = nblk - 1; blk >= 0; --blk) {
-        const int64_t t0 = (int64_t)blk * TBt;
-        const int Tv = (int)min((int64_t)TBt, T - t0);
+    if (mode == 2) {
         __syncthreads();
-        stage_block<Io>(p, L, b, h, t0, Tv, true);
+        for (int e = tid; e < R * kCW; e += 256) sm[L::SPN + e] = 0.f;
+    }
+    float dDacc = 0.f;
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        const int64_t t0 = ts + (int64_t)blk * TBt;
+        const int Tv = (int)min((int64_t)TBt, te - t0);
+        __syncthreads();
+        stage<Io, NPAD>(p, sm, b, h, cg, t0, Tv, true, mode == 2);
         __syncthreads();
         for (int k = Tv - 1; k >= 0; --k) {
-            const float al = L.ssc[k * 8 + 0], be = L.ssc[k * 8 + 1], ga = L.ssc[k * 8 + 2];
-            float sq = 0.f, sbe = 0.f, sga = 0.f;  // this lane's pairs' shares of the token scalars
+            const float al = sm[L::SSC + k * 8 + 0], be = sm[L::SSC + k * 8 + 1], ga = sm[L::SSC + k * 8 + 2];
+            if (mode == 1) {
 #pragma unroll
-            for (int j = 0; j < NPLM; ++j) {
-                if (j >= npl) break;
-                const int i = grp * npl + j;
-                const bool iv = i < N2;
-                const float c = iv ? L.scs[(k * N2 + i) * 2] : 1.f, s = iv ? L.scs[(k * N2 + i) * 2 + 1] : 0.f;
-                // adjoint input and K update
-                float Kj00 = K[j][0][0], Kj01 = K[j][0][1], Kj10 = K[j][1][0], Kj11 = K[j][1][1];
+                for (int j = 0; j < NPL; ++j) {
+                    const int i = i0 + j;
+                    if (!piv(j)) continue;
+                    const float c = CS(k, i, 0), s = CS(k, i, 1);
+                    float g0 = Gb[j][0], g1 = Gb[j][1];
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r) {
+                        if (r >= R) break;
+                        const int q_ = k * R + r;
+                        const float yv = sm[L::SY + q_ * kCW + cc];
+                        g0 += sm[L::SC + q_ * NPAD + 2 * i] * yv;
+                        g1 += sm[L::SC + q_ * NPAD + 2 * i + 1] * yv;
+                    }
+                    Gb[j][0] = al * (c * g0 - s * g1);
+                    Gb[j][1] = al * (s * g0 + c * g1);
+                }
+                continue;
+            }
+            float sq = 0.f, sbe = 0.f, sga = 0.f;
+#pragma unroll
+            for (int j = 0; j < NPL; ++j) {
+                const int i = i0 + j;
+                const bool iv = piv(j);
+                const float c = iv ? CS(k, i, 0) : 1.f, s = iv ? CS(k, i, 1) : 0.f;
+                float K00 = K[j][0][0], K01 = K[j][0][1], K10 = K[j][1][0], K11 = K[j][1][1];
 #pragma unroll
                 for (int r = 0; r < RMAX; ++r) {
                     if (r >= R) break;
                     const int q_ = k * R + r;
-                    const float c0 = iv ? L.sc[q_ * N + 2 * i] : 0.f, c1 = iv ? L.sc[q_ * N + 2 * i + 1] : 0.f;
-                    const float d0 = iv ? L.scb[q_ * N + 2 * i] : 0.f, d1 = iv ? L.scb[q_ * N + 2 * i + 1] : 0.f;
-                    Kj00 += c0 * d0;
-                    Kj01 += c0 * d1;
-                    Kj10 += c1 * d0;
-                    Kj11 += c1 * d1;
-#pragma unroll
-                    for (int q = 0; q < CPLM; ++q) {
-                        if (q >= cpl) break;
-                        const int pc = cc * cpl + q;
-                        const float yv = pc < P ? L.sy[q_ * P + pc] : 0.f;
-                        Gb[j][0][q] += c0 * yv;
-                        Gb[j][1][q] += c1 * yv;
-                    }
+                    const float c0 = iv ? sm[L::SC + q_ * NPAD + 2 * i] : 0.f, c1 = iv ? sm[L::SC + q_ * NPAD + 2 * i + 1] : 0.f;
+                    const float d0 = iv ? sm[L::SCB + q_ * NPAD + 2 * i] : 0.f, d1 = iv ? sm[L::SCB + q_ * NPAD + 2 * i + 1] : 0.f;
+                    K00 += c0 * d0;
+                    K01 += c0 * d1;
+                    K10 += c1 * d0;
+                    K11 += c1 * d1;
+                    const float yv = sm[L::SY + q_ * kCW + cc];
+                    Gb[j][0] += c0 * yv;
+                    Gb[j][1] += c1 * yv;
                 }
-                // F = K - gamma sum_r u_r b_r^T ;  E = F Q - beta sum_r v_r bprev_r^T
-                float F00 = Kj00, F01 = Kj01, F10 = Kj10, F11 = Kj11;
-                float V00 = 0.f, V01 = 0.f, V10 = 0.f, V11 = 0.f;  // sum_r v_r bprev_r^T
+                float F00 = K00, F01 = K01, F10 = K10, F11 = K11;
+                float V00 = 0.f, V01 = 0.f, V10 = 0.f, V11 = 0.f;
 #pragma unroll
                 for (int r = 0; r < RMAX; ++r) {
                     if (r >= R) break;
-                    float u0 = 0.f, u1 = 0.f, v0 = 0.f, v1 = 0.f;
-#pragma unroll
-                    for (int q = 0; q < CPLM; ++q) {
-                        if (q >= cpl) break;
-                        const int pc = cc * cpl + q;
-                        const float xc = pc < P ? L.sx[(R + k * R + r) * P + pc] : 0.f;
-                        const float xp = pc < P ? L.sx[(k * R + r) * P + pc] : 0.f;
-                        u0 += Gb[j][0][q] * xc;
-                        u1 += Gb[j][1][q] * xc;
-                        v0 += Gb[j][0][q] * xp;
-                        v1 += Gb[j][1][q] * xp;
-                    }
-                    u0 = row_sum16(u0);
-                    u1 = row_sum16(u1);
-                    v0 = row_sum16(v0);
-                    v1 = row_sum16(v1);
-                    const float b0 = iv ? L.sb[(R + k * R + r) * N + 2 * i] : 0.f, b1 = iv ? L.sb[(R + k * R + r) * N + 2 * i + 1] : 0.f;
-                    const float p0 = iv ? L.sb[(k * R + r) * N + 2 * i] : 0.f, p1 = iv ? L.sb[(k * R + r) * N + 2 * i + 1] : 0.f;
+                    const float xc = SX(R + k * R + r), xp = SX(k * R + r);
+                    const float u0 = row_sum16(Gb[j][0] * xc), u1 = row_sum16(Gb[j][1] * xc);
+                    const float v0 = row_sum16(Gb[j][0] * xp), v1 = row_sum16(Gb[j][1] * xp);
+                    const float b0 = iv ? SB(R + k * R + r, 2 * i) : 0.f, b1 = iv ? SB(R + k * R + r, 2 * i + 1) : 0.f;
+                    const float p0 = iv ? SB(k * R + r, 2 * i) : 0.f, p1 = iv ? SB(k * R + r, 2 * i + 1) : 0.f;
                     F00 -= ga * u0 * b0;
                     F01 -= ga * u0 * b1;
                     F10 -= ga * u1 * b0;
@@ -552,7 +547,6 @@ __global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p) {
                     V01 += v0 * p1;
                     V10 += v1 * p0;
                     V11 += v1 * p1;
-                    // gradient of b_t (complete with the part from token t+1) and the part for b_{t-1}
                     const float qv0 = c * v0 - s * v1, qv1 = s * v0 + c * v1;  // Q^T v
                     sga += b0 * u0 + b1 * u1;
                     sbe += p0 * qv0 + p1 * qv1;
@@ -561,219 +555,484 @@ __global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p) {
                     for (int rr = 0; rr < RMAX; ++rr)
                         if (rr == r) { nb0 = bpend[rr][j][0]; nb1 = bpend[rr][j][1]; }
                     if (cc == 0 && iv) {
-                        L.sbb[(k * R + r) * N + 2 * i] = nb0 + ga * u0;
-                        L.sbb[(k * R + r) * N + 2 * i + 1] = nb1 + ga * u1;
+                        const int64_t t = t0 + k;
+                        float *dst = p.bbar + ((cg * BH + bh) * T + t) * (int64_t)N * R;
+                        dst[(2 * i) * R + r] = nb0 + ga * u0;
+                        dst[(2 * i + 1) * R + r] = nb1 + ga * u1;
                     }
 #pragma unroll
                     for (int rr = 0; rr < RMAX; ++rr)
                         if (rr == r) { bpend[rr][j][0] = be * qv0; bpend[rr][j][1] = be * qv1; }
                 }
-                if (cc == 0 && iv && i < NR) L.sth[k * N2 + i] = F01 - F10;
-                // E = F Q - beta V, with Q = [[c, s], [-s, c]]
+                if (cc == 0 && iv && i < NR) p.tbar[((cg * BH + bh) * T + t0 + k) * (int64_t)N2 + i] = F01 - F10;
                 const float E00 = F00 * c - F01 * s - be * V00, E01 = F00 * s + F01 * c - be * V01;
                 const float E10 = F10 * c - F11 * s - be * V10, E11 = F10 * s + F11 * c - be * V11;
-                // d log alpha share: trace(Q^T E) = sum Q[m][a] E[m][a]
                 sq += c * E00 + s * E01 - s * E10 + c * E11;
-                // K_{t-1} = Q^T E (the c dc^T term of token t-1 is added at its own step)
                 K[j][0][0] = c * E00 - s * E10;
                 K[j][0][1] = c * E01 - s * E11;
                 K[j][1][0] = s * E00 + c * E10;
                 K[j][1][1] = s * E01 + c * E11;
             }
-            // dx partials: gamma part for token t, beta part for token t-1 (sums over this lane's pairs)
+            // dx partials: gamma part for token t, beta part for token t-1 (this lane's pairs)
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) {
                 if (r >= R) break;
                 const int q_ = k * R + r;
+                float xg = 0.f, xb = 0.f;
 #pragma unroll
-                for (int q = 0; q < CPLM; ++q) {
-                    if (q >= cpl) break;
-                    const int pc = cc * cpl + q;
-                    float xg = 0.f, xb = 0.f;
-#pragma unroll
-                    for (int j = 0; j < NPLM; ++j) {
-                        if (j >= npl) break;
-                        const int i = grp * npl + j;
-                        if (i >= N2) continue;
-                        const float c = L.scs[(k * N2 + i) * 2], s = L.scs[(k * N2 + i) * 2 + 1];
-                        const float b0 = L.sb[(R + q_) * N + 2 * i], b1 = L.sb[(R + q_) * N + 2 * i + 1];
-                        const float p0 = L.sb[q_ * N + 2 * i], p1 = L.sb[q_ * N + 2 * i + 1];
-                        const float qp0 = c * p0 + s * p1, qp1 = -s * p0 + c * p1;  // Q bprev
-                        xg += b0 * Gb[j][0][q] + b1 * Gb[j][1][q];
-                        xb += qp0 * Gb[j][0][q] + qp1 * Gb[j][1][q];
-                    }
-                    xg = rows_sum4(xg);
-                    xb = rows_sum4(xb);
-                    if (rho == 0 && pc < P) {
-                        L.sxg[(w * kRows + q_) * P + pc] = ga * xg;
-                        L.sxb[(w * kRows + q_) * P + pc] = be * xb;
-                    }
+                for (int j = 0; j < NPL; ++j) {
+                    const int i = i0 + j;
+                    if (!piv(j)) continue;
+                    const float c = CS(k, i, 0), s = CS(k, i, 1);
+                    const float b0 = SB(R + q_, 2 * i), b1 = SB(R + q_, 2 * i + 1);
+                    const float p0 = SB(q_, 2 * i), p1 = SB(q_, 2 * i + 1);
+                    const float qp0 = c * p0 + s * p1, qp1 = -s * p0 + c * p1;  // Q bprev
+                    xg += b0 * Gb[j][0] + b1 * Gb[j][1];
+                    xb += qp0 * Gb[j][0] + qp1 * Gb[j][1];
+                }
+                xg = rows_sum4(xg);
+                xb = rows_sum4(xb);
+                if (rho == 0) {
+                    sm[L::SXG + (w * kRows + q_) * kCW + cc] = ga * xg;
+                    sm[L::SXB + (w * kRows + q_) * kCW + cc] = be * xb;
                 }
             }
-            // token scalars: one share per row of lanes
             sq = rows_sum4(cc == 0 ? sq : 0.f);
             sbe = rows_sum4(cc == 0 ? sbe : 0.f);
             sga = rows_sum4(cc == 0 ? sga : 0.f);
             if (lane == 0) {
-                L.ssp[(k * 4 + w) * 4 + 0] = sq;
-                L.ssp[(k * 4 + w) * 4 + 1] = sbe;
-                L.ssp[(k * 4 + w) * 4 + 2] = sga;
+                sm[L::SSP + (k * 4 + w) * 4 + 0] = sq;
+                sm[L::SSP + (k * 4 + w) * 4 + 1] = sbe;
+                sm[L::SSP + (k * 4 + w) * 4 + 2] = sga;
             }
             // carry: G <- alpha Q^T G
 #pragma unroll
-            for (int j = 0; j < NPLM; ++j) {
-                if (j >= npl) break;
-                const int i = grp * npl + j;
-                const bool iv = i < N2;
-                const float c = iv ? L.scs[(k * N2 + i) * 2] : 1.f, s = iv ? L.scs[(k * N2 + i) * 2 + 1] : 0.f;
-#pragma unroll
-                for (int q = 0; q < CPLM; ++q) {
-                    if (q >= cpl) break;
-                    const float g0 = Gb[j][0][q], g1 = Gb[j][1][q];
-                    Gb[j][0][q] = al * (c * g0 - s * g1);
-                    Gb[j][1][q] = al * (s * g0 + c * g1);
-                }
+            for (int j = 0; j < NPL; ++j) {
+                const int i = i0 + j;
+                if (!piv(j)) continue;
+                const float c = CS(k, i, 0), s = CS(k, i, 1);
+                const float g0 = Gb[j][0], g1 = Gb[j][1];
+                Gb[j][0] = al * (c * g0 - s * g1);
+                Gb[j][1] = al * (s * g0 + c * g1);
             }
         }
+        if (mode == 1) continue;
         __syncthreads();
-        // ---- per-token gradients of the block
-        if (tid < Tv) {
-            const int k = tid;
-            const int64_t bth = (b * T + t0 + k) * H + h;
-            float qv = 0.f, bb = 0.f, gb = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < 4; ++ww) {
-                qv += L.ssp[(k * 4 + ww) * 4 + 0];
-                bb += L.ssp[(k * 4 + ww) * 4 + 1];
-                gb += L.ssp[(k * 4 + ww) * 4 + 2];
-            }
-            const float *sc_ = L.ssc + k * 8;
-            const float al = sc_[0], be = sc_[1], dt = sc_[3], lam = sc_[4], A = sc_[5];
-            float ddt = qv * A + bb * al * (1.f - lam) * (1.f + dt * A) + gb * lam;
-            float dlm = -bb * al * dt + gb * dt;
-            const float dAv = qv * dt + bb * be * dt;
-            ddt *= sc_[6];
-            dlm *= sc_[7];
-            if (p.flags & kFlagDtSoftplus) aDtb += ddt;
-            if (p.flags & kFlagAPerToken) {
-                if (p.dAt) p.dAt[bth] = dAv;
-            } else {
-                aA += dAv;
-            }
-            if (p.ddt) p.ddt[bth] = ddt;
-            if (p.dlam) p.dlam[bth] = dlm;
-        }
-        if (p.dtheta)
-            for (int e = tid; e < Tv * NR; e += 256) {
-                const int k = e / NR, i = e - k * NR;
-                p.dtheta[((b * T + t0 + k) * H + h) * (int64_t)NR + i] = L.sth[k * N2 + i] + L.sthf[i];
-            }
-        // dx: D dy + gamma part + beta part from the next token (or the pending one)
-        for (int e = tid; e < Tv * R * P; e += 256) {
-            const int q_ = e / P, pc = e - q_ * P;
-            const int k = q_ / R, r = q_ - k * R;
-            float v = Dh * L.sy[q_ * P + pc];
-            aD += L.sy[q_ * P + pc] * L.sx[(R + q_) * P + pc];
-#pragma unroll
-            for (int ww = 0; ww < 4; ++ww) v += L.sxg[(ww * kRows + q_) * P + pc];
-            if (k + 1 < Tv) {
-#pragma unroll
-                for (int ww = 0; ww < 4; ++ww) v += L.sxb[(ww * kRows + q_ + R) * P + pc];
-            } else {
-                v += L.spend[r * P + pc];
-            }
-            if (p.dx) Io::st((ET *)p.dx + ((b * T + t0 + k) * H + h) * P * R + (int64_t)pc * R + r, v);
-        }
-        // db rows -> dB
-        for (int r = w, sl = 0; r < R; r += 4, ++sl) {
-            for (int k = 0; k < Tv; ++k) {
-                const int q_ = k * R + r;
-                const int64_t bth = (b * T + t0 + k) * H + h;
-                norm_row_bwd<Io>(p, (const ET *)p.Bm + bth * N * R + r, R, p.bnw, L.srn[q_ * 2 + 0], L.sbb + q_ * N,
-                                 p.dB ? (ET *)p.dB + bth * N * R + r : nullptr, gB, bB[sl]);
-            }
-        }
-        __syncthreads();
-        // pending dx of the previous block's last token: the beta part produced at this block's first token
-        for (int e = tid; e < R * P; e += 256) {
-            const int r = e / P, pc = e - r * P;
+        // token scalars (this group's shares)
+        if (tid < Tv * 3) {
+            const int k = tid / 3, which = tid - 3 * k;
             float v = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < 4; ++ww) v += L.sxb[(ww * kRows + r) * P + pc];
-            L.spend[r * P + pc] = v;
+            for (int ww = 0; ww < 4; ++ww) v += sm[L::SSP + (k * 4 + ww) * 4 + which];
+            p.sbar[((cg * BH + bh) * T + t0 + k) * 4 + which] = v;
+        }
+        // dx of the group's columns: D dy + gamma part + beta part of the next token; a
+        // segment's last token also gets the next segment's share, added by the final kernel
+        for (int e = tid; e < Tv * R * kCW; e += 256) {
+            const int q_ = e / kCW, c2 = e - q_ * kCW;
+            const int k = q_ / R, r = q_ - k * R;
+            const int col = cg * kCW + c2;
+            const float yv = sm[L::SY + q_ * kCW + c2];
+            float v = p.D[h] * yv;
+            dDacc += yv * sm[L::SX + (R + q_) * kCW + c2];
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) v += sm[L::SXG + (ww * kRows + q_) * kCW + c2];
+            const bool last_blk = blk == nblk - 1;
+            if (k + 1 < Tv) {
+#pragma unroll
+                for (int ww = 0; ww < 4; ++ww) v += sm[L::SXB + (ww * kRows + q_ + R) * kCW + c2];
+            } else if (!last_blk) {
+                v += sm[L::SPN + r * kCW + c2];
+            }
+            if (col >= P) continue;
+            if (k + 1 == Tv && last_blk) {
+                p.xlast[(sidx * R + r) * kCW + c2] = v;
+            } else if (p.dx) {
+                Io::st((ET *)p.dx + ((b * T + t0 + k) * H + h) * P * R + (int64_t)col * R + r, v);
+            }
+        }
+        __syncthreads();
+        // beta part produced at this block's first token: for the previous block's last token
+        for (int e = tid; e < R * kCW; e += 256) {
+            float v = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) v += sm[L::SXB + (ww * kRows + e / kCW) * kCW + e % kCW];
+            sm[L::SPN + e] = v;
         }
     }
-    __syncthreads();
-
-    // ---------------------------------------------------------------- initial state
-    // gradient of g_{-1}: Gb;  of b_{-1}: bpend;  of x_{-1}: spend
+    if (mode == 1) {
 #pragma unroll
-    for (int j = 0; j < NPLM; ++j) {
-        const int i = grp * npl + j;
-        const bool iv = j < npl && i < N2;
-        float s0 = 0.f, c0 = 1.f;
-        if (iv && i < NR && p.ang0) fast_sincos((float)wrap_2pi((double)p.ang0[bh * NR + i]), s0, c0);
-        float ta = 0.f;
-#pragma unroll
-        for (int q = 0; q < CPLM; ++q) {
-            const int pc = cc * cpl + q;
-            if (!(iv && q < cpl && pc < P)) continue;
-            const float g0 = Gb[j][0][q], g1 = Gb[j][1][q];
-            if (p.dh0) {
-                p.dh0[(bh * N + 2 * i) * P + pc] = c0 * g0 - s0 * g1;
-                p.dh0[(bh * N + 2 * i + 1) * P + pc] = s0 * g0 + c0 * g1;
-            }
-            float u = 0.f, v = 0.f;
-            if (p.h0) {
-                u = p.h0[(bh * N + 2 * i) * P + pc];
-                v = p.h0[(bh * N + 2 * i + 1) * P + pc];
-            }
-            const float gi0 = c0 * u + s0 * v, gi1 = -s0 * u + c0 * v;  // g_{-1}
-            ta += g0 * gi1 - g1 * gi0;
+        for (int j = 0; j < NPL; ++j) {
+            const int i = i0 + j;
+            if (!piv(j)) continue;
+            p.Ragg[(sidx * N + 2 * i) * kCW + cc] = Gb[j][0];
+            p.Ragg[(sidx * N + 2 * i + 1) * kCW + cc] = Gb[j][1];
         }
-        ta = row_sum16(ta);
+        return;
+    }
+    __syncthreads();
+    // shares of the token before the segment: db (per pair, rank), dx (per column, rank)
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int i = i0 + j;
+        if (!piv(j) || cc != 0) continue;
 #pragma unroll
         for (int r = 0; r < RMAX; ++r) {
-            if (r >= R || !iv) continue;
-            const float d0 = bpend[r][j][0], d1 = bpend[r][j][1];
-            if (p.dpB0 && cc == 0) {
-                p.dpB0[(bh * N + 2 * i) * R + r] = c0 * d0 - s0 * d1;
-                p.dpB0[(bh * N + 2 * i + 1) * R + r] = s0 * d0 + c0 * d1;
-            }
-            const float bi0 = L.sb[r * N + 2 * i], bi1 = L.sb[r * N + 2 * i + 1];  // b_{-1} (staged with block 0)
-            ta += d0 * bi1 - d1 * bi0;
+            if (r >= R) break;
+            p.bpend[(sidx * N + 2 * i) * R + r] = bpend[r][j][0];
+            p.bpend[(sidx * N + 2 * i + 1) * R + r] = bpend[r][j][1];
         }
-        if (p.dang0 && cc == 0 && iv && i < NR) p.dang0[bh * NR + i] = thf[j] + ta;
     }
-    if (p.dpx0)
-        for (int e = tid; e < R * P; e += 256) {
-            const int r = e / P, pc = e - r * P;
-            p.dpx0[(bh * P + pc) * R + r] = L.spend[r * P + pc];
-        }
+    for (int e = tid; e < R * kCW; e += 256) p.xpend[sidx * R * kCW + e] = sm[L::SPN + e];
+    // D gradient share
+    dDacc = wave_sum(dDacc);
+    if (lane == 0) sm[L::SRD + w] = dDacc;
+    __syncthreads();
+    if (tid == 0) p.dDp[sidx] = sm[L::SRD] + sm[L::SRD + 1] + sm[L::SRD + 2] + sm[L::SRD + 3];
+}
 
-    // ---------------------------------------------------------------- parameter partials
-    float *part = p.part + bh * (int64_t)p.pw;
-    // per-thread scalars -> block sums
+// Segment start states from the forward aggregates (in place), and the final angle.
+// One thread per (sequence, column group, pair).
+__global__ __launch_bounds__(256) void bwd_ffold_kernel(BwdParams p) {
+    const int N = p.N, N2 = N / 2, P = p.P, NR = p.nr;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= p.B * p.H * p.ncg * N2) return;
+    const int i = (int)(e % N2);
+    const int64_t q = e / N2;
+    const int cg = (int)(q % p.ncg);
+    const int64_t bh = q / p.ncg;
+    float s0 = 0.f, c0 = 1.f;
+    double th = 0.0;
+    if (p.ang0 && i < NR) {
+        th = (double)p.ang0[bh * NR + i];
+        fast_sincos((float)wrap_2pi(th), s0, c0);
+    }
+    float g[kCW][2];
+#pragma unroll
+    for (int c = 0; c < kCW; ++c) {
+        const int pc = cg * kCW + c;
+        float u = 0.f, v = 0.f;
+        if (p.h0 && pc < P) {
+            u = p.h0[(bh * N + 2 * i) * P + pc];
+            v = p.h0[(bh * N + 2 * i + 1) * P + pc];
+        }
+        g[c][0] = c0 * u + s0 * v;
+        g[c][1] = -s0 * u + c0 * v;
+    }
+    for (int k = 0; k < p.nseg; ++k) {
+        const int64_t sidx = (bh * p.ncg + cg) * p.nseg + k;
+        const float dec = __expf(p.lseg[bh * p.nseg + k]);
+        const float ang = p.pseg[(bh * p.nseg + k) * N2 + i];
+        th += (double)ang;
+        float s, c;
+        fast_sincos((float)wrap_2pi((double)ang), s, c);
+        float *ga = p.Gagg + (sidx * N + 2 * i) * kCW;
+#pragma unroll
+        for (int cc = 0; cc < kCW; ++cc) {
+            const float a0 = ga[cc], a1 = ga[kCW + cc];
+            ga[cc] = g[cc][0];
+            ga[kCW + cc] = g[cc][1];
+            const float u = dec * g[cc][0], v = dec * g[cc][1];
+            g[cc][0] = c * u + s * v + a0;  // Rot(-phi)
+            g[cc][1] = -s * u + c * v + a1;
+        }
+    }
+    if (cg == 0) p.thfin[bh * N2 + i] = i < NR ? (float)wrap_2pi(th) : 0.f;
+}
+
+// Segment end adjoints from the adjoint aggregates (in place), the gradient of the
+// initial h and the initial-angle share from it.  One thread per (sequence, group, pair).
+__global__ __launch_bounds__(256) void bwd_rfold_kernel(BwdParams p) {
+    const int N = p.N, N2 = N / 2, P = p.P, NR = p.nr;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= p.B * p.H * p.ncg * N2) return;
+    const int i = (int)(e % N2);
+    const int64_t q = e / N2;
+    const int cg = (int)(q % p.ncg);
+    const int64_t bh = q / p.ncg;
+    float s0 = 0.f, c0 = 1.f;
+    if (i < NR) fast_sincos(p.thfin[bh * N2 + i], s0, c0);
+    float a[kCW][2];
+#pragma unroll
+    for (int c = 0; c < kCW; ++c) {
+        const int pc = cg * kCW + c;
+        float u = 0.f, v = 0.f;
+        if (p.dh1 && pc < P) {
+            u = p.dh1[(bh * N + 2 * i) * P + pc];
+            v = p.dh1[(bh * N + 2 * i + 1) * P + pc];
+        }
+        a[c][0] = c0 * u + s0 * v;  // Rot(-Theta_final) dh_final
+        a[c][1] = -s0 * u + c0 * v;
+    }
+    for (int k = p.nseg - 1; k >= 0; --k) {
+        const int64_t sidx = (bh * p.ncg + cg) * p.nseg + k;
+        const float dec = __expf(p.lseg[bh * p.nseg + k]);
+        float s, c;
+        fast_sincos((float)wrap_2pi((double)p.pseg[(bh * p.nseg + k) * N2 + i]), s, c);
+        float *ra = p.Ragg + (sidx * N + 2 * i) * kCW;
+#pragma unroll
+        for (int cc = 0; cc < kCW; ++cc) {
+            const float r0 = ra[cc], r1 = ra[kCW + cc];
+            ra[cc] = a[cc][0];
+            ra[kCW + cc] = a[cc][1];
+            const float u = dec * a[cc][0], v = dec * a[cc][1];
+            a[cc][0] = c * u - s * v + r0;  // Rot(+phi)
+            a[cc][1] = s * u + c * v + r1;
+        }
+    }
+    // gradient of g_{-1} -> dh0 = Rot(Theta_init) a ; initial-angle share <a, -J g_{-1}>
+    float si = 0.f, ci = 1.f;
+    if (p.ang0 && i < NR) fast_sincos((float)wrap_2pi((double)p.ang0[bh * NR + i]), si, ci);
+    float ta = 0.f;
+#pragma unroll
+    for (int c = 0; c < kCW; ++c) {
+        const int pc = cg * kCW + c;
+        if (pc >= P) continue;
+        if (p.dh0) {
+            p.dh0[(bh * N + 2 * i) * P + pc] = ci * a[c][0] - si * a[c][1];
+            p.dh0[(bh * N + 2 * i + 1) * P + pc] = si * a[c][0] + ci * a[c][1];
+        }
+        if (p.h0) {
+            const float u = p.h0[(bh * N + 2 * i) * P + pc], v = p.h0[(bh * N + 2 * i + 1) * P + pc];
+            const float g0 = ci * u + si * v, g1 = -si * u + ci * v;
+            ta += a[c][0] * g1 - a[c][1] * g0;
+        }
+    }
+    p.dang0p[(bh * p.ncg + cg) * N2 + i] = ta;
+}
+
+// Per-token sums of the column-group shares, the boundary terms, the norm backward
+// of B and C, and the initial state's remaining gradients.  Grid (sequence, 16-token
+// block); one wave per (token, rank) row in the norm backward.
+template <class Io>
+__global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
+    using ET = typename Io::T;
+    __shared__ float s_thf[64];        // total final-angle gradient of the sequence, per pair
+    __shared__ float s_bl[8][128];     // b of the last token (complex form), per rank
+    __shared__ float s_acc[4][3];
+    __shared__ float s_bias[4 * 2 * 8 * 128];  // per wave, side, rank, n
+    const int N = p.N, N2 = N / 2, P = p.P, R = p.R, NR = p.nr;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t bh = blockIdx.x;
+    const int tb = blockIdx.y;
+    const int64_t b = bh / p.H;
+    const int h = (int)(bh - b * p.H);
+    const int64_t T = p.T, H = p.H, BH = p.B * p.H;
+    const int ncg = p.ncg;
+    // b of the last token, then the final-angle gradient
+    for (int r = w; r < R; r += 4) {
+        const int64_t bth = (b * T + T - 1) * H + h;
+        norm_row<Io>(p, (const ET *)p.Bm + bth * N * R + r, R, p.bnw,
+                     p.bbias ? p.bbias + ((int64_t)h * R + r) * N : nullptr, s_bl[r]);
+    }
     __syncthreads();
-    {
-        float v0 = rows_sum4(row_sum16(aD)), v1 = rows_sum4(row_sum16(aA)), v2 = rows_sum4(row_sum16(aDtb));
-        if (lane == 0) {
-            L.sred[w * 4 + 0] = v0;
-            L.sred[w * 4 + 1] = v1;
-            L.sred[w * 4 + 2] = v2;
+    if (tid < N2) {
+        const int i = tid;
+        float v = 0.f;
+        if (i < NR) {
+            for (int cg = 0; cg < ncg; ++cg) v += p.thfp[(bh * ncg + cg) * N2 + i];
+            if (p.dang1) v += p.dang1[bh * NR + i];
+            float s0, c0;
+            fast_sincos(p.thfin[bh * N2 + i], s0, c0);
+            if (p.dpB1)
+                for (int r = 0; r < R; ++r) {
+                    const float u = s_bl[r][2 * i], vv = s_bl[r][2 * i + 1];
+                    const float pb0 = c0 * u - s0 * vv, pb1 = s0 * u + c0 * vv;  // prev_B of the final state
+                    v += -p.dpB1[(bh * N + 2 * i) * R + r] * pb1 + p.dpB1[(bh * N + 2 * i + 1) * R + r] * pb0;
+                }
+        }
+        s_thf[i] = v;
+    }
+    __syncthreads();
+    float aA = 0.f, aDtb = 0.f;
+    float gB[2] = {0.f, 0.f}, gC[2] = {0.f, 0.f};
+    float *part = p.part + (bh * p.ntb + tb) * (int64_t)p.pw;
+    const int64_t t0 = (int64_t)tb * 16;
+    const int Tv = (int)min((int64_t)16, T - t0);
+    // token scalars
+    if (tid < Tv) {
+        const int64_t t = t0 + tid;
+        const int64_t bth = (b * T + t) * H + h;
+        float qv = 0.f, bb = 0.f, gb = 0.f;
+        for (int cg = 0; cg < ncg; ++cg) {
+            const float *s = p.sbar + ((cg * BH + bh) * T + t) * 4;
+            qv += s[0];
+            bb += s[1];
+            gb += s[2];
+        }
+        float dt, lam, dsp, dsg;
+        act_scalars(p, bth, h, dt, lam, dsp, dsg);
+        const float A = (p.flags & kFlagAPerToken) ? p.A[bth] : p.A[h];
+        const float al = __expf(dt * A), be = al * dt * (1.f - lam);
+        float ddt = qv * A + bb * al * (1.f - lam) * (1.f + dt * A) + gb * lam;
+        float dlm = -bb * al * dt + gb * dt;
+        const float dAv = qv * dt + bb * be * dt;
+        ddt *= dsp;
+        dlm *= dsg;
+        if (p.flags & kFlagDtSoftplus) aDtb += ddt;
+        if (p.flags & kFlagAPerToken) {
+            if (p.dAt) p.dAt[bth] = dAv;
+        } else {
+            aA += dAv;
+        }
+        if (p.ddt) p.ddt[bth] = ddt;
+        if (p.dlam) p.dlam[bth] = dlm;
+    }
+    if (p.dtheta)
+        for (int e = tid; e < Tv * NR; e += 256) {
+            const int k = e / NR, i = e - k * NR;
+            const int64_t t = t0 + k;
+            float v = s_thf[i];
+            for (int cg = 0; cg < ncg; ++cg) v += p.tbar[((cg * BH + bh) * T + t) * (int64_t)N2 + i];
+            p.dtheta[((b * T + t) * H + h) * (int64_t)NR + i] = v;
+        }
+    // dx of segment-last tokens: the segment's own part and the next segment's share
+    for (int e = tid; e < Tv * R * P; e += 256) {
+        const int k = e / (R * P), rem = e - k * R * P, r = rem / P, pc = rem - r * P;
+        const int64_t t = t0 + k;
+        if ((t + 1) % p.segT != 0 && t != T - 1) continue;
+        const int seg = (int)(t / p.segT), cg = pc / kCW, c2 = pc - cg * kCW;
+        const int64_t sidx = (bh * ncg + cg) * p.nseg + seg;
+        float v = p.xlast[(sidx * R + r) * kCW + c2];
+        if (t == T - 1) {
+            if (p.dpx1) v += p.dpx1[(bh * P + pc) * R + r];
+        } else {
+            v += p.xpend[((sidx + 1) * R + r) * kCW + c2];
+        }
+        if (p.dx) Io::st((ET *)p.dx + ((b * T + t) * H + h) * P * R + (int64_t)pc * R + r, v);
+    }
+    // db and dc rows: sums of the shares (plus the boundary shares of db), norm backward;
+    // rows spread over the waves, bias gradients collected per wave in LDS
+    for (int e = tid; e < 4 * 2 * R * N; e += 256) s_bias[e] = 0.f;
+    __syncthreads();
+    for (int q = w; q < Tv * R; q += 4) {
+        const int k = q / R, r = q - k * R;
+        const int64_t t = t0 + k;
+        const int64_t bth = (b * T + t) * H + h;
+        const int seg = (int)(t / p.segT);
+        const bool segl = (t + 1) % p.segT == 0 && t != T - 1;
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            const ET *raw = (const ET *)(side == 0 ? p.Bm : p.Cm) + bth * N * R + r;
+            const float *gain = side == 0 ? p.bnw : p.cnw;
+            const float *src = side == 0 ? p.bbar : p.cbar;
+            const bool norm = (p.flags & kFlagNorm) != 0;
+            float v[2], gv[2], ss = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int n = lane + 64 * kk;
+                v[kk] = n < N ? Io::ld(raw + (int64_t)n * R) : 0.f;
+                ss += v[kk] * v[kk];
+                float g = 0.f;
+                if (n < N) {
+                    for (int cg = 0; cg < ncg; ++cg) g += src[((cg * BH + bh) * T + t) * (int64_t)N * R + n * R + r];
+                    if (side == 0 && segl)
+                        for (int cg = 0; cg < ncg; ++cg)
+                            g += p.bpend[(((bh * ncg + cg) * p.nseg + seg + 1) * N + n) * R + r];
+                    if (side == 0 && t == T - 1 && p.dpB1) {
+                        // prev_B of the final state is Rot(Theta_final) b_{T-1}
+                        const int i = n >> 1;
+                        float s0 = 0.f, c0 = 1.f;
+                        if (i < NR) fast_sincos(p.thfin[bh * N2 + i], s0, c0);
+                        const float d0 = p.dpB1[(bh * N + 2 * i) * R + r], d1 = p.dpB1[(bh * N + 2 * i + 1) * R + r];
+                        g += (n & 1) ? (-s0 * d0 + c0 * d1) : (c0 * d0 + s0 * d1);
+                    }
+                }
+                gv[kk] = g;
+            }
+            ss = wave_sum(ss);
+            const float rs = norm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
+            float dot = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int n = lane + 64 * kk;
+                const float gn = (n < N && gain) ? gain[n] : 1.f;
+                dot += gv[kk] * gn * v[kk];
+                if (n < N) s_bias[((w * 2 + side) * R + r) * N + n] += gv[kk];
+                if (norm) (side == 0 ? gB : gC)[kk] += gv[kk] * v[kk] * rs;
+            }
+            dot = wave_sum(dot);
+            ET *out = (ET *)(side == 0 ? p.dB : p.dC);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int n = lane + 64 * kk;
+                if (n >= N || !out) continue;
+                const float gn = gain ? gain[n] : 1.f;
+                const float d = norm ? gv[kk] * gn * rs - dot * rs * rs * rs * v[kk] / (float)N : gv[kk];
+                Io::st(out + bth * N * R + (int64_t)n * R + r, d);
+            }
         }
     }
     __syncthreads();
-    if (tid < 3) part[tid == 0 ? 1 : (tid == 1 ? 0 : 2)] =
-        L.sred[0 * 4 + tid] + L.sred[1 * 4 + tid] + L.sred[2 * 4 + tid] + L.sred[3 * 4 + tid];
-    __syncthreads();
-    // gains: per-wave partials -> sum over waves
+    for (int e = tid; e < 2 * R * N; e += 256) {
+        const int side = e / (R * N), rn = e - side * R * N;
+        float v = 0.f;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int n = lane + 64 * k;
+        for (int ww = 0; ww < 4; ++ww) v += s_bias[(ww * 2 + side) * R * N + rn];
+        part[3 + 2 * N + side * R * N + rn] = v;
+    }
+    // the initial state's prev_B, prev_x and angle gradients (first token block only)
+    if (tb == 0) {
+        for (int e = tid; e < N2 * R; e += 256) {
+            const int i = e / R, r = e - i * R;
+            float d0 = 0.f, d1 = 0.f;
+            for (int cg = 0; cg < ncg; ++cg) {
+                const int64_t sidx = (bh * ncg + cg) * p.nseg;
+                d0 += p.bpend[(sidx * N + 2 * i) * R + r];
+                d1 += p.bpend[(sidx * N + 2 * i + 1) * R + r];
+            }
+            float si = 0.f, ci = 1.f;
+            if (p.ang0 && i < NR) fast_sincos((float)wrap_2pi((double)p.ang0[bh * NR + i]), si, ci);
+            if (p.dpB0) {
+                p.dpB0[(bh * N + 2 * i) * R + r] = ci * d0 - si * d1;
+                p.dpB0[(bh * N + 2 * i + 1) * R + r] = si * d0 + ci * d1;
+            }
+        }
+        if (p.dpx0)
+            for (int e = tid; e < P * R; e += 256) {
+                const int pc = e / R, r = e - pc * R, cg = pc / kCW;
+                p.dpx0[(bh * P + pc) * R + r] = p.xpend[(((bh * ncg + cg) * p.nseg) * R + r) * kCW + pc % kCW];
+            }
+        if (p.dang0 && tid < NR) {
+            const int i = tid;
+            float v = s_thf[i];
+            for (int cg = 0; cg < ncg; ++cg) v += p.dang0p[(bh * ncg + cg) * N2 + i];
+            for (int r = 0; r < R; ++r) {
+                float d0 = 0.f, d1 = 0.f;
+                for (int cg = 0; cg < ncg; ++cg) {
+                    const int64_t sidx = (bh * ncg + cg) * p.nseg;
+                    d0 += p.bpend[(sidx * N + 2 * i) * R + r];
+                    d1 += p.bpend[(sidx * N + 2 * i + 1) * R + r];
+                }
+                float u, vv;
+                init_b(p, bh, i, r, u, vv);
+                v += d0 * vv - d1 * u;
+            }
+            p.dang0[bh * NR + i] = v;
+        }
+    }
+    // parameter partials of this block
+    {
+        const float v1 = wave_sum(aA), v2 = wave_sum(aDtb);
+        if (lane == 0) {
+            s_acc[w][0] = v1;
+            s_acc[w][1] = v2;
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        part[0] = s_acc[0][0] + s_acc[1][0] + s_acc[2][0] + s_acc[3][0];
+        part[2] = s_acc[0][1] + s_acc[1][1] + s_acc[2][1] + s_acc[3][1];
+        part[1] = 0.f;  // D is summed from the sweep shares
+    }
+    __syncthreads();
+    // gains: per-wave sums through LDS
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int n = lane + 64 * kk;
         if (n < N) {
-            L.sred[(w * 2 + 0) * N + n] = gB[k];
-            L.sred[(w * 2 + 1) * N + n] = gC[k];
+            s_bias[(w * 2 + 0) * N + n] = gB[kk];
+            s_bias[(w * 2 + 1) * N + n] = gC[kk];
         }
     }
     __syncthreads();
@@ -781,53 +1040,61 @@ __global__ __launch_bounds__(256) void bwd_seq_kernel(BwdParams p) {
         const int side = e / N, n = e - side * N;
         float v = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) v += L.sred[(ww * 2 + side) * N + n];
+        for (int ww = 0; ww < 4; ++ww) v += s_bias[(ww * 2 + side) * N + n];
         part[3 + side * N + n] = v;
     }
-    // biases: rank r is owned by wave r % 4 (slot r / 4)
-    for (int r = w, sl = 0; r < R; r += 4, ++sl) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int n = lane + 64 * k;
-            if (n < N) {
-                part[3 + 2 * N + r * N + n] = sl == 0 ? bB[0][k] : bB[1][k];
-                part[3 + 2 * N + R * N + r * N + n] = sl == 0 ? bC[0][k] : bC[1][k];
-            }
-        }
-    }
-    (void)H;
 }
 
-// Sums of the per-sequence partials: A (per head), D, dt bias over the batch; gains over
-// batch and heads; biases over the batch.
+// Parameter gradients: one workgroup per parameter element sums its records (the final
+// kernel's per (sequence, token block) records, the sweeps' D shares) in a fixed order.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
+    __shared__ float s_red[256];
     const int H = p.H, N = p.N, R = p.R;
     const int64_t Bn = p.B;
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    const int nH = 3 * H, nG = 2 * N, nBias = 2 * H * R * N;
+    const int e = blockIdx.x, tid = threadIdx.x;
+    const int nH = 3 * H, nG = 2 * N;
+    const int ntb = p.ntb;
+    float *dst = nullptr;
+    float v = 0.f;
     if (e < nH) {
         const int which = e / H, h = e - which * H;  // 0: A, 1: D, 2: dt bias
-        float *dst = which == 0 ? p.dA : (which == 1 ? p.dD : p.ddtb);
-        if (!dst) return;
-        float v = 0.f;
-        for (int64_t b = 0; b < Bn; ++b) v += p.part[(b * H + h) * (int64_t)p.pw + which];
-        dst[h] = v;
+        dst = which == 0 ? p.dA : (which == 1 ? p.dD : p.ddtb);
+        if (dst) dst += h;
+        if (which == 1) {
+            const int per = p.ncg * p.nseg;
+            for (int64_t k = tid; k < Bn * per; k += 256) {
+                const int64_t b = k / per;
+                v += p.dDp[(b * H + h) * (int64_t)per + (k - b * per)];
+            }
+        } else {
+            for (int64_t k = tid; k < Bn * ntb; k += 256) {
+                const int64_t b = k / ntb;
+                v += p.part[((b * H + h) * ntb + (k - b * ntb)) * (int64_t)p.pw + which];
+            }
+        }
     } else if (e < nH + nG) {
-        const int k = e - nH, side = k / N, n = k - side * N;
-        float *dst = side == 0 ? p.dbnw : p.dcnw;
-        if (!dst) return;
-        float v = 0.f;
-        for (int64_t s = 0; s < Bn * H; ++s) v += p.part[s * p.pw + 3 + side * N + n];
-        dst[n] = v;
-    } else if (e < nH + nG + nBias) {
-        const int k = e - nH - nG, side = k / (H * R * N), rem = k - side * (H * R * N);
+        const int k2 = e - nH, side = k2 / N, n = k2 - side * N;
+        dst = side == 0 ? p.dbnw : p.dcnw;
+        if (dst) dst += n;
+        for (int64_t s = tid; s < Bn * H * ntb; s += 256) v += p.part[s * p.pw + 3 + side * N + n];
+    } else {
+        const int k2 = e - nH - nG, side = k2 / (H * R * N), rem = k2 - side * (H * R * N);
         const int h = rem / (R * N), rn = rem - h * (R * N);
-        float *dst = side == 0 ? p.dbb : p.dcb;
-        if (!dst) return;
-        float v = 0.f;
-        for (int64_t b = 0; b < Bn; ++b) v += p.part[(b * H + h) * (int64_t)p.pw + 3 + 2 * N + side * R * N + rn];
-        dst[(int64_t)h * R * N + rn] = v;
+        dst = side == 0 ? p.dbb : p.dcb;
+        if (dst) dst += rem;
+        for (int64_t k = tid; k < Bn * ntb; k += 256) {
+            const int64_t b = k / ntb;
+            v += p.part[((b * H + h) * ntb + (k - b * ntb)) * (int64_t)p.pw + 3 + 2 * N + side * R * N + rn];
+        }
     }
+    if (!dst) return;  // uniform over the workgroup
+    s_red[tid] = v;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+        if (tid < st) s_red[tid] += s_red[tid + st];
+        __syncthreads();
+    }
+    if (tid == 0) *dst = s_red[0];
 }
 
 // T == 0: the initial state's gradients are the final state's, every parameter gradient is 0.
@@ -840,7 +1107,7 @@ __global__ __launch_bounds__(256) void bwd_empty_kernel(BwdParams p) {
     if (p.dpx0 && e < nbh * P * R) p.dpx0[e] = p.dpx1 ? p.dpx1[e] : 0.f;
     if (p.dang0 && e < nbh * p.nr) p.dang0[e] = p.dang1 ? p.dang1[e] : 0.f;
     if (e < H) {
-        if (p.dA && !(p.flags & kFlagAPerToken)) p.dA[e] = 0.f;
+        if (p.dA) p.dA[e] = 0.f;
         if (p.dD) p.dD[e] = 0.f;
         if (p.ddtb) p.ddtb[e] = 0.f;
     }
@@ -854,29 +1121,29 @@ __global__ __launch_bounds__(256) void bwd_empty_kernel(BwdParams p) {
     }
 }
 
+template <class Io, int NPAD>
+static void launch_sweeps(const BwdParams &p, hipStream_t st, int mode) {
+    const dim3 grid((unsigned)(p.B * p.H * p.ncg * p.nseg)), blk(256);
+    if (p.R == 1) hipLaunchKernelGGL((bwd_sweep_kernel<Io, NPAD, 1>), grid, blk, 0, st, p, mode);
+    else hipLaunchKernelGGL((bwd_sweep_kernel<Io, NPAD, 8>), grid, blk, 0, st, p, mode);
+}
+
 template <class Io>
 static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
-    const size_t lds = bwd_lds_bytes(p.N, p.P, p.R);
-    const bool big = (p.N / 2 + 15) / 16 > 2 || (p.P + 15) / 16 > 4;
-    const dim3 grid((unsigned)(p.B * p.H)), blk(256);
-#define M3_BWD_LAUNCH(NPLM, CPLM, RMAX)                                                                      \
-    do {                                                                                                     \
-        auto kern = bwd_seq_kernel<Io, NPLM, CPLM, RMAX>;                                                    \
-        if (lds > 65536) {                                                                                   \
-            hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                               (int)lds);                                                    \
-            if (e != hipSuccess) return e;                                                                   \
-        }                                                                                                    \
-        hipLaunchKernelGGL(kern, grid, blk, lds, st, p);                                                     \
-    } while (0)
-    if (p.B * p.H > 0 && p.T > 0) {
-        if (big) {
-            if (p.R == 1) M3_BWD_LAUNCH(4, 8, 1); else M3_BWD_LAUNCH(4, 8, 8);
-        } else {
-            if (p.R == 1) M3_BWD_LAUNCH(2, 4, 1); else M3_BWD_LAUNCH(2, 4, 8);
-        }
-    }
-#undef M3_BWD_LAUNCH
+    const int npad = p.N <= 32 ? 32 : (p.N <= 64 ? 64 : 128);
+    auto sweep = [&](int mode) {
+        if (npad == 32) launch_sweeps<Io, 32>(p, st, mode);
+        else if (npad == 64) launch_sweeps<Io, 64>(p, st, mode);
+        else launch_sweeps<Io, 128>(p, st, mode);
+    };
+    const int64_t nfold = p.B * p.H * p.ncg * (p.N / 2);
+    const dim3 fgrid((unsigned)((nfold + 255) / 256));
+    sweep(0);
+    hipLaunchKernelGGL(bwd_ffold_kernel, fgrid, dim3(256), 0, st, p);
+    sweep(1);
+    hipLaunchKernelGGL(bwd_rfold_kernel, fgrid, dim3(256), 0, st, p);
+    sweep(2);
+    hipLaunchKernelGGL((bwd_final_kernel<Io>), dim3((unsigned)(p.B * p.H), (unsigned)p.ntb), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -892,11 +1159,8 @@ hipError_t launch_bwd(bool bf16, const BwdParams &p, hipStream_t st) {
     hipError_t e = bf16 ? launch_bwd_t<IoBF16>(p, st) : launch_bwd_t<IoF32>(p, st);
     if (e != hipSuccess) return e;
     const int total = 3 * p.H + 2 * p.N + 2 * p.H * p.R * p.N;
-    if (p.B * p.H > 0 && p.T > 0) {
-        hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, p);
-        e = hipGetLastError();
-    }
-    return e;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)total), dim3(256), 0, st, p);
+    return hipGetLastError();
 }
 
 }  // namespace m3

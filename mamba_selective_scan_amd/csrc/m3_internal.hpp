@@ -67,7 +67,9 @@ struct StepParams {
     float *h, *pB, *px, *ang;
 };
 
-// Gradients of a scan (reverse-mode), one workgroup per (batch, head) sequence.
+// Gradients of a scan (reverse-mode).  The state columns are split into groups of 16
+// and the tokens into segments; every backward quantity is linear in the per-column
+// contributions, so per-group partial sums are added by a final per-token kernel.
 struct BwdParams {
     int64_t B, T;
     int H, P, N, R;
@@ -87,14 +89,32 @@ struct BwdParams {
     void *dx, *dB, *dC, *dz;                  // io dtype
     float *ddt, *dlam, *dtheta, *dAt;         // dAt: per-token A gradient (kFlagAPerToken) or NULL
     float *dh0, *dpB0, *dpx0, *dang0;         // or NULL
-    // parameter gradients, summed over sequences by bwd_reduce_kernel (each may be NULL)
+    // parameter gradients (each may be NULL); summed by bwd_reduce_kernel
     float *dA, *dD, *dbnw, *dcnw, *dbb, *dcb, *ddtb;
-    // workspace
-    float *cbar;  // [B*H][T][N][R] gradient of the normalised C (forward sweep -> reverse sweep)
-    float *part;  // [B*H][pw] per-sequence partial sums of the parameter gradients
-    int pw;
+    // plan
+    int ncg;   // column groups of 16 columns
+    int nseg;  // segments per sequence
+    int segT;  // tokens per segment (a multiple of the tokens per staged block)
+    int ntb;   // token blocks of the final kernel (16 tokens each)
+    int pw;    // floats per partial-sum record of the final kernel
+    // workspace (fp32)
+    float *Gagg;   // [BH][ncg][nseg][N][16]  forward aggregates -> (in place) segment start states
+    float *Ragg;   // [BH][ncg][nseg][N][16]  reverse aggregates -> (in place) segment end adjoints
+    float *lseg;   // [BH][nseg]       sum of log alpha over the segment
+    float *pseg;   // [BH][nseg][N/2]  sum of theta over the segment
+    float *thfin;  // [BH][N/2]        final angle
+    float *cbar;   // [ncg][BH*T][N][R] gradient of c, share of the column group
+    float *bbar;   // [ncg][BH*T][N][R] gradient of b, share
+    float *tbar;   // [ncg][BH*T][N/2]  local angle gradient, share
+    float *sbar;   // [ncg][BH*T][4]    d log alpha, beta and gamma gradients, shares
+    float *xlast;  // [BH][ncg][nseg][R][16] dx of a segment's last token without the next segment's share
+    float *xpend;  // [BH][ncg][nseg][R][16] dx share of the token before the segment
+    float *bpend;  // [BH][ncg][nseg][N][R]  db share of the token before the segment
+    float *thfp;   // [BH][ncg][N/2]  final-angle gradient share (last segment)
+    float *dang0p; // [BH][ncg][N/2]  initial-angle gradient share from the initial state
+    float *dDp;    // [BH][ncg][nseg] D gradient shares
+    float *part;   // [BH][ntb][pw]   parameter partial sums of the final kernel
 };
-size_t bwd_lds_bytes(int N, int P, int R);
 hipError_t launch_bwd(bool bf16, const BwdParams &p, hipStream_t stream);
 
 // Tile variant chosen by the host.
