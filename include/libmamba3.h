@@ -199,8 +199,14 @@ size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape);
  *   dinit:  where to write the gradients of the initial state, or NULL.
  * The pages ask for a differentiable scan (torchmamba "Verification": fp64 gradchecks;
  * dotLLM PR #136: a trainable block) but print no backward; this is the adjoint of the
- * recurrence, recomputing the forward states (no forward activations are stored);
- * the workspace holds per-segment states and per-token partial sums.
+ * chunked forward, recomputing the forward states (no forward activations are stored):
+ * chunks of 64 (token, rank) rows; the workspace holds the state before and the adjoint
+ * after every chunk (2 * B * H * ceil(T / (64 / R)) * N * P floats) plus per-chunk and
+ * per-token partial sums.  The chunk length of the shape is not used.  Gradient pointers
+ * in grads may be NULL (not computed), except dz of a gated call.  Parameter gradients
+ * are sums over the batch in a fixed order; the gains' and biases' per-chunk parts are
+ * accumulated with LDS atomics (last-bit differences between calls are possible there).
+ * Errors as for the forward call; T == 0 passes the final state's gradients through.
  */
 m3_status m3_scan_bwd(const m3_shape *shape, const m3_inputs *in, const void *dy, const m3_state *init,
                       const m3_state *dfinal, m3_grads *grads, m3_state *dinit, void *ws, size_t ws_bytes,

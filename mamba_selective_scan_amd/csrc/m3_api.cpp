@@ -236,47 +236,33 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
 }
 
 struct BwdPlan {
-    int ncg, nseg, segT, ntb, pw;
-    size_t Gagg, Ragg, lseg, pseg, thfin, cbar, bbar, tbar, sbar, xlast, xpend, bpend, thfp, dang0p, dDp, part;
+    int nck, pw;
+    size_t Sst, Ust, lsum, phic, thst, G0w, hfin, tot, dsc, deta0, part;
     size_t total;
 };
 
-// Column groups of 16 state columns, time segments of a whole number of 16-row blocks,
-// about 4096 (sequence, group, segment) workgroups.
+// Chunks of 64 (token, rank) rows; per chunk a state and an adjoint (N x P fp32 each).
 BwdPlan bwd_plan_of(const m3_shape *s) {
     BwdPlan pl{};
     const int64_t BH = s->batch * (int64_t)s->nheads, T = s->seqlen;
-    const int N = s->dstate, R = s->rank, N2 = N / 2;
-    pl.ncg = (s->headdim + 15) / 16;
-    const int tbt = 16 / R;  // tokens per staged block
-    const int64_t nbt = T > 0 ? (T + tbt - 1) / tbt : 0;
-    int64_t want = BH * pl.ncg > 0 ? (4096 + BH * pl.ncg - 1) / (BH * pl.ncg) : 1;
-    if (want < 1) want = 1;
-    if (want > nbt) want = nbt > 0 ? nbt : 1;
-    const int64_t bps = nbt > 0 ? (nbt + want - 1) / want : 1;
-    pl.segT = (int)(bps * tbt);
-    pl.nseg = T > 0 ? (int)((T + pl.segT - 1) / pl.segT) : 1;
-    pl.ntb = T > 0 ? (int)((T + 15) / 16) : 1;
+    const int N = s->dstate, R = s->rank, N2 = N / 2, P = s->headdim;
+    const int qt = 64 / R;
+    pl.nck = T > 0 ? (int)((T + qt - 1) / qt) : 1;
     pl.pw = 3 + 2 * N + 2 * R * N;
-    const int64_t G = BH * pl.ncg * pl.nseg;
+    const int64_t C = BH * pl.nck;
     size_t off = 0;
     auto take = [&](size_t &at, int64_t floats) { at = off; off = align_up(off + sizeof(float) * (size_t)floats); };
-    take(pl.Gagg, G * N * 16);
-    take(pl.Ragg, G * N * 16);
-    take(pl.lseg, BH * pl.nseg);
-    take(pl.pseg, BH * pl.nseg * N2);
-    take(pl.thfin, BH * N2);
-    take(pl.cbar, pl.ncg * BH * T * N * R);
-    take(pl.bbar, pl.ncg * BH * T * N * R);
-    take(pl.tbar, pl.ncg * BH * T * N2);
-    take(pl.sbar, pl.ncg * BH * T * 4);
-    take(pl.xlast, G * R * 16);
-    take(pl.xpend, G * R * 16);
-    take(pl.bpend, G * N * R);
-    take(pl.thfp, BH * pl.ncg * N2);
-    take(pl.dang0p, BH * pl.ncg * N2);
-    take(pl.dDp, G);
-    take(pl.part, BH * pl.ntb * pl.pw);
+    take(pl.Sst, C * N * P);
+    take(pl.Ust, C * N * P);
+    take(pl.lsum, C);
+    take(pl.phic, C * N2);
+    take(pl.thst, BH * N2);
+    take(pl.G0w, BH * N * P);
+    take(pl.hfin, BH * N * P);
+    take(pl.tot, C * N2);
+    take(pl.dsc, BH * T * 3);
+    take(pl.deta0, BH);
+    take(pl.part, C * pl.pw);
     pl.total = (T == 0 || BH == 0) ? 0 : off;
     return pl;
 }
@@ -362,28 +348,20 @@ m3_status bwd_impl(const m3_shape *s, const m3_inputs *in, const void *dy, const
         p.dpx0 = dinit->prev_x;
         p.dang0 = dinit->angle;
     }
-    p.ncg = pl.ncg;
-    p.nseg = pl.nseg;
-    p.segT = pl.segT;
-    p.ntb = pl.ntb;
+    p.nck = pl.nck;
     p.pw = pl.pw;
     char *base = static_cast<char *>(ws);
     auto at = [&](size_t off) { return pl.total ? reinterpret_cast<float *>(base + off) : nullptr; };
-    p.Gagg = at(pl.Gagg);
-    p.Ragg = at(pl.Ragg);
-    p.lseg = at(pl.lseg);
-    p.pseg = at(pl.pseg);
-    p.thfin = at(pl.thfin);
-    p.cbar = at(pl.cbar);
-    p.bbar = at(pl.bbar);
-    p.tbar = at(pl.tbar);
-    p.sbar = at(pl.sbar);
-    p.xlast = at(pl.xlast);
-    p.xpend = at(pl.xpend);
-    p.bpend = at(pl.bpend);
-    p.thfp = at(pl.thfp);
-    p.dang0p = at(pl.dang0p);
-    p.dDp = at(pl.dDp);
+    p.Sst = at(pl.Sst);
+    p.Ust = at(pl.Ust);
+    p.lsum = at(pl.lsum);
+    p.phic = at(pl.phic);
+    p.thst = at(pl.thst);
+    p.G0w = at(pl.G0w);
+    p.hfin = at(pl.hfin);
+    p.tot = at(pl.tot);
+    p.dsc = at(pl.dsc);
+    p.deta0 = at(pl.deta0);
     p.part = at(pl.part);
     return m3::launch_bwd(s->io == M3_BF16, p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? M3_OK
                                                                                                      : M3_EHIP;

@@ -1,44 +1,46 @@
-// m3_bwd.hip -- gradients of the Mamba-3 trapezoidal scan (reverse mode).
+// m3_bwd.hip -- gradients of the chunked Mamba-3 scan (reverse mode) on gfx950.
 //
 // The pages ask for the scan to be differentiable (torchmamba "Verification":
-// fp64 gradchecks of the scans; dotLLM PR #136: the block trains); they print
-// no backward algorithm.  This is the adjoint of the recurrence, computed in
-// the complex-state form of the rotation (torchmamba "Math notes", M3 SISO,
-// RoPE trick): per pair i the state g_t = Rot(-Theta_t) h_t evolves as
-//     g_t = Q_t (alpha_t g_{t-1} + beta_t b_{t-1} x_{t-1}^T) + gamma_t b_t x_t^T,
-//     y_t = sum_i c_t^T g_t + D x_t,        Q_t = Rot(-theta_t),
-// with b, c the normalised, biased and unrotated B and C, so no cumulative
-// angle enters the sweeps.  The adjoint is
-//     G_{t-1} = alpha_t Q_t^T G_t + c_{t-1} dy_{t-1}^T,
-// and the decay and angle gradients, which need <G_t, g_{t-1}>-type inner
-// products, come from the per-pair 2x2 matrix K_t = sum_p G_t[:, p] g_t[:, p]^T:
-//     K_{t-1} = Q_t^T E_t + c_{t-1} dc_{t-1}^T,
-//     E_t     = (K_t - gamma_t u_t b_t^T) Q_t - beta_t v_t b_{t-1}^T,
-//     u_t = G_t x_t,  v_t = G_t x_{t-1},  dc_t = g_t dy_t   (sums over the columns p),
-//     d log alpha_t = sum_i trace(Q_t^T E_t),  local angle gradient = F01 - F10 of
-//     F = K_t - gamma_t u_t b_t^T.
+// fp64 gradchecks of the scans; dotLLM PR #136: the block trains) and print no
+// backward algorithm.  This is the adjoint of the chunked forward: the same
+// single-scan form of the trapezoid (dotLLM PR #136, "Mamba-3 streaming decode":
+// shifted state g_t = h_t + eta_t B~_t x_t^T with eta_t = dt_{t+1}(1 - lambda_{t+1}))
+// and the same chunk decomposition (torchmamba README, "Math notes", M2 chunked
+// SSD; M3 RoPE trick: B and C rotated by the cumulative angle, so the state
+// carries no rotation inside a chunk).  Per chunk of 64 rows ((token, rank)
+// pairs), in the chunk's own rotation frame (angles summed from the chunk start):
+//     Y   = (L o C~ B~^T) X + diag(e^cs) C~ H,          H: state before the chunk
+//     H'  = Rot(-Phi_end) (e^cs_end H + S),   S = sum_s e^(cs_end - cs_s) kappa_s B~_s x_s^T
+//     L[t, s] = e^(cs_t - cs_s) kappa_s (token(t) > token(s)), gamma_t (same token), 0 (earlier)
+// with kappa = gamma + eta.  With Gb the adjoint of the state after the chunk:
+//     dX   = (L o G)^T dY + diag(e^(cs_end - cs) kappa) B~ Gb + D dY,      G = C~ B~^T
+//     dC~  = (L o dY X^T) B~ + diag(e^cs) dY H^T
+//     dB~  = (L o dY X^T)^T C~ + diag(e^(cs_end - cs) kappa) X Gb^T
+//     d cs_t: row sums minus column sums of L o G o dY X^T over strictly earlier tokens,
+//             plus C~_t . (state term of dC~_t), minus kappa_s B~_s . (state term of dB~_s / kappa_s);
+//             at the chunk's last token also e^cs_end <Gb, H> + the sum of the latter
+//     d log alpha_k = sum of d cs over the chunk's tokens t >= k
+//     d Theta_t (per pair) = <dC~_t, J C~_t> + <dB~_t, J B~_t>,   J = [[0, -1], [1, 0]]
+//     d theta_k = sum of d Theta over all tokens t >= k (+ the final angle's gradient)
+// The state adjoints obey
+//     Gb(before chunk) = Rot(Phi_end of the previous chunk) (e^cs_end Gb + sum_t e^cs_t C~_t dy_t^T).
+// Kernels, in launch order:
+//   bwd_chunk_state_kernel  per chunk: S and U = sum_t e^cs_t C~_t dy_t^T (MFMA), chunk totals
+//   bwd_state_pass_kernel   per (sequence, pair, column): states before each chunk (forward
+//                           over the chunks) and adjoints after each chunk (reverse), in place
+//   bwd_chunk_grad_kernel   per chunk: every gradient above (ten MFMA products), the norm
+//                           backward, local angle sums, per-token scalar gradients
+//   bwd_angle_suffix_kernel per sequence: angle gradient sums of the later chunks
+//   bwd_init_kernel         per sequence: gradients of the initial state (angle: frame rotation)
+//   bwd_token_kernel        per chunk: dt, lambda, A gradients; angle gradients completed
+//   bwd_reduce_kernel       parameter gradients (fixed-order sums of per-chunk records)
 //
-// Every quantity above is linear in the per-column contributions, and the
-// state columns evolve independently, so a workgroup handles one group of 16
-// columns of one time segment of one (batch, head) sequence; partial sums over
-// the column groups are added by the final per-token kernel.  Segments are
-// chained like the forward's: forward aggregates from zero, a fold that turns
-// them into segment start states; reverse aggregates of the adjoint from zero,
-// a fold that turns them into segment end adjoints.  Kernels, in launch order:
-//   bwd_sweep_kernel (mode 0)  forward aggregate of each segment
-//   bwd_ffold_kernel           segment start states, final angle
-//   bwd_sweep_kernel (mode 1)  adjoint aggregate of each segment
-//   bwd_rfold_kernel           segment end adjoints, gradient of the initial h
-//   bwd_sweep_kernel (mode 2)  both sweeps of each segment: column-group shares
-//   bwd_final_kernel           per-token sums, norm backward, boundary terms
-//   bwd_reduce_kernel          parameter gradients
-//
-// Lane layout of a sweep: lane (wave w, row rho, column cc) owns pairs
-// (4 w + rho) * NPL + j of the state and column cc of the group; sums over
-// columns are row all-reduces (DPP), sums over pairs go through per-wave
-// partials in LDS added once per block of 16 (token, rank) rows.
-#include <type_traits>
-
+// Matrix cores: v_mfma_f32_16x16x4_f32 on fp32 operands (full fp32 products for
+// every I/O type).  A 32-wide contraction chunk is a fragment of 8 values per lane,
+// slot j of lane group g carrying logical index 8 g + j (or, for operands taken
+// from result tiles, 16 a + 4 g + j over a pair of tiles); A and B agree on it.
+// Eight waves per chunk: wave (w, half) owns rows 16 w .. 16 w + 15 of the chunk and
+// half of the output column tiles.
 #include "m3_device.hpp"
 #include "m3_internal.hpp"
 
@@ -46,8 +48,9 @@ namespace m3 {
 
 namespace {
 
-constexpr int kRows = 16;  // (token, rank) rows per staged block
-constexpr int kCW = 16;    // state columns per workgroup
+constexpr int kRows = 64;     // rows per chunk
+constexpr int kWaves = 8;     // waves per chunk workgroup
+constexpr int kThreads = 64 * kWaves;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -68,36 +71,26 @@ __device__ __forceinline__ float rows_sum4(float v) {
     return v;
 }
 __device__ __forceinline__ float wave_sum(float v) { return rows_sum4(row_sum16(v)); }
-
-// Normalised (gain, bias) row of raw B or C: one wave, lanes over n.  Returns the norm
-// factor; writes the row to dst[N] (when dst is not NULL).
-template <class Io>
-__device__ __forceinline__ float norm_row(const BwdParams &p, const typename Io::T *raw, int R, const float *gain,
-                                          const float *bias, float *dst) {
-    const int lane = threadIdx.x & 63, N = p.N;
-    const bool norm = (p.flags & kFlagNorm) != 0;
-    float v[2], ss = 0.f;
+// inclusive prefix sum over the 64 lanes of a wave (all lanes active)
+__device__ __forceinline__ float wave_scan_incl(float v) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int n = lane + 64 * k;
-        v[k] = n < N ? Io::ld(raw + (int64_t)n * R) : 0.f;
-        ss += v[k] * v[k];
+    for (int d = 1; d < 64; d <<= 1) {
+        const float u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
     }
-    ss = wave_sum(ss);
-    const float rs = norm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
-    if (dst) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int n = lane + 64 * k;
-            if (n < N) {
-                float u = norm ? v[k] * rs * (gain ? gain[n] : 1.f) : v[k];
-                if (bias) u += bias[n];
-                dst[n] = u;
-            }
-        }
-    }
-    return rs;
+    return v;
 }
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+// acc += A B over one 32-wide contraction chunk (slot j -> instruction j)
+__device__ __forceinline__ f32x4_t mma8(const float (&a)[8], const float (&b)[8], f32x4_t acc) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = mfma_f(a[j], b[j], acc);
+    return acc;
+}
+// logical contraction index of slot j for operands taken from result tiles 2 kc and 2 kc + 1
+__device__ __forceinline__ int tile_k(int kc, int g, int j) { return 32 * kc + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4); }
 
 // dt and lambda after the optional activations, with the activations' derivatives
 __device__ __forceinline__ void act_scalars(const BwdParams &p, int64_t bth, int h, float &dt, float &lam,
@@ -116,975 +109,1099 @@ __device__ __forceinline__ void act_scalars(const BwdParams &p, int64_t bth, int
         dlam_draw = lam * (1.f - lam);
     }
 }
-
-// Complex-form b of the carried previous token: Rot(-Theta_init) prev_B (pair i, rank r)
-__device__ __forceinline__ void init_b(const BwdParams &p, int64_t bh, int i, int r, float &u, float &v) {
-    const int N = p.N, R = p.R;
-    u = v = 0.f;
-    if (p.pB0) {
-        u = p.pB0[(bh * N + 2 * i) * R + r];
-        v = p.pB0[(bh * N + 2 * i + 1) * R + r];
-    }
-    if (p.ang0 && i < p.nr) {
-        float s, c;
-        fast_sincos((float)wrap_2pi((double)p.ang0[bh * p.nr + i]), s, c);
-        const float u2 = c * u + s * v, v2 = -s * u + c * v;
-        u = u2;
-        v = v2;
-    }
+// eta_t = dt_{t+1} (1 - lambda_{t+1}), 0 at the last token (t = -1 gives the initial state's)
+__device__ __forceinline__ float eta_at(const BwdParams &p, int64_t b, int h, int64_t t) {
+    if (t + 1 >= p.T) return 0.f;
+    float dt, lam, u, v;
+    act_scalars(p, (b * p.T + t + 1) * p.H + h, h, dt, lam, u, v);
+    return dt * (1.f - lam);
 }
 
-// LDS layout of the sweep kernel (floats)
-template <int NPAD>
-struct SweepLds {
-    static constexpr int RW = kRows + 8;                // rows incl. the previous token's (R <= 8)
-    static constexpr int SB = 0;                        // [RW][NPAD] b rows (rows 0..R-1: previous token)
-    static constexpr int SX = SB + RW * NPAD;           // [RW][16]   x rows (own columns)
-    static constexpr int SC = SX + RW * kCW;            // [16][NPAD] c rows
-    static constexpr int SY = SC + kRows * NPAD;        // [16][16]   gated dy rows
-    static constexpr int SCB = SY + kRows * kCW;        // [16][NPAD] gradient of c (share)
-    static constexpr int SCS = SCB + kRows * NPAD;      // [16][NPAD/2][2] (cos, sin) of the angle steps
-    static constexpr int SXG = SCS + kRows * NPAD;      // [4][16][16] per-wave partials (ungated y / gamma part of dx)
-    static constexpr int SXB = SXG + 4 * kRows * kCW;   // [4][16][16] beta part of dx of the previous token
-    static constexpr int SSC = SXB + 4 * kRows * kCW;   // [16][8] alpha, beta, gamma, dt, lambda, A, -, -
-    static constexpr int SSP = SSC + kRows * 8;         // [16][4][4] per-wave partial scalars
-    static constexpr int SPN = SSP + kRows * 16;        // [8][16] dx pending for the previous block's last token
-    static constexpr int SRD = SPN + 8 * kCW;           // [8] reductions
-    static constexpr int TOTAL = SRD + 8;
+// LDS layout of the chunk kernels (floats)
+template <int NPAD, int PPAD>
+struct CL {
+    static constexpr int BP = NPAD + 1, XP = PPAD + 1, N2P = NPAD / 2;
+    static constexpr int SLAB = 32 * XP > kRows * N2P ? 32 * XP : kRows * N2P;
+    static constexpr int SB = 0;                    // [64][BP] B~ rows (then dB~)
+    static constexpr int SC = SB + kRows * BP;      // [64][BP] C~ rows (then dC~)
+    static constexpr int SX = SC + kRows * BP;      // [64][XP] x rows
+    static constexpr int SY = SX + kRows * XP;      // [64][XP] gated dy rows
+    static constexpr int SS = SY + kRows * XP;      // state slab [32][XP] / angles [64][N2P]
+    static constexpr int TK = SS + SLAB;            // per token: cs, kappa, gamma
+    static constexpr int RT = TK + 3 * 64;          // per row: cs, kappa, gamma, token, e^(cs_end-cs), e^cs
+    static constexpr int RW = RT + 6 * 64;          // [4][64] strict row sums (with RD: [8][64] scan scratch)
+    static constexpr int RD = RW + 4 * 64;          // [4][64] same-token row sums
+    static constexpr int CE = RD + 4 * 64;          // [64] strict column sums
+    static constexpr int AT = CE + 64;              // [2][64] C~ . (state term of dC~) per row
+    static constexpr int KS = AT + 128;             // [2][64] B~ . (state term of dB~ / kappa) per row
+    static constexpr int MS = KS + 128;             // misc
+    static constexpr int TOTAL = MS + 32;
 };
 
-// Stage tokens t0 .. t0+Tv-1 of one sequence (b and x rows of the previous token too).
-// Every global load of the block is issued before the first use, so the block pays
-// the memory latency once.
-template <class Io, int NPAD>
-__device__ void stage(const BwdParams &p, float *sm, int64_t b, int h, int cg, int64_t t0, int Tv, bool want_c,
-                      bool want_cb) {
-    using ET = typename Io::T;
-    using L = SweepLds<NPAD>;
-    constexpr int MB = (kRows + 8) / 4, MC = kRows / 4, MT = kRows * (NPAD / 2) / 256 > 0 ? kRows * (NPAD / 2) / 256 : 1;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int N = p.N, P = p.P, R = p.R, N2 = N / 2, NR = p.nr;
+// Running angle sums of a chunk: phi[k][i] = theta summed over tokens 0..k of the chunk
+// (pairs i >= nr: 0).  scratch: [8][64].
+template <int N2P>
+__device__ void chunk_angles(const BwdParams &p, float *phi, float *scratch, int64_t b, int h, int64_t t0, int Tv) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int NR = p.nr;
     const int64_t T = p.T, H = p.H;
-    const int64_t bh = b * H + h;
-    const int p0 = cg * kCW;
+    for (int e = tid; e < kRows * N2P; e += kThreads) {
+        const int k = e / N2P, i = e - k * N2P;
+        phi[e] = (k < Tv && i < NR) ? p.theta[((b * T + t0 + k) * H + h) * (int64_t)NR + i] : 0.f;
+    }
+    __syncthreads();
+    float run = 0.f;
+    if (lane < N2P) {
+        for (int k = 8 * wv; k < 8 * wv + 8; ++k) run += phi[k * N2P + lane];
+        scratch[wv * 64 + lane] = run;
+    }
+    __syncthreads();
+    if (lane < N2P) {
+        float off = 0.f;
+        for (int ww = 0; ww < wv; ++ww) off += scratch[ww * 64 + lane];
+        for (int k = 8 * wv; k < 8 * wv + 8; ++k) {
+            off += phi[k * N2P + lane];
+            phi[k * N2P + lane] = off;
+        }
+    }
+    __syncthreads();
+}
+
+// Stage one chunk: per-token scalars, normalised + biased + rotated B and C rows (scaled by
+// e^(cs_end - cs) kappa and e^cs when SCALED), x and gated dy rows, zero padding.
+// Returns (per thread) its part of sum(dy_gated * x).
+template <class Io, int NPAD, int PPAD, bool SCALED>
+__device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h, int64_t t0, int Tv) {
+    using ET = typename Io::T;
+    using L = CL<NPAD, PPAD>;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int N = p.N, P = p.P, R = p.R, N2 = N / 2;
+    const int Qt = kRows / R;
+    const int64_t T = p.T, H = p.H;
+    float *tk = sm + L::TK, *rt = sm + L::RT;
+    // per-token scalars (wave 0; lane = token of the chunk)
+    if (tid < 64) {
+        const int k = tid;
+        float la = 0.f, kap = 0.f, gam = 0.f;
+        if (k < Tv) {
+            const int64_t t = t0 + k, bth = (b * T + t) * H + h;
+            float dt, lam, u, v;
+            act_scalars(p, bth, h, dt, lam, u, v);
+            const float Av = (p.flags & kFlagAPerToken) ? p.A[bth] : p.A[h];
+            la = dt * Av;
+            gam = lam * dt;
+            kap = gam + eta_at(p, b, h, t);
+        }
+        const float cs = wave_scan_incl(la);
+        tk[k] = cs;
+        tk[64 + k] = kap;
+        tk[128 + k] = gam;
+    }
+    chunk_angles<L::N2P>(p, sm + L::SS, sm + L::RW, b, h, t0, Tv);  // (its barriers publish tk)
+    const float cs_end = tk[Tv - 1];
+    // per-row tables
+    if (tid < kRows) {
+        const int rho = tid, k = rho / R;
+        const bool valid = k < Qt && k < Tv;
+        const float cs = valid ? tk[k] : cs_end;
+        rt[rho] = cs;
+        rt[64 + rho] = valid ? tk[64 + k] : 0.f;
+        rt[128 + rho] = valid ? tk[128 + k] : 0.f;
+        rt[192 + rho] = __int_as_float(valid ? k : 1 << 20);
+        rt[256 + rho] = __expf(cs_end - cs);
+        rt[320 + rho] = __expf(cs);
+    }
+    // x and gated dy rows (elements in memory order (token, p, rank))
+    float dDp = 0.f;
+    for (int e = tid; e < Qt * PPAD * R; e += kThreads) {
+        const int k = e / (PPAD * R), rem = e - k * PPAD * R, pc = rem / R, r = rem - pc * R;
+        float xv = 0.f, yv = 0.f;
+        if (k < Tv && pc < P) {
+            const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)P * R + (int64_t)pc * R + r;
+            xv = Io::ld((const ET *)p.x + o);
+            yv = Io::ld((const ET *)p.dy + o);
+            if (p.z) yv *= silu_f(Io::ld((const ET *)p.z + o));
+        }
+        sm[L::SX + (k * R + r) * L::XP + pc] = xv;
+        sm[L::SY + (k * R + r) * L::XP + pc] = yv;
+        dDp += xv * yv;
+    }
+    for (int e = tid; e < (kRows - Qt * R) * L::XP; e += kThreads) {
+        sm[L::SX + Qt * R * L::XP + e] = 0.f;
+        sm[L::SY + Qt * R * L::XP + e] = 0.f;
+    }
+    __syncthreads();  // row tables
+    // B and C rows: wave wv takes rows wv + 8 m; lane = pair
     const bool norm = (p.flags & kFlagNorm) != 0;
-    const int nbr = (Tv + 1) * R, ncr = Tv * R;
-    // ---- loads
-    float bv[MB][2], xv[MB], cvv[MC][2], yv[MC], zv[MC], cb[MC][2];
+    float rb[8][2], rc[8][2];
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        const int row = w + 4 * m;
-        bv[m][0] = bv[m][1] = xv[m] = 0.f;
-        const int64_t t = t0 - 1 + row / R;
-        if (row < nbr && t >= 0) {
-            const int r = row % R;
-            const int64_t bth = (b * T + t) * H + h;
-            const ET *raw = (const ET *)p.Bm + bth * N * R + r;
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int n = lane + 64 * k;
-                if (n < N) bv[m][k] = Io::ld(raw + (int64_t)n * R);
-            }
-            if (lane < kCW && p0 + lane < P) xv[m] = Io::ld((const ET *)p.x + bth * P * R + (int64_t)(p0 + lane) * R + r);
+    for (int m = 0; m < 8; ++m) {
+        const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
+        rb[m][0] = rb[m][1] = rc[m][0] = rc[m][1] = 0.f;
+        if (k < Qt && k < Tv && lane < N2) {
+            const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)N * R + (int64_t)(2 * lane) * R + r;
+            rb[m][0] = Io::ld((const ET *)p.Bm + o);
+            rb[m][1] = Io::ld((const ET *)p.Bm + o + R);
+            rc[m][0] = Io::ld((const ET *)p.Cm + o);
+            rc[m][1] = Io::ld((const ET *)p.Cm + o + R);
         }
     }
+    const float *phi = sm + L::SS;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-        const int q = w + 4 * m;
-        cvv[m][0] = cvv[m][1] = yv[m] = cb[m][0] = cb[m][1] = 0.f;
-        zv[m] = 1.f;
-        if (want_c && q < ncr) {
-            const int64_t t = t0 + q / R;
-            const int r = q % R;
-            const int64_t bth = (b * T + t) * H + h;
-            const ET *raw = (const ET *)p.Cm + bth * N * R + r;
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int n = lane + 64 * k;
-                if (n < N) cvv[m][k] = Io::ld(raw + (int64_t)n * R);
-                if (want_cb && n < N) cb[m][k] = p.cbar[((cg * (p.B * H) + bh) * T + t) * (int64_t)N * R + n * R + r];
-            }
-            if (lane < kCW && p0 + lane < P) {
-                const int64_t o = bth * P * R + (int64_t)(p0 + lane) * R + r;
-                yv[m] = Io::ld((const ET *)p.dy + o);
-                if (p.z) zv[m] = Io::ld((const ET *)p.z + o);
-            }
+    for (int m = 0; m < 8; ++m) {
+        const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
+        const bool valid = k < Qt && k < Tv;
+        float sb = 1.f, sc = 1.f;
+        if (norm) {
+            sb = rsqrtf(wave_sum(rb[m][0] * rb[m][0] + rb[m][1] * rb[m][1]) / (float)N + p.eps);
+            sc = rsqrtf(wave_sum(rc[m][0] * rc[m][0] + rc[m][1] * rc[m][1]) / (float)N + p.eps);
         }
-    }
-    float sdt = 0.f, slam = 0.f, sA = 0.f;
-    if (tid < Tv) {
-        const int64_t bth = (b * T + t0 + tid) * H + h;
-        sdt = p.dt[bth];
-        slam = p.lam[bth];
-        sA = (p.flags & kFlagAPerToken) ? p.A[bth] : p.A[h];
-    }
-    float th[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int e = tid + 256 * m;
-        const int k = e / N2, i = e - k * N2;
-        th[m] = 0.f;
-        if (k < Tv && i < NR) th[m] = p.theta[((b * T + t0 + k) * H + h) * (int64_t)NR + i];
-    }
-    // ---- normalised rows and the rest
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        const int row = w + 4 * m;
-        if (row >= nbr) continue;  // uniform per wave
-        const int64_t t = t0 - 1 + row / R;
-        const int r = row % R;
-        float *db = sm + L::SB + row * NPAD;
-        if (t >= 0) {
-            const float ss = wave_sum(bv[m][0] * bv[m][0] + bv[m][1] * bv[m][1]);
-            const float rs = norm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
-            const float *bias = p.bbias ? p.bbias + ((int64_t)h * R + r) * N : nullptr;
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int n = lane + 64 * k;
-                if (n < N) {
-                    float u = norm ? bv[m][k] * rs * (p.bnw ? p.bnw[n] : 1.f) : bv[m][k];
-                    if (bias) u += bias[n];
-                    db[n] = u;
+        if (lane < L::N2P) {
+            float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
+            if (valid && lane < N2) {
+                const int n0 = 2 * lane;
+                b0 = norm ? rb[m][0] * sb * (p.bnw ? p.bnw[n0] : 1.f) : rb[m][0];
+                b1 = norm ? rb[m][1] * sb * (p.bnw ? p.bnw[n0 + 1] : 1.f) : rb[m][1];
+                c0 = norm ? rc[m][0] * sc * (p.cnw ? p.cnw[n0] : 1.f) : rc[m][0];
+                c1 = norm ? rc[m][1] * sc * (p.cnw ? p.cnw[n0 + 1] : 1.f) : rc[m][1];
+                if (p.bbias) {
+                    b0 += p.bbias[((int64_t)h * R + r) * N + n0];
+                    b1 += p.bbias[((int64_t)h * R + r) * N + n0 + 1];
                 }
+                if (p.cbias) {
+                    c0 += p.cbias[((int64_t)h * R + r) * N + n0];
+                    c1 += p.cbias[((int64_t)h * R + r) * N + n0 + 1];
+                }
+                float s, c;
+                fast_sincos(phi[k * L::N2P + lane], s, c);
+                float fb = 1.f, fc = 1.f;
+                if (SCALED) {
+                    fb = rt[256 + rho] * rt[64 + rho];
+                    fc = rt[320 + rho];
+                }
+                const float u0 = c * b0 - s * b1, u1 = s * b0 + c * b1;
+                const float v0 = c * c0 - s * c1, v1 = s * c0 + c * c1;
+                b0 = fb * u0;
+                b1 = fb * u1;
+                c0 = fc * v0;
+                c1 = fc * v1;
             }
-            if (lane < kCW) sm[L::SX + row * kCW + lane] = xv[m];
-        } else {
-            for (int i = lane; i < N2; i += 64) init_b(p, bh, i, r, db[2 * i], db[2 * i + 1]);
-            if (lane < kCW) sm[L::SX + row * kCW + lane] = (p.px0 && p0 + lane < P) ? p.px0[(bh * P + p0 + lane) * R + r] : 0.f;
+            sm[L::SB + rho * L::BP + 2 * lane] = b0;
+            sm[L::SB + rho * L::BP + 2 * lane + 1] = b1;
+            sm[L::SC + rho * L::BP + 2 * lane] = c0;
+            sm[L::SC + rho * L::BP + 2 * lane + 1] = c1;
         }
     }
+    __syncthreads();
+    return dDp;
+}
+
+__device__ __forceinline__ float block_sum(float v, float *scratch) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) scratch[wv] = v;
+    __syncthreads();
+    float s = 0.f;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-        const int q = w + 4 * m;
-        if (!want_c || q >= ncr) continue;  // uniform per wave
-        const int r = q % R;
-        const float ss = wave_sum(cvv[m][0] * cvv[m][0] + cvv[m][1] * cvv[m][1]);
-        const float rs = norm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
-        const float *bias = p.cbias ? p.cbias + ((int64_t)h * R + r) * N : nullptr;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int n = lane + 64 * k;
-            if (n < N) {
-                float u = norm ? cvv[m][k] * rs * (p.cnw ? p.cnw[n] : 1.f) : cvv[m][k];
-                if (bias) u += bias[n];
-                sm[L::SC + q * NPAD + n] = u;
-                if (want_cb) sm[L::SCB + q * NPAD + n] = cb[m][k];
-            }
-        }
-        if (lane < kCW) sm[L::SY + q * kCW + lane] = p.z ? yv[m] * silu_f(zv[m]) : yv[m];
-    }
-    if (tid < Tv) {
-        float dt = sdt, lam = slam;
-        if (p.flags & kFlagDtSoftplus) dt = softplus_f(dt + (p.dtbias ? p.dtbias[h] : 0.f));
-        if (p.flags & kFlagLamSigmoid) lam = sigmoid_f(lam);
-        const float al = __expf(dt * sA);
-        float *s = sm + L::SSC + tid * 8;
-        s[0] = al;
-        s[1] = al * dt * (1.f - lam);
-        s[2] = lam * dt;
-        s[3] = dt;
-        s[4] = lam;
-        s[5] = sA;
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int e = tid + 256 * m;
-        const int k = e / N2, i = e - k * N2;
-        if (k >= Tv) continue;
-        sm[L::SCS + (k * (NPAD / 2) + i) * 2 + 0] = i < NR ? __cosf(th[m]) : 1.f;
-        sm[L::SCS + (k * (NPAD / 2) + i) * 2 + 1] = i < NR ? __sinf(th[m]) : 0.f;
-    }
+    for (int w = 0; w < kWaves; ++w) s += scratch[w];
+    return s;
 }
 
 }  // namespace
 
-// mode 0: forward aggregate; 1: adjoint aggregate; 2: both sweeps with the shares
-template <class Io, int NPAD, int RMAX>
-__global__ __launch_bounds__(256) void bwd_sweep_kernel(BwdParams p, int mode) {
-    using ET = typename Io::T;
-    using L = SweepLds<NPAD>;
-    constexpr int N2P = NPAD / 2;
-    constexpr int NPL = N2P >= 16 ? N2P / 16 : 1;
-    __shared__ __attribute__((aligned(16))) float sm[L::TOTAL];
-    const int N = p.N, P = p.P, R = RMAX == 1 ? 1 : p.R, N2 = N / 2, NR = p.nr;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int rho = lane >> 4, cc = lane & 15, grp = w * 4 + rho;
-    const int64_t bid = blockIdx.x;
-    const int seg = (int)(bid % p.nseg);
-    const int64_t q1 = bid / p.nseg;
-    const int cg = (int)(q1 % p.ncg);
-    const int64_t bh = q1 / p.ncg;
+// ---------------------------------------------------------------- per-chunk state sums
+template <class Io, int NPAD, int PPAD>
+__global__ __launch_bounds__(kThreads) void bwd_chunk_state_kernel(BwdParams p) {
+    using L = CL<NPAD, PPAD>;
+    constexpr int NT = NPAD / 16, PT = PPAD / 16;
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, l16 = lane & 15;
+    const int nck = p.nck, N = p.N, P = p.P, N2 = N / 2;
+    const int64_t bh = blockIdx.x / nck;
+    const int c = (int)(blockIdx.x - bh * nck);
     const int64_t b = bh / p.H;
     const int h = (int)(bh - b * p.H);
-    const int64_t T = p.T, H = p.H, BH = p.B * p.H;
-    const int TBt = kRows / R;
-    const int64_t ts = (int64_t)seg * p.segT, te = min(T, ts + (int64_t)p.segT);
-    const int nblk = (int)((te - ts + TBt - 1) / TBt);
-    const int pc = cg * kCW + cc;  // this lane's column
-    const bool cv = pc < P;
-    const int64_t sidx = (bh * p.ncg + cg) * p.nseg + seg;  // (sequence, group, segment)
-    const int i0 = grp * NPL;
-    auto piv = [&](int j) { return i0 + j < N2; };
-    auto CS = [&](int k, int i, int c) { return sm[L::SCS + (k * N2P + i) * 2 + c]; };
-    auto SB = [&](int row, int n) { return sm[L::SB + row * NPAD + n]; };
-    auto SX = [&](int row) { return sm[L::SX + row * kCW + cc]; };
+    const int Qt = kRows / p.R;
+    const int64_t t0 = (int64_t)c * Qt;
+    const int Tv = (int)min((int64_t)Qt, p.T - t0);
+    chunk_prologue<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
+    const int64_t cidx = bh * nck + c;
+    for (int q = wv; q < 2 * NT * PT; q += kWaves) {
+        const int which = q / (NT * PT), rem = q - which * NT * PT, a = rem / PT, bq = rem - a * PT;
+        const float *Ao = sm + (which ? L::SC : L::SB), *Bo = sm + (which ? L::SY : L::SX);
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int kc = 0; kc < kRows / 32; ++kc) {
+            float av[8], bv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int s = 32 * kc + 8 * g + j;
+                av[j] = Ao[s * L::BP + 16 * a + l16];
+                bv[j] = Bo[s * L::XP + 16 * bq + l16];
+            }
+            acc = mma8(av, bv, acc);
+        }
+        float *dst = (which ? p.Ust : p.Sst) + cidx * N * (int64_t)P;
+        const int pc = 16 * bq + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = 16 * a + 4 * g + i;
+            if (n < N && pc < P) dst[(int64_t)n * P + pc] = acc[i];
+        }
+    }
+    if (tid < N2) p.phic[cidx * N2 + tid] = sm[L::SS + (Tv - 1) * L::N2P + tid];
+    if (tid == 0) p.lsum[cidx] = sm[L::TK + Tv - 1];
+}
 
-    float G[NPL][2];
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) G[j][0] = G[j][1] = 0.f;
-    // ---------------------------------------------------------------- forward sweep (modes 0, 2)
-    if (mode != 1) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) {
-            const int i = i0 + j;
-            G[j][0] = G[j][1] = 0.f;
-            if (mode == 2 && piv(j)) {
-                G[j][0] = p.Gagg[(sidx * N + 2 * i) * kCW + cc];
-                G[j][1] = p.Gagg[(sidx * N + 2 * i + 1) * kCW + cc];
-            }
+// ---------------------------------------------------------------- state passes over the chunks
+// blockIdx.y 0: states before each chunk (in place of S); 1: adjoints after each chunk (in
+// place of U) and the initial state's adjoint.  Thread: (sequence, pair, column).
+__global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
+    const int N = p.N, P = p.P, N2 = N / 2, NR = p.nr, R = p.R, nck = p.nck;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= p.B * p.H * N2 * (int64_t)P) return;
+    const int pc = (int)(e % P);
+    const int i = (int)((e / P) % N2);
+    const int64_t bh = e / ((int64_t)P * N2);
+    const int64_t b = bh / p.H;
+    const int h = (int)(bh - b * p.H);
+    const bool rot = i < NR;
+    const int64_t NP = (int64_t)N * P;
+    if (blockIdx.y == 0) {
+        float g0 = 0.f, g1 = 0.f;
+        if (p.h0) {
+            g0 = p.h0[(bh * N + 2 * i) * P + pc];
+            g1 = p.h0[(bh * N + 2 * i + 1) * P + pc];
         }
-        for (int blk = 0; blk < nblk; ++blk) {
-            const int64_t t0 = ts + (int64_t)blk * TBt;
-            const int Tv = (int)min((int64_t)TBt, te - t0);
-            __syncthreads();
-            stage<Io, NPAD>(p, sm, b, h, cg, t0, Tv, mode == 2, false);
-            __syncthreads();
-            if (mode == 0) {
-                // segment totals of log alpha and of the angle steps (one group writes them)
-                if (cg == 0 && tid == 0)
-                    for (int k = 0; k < Tv; ++k) lsum += sm[L::SSC + k * 8 + 3] * sm[L::SSC + k * 8 + 5];
+        if (p.pB0 && p.px0) {
+            const float eta = eta_at(p, b, h, -1);
+            float a0 = 0.f, a1 = 0.f;
+            for (int r = 0; r < R; ++r) {
+                const float xv = p.px0[(bh * P + pc) * R + r];
+                a0 += p.pB0[(bh * N + 2 * i) * R + r] * xv;
+                a1 += p.pB0[(bh * N + 2 * i + 1) * R + r] * xv;
             }
-            for (int k = 0; k < Tv; ++k) {
-                const float al = sm[L::SSC + k * 8 + 0], be = sm[L::SSC + k * 8 + 1], ga = sm[L::SSC + k * 8 + 2];
-#pragma unroll
-                for (int j = 0; j < NPL; ++j) {
-                    const int i = i0 + j;
-                    if (!piv(j)) continue;
-                    const float c = CS(k, i, 0), s = CS(k, i, 1);
-                    float m0 = al * G[j][0], m1 = al * G[j][1], a0 = 0.f, a1 = 0.f;
-#pragma unroll
-                    for (int r = 0; r < RMAX; ++r) {
-                        if (r >= R) break;
-                        const float xp = SX(k * R + r), xc = SX(R + k * R + r);
-                        m0 += be * SB(k * R + r, 2 * i) * xp;
-                        m1 += be * SB(k * R + r, 2 * i + 1) * xp;
-                        a0 += SB(R + k * R + r, 2 * i) * xc;
-                        a1 += SB(R + k * R + r, 2 * i + 1) * xc;
-                    }
-                    G[j][0] = c * m0 + s * m1 + ga * a0;
-                    G[j][1] = -s * m0 + c * m1 + ga * a1;
-                }
-                if (mode == 2) {
-#pragma unroll
-                    for (int r = 0; r < RMAX; ++r) {
-                        if (r >= R) break;
-                        const int q_ = k * R + r;
-                        const float yv = sm[L::SY + q_ * kCW + cc];
-                        float yt = 0.f;
-#pragma unroll
-                        for (int j = 0; j < NPL; ++j) {
-                            const int i = i0 + j;
-                            const float c0 = row_sum16(G[j][0] * yv), c1 = row_sum16(G[j][1] * yv);
-                            if (cc == 0 && piv(j)) {
-                                sm[L::SCB + q_ * NPAD + 2 * i] = c0;
-                                sm[L::SCB + q_ * NPAD + 2 * i + 1] = c1;
-                            }
-                            if (piv(j)) yt += sm[L::SC + q_ * NPAD + 2 * i] * G[j][0] + sm[L::SC + q_ * NPAD + 2 * i + 1] * G[j][1];
-                        }
-                        if (p.z) {
-                            yt = rows_sum4(yt);
-                            if (rho == 0) sm[L::SXG + (w * kRows + q_) * kCW + cc] = yt;
-                        }
-                    }
-                }
-            }
-            if (mode == 2) {
-                __syncthreads();
-                // the gradient of c (this group's share) for the reverse sweep and the final kernel
-                for (int e = tid; e < Tv * R * N; e += 256) {
-                    const int q_ = e / N, n = e - q_ * N;
-                    const int64_t t = t0 + q_ / R;
-                    p.cbar[((cg * BH + bh) * T + t) * (int64_t)N * R + n * R + q_ % R] = sm[L::SCB + q_ * NPAD + n];
-                }
-                if (p.z && p.dz) {
-                    for (int e = tid; e < Tv * R * kCW; e += 256) {
-                        const int q_ = e / kCW, c2 = e - q_ * kCW;
-                        if (cg * kCW + c2 >= P) continue;
-                        const int64_t t = t0 + q_ / R;
-                        const int64_t o = ((b * T + t) * H + h) * P * R + (int64_t)(cg * kCW + c2) * R + q_ % R;
-                        float yf = p.D[h] * sm[L::SX + (R + q_) * kCW + c2];
-#pragma unroll
-                        for (int ww = 0; ww < 4; ++ww) yf += sm[L::SXG + (ww * kRows + q_) * kCW + c2];
-                        const float zv = Io::ld((const ET *)p.z + o), sgz = sigmoid_f(zv);
-                        Io::st((ET *)p.dz + o, Io::ld((const ET *)p.dy + o) * yf * sgz * (1.f + zv * (1.f - sgz)));
-                    }
-                }
-            }
-            if (mode == 0 && cg == 0) {
-                // angle totals of the segment, per pair
-                for (int i = tid; i < N2; i += 256) {
-                    float a = blk == 0 ? 0.f : p.pseg[(bh * p.nseg + seg) * N2 + i];
-                    if (i < NR)
-                        for (int k = 0; k < Tv; ++k) a += p.theta[((b * T + t0 + k) * H + h) * (int64_t)NR + i];
-                    p.pseg[(bh * p.nseg + seg) * N2 + i] = a;
-                }
-            }
+            g0 += eta * a0;
+            g1 += eta * a1;
         }
-        if (mode == 0) {
-#pragma unroll
-            for (int j = 0; j < NPL; ++j) {
-                const int i = i0 + j;
-                if (!piv(j)) continue;
-                p.Gagg[(sidx * N + 2 * i) * kCW + cc] = G[j][0];
-                p.Gagg[(sidx * N + 2 * i + 1) * kCW + cc] = G[j][1];
-            }
-            if (cg == 0 && tid == 0) p.lseg[bh * p.nseg + seg] = lsum;
-            return;
+        if (rot && p.ang0) {
+            float s, c;
+            fast_sincos((float)wrap_2pi((double)p.ang0[bh * NR + i]), s, c);
+            const float u = c * g0 + s * g1, v = -s * g0 + c * g1;
+            g0 = u;
+            g1 = v;
         }
-    }
-
-    // ---------------------------------------------------------------- reverse sweep (modes 1, 2)
-    float Gb[NPL][2], K[NPL][2][2], bpend[RMAX][NPL][2];
+        float *S = p.Sst + bh * nck * NP + (int64_t)(2 * i) * P + pc;
+        for (int c0 = 0; c0 < nck; c0 += 4) {
+            float s0[4], s1[4], dec[4], ph[4];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-        const int i = i0 + j;
-        Gb[j][0] = Gb[j][1] = 0.f;
-        if (mode == 2 && piv(j)) {
-            Gb[j][0] = p.Ragg[(sidx * N + 2 * i) * kCW + cc];
-            Gb[j][1] = p.Ragg[(sidx * N + 2 * i + 1) * kCW + cc];
-        }
-#pragma unroll
-        for (int r = 0; r < RMAX; ++r) bpend[r][j][0] = bpend[r][j][1] = 0.f;
-        // K at the segment end: sum over the columns of G_end g_end^T
-        K[j][0][0] = row_sum16(Gb[j][0] * G[j][0]);
-        K[j][0][1] = row_sum16(Gb[j][0] * G[j][1]);
-        K[j][1][0] = row_sum16(Gb[j][1] * G[j][0]);
-        K[j][1][1] = row_sum16(Gb[j][1] * G[j][1]);
-        if (mode == 2 && seg == p.nseg - 1) {
-            // share of the final-angle gradient: <dh_final, J h_final>, h_final = Rot(Theta_final) g
-            float s0 = 0.f, c0 = 1.f;
-            if (piv(j) && i < NR) fast_sincos((float)wrap_2pi((double)p.thfin[bh * N2 + i]), s0, c0);
-            float a = 0.f, bq = 0.f;
-            if (piv(j) && cv && p.dh1) {
-                a = p.dh1[(bh * N + 2 * i) * P + pc];
-                bq = p.dh1[(bh * N + 2 * i + 1) * P + pc];
-            }
-            const float hf0 = c0 * G[j][0] - s0 * G[j][1], hf1 = s0 * G[j][0] + c0 * G[j][1];
-            const float tj = row_sum16(-a * hf1 + bq * hf0);
-            if (cc == 0 && piv(j)) p.thfp[(bh * p.ncg + cg) * N2 + i] = i < NR ? tj : 0.f;
-        }
-    }
-    if (mode == 2) {
-        __syncthreads();
-        for (int e = tid; e < R * kCW; e += 256) sm[L::SPN + e] = 0.f;
-    }
-    float dDacc = 0.f;
-    for (int blk = nblk - 1; blk >= 0; --blk) {
-        const int64_t t0 = ts + (int64_t)blk * TBt;
-        const int Tv = (int)min((int64_t)TBt, te - t0);
-        __syncthreads();
-        stage<Io, NPAD>(p, sm, b, h, cg, t0, Tv, true, mode == 2);
-        __syncthreads();
-        for (int k = Tv - 1; k >= 0; --k) {
-            const float al = sm[L::SSC + k * 8 + 0], be = sm[L::SSC + k * 8 + 1], ga = sm[L::SSC + k * 8 + 2];
-            if (mode == 1) {
-#pragma unroll
-                for (int j = 0; j < NPL; ++j) {
-                    const int i = i0 + j;
-                    if (!piv(j)) continue;
-                    const float c = CS(k, i, 0), s = CS(k, i, 1);
-                    float g0 = Gb[j][0], g1 = Gb[j][1];
-#pragma unroll
-                    for (int r = 0; r < RMAX; ++r) {
-                        if (r >= R) break;
-                        const int q_ = k * R + r;
-                        const float yv = sm[L::SY + q_ * kCW + cc];
-                        g0 += sm[L::SC + q_ * NPAD + 2 * i] * yv;
-                        g1 += sm[L::SC + q_ * NPAD + 2 * i + 1] * yv;
-                    }
-                    Gb[j][0] = al * (c * g0 - s * g1);
-                    Gb[j][1] = al * (s * g0 + c * g1);
-                }
-                continue;
-            }
-            float sq = 0.f, sbe = 0.f, sga = 0.f;
-#pragma unroll
-            for (int j = 0; j < NPL; ++j) {
-                const int i = i0 + j;
-                const bool iv = piv(j);
-                const float c = iv ? CS(k, i, 0) : 1.f, s = iv ? CS(k, i, 1) : 0.f;
-                float K00 = K[j][0][0], K01 = K[j][0][1], K10 = K[j][1][0], K11 = K[j][1][1];
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r) {
-                    if (r >= R) break;
-                    const int q_ = k * R + r;
-                    const float c0 = iv ? sm[L::SC + q_ * NPAD + 2 * i] : 0.f, c1 = iv ? sm[L::SC + q_ * NPAD + 2 * i + 1] : 0.f;
-                    const float d0 = iv ? sm[L::SCB + q_ * NPAD + 2 * i] : 0.f, d1 = iv ? sm[L::SCB + q_ * NPAD + 2 * i + 1] : 0.f;
-                    K00 += c0 * d0;
-                    K01 += c0 * d1;
-                    K10 += c1 * d0;
-                    K11 += c1 * d1;
-                    const float yv = sm[L::SY + q_ * kCW + cc];
-                    Gb[j][0] += c0 * yv;
-                    Gb[j][1] += c1 * yv;
-                }
-                float F00 = K00, F01 = K01, F10 = K10, F11 = K11;
-                float V00 = 0.f, V01 = 0.f, V10 = 0.f, V11 = 0.f;
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r) {
-                    if (r >= R) break;
-                    const float xc = SX(R + k * R + r), xp = SX(k * R + r);
-                    const float u0 = row_sum16(Gb[j][0] * xc), u1 = row_sum16(Gb[j][1] * xc);
-                    const float v0 = row_sum16(Gb[j][0] * xp), v1 = row_sum16(Gb[j][1] * xp);
-                    const float b0 = iv ? SB(R + k * R + r, 2 * i) : 0.f, b1 = iv ? SB(R + k * R + r, 2 * i + 1) : 0.f;
-                    const float p0 = iv ? SB(k * R + r, 2 * i) : 0.f, p1 = iv ? SB(k * R + r, 2 * i + 1) : 0.f;
-                    F00 -= ga * u0 * b0;
-                    F01 -= ga * u0 * b1;
-                    F10 -= ga * u1 * b0;
-                    F11 -= ga * u1 * b1;
-                    V00 += v0 * p0;
-                    V01 += v0 * p1;
-                    V10 += v1 * p0;
-                    V11 += v1 * p1;
-                    const float qv0 = c * v0 - s * v1, qv1 = s * v0 + c * v1;  // Q^T v
-                    sga += b0 * u0 + b1 * u1;
-                    sbe += p0 * qv0 + p1 * qv1;
-                    float nb0 = 0.f, nb1 = 0.f;
-#pragma unroll
-                    for (int rr = 0; rr < RMAX; ++rr)
-                        if (rr == r) { nb0 = bpend[rr][j][0]; nb1 = bpend[rr][j][1]; }
-                    if (cc == 0 && iv) {
-                        const int64_t t = t0 + k;
-                        float *dst = p.bbar + ((cg * BH + bh) * T + t) * (int64_t)N * R;
-                        dst[(2 * i) * R + r] = nb0 + ga * u0;
-                        dst[(2 * i + 1) * R + r] = nb1 + ga * u1;
-                    }
-#pragma unroll
-                    for (int rr = 0; rr < RMAX; ++rr)
-                        if (rr == r) { bpend[rr][j][0] = be * qv0; bpend[rr][j][1] = be * qv1; }
-                }
-                if (cc == 0 && iv && i < NR) p.tbar[((cg * BH + bh) * T + t0 + k) * (int64_t)N2 + i] = F01 - F10;
-                const float E00 = F00 * c - F01 * s - be * V00, E01 = F00 * s + F01 * c - be * V01;
-                const float E10 = F10 * c - F11 * s - be * V10, E11 = F10 * s + F11 * c - be * V11;
-                sq += c * E00 + s * E01 - s * E10 + c * E11;
-                K[j][0][0] = c * E00 - s * E10;
-                K[j][0][1] = c * E01 - s * E11;
-                K[j][1][0] = s * E00 + c * E10;
-                K[j][1][1] = s * E01 + c * E11;
-            }
-            // dx partials: gamma part for token t, beta part for token t-1 (this lane's pairs)
-#pragma unroll
-            for (int r = 0; r < RMAX; ++r) {
-                if (r >= R) break;
-                const int q_ = k * R + r;
-                float xg = 0.f, xb = 0.f;
-#pragma unroll
-                for (int j = 0; j < NPL; ++j) {
-                    const int i = i0 + j;
-                    if (!piv(j)) continue;
-                    const float c = CS(k, i, 0), s = CS(k, i, 1);
-                    const float b0 = SB(R + q_, 2 * i), b1 = SB(R + q_, 2 * i + 1);
-                    const float p0 = SB(q_, 2 * i), p1 = SB(q_, 2 * i + 1);
-                    const float qp0 = c * p0 + s * p1, qp1 = -s * p0 + c * p1;  // Q bprev
-                    xg += b0 * Gb[j][0] + b1 * Gb[j][1];
-                    xb += qp0 * Gb[j][0] + qp1 * Gb[j][1];
-                }
-                xg = rows_sum4(xg);
-                xb = rows_sum4(xb);
-                if (rho == 0) {
-                    sm[L::SXG + (w * kRows + q_) * kCW + cc] = ga * xg;
-                    sm[L::SXB + (w * kRows + q_) * kCW + cc] = be * xb;
+            for (int q = 0; q < 4; ++q) {
+                const int ck = c0 + q;
+                s0[q] = s1[q] = ph[q] = dec[q] = 0.f;
+                if (ck < nck) {
+                    s0[q] = S[ck * NP];
+                    s1[q] = S[ck * NP + P];
+                    dec[q] = p.lsum[bh * nck + ck];
+                    ph[q] = rot ? p.phic[(bh * nck + ck) * N2 + i] : 0.f;
                 }
             }
-            sq = rows_sum4(cc == 0 ? sq : 0.f);
-            sbe = rows_sum4(cc == 0 ? sbe : 0.f);
-            sga = rows_sum4(cc == 0 ? sga : 0.f);
-            if (lane == 0) {
-                sm[L::SSP + (k * 4 + w) * 4 + 0] = sq;
-                sm[L::SSP + (k * 4 + w) * 4 + 1] = sbe;
-                sm[L::SSP + (k * 4 + w) * 4 + 2] = sga;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ck = c0 + q;
+                if (ck >= nck) break;
+                S[ck * NP] = g0;
+                S[ck * NP + P] = g1;
+                const float d = __expf(dec[q]);
+                const float u = d * g0 + s0[q], v = d * g1 + s1[q];
+                if (ck == nck - 1) {  // state after the last chunk, in its frame
+                    p.hfin[(bh * N + 2 * i) * P + pc] = u;
+                    p.hfin[(bh * N + 2 * i + 1) * P + pc] = v;
+                    break;
+                }
+                float s, c;
+                fast_sincos(ph[q], s, c);
+                g0 = c * u + s * v;
+                g1 = -s * u + c * v;
             }
-            // carry: G <- alpha Q^T G
-#pragma unroll
-            for (int j = 0; j < NPL; ++j) {
-                const int i = i0 + j;
-                if (!piv(j)) continue;
-                const float c = CS(k, i, 0), s = CS(k, i, 1);
-                const float g0 = Gb[j][0], g1 = Gb[j][1];
-                Gb[j][0] = al * (c * g0 - s * g1);
-                Gb[j][1] = al * (s * g0 + c * g1);
-            }
-        }
-        if (mode == 1) continue;
-        __syncthreads();
-        // token scalars (this group's shares)
-        if (tid < Tv * 3) {
-            const int k = tid / 3, which = tid - 3 * k;
-            float v = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < 4; ++ww) v += sm[L::SSP + (k * 4 + ww) * 4 + which];
-            p.sbar[((cg * BH + bh) * T + t0 + k) * 4 + which] = v;
-        }
-        // dx of the group's columns: D dy + gamma part + beta part of the next token; a
-        // segment's last token also gets the next segment's share, added by the final kernel
-        for (int e = tid; e < Tv * R * kCW; e += 256) {
-            const int q_ = e / kCW, c2 = e - q_ * kCW;
-            const int k = q_ / R, r = q_ - k * R;
-            const int col = cg * kCW + c2;
-            const float yv = sm[L::SY + q_ * kCW + c2];
-            float v = p.D[h] * yv;
-            dDacc += yv * sm[L::SX + (R + q_) * kCW + c2];
-#pragma unroll
-            for (int ww = 0; ww < 4; ++ww) v += sm[L::SXG + (ww * kRows + q_) * kCW + c2];
-            const bool last_blk = blk == nblk - 1;
-            if (k + 1 < Tv) {
-#pragma unroll
-                for (int ww = 0; ww < 4; ++ww) v += sm[L::SXB + (ww * kRows + q_ + R) * kCW + c2];
-            } else if (!last_blk) {
-                v += sm[L::SPN + r * kCW + c2];
-            }
-            if (col >= P) continue;
-            if (k + 1 == Tv && last_blk) {
-                p.xlast[(sidx * R + r) * kCW + c2] = v;
-            } else if (p.dx) {
-                Io::st((ET *)p.dx + ((b * T + t0 + k) * H + h) * P * R + (int64_t)col * R + r, v);
-            }
-        }
-        __syncthreads();
-        // beta part produced at this block's first token: for the previous block's last token
-        for (int e = tid; e < R * kCW; e += 256) {
-            float v = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < 4; ++ww) v += sm[L::SXB + (ww * kRows + e / kCW) * kCW + e % kCW];
-            sm[L::SPN + e] = v;
-        }
-    }
-    if (mode == 1) {
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) {
-            const int i = i0 + j;
-            if (!piv(j)) continue;
-            p.Ragg[(sidx * N + 2 * i) * kCW + cc] = Gb[j][0];
-            p.Ragg[(sidx * N + 2 * i + 1) * kCW + cc] = Gb[j][1];
         }
         return;
     }
-    __syncthreads();
-    // shares of the token before the segment: db (per pair, rank), dx (per column, rank)
+    // reverse: the frame of the last chunk is the angle before it
+    double th = (rot && p.ang0) ? (double)p.ang0[bh * NR + i] : 0.0;
+    if (rot)
+        for (int ck = 0; ck + 1 < nck; ++ck) th += (double)p.phic[(bh * nck + ck) * N2 + i];
+    const float thl = rot ? (float)wrap_2pi(th) : 0.f;
+    if (pc == 0) p.thst[bh * N2 + i] = thl;
+    float gb0 = 0.f, gb1 = 0.f;
+    if (p.dh1) {
+        const float d0 = p.dh1[(bh * N + 2 * i) * P + pc], d1 = p.dh1[(bh * N + 2 * i + 1) * P + pc];
+        float s = 0.f, c = 1.f;
+        if (rot) fast_sincos(thl, s, c);
+        gb0 = c * d0 + s * d1;
+        gb1 = -s * d0 + c * d1;
+    }
+    float *U = p.Ust + bh * nck * NP + (int64_t)(2 * i) * P + pc;
+    for (int c0 = nck - 1; c0 >= 0; c0 -= 4) {
+        float u0[4], u1[4], dec[4], ph[4];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-        const int i = i0 + j;
-        if (!piv(j) || cc != 0) continue;
+        for (int q = 0; q < 4; ++q) {
+            const int ck = c0 - q;
+            u0[q] = u1[q] = ph[q] = dec[q] = 0.f;
+            if (ck >= 0) {
+                u0[q] = U[ck * NP];
+                u1[q] = U[ck * NP + P];
+                dec[q] = p.lsum[bh * nck + ck];
+                ph[q] = (rot && ck > 0) ? p.phic[(bh * nck + ck - 1) * N2 + i] : 0.f;
+            }
+        }
 #pragma unroll
-        for (int r = 0; r < RMAX; ++r) {
-            if (r >= R) break;
-            p.bpend[(sidx * N + 2 * i) * R + r] = bpend[r][j][0];
-            p.bpend[(sidx * N + 2 * i + 1) * R + r] = bpend[r][j][1];
+        for (int q = 0; q < 4; ++q) {
+            const int ck = c0 - q;
+            if (ck < 0) break;
+            U[ck * NP] = gb0;
+            U[ck * NP + P] = gb1;
+            const float d = __expf(dec[q]);
+            const float a = d * gb0 + u0[q], v = d * gb1 + u1[q];
+            float s, c;
+            fast_sincos(ph[q], s, c);
+            gb0 = c * a - s * v;
+            gb1 = s * a + c * v;
         }
     }
-    for (int e = tid; e < R * kCW; e += 256) p.xpend[sidx * R * kCW + e] = sm[L::SPN + e];
-    // D gradient share
-    dDacc = wave_sum(dDacc);
-    if (lane == 0) sm[L::SRD + w] = dDacc;
-    __syncthreads();
-    if (tid == 0) p.dDp[sidx] = sm[L::SRD] + sm[L::SRD + 1] + sm[L::SRD + 2] + sm[L::SRD + 3];
+    // adjoint of the state before the first chunk, in the global frame
+    float s = 0.f, c = 1.f;
+    if (rot && p.ang0) fast_sincos((float)wrap_2pi((double)p.ang0[bh * NR + i]), s, c);
+    p.G0w[(bh * N + 2 * i) * P + pc] = c * gb0 - s * gb1;
+    p.G0w[(bh * N + 2 * i + 1) * P + pc] = s * gb0 + c * gb1;
 }
 
-// Segment start states from the forward aggregates (in place), and the final angle.
-// One thread per (sequence, column group, pair).
-__global__ __launch_bounds__(256) void bwd_ffold_kernel(BwdParams p) {
-    const int N = p.N, N2 = N / 2, P = p.P, NR = p.nr;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= p.B * p.H * p.ncg * N2) return;
-    const int i = (int)(e % N2);
-    const int64_t q = e / N2;
-    const int cg = (int)(q % p.ncg);
-    const int64_t bh = q / p.ncg;
-    float s0 = 0.f, c0 = 1.f;
-    double th = 0.0;
-    if (p.ang0 && i < NR) {
-        th = (double)p.ang0[bh * NR + i];
-        fast_sincos((float)wrap_2pi(th), s0, c0);
-    }
-    float g[kCW][2];
-#pragma unroll
-    for (int c = 0; c < kCW; ++c) {
-        const int pc = cg * kCW + c;
-        float u = 0.f, v = 0.f;
-        if (p.h0 && pc < P) {
-            u = p.h0[(bh * N + 2 * i) * P + pc];
-            v = p.h0[(bh * N + 2 * i + 1) * P + pc];
-        }
-        g[c][0] = c0 * u + s0 * v;
-        g[c][1] = -s0 * u + c0 * v;
-    }
-    for (int k = 0; k < p.nseg; ++k) {
-        const int64_t sidx = (bh * p.ncg + cg) * p.nseg + k;
-        const float dec = __expf(p.lseg[bh * p.nseg + k]);
-        const float ang = p.pseg[(bh * p.nseg + k) * N2 + i];
-        th += (double)ang;
-        float s, c;
-        fast_sincos((float)wrap_2pi((double)ang), s, c);
-        float *ga = p.Gagg + (sidx * N + 2 * i) * kCW;
-#pragma unroll
-        for (int cc = 0; cc < kCW; ++cc) {
-            const float a0 = ga[cc], a1 = ga[kCW + cc];
-            ga[cc] = g[cc][0];
-            ga[kCW + cc] = g[cc][1];
-            const float u = dec * g[cc][0], v = dec * g[cc][1];
-            g[cc][0] = c * u + s * v + a0;  // Rot(-phi)
-            g[cc][1] = -s * u + c * v + a1;
-        }
-    }
-    if (cg == 0) p.thfin[bh * N2 + i] = i < NR ? (float)wrap_2pi(th) : 0.f;
-}
-
-// Segment end adjoints from the adjoint aggregates (in place), the gradient of the
-// initial h and the initial-angle share from it.  One thread per (sequence, group, pair).
-__global__ __launch_bounds__(256) void bwd_rfold_kernel(BwdParams p) {
-    const int N = p.N, N2 = N / 2, P = p.P, NR = p.nr;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= p.B * p.H * p.ncg * N2) return;
-    const int i = (int)(e % N2);
-    const int64_t q = e / N2;
-    const int cg = (int)(q % p.ncg);
-    const int64_t bh = q / p.ncg;
-    float s0 = 0.f, c0 = 1.f;
-    if (i < NR) fast_sincos(p.thfin[bh * N2 + i], s0, c0);
-    float a[kCW][2];
-#pragma unroll
-    for (int c = 0; c < kCW; ++c) {
-        const int pc = cg * kCW + c;
-        float u = 0.f, v = 0.f;
-        if (p.dh1 && pc < P) {
-            u = p.dh1[(bh * N + 2 * i) * P + pc];
-            v = p.dh1[(bh * N + 2 * i + 1) * P + pc];
-        }
-        a[c][0] = c0 * u + s0 * v;  // Rot(-Theta_final) dh_final
-        a[c][1] = -s0 * u + c0 * v;
-    }
-    for (int k = p.nseg - 1; k >= 0; --k) {
-        const int64_t sidx = (bh * p.ncg + cg) * p.nseg + k;
-        const float dec = __expf(p.lseg[bh * p.nseg + k]);
-        float s, c;
-        fast_sincos((float)wrap_2pi((double)p.pseg[(bh * p.nseg + k) * N2 + i]), s, c);
-        float *ra = p.Ragg + (sidx * N + 2 * i) * kCW;
-#pragma unroll
-        for (int cc = 0; cc < kCW; ++cc) {
-            const float r0 = ra[cc], r1 = ra[kCW + cc];
-            ra[cc] = a[cc][0];
-            ra[kCW + cc] = a[cc][1];
-            const float u = dec * a[cc][0], v = dec * a[cc][1];
-            a[cc][0] = c * u - s * v + r0;  // Rot(+phi)
-            a[cc][1] = s * u + c * v + r1;
-        }
-    }
-    // gradient of g_{-1} -> dh0 = Rot(Theta_init) a ; initial-angle share <a, -J g_{-1}>
-    float si = 0.f, ci = 1.f;
-    if (p.ang0 && i < NR) fast_sincos((float)wrap_2pi((double)p.ang0[bh * NR + i]), si, ci);
-    float ta = 0.f;
-#pragma unroll
-    for (int c = 0; c < kCW; ++c) {
-        const int pc = cg * kCW + c;
-        if (pc >= P) continue;
-        if (p.dh0) {
-            p.dh0[(bh * N + 2 * i) * P + pc] = ci * a[c][0] - si * a[c][1];
-            p.dh0[(bh * N + 2 * i + 1) * P + pc] = si * a[c][0] + ci * a[c][1];
-        }
-        if (p.h0) {
-            const float u = p.h0[(bh * N + 2 * i) * P + pc], v = p.h0[(bh * N + 2 * i + 1) * P + pc];
-            const float g0 = ci * u + si * v, g1 = -si * u + ci * v;
-            ta += a[c][0] * g1 - a[c][1] * g0;
-        }
-    }
-    p.dang0p[(bh * p.ncg + cg) * N2 + i] = ta;
-}
-
-// Per-token sums of the column-group shares, the boundary terms, the norm backward
-// of B and C, and the initial state's remaining gradients.  Grid (sequence, 16-token
-// block); one wave per (token, rank) row in the norm backward.
-template <class Io>
-__global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
+// ---------------------------------------------------------------- per-chunk gradients
+template <class Io, int NPAD, int PPAD>
+__global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     using ET = typename Io::T;
-    __shared__ float s_thf[64];        // total final-angle gradient of the sequence, per pair
-    __shared__ float s_bl[8][128];     // b of the last token (complex form), per rank
-    __shared__ float s_acc[4][3];
-    __shared__ float s_bias[4 * 2 * 8 * 128];  // per wave, side, rank, n
-    const int N = p.N, N2 = N / 2, P = p.P, R = p.R, NR = p.nr;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t bh = blockIdx.x;
-    const int tb = blockIdx.y;
+    using L = CL<NPAD, PPAD>;
+    constexpr int NT = NPAD / 16, PT = PPAD / 16, NH = NT / 2, PH = PT / 2, NS = NPAD / 32;
+    constexpr int BP = L::BP, XP = L::XP, N2P = L::N2P;
+    constexpr int SQ = 32 * PPAD / kThreads;  // slab elements per thread
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, l16 = lane & 15;
+    const int w = wv & 3, hf = wv >> 2;
+    const int nck = p.nck, N = p.N, P = p.P, R = p.R, N2 = N / 2, NR = p.nr;
+    const int64_t bh = blockIdx.x / nck;
+    const int c = (int)(blockIdx.x - bh * nck);
     const int64_t b = bh / p.H;
     const int h = (int)(bh - b * p.H);
-    const int64_t T = p.T, H = p.H, BH = p.B * p.H;
-    const int ncg = p.ncg;
-    // b of the last token, then the final-angle gradient
-    for (int r = w; r < R; r += 4) {
-        const int64_t bth = (b * T + T - 1) * H + h;
-        norm_row<Io>(p, (const ET *)p.Bm + bth * N * R + r, R, p.bnw,
-                     p.bbias ? p.bbias + ((int64_t)h * R + r) * N : nullptr, s_bl[r]);
-    }
-    __syncthreads();
-    if (tid < N2) {
-        const int i = tid;
-        float v = 0.f;
-        if (i < NR) {
-            for (int cg = 0; cg < ncg; ++cg) v += p.thfp[(bh * ncg + cg) * N2 + i];
-            if (p.dang1) v += p.dang1[bh * NR + i];
-            float s0, c0;
-            fast_sincos(p.thfin[bh * N2 + i], s0, c0);
-            if (p.dpB1)
-                for (int r = 0; r < R; ++r) {
-                    const float u = s_bl[r][2 * i], vv = s_bl[r][2 * i + 1];
-                    const float pb0 = c0 * u - s0 * vv, pb1 = s0 * u + c0 * vv;  // prev_B of the final state
-                    v += -p.dpB1[(bh * N + 2 * i) * R + r] * pb1 + p.dpB1[(bh * N + 2 * i + 1) * R + r] * pb0;
+    const int Qt = kRows / R;
+    // row tiles that can hold a nonzero of row tile w: every later tile, and, when a token's
+    // rows can straddle two tiles (R not dividing 16), the neighbouring earlier one
+    const int st = (16 % R) != 0 ? 1 : 0, amin = w - st, amax = w + st;
+    const int64_t T = p.T, H = p.H;
+    const int64_t t0 = (int64_t)c * Qt;
+    const int Tv = (int)min((int64_t)Qt, T - t0);
+    const int64_t cidx = bh * nck + c;
+    const bool last = c == nck - 1;
+    const float *Gend = p.Ust + cidx * N * (int64_t)P, *Hst = p.Sst + cidx * N * (int64_t)P;
+    // the first state slab, early
+    float stg[SQ];
+    auto load_slab = [&](const float *src, int ns) {
+#pragma unroll
+        for (int q = 0; q < SQ; ++q) {
+            const int e = tid + kThreads * q, row = e / PPAD, col = e - row * PPAD, n = 32 * ns + row;
+            stg[q] = (n < N && col < P) ? src[(int64_t)n * P + col] : 0.f;
+        }
+    };
+    load_slab(Gend, 0);
+    const float dDp = chunk_prologue<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv);
+    float *sB = sm + L::SB, *sC = sm + L::SC, *sX = sm + L::SX, *sY = sm + L::SY, *sS = sm + L::SS;
+    const float *rt = sm + L::RT;
+    auto rcs = [&](int r) { return rt[r]; };
+    auto rkap = [&](int r) { return rt[64 + r]; };
+    auto rgam = [&](int r) { return rt[128 + r]; };
+    auto rtok = [&](int r) { return __float_as_int(rt[192 + r]); };
+    auto rdec = [&](int r) { return rt[256 + r]; };
+    auto recs = [&](int r) { return rt[320 + r]; };
+
+    // ------------------------------------------------ s-oriented triangle: P1 = L o G, P2 = L o dY X^T
+    // lane value [a][i]: t = 16 a + 4 g + i, s = 16 w + l16 (tiles a < amin are zero)
+    f32x4_t P1s[4], P2s[4];
+    {
+        const int s = 16 * w + l16;
+        const float cs_s = rcs(s), kap_s = rkap(s);
+        const int tok_s = rtok(s);
+        float ce = 0.f;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            P1s[a] = P2s[a] = zero4();
+            float rw[4] = {0.f, 0.f, 0.f, 0.f}, rd[4] = {0.f, 0.f, 0.f, 0.f};
+            if (a >= amin) {
+                f32x4_t ga = zero4(), da = zero4();
+#pragma unroll
+                for (int kc = 0; kc < NPAD / 32; ++kc) {
+                    float av[8], bv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        av[j] = sC[(16 * a + l16) * BP + 32 * kc + 8 * g + j];
+                        bv[j] = sB[s * BP + 32 * kc + 8 * g + j];
+                    }
+                    ga = mma8(av, bv, ga);
                 }
+#pragma unroll
+                for (int kc = 0; kc < PPAD / 32; ++kc) {
+                    float av[8], bv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        av[j] = sY[(16 * a + l16) * XP + 32 * kc + 8 * g + j];
+                        bv[j] = sX[s * XP + 32 * kc + 8 * g + j];
+                    }
+                    da = mma8(av, bv, da);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * a + 4 * g + i, tok_t = rtok(t);
+                    const bool later = tok_t > tok_s, same = tok_t == tok_s;
+                    const float ev = later ? __expf(rcs(t) - cs_s) : 0.f;
+                    const float lv = later ? ev * kap_s : (same ? rgam(t) : 0.f);
+                    P1s[a][i] = lv * ga[i];
+                    P2s[a][i] = lv * da[i];
+                    const float gd = ga[i] * da[i];
+                    ce += ev * gd;
+                    rw[i] = kap_s * ev * gd;
+                    rd[i] = same ? gd : 0.f;
+                }
+            }
+            if (hf == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v1 = row_sum16(rw[i]), v2 = row_sum16(rd[i]);
+                    if (l16 == 0) {
+                        sm[L::RW + w * 64 + 16 * a + 4 * g + i] = v1;
+                        sm[L::RD + w * 64 + 16 * a + 4 * g + i] = v2;
+                    }
+                }
+            }
         }
-        s_thf[i] = v;
+        ce = rows_sum4(ce);
+        if (hf == 0 && g == 0) sm[L::CE + s] = ce;
+    }
+    // dX intra (this half's p tiles) and dB~ intra (this half's n tiles): rows s = 16 w + 4 g + i
+    f32x4_t accX[PH], accB[NH];
+#pragma unroll
+    for (int q = 0; q < PH; ++q) {
+        const int bq = hf * PH + q;
+        accX[q] = zero4();
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            if (2 * kc + 1 < amin) continue;
+            float av[8], bv[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                av[j] = P1s[2 * kc][j];
+                av[j + 4] = P1s[2 * kc + 1][j];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bv[j] = sY[tile_k(kc, g, j) * XP + 16 * bq + l16];
+            accX[q] = mma8(av, bv, accX[q]);
+        }
+    }
+#pragma unroll
+    for (int ns = 0; ns < NH; ++ns) {
+        const int nq = 2 * ns + hf;
+        accB[ns] = zero4();
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            if (2 * kc + 1 < amin) continue;
+            float av[8], bv[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                av[j] = P2s[2 * kc][j];
+                av[j + 4] = P2s[2 * kc + 1][j];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bv[j] = sC[tile_k(kc, g, j) * BP + 16 * nq + l16];
+            accB[ns] = mma8(av, bv, accB[ns]);
+        }
+    }
+    // ------------------------------------------------ t-oriented triangle: lane value [a][i]: t = 16 w + l16, s = 16 a + 4 g + i
+    f32x4_t accC[NH], accY[PH];
+    {
+        f32x4_t P2t[4], P1t[4];
+        const int t = 16 * w + l16;
+        const float cs_t = rcs(t), gam_t = rgam(t);
+        const int tok_t = rtok(t);
+        const bool gate = p.z != nullptr;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            P2t[a] = P1t[a] = zero4();
+            if (a > amax) continue;
+            f32x4_t da = zero4(), ga = zero4();
+#pragma unroll
+            for (int kc = 0; kc < PPAD / 32; ++kc) {
+                float av[8], bv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    av[j] = sX[(16 * a + l16) * XP + 32 * kc + 8 * g + j];
+                    bv[j] = sY[t * XP + 32 * kc + 8 * g + j];
+                }
+                da = mma8(av, bv, da);
+            }
+            if (gate) {
+#pragma unroll
+                for (int kc = 0; kc < NPAD / 32; ++kc) {
+                    float av[8], bv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        av[j] = sB[(16 * a + l16) * BP + 32 * kc + 8 * g + j];
+                        bv[j] = sC[t * BP + 32 * kc + 8 * g + j];
+                    }
+                    ga = mma8(av, bv, ga);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * a + 4 * g + i, tok_s = rtok(s);
+                const float lv = tok_t > tok_s ? __expf(cs_t - rcs(s)) * rkap(s) : (tok_t == tok_s ? gam_t : 0.f);
+                P2t[a][i] = lv * da[i];
+                P1t[a][i] = lv * ga[i];
+            }
+        }
+#pragma unroll
+        for (int ns = 0; ns < NH; ++ns) {
+            const int nq = 2 * ns + hf;
+            accC[ns] = zero4();
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                if (2 * kc > amax) continue;
+                float av[8], bv[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    av[j] = P2t[2 * kc][j];
+                    av[j + 4] = P2t[2 * kc + 1][j];
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) bv[j] = sB[tile_k(kc, g, j) * BP + 16 * nq + l16];
+                accC[ns] = mma8(av, bv, accC[ns]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < PH; ++q) {
+            const int bq = hf * PH + q;
+            accY[q] = zero4();
+            if (!gate) continue;
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                if (2 * kc > amax) continue;
+                float av[8], bv[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    av[j] = P1t[2 * kc][j];
+                    av[j + 4] = P1t[2 * kc + 1][j];
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) bv[j] = sX[tile_k(kc, g, j) * XP + 16 * bq + l16];
+                accY[q] = mma8(av, bv, accY[q]);
+            }
+        }
+    }
+    // ------------------------------------------------ state terms, one slab of 32 state rows at a time
+    f32x4_t accXi[PH], accZ[NH], accCi[NH], accYi[PH];
+#pragma unroll
+    for (int q = 0; q < PH; ++q) accXi[q] = accYi[q] = zero4();
+    float hdot = 0.f;
+    float gk[SQ];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+        // adjoint after the chunk (Gb), rows 32 ns ..
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < SQ; ++q) {
+            const int e = tid + kThreads * q, row = e / PPAD, col = e - row * PPAD;
+            sS[row * XP + col] = stg[q];
+            gk[q] = stg[q];
+        }
+        __syncthreads();
+        load_slab(Hst, ns);
+#pragma unroll
+        for (int q = 0; q < PH; ++q) {
+            const int bq = hf * PH + q;
+            float av[8], bv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                av[j] = sB[(16 * w + l16) * BP + 32 * ns + 8 * g + j];
+                bv[j] = sS[(8 * g + j) * XP + 16 * bq + l16];
+            }
+            accXi[q] = mma8(av, bv, accXi[q]);
+        }
+        accZ[ns] = zero4();
+#pragma unroll
+        for (int kc = 0; kc < PPAD / 32; ++kc) {
+            float av[8], bv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                av[j] = sX[(16 * w + l16) * XP + 32 * kc + 8 * g + j];
+                bv[j] = sS[(16 * hf + l16) * XP + 32 * kc + 8 * g + j];
+            }
+            accZ[ns] = mma8(av, bv, accZ[ns]);
+        }
+        // state before the chunk (H), same rows
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < SQ; ++q) {
+            const int e = tid + kThreads * q, row = e / PPAD, col = e - row * PPAD;
+            sS[row * XP + col] = stg[q];
+            hdot += gk[q] * stg[q];
+        }
+        __syncthreads();
+        if (ns + 1 < NS) load_slab(Gend, ns + 1);
+        accCi[ns] = zero4();
+#pragma unroll
+        for (int kc = 0; kc < PPAD / 32; ++kc) {
+            float av[8], bv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                av[j] = sY[(16 * w + l16) * XP + 32 * kc + 8 * g + j];
+                bv[j] = sS[(16 * hf + l16) * XP + 32 * kc + 8 * g + j];
+            }
+            accCi[ns] = mma8(av, bv, accCi[ns]);
+        }
+        if (p.z) {
+#pragma unroll
+            for (int q = 0; q < PH; ++q) {
+                const int bq = hf * PH + q;
+                float av[8], bv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    av[j] = sC[(16 * w + l16) * BP + 32 * ns + 8 * g + j];
+                    bv[j] = sS[(8 * g + j) * XP + 16 * bq + l16];
+                }
+                accYi[q] = mma8(av, bv, accYi[q]);
+            }
+        }
+    }
+    // ------------------------------------------------ epilogue 1: dx, dz, row partials, angle terms
+    const float Dh = p.D[h];
+    const int64_t bth0 = (b * T + t0) * H + h;  // (b, t0, h); token k adds k H
+    float dph[NH][4];
+#pragma unroll
+    for (int q = 0; q < PH; ++q) {
+        const int pc = 16 * (hf * PH + q) + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 16 * w + 4 * g + i, k = rtok(s), r = s - k * R;
+            if (k >= Tv || pc >= P) continue;
+            const int64_t o = (bth0 + (int64_t)k * H) * P * R + (int64_t)pc * R + r;
+            float v = accX[q][i] + rdec(s) * rkap(s) * accXi[q][i] + Dh * sY[s * XP + pc];
+            if (last && k == Tv - 1 && p.dpx1) v += p.dpx1[(bh * P + pc) * R + r];
+            if (p.dx) Io::st((ET *)p.dx + o, v);
+            if (p.z && p.dz) {
+                const float yp = accY[q][i] + recs(s) * accYi[q][i] + Dh * sX[s * XP + pc];
+                const float zv = Io::ld((const ET *)p.z + o), sg = sigmoid_f(zv);
+                Io::st((ET *)p.dz + o, Io::ld((const ET *)p.dy + o) * yp * sg * (1.f + zv * (1.f - sg)));
+            }
+        }
+    }
+    {
+        float ksum[4] = {0.f, 0.f, 0.f, 0.f}, asum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ns = 0; ns < NH; ++ns) {
+            const int n = 16 * (2 * ns + hf) + l16;
+            const bool odd = (n & 1) != 0;
+            const int i2 = n >> 1;
+            float thc = 1.f, ths = 0.f;
+            if (last && p.dpB1 && n < N && i2 < NR) fast_sincos(p.thst[bh * N2 + i2], ths, thc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * w + 4 * g + i, k = rtok(row), r = row - k * R;
+                const float z = rdec(row) * accZ[ns][i];
+                float db = accB[ns][i] + rkap(row) * z;
+                if (last && k == Tv - 1 && p.dpB1 && n < N) {
+                    const float d0 = p.dpB1[(bh * N + 2 * i2) * R + r], d1 = p.dpB1[(bh * N + 2 * i2 + 1) * R + r];
+                    db += odd ? (-ths * d0 + thc * d1) : (thc * d0 + ths * d1);
+                }
+                const float ci = recs(row) * accCi[ns][i];
+                const float dc = accC[ns][i] + ci;
+                const float bn = sB[row * BP + n], cn = sC[row * BP + n];
+                ksum[i] += bn * z;
+                asum[i] += cn * ci;
+                // <d, J v> over the pair: component 0 pairs with -v1, component 1 with v0
+                const float bo = sB[row * BP + (n ^ 1)], co = sC[row * BP + (n ^ 1)];
+                float term = odd ? (db * bo + dc * co) : -(db * bo + dc * co);
+                term += dpp_f<0xB1>(term);
+                dph[ns][i] = term;
+                accB[ns][i] = db;
+                accC[ns][i] = dc;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float kv = row_sum16(ksum[i]), av = row_sum16(asum[i]);
+            if (l16 == 0) {
+                sm[L::KS + hf * 64 + 16 * w + 4 * g + i] = kv;
+                sm[L::AT + hf * 64 + 16 * w + 4 * g + i] = av;
+            }
+        }
+    }
+    const float hd = block_sum(hdot, sm + L::MS);  // (its barriers end every read of x, dy, B~, C~)
+    const float dD = block_sum(dDp, sm + L::MS + 8);
+    // ------------------------------------------------ epilogue 2: angle terms and dB~, dC~ to LDS
+    float *dphi = sm + L::SX;  // [64][N2P], over the x and dy rows
+#pragma unroll
+    for (int ns = 0; ns < NH; ++ns) {
+        const int n = 16 * (2 * ns + hf) + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * g + i;
+            if (!(n & 1)) dphi[row * N2P + (n >> 1)] = (n >> 1) < NR ? dph[ns][i] : 0.f;
+            sB[row * BP + n] = accB[ns][i];
+            sC[row * BP + n] = accC[ns][i];
+        }
     }
     __syncthreads();
-    float aA = 0.f, aDtb = 0.f;
-    float gB[2] = {0.f, 0.f}, gC[2] = {0.f, 0.f};
-    float *part = p.part + (bh * p.ntb + tb) * (int64_t)p.pw;
-    const int64_t t0 = (int64_t)tb * 16;
-    const int Tv = (int)min((int64_t)16, T - t0);
-    // token scalars
-    if (tid < Tv) {
-        const int64_t t = t0 + tid;
-        const int64_t bth = (b * T + t) * H + h;
-        float qv = 0.f, bb = 0.f, gb = 0.f;
-        for (int cg = 0; cg < ncg; ++cg) {
-            const float *s = p.sbar + ((cg * BH + bh) * T + t) * 4;
-            qv += s[0];
-            bb += s[1];
-            gb += s[2];
+    // ------------------------------------------------ per-token scalars (wave 0)
+    if (tid < 64) {
+        const int k = tid;
+        float dcs = 0.f, dk = 0.f, dgd = 0.f;
+        if (k < Tv) {
+            const float kap = sm[L::TK + 64 + k];
+            for (int r = 0; r < R; ++r) {
+                const int row = k * R + r;
+                const float rw = sm[L::RW + row] + sm[L::RW + 64 + row] + sm[L::RW + 128 + row] + sm[L::RW + 192 + row];
+                const float rd = sm[L::RD + row] + sm[L::RD + 64 + row] + sm[L::RD + 128 + row] + sm[L::RD + 192 + row];
+                const float ks = sm[L::KS + row] + sm[L::KS + 64 + row];
+                const float at = sm[L::AT + row] + sm[L::AT + 64 + row];
+                const float ce = sm[L::CE + row];
+                dcs += rw + at - kap * (ce + ks);
+                dk += ce + ks;
+                dgd += rd;
+            }
         }
-        float dt, lam, dsp, dsg;
-        act_scalars(p, bth, h, dt, lam, dsp, dsg);
-        const float A = (p.flags & kFlagAPerToken) ? p.A[bth] : p.A[h];
-        const float al = __expf(dt * A), be = al * dt * (1.f - lam);
-        float ddt = qv * A + bb * al * (1.f - lam) * (1.f + dt * A) + gb * lam;
-        float dlm = -bb * al * dt + gb * dt;
-        const float dAv = qv * dt + bb * be * dt;
-        ddt *= dsp;
-        dlm *= dsg;
-        if (p.flags & kFlagDtSoftplus) aDtb += ddt;
-        if (p.flags & kFlagAPerToken) {
-            if (p.dAt) p.dAt[bth] = dAv;
-        } else {
-            aA += dAv;
+        // the chunk's last token: e^cs_end <Gb, H> and the state terms of every row
+        if (k == Tv - 1) {
+            float btot = 0.f;
+            for (int row = 0; row < Tv * R; ++row)
+                btot += sm[L::TK + 64 + row / R] * (sm[L::KS + row] + sm[L::KS + 64 + row]);
+            dcs += __expf(sm[L::TK + Tv - 1]) * hd + btot;
         }
-        if (p.ddt) p.ddt[bth] = ddt;
-        if (p.dlam) p.dlam[bth] = dlm;
+        // d log alpha_k = sum over the chunk's tokens >= k
+        const float incl = wave_scan_incl(dcs);
+        const float tot = __shfl(incl, 63, 64);
+        const float dla = tot - incl + dcs;
+        if (k < Tv) {
+            float *d = p.dsc + ((bh * T) + t0 + k) * 3;
+            d[0] = dla;
+            d[1] = dk + dgd;
+            d[2] = dk;
+        }
     }
+    // ------------------------------------------------ angle gradients: per pair, sums over the ranks, reverse running sums
+    {
+        float *scr = sm + L::SS;  // [8][64]
+        float seg = 0.f;
+        if (lane < N2P)
+            for (int k = 8 * wv; k < 8 * wv + 8; ++k)
+                if (k < Tv)
+                    for (int r = 0; r < R; ++r) seg += dphi[(k * R + r) * N2P + lane];
+        if (lane < N2P) scr[wv * 64 + lane] = seg;
+        __syncthreads();
+        if (lane < N2P) {
+            float run = 0.f;
+            for (int ww = wv + 1; ww < kWaves; ++ww) run += scr[ww * 64 + lane];
+            if (wv == 0 && lane < N2) p.tot[cidx * N2 + lane] = lane < NR ? run + seg : 0.f;
+            for (int k = 8 * wv + 7; k >= 8 * wv; --k) {
+                if (k >= Tv) continue;
+                for (int r = 0; r < R; ++r) run += dphi[(k * R + r) * N2P + lane];
+                if (lane < NR && p.dtheta) p.dtheta[(bth0 + (int64_t)k * H) * NR + lane] = run;
+            }
+        }
+        __syncthreads();
+    }
+    // ------------------------------------------------ un-rotation and norm backward of each B and C row
+    chunk_angles<N2P>(p, sm + L::SS, sm + L::RW, b, h, t0, Tv);
+    float *acc = sm + L::SX;  // [2][R][NPAD] bias sums, then [2][NPAD] gain sums (over the x and dy rows)
+    for (int e = tid; e < 2 * R * NPAD + 2 * NPAD; e += kThreads) acc[e] = 0.f;
+    __syncthreads();
+    {
+        const bool norm = (p.flags & kFlagNorm) != 0;
+        const float *phi = sm + L::SS;
+        for (int m = 0; m < 8; ++m) {
+            const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
+            if (k >= Qt || k >= Tv) continue;  // uniform per wave
+            const int64_t o = (bth0 + (int64_t)k * H) * N * R + (int64_t)(2 * lane) * R + r;
+            float sn = 0.f, cn = 1.f;
+            if (lane < N2) fast_sincos(phi[k * N2P + lane], sn, cn);
+#pragma unroll
+            for (int side = 0; side < 2; ++side) {
+                const float *rows = side == 0 ? sB : sC;
+                const ET *raw = (const ET *)(side == 0 ? p.Bm : p.Cm);
+                const float *gain = side == 0 ? p.bnw : p.cnw;
+                float v0 = 0.f, v1 = 0.f, d0 = 0.f, d1 = 0.f, g0 = 1.f, g1 = 1.f;
+                if (lane < N2) {
+                    v0 = Io::ld(raw + o);
+                    v1 = Io::ld(raw + o + R);
+                    const float e0 = rows[rho * BP + 2 * lane], e1 = rows[rho * BP + 2 * lane + 1];
+                    d0 = cn * e0 + sn * e1;
+                    d1 = -sn * e0 + cn * e1;
+                    if (gain) {
+                        g0 = gain[2 * lane];
+                        g1 = gain[2 * lane + 1];
+                    }
+                }
+                float rs = 1.f, dot = 0.f;
+                if (norm) {
+                    rs = rsqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)N + p.eps);
+                    dot = wave_sum(d0 * g0 * v0 + d1 * g1 * v1);
+                }
+                if (lane < N2) {
+                    float o0 = d0, o1 = d1;
+                    if (norm) {
+                        const float f = dot * rs * rs * rs / (float)N;
+                        o0 = d0 * g0 * rs - f * v0;
+                        o1 = d1 * g1 * rs - f * v1;
+                        atomicAdd(&acc[2 * R * NPAD + side * NPAD + 2 * lane], d0 * v0 * rs);
+                        atomicAdd(&acc[2 * R * NPAD + side * NPAD + 2 * lane + 1], d1 * v1 * rs);
+                    }
+                    ET *out = (ET *)(side == 0 ? p.dB : p.dC);
+                    if (out) {
+                        Io::st(out + o, o0);
+                        Io::st(out + o + R, o1);
+                    }
+                    atomicAdd(&acc[(side * R + r) * NPAD + 2 * lane], d0);
+                    atomicAdd(&acc[(side * R + r) * NPAD + 2 * lane + 1], d1);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    float *part = p.part + cidx * (int64_t)p.pw;
+    for (int e = tid; e < 2 * N; e += kThreads) {
+        const int side = e / N, n = e - side * N;
+        part[3 + e] = acc[2 * R * NPAD + side * NPAD + n];
+    }
+    for (int e = tid; e < 2 * R * N; e += kThreads) {
+        const int side = e / (R * N), rn = e - side * R * N, r = rn / N, n = rn - r * N;
+        part[3 + 2 * N + e] = acc[(side * R + r) * NPAD + n];
+    }
+    if (tid == 0) part[1] = dD;
+}
+
+// ---------------------------------------------------------------- angle gradient suffix sums
+// tot[c] <- final-angle gradient + sum of tot over the chunks after c.
+__global__ __launch_bounds__(kThreads) void bwd_angle_suffix_kernel(BwdParams p) {
+    __shared__ float scr[kWaves][64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t bh = blockIdx.x;
+    const int N2 = p.N / 2, NR = p.nr, nck = p.nck;
+    const int per = (nck + kWaves - 1) / kWaves;
+    const int c0 = wv * per, c1 = min(nck, c0 + per);
+    float *tot = p.tot + bh * nck * (int64_t)N2;
+    float s = 0.f;
+    if (lane < NR)
+        for (int c = c0; c < c1; ++c) s += tot[(int64_t)c * N2 + lane];
+    scr[wv][lane] = s;
+    __syncthreads();
+    if (lane >= NR) return;
+    float run = p.dang1 ? p.dang1[bh * NR + lane] : 0.f;
+    for (int ww = wv + 1; ww < kWaves; ++ww) run += scr[ww][lane];
+    for (int c = c1 - 1; c >= c0; --c) {
+        const float v = tot[(int64_t)c * N2 + lane];
+        tot[(int64_t)c * N2 + lane] = run;
+        run += v;
+    }
+}
+
+// ---------------------------------------------------------------- initial state
+// h_init, prev_B, prev_x enter as H_0 = Rot(-Theta_init)(h_init + eta_{-1} prev_B prev_x^T);
+// G0w holds the adjoint of h_init + eta_{-1} prev_B prev_x^T (global frame).
+// The initial angle's gradient comes from rotating the whole frame by the same angle,
+// which changes only the states at both ends (the loss sees the final state):
+//   d Theta_init = d Theta_final + <dh_final, J h_final> + <dprevB_final, J prevB_final>
+//                  - <dh_init, J h_init> - <dprevB_init, J prevB_init>      (per pair)
+// with <a, J v> = -a_0 v_1 + a_1 v_0; exact zero when no state enters or leaves.
+template <class Io>
+__global__ __launch_bounds__(256) void bwd_init_kernel(BwdParams p) {
+    using ET = typename Io::T;
+    __shared__ float red[4];
+    __shared__ float sang[4][64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / p.H;
+    const int h = (int)(bh - b * p.H);
+    const int N = p.N, P = p.P, R = p.R, N2 = N / 2, NR = p.nr, nck = p.nck;
+    const int64_t T = p.T;
+    const float *G0 = p.G0w + bh * N * (int64_t)P;
+    if (p.dh0)
+        for (int e = tid; e < N * P; e += 256) p.dh0[bh * N * (int64_t)P + e] = G0[e];
+    const float eta = eta_at(p, b, h, -1);
+    float de = 0.f;
+    for (int e = tid; e < N * R; e += 256) {
+        const int n = e / R, r = e - n * R;
+        float s = 0.f;
+        if (p.px0)
+            for (int pc = 0; pc < P; ++pc) s += G0[(int64_t)n * P + pc] * p.px0[(bh * P + pc) * R + r];
+        if (p.dpB0) p.dpB0[(bh * N + n) * R + r] = eta * s;
+        if (p.pB0) de += p.pB0[(bh * N + n) * R + r] * s;
+    }
+    for (int e = tid; e < P * R; e += 256) {
+        const int pc = e / R, r = e - pc * R;
+        float s = 0.f;
+        if (p.pB0)
+            for (int n = 0; n < N; ++n) s += G0[(int64_t)n * P + pc] * p.pB0[(bh * N + n) * R + r];
+        if (p.dpx0) p.dpx0[(bh * P + pc) * R + r] = eta * s;
+    }
+    de = wave_sum(de);
+    if (lane == 0) red[wv] = de;
+    // initial angle: wave wv sums its share of the columns per pair (lane = pair)
+    float a = 0.f;
+    if (lane < NR) {
+        const int i = lane;
+        const float *Gl = p.Ust + (bh * nck + nck - 1) * N * (int64_t)P;  // adjoint after the last chunk
+        const float *Hf = p.hfin + bh * N * (int64_t)P;                     // state after it, same frame
+        for (int pc = wv; pc < P; pc += 4) {
+            const int64_t o0 = (int64_t)(2 * i) * P + pc, o1 = o0 + P;
+            a += -Gl[o0] * Hf[o1] + Gl[o1] * Hf[o0];
+            if (p.h0) a -= -G0[o0] * p.h0[bh * N * (int64_t)P + o1] + G0[o1] * p.h0[bh * N * (int64_t)P + o0];
+        }
+        for (int r = wv; r < R; r += 4) {
+            if (p.pB0) {
+                // dprev_B_init = eta G0 prev_x (as above)
+                float d0 = 0.f, d1 = 0.f;
+                if (p.px0)
+                    for (int pc = 0; pc < P; ++pc) {
+                        const float xv = p.px0[(bh * P + pc) * R + r];
+                        d0 += G0[(int64_t)(2 * i) * P + pc] * xv;
+                        d1 += G0[(int64_t)(2 * i + 1) * P + pc] * xv;
+                    }
+                d0 *= eta;
+                d1 *= eta;
+                a -= -d0 * p.pB0[(bh * N + 2 * i + 1) * R + r] + d1 * p.pB0[(bh * N + 2 * i) * R + r];
+            }
+        }
+    }
+    // prev_B of the final state: the normalised, biased B of the last token rotated by the
+    // final angle; <dprevB, J Rot(Theta) b> = <Rot(-Theta) dprevB, J b>
+    if (p.dpB1)
+        for (int r = wv; r < R; r += 4) {
+            const int64_t bth = (b * T + T - 1) * p.H + h;
+            const ET *raw = (const ET *)p.Bm + bth * N * R + r;
+            const bool norm = (p.flags & kFlagNorm) != 0;
+            float v0 = 0.f, v1 = 0.f;
+            if (lane < N2) {
+                v0 = Io::ld(raw + (int64_t)(2 * lane) * R);
+                v1 = Io::ld(raw + (int64_t)(2 * lane + 1) * R);
+            }
+            const float rs = norm ? rsqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)N + p.eps) : 1.f;
+            if (lane < NR) {
+                const int i = lane;
+                float b0 = norm ? v0 * rs * (p.bnw ? p.bnw[2 * i] : 1.f) : v0;
+                float b1 = norm ? v1 * rs * (p.bnw ? p.bnw[2 * i + 1] : 1.f) : v1;
+                if (p.bbias) {
+                    b0 += p.bbias[((int64_t)h * R + r) * N + 2 * i];
+                    b1 += p.bbias[((int64_t)h * R + r) * N + 2 * i + 1];
+                }
+                const float th = (float)wrap_2pi((double)p.thst[bh * N2 + i] + (double)p.phic[(bh * nck + nck - 1) * N2 + i]);
+                float sn, cn;
+                fast_sincos(th, sn, cn);
+                const float e0 = p.dpB1[(bh * N + 2 * i) * R + r], e1 = p.dpB1[(bh * N + 2 * i + 1) * R + r];
+                const float f0 = cn * e0 + sn * e1, f1 = -sn * e0 + cn * e1;
+                a += -f0 * b1 + f1 * b0;
+            }
+        }
+    sang[wv][lane] = a;
+    __syncthreads();
+    if (tid == 0) p.deta0[bh] = red[0] + red[1] + red[2] + red[3];
+    if (tid < NR && p.dang0)
+        p.dang0[bh * NR + tid] = (p.dang1 ? p.dang1[bh * NR + tid] : 0.f) + sang[0][tid] + sang[1][tid] +
+                                 sang[2][tid] + sang[3][tid];
+}
+
+// ---------------------------------------------------------------- per-token gradients
+// d dt, d lambda, d A from the chunk kernel's per-token sums; angle gradients completed
+// with the later chunks' sums; per-chunk records of the A and dt-bias gradients.
+__global__ __launch_bounds__(256) void bwd_token_kernel(BwdParams p) {
+    __shared__ float red[4][2];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nck = p.nck, NR = p.nr, N2 = p.N / 2;
+    const int64_t bh = blockIdx.x / nck;
+    const int c = (int)(blockIdx.x - bh * nck);
+    const int64_t b = bh / p.H;
+    const int h = (int)(bh - b * p.H);
+    const int Qt = kRows / p.R;
+    const int64_t T = p.T, H = p.H, t0 = (int64_t)c * Qt;
+    const int Tv = (int)min((int64_t)Qt, T - t0);
+    const int64_t cidx = bh * nck + c;
     if (p.dtheta)
         for (int e = tid; e < Tv * NR; e += 256) {
             const int k = e / NR, i = e - k * NR;
-            const int64_t t = t0 + k;
-            float v = s_thf[i];
-            for (int cg = 0; cg < ncg; ++cg) v += p.tbar[((cg * BH + bh) * T + t) * (int64_t)N2 + i];
-            p.dtheta[((b * T + t) * H + h) * (int64_t)NR + i] = v;
+            p.dtheta[((b * T + t0 + k) * H + h) * (int64_t)NR + i] += p.tot[cidx * N2 + i];
         }
-    // dx of segment-last tokens: the segment's own part and the next segment's share
-    for (int e = tid; e < Tv * R * P; e += 256) {
-        const int k = e / (R * P), rem = e - k * R * P, r = rem / P, pc = rem - r * P;
-        const int64_t t = t0 + k;
-        if ((t + 1) % p.segT != 0 && t != T - 1) continue;
-        const int seg = (int)(t / p.segT), cg = pc / kCW, c2 = pc - cg * kCW;
-        const int64_t sidx = (bh * ncg + cg) * p.nseg + seg;
-        float v = p.xlast[(sidx * R + r) * kCW + c2];
-        if (t == T - 1) {
-            if (p.dpx1) v += p.dpx1[(bh * P + pc) * R + r];
+    float aA = 0.f, aB = 0.f;
+    if (tid < Tv) {
+        const int64_t t = t0 + tid, bth = (b * T + t) * H + h;
+        const float *d = p.dsc + (bh * T + t) * 3;
+        const float dprev = t == 0 ? p.deta0[bh] : p.dsc[(bh * T + t - 1) * 3 + 2];
+        float dt, lam, dsp, dsg;
+        act_scalars(p, bth, h, dt, lam, dsp, dsg);
+        const float Av = (p.flags & kFlagAPerToken) ? p.A[bth] : p.A[h];
+        float ddt = d[0] * Av + d[1] * lam + dprev * (1.f - lam);
+        float dlm = (d[1] - dprev) * dt;
+        const float dAv = d[0] * dt;
+        ddt *= dsp;
+        dlm *= dsg;
+        if (p.ddt) p.ddt[bth] = ddt;
+        if (p.dlam) p.dlam[bth] = dlm;
+        if (p.flags & kFlagAPerToken) {
+            if (p.dAt) p.dAt[bth] = dAv;
         } else {
-            v += p.xpend[((sidx + 1) * R + r) * kCW + c2];
+            aA = dAv;
         }
-        if (p.dx) Io::st((ET *)p.dx + ((b * T + t) * H + h) * P * R + (int64_t)pc * R + r, v);
+        if (p.flags & kFlagDtSoftplus) aB = ddt;
     }
-    // db and dc rows: sums of the shares (plus the boundary shares of db), norm backward;
-    // rows spread over the waves, bias gradients collected per wave in LDS
-    for (int e = tid; e < 4 * 2 * R * N; e += 256) s_bias[e] = 0.f;
-    __syncthreads();
-    for (int q = w; q < Tv * R; q += 4) {
-        const int k = q / R, r = q - k * R;
-        const int64_t t = t0 + k;
-        const int64_t bth = (b * T + t) * H + h;
-        const int seg = (int)(t / p.segT);
-        const bool segl = (t + 1) % p.segT == 0 && t != T - 1;
-#pragma unroll
-        for (int side = 0; side < 2; ++side) {
-            const ET *raw = (const ET *)(side == 0 ? p.Bm : p.Cm) + bth * N * R + r;
-            const float *gain = side == 0 ? p.bnw : p.cnw;
-            const float *src = side == 0 ? p.bbar : p.cbar;
-            const bool norm = (p.flags & kFlagNorm) != 0;
-            float v[2], gv[2], ss = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int n = lane + 64 * kk;
-                v[kk] = n < N ? Io::ld(raw + (int64_t)n * R) : 0.f;
-                ss += v[kk] * v[kk];
-                float g = 0.f;
-                if (n < N) {
-                    for (int cg = 0; cg < ncg; ++cg) g += src[((cg * BH + bh) * T + t) * (int64_t)N * R + n * R + r];
-                    if (side == 0 && segl)
-                        for (int cg = 0; cg < ncg; ++cg)
-                            g += p.bpend[(((bh * ncg + cg) * p.nseg + seg + 1) * N + n) * R + r];
-                    if (side == 0 && t == T - 1 && p.dpB1) {
-                        // prev_B of the final state is Rot(Theta_final) b_{T-1}
-                        const int i = n >> 1;
-                        float s0 = 0.f, c0 = 1.f;
-                        if (i < NR) fast_sincos(p.thfin[bh * N2 + i], s0, c0);
-                        const float d0 = p.dpB1[(bh * N + 2 * i) * R + r], d1 = p.dpB1[(bh * N + 2 * i + 1) * R + r];
-                        g += (n & 1) ? (-s0 * d0 + c0 * d1) : (c0 * d0 + s0 * d1);
-                    }
-                }
-                gv[kk] = g;
-            }
-            ss = wave_sum(ss);
-            const float rs = norm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
-            float dot = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int n = lane + 64 * kk;
-                const float gn = (n < N && gain) ? gain[n] : 1.f;
-                dot += gv[kk] * gn * v[kk];
-                if (n < N) s_bias[((w * 2 + side) * R + r) * N + n] += gv[kk];
-                if (norm) (side == 0 ? gB : gC)[kk] += gv[kk] * v[kk] * rs;
-            }
-            dot = wave_sum(dot);
-            ET *out = (ET *)(side == 0 ? p.dB : p.dC);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int n = lane + 64 * kk;
-                if (n >= N || !out) continue;
-                const float gn = gain ? gain[n] : 1.f;
-                const float d = norm ? gv[kk] * gn * rs - dot * rs * rs * rs * v[kk] / (float)N : gv[kk];
-                Io::st(out + bth * N * R + (int64_t)n * R + r, d);
-            }
-        }
-    }
-    __syncthreads();
-    for (int e = tid; e < 2 * R * N; e += 256) {
-        const int side = e / (R * N), rn = e - side * R * N;
-        float v = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) v += s_bias[(ww * 2 + side) * R * N + rn];
-        part[3 + 2 * N + side * R * N + rn] = v;
-    }
-    // the initial state's prev_B, prev_x and angle gradients (first token block only)
-    if (tb == 0) {
-        for (int e = tid; e < N2 * R; e += 256) {
-            const int i = e / R, r = e - i * R;
-            float d0 = 0.f, d1 = 0.f;
-            for (int cg = 0; cg < ncg; ++cg) {
-                const int64_t sidx = (bh * ncg + cg) * p.nseg;
-                d0 += p.bpend[(sidx * N + 2 * i) * R + r];
-                d1 += p.bpend[(sidx * N + 2 * i + 1) * R + r];
-            }
-            float si = 0.f, ci = 1.f;
-            if (p.ang0 && i < NR) fast_sincos((float)wrap_2pi((double)p.ang0[bh * NR + i]), si, ci);
-            if (p.dpB0) {
-                p.dpB0[(bh * N + 2 * i) * R + r] = ci * d0 - si * d1;
-                p.dpB0[(bh * N + 2 * i + 1) * R + r] = si * d0 + ci * d1;
-            }
-        }
-        if (p.dpx0)
-            for (int e = tid; e < P * R; e += 256) {
-                const int pc = e / R, r = e - pc * R, cg = pc / kCW;
-                p.dpx0[(bh * P + pc) * R + r] = p.xpend[(((bh * ncg + cg) * p.nseg) * R + r) * kCW + pc % kCW];
-            }
-        if (p.dang0 && tid < NR) {
-            const int i = tid;
-            float v = s_thf[i];
-            for (int cg = 0; cg < ncg; ++cg) v += p.dang0p[(bh * ncg + cg) * N2 + i];
-            for (int r = 0; r < R; ++r) {
-                float d0 = 0.f, d1 = 0.f;
-                for (int cg = 0; cg < ncg; ++cg) {
-                    const int64_t sidx = (bh * ncg + cg) * p.nseg;
-                    d0 += p.bpend[(sidx * N + 2 * i) * R + r];
-                    d1 += p.bpend[(sidx * N + 2 * i + 1) * R + r];
-                }
-                float u, vv;
-                init_b(p, bh, i, r, u, vv);
-                v += d0 * vv - d1 * u;
-            }
-            p.dang0[bh * NR + i] = v;
-        }
-    }
-    // parameter partials of this block
-    {
-        const float v1 = wave_sum(aA), v2 = wave_sum(aDtb);
-        if (lane == 0) {
-            s_acc[w][0] = v1;
-            s_acc[w][1] = v2;
-        }
+    aA = wave_sum(aA);
+    aB = wave_sum(aB);
+    if (lane == 0) {
+        red[wv][0] = aA;
+        red[wv][1] = aB;
     }
     __syncthreads();
     if (tid == 0) {
-        part[0] = s_acc[0][0] + s_acc[1][0] + s_acc[2][0] + s_acc[3][0];
-        part[2] = s_acc[0][1] + s_acc[1][1] + s_acc[2][1] + s_acc[3][1];
-        part[1] = 0.f;  // D is summed from the sweep shares
-    }
-    __syncthreads();
-    // gains: per-wave sums through LDS
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int n = lane + 64 * kk;
-        if (n < N) {
-            s_bias[(w * 2 + 0) * N + n] = gB[kk];
-            s_bias[(w * 2 + 1) * N + n] = gC[kk];
-        }
-    }
-    __syncthreads();
-    for (int e = tid; e < 2 * N; e += 256) {
-        const int side = e / N, n = e - side * N;
-        float v = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) v += s_bias[(ww * 2 + side) * N + n];
-        part[3 + side * N + n] = v;
+        float *part = p.part + cidx * (int64_t)p.pw;
+        part[0] = red[0][0] + red[1][0] + red[2][0] + red[3][0];
+        part[2] = red[0][1] + red[1][1] + red[2][1] + red[3][1];
     }
 }
 
-// Parameter gradients: one workgroup per parameter element sums its records (the final
-// kernel's per (sequence, token block) records, the sweeps' D shares) in a fixed order.
+// Parameter gradients: one workgroup per parameter element sums its per-(sequence, chunk)
+// records in a fixed order.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p) {
     __shared__ float s_red[256];
     const int H = p.H, N = p.N, R = p.R;
     const int64_t Bn = p.B;
     const int e = blockIdx.x, tid = threadIdx.x;
     const int nH = 3 * H, nG = 2 * N;
-    const int ntb = p.ntb;
+    const int nck = p.nck;
     float *dst = nullptr;
     float v = 0.f;
     if (e < nH) {
         const int which = e / H, h = e - which * H;  // 0: A, 1: D, 2: dt bias
         dst = which == 0 ? p.dA : (which == 1 ? p.dD : p.ddtb);
         if (dst) dst += h;
-        if (which == 1) {
-            const int per = p.ncg * p.nseg;
-            for (int64_t k = tid; k < Bn * per; k += 256) {
-                const int64_t b = k / per;
-                v += p.dDp[(b * H + h) * (int64_t)per + (k - b * per)];
-            }
-        } else {
-            for (int64_t k = tid; k < Bn * ntb; k += 256) {
-                const int64_t b = k / ntb;
-                v += p.part[((b * H + h) * ntb + (k - b * ntb)) * (int64_t)p.pw + which];
-            }
+        for (int64_t k = tid; k < Bn * nck; k += 256) {
+            const int64_t b = k / nck;
+            v += p.part[((b * H + h) * nck + (k - b * nck)) * (int64_t)p.pw + which];
         }
     } else if (e < nH + nG) {
         const int k2 = e - nH, side = k2 / N, n = k2 - side * N;
         dst = side == 0 ? p.dbnw : p.dcnw;
         if (dst) dst += n;
-        for (int64_t s = tid; s < Bn * H * ntb; s += 256) v += p.part[s * p.pw + 3 + side * N + n];
+        for (int64_t s = tid; s < Bn * H * nck; s += 256) v += p.part[s * p.pw + 3 + side * N + n];
     } else {
         const int k2 = e - nH - nG, side = k2 / (H * R * N), rem = k2 - side * (H * R * N);
         const int h = rem / (R * N), rn = rem - h * (R * N);
         dst = side == 0 ? p.dbb : p.dcb;
         if (dst) dst += rem;
-        for (int64_t k = tid; k < Bn * ntb; k += 256) {
-            const int64_t b = k / ntb;
-            v += p.part[((b * H + h) * ntb + (k - b * ntb)) * (int64_t)p.pw + 3 + 2 * N + side * R * N + rn];
+        for (int64_t k = tid; k < Bn * nck; k += 256) {
+            const int64_t b = k / nck;
+            v += p.part[((b * H + h) * nck + (k - b * nck)) * (int64_t)p.pw + 3 + 2 * N + side * R * N + rn];
         }
     }
     if (!dst) return;  // uniform over the workgroup
@@ -1121,31 +1238,44 @@ __global__ __launch_bounds__(256) void bwd_empty_kernel(BwdParams p) {
     }
 }
 
+namespace {
+
+template <int NPAD, int PPAD>
+constexpr size_t chunk_lds() { return sizeof(float) * CL<NPAD, PPAD>::TOTAL; }
+
+template <class Io, int NPAD, int PPAD>
+hipError_t launch_chunks(const BwdParams &p, hipStream_t st) {
+    const size_t lds = chunk_lds<NPAD, PPAD>();
+    const dim3 grid((unsigned)(p.B * p.H * p.nck)), blk(kThreads);
+    hipError_t e;
+    if ((e = hipFuncSetAttribute((const void *)bwd_chunk_state_kernel<Io, NPAD, PPAD>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    if ((e = hipFuncSetAttribute((const void *)bwd_chunk_grad_kernel<Io, NPAD, PPAD>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((bwd_chunk_state_kernel<Io, NPAD, PPAD>), grid, blk, lds, st, p);
+    const int64_t ne = p.B * p.H * (p.N / 2) * (int64_t)p.P;
+    hipLaunchKernelGGL(bwd_state_pass_kernel, dim3((unsigned)((ne + 255) / 256), 2), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_chunk_grad_kernel<Io, NPAD, PPAD>), grid, blk, lds, st, p);
+    return hipGetLastError();
+}
+
 template <class Io, int NPAD>
-static void launch_sweeps(const BwdParams &p, hipStream_t st, int mode) {
-    const dim3 grid((unsigned)(p.B * p.H * p.ncg * p.nseg)), blk(256);
-    if (p.R == 1) hipLaunchKernelGGL((bwd_sweep_kernel<Io, NPAD, 1>), grid, blk, 0, st, p, mode);
-    else hipLaunchKernelGGL((bwd_sweep_kernel<Io, NPAD, 8>), grid, blk, 0, st, p, mode);
+hipError_t launch_np(const BwdParams &p, hipStream_t st) {
+    if (p.P <= 32) return launch_chunks<Io, NPAD, 32>(p, st);
+    if (p.P <= 64) return launch_chunks<Io, NPAD, 64>(p, st);
+    return launch_chunks<Io, NPAD, 128>(p, st);
 }
 
 template <class Io>
-static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
-    const int npad = p.N <= 32 ? 32 : (p.N <= 64 ? 64 : 128);
-    auto sweep = [&](int mode) {
-        if (npad == 32) launch_sweeps<Io, 32>(p, st, mode);
-        else if (npad == 64) launch_sweeps<Io, 64>(p, st, mode);
-        else launch_sweeps<Io, 128>(p, st, mode);
-    };
-    const int64_t nfold = p.B * p.H * p.ncg * (p.N / 2);
-    const dim3 fgrid((unsigned)((nfold + 255) / 256));
-    sweep(0);
-    hipLaunchKernelGGL(bwd_ffold_kernel, fgrid, dim3(256), 0, st, p);
-    sweep(1);
-    hipLaunchKernelGGL(bwd_rfold_kernel, fgrid, dim3(256), 0, st, p);
-    sweep(2);
-    hipLaunchKernelGGL((bwd_final_kernel<Io>), dim3((unsigned)(p.B * p.H), (unsigned)p.ntb), dim3(256), 0, st, p);
-    return hipGetLastError();
+hipError_t launch_io(const BwdParams &p, hipStream_t st) {
+    if (p.N <= 32) return launch_np<Io, 32>(p, st);
+    if (p.N <= 64) return launch_np<Io, 64>(p, st);
+    return launch_np<Io, 128>(p, st);
 }
+
+}  // namespace
 
 hipError_t launch_bwd(bool bf16, const BwdParams &p, hipStream_t st) {
     if (p.T == 0) {
@@ -1156,8 +1286,13 @@ hipError_t launch_bwd(bool bf16, const BwdParams &p, hipStream_t st) {
         if (m > 0) hipLaunchKernelGGL(bwd_empty_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, p);
         return hipGetLastError();
     }
-    hipError_t e = bf16 ? launch_bwd_t<IoBF16>(p, st) : launch_bwd_t<IoF32>(p, st);
+    hipError_t e = bf16 ? launch_io<IoBF16>(p, st) : launch_io<IoF32>(p, st);
     if (e != hipSuccess) return e;
+    const unsigned nbh = (unsigned)(p.B * p.H);
+    hipLaunchKernelGGL(bwd_angle_suffix_kernel, dim3(nbh), dim3(kThreads), 0, st, p);
+    if (bf16) hipLaunchKernelGGL(bwd_init_kernel<IoBF16>, dim3(nbh), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(bwd_init_kernel<IoF32>, dim3(nbh), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_token_kernel, dim3((unsigned)(nbh * p.nck)), dim3(256), 0, st, p);
     const int total = 3 * p.H + 2 * p.N + 2 * p.H * p.R * p.N;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)total), dim3(256), 0, st, p);
     return hipGetLastError();

@@ -67,9 +67,8 @@ struct StepParams {
     float *h, *pB, *px, *ang;
 };
 
-// Gradients of a scan (reverse-mode).  The state columns are split into groups of 16
-// and the tokens into segments; every backward quantity is linear in the per-column
-// contributions, so per-group partial sums are added by a final per-token kernel.
+// Gradients of a scan (reverse-mode), chunk by chunk: 64 (token, rank) rows per chunk,
+// states before and adjoints after every chunk in the workspace.
 struct BwdParams {
     int64_t B, T;
     int H, P, N, R;
@@ -92,28 +91,20 @@ struct BwdParams {
     // parameter gradients (each may be NULL); summed by bwd_reduce_kernel
     float *dA, *dD, *dbnw, *dcnw, *dbb, *dcb, *ddtb;
     // plan
-    int ncg;   // column groups of 16 columns
-    int nseg;  // segments per sequence
-    int segT;  // tokens per segment (a multiple of the tokens per staged block)
-    int ntb;   // token blocks of the final kernel (16 tokens each)
-    int pw;    // floats per partial-sum record of the final kernel
+    int nck;   // chunks per sequence (64 / R tokens each)
+    int pw;    // floats per partial-sum record (one per (sequence, chunk))
     // workspace (fp32)
-    float *Gagg;   // [BH][ncg][nseg][N][16]  forward aggregates -> (in place) segment start states
-    float *Ragg;   // [BH][ncg][nseg][N][16]  reverse aggregates -> (in place) segment end adjoints
-    float *lseg;   // [BH][nseg]       sum of log alpha over the segment
-    float *pseg;   // [BH][nseg][N/2]  sum of theta over the segment
-    float *thfin;  // [BH][N/2]        final angle
-    float *cbar;   // [ncg][BH*T][N][R] gradient of c, share of the column group
-    float *bbar;   // [ncg][BH*T][N][R] gradient of b, share
-    float *tbar;   // [ncg][BH*T][N/2]  local angle gradient, share
-    float *sbar;   // [ncg][BH*T][4]    d log alpha, beta and gamma gradients, shares
-    float *xlast;  // [BH][ncg][nseg][R][16] dx of a segment's last token without the next segment's share
-    float *xpend;  // [BH][ncg][nseg][R][16] dx share of the token before the segment
-    float *bpend;  // [BH][ncg][nseg][N][R]  db share of the token before the segment
-    float *thfp;   // [BH][ncg][N/2]  final-angle gradient share (last segment)
-    float *dang0p; // [BH][ncg][N/2]  initial-angle gradient share from the initial state
-    float *dDp;    // [BH][ncg][nseg] D gradient shares
-    float *part;   // [BH][ntb][pw]   parameter partial sums of the final kernel
+    float *Sst;    // [BH][nck][N][P] chunk state sums -> (in place) state before each chunk
+    float *Ust;    // [BH][nck][N][P] chunk adjoint sums -> (in place) adjoint after each chunk
+    float *lsum;   // [BH][nck]       sum of log alpha over the chunk
+    float *phic;   // [BH][nck][N/2]  sum of theta over the chunk
+    float *thst;   // [BH][N/2]       angle before the last chunk
+    float *G0w;    // [BH][N][P]      adjoint of the initial state (global frame)
+    float *hfin;   // [BH][N][P]      state after the last chunk (that chunk's frame)
+    float *tot;    // [BH][nck][N/2]  angle gradient sum of the chunk -> (in place) of the later chunks
+    float *dsc;    // [BH][T][3]      d log alpha, d gamma, d eta per token
+    float *deta0;  // [BH]            d eta of the initial state
+    float *part;   // [BH][nck][pw]   parameter partial sums
 };
 hipError_t launch_bwd(bool bf16, const BwdParams &p, hipStream_t stream);
 
