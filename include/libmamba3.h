@@ -204,8 +204,7 @@ size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape);
  * after every chunk (2 * B * H * ceil(T / (64 / R)) * N * P floats) plus per-chunk and
  * per-token partial sums.  The chunk length of the shape is not used.  Gradient pointers
  * in grads may be NULL (not computed), except dz of a gated call.  Parameter gradients
- * are sums over the batch in a fixed order; the gains' and biases' per-chunk parts are
- * accumulated with LDS atomics (last-bit differences between calls are possible there).
+ * are sums in a fixed order (results repeat bit for bit between calls).
  * Errors as for the forward call; T == 0 passes the final state's gradients through.
  */
 m3_status m3_scan_bwd(const m3_shape *shape, const m3_inputs *in, const void *dy, const m3_state *init,

@@ -70,7 +70,14 @@ __device__ __forceinline__ float rows_sum4(float v) {
     v += __shfl_xor(v, 32, 64);
     return v;
 }
-__device__ __forceinline__ float wave_sum(float v) { return rows_sum4(row_sum16(v)); }
+// sum over the wave, returned to every lane: row sums, then rows 0+1 and 2+3 (row_bcast:15
+// into rows 1 and 3), then all four (row_bcast:31 into rows 2 and 3); lane 63 holds the total
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row_sum16(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 // inclusive prefix sum over the 64 lanes of a wave (all lanes active)
 __device__ __forceinline__ float wave_scan_incl(float v) {
     const int lane = threadIdx.x & 63;
@@ -83,6 +90,18 @@ __device__ __forceinline__ float wave_scan_incl(float v) {
 }
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+// Branch-free loads: an absent element is loaded from offset 0 and replaced by 0 afterwards,
+// so that a run of loads is issued before the first wait (a load inside a divergent branch
+// whose value is used in that branch costs a full memory round trip each).
+template <class T>
+__device__ __forceinline__ T ld_raw(const T *base, int64_t off, bool ok) { return base[ok ? off : 0]; }
+template <class Io>
+__device__ __forceinline__ float raw_f(typename Io::T v, bool ok) {
+    float f;
+    if constexpr (Io::bytes == 2) f = bf2f(v);
+    else f = v;
+    return ok ? f : 0.f;
+}
 // acc += A B over one 32-wide contraction chunk (slot j -> instruction j)
 __device__ __forceinline__ f32x4_t mma8(const float (&a)[8], const float (&b)[8], f32x4_t acc) {
 #pragma unroll
@@ -136,22 +155,41 @@ struct CL {
     static constexpr int KS = AT + 128;             // [2][64] B~ . (state term of dB~ / kappa) per row
     static constexpr int MS = KS + 128;             // misc
     static constexpr int TOTAL = MS + 32;
+    static_assert(32 * NPAD <= 2 * kRows * XP, "bias and gain sums must fit over the x and dy rows");
+    static_assert(kRows * N2P <= 2 * kRows * XP, "angle terms must fit over the x and dy rows");
 };
 
 // Running angle sums of a chunk: phi[k][i] = theta summed over tokens 0..k of the chunk
-// (pairs i >= nr: 0).  scratch: [8][64].
+// (pairs i >= nr: 0).  The loads are issued by angle_load, the sums by angle_scan
+// (scratch: [8][64]).
 template <int N2P>
-__device__ void chunk_angles(const BwdParams &p, float *phi, float *scratch, int64_t b, int h, int64_t t0, int Tv) {
+struct AngleTile {
+    static constexpr int Q = kRows * N2P / kThreads > 0 ? kRows * N2P / kThreads : 1;
+    float v[Q];
+};
+template <int N2P>
+__device__ __forceinline__ void angle_load(const BwdParams &p, AngleTile<N2P> &a, int64_t b, int h, int64_t t0, int Tv) {
+    const int tid = threadIdx.x, NR = p.nr;
+#pragma unroll
+    for (int q = 0; q < AngleTile<N2P>::Q; ++q) {
+        const int e = tid + kThreads * q, k = e / N2P, i = e - k * N2P;
+        const bool ok = NR > 0 && e < kRows * N2P && k < Tv && i < NR;
+        const float v = NR > 0 ? ld_raw(p.theta, ((b * p.T + t0 + k) * p.H + h) * (int64_t)NR + i, ok) : 0.f;
+        a.v[q] = ok ? v : 0.f;
+    }
+}
+template <int N2P>
+__device__ void angle_scan(const AngleTile<N2P> &a, float *phi, float *scratch) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int NR = p.nr;
-    const int64_t T = p.T, H = p.H;
-    for (int e = tid; e < kRows * N2P; e += kThreads) {
-        const int k = e / N2P, i = e - k * N2P;
-        phi[e] = (k < Tv && i < NR) ? p.theta[((b * T + t0 + k) * H + h) * (int64_t)NR + i] : 0.f;
+#pragma unroll
+    for (int q = 0; q < AngleTile<N2P>::Q; ++q) {
+        const int e = tid + kThreads * q;
+        if (e < kRows * N2P) phi[e] = a.v[q];
     }
     __syncthreads();
     float run = 0.f;
     if (lane < N2P) {
+#pragma unroll
         for (int k = 8 * wv; k < 8 * wv + 8; ++k) run += phi[k * N2P + lane];
         scratch[wv * 64 + lane] = run;
     }
@@ -159,6 +197,7 @@ __device__ void chunk_angles(const BwdParams &p, float *phi, float *scratch, int
     if (lane < N2P) {
         float off = 0.f;
         for (int ww = 0; ww < wv; ++ww) off += scratch[ww * 64 + lane];
+#pragma unroll
         for (int k = 8 * wv; k < 8 * wv + 8; ++k) {
             off += phi[k * N2P + lane];
             phi[k * N2P + lane] = off;
@@ -168,36 +207,127 @@ __device__ void chunk_angles(const BwdParams &p, float *phi, float *scratch, int
 }
 
 // Stage one chunk: per-token scalars, normalised + biased + rotated B and C rows (scaled by
-// e^(cs_end - cs) kappa and e^cs when SCALED), x and gated dy rows, zero padding.
+// e^(cs_end - cs) kappa and e^cs when SCALED), x and gated dy rows, zero padding.  Every
+// global load of the chunk is issued before the first use.
 // Returns (per thread) its part of sum(dy_gated * x).
 template <class Io, int NPAD, int PPAD, bool SCALED>
 __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h, int64_t t0, int Tv) {
     using ET = typename Io::T;
     using L = CL<NPAD, PPAD>;
+    constexpr int QX = kRows * PPAD / kThreads;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int N = p.N, P = p.P, R = p.R, N2 = N / 2;
     const int Qt = kRows / R;
     const int64_t T = p.T, H = p.H;
     float *tk = sm + L::TK, *rt = sm + L::RT;
-    // per-token scalars (wave 0; lane = token of the chunk)
+    // ---- loads
+    const int k0 = tid;  // token of the chunk (wave 0)
+    const bool okt = tid < 64 && k0 < Tv, okn = okt && t0 + k0 + 1 < T;
+    const int64_t btt = (b * T + t0 + k0) * H + h;
+    float dtr = ld_raw(p.dt, btt, okt), lmr = ld_raw(p.lam, btt, okt);
+    float Ar = (p.flags & kFlagAPerToken) ? ld_raw(p.A, btt, okt) : p.A[h];
+    float dtn = ld_raw(p.dt, btt + H, okn), lmn = ld_raw(p.lam, btt + H, okn);
+    AngleTile<L::N2P> ang;
+    angle_load<L::N2P>(p, ang, b, h, t0, Tv);
+    ET xr[QX], yr[QX], zr[QX];
+    bool xo[QX];
+    const int nx = Qt * PPAD * R;
+    const ET *zp = (const ET *)(p.z ? p.z : p.x);
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+        const int e = tid + kThreads * q;
+        const int k = e / (PPAD * R), rem = e - k * PPAD * R, pc = rem / R, r = rem - pc * R;
+        xo[q] = e < nx && k < Tv && pc < P;
+        const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)P * R + (int64_t)pc * R + r;
+        xr[q] = ld_raw((const ET *)p.x, o, xo[q]);
+        yr[q] = ld_raw((const ET *)p.dy, o, xo[q]);
+        zr[q] = ld_raw(zp, o, xo[q]);
+    }
+    ET rbr[8][2], rcr[8][2];
+    float bb[8][2], cb[8][2];
+    bool ro[8];
+    const float *bbp = p.bbias ? p.bbias : p.dt, *cbp = p.cbias ? p.cbias : p.dt;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
+        ro[m] = k < Qt && k < Tv && lane < N2;
+        const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)N * R + (int64_t)(2 * lane) * R + r;
+        rbr[m][0] = ld_raw((const ET *)p.Bm, o, ro[m]);
+        rbr[m][1] = ld_raw((const ET *)p.Bm, o + R, ro[m]);
+        rcr[m][0] = ld_raw((const ET *)p.Cm, o, ro[m]);
+        rcr[m][1] = ld_raw((const ET *)p.Cm, o + R, ro[m]);
+        const int64_t ob = ((int64_t)h * R + r) * N + 2 * lane;
+        bb[m][0] = ld_raw(bbp, ob, ro[m] && p.bbias);
+        bb[m][1] = ld_raw(bbp, ob + 1, ro[m] && p.bbias);
+        cb[m][0] = ld_raw(cbp, ob, ro[m] && p.cbias);
+        cb[m][1] = ld_raw(cbp, ob + 1, ro[m] && p.cbias);
+    }
+    const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
+    const bool okg = lane < N2;
+    float gb0 = ld_raw(bnp, 2 * lane, okg && p.bnw), gb1 = ld_raw(bnp, 2 * lane + 1, okg && p.bnw);
+    float gc0 = ld_raw(cnp, 2 * lane, okg && p.cnw), gc1 = ld_raw(cnp, 2 * lane + 1, okg && p.cnw);
+    // ---- values (after every load is in flight)
+    dtr = okt ? dtr : 0.f;
+    lmr = okt ? lmr : 0.f;
+    Ar = okt ? Ar : 0.f;
+    dtn = okn ? dtn : 0.f;
+    lmn = okn ? lmn : 0.f;
+    gb0 = okg && p.bnw ? gb0 : 1.f;
+    gb1 = okg && p.bnw ? gb1 : 1.f;
+    gc0 = okg && p.cnw ? gc0 : 1.f;
+    gc1 = okg && p.cnw ? gc1 : 1.f;
+    float rb[8][2], rc[8][2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            rb[m][j] = raw_f<Io>(rbr[m][j], ro[m]);
+            rc[m][j] = raw_f<Io>(rcr[m][j], ro[m]);
+            bb[m][j] = ro[m] && p.bbias ? bb[m][j] : 0.f;
+            cb[m][j] = ro[m] && p.cbias ? cb[m][j] : 0.f;
+        }
+    }
+    // ---- per-token scalars (wave 0; lane = token of the chunk)
     if (tid < 64) {
-        const int k = tid;
         float la = 0.f, kap = 0.f, gam = 0.f;
-        if (k < Tv) {
-            const int64_t t = t0 + k, bth = (b * T + t) * H + h;
-            float dt, lam, u, v;
-            act_scalars(p, bth, h, dt, lam, u, v);
-            const float Av = (p.flags & kFlagAPerToken) ? p.A[bth] : p.A[h];
-            la = dt * Av;
+        if (k0 < Tv) {
+            float dt = dtr, lam = lmr, dn = dtn, ln = lmn;
+            if (p.flags & kFlagDtSoftplus) {
+                const float bias = p.dtbias ? p.dtbias[h] : 0.f;
+                dt = softplus_f(dt + bias);
+                dn = softplus_f(dn + bias);
+            }
+            if (p.flags & kFlagLamSigmoid) {
+                lam = sigmoid_f(lam);
+                ln = sigmoid_f(ln);
+            }
+            la = dt * Ar;
             gam = lam * dt;
-            kap = gam + eta_at(p, b, h, t);
+            kap = gam + (t0 + k0 + 1 < T ? dn * (1.f - ln) : 0.f);
         }
         const float cs = wave_scan_incl(la);
-        tk[k] = cs;
-        tk[64 + k] = kap;
-        tk[128 + k] = gam;
+        tk[k0] = cs;
+        tk[64 + k0] = kap;
+        tk[128 + k0] = gam;
     }
-    chunk_angles<L::N2P>(p, sm + L::SS, sm + L::RW, b, h, t0, Tv);  // (its barriers publish tk)
+    // ---- x and gated dy rows
+    float dDp = 0.f;
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+        const int e = tid + kThreads * q;
+        if (e >= nx) continue;
+        const int k = e / (PPAD * R), rem = e - k * PPAD * R, pc = rem / R, r = rem - pc * R;
+        const float xv = raw_f<Io>(xr[q], xo[q]), yv = raw_f<Io>(yr[q], xo[q]);
+        const float y = p.z ? yv * silu_f(raw_f<Io>(zr[q], xo[q])) : yv;
+        sm[L::SX + (k * R + r) * L::XP + pc] = xv;
+        sm[L::SY + (k * R + r) * L::XP + pc] = y;
+        dDp += xv * y;
+    }
+    for (int e = tid; e < (kRows - Qt * R) * L::XP; e += kThreads) {
+        sm[L::SX + Qt * R * L::XP + e] = 0.f;
+        sm[L::SY + Qt * R * L::XP + e] = 0.f;
+    }
+    angle_scan<L::N2P>(ang, sm + L::SS, sm + L::RW);  // (its barriers publish tk)
     const float cs_end = tk[Tv - 1];
     // per-row tables
     if (tid < kRows) {
@@ -211,85 +341,41 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         rt[256 + rho] = __expf(cs_end - cs);
         rt[320 + rho] = __expf(cs);
     }
-    // x and gated dy rows (elements in memory order (token, p, rank))
-    float dDp = 0.f;
-    for (int e = tid; e < Qt * PPAD * R; e += kThreads) {
-        const int k = e / (PPAD * R), rem = e - k * PPAD * R, pc = rem / R, r = rem - pc * R;
-        float xv = 0.f, yv = 0.f;
-        if (k < Tv && pc < P) {
-            const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)P * R + (int64_t)pc * R + r;
-            xv = Io::ld((const ET *)p.x + o);
-            yv = Io::ld((const ET *)p.dy + o);
-            if (p.z) yv *= silu_f(Io::ld((const ET *)p.z + o));
-        }
-        sm[L::SX + (k * R + r) * L::XP + pc] = xv;
-        sm[L::SY + (k * R + r) * L::XP + pc] = yv;
-        dDp += xv * yv;
-    }
-    for (int e = tid; e < (kRows - Qt * R) * L::XP; e += kThreads) {
-        sm[L::SX + Qt * R * L::XP + e] = 0.f;
-        sm[L::SY + Qt * R * L::XP + e] = 0.f;
-    }
     __syncthreads();  // row tables
-    // B and C rows: wave wv takes rows wv + 8 m; lane = pair
+    // B and C rows: wave wv takes rows wv + 8 m; lane = pair.  Branch-free (absent lanes and
+    // rows compute on zeros and are masked at the store) so that the rows' reductions overlap.
     const bool norm = (p.flags & kFlagNorm) != 0;
-    float rb[8][2], rc[8][2];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
-        rb[m][0] = rb[m][1] = rc[m][0] = rc[m][1] = 0.f;
-        if (k < Qt && k < Tv && lane < N2) {
-            const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)N * R + (int64_t)(2 * lane) * R + r;
-            rb[m][0] = Io::ld((const ET *)p.Bm + o);
-            rb[m][1] = Io::ld((const ET *)p.Bm + o + R);
-            rc[m][0] = Io::ld((const ET *)p.Cm + o);
-            rc[m][1] = Io::ld((const ET *)p.Cm + o + R);
-        }
-    }
+    const float invN = 1.f / (float)N;
     const float *phi = sm + L::SS;
+    const int lp = lane < L::N2P ? lane : 0;  // clamped pair for the LDS reads
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
-        const bool valid = k < Qt && k < Tv;
+        const int rho = wv + 8 * m, k = rho / R;
+        const bool valid = ro[m];
+        const int kc = k < kRows ? k : 0;
         float sb = 1.f, sc = 1.f;
         if (norm) {
-            sb = rsqrtf(wave_sum(rb[m][0] * rb[m][0] + rb[m][1] * rb[m][1]) / (float)N + p.eps);
-            sc = rsqrtf(wave_sum(rc[m][0] * rc[m][0] + rc[m][1] * rc[m][1]) / (float)N + p.eps);
+            sb = rsqrtf(wave_sum(rb[m][0] * rb[m][0] + rb[m][1] * rb[m][1]) * invN + p.eps);
+            sc = rsqrtf(wave_sum(rc[m][0] * rc[m][0] + rc[m][1] * rc[m][1]) * invN + p.eps);
         }
+        float b0 = (norm ? rb[m][0] * sb * gb0 : rb[m][0]) + bb[m][0];
+        float b1 = (norm ? rb[m][1] * sb * gb1 : rb[m][1]) + bb[m][1];
+        float c0 = (norm ? rc[m][0] * sc * gc0 : rc[m][0]) + cb[m][0];
+        float c1 = (norm ? rc[m][1] * sc * gc1 : rc[m][1]) + cb[m][1];
+        float sn, cn;
+        fast_sincos(phi[kc * L::N2P + lp], sn, cn);
+        float fb = 1.f, fc = 1.f;
+        if (SCALED) {
+            fb = rt[256 + rho] * rt[64 + rho];
+            fc = rt[320 + rho];
+        }
+        const float u0 = fb * (cn * b0 - sn * b1), u1 = fb * (sn * b0 + cn * b1);
+        const float v0 = fc * (cn * c0 - sn * c1), v1 = fc * (sn * c0 + cn * c1);
         if (lane < L::N2P) {
-            float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
-            if (valid && lane < N2) {
-                const int n0 = 2 * lane;
-                b0 = norm ? rb[m][0] * sb * (p.bnw ? p.bnw[n0] : 1.f) : rb[m][0];
-                b1 = norm ? rb[m][1] * sb * (p.bnw ? p.bnw[n0 + 1] : 1.f) : rb[m][1];
-                c0 = norm ? rc[m][0] * sc * (p.cnw ? p.cnw[n0] : 1.f) : rc[m][0];
-                c1 = norm ? rc[m][1] * sc * (p.cnw ? p.cnw[n0 + 1] : 1.f) : rc[m][1];
-                if (p.bbias) {
-                    b0 += p.bbias[((int64_t)h * R + r) * N + n0];
-                    b1 += p.bbias[((int64_t)h * R + r) * N + n0 + 1];
-                }
-                if (p.cbias) {
-                    c0 += p.cbias[((int64_t)h * R + r) * N + n0];
-                    c1 += p.cbias[((int64_t)h * R + r) * N + n0 + 1];
-                }
-                float s, c;
-                fast_sincos(phi[k * L::N2P + lane], s, c);
-                float fb = 1.f, fc = 1.f;
-                if (SCALED) {
-                    fb = rt[256 + rho] * rt[64 + rho];
-                    fc = rt[320 + rho];
-                }
-                const float u0 = c * b0 - s * b1, u1 = s * b0 + c * b1;
-                const float v0 = c * c0 - s * c1, v1 = s * c0 + c * c1;
-                b0 = fb * u0;
-                b1 = fb * u1;
-                c0 = fc * v0;
-                c1 = fc * v1;
-            }
-            sm[L::SB + rho * L::BP + 2 * lane] = b0;
-            sm[L::SB + rho * L::BP + 2 * lane + 1] = b1;
-            sm[L::SC + rho * L::BP + 2 * lane] = c0;
-            sm[L::SC + rho * L::BP + 2 * lane + 1] = c1;
+            sm[L::SB + rho * L::BP + 2 * lane] = valid ? u0 : 0.f;
+            sm[L::SB + rho * L::BP + 2 * lane + 1] = valid ? u1 : 0.f;
+            sm[L::SC + rho * L::BP + 2 * lane] = valid ? v0 : 0.f;
+            sm[L::SC + rho * L::BP + 2 * lane + 1] = valid ? v1 : 0.f;
         }
     }
     __syncthreads();
@@ -486,7 +572,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     constexpr int SQ = 32 * PPAD / kThreads;  // slab elements per thread
     extern __shared__ __attribute__((aligned(16))) float sm[];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, l16 = lane & 15;
-    const int w = wv & 3, hf = wv >> 2;
+    // wave (row tile w, column half hf); SIMD wv & 3 hosts row tiles w and 3 - w, which
+    // balances the triangular work
+    const int hf = wv >> 2, w = hf == 0 ? (wv & 3) : 3 - (wv & 3);
     const int nck = p.nck, N = p.N, P = p.P, R = p.R, N2 = N / 2, NR = p.nr;
     const int64_t bh = blockIdx.x / nck;
     const int c = (int)(blockIdx.x - bh * nck);
@@ -508,7 +596,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
 #pragma unroll
         for (int q = 0; q < SQ; ++q) {
             const int e = tid + kThreads * q, row = e / PPAD, col = e - row * PPAD, n = 32 * ns + row;
-            stg[q] = (n < N && col < P) ? src[(int64_t)n * P + col] : 0.f;
+            const bool ok = n < N && col < P;
+            const float v = ld_raw(src, (int64_t)n * P + col, ok);
+            stg[q] = ok ? v : 0.f;
         }
     };
     load_slab(Gend, 0);
@@ -782,21 +872,43 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     const float Dh = p.D[h];
     const int64_t bth0 = (b * T + t0) * H + h;  // (b, t0, h); token k adds k H
     float dph[NH][4];
+    {
+        const bool gz = p.z && p.dz;
+        const ET *zp = (const ET *)(p.z ? p.z : p.x);
+        const float *dpx = p.dpx1 ? p.dpx1 : p.dt;
+        ET zr[PH][4], yr[PH][4];
+        float xf[PH][4];
+        bool eo[PH][4];
 #pragma unroll
-    for (int q = 0; q < PH; ++q) {
-        const int pc = 16 * (hf * PH + q) + l16;
+        for (int q = 0; q < PH; ++q) {
+            const int pc = 16 * (hf * PH + q) + l16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 16 * w + 4 * g + i, k = rtok(s), r = s - k * R;
-            if (k >= Tv || pc >= P) continue;
-            const int64_t o = (bth0 + (int64_t)k * H) * P * R + (int64_t)pc * R + r;
-            float v = accX[q][i] + rdec(s) * rkap(s) * accXi[q][i] + Dh * sY[s * XP + pc];
-            if (last && k == Tv - 1 && p.dpx1) v += p.dpx1[(bh * P + pc) * R + r];
-            if (p.dx) Io::st((ET *)p.dx + o, v);
-            if (p.z && p.dz) {
-                const float yp = accY[q][i] + recs(s) * accYi[q][i] + Dh * sX[s * XP + pc];
-                const float zv = Io::ld((const ET *)p.z + o), sg = sigmoid_f(zv);
-                Io::st((ET *)p.dz + o, Io::ld((const ET *)p.dy + o) * yp * sg * (1.f + zv * (1.f - sg)));
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * w + 4 * g + i, k = rtok(s), r = s - k * R;
+                eo[q][i] = k < Tv && pc < P;
+                const int64_t o = (bth0 + (int64_t)k * H) * P * R + (int64_t)pc * R + r;
+                zr[q][i] = ld_raw(zp, o, eo[q][i] && gz);
+                yr[q][i] = ld_raw((const ET *)p.dy, o, eo[q][i] && gz);
+                const bool okf = eo[q][i] && last && k == Tv - 1 && p.dpx1;
+                const float f = ld_raw(dpx, (bh * P + pc) * R + r, okf);
+                xf[q][i] = okf ? f : 0.f;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < PH; ++q) {
+            const int pc = 16 * (hf * PH + q) + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * w + 4 * g + i, k = rtok(s), r = s - k * R;
+                if (!eo[q][i]) continue;
+                const int64_t o = (bth0 + (int64_t)k * H) * P * R + (int64_t)pc * R + r;
+                const float v = accX[q][i] + rdec(s) * rkap(s) * accXi[q][i] + Dh * sY[s * XP + pc] + xf[q][i];
+                if (p.dx) Io::st((ET *)p.dx + o, v);
+                if (gz) {
+                    const float yp = accY[q][i] + recs(s) * accYi[q][i] + Dh * sX[s * XP + pc];
+                    const float zv = raw_f<Io>(zr[q][i], true), sg = sigmoid_f(zv);
+                    Io::st((ET *)p.dz + o, raw_f<Io>(yr[q][i], true) * yp * sg * (1.f + zv * (1.f - sg)));
+                }
             }
         }
     }
@@ -857,31 +969,35 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         }
     }
     __syncthreads();
-    // ------------------------------------------------ per-token scalars (wave 0)
+    // ------------------------------------------------ per-token scalars (wave 0; lane = row, then token)
     if (tid < 64) {
-        const int k = tid;
+        const int row = tid, k = tid;
+        const bool rv = row / R < Tv && row < Qt * R;
+        float dcs_r = 0.f, dk_r = 0.f, dgd_r = 0.f, bst = 0.f;
+        if (rv) {
+            const float kap = rkap(row);
+            const float rw = sm[L::RW + row] + sm[L::RW + 64 + row] + sm[L::RW + 128 + row] + sm[L::RW + 192 + row];
+            const float ks = sm[L::KS + row] + sm[L::KS + 64 + row];
+            const float ce = sm[L::CE + row];
+            dcs_r = rw + sm[L::AT + row] + sm[L::AT + 64 + row] - kap * (ce + ks);
+            dk_r = ce + ks;
+            dgd_r = sm[L::RD + row] + sm[L::RD + 64 + row] + sm[L::RD + 128 + row] + sm[L::RD + 192 + row];
+            bst = kap * ks;
+        }
+        const float btot = wave_sum(bst);
         float dcs = 0.f, dk = 0.f, dgd = 0.f;
-        if (k < Tv) {
-            const float kap = sm[L::TK + 64 + k];
-            for (int r = 0; r < R; ++r) {
-                const int row = k * R + r;
-                const float rw = sm[L::RW + row] + sm[L::RW + 64 + row] + sm[L::RW + 128 + row] + sm[L::RW + 192 + row];
-                const float rd = sm[L::RD + row] + sm[L::RD + 64 + row] + sm[L::RD + 128 + row] + sm[L::RD + 192 + row];
-                const float ks = sm[L::KS + row] + sm[L::KS + 64 + row];
-                const float at = sm[L::AT + row] + sm[L::AT + 64 + row];
-                const float ce = sm[L::CE + row];
-                dcs += rw + at - kap * (ce + ks);
-                dk += ce + ks;
-                dgd += rd;
+        for (int r = 0; r < R; ++r) {
+            const int src = min(k * R + r, 63);
+            const float a0 = __shfl(dcs_r, src, 64), a1 = __shfl(dk_r, src, 64), a2 = __shfl(dgd_r, src, 64);
+            if (k * R + r < 64) {
+                dcs += a0;
+                dk += a1;
+                dgd += a2;
             }
         }
+        if (k >= Tv) dcs = dk = dgd = 0.f;
         // the chunk's last token: e^cs_end <Gb, H> and the state terms of every row
-        if (k == Tv - 1) {
-            float btot = 0.f;
-            for (int row = 0; row < Tv * R; ++row)
-                btot += sm[L::TK + 64 + row / R] * (sm[L::KS + row] + sm[L::KS + 64 + row]);
-            dcs += __expf(sm[L::TK + Tv - 1]) * hd + btot;
-        }
+        if (k == Tv - 1) dcs += __expf(sm[L::TK + Tv - 1]) * hd + btot;
         // d log alpha_k = sum over the chunk's tokens >= k
         const float incl = wave_scan_incl(dcs);
         const float tot = __shfl(incl, 63, 64);
@@ -896,90 +1012,165 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     // ------------------------------------------------ angle gradients: per pair, sums over the ranks, reverse running sums
     {
         float *scr = sm + L::SS;  // [8][64]
+        float dk8[8];
         float seg = 0.f;
-        if (lane < N2P)
-            for (int k = 8 * wv; k < 8 * wv + 8; ++k)
-                if (k < Tv)
-                    for (int r = 0; r < R; ++r) seg += dphi[(k * R + r) * N2P + lane];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int k = 8 * wv + j;
+            float v = 0.f;
+            if (lane < N2P && k < Tv)
+                for (int r = 0; r < R; ++r) v += dphi[(k * R + r) * N2P + lane];
+            dk8[j] = v;
+            seg += v;
+        }
         if (lane < N2P) scr[wv * 64 + lane] = seg;
         __syncthreads();
         if (lane < N2P) {
             float run = 0.f;
             for (int ww = wv + 1; ww < kWaves; ++ww) run += scr[ww * 64 + lane];
             if (wv == 0 && lane < N2) p.tot[cidx * N2 + lane] = lane < NR ? run + seg : 0.f;
-            for (int k = 8 * wv + 7; k >= 8 * wv; --k) {
-                if (k >= Tv) continue;
-                for (int r = 0; r < R; ++r) run += dphi[(k * R + r) * N2P + lane];
-                if (lane < NR && p.dtheta) p.dtheta[(bth0 + (int64_t)k * H) * NR + lane] = run;
+#pragma unroll
+            for (int j = 7; j >= 0; --j) {
+                const int k = 8 * wv + j;
+                run += dk8[j];
+                if (k < Tv && lane < NR && p.dtheta) p.dtheta[(bth0 + (int64_t)k * H) * NR + lane] = run;
             }
         }
         __syncthreads();
     }
     // ------------------------------------------------ un-rotation and norm backward of each B and C row
-    chunk_angles<N2P>(p, sm + L::SS, sm + L::RW, b, h, t0, Tv);
-    float *acc = sm + L::SX;  // [2][R][NPAD] bias sums, then [2][NPAD] gain sums (over the x and dy rows)
-    for (int e = tid; e < 2 * R * NPAD + 2 * NPAD; e += kThreads) acc[e] = 0.f;
-    __syncthreads();
     {
-        const bool norm = (p.flags & kFlagNorm) != 0;
-        const float *phi = sm + L::SS;
+        // raw B and C rows of this wave (rows wv + 8 m) and the angles, loaded together
+        ET rr[8][2][2];
+        bool ro[8];
+#pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
-            if (k >= Qt || k >= Tv) continue;  // uniform per wave
+            ro[m] = k < Qt && k < Tv && lane < N2;
             const int64_t o = (bth0 + (int64_t)k * H) * N * R + (int64_t)(2 * lane) * R + r;
-            float sn = 0.f, cn = 1.f;
-            if (lane < N2) fast_sincos(phi[k * N2P + lane], sn, cn);
+            rr[m][0][0] = ld_raw((const ET *)p.Bm, o, ro[m]);
+            rr[m][0][1] = ld_raw((const ET *)p.Bm, o + R, ro[m]);
+            rr[m][1][0] = ld_raw((const ET *)p.Cm, o, ro[m]);
+            rr[m][1][1] = ld_raw((const ET *)p.Cm, o + R, ro[m]);
+        }
+        AngleTile<N2P> ang;
+        angle_load<N2P>(p, ang, b, h, t0, Tv);
+        angle_scan<N2P>(ang, sm + L::SS, sm + L::RW);
+        // bias sums: per (side, rank, pair), over the chunk's tokens, of the un-rotated dB~ / dC~
+        // (over the x and dy rows: [8][2][NPAD] per-wave gain sums, then either [8][2][NPAD]
+        // per-wave bias sums or [2][R][NPAD] column bias sums; at most 32 NPAD floats).  When R divides 8 every row of a wave has rank
+        // wv % R and the sums are taken in the row loop below; otherwise a pass over the columns.
+        float *acc = sm + L::SX;
+        const bool rdiv = (8 % R) == 0;
+        if (!rdiv)
+        for (int e = tid; e < 2 * R * (NPAD / 2); e += kThreads) {
+            const int side = e / (R * (NPAD / 2)), rem = e - side * R * (NPAD / 2), r = rem / (NPAD / 2),
+                      i = rem - r * (NPAD / 2);
+            const float *rows = side == 0 ? sB : sC;
+            float a0 = 0.f, a1 = 0.f;
+            for (int k = 0; k < Tv; ++k) {
+                float sn, cn;
+                fast_sincos(sm[L::SS + k * N2P + i], sn, cn);
+                const float e0 = rows[(k * R + r) * BP + 2 * i], e1 = rows[(k * R + r) * BP + 2 * i + 1];
+                a0 += cn * e0 + sn * e1;
+                a1 += -sn * e0 + cn * e1;
+            }
+            acc[16 * NPAD + (side * R + r) * NPAD + 2 * i] = a0;
+            acc[16 * NPAD + (side * R + r) * NPAD + 2 * i + 1] = a1;
+        }
+        __syncthreads();
+        const bool norm = (p.flags & kFlagNorm) != 0;
+        float ga[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this wave's gain sums (lane = pair)
+        float ba[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this wave's bias sums (rank wv % R)
+        const float invN = 1.f / (float)N;
+        const float *phi = sm + L::SS;
+        float gn[2][2];
+        {
+            const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
+            const bool okb = lane < N2 && p.bnw, okc = lane < N2 && p.cnw;
+            gn[0][0] = ld_raw(bnp, 2 * lane, okb);
+            gn[0][1] = ld_raw(bnp, 2 * lane + 1, okb);
+            gn[1][0] = ld_raw(cnp, 2 * lane, okc);
+            gn[1][1] = ld_raw(cnp, 2 * lane + 1, okc);
+            gn[0][0] = okb ? gn[0][0] : 1.f;
+            gn[0][1] = okb ? gn[0][1] : 1.f;
+            gn[1][0] = okc ? gn[1][0] : 1.f;
+            gn[1][1] = okc ? gn[1][1] : 1.f;
+        }
+        const int lp = lane < N2P ? lane : 0;  // clamped pair for the LDS reads
+        const bool lv = lane < N2;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int rho = wv + 8 * m, k = rho / R;
+            if (k >= Qt || k >= Tv) continue;  // uniform per wave
+            float sn, cn;
+            fast_sincos(phi[k * N2P + lp], sn, cn);
 #pragma unroll
             for (int side = 0; side < 2; ++side) {
-                const float *rows = side == 0 ? sB : sC;
-                const ET *raw = (const ET *)(side == 0 ? p.Bm : p.Cm);
-                const float *gain = side == 0 ? p.bnw : p.cnw;
-                float v0 = 0.f, v1 = 0.f, d0 = 0.f, d1 = 0.f, g0 = 1.f, g1 = 1.f;
-                if (lane < N2) {
-                    v0 = Io::ld(raw + o);
-                    v1 = Io::ld(raw + o + R);
-                    const float e0 = rows[rho * BP + 2 * lane], e1 = rows[rho * BP + 2 * lane + 1];
-                    d0 = cn * e0 + sn * e1;
-                    d1 = -sn * e0 + cn * e1;
-                    if (gain) {
-                        g0 = gain[2 * lane];
-                        g1 = gain[2 * lane + 1];
-                    }
-                }
-                float rs = 1.f, dot = 0.f;
+                float *rows = side == 0 ? sB : sC;
+                const float v0 = raw_f<Io>(rr[m][side][0], ro[m]), v1 = raw_f<Io>(rr[m][side][1], ro[m]);
+                const float g0 = gn[side][0], g1 = gn[side][1];
+                const float e0 = rows[rho * BP + 2 * lp], e1 = rows[rho * BP + 2 * lp + 1];
+                const float d0 = lv ? cn * e0 + sn * e1 : 0.f, d1 = lv ? -sn * e0 + cn * e1 : 0.f;
+                float o0 = d0, o1 = d1;
                 if (norm) {
-                    rs = rsqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)N + p.eps);
-                    dot = wave_sum(d0 * g0 * v0 + d1 * g1 * v1);
+                    const float rs = rsqrtf(wave_sum(v0 * v0 + v1 * v1) * invN + p.eps);
+                    const float dot = wave_sum(d0 * g0 * v0 + d1 * g1 * v1);
+                    const float f = dot * rs * rs * rs * invN;
+                    o0 = d0 * g0 * rs - f * v0;
+                    o1 = d1 * g1 * rs - f * v1;
+                    ga[side][0] += d0 * v0 * rs;
+                    ga[side][1] += d1 * v1 * rs;
                 }
-                if (lane < N2) {
-                    float o0 = d0, o1 = d1;
-                    if (norm) {
-                        const float f = dot * rs * rs * rs / (float)N;
-                        o0 = d0 * g0 * rs - f * v0;
-                        o1 = d1 * g1 * rs - f * v1;
-                        atomicAdd(&acc[2 * R * NPAD + side * NPAD + 2 * lane], d0 * v0 * rs);
-                        atomicAdd(&acc[2 * R * NPAD + side * NPAD + 2 * lane + 1], d1 * v1 * rs);
-                    }
-                    ET *out = (ET *)(side == 0 ? p.dB : p.dC);
-                    if (out) {
-                        Io::st(out + o, o0);
-                        Io::st(out + o + R, o1);
-                    }
-                    atomicAdd(&acc[(side * R + r) * NPAD + 2 * lane], d0);
-                    atomicAdd(&acc[(side * R + r) * NPAD + 2 * lane + 1], d1);
+                ba[side][0] += d0;
+                ba[side][1] += d1;
+                if (lv) {
+                    rows[rho * BP + 2 * lane] = o0;
+                    rows[rho * BP + 2 * lane + 1] = o1;
                 }
             }
         }
+        if (lane < NPAD / 2)
+#pragma unroll
+            for (int side = 0; side < 2; ++side) {
+                acc[(wv * 2 + side) * NPAD + 2 * lane] = ga[side][0];
+                acc[(wv * 2 + side) * NPAD + 2 * lane + 1] = ga[side][1];
+                if (rdiv) {
+                    acc[16 * NPAD + (wv * 2 + side) * NPAD + 2 * lane] = ba[side][0];
+                    acc[16 * NPAD + (wv * 2 + side) * NPAD + 2 * lane + 1] = ba[side][1];
+                }
+            }
     }
     __syncthreads();
+    // dB and dC, in memory order (token, n, rank)
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+        ET *out = (ET *)(side == 0 ? p.dB : p.dC);
+        if (!out) continue;
+        const float *rows = side == 0 ? sB : sC;
+        for (int e = tid; e < Tv * N * R; e += kThreads) {
+            const int k = e / (N * R), rem = e - k * N * R, n = rem / R, r = rem - n * R;
+            Io::st(out + (bth0 + (int64_t)k * H) * N * R + rem, rows[(k * R + r) * BP + n]);
+        }
+    }
+    const float *acc = sm + L::SX;
     float *part = p.part + cidx * (int64_t)p.pw;
     for (int e = tid; e < 2 * N; e += kThreads) {
         const int side = e / N, n = e - side * N;
-        part[3 + e] = acc[2 * R * NPAD + side * NPAD + n];
+        float v = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) v += acc[(ww * 2 + side) * NPAD + n];
+        part[3 + e] = v;
     }
     for (int e = tid; e < 2 * R * N; e += kThreads) {
         const int side = e / (R * N), rn = e - side * R * N, r = rn / N, n = rn - r * N;
-        part[3 + 2 * N + e] = acc[(side * R + r) * NPAD + n];
+        float v = 0.f;
+        if ((8 % R) == 0) {
+            for (int ww = r; ww < kWaves; ww += R) v += acc[16 * NPAD + (ww * 2 + side) * NPAD + n];
+        } else {
+            v = acc[16 * NPAD + (side * R + r) * NPAD + n];
+        }
+        part[3 + 2 * N + e] = v;
     }
     if (tid == 0) part[1] = dD;
 }
