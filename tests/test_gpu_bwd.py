@@ -160,3 +160,47 @@ def test_bwd_empty_sequence():
     for k in ("h", "prev_B", "prev_x", "angle"):
         assert np.array_equal(g["init"][k].cpu().numpy(), dfin[k].astype(np.float32))
     assert float(g["D"].abs().sum()) == 0.0 and float(g["A"].abs().sum()) == 0.0
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_bwd_full_workloads(k):
+    """The bench workloads at full size (SISO config, MIMO rank 4, the 16384-token N 128 one):
+    every gradient against the oracle's reverse sweep on the same inputs, with norm gains and
+    biases, an initial state and final-state gradients."""
+    import torch
+    from synth import WORKLOADS, bf16_round
+    m3 = _m3()
+    w = WORKLOADS[k]
+    log(f"case bwd full workload {k} {w}")
+    inp = make_inputs(w)
+    params = make_norm_params(w)
+    st0 = make_state(w, scale=0.4)
+    rng = np.random.default_rng(w.seed + 5)
+    dy = bf16_round(rng.standard_normal(np.shape(inp["x"])).astype(np.float32))
+    R, NR = w.rank, w.dstate // 2
+    dfin = dict(h=rng.standard_normal((w.batch, w.nheads, w.dstate, w.headdim)).astype(np.float32),
+                prev_B=rng.standard_normal((w.batch, w.nheads, w.dstate, R)).astype(np.float32),
+                prev_x=rng.standard_normal((w.batch, w.nheads, w.headdim, R)).astype(np.float32),
+                angle=rng.standard_normal((w.batch, w.nheads, NR)).astype(np.float32))
+    data = [inp[n] for n in ("x", "B", "C", "dt", "lam", "theta", "A", "D")]
+    ref = oracle.scan_bwd(*data, dy, init=st0, dfinal=dfin, **params)
+    bf = torch.bfloat16 if w.io == "bf16" else torch.float32
+    dev = [torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in data]
+    for i in range(3):
+        dev[i] = dev[i].to(bf)
+    sd = lambda st: {kk: torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).cuda() for kk, v in st.items()}
+    g = m3.m3_scan_bwd(*dev, torch.from_numpy(dy).cuda().to(bf), init=sd(st0), dfinal=sd(dfin),
+                       **{kk: torch.from_numpy(v).cuda() for kk, v in params.items()})
+    torch.cuda.synchronize()
+    bad = []
+    for name in ("x", "B", "C", "dt", "lam", "theta", "A", "D", "b_bias", "c_bias", "b_norm_w", "c_norm_w"):
+        e = _err(g[name].float().cpu().numpy(), ref[name], w.io == "bf16" and name in ("x", "B", "C"))
+        log(f"  d{name}: {e:.3e}")
+        if not e <= GATE:
+            bad.append((name, e))
+    for name in ("h", "prev_B", "prev_x", "angle"):
+        e = _err(g["init"][name].cpu().numpy(), ref["init"][name], False)
+        log(f"  dinit.{name}: {e:.3e}")
+        if not e <= GATE:
+            bad.append(("init." + name, e))
+    assert not bad, bad
