@@ -349,6 +349,10 @@ m3_status bwd_impl(const m3_shape *s, const m3_inputs *in, const void *dy, const
         p.dang0 = dinit->angle;
     }
     p.nck = pl.nck;
+    {
+        const int e = s->io == M3_BF16 ? 8 : 4;
+        p.vec = (s->headdim * s->rank) % e == 0 && (s->dstate * s->rank) % e == 0 && nr % 4 == 0;
+    }
     p.pw = pl.pw;
     char *base = static_cast<char *>(ws);
     auto at = [&](size_t off) { return pl.total ? reinterpret_cast<float *>(base + off) : nullptr; };

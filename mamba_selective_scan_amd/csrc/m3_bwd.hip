@@ -179,13 +179,22 @@ __device__ __forceinline__ void angle_load(const BwdParams &p, AngleTile<N2P> &a
     }
 }
 template <int N2P>
+__device__ void angle_scan_lds(float *phi, float *scratch);
+template <int N2P>
 __device__ void angle_scan(const AngleTile<N2P> &a, float *phi, float *scratch) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int q = 0; q < AngleTile<N2P>::Q; ++q) {
         const int e = tid + kThreads * q;
         if (e < kRows * N2P) phi[e] = a.v[q];
     }
+    angle_scan_lds<N2P>(phi, scratch);
+}
+// running sums over the tokens of the angles staged in phi[64][N2P]
+template <int N2P>
+__device__ void angle_scan_lds(float *phi, float *scratch) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    (void)tid;
     __syncthreads();
     float run = 0.f;
     if (lane < N2P) {
@@ -204,6 +213,234 @@ __device__ void angle_scan(const AngleTile<N2P> &a, float *phi, float *scratch) 
         }
     }
     __syncthreads();
+}
+
+// 16-byte load of 16 / sizeof(T) consecutive elements (offset 0 when absent)
+template <class T>
+__device__ __forceinline__ u32x4_t ld_vec(const T *base, int64_t off, bool ok) {
+    return *reinterpret_cast<const u32x4_t *>(base + (ok ? off : 0));
+}
+template <class Io>
+__device__ __forceinline__ float vec_elem(const u32x4_t &v, int j) {
+    if constexpr (Io::bytes == 2) {
+        const uint32_t w = v[j >> 1];
+        return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+        return __uint_as_float(v[j]);
+    }
+}
+
+// The chunk staging of chunk_prologue with 16-byte loads: each (token, rank-interleaved row)
+// run of x, dy, z, B and C and each token's angles are read as whole vectors (one or two per
+// thread), unpacked into the LDS tiles, and the B and C rows are then normalised and rotated
+// in place.  Needs P R and N R multiples of 16 / sizeof(element) and nr a multiple of 4.
+template <class Io, int NPAD, int PPAD, bool SCALED>
+__device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, int h, int64_t t0, int Tv) {
+    using ET = typename Io::T;
+    using L = CL<NPAD, PPAD>;
+    constexpr int E = 16 / Io::bytes;
+    constexpr int QX = (kRows * PPAD / E + kThreads - 1) / kThreads;
+    constexpr int QB = (kRows * NPAD / E + kThreads - 1) / kThreads;
+    constexpr int QT = (kRows * L::N2P / 4 + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int N = p.N, P = p.P, R = p.R, N2 = N / 2, NR = p.nr;
+    const int Qt = kRows / R, rows = Tv * R;
+    const int64_t T = p.T, H = p.H;
+    float *tk = sm + L::TK, *rt = sm + L::RT, *phi = sm + L::SS;
+    // ---- loads
+    const int k0 = tid;  // token of the chunk (wave 0)
+    const bool okt = tid < 64 && k0 < Tv, okn = okt && t0 + k0 + 1 < T;
+    const int64_t btt = (b * T + t0 + k0) * H + h;
+    float dtr = ld_raw(p.dt, btt, okt), lmr = ld_raw(p.lam, btt, okt);
+    float Ar = (p.flags & kFlagAPerToken) ? ld_raw(p.A, btt, okt) : p.A[h];
+    float dtn = ld_raw(p.dt, btt + H, okn), lmn = ld_raw(p.lam, btt + H, okn);
+    const int vx = P * R / E, vb = N * R / E, vt = NR / 4;
+    const ET *zp = (const ET *)(p.z ? p.z : p.x);
+    u32x4_t xv[QX], yv[QX], zv[QX], bv[QB], cv[QB], tv[QT];
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+        const int e = tid + kThreads * q, k = e / vx, v = e - k * vx;
+        const bool ok = e < Tv * vx;
+        const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)P * R + (int64_t)v * E;
+        xv[q] = ld_vec((const ET *)p.x, o, ok);
+        yv[q] = ld_vec((const ET *)p.dy, o, ok);
+        zv[q] = ld_vec(zp, o, ok);
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+        const int e = tid + kThreads * q, k = e / vb, v = e - k * vb;
+        const bool ok = e < Tv * vb;
+        const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)N * R + (int64_t)v * E;
+        bv[q] = ld_vec((const ET *)p.Bm, o, ok);
+        cv[q] = ld_vec((const ET *)p.Cm, o, ok);
+    }
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+        const int e = tid + kThreads * q, k = vt > 0 ? e / vt : 0, v = e - k * vt;
+        const bool ok = vt > 0 && e < Tv * vt;
+        tv[q] = ld_vec(p.theta ? p.theta : p.dt, ((b * T + t0 + k) * H + h) * (int64_t)NR + 4 * v, ok);
+    }
+    // gains and (rank wv % R when R divides 8) biases of this lane's pair
+    const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
+    const bool okg = lane < N2;
+    float gb0 = ld_raw(bnp, 2 * lane, okg && p.bnw), gb1 = ld_raw(bnp, 2 * lane + 1, okg && p.bnw);
+    float gc0 = ld_raw(cnp, 2 * lane, okg && p.cnw), gc1 = ld_raw(cnp, 2 * lane + 1, okg && p.cnw);
+    const bool rdiv = (8 % R) == 0;
+    const float *bbp = p.bbias ? p.bbias : p.dt, *cbp = p.cbias ? p.cbias : p.dt;
+    const int64_t obw = ((int64_t)h * R + (wv % R)) * N + 2 * lane;
+    float bw0 = ld_raw(bbp, obw, okg && rdiv && p.bbias), bw1 = ld_raw(bbp, obw + 1, okg && rdiv && p.bbias);
+    float cw0 = ld_raw(cbp, obw, okg && rdiv && p.cbias), cw1 = ld_raw(cbp, obw + 1, okg && rdiv && p.cbias);
+    // ---- zero padding of the tiles (disjoint from the loaded elements)
+    for (int row = wv; row < kRows; row += kWaves) {
+        for (int col = lane; col < L::XP; col += 64)
+            if (row >= rows || col >= P) {
+                sm[L::SX + row * L::XP + col] = 0.f;
+                sm[L::SY + row * L::XP + col] = 0.f;
+            }
+        for (int col = lane; col < L::BP; col += 64)
+            if (row >= rows || col >= N) {
+                sm[L::SB + row * L::BP + col] = 0.f;
+                sm[L::SC + row * L::BP + col] = 0.f;
+            }
+        if (lane < L::N2P && (row >= Tv || lane >= NR)) phi[row * L::N2P + lane] = 0.f;
+    }
+    // ---- per-token scalars (wave 0; lane = token of the chunk)
+    if (tid < 64) {
+        float la = 0.f, kap = 0.f, gam = 0.f;
+        if (k0 < Tv) {
+            float dt = dtr, lam = lmr, dn = dtn, ln = lmn;
+            if (p.flags & kFlagDtSoftplus) {
+                const float bias = p.dtbias ? p.dtbias[h] : 0.f;
+                dt = softplus_f(dt + bias);
+                dn = softplus_f(dn + bias);
+            }
+            if (p.flags & kFlagLamSigmoid) {
+                lam = sigmoid_f(lam);
+                ln = sigmoid_f(ln);
+            }
+            la = dt * Ar;
+            gam = lam * dt;
+            kap = gam + (okn ? dn * (1.f - ln) : 0.f);
+        }
+        const float cs = wave_scan_incl(la);
+        tk[k0] = cs;
+        tk[64 + k0] = kap;
+        tk[128 + k0] = gam;
+    }
+    // ---- unpack x, gated dy, raw B and C, angles
+    float dDp = 0.f;
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+        const int e = tid + kThreads * q, k = e / vx, v = e - k * vx;
+        if (e >= Tv * vx) continue;
+        int pc = (v * E) / R, r = v * E - pc * R;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const float xf = vec_elem<Io>(xv[q], j);
+            float yf = vec_elem<Io>(yv[q], j);
+            if (p.z) yf *= silu_f(vec_elem<Io>(zv[q], j));
+            sm[L::SX + (k * R + r) * L::XP + pc] = xf;
+            sm[L::SY + (k * R + r) * L::XP + pc] = yf;
+            dDp += xf * yf;
+            if (++r == R) {
+                r = 0;
+                ++pc;
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+        const int e = tid + kThreads * q, k = e / vb, v = e - k * vb;
+        if (e >= Tv * vb) continue;
+        int n = (v * E) / R, r = v * E - n * R;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            sm[L::SB + (k * R + r) * L::BP + n] = vec_elem<Io>(bv[q], j);
+            sm[L::SC + (k * R + r) * L::BP + n] = vec_elem<Io>(cv[q], j);
+            if (++r == R) {
+                r = 0;
+                ++n;
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+        const int e = tid + kThreads * q, k = vt > 0 ? e / vt : 0, v = e - k * vt;
+        if (vt == 0 || e >= Tv * vt) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) phi[k * L::N2P + 4 * v + j] = __uint_as_float(tv[q][j]);
+    }
+    angle_scan_lds<L::N2P>(phi, sm + L::RW);  // (its barriers publish every tile and tk)
+    const float cs_end = tk[Tv - 1];
+    if (tid < kRows) {
+        const int rho = tid, k = rho / R;
+        const bool valid = k < Qt && k < Tv;
+        const float cs = valid ? tk[k] : cs_end;
+        rt[rho] = cs;
+        rt[64 + rho] = valid ? tk[64 + k] : 0.f;
+        rt[128 + rho] = valid ? tk[128 + k] : 0.f;
+        rt[192 + rho] = __int_as_float(valid ? k : 1 << 20);
+        rt[256 + rho] = __expf(cs_end - cs);
+        rt[320 + rho] = __expf(cs);
+    }
+    __syncthreads();  // row tables
+    // ---- B and C rows in place: norm, gain, bias, rotation (and scale); lane = pair
+    const bool norm = (p.flags & kFlagNorm) != 0;
+    const float invN = 1.f / (float)N;
+    gb0 = okg && p.bnw ? gb0 : 1.f;
+    gb1 = okg && p.bnw ? gb1 : 1.f;
+    gc0 = okg && p.cnw ? gc0 : 1.f;
+    gc1 = okg && p.cnw ? gc1 : 1.f;
+    const int lp = lane < L::N2P ? lane : 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
+        const bool valid = k < Qt && k < Tv && lane < N2;
+        float b0 = sm[L::SB + rho * L::BP + 2 * lp], b1 = sm[L::SB + rho * L::BP + 2 * lp + 1];
+        float c0 = sm[L::SC + rho * L::BP + 2 * lp], c1 = sm[L::SC + rho * L::BP + 2 * lp + 1];
+        b0 = valid ? b0 : 0.f;
+        b1 = valid ? b1 : 0.f;
+        c0 = valid ? c0 : 0.f;
+        c1 = valid ? c1 : 0.f;
+        float sb = 1.f, sc = 1.f;
+        if (norm) {
+            sb = rsqrtf(wave_sum(b0 * b0 + b1 * b1) * invN + p.eps);
+            sc = rsqrtf(wave_sum(c0 * c0 + c1 * c1) * invN + p.eps);
+        }
+        float bi0 = bw0, bi1 = bw1, ci0 = cw0, ci1 = cw1;
+        if (!rdiv) {
+            const int64_t ob = ((int64_t)h * R + r) * N + 2 * lane;
+            bi0 = ld_raw(bbp, ob, valid && p.bbias);
+            bi1 = ld_raw(bbp, ob + 1, valid && p.bbias);
+            ci0 = ld_raw(cbp, ob, valid && p.cbias);
+            ci1 = ld_raw(cbp, ob + 1, valid && p.cbias);
+        }
+        bi0 = p.bbias ? bi0 : 0.f;
+        bi1 = p.bbias ? bi1 : 0.f;
+        ci0 = p.cbias ? ci0 : 0.f;
+        ci1 = p.cbias ? ci1 : 0.f;
+        b0 = (norm ? b0 * sb * gb0 : b0) + bi0;
+        b1 = (norm ? b1 * sb * gb1 : b1) + bi1;
+        c0 = (norm ? c0 * sc * gc0 : c0) + ci0;
+        c1 = (norm ? c1 * sc * gc1 : c1) + ci1;
+        float sn, cn;
+        fast_sincos(phi[(k < kRows ? k : 0) * L::N2P + lp], sn, cn);
+        float fb = 1.f, fc = 1.f;
+        if (SCALED) {
+            fb = rt[256 + rho] * rt[64 + rho];
+            fc = rt[320 + rho];
+        }
+        const float u0 = fb * (cn * b0 - sn * b1), u1 = fb * (sn * b0 + cn * b1);
+        const float v0 = fc * (cn * c0 - sn * c1), v1 = fc * (sn * c0 + cn * c1);
+        if (lane < L::N2P) {
+            sm[L::SB + rho * L::BP + 2 * lane] = valid ? u0 : 0.f;
+            sm[L::SB + rho * L::BP + 2 * lane + 1] = valid ? u1 : 0.f;
+            sm[L::SC + rho * L::BP + 2 * lane] = valid ? v0 : 0.f;
+            sm[L::SC + rho * L::BP + 2 * lane + 1] = valid ? v1 : 0.f;
+        }
+    }
+    __syncthreads();
+    return dDp;
 }
 
 // Stage one chunk: per-token scalars, normalised + biased + rotated B and C rows (scaled by
@@ -411,7 +648,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_state_kernel(BwdParams p) 
     const int Qt = kRows / p.R;
     const int64_t t0 = (int64_t)c * Qt;
     const int Tv = (int)min((int64_t)Qt, p.T - t0);
-    chunk_prologue<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
+    if (p.vec) chunk_prologue_vec<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
+    else chunk_prologue<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
     const int64_t cidx = bh * nck + c;
     for (int q = wv; q < 2 * NT * PT; q += kWaves) {
         const int which = q / (NT * PT), rem = q - which * NT * PT, a = rem / PT, bq = rem - a * PT;
@@ -602,7 +840,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         }
     };
     load_slab(Gend, 0);
-    const float dDp = chunk_prologue<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv);
+    const float dDp = p.vec ? chunk_prologue_vec<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv)
+                            : chunk_prologue<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv);
     float *sB = sm + L::SB, *sC = sm + L::SC, *sX = sm + L::SX, *sY = sm + L::SY, *sS = sm + L::SS;
     const float *rt = sm + L::RT;
     auto rcs = [&](int r) { return rt[r]; };

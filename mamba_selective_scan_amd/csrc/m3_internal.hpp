@@ -92,6 +92,7 @@ struct BwdParams {
     float *dA, *dD, *dbnw, *dcnw, *dbb, *dcb, *ddtb;
     // plan
     int nck;   // chunks per sequence (64 / R tokens each)
+    int vec;   // 16-byte staging loads (P R, N R multiples of 16 / element size, nr of 4)
     int pw;    // floats per partial-sum record (one per (sequence, chunk))
     // workspace (fp32)
     float *Sst;    // [BH][nck][N][P] chunk state sums -> (in place) state before each chunk
