@@ -37,7 +37,7 @@ class _Args(ctypes.Structure):
         ("mutation", ctypes.c_int32), ("nthreads", ctypes.c_int32),
         ("rope_pairs", ctypes.c_int32), ("a_per_token", ctypes.c_int32),
         ("dt_softplus", ctypes.c_int32), ("lam_sigmoid", ctypes.c_int32),
-        ("dt_bias", _dp), ("z", _dp),
+        ("dt_bias", _dp), ("z", _dp), ("half_split", ctypes.c_int32),
     ]
 
 
@@ -91,7 +91,7 @@ def _ptr(a):
 def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
          b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None,
          init=None, nthreads=None, mutation=0, rope_pairs=None,
-         dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None):
+         dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None, half_split=False):
     """Run the sequential fp64 loop.
 
     Shapes: x [Bt,T,H,P] (or [Bt,T,H,P,R]), B/C [Bt,T,H,N] (or [...,N,R]),
@@ -101,7 +101,8 @@ def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
     prev_x [Bt,H,P,R], angle [Bt,H,NR].  NR = ``rope_pairs`` (default N/2:
     every pair rotates).  ``dt_softplus``/``dt_bias`` and ``lam_sigmoid``
     take dt and lam as raw values; ``z`` (shaped like x) gates the output
-    with silu(z).
+    with silu(z); ``half_split`` pairs components (i, i + N/2) instead of
+    (2i, 2i + 1).
 
     Returns (y, final) with y shaped like x (float64) and final a dict of
     float64 arrays h, prev_B, prev_x, angle (angle is the unreduced running
@@ -151,6 +152,7 @@ def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
                                   _ptr(fin["prev_x"]), _ptr(fin["angle"]))
     a.mutation = int(mutation)
     a.nthreads = int(nthreads or os.cpu_count() or 1)
+    a.half_split = int(bool(half_split))
     rc = _load().m3o_scan(ctypes.byref(a))
     if rc != 0:
         raise ValueError("oracle: unsupported sizes")
@@ -198,7 +200,7 @@ def _prepare(x, B, C, dt, lam, theta, A, D, bcnorm, eps, b_norm_w, c_norm_w, b_b
 def scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5,
              b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, init=None, dfinal=None,
              nthreads=None, mutation=0, rope_pairs=None, dt_softplus=False, dt_bias=None,
-             lam_sigmoid=False, z=None):
+             lam_sigmoid=False, z=None, half_split=False):
     """Gradients of the scan by the fp64 reverse sweep (m3_oracle_bwd.c).
 
     Same inputs and options as ``scan``; ``dy`` is the gradient of y (shaped like x) and
@@ -207,7 +209,30 @@ def scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5,
     theta, A (per head, or per token when A is), D, b_norm_w, c_norm_w, b_bias, c_bias
     ([H, R, N]), dt_bias, z (when gated), and init (a dict h, prev_B, prev_x, angle).
     Gradients of raw dt / lam when the activations are on.
+
+    ``half_split``: the pairing (i, i + N/2) is the adjacent pairing on the N axis
+    permuted (component c of pair i at 2i + c); the sweep runs on the permuted
+    problem (B, C, gains, biases, the N rows of h and prev_B and of their final-state
+    gradients) and the gradients of those inputs are permuted back.
     """
+    if half_split:
+        N = np.shape(B)[3]
+        perm = np.concatenate([np.arange(0, N, 2), np.arange(1, N, 2)])  # user n -> adjacent slot
+        fw = np.empty(N, dtype=np.int64)  # adjacent slot m holds user component fw[m]
+        fw[perm] = np.arange(N)
+        take = lambda v, ax: None if v is None else np.take(np.asarray(v, np.float64), fw, axis=ax)
+        back = lambda v, ax: None if v is None else np.take(v, perm, axis=ax)
+        st = lambda d: None if d is None else {k: (take(v, 2) if k in ("h", "prev_B") else v) for k, v in d.items()}
+        g = scan_bwd(x, take(B, 3), take(C, 3), dt, lam, theta, A, D, dy, bcnorm=bcnorm, eps=eps,
+                     b_norm_w=take(b_norm_w, 0), c_norm_w=take(c_norm_w, 0), b_bias=take(b_bias, 2),
+                     c_bias=take(c_bias, 2), init=st(init), dfinal=st(dfinal), nthreads=nthreads,
+                     mutation=mutation, rope_pairs=rope_pairs, dt_softplus=dt_softplus, dt_bias=dt_bias,
+                     lam_sigmoid=lam_sigmoid, z=z)
+        for k, ax in (("B", 3), ("C", 3), ("b_norm_w", 0), ("c_norm_w", 0), ("b_bias", 2), ("c_bias", 2)):
+            g[k] = back(g[k], ax)
+        for k in ("h", "prev_B"):
+            g["init"][k] = back(g["init"][k], 2)
+        return g
     a, keep, (Bsz, T, H, P, N, R, NR) = _prepare(
         x, B, C, dt, lam, theta, A, D, bcnorm, eps, b_norm_w, c_norm_w, b_bias, c_bias, init,
         nthreads, 0, rope_pairs, dt_softplus, dt_bias, lam_sigmoid, z)

@@ -110,9 +110,11 @@ static void prep_vec(const m3o_args *a, const double *v, int64_t stride, const d
     for (int i = 0; i < N / 2; ++i) {
         double c = cos(ang[i]), sn = sin(ang[i]);
         if (a->mutation == 3) sn = -sn; /* planted: rotation in the other direction for B and C */
-        double u = hat[2 * i], w = hat[2 * i + 1];
-        out[2 * i] = u * c - w * sn;
-        out[2 * i + 1] = u * sn + w * c;
+        /* the two components of pair i: adjacent, or one in each half of N */
+        const int i0 = a->half_split ? i : 2 * i, i1 = a->half_split ? i + N / 2 : 2 * i + 1;
+        double u = hat[i0], w = hat[i1];
+        out[i0] = u * c - w * sn;
+        out[i1] = u * sn + w * c;
     }
 }
 

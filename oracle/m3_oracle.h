@@ -31,6 +31,7 @@ typedef struct {
     int32_t lam_sigmoid;  /* 1: lam holds raw values; lambda = sigmoid(lam) */
     const double *dt_bias; /* [H] or NULL (= 0) */
     const double *z;       /* gate input laid out like y, or NULL (no gate) */
+    int32_t half_split;    /* 1: pair i is components (i, i + N/2); 0: (2i, 2i + 1) */
 } m3o_args;
 
 int m3o_scan(const m3o_args *a);

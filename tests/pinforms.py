@@ -89,7 +89,7 @@ def quadratic(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
 
 
 def complex_state_loop(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
-                       gains=(None, None), biases=(None, None)):
+                       gains=(None, None), biases=(None, None), half_split=False):
     """The scan with an explicitly complex state and no cumulative angle.
 
     torchmamba "Math notes" (M3 SISO, RoPE trick): the complex state
@@ -98,7 +98,8 @@ def complex_state_loop(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
     alpha_t * exp(-i theta_t); B and C stay unrotated:
         g_t = exp(-i theta_t) (alpha_t g_{t-1} + beta_t B^_{t-1} x_{t-1}^T) + gamma_t B^_t x_t^T
         y_t = Re(conj(C^_t) . g_t)   (summed over pairs; real dot product of 2-vectors)
-    Zero initial state.
+    Zero initial state.  ``half_split``: the complex number of pair i is made of
+    components i and i + N/2 instead of 2i and 2i + 1.
     """
     x, B, C, siso = _as_mimo(x, B, C)
     Bsz, T, H, P, R = x.shape
@@ -108,8 +109,12 @@ def complex_state_loop(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
         for h in range(H):
             Bh = prep_hat(B[b, :, h], gains[0], biases[0], h, bcnorm, eps)
             Ch = prep_hat(C[b, :, h], gains[1], biases[1], h, bcnorm, eps)
-            Bc = Bh[:, 0::2, :] + 1j * Bh[:, 1::2, :]   # [T, N/2, R]
-            Cc = Ch[:, 0::2, :] + 1j * Ch[:, 1::2, :]
+            if half_split:
+                Bc = Bh[:, :N // 2, :] + 1j * Bh[:, N // 2:, :]
+                Cc = Ch[:, :N // 2, :] + 1j * Ch[:, N // 2:, :]
+            else:
+                Bc = Bh[:, 0::2, :] + 1j * Bh[:, 1::2, :]   # [T, N/2, R]
+                Cc = Ch[:, 0::2, :] + 1j * Ch[:, 1::2, :]
             g = np.zeros((N // 2, P), dtype=np.complex128)
             prev = np.zeros((N // 2, P), dtype=np.complex128)
             Ah = np.asarray(A, np.float64)

@@ -112,6 +112,17 @@ def test_gradients_with_every_option(rank):
     assert all(v < TOL for v in worst.values()), worst
 
 
+@pytest.mark.parametrize("rank", [1, 2])
+def test_gradients_half_split(rank):
+    """Half-split pairing: the reverse sweep on the N-permuted problem equals finite
+    differences of the forward loop, which pairs (i, i + N/2) natively."""
+    kw, W, V = _case(rank=rank, seed=15 + rank)
+    kw["half_split"] = True
+    g = _analytic(kw, W, V)
+    worst = _fd_check(kw, W, V, g, CORE)
+    assert all(v < TOL for v in worst.values()), worst
+
+
 def test_empty_sequence_passes_state_gradients():
     kw, W, V = _case(T=0, seed=3)
     g = _analytic(kw, W, V)

@@ -151,6 +151,47 @@ def test_streaming_with_options(rank):
             assert rel_err(st[k], full_f[k]) < TOL, k
 
 
+# ---------------------------------------------------------------- P15: half-split pairing
+@pytest.mark.parametrize("rank,nr", [(1, None), (2, None), (1, 2)])
+def test_half_split_pairing_equals_complex_form(rank, nr):
+    """Pair i made of components (i, i + N/2) (the rotate-half layout of the canonical block):
+    the loop equals the complex-state form whose complex numbers are built from the two halves
+    of N, with norm gains and biases and partial rotation; it differs from adjacent pairing."""
+    w, inp, ex = draw(rope_pairs=nr, batch=2, seqlen=12, nheads=2, headdim=3, dstate=8, rank=rank, seed=117)
+    inp["dt"] = (inp["dt"] * 6).astype(np.float32)
+    th = (ex["theta_p"] if nr is not None else inp["theta"]) * 4
+    args = (inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], th, inp["A"], inp["D"])
+    prm = make_norm_params(w)
+    kw = dict(rope_pairs=nr) if nr is not None else {}
+    y, _ = oracle.scan(*args, half_split=True, **prm, **kw)
+    ref = pf.complex_state_loop(*args, gains=(prm["b_norm_w"], prm["c_norm_w"]),
+                                biases=(prm["b_bias"], prm["c_bias"]), half_split=True)
+    assert rel_err(y, ref) < TOL
+    y_adj, _ = oracle.scan(*args, **prm, **kw)
+    assert rel_err(y_adj, ref) > 1e-3
+
+
+def test_half_split_streaming():
+    """Split schedules with the carried state (h and prev_B rows in the half-split layout)."""
+    w, inp, ex = draw(batch=2, seqlen=11, nheads=2, headdim=3, dstate=8, rank=2, seed=119)
+    full = {k: inp[k] for k in ("x", "B", "C", "dt", "lam", "theta")}
+    st0 = make_state(w, scale=0.5)
+
+    def run(part, init):
+        return oracle.scan(part["x"], part["B"], part["C"], part["dt"], part["lam"], part["theta"],
+                           inp["A"], inp["D"], init=init, half_split=True)
+
+    full_y, full_f = run(full, st0)
+    st, ys, t0 = st0, [], 0
+    for n in (4, 1, 6):
+        y, st = run({k: v[:, t0:t0 + n] for k, v in full.items()}, st)
+        ys.append(y)
+        t0 += n
+    assert rel_err(np.concatenate(ys, axis=1), full_y) < TOL
+    for k in ("h", "prev_B", "prev_x", "angle"):
+        assert rel_err(st[k], full_f[k]) < TOL, k
+
+
 # ---------------------------------------------------------------- planted mistakes
 def _option_pins_pass(mutation):
     w, inp, ex = draw(rope_pairs=2, batch=1, seqlen=10, nheads=2, headdim=3, dstate=8, seed=113)
