@@ -43,6 +43,14 @@
  *                         Both: dotLLM PR #136, "Stage C" (in_proj split -> softplus/sigmoid).
  *   z != NULL             gated output y = (C~^T h + D x) * silu(z), silu(v) = v sigmoid(v).
  *                         dotLLM PR #136, "Stage C" (D skip -> silu(z) gate).
+ *   M3_FLAG_HALF_SPLIT    rotation pair i is components (i, i + N/2) of B, C (and of the
+ *                         state's rows) instead of (2i, 2i + 1): the rotate-half layout of
+ *                         the canonical block.  torchmamba "Math notes" (RoPE trick on pairs
+ *                         of state components); the pages leave the pairing layout open and
+ *                         the two differ only by a permutation of N.  The scans and the
+ *                         gradient call permute B, C, gains, biases and the state rows into
+ *                         the workspace (larger workspace, one extra pass over B and C);
+ *                         the decode step pairs natively.
  *
  * Layouts: row-major, contiguous, last index fastest.
  *   x, y, z [B, T, H, P]        MIMO: [B, T, H, P, R]       io dtype
@@ -94,7 +102,8 @@ enum {
     M3_FLAG_PARTIAL_ROPE = 1u << 1, /* rotate only the leading rope_pairs pairs */
     M3_FLAG_A_PER_TOKEN = 1u << 2,  /* A is [B, T, H] */
     M3_FLAG_DT_SOFTPLUS = 1u << 3,  /* dt is raw: use softplus(dt + dt_bias[h]) */
-    M3_FLAG_LAM_SIGMOID = 1u << 4   /* lam is raw: use sigmoid(lam) */
+    M3_FLAG_LAM_SIGMOID = 1u << 4,  /* lam is raw: use sigmoid(lam) */
+    M3_FLAG_HALF_SPLIT = 1u << 5    /* rotation pairs (i, i + N/2) */
 };
 
 typedef struct {

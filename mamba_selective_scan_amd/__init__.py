@@ -21,7 +21,8 @@ import torch
 __all__ = ["m3_scan_siso", "m3_scan_mimo", "m3_step", "m3_scan_bwd", "m3_scan_workspace_bytes",
            "m3_scan_bwd_workspace_bytes",
            "m3_status_str", "Shape", "M3_F32", "M3_BF16", "M3_FLAG_BCNORM", "M3_FLAG_PARTIAL_ROPE",
-           "M3_FLAG_A_PER_TOKEN", "M3_FLAG_DT_SOFTPLUS", "M3_FLAG_LAM_SIGMOID", "lib_path", "load"]
+           "M3_FLAG_A_PER_TOKEN", "M3_FLAG_DT_SOFTPLUS", "M3_FLAG_LAM_SIGMOID", "M3_FLAG_HALF_SPLIT", "lib_path",
+           "load"]
 
 M3_F32, M3_BF16 = 0, 1
 M3_FLAG_BCNORM = 1 << 0
@@ -29,6 +30,7 @@ M3_FLAG_PARTIAL_ROPE = 1 << 1
 M3_FLAG_A_PER_TOKEN = 1 << 2
 M3_FLAG_DT_SOFTPLUS = 1 << 3
 M3_FLAG_LAM_SIGMOID = 1 << 4
+M3_FLAG_HALF_SPLIT = 1 << 5
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmamba3.so")
 
@@ -152,6 +154,8 @@ def _shape_of(x, B, chunk, bcnorm, eps, mimo, opts):
         flags |= M3_FLAG_DT_SOFTPLUS
     if opts.get("lam_sigmoid"):
         flags |= M3_FLAG_LAM_SIGMOID
+    if opts.get("half_split"):
+        flags |= M3_FLAG_HALF_SPLIT
     return Shape(Bsz, T, H, P, N, R, int(chunk), io, flags, float(eps), int(nr or 0))
 
 
@@ -211,10 +215,10 @@ def m3_scan_workspace_bytes(shape: Shape) -> int:
 def _scan(mimo, x, B, C, dt, lam, theta, A, D, *, chunk=64, bcnorm=True, eps=1e-5,
           b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, init=None, final=None,
           y=None, workspace=None, stream=None, rope_pairs=None, dt_softplus=False, dt_bias=None,
-          lam_sigmoid=False, z=None):
+          lam_sigmoid=False, z=None, half_split=False):
     lib = load()
-    s = _shape_of(x, B, chunk, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A,
-                                                        dt_softplus=dt_softplus, lam_sigmoid=lam_sigmoid))
+    s = _shape_of(x, B, chunk, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A, dt_softplus=dt_softplus,
+                                                        lam_sigmoid=lam_sigmoid, half_split=half_split))
     _need(x, "x", x.dtype, x.device)
     inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
                   dt_bias, z)
@@ -245,7 +249,8 @@ def m3_scan_siso(x, B, C, dt, lam, theta, A, D, **kw):
 
     Canonical-block options: ``rope_pairs`` (rotate only the leading pairs; theta and the
     state angle then hold that many), A of shape [B,T,H] (per-token decay rate),
-    ``dt_softplus`` / ``dt_bias`` and ``lam_sigmoid`` (raw dt / lam), ``z`` (silu gate)."""
+    ``dt_softplus`` / ``dt_bias`` and ``lam_sigmoid`` (raw dt / lam), ``z`` (silu gate),
+    ``half_split`` (rotation pairs (i, i + N/2))."""
     return _scan(False, x, B, C, dt, lam, theta, A, D, **kw)
 
 
@@ -256,15 +261,15 @@ def m3_scan_mimo(x, B, C, dt, lam, theta, A, D, **kw):
 
 def m3_step(x, B, C, dt, lam, theta, A, D, state, *, bcnorm=True, eps=1e-5, b_norm_w=None,
             c_norm_w=None, b_bias=None, c_bias=None, y=None, stream=None, rope_pairs=None,
-            dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None):
+            dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None, half_split=False):
     """One decode step (T == 1) that updates ``state`` in place; returns y.
 
     x [B,1,H,P] (or [B,1,H,P,R]), B/C [B,1,H,N(,R)], dt/lam [B,1,H], theta [B,1,H,N/2]
     (the same options as the scans; a per-token A is [B,1,H])."""
     lib = load()
     mimo = x.dim() == 5
-    s = _shape_of(x, B, 16, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A,
-                                                     dt_softplus=dt_softplus, lam_sigmoid=lam_sigmoid))
+    s = _shape_of(x, B, 16, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A, dt_softplus=dt_softplus,
+                                                     lam_sigmoid=lam_sigmoid, half_split=half_split))
     if s.seqlen != 1:
         raise ValueError("m3_step takes exactly one token (T == 1)")
     _need(x, "x", x.dtype, x.device)
@@ -287,7 +292,7 @@ def m3_scan_bwd_workspace_bytes(shape: Shape) -> int:
 def m3_scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5, b_norm_w=None,
                 c_norm_w=None, b_bias=None, c_bias=None, init=None, dfinal=None, rope_pairs=None,
                 dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None, workspace=None,
-                stream=None):
+                stream=None, half_split=False):
     """Gradients of m3_scan_siso / m3_scan_mimo (SISO when x is 4-D) given ``dy``.
 
     ``init`` is the forward call's initial state and ``dfinal`` the gradients of its final
@@ -298,8 +303,8 @@ def m3_scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5, b_n
     """
     lib = load()
     mimo = x.dim() == 5
-    s = _shape_of(x, B, 16, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A,
-                                                     dt_softplus=dt_softplus, lam_sigmoid=lam_sigmoid))
+    s = _shape_of(x, B, 16, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A, dt_softplus=dt_softplus,
+                                                     lam_sigmoid=lam_sigmoid, half_split=half_split))
     _need(x, "x", x.dtype, x.device)
     inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
                   dt_bias, z)

@@ -31,7 +31,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-result", "-munsafe-fp-atomics"]
 
 SOURCES = ["m3_scan_bf16_vec.hip", "m3_scan_bf16_gen.hip", "m3_scan_bf16_mimo.hip", "m3_scan_f32_vec.hip",
-           "m3_scan_f32_gen.hip", "m3_scan.hip", "m3_state.hip", "m3_bwd.hip", "m3_api.cpp"]
+           "m3_scan_f32_gen.hip", "m3_scan.hip", "m3_state.hip", "m3_bwd.hip", "m3_perm.hip", "m3_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -22,10 +22,10 @@ bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr
 
 static_assert(M3_FLAG_BCNORM == m3::kFlagNorm && M3_FLAG_PARTIAL_ROPE == m3::kFlagPartialRope &&
                   M3_FLAG_A_PER_TOKEN == m3::kFlagAPerToken && M3_FLAG_DT_SOFTPLUS == m3::kFlagDtSoftplus &&
-                  M3_FLAG_LAM_SIGMOID == m3::kFlagLamSigmoid,
+                  M3_FLAG_LAM_SIGMOID == m3::kFlagLamSigmoid && M3_FLAG_HALF_SPLIT == m3::kFlagHalfSplit,
               "flag values of the C ABI and the kernels differ");
 constexpr uint32_t kAllFlags = M3_FLAG_BCNORM | M3_FLAG_PARTIAL_ROPE | M3_FLAG_A_PER_TOKEN | M3_FLAG_DT_SOFTPLUS |
-                               M3_FLAG_LAM_SIGMOID;
+                               M3_FLAG_LAM_SIGMOID | M3_FLAG_HALF_SPLIT;
 
 // Rotated pairs: rope_pairs with M3_FLAG_PARTIAL_ROPE, otherwise all N/2.
 int rotated_pairs(const m3_shape *s) {
@@ -371,6 +371,195 @@ m3_status bwd_impl(const m3_shape *s, const m3_inputs *in, const void *dy, const
                                                                                                      : M3_EHIP;
 }
 
+// ---------------------------------------------------------------- half-split pairing
+// The kernels pair components (2i, 2i + 1).  A half-split call (pairs (i, i + N/2)) runs the
+// same path on copies in the workspace with the N axis permuted: B, C, gains, biases and the
+// N rows of the states in, the N-indexed outputs back.  The copies follow the plain call's
+// workspace, one 256-byte aligned slot per tensor:
+//   B, C, gains, biases (inputs); H0/PB0 the initial state's h / prev_B; H1/PB1 the final
+//   state's (scan) or its gradients (gradient call); H2/PB2 the initial state's gradients;
+//   DB .. DCB the gradients of B, C, the gains and the biases.
+enum HsSlot {
+    kHsB, kHsC, kHsBnw, kHsCnw, kHsBb, kHsCb, kHsH0, kHsPb0, kHsH1, kHsPb1,
+    kHsH2, kHsPb2, kHsDB, kHsDC, kHsDBnw, kHsDCnw, kHsDBb, kHsDCb, kHsCount
+};
+struct HsLayout {
+    size_t off[kHsCount];
+    size_t total;
+};
+HsLayout hs_layout(const m3_shape *s, bool bwd) {
+    HsLayout l{};
+    const int64_t BTH = s->batch * s->seqlen * (int64_t)s->nheads, BH = s->batch * (int64_t)s->nheads;
+    const int64_t N = s->dstate, R = s->rank, P = s->headdim, H = s->nheads;
+    const size_t es = s->io == M3_BF16 ? 2 : 4;
+    const size_t bc = BTH * N * R * es, g = N * 4, bi = H * R * N * 4, hs = BH * N * P * 4, pb = BH * N * R * 4;
+    const size_t bytes[kHsCount] = {bc, bc, g, g, bi, bi, hs, pb, hs, pb,
+                                    bwd ? hs : 0, bwd ? pb : 0, bwd ? bc : 0, bwd ? bc : 0,
+                                    bwd ? g : 0, bwd ? g : 0, bwd ? bi : 0, bwd ? bi : 0};
+    size_t off = 0;
+    for (int k = 0; k < kHsCount; ++k) {
+        l.off[k] = off;
+        off = align_up(off + bytes[k]);
+    }
+    l.total = off;
+    return l;
+}
+
+size_t scan_ws_bytes(const m3_shape *s) {
+    if (!(s->flags & M3_FLAG_HALF_SPLIT)) return plan_of(s).total;
+    m3_shape s2 = *s;
+    s2.flags &= ~M3_FLAG_HALF_SPLIT;
+    return align_up(plan_of(&s2).total) + hs_layout(s, false).total;
+}
+
+size_t bwd_ws_bytes(const m3_shape *s) {
+    if (!(s->flags & M3_FLAG_HALF_SPLIT)) return bwd_plan_of(s).total;
+    m3_shape s2 = *s;
+    s2.flags &= ~M3_FLAG_HALF_SPLIT;
+    return align_up(bwd_plan_of(&s2).total) + hs_layout(s, true).total;
+}
+
+// Permutations of one call's N-indexed tensors between the caller's buffers and the slots.
+struct HsPerm {
+    const m3_shape *s;
+    char *w;
+    HsLayout hl;
+    hipStream_t st;
+    hipError_t e = hipSuccess;
+    void *slot(int k) const { return w + hl.off[k]; }
+    // [outer][N][inner] from src into slot k (to the kernels' order); returns the slot, or NULL
+    template <class T>
+    T *in(const T *src, int k, int64_t outer, int inner, int es) {
+        if (!src) return nullptr;
+        if (e == hipSuccess) e = m3::launch_perm_n(src, slot(k), outer, s->dstate, inner, es, true, st);
+        return static_cast<T *>(slot(k));
+    }
+    // slot k back into dst (the caller's order)
+    void out(int k, void *dst, int64_t outer, int inner, int es) {
+        if (dst && e == hipSuccess) e = m3::launch_perm_n(slot(k), dst, outer, s->dstate, inner, es, false, st);
+    }
+};
+
+m3_status scan_half_split(const m3_shape *s, const m3_inputs *in, void *y, const m3_state *init, m3_state *fin,
+                          void *ws, size_t ws_bytes, void *stream, bool mimo) {
+    m3_status rc = check_shape(s, false);
+    if (rc != M3_OK) return rc;
+    const int nr = rotated_pairs(s);
+    if ((rc = check_inputs(in, s->seqlen > 0 && s->batch > 0, nr)) != M3_OK) return rc;
+    if ((rc = check_state(init, false, nr)) != M3_OK) return rc;
+    if ((rc = check_state(fin, false, nr)) != M3_OK) return rc;
+    if (s->batch == 0) return M3_OK;
+    m3_shape s2 = *s;
+    s2.flags &= ~M3_FLAG_HALF_SPLIT;
+    const size_t base = align_up(plan_of(&s2).total);
+    HsPerm hp{s, nullptr, hs_layout(s, false), reinterpret_cast<hipStream_t>(stream)};
+    if (!ws || ws_bytes < base + hp.hl.total) return M3_EWORKSPACE;
+    if (!aligned16(ws)) return M3_EINVAL;
+    hp.w = static_cast<char *>(ws) + base;
+    const int64_t BTH = s->batch * s->seqlen * (int64_t)s->nheads, BH = s->batch * (int64_t)s->nheads;
+    const int R = s->rank, P = s->headdim, H = s->nheads, es = s->io == M3_BF16 ? 2 : 4;
+    m3_inputs in2 = *in;
+    if (s->seqlen > 0) {
+        in2.Bm = hp.in(static_cast<const char *>(in->Bm), kHsB, BTH, R, es);
+        in2.Cm = hp.in(static_cast<const char *>(in->Cm), kHsC, BTH, R, es);
+    }
+    in2.b_norm_w = hp.in(in->b_norm_w, kHsBnw, 1, 1, 4);
+    in2.c_norm_w = hp.in(in->c_norm_w, kHsCnw, 1, 1, 4);
+    in2.b_bias = hp.in(in->b_bias, kHsBb, (int64_t)H * R, 1, 4);
+    in2.c_bias = hp.in(in->c_bias, kHsCb, (int64_t)H * R, 1, 4);
+    m3_state init2{}, fin2{};
+    if (init) {
+        init2 = *init;
+        init2.h = hp.in(init->h, kHsH0, BH, P, 4);
+        init2.prev_B = hp.in(init->prev_B, kHsPb0, BH, R, 4);
+    }
+    if (fin) {
+        fin2 = *fin;
+        fin2.h = static_cast<float *>(hp.slot(kHsH1));
+        fin2.prev_B = static_cast<float *>(hp.slot(kHsPb1));
+    }
+    if (hp.e != hipSuccess) return M3_EHIP;
+    rc = scan_impl(&s2, &in2, y, init ? &init2 : nullptr, fin ? &fin2 : nullptr, ws, base, stream, mimo);
+    if (rc != M3_OK) return rc;
+    if (fin) {
+        hp.out(kHsH1, fin->h, BH, P, 4);
+        hp.out(kHsPb1, fin->prev_B, BH, R, 4);
+    }
+    return hp.e == hipSuccess ? M3_OK : M3_EHIP;
+}
+
+m3_status bwd_half_split(const m3_shape *s, const m3_inputs *in, const void *dy, const m3_state *init,
+                         const m3_state *dfin, m3_grads *g, m3_state *dinit, void *ws, size_t ws_bytes,
+                         void *stream) {
+    m3_status rc = check_shape(s, false);
+    if (rc != M3_OK) return rc;
+    const int nr = rotated_pairs(s);
+    if ((rc = check_inputs(in, s->seqlen > 0 && s->batch > 0, nr)) != M3_OK) return rc;
+    if ((rc = check_state(init, false, nr)) != M3_OK) return rc;
+    if ((rc = check_state(dfin, false, nr)) != M3_OK) return rc;
+    if ((rc = check_state(dinit, false, nr)) != M3_OK) return rc;
+    if (!g) return M3_EINVAL;
+    if (s->batch == 0) return M3_OK;
+    m3_shape s2 = *s;
+    s2.flags &= ~M3_FLAG_HALF_SPLIT;
+    const size_t base = align_up(bwd_plan_of(&s2).total);
+    HsPerm hp{s, nullptr, hs_layout(s, true), reinterpret_cast<hipStream_t>(stream)};
+    if (!ws || ws_bytes < base + hp.hl.total) return M3_EWORKSPACE;
+    if (!aligned16(ws)) return M3_EINVAL;
+    hp.w = static_cast<char *>(ws) + base;
+    const int64_t BTH = s->batch * s->seqlen * (int64_t)s->nheads, BH = s->batch * (int64_t)s->nheads;
+    const int R = s->rank, P = s->headdim, H = s->nheads, es = s->io == M3_BF16 ? 2 : 4;
+    m3_inputs in2 = *in;
+    if (s->seqlen > 0) {
+        in2.Bm = hp.in(static_cast<const char *>(in->Bm), kHsB, BTH, R, es);
+        in2.Cm = hp.in(static_cast<const char *>(in->Cm), kHsC, BTH, R, es);
+    }
+    in2.b_norm_w = hp.in(in->b_norm_w, kHsBnw, 1, 1, 4);
+    in2.c_norm_w = hp.in(in->c_norm_w, kHsCnw, 1, 1, 4);
+    in2.b_bias = hp.in(in->b_bias, kHsBb, (int64_t)H * R, 1, 4);
+    in2.c_bias = hp.in(in->c_bias, kHsCb, (int64_t)H * R, 1, 4);
+    m3_state init2{}, dfin2{}, dinit2{};
+    if (init) {
+        init2 = *init;
+        init2.h = hp.in(init->h, kHsH0, BH, P, 4);
+        init2.prev_B = hp.in(init->prev_B, kHsPb0, BH, R, 4);
+    }
+    if (dfin) {
+        dfin2 = *dfin;
+        dfin2.h = hp.in(dfin->h, kHsH1, BH, P, 4);
+        dfin2.prev_B = hp.in(dfin->prev_B, kHsPb1, BH, R, 4);
+    }
+    if (dinit) {
+        dinit2 = *dinit;
+        dinit2.h = static_cast<float *>(hp.slot(kHsH2));
+        dinit2.prev_B = static_cast<float *>(hp.slot(kHsPb2));
+    }
+    m3_grads g2 = *g;
+    if (g->dB) g2.dB = hp.slot(kHsDB);
+    if (g->dC) g2.dC = hp.slot(kHsDC);
+    if (g->db_norm_w) g2.db_norm_w = static_cast<float *>(hp.slot(kHsDBnw));
+    if (g->dc_norm_w) g2.dc_norm_w = static_cast<float *>(hp.slot(kHsDCnw));
+    if (g->db_bias) g2.db_bias = static_cast<float *>(hp.slot(kHsDBb));
+    if (g->dc_bias) g2.dc_bias = static_cast<float *>(hp.slot(kHsDCb));
+    if (hp.e != hipSuccess) return M3_EHIP;
+    rc = bwd_impl(&s2, &in2, dy, init ? &init2 : nullptr, dfin ? &dfin2 : nullptr, &g2, dinit ? &dinit2 : nullptr,
+                  ws, base, stream);
+    if (rc != M3_OK) return rc;
+    if (s->seqlen > 0) {
+        hp.out(kHsDB, g->dB, BTH, R, es);
+        hp.out(kHsDC, g->dC, BTH, R, es);
+    }
+    hp.out(kHsDBnw, g->db_norm_w, 1, 1, 4);
+    hp.out(kHsDCnw, g->dc_norm_w, 1, 1, 4);
+    hp.out(kHsDBb, g->db_bias, (int64_t)H * R, 1, 4);
+    hp.out(kHsDCb, g->dc_bias, (int64_t)H * R, 1, 4);
+    if (dinit) {
+        hp.out(kHsH2, dinit->h, BH, P, 4);
+        hp.out(kHsPb2, dinit->prev_B, BH, R, 4);
+    }
+    return hp.e == hipSuccess ? M3_OK : M3_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -380,12 +569,14 @@ size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape) {
         shape->dstate < 2 || shape->rank < 1 || shape->rank > 8 || (shape->dstate & 1) || shape->dstate > 128 ||
         shape->headdim > 128)
         return 0;
-    return bwd_plan_of(shape).total;
+    return bwd_ws_bytes(shape);
 }
 
 m3_status m3_scan_bwd(const m3_shape *shape, const m3_inputs *in, const void *dy, const m3_state *init,
                       const m3_state *dfinal, m3_grads *grads, m3_state *dinit, void *ws, size_t ws_bytes,
                       void *stream) {
+    if (shape && (shape->flags & M3_FLAG_HALF_SPLIT))
+        return bwd_half_split(shape, in, dy, init, dfinal, grads, dinit, ws, ws_bytes, stream);
     return bwd_impl(shape, in, dy, init, dfinal, grads, dinit, ws, ws_bytes, stream);
 }
 
@@ -396,16 +587,22 @@ size_t m3_scan_workspace_bytes(const m3_shape *shape) {
         return 0;
     if (shape->rank < 1 || shape->rank > 8 || (shape->dstate & 1) || shape->dstate > 128 || shape->headdim > 128)
         return 0;
-    return plan_of(shape).total;
+    return scan_ws_bytes(shape);
 }
 
 m3_status m3_scan_siso(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,
                        m3_state *final, void *ws, size_t ws_bytes, void *stream) {
+    if (shape && (shape->flags & M3_FLAG_HALF_SPLIT)) {
+        if (shape->rank != 1) return M3_EINVAL;
+        return scan_half_split(shape, in, y, init, final, ws, ws_bytes, stream, false);
+    }
     return scan_impl(shape, in, y, init, final, ws, ws_bytes, stream, false);
 }
 
 m3_status m3_scan_mimo(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,
                        m3_state *final, void *ws, size_t ws_bytes, void *stream) {
+    if (shape && (shape->flags & M3_FLAG_HALF_SPLIT))
+        return scan_half_split(shape, in, y, init, final, ws, ws_bytes, stream, true);
     return scan_impl(shape, in, y, init, final, ws, ws_bytes, stream, true);
 }
 

@@ -12,7 +12,7 @@ constexpr int kBlockRows = 64;
 
 // Option bits of ScanParams::flags / StepParams::flags (the values of the public M3_FLAG_*).
 constexpr uint32_t kFlagNorm = 1u << 0, kFlagPartialRope = 1u << 1, kFlagAPerToken = 1u << 2,
-                   kFlagDtSoftplus = 1u << 3, kFlagLamSigmoid = 1u << 4;
+                   kFlagDtSoftplus = 1u << 3, kFlagLamSigmoid = 1u << 4, kFlagHalfSplit = 1u << 5;
 
 struct ScanParams {
     // sizes
@@ -108,6 +108,12 @@ struct BwdParams {
     float *part;   // [BH][nck][pw]   parameter partial sums
 };
 hipError_t launch_bwd(bool bf16, const BwdParams &p, hipStream_t stream);
+
+// N-axis permutation between the half-split pairing (component c of pair i at i + c N/2) and
+// the kernels' adjacent pairing (at 2 i + c), of a tensor viewed as [outer][N][inner] with
+// elements of esize bytes (2 or 4); to_kernel: half-split -> adjacent, else the inverse.
+hipError_t launch_perm_n(const void *in, void *out, int64_t outer, int N, int inner, int esize, bool to_kernel,
+                         hipStream_t stream);
 
 // Tile variant chosen by the host.
 enum TileMode { kTileGen = 0, kTileVec = 1, kTileMimo = 2 };

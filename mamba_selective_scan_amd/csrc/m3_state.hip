@@ -139,28 +139,31 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
         if (lane == 0) s_rs[cb] = bcnorm ? rsqrtf(ss / (float)N + p.eps) : 1.f;
     }
     __syncthreads();
-    // norm, gain, bias, rotation: one thread per (pair, rank)
+    // norm, gain, bias, rotation: one thread per (pair, rank); the pair's components are
+    // adjacent, or one in each half of N (half-split pairing)
+    const bool hsplit = (p.flags & kFlagHalfSplit) != 0;
     for (int e = tid; e < N2 * R; e += 256) {
-        const int i = e / R, r = e - i * R, n = 2 * i;
+        const int i = e / R, r = e - i * R;
+        const int n0 = hsplit ? i : 2 * i, n1 = hsplit ? i + N2 : 2 * i + 1;
         const float rb = s_rs[r], rc = s_rs[R + r];
         float gb0 = 1.f, gb1 = 1.f, gc0 = 1.f, gc1 = 1.f;
-        if (bcnorm && p.bnw) { gb0 = p.bnw[n]; gb1 = p.bnw[n + 1]; }
-        if (bcnorm && p.cnw) { gc0 = p.cnw[n]; gc1 = p.cnw[n + 1]; }
-        float u = s_bt[n * R + r] * rb * gb0, w = s_bt[(n + 1) * R + r] * rb * gb1;
-        float uc = s_ct[n * R + r] * rc * gc0, wc = s_ct[(n + 1) * R + r] * rc * gc1;
+        if (bcnorm && p.bnw) { gb0 = p.bnw[n0]; gb1 = p.bnw[n1]; }
+        if (bcnorm && p.cnw) { gc0 = p.cnw[n0]; gc1 = p.cnw[n1]; }
+        float u = s_bt[n0 * R + r] * rb * gb0, w = s_bt[n1 * R + r] * rb * gb1;
+        float uc = s_ct[n0 * R + r] * rc * gc0, wc = s_ct[n1 * R + r] * rc * gc1;
         if (p.bbias) {
-            u += p.bbias[((int64_t)h * R + r) * N + n];
-            w += p.bbias[((int64_t)h * R + r) * N + n + 1];
+            u += p.bbias[((int64_t)h * R + r) * N + n0];
+            w += p.bbias[((int64_t)h * R + r) * N + n1];
         }
         if (p.cbias) {
-            uc += p.cbias[((int64_t)h * R + r) * N + n];
-            wc += p.cbias[((int64_t)h * R + r) * N + n + 1];
+            uc += p.cbias[((int64_t)h * R + r) * N + n0];
+            wc += p.cbias[((int64_t)h * R + r) * N + n1];
         }
         const float cn = s_cos[i], sn = s_sin[i];
-        s_bt[n * R + r] = u * cn - w * sn;
-        s_bt[(n + 1) * R + r] = u * sn + w * cn;
-        s_ct[n * R + r] = uc * cn - wc * sn;
-        s_ct[(n + 1) * R + r] = uc * sn + wc * cn;
+        s_bt[n0 * R + r] = u * cn - w * sn;
+        s_bt[n1 * R + r] = u * sn + w * cn;
+        s_ct[n0 * R + r] = uc * cn - wc * sn;
+        s_ct[n1 * R + r] = uc * sn + wc * cn;
     }
     __syncthreads();
     for (int e = tid; e < N * R; e += 256) p.pB[bh * N * R + e] = s_bt[e];
@@ -344,7 +347,7 @@ static size_t step_lds_bytes(const StepParams &p, int vec) {
 }
 
 hipError_t launch_step(bool bf16, const StepParams &p, hipStream_t stream) {
-    if (p.R == 1 && p.P % 4 == 0) {
+    if (p.R == 1 && p.P % 4 == 0 && !(p.flags & kFlagHalfSplit)) {  // adjacent pairs across neighbouring lanes
         const int NG = 256 / (p.P / 4);
         const int NA = (p.N + 3) & ~3, PA = (p.P + 3) & ~3, N2A = (p.N / 2 + 3) & ~3;
         const size_t lds = sizeof(float) * (size_t)(3 * NA + 2 * PA + N2A + NG * p.P);

@@ -87,7 +87,8 @@ def _call_scan(m3, lib, s, inp_over=None, y=True, ws_bytes=None, init=None, fin=
     (dict(batch=-1), 1),
     (dict(seqlen=-5), 1),
     (dict(io=7), 1),
-    (dict(flags=0x20), 1),         # unknown flag
+    (dict(flags=0x40), 1),         # unknown flag
+    (dict(flags=0x21, rank=2), 1),  # half-split SISO call with rank 2
     (dict(flags=0x80000001), 1),
     (dict(flags=3, rope_pairs=33), 1),   # more rotated pairs than N/2
     (dict(flags=3, rope_pairs=-1), 1),
@@ -132,6 +133,22 @@ def test_option_pointers():
     s1 = _shape(m3, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_PARTIAL_ROPE, rope_pairs=1)
     assert _call_scan(m3, lib, s1, inp_over={"theta": None}, ws_bytes=100) == 1
     assert _call_scan(m3, lib, s1, init=st, ws_bytes=100) == 1
+
+
+def test_half_split_workspace():
+    """The half-split pairing needs room for the N-permuted copies of B, C (and, for the
+    gradient call, of their gradients) beside the plain call's workspace; a workspace of the
+    plain size is short (checked before any launch)."""
+    m3, lib = _lib()
+    s = _shape(m3)
+    sh = _shape(m3, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_HALF_SPLIT)
+    plain, split = lib.m3_scan_workspace_bytes(ctypes.byref(s)), lib.m3_scan_workspace_bytes(ctypes.byref(sh))
+    bc = 2 * s.batch * s.seqlen * s.nheads * s.dstate * s.rank * 2  # bf16 copies of B and C
+    assert split >= plain + bc
+    assert _call_scan(m3, lib, sh, ws_bytes=plain) == 3
+    bplain = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(s))
+    bsplit = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(sh))
+    assert bsplit >= bplain + 2 * bc
 
 
 def test_mimo_limits():

@@ -45,6 +45,8 @@ def build_case(w, opts, nr=None):
         o_kw["lam_sigmoid"] = g_kw["lam_sigmoid"] = True
     if "gate" in opts:
         o_kw["z"] = g_kw["z"] = ex["z"]
+    if "half" in opts:
+        o_kw["half_split"] = g_kw["half_split"] = True
     data = dict(x=inp["x"], B=inp["B"], C=inp["C"], dt=dt, lam=lam, theta=theta, A=A, D=inp["D"])
     return data, o_kw, g_kw, (theta.shape[-1] if "rope" in opts else N // 2)
 
@@ -145,6 +147,21 @@ def test_all_options_long_segments(io):
     run_scan(w, set(ALL), nr=8)
 
 
+# ---------------------------------------------------------------- half-split pairing
+@pytest.mark.parametrize("T,P,N,R,Q,io,opts", [
+    (300, 64, 64, 1, 64, "bf16", ("half",)),                 # rank-1 16-byte path
+    (130, 128, 128, 1, 64, "f32", ("half", "rope")),          # N 128, partial rotation
+    (77, 5, 6, 1, 16, "f32", ("half",)),                      # odd sizes, element path
+    (97, 64, 64, 2, 32, "bf16", ("half",) + ALL),             # MIMO with every option
+    (40, 32, 16, 3, 16, "f32", ("half", "gate")),             # element-path MIMO
+])
+def test_half_split(T, P, N, R, Q, io, opts):
+    """Rotation pairs (i, i + N/2): the scans run on N-permuted copies; states in and out in
+    the caller's (half-split) layout."""
+    w = custom(batch=2, seqlen=T, nheads=2, headdim=P, dstate=N, rank=R, chunk=Q, io=io, seed=T + 7)
+    run_scan(w, set(opts), nr=N // 4 if "rope" in opts else None)
+
+
 # ---------------------------------------------------------------- decode step and streaming
 @pytest.mark.parametrize("R,P,N,io", [(1, 64, 64, "bf16"), (1, 6, 8, "f32"), (2, 16, 32, "f32")])
 def test_split_schedule_with_options(R, P, N, io):
@@ -180,6 +197,42 @@ def test_split_schedule_with_options(R, P, N, io):
                                          one["A"], one["D"], state, z=zs[:, k:k + 1].contiguous(), **kw, **pk))
         t0 += n
     assert t0 == w.seqlen
+    torch.cuda.synchronize()
+    check("y", torch.cat(pieces, dim=1), y_ref, io)
+    check_state(state, f_ref, io)
+
+
+@pytest.mark.parametrize("R,P,N,io", [(1, 64, 64, "bf16"), (2, 16, 32, "f32")])
+def test_split_schedule_half_split(R, P, N, io):
+    """scan -> steps -> scan with the half-split pairing (the step pairs natively, the scans
+    through the permuted copies) == one-shot oracle."""
+    import torch
+    m3 = _m3()
+    w = custom(batch=2, seqlen=90, nheads=2, headdim=P, dstate=N, rank=R, chunk=32, io=io, seed=R + 11)
+    log(f"case split schedule half split {w}")
+    data, o_kw, g_kw, NR = build_case(w, {"half"})
+    params = make_norm_params(w)
+    st0 = make_state(w, scale=0.3)
+    y_ref, f_ref = oracle.scan(data["x"], data["B"], data["C"], data["dt"], data["lam"], data["theta"],
+                               data["A"], data["D"], init=st0, **params, **o_kw)
+    d, kw = to_gpu(data, g_kw, io)
+    pk = {k: torch.from_numpy(v).cuda() for k, v in params.items()}
+    state = state_to_dev(st0)
+    scan = m3.m3_scan_mimo if R > 1 else m3.m3_scan_siso
+    per_tok = ("x", "B", "C", "dt", "lam", "theta")  # A is per head here
+    pieces, t0 = [], 0
+    for kind, n in (("scan", 41), ("step", 2), ("scan", 47)):
+        sl = {k: (v[:, t0:t0 + n].contiguous() if k in per_tok else v) for k, v in d.items()}
+        if kind == "scan":
+            y, _ = scan(sl["x"], sl["B"], sl["C"], sl["dt"], sl["lam"], sl["theta"], sl["A"], sl["D"],
+                        chunk=32, init=state, final=state, **kw, **pk)
+            pieces.append(y)
+        else:
+            for k in range(n):
+                one = {kk: (vv[:, k:k + 1].contiguous() if kk in per_tok else vv) for kk, vv in sl.items()}
+                pieces.append(m3.m3_step(one["x"], one["B"], one["C"], one["dt"], one["lam"], one["theta"],
+                                         one["A"], one["D"], state, **kw, **pk))
+        t0 += n
     torch.cuda.synchronize()
     check("y", torch.cat(pieces, dim=1), y_ref, io)
     check_state(state, f_ref, io)

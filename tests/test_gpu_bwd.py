@@ -63,6 +63,8 @@ def run_case(w, *, opts=(), nr=None, init=True, dfinal=True, npar=True, bcnorm=T
         kw.update(dt_softplus=True, dt_bias=ex["dt_bias"], lam_sigmoid=True)
     if "gate" in opts:
         kw["z"] = ex["z"]
+    if "half" in opts:
+        kw["half_split"] = True
     params = make_norm_params(w) if npar else {}
     st0 = make_state(w, scale=0.4, rope_pairs=NR) if init else None
     rng = np.random.default_rng(w.seed + 5)
@@ -135,6 +137,13 @@ def test_bwd_shapes(T, P, N, R, io):
 def test_bwd_all_options(R):
     w = custom(batch=2, seqlen=90, nheads=2, headdim=32, dstate=32, rank=R, io="f32", seed=17 + R)
     run_case(w, opts=("rope", "atok", "act", "gate"), nr=8)
+
+
+@pytest.mark.parametrize("R,io,opts", [(1, "bf16", ("half",)), (2, "f32", ("half", "rope", "atok", "act", "gate"))])
+def test_bwd_half_split(R, io, opts):
+    """Gradients with the half-split pairing (N-permuted copies in the workspace)."""
+    w = custom(batch=2, seqlen=90, nheads=2, headdim=32, dstate=32, rank=R, io=io, seed=29 + R)
+    run_case(w, opts=opts, nr=8 if "rope" in opts else None)
 
 
 def test_bwd_norm_off_no_state():
