@@ -634,7 +634,7 @@ __device__ __forceinline__ float block_sum(float v, float *scratch) {
 }  // namespace
 
 // ---------------------------------------------------------------- per-chunk state sums
-template <class Io, int NPAD, int PPAD>
+template <class Io, int NPAD, int PPAD, bool VEC>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_state_kernel(BwdParams p) {
     using L = CL<NPAD, PPAD>;
     constexpr int NT = NPAD / 16, PT = PPAD / 16;
@@ -648,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_state_kernel(BwdParams p) 
     const int Qt = kRows / p.R;
     const int64_t t0 = (int64_t)c * Qt;
     const int Tv = (int)min((int64_t)Qt, p.T - t0);
-    if (p.vec) chunk_prologue_vec<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
+    if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
     else chunk_prologue<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
     const int64_t cidx = bh * nck + c;
     for (int q = wv; q < 2 * NT * PT; q += kWaves) {
@@ -840,6 +840,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         }
     };
     load_slab(Gend, 0);
+    // (a run-time choice here: with both staging variants in one kernel the register
+    // allocation of the matrix phases comes out better than with either alone)
     const float dDp = p.vec ? chunk_prologue_vec<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv)
                             : chunk_prologue<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv);
     float *sB = sm + L::SB, *sC = sm + L::SC, *sX = sm + L::SX, *sY = sm + L::SY, *sS = sm + L::SS;
@@ -1673,22 +1675,27 @@ namespace {
 template <int NPAD, int PPAD>
 constexpr size_t chunk_lds() { return sizeof(float) * CL<NPAD, PPAD>::TOTAL; }
 
-template <class Io, int NPAD, int PPAD>
-hipError_t launch_chunks(const BwdParams &p, hipStream_t st) {
+template <class Io, int NPAD, int PPAD, bool VEC>
+hipError_t launch_chunks_v(const BwdParams &p, hipStream_t st) {
     const size_t lds = chunk_lds<NPAD, PPAD>();
     const dim3 grid((unsigned)(p.B * p.H * p.nck)), blk(kThreads);
     hipError_t e;
-    if ((e = hipFuncSetAttribute((const void *)bwd_chunk_state_kernel<Io, NPAD, PPAD>,
+    if ((e = hipFuncSetAttribute((const void *)bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC>,
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
         return e;
     if ((e = hipFuncSetAttribute((const void *)bwd_chunk_grad_kernel<Io, NPAD, PPAD>,
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
         return e;
-    hipLaunchKernelGGL((bwd_chunk_state_kernel<Io, NPAD, PPAD>), grid, blk, lds, st, p);
+    hipLaunchKernelGGL((bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC>), grid, blk, lds, st, p);
     const int64_t ne = p.B * p.H * (p.N / 2) * (int64_t)p.P;
     hipLaunchKernelGGL(bwd_state_pass_kernel, dim3((unsigned)((ne + 255) / 256), 2), dim3(256), 0, st, p);
     hipLaunchKernelGGL((bwd_chunk_grad_kernel<Io, NPAD, PPAD>), grid, blk, lds, st, p);
     return hipGetLastError();
+}
+
+template <class Io, int NPAD, int PPAD>
+hipError_t launch_chunks(const BwdParams &p, hipStream_t st) {
+    return p.vec ? launch_chunks_v<Io, NPAD, PPAD, true>(p, st) : launch_chunks_v<Io, NPAD, PPAD, false>(p, st);
 }
 
 template <class Io, int NPAD>

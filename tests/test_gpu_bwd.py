@@ -128,6 +128,12 @@ def test_bwd_tiny_f32():
     (50, 16, 32, 2, "f32"),      # MIMO R 2
     (41, 8, 16, 3, "f32"),       # MIMO R 3 (5 tokens per block)
     (30, 64, 64, 4, "bf16"),     # MIMO R 4
+    (1, 16, 16, 1, "f32"),       # a single token (the last token is the first)
+    (64, 32, 32, 1, "bf16"),     # exactly one chunk
+    (129, 32, 64, 1, "f32"),     # one token past two chunks
+    (33, 16, 16, 8, "f32"),      # MIMO R 8 (8 tokens per chunk)
+    (70, 128, 32, 1, "bf16"),    # P 128 with N 32
+    (45, 24, 40, 5, "f32"),      # MIMO R 5, N and P not multiples of 16
 ])
 def test_bwd_shapes(T, P, N, R, io):
     run_case(custom(batch=2, seqlen=T, nheads=2, headdim=P, dstate=N, rank=R, io=io, seed=T + N + R))
