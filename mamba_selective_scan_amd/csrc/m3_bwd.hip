@@ -136,17 +136,23 @@ __device__ __forceinline__ float eta_at(const BwdParams &p, int64_t b, int h, in
     return dt * (1.f - lam);
 }
 
-// LDS layout of the chunk kernels (floats)
-template <int NPAD, int PPAD>
+// LDS layout of the chunk kernels (floats).  GRAD: the gradient kernel's layout, which keeps
+// the chunk's running angles (PH) and the rows' norm factors (RS) for the norm backward when
+// they fit beside the rest; otherwise the angles share the slab area and are computed again.
+template <int NPAD, int PPAD, bool GRAD = false>
 struct CL {
     static constexpr int BP = NPAD + 1, XP = PPAD + 1, N2P = NPAD / 2;
-    static constexpr int SLAB = 32 * XP > kRows * N2P ? 32 * XP : kRows * N2P;
     static constexpr int SB = 0;                    // [64][BP] B~ rows (then dB~)
     static constexpr int SC = SB + kRows * BP;      // [64][BP] C~ rows (then dC~)
     static constexpr int SX = SC + kRows * BP;      // [64][XP] x rows
     static constexpr int SY = SX + kRows * XP;      // [64][XP] gated dy rows
-    static constexpr int SS = SY + kRows * XP;      // state slab [32][XP] / angles [64][N2P]
-    static constexpr int TK = SS + SLAB;            // per token: cs, kappa, gamma
+    static constexpr int SS = SY + kRows * XP;      // state slab [32][XP]
+    static constexpr int REST = 3 * 64 + 6 * 64 + 8 * 64 + 64 + 128 + 128 + 32;
+    static constexpr bool KEEP = GRAD && (SS + 32 * XP + kRows * N2P + 128 + REST) * 4 <= 160 * 1024;
+    static constexpr int SLAB = KEEP ? 32 * XP : (32 * XP > kRows * N2P ? 32 * XP : kRows * N2P);
+    static constexpr int PH = KEEP ? SS + SLAB : SS;  // [64][N2P] running angles of the chunk
+    static constexpr int RS = PH + kRows * N2P;     // [2][64] norm factors of the B and C rows (KEEP)
+    static constexpr int TK = KEEP ? RS + 128 : SS + SLAB;  // per token: cs, kappa, gamma
     static constexpr int RT = TK + 3 * 64;          // per row: cs, kappa, gamma, token, e^(cs_end-cs), e^cs
     static constexpr int RW = RT + 6 * 64;          // [4][64] strict row sums (with RD: [8][64] scan scratch)
     static constexpr int RD = RW + 4 * 64;          // [4][64] same-token row sums
@@ -157,6 +163,8 @@ struct CL {
     static constexpr int TOTAL = MS + 32;
     static_assert(32 * NPAD <= 2 * kRows * XP, "bias and gain sums must fit over the x and dy rows");
     static_assert(kRows * N2P <= 2 * kRows * XP, "angle terms must fit over the x and dy rows");
+    static_assert(kWaves * 64 <= SLAB, "angle-sum scratch must fit in the slab area");
+    static_assert(TOTAL * 4 <= 160 * 1024, "LDS");
 };
 
 // Running angle sums of a chunk: phi[k][i] = theta summed over tokens 0..k of the chunk
@@ -237,7 +245,7 @@ __device__ __forceinline__ float vec_elem(const u32x4_t &v, int j) {
 template <class Io, int NPAD, int PPAD, bool SCALED>
 __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, int h, int64_t t0, int Tv) {
     using ET = typename Io::T;
-    using L = CL<NPAD, PPAD>;
+    using L = CL<NPAD, PPAD, !SCALED>;
     constexpr int E = 16 / Io::bytes;
     constexpr int QX = (kRows * PPAD / E + kThreads - 1) / kThreads;
     constexpr int QB = (kRows * NPAD / E + kThreads - 1) / kThreads;
@@ -246,7 +254,7 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
     const int N = p.N, P = p.P, R = p.R, N2 = N / 2, NR = p.nr;
     const int Qt = kRows / R, rows = Tv * R;
     const int64_t T = p.T, H = p.H;
-    float *tk = sm + L::TK, *rt = sm + L::RT, *phi = sm + L::SS;
+    float *tk = sm + L::TK, *rt = sm + L::RT, *phi = sm + L::PH;
     // ---- loads
     const int k0 = tid;  // token of the chunk (wave 0)
     const bool okt = tid < 64 && k0 < Tv, okn = okt && t0 + k0 + 1 < T;
@@ -406,6 +414,10 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         if (norm) {
             sb = rsqrtf(wave_sum(b0 * b0 + b1 * b1) * invN + p.eps);
             sc = rsqrtf(wave_sum(c0 * c0 + c1 * c1) * invN + p.eps);
+            if (L::KEEP && lane == 0) {
+                sm[L::RS + rho] = sb;
+                sm[L::RS + 64 + rho] = sc;
+            }
         }
         float bi0 = bw0, bi1 = bw1, ci0 = cw0, ci1 = cw1;
         if (!rdiv) {
@@ -450,7 +462,7 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
 template <class Io, int NPAD, int PPAD, bool SCALED>
 __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h, int64_t t0, int Tv) {
     using ET = typename Io::T;
-    using L = CL<NPAD, PPAD>;
+    using L = CL<NPAD, PPAD, !SCALED>;
     constexpr int QX = kRows * PPAD / kThreads;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int N = p.N, P = p.P, R = p.R, N2 = N / 2;
@@ -564,7 +576,7 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         sm[L::SX + Qt * R * L::XP + e] = 0.f;
         sm[L::SY + Qt * R * L::XP + e] = 0.f;
     }
-    angle_scan<L::N2P>(ang, sm + L::SS, sm + L::RW);  // (its barriers publish tk)
+    angle_scan<L::N2P>(ang, sm + L::PH, sm + L::RW);  // (its barriers publish tk)
     const float cs_end = tk[Tv - 1];
     // per-row tables
     if (tid < kRows) {
@@ -583,7 +595,7 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
     // rows compute on zeros and are masked at the store) so that the rows' reductions overlap.
     const bool norm = (p.flags & kFlagNorm) != 0;
     const float invN = 1.f / (float)N;
-    const float *phi = sm + L::SS;
+    const float *phi = sm + L::PH;
     const int lp = lane < L::N2P ? lane : 0;  // clamped pair for the LDS reads
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -594,6 +606,10 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         if (norm) {
             sb = rsqrtf(wave_sum(rb[m][0] * rb[m][0] + rb[m][1] * rb[m][1]) * invN + p.eps);
             sc = rsqrtf(wave_sum(rc[m][0] * rc[m][0] + rc[m][1] * rc[m][1]) * invN + p.eps);
+            if (L::KEEP && lane == 0) {
+                sm[L::RS + rho] = sb;
+                sm[L::RS + 64 + rho] = sc;
+            }
         }
         float b0 = (norm ? rb[m][0] * sb * gb0 : rb[m][0]) + bb[m][0];
         float b1 = (norm ? rb[m][1] * sb * gb1 : rb[m][1]) + bb[m][1];
@@ -674,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_state_kernel(BwdParams p) 
             if (n < N && pc < P) dst[(int64_t)n * P + pc] = acc[i];
         }
     }
-    if (tid < N2) p.phic[cidx * N2 + tid] = sm[L::SS + (Tv - 1) * L::N2P + tid];
+    if (tid < N2) p.phic[cidx * N2 + tid] = sm[L::PH + (Tv - 1) * L::N2P + tid];
     if (tid == 0) p.lsum[cidx] = sm[L::TK + Tv - 1];
 }
 
@@ -804,7 +820,7 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
 template <class Io, int NPAD, int PPAD>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     using ET = typename Io::T;
-    using L = CL<NPAD, PPAD>;
+    using L = CL<NPAD, PPAD, true>;
     constexpr int NT = NPAD / 16, PT = PPAD / 16, NH = NT / 2, PH = PT / 2, NS = NPAD / 32;
     constexpr int BP = L::BP, XP = L::XP, N2P = L::N2P;
     constexpr int SQ = 32 * PPAD / kThreads;  // slab elements per thread
@@ -1294,9 +1310,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
             rr[m][1][0] = ld_raw((const ET *)p.Cm, o, ro[m]);
             rr[m][1][1] = ld_raw((const ET *)p.Cm, o + R, ro[m]);
         }
-        AngleTile<N2P> ang;
-        angle_load<N2P>(p, ang, b, h, t0, Tv);
-        angle_scan<N2P>(ang, sm + L::SS, sm + L::RW);
+        if constexpr (!L::KEEP) {
+            AngleTile<N2P> ang;
+            angle_load<N2P>(p, ang, b, h, t0, Tv);
+            angle_scan<N2P>(ang, sm + L::PH, sm + L::RW);
+        }
         // bias sums: per (side, rank, pair), over the chunk's tokens, of the un-rotated dB~ / dC~
         // (over the x and dy rows: [8][2][NPAD] per-wave gain sums, then either [8][2][NPAD]
         // per-wave bias sums or [2][R][NPAD] column bias sums; at most 32 NPAD floats).  When R divides 8 every row of a wave has rank
@@ -1311,7 +1329,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
             float a0 = 0.f, a1 = 0.f;
             for (int k = 0; k < Tv; ++k) {
                 float sn, cn;
-                fast_sincos(sm[L::SS + k * N2P + i], sn, cn);
+                fast_sincos(sm[L::PH + k * N2P + i], sn, cn);
                 const float e0 = rows[(k * R + r) * BP + 2 * i], e1 = rows[(k * R + r) * BP + 2 * i + 1];
                 a0 += cn * e0 + sn * e1;
                 a1 += -sn * e0 + cn * e1;
@@ -1324,7 +1342,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         float ga[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this wave's gain sums (lane = pair)
         float ba[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this wave's bias sums (rank wv % R)
         const float invN = 1.f / (float)N;
-        const float *phi = sm + L::SS;
+        const float *phi = sm + L::PH;
         float gn[2][2];
         {
             const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
@@ -1355,7 +1373,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
                 const float d0 = lv ? cn * e0 + sn * e1 : 0.f, d1 = lv ? -sn * e0 + cn * e1 : 0.f;
                 float o0 = d0, o1 = d1;
                 if (norm) {
-                    const float rs = rsqrtf(wave_sum(v0 * v0 + v1 * v1) * invN + p.eps);
+                    const float rs = L::KEEP ? sm[L::RS + 64 * side + rho]
+                                             : rsqrtf(wave_sum(v0 * v0 + v1 * v1) * invN + p.eps);
                     const float dot = wave_sum(d0 * g0 * v0 + d1 * g1 * v1);
                     const float f = dot * rs * rs * rs * invN;
                     o0 = d0 * g0 * rs - f * v0;
@@ -1389,9 +1408,29 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         ET *out = (ET *)(side == 0 ? p.dB : p.dC);
         if (!out) continue;
         const float *rows = side == 0 ? sB : sC;
-        for (int e = tid; e < Tv * N * R; e += kThreads) {
-            const int k = e / (N * R), rem = e - k * N * R, n = rem / R, r = rem - n * R;
-            Io::st(out + (bth0 + (int64_t)k * H) * N * R + rem, rows[(k * R + r) * BP + n]);
+        constexpr int E = 16 / Io::bytes;
+        if (R == 1 && N % E == 0) {
+            // single-rank rows: 16-byte stores of E consecutive elements (N a multiple of E
+            // keeps every row start 16-byte aligned)
+            const int ne = N / E;
+            for (int e = tid; e < Tv * ne; e += kThreads) {
+                const int k = e / ne, n = E * (e - k * ne);
+                const float *src = rows + k * BP + n;
+                u32x4_t v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (Io::bytes == 2)
+                        v[j] = (uint32_t)f2bf(src[2 * j]) | ((uint32_t)f2bf(src[2 * j + 1]) << 16);
+                    else
+                        v[j] = __float_as_uint(src[j]);
+                }
+                *reinterpret_cast<u32x4_t *>(out + (bth0 + (int64_t)k * H) * N + n) = v;
+            }
+        } else {
+            for (int e = tid; e < Tv * N * R; e += kThreads) {
+                const int k = e / (N * R), rem = e - k * N * R, n = rem / R, r = rem - n * R;
+                Io::st(out + (bth0 + (int64_t)k * H) * N * R + rem, rows[(k * R + r) * BP + n]);
+            }
         }
     }
     const float *acc = sm + L::SX;
@@ -1672,24 +1711,24 @@ __global__ __launch_bounds__(256) void bwd_empty_kernel(BwdParams p) {
 
 namespace {
 
-template <int NPAD, int PPAD>
-constexpr size_t chunk_lds() { return sizeof(float) * CL<NPAD, PPAD>::TOTAL; }
+template <int NPAD, int PPAD, bool GRAD>
+constexpr size_t chunk_lds() { return sizeof(float) * CL<NPAD, PPAD, GRAD>::TOTAL; }
 
 template <class Io, int NPAD, int PPAD, bool VEC>
 hipError_t launch_chunks_v(const BwdParams &p, hipStream_t st) {
-    const size_t lds = chunk_lds<NPAD, PPAD>();
+    const size_t lds = chunk_lds<NPAD, PPAD, false>(), ldg = chunk_lds<NPAD, PPAD, true>();
     const dim3 grid((unsigned)(p.B * p.H * p.nck)), blk(kThreads);
     hipError_t e;
     if ((e = hipFuncSetAttribute((const void *)bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC>,
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
         return e;
     if ((e = hipFuncSetAttribute((const void *)bwd_chunk_grad_kernel<Io, NPAD, PPAD>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldg)) != hipSuccess)
         return e;
     hipLaunchKernelGGL((bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC>), grid, blk, lds, st, p);
     const int64_t ne = p.B * p.H * (p.N / 2) * (int64_t)p.P;
     hipLaunchKernelGGL(bwd_state_pass_kernel, dim3((unsigned)((ne + 255) / 256), 2), dim3(256), 0, st, p);
-    hipLaunchKernelGGL((bwd_chunk_grad_kernel<Io, NPAD, PPAD>), grid, blk, lds, st, p);
+    hipLaunchKernelGGL((bwd_chunk_grad_kernel<Io, NPAD, PPAD>), grid, blk, ldg, st, p);
     return hipGetLastError();
 }
 
