@@ -78,6 +78,28 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// sum over each half of the wave (lanes 0..31, 32..63), returned to every lane of that half:
+// row sums, then rows 0+1 and 2+3 (row_bcast:15 into rows 1 and 3); lanes 31 and 63 hold them
+__device__ __forceinline__ float half_sum(float v) {
+    v = row_sum16(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    return (threadIdx.x & 32) ? hi : lo;
+}
+// Row passes over the B and C rows: with at most 32 pairs a wave takes two rows per
+// instruction (lanes 0..31 and 32..63, lane = pair), otherwise one (lane = pair).
+template <int N2P>
+struct RowPass {
+    static constexpr bool HV = N2P <= 32;
+    static constexpr int NM = HV ? 4 : 8;  // rows per wave: wv + 8 (NM-step index)
+    __device__ static int half() { return HV ? (int)((threadIdx.x >> 5) & 1) : 0; }
+    __device__ static int pair() { return HV ? (int)(threadIdx.x & 31) : (int)(threadIdx.x & 63); }
+    __device__ static int row(int wv, int m) { return wv + 8 * (HV ? 2 * m + half() : m); }
+    __device__ static float sum(float v) { return HV ? half_sum(v) : wave_sum(v); }
+    // the other half's value of v (0 when a row of the wave takes every lane)
+    __device__ static float other(float v) { return HV ? __shfl_xor(v, 32, 64) : 0.f; }
+};
 // inclusive prefix sum over the 64 lanes of a wave (all lanes active)
 __device__ __forceinline__ float wave_scan_incl(float v) {
     const int lane = threadIdx.x & 63;
@@ -289,13 +311,15 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         tv[q] = ld_vec(p.theta ? p.theta : p.dt, ((b * T + t0 + k) * H + h) * (int64_t)NR + 4 * v, ok);
     }
     // gains and (rank wv % R when R divides 8) biases of this lane's pair
+    using RP = RowPass<L::N2P>;
+    const int pl = RP::pair();
     const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
-    const bool okg = lane < N2;
-    float gb0 = ld_raw(bnp, 2 * lane, okg && p.bnw), gb1 = ld_raw(bnp, 2 * lane + 1, okg && p.bnw);
-    float gc0 = ld_raw(cnp, 2 * lane, okg && p.cnw), gc1 = ld_raw(cnp, 2 * lane + 1, okg && p.cnw);
+    const bool okg = pl < N2;
+    float gb0 = ld_raw(bnp, 2 * pl, okg && p.bnw), gb1 = ld_raw(bnp, 2 * pl + 1, okg && p.bnw);
+    float gc0 = ld_raw(cnp, 2 * pl, okg && p.cnw), gc1 = ld_raw(cnp, 2 * pl + 1, okg && p.cnw);
     const bool rdiv = (8 % R) == 0;
     const float *bbp = p.bbias ? p.bbias : p.dt, *cbp = p.cbias ? p.cbias : p.dt;
-    const int64_t obw = ((int64_t)h * R + (wv % R)) * N + 2 * lane;
+    const int64_t obw = ((int64_t)h * R + (wv % R)) * N + 2 * pl;
     float bw0 = ld_raw(bbp, obw, okg && rdiv && p.bbias), bw1 = ld_raw(bbp, obw + 1, okg && rdiv && p.bbias);
     float cw0 = ld_raw(cbp, obw, okg && rdiv && p.cbias), cw1 = ld_raw(cbp, obw + 1, okg && rdiv && p.cbias);
     // ---- zero padding of the tiles (disjoint from the loaded elements)
@@ -399,11 +423,11 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
     gb1 = okg && p.bnw ? gb1 : 1.f;
     gc0 = okg && p.cnw ? gc0 : 1.f;
     gc1 = okg && p.cnw ? gc1 : 1.f;
-    const int lp = lane < L::N2P ? lane : 0;
+    const int lp = pl < L::N2P ? pl : 0;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
-        const bool valid = k < Qt && k < Tv && lane < N2;
+    for (int m = 0; m < RP::NM; ++m) {
+        const int rho = RP::row(wv, m), k = rho / R, r = rho - k * R;
+        const bool valid = k < Qt && k < Tv && pl < N2;
         float b0 = sm[L::SB + rho * L::BP + 2 * lp], b1 = sm[L::SB + rho * L::BP + 2 * lp + 1];
         float c0 = sm[L::SC + rho * L::BP + 2 * lp], c1 = sm[L::SC + rho * L::BP + 2 * lp + 1];
         b0 = valid ? b0 : 0.f;
@@ -412,16 +436,16 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         c1 = valid ? c1 : 0.f;
         float sb = 1.f, sc = 1.f;
         if (norm) {
-            sb = rsqrtf(wave_sum(b0 * b0 + b1 * b1) * invN + p.eps);
-            sc = rsqrtf(wave_sum(c0 * c0 + c1 * c1) * invN + p.eps);
-            if (L::KEEP && lane == 0) {
+            sb = rsqrtf(RP::sum(b0 * b0 + b1 * b1) * invN + p.eps);
+            sc = rsqrtf(RP::sum(c0 * c0 + c1 * c1) * invN + p.eps);
+            if (L::KEEP && pl == 0) {
                 sm[L::RS + rho] = sb;
                 sm[L::RS + 64 + rho] = sc;
             }
         }
         float bi0 = bw0, bi1 = bw1, ci0 = cw0, ci1 = cw1;
         if (!rdiv) {
-            const int64_t ob = ((int64_t)h * R + r) * N + 2 * lane;
+            const int64_t ob = ((int64_t)h * R + r) * N + 2 * pl;
             bi0 = ld_raw(bbp, ob, valid && p.bbias);
             bi1 = ld_raw(bbp, ob + 1, valid && p.bbias);
             ci0 = ld_raw(cbp, ob, valid && p.cbias);
@@ -444,11 +468,11 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         }
         const float u0 = fb * (cn * b0 - sn * b1), u1 = fb * (sn * b0 + cn * b1);
         const float v0 = fc * (cn * c0 - sn * c1), v1 = fc * (sn * c0 + cn * c1);
-        if (lane < L::N2P) {
-            sm[L::SB + rho * L::BP + 2 * lane] = valid ? u0 : 0.f;
-            sm[L::SB + rho * L::BP + 2 * lane + 1] = valid ? u1 : 0.f;
-            sm[L::SC + rho * L::BP + 2 * lane] = valid ? v0 : 0.f;
-            sm[L::SC + rho * L::BP + 2 * lane + 1] = valid ? v1 : 0.f;
+        if (pl < L::N2P) {
+            sm[L::SB + rho * L::BP + 2 * pl] = valid ? u0 : 0.f;
+            sm[L::SB + rho * L::BP + 2 * pl + 1] = valid ? u1 : 0.f;
+            sm[L::SC + rho * L::BP + 2 * pl] = valid ? v0 : 0.f;
+            sm[L::SC + rho * L::BP + 2 * pl + 1] = valid ? v1 : 0.f;
         }
     }
     __syncthreads();
@@ -492,29 +516,32 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         yr[q] = ld_raw((const ET *)p.dy, o, xo[q]);
         zr[q] = ld_raw(zp, o, xo[q]);
     }
-    ET rbr[8][2], rcr[8][2];
-    float bb[8][2], cb[8][2];
-    bool ro[8];
+    using RP = RowPass<L::N2P>;
+    constexpr int NM = RP::NM;
+    const int pl = RP::pair();
+    ET rbr[NM][2], rcr[NM][2];
+    float bb[NM][2], cb[NM][2];
+    bool ro[NM];
     const float *bbp = p.bbias ? p.bbias : p.dt, *cbp = p.cbias ? p.cbias : p.dt;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
-        ro[m] = k < Qt && k < Tv && lane < N2;
-        const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)N * R + (int64_t)(2 * lane) * R + r;
+    for (int m = 0; m < NM; ++m) {
+        const int rho = RP::row(wv, m), k = rho / R, r = rho - k * R;
+        ro[m] = k < Qt && k < Tv && pl < N2;
+        const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)N * R + (int64_t)(2 * pl) * R + r;
         rbr[m][0] = ld_raw((const ET *)p.Bm, o, ro[m]);
         rbr[m][1] = ld_raw((const ET *)p.Bm, o + R, ro[m]);
         rcr[m][0] = ld_raw((const ET *)p.Cm, o, ro[m]);
         rcr[m][1] = ld_raw((const ET *)p.Cm, o + R, ro[m]);
-        const int64_t ob = ((int64_t)h * R + r) * N + 2 * lane;
+        const int64_t ob = ((int64_t)h * R + r) * N + 2 * pl;
         bb[m][0] = ld_raw(bbp, ob, ro[m] && p.bbias);
         bb[m][1] = ld_raw(bbp, ob + 1, ro[m] && p.bbias);
         cb[m][0] = ld_raw(cbp, ob, ro[m] && p.cbias);
         cb[m][1] = ld_raw(cbp, ob + 1, ro[m] && p.cbias);
     }
     const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
-    const bool okg = lane < N2;
-    float gb0 = ld_raw(bnp, 2 * lane, okg && p.bnw), gb1 = ld_raw(bnp, 2 * lane + 1, okg && p.bnw);
-    float gc0 = ld_raw(cnp, 2 * lane, okg && p.cnw), gc1 = ld_raw(cnp, 2 * lane + 1, okg && p.cnw);
+    const bool okg = pl < N2;
+    float gb0 = ld_raw(bnp, 2 * pl, okg && p.bnw), gb1 = ld_raw(bnp, 2 * pl + 1, okg && p.bnw);
+    float gc0 = ld_raw(cnp, 2 * pl, okg && p.cnw), gc1 = ld_raw(cnp, 2 * pl + 1, okg && p.cnw);
     // ---- values (after every load is in flight)
     dtr = okt ? dtr : 0.f;
     lmr = okt ? lmr : 0.f;
@@ -525,9 +552,9 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
     gb1 = okg && p.bnw ? gb1 : 1.f;
     gc0 = okg && p.cnw ? gc0 : 1.f;
     gc1 = okg && p.cnw ? gc1 : 1.f;
-    float rb[8][2], rc[8][2];
+    float rb[NM][2], rc[NM][2];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < NM; ++m) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             rb[m][j] = raw_f<Io>(rbr[m][j], ro[m]);
@@ -596,17 +623,17 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
     const bool norm = (p.flags & kFlagNorm) != 0;
     const float invN = 1.f / (float)N;
     const float *phi = sm + L::PH;
-    const int lp = lane < L::N2P ? lane : 0;  // clamped pair for the LDS reads
+    const int lp = pl < L::N2P ? pl : 0;  // clamped pair for the LDS reads
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int rho = wv + 8 * m, k = rho / R;
+    for (int m = 0; m < NM; ++m) {
+        const int rho = RP::row(wv, m), k = rho / R;
         const bool valid = ro[m];
         const int kc = k < kRows ? k : 0;
         float sb = 1.f, sc = 1.f;
         if (norm) {
-            sb = rsqrtf(wave_sum(rb[m][0] * rb[m][0] + rb[m][1] * rb[m][1]) * invN + p.eps);
-            sc = rsqrtf(wave_sum(rc[m][0] * rc[m][0] + rc[m][1] * rc[m][1]) * invN + p.eps);
-            if (L::KEEP && lane == 0) {
+            sb = rsqrtf(RP::sum(rb[m][0] * rb[m][0] + rb[m][1] * rb[m][1]) * invN + p.eps);
+            sc = rsqrtf(RP::sum(rc[m][0] * rc[m][0] + rc[m][1] * rc[m][1]) * invN + p.eps);
+            if (L::KEEP && pl == 0) {
                 sm[L::RS + rho] = sb;
                 sm[L::RS + 64 + rho] = sc;
             }
@@ -624,11 +651,11 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         }
         const float u0 = fb * (cn * b0 - sn * b1), u1 = fb * (sn * b0 + cn * b1);
         const float v0 = fc * (cn * c0 - sn * c1), v1 = fc * (sn * c0 + cn * c1);
-        if (lane < L::N2P) {
-            sm[L::SB + rho * L::BP + 2 * lane] = valid ? u0 : 0.f;
-            sm[L::SB + rho * L::BP + 2 * lane + 1] = valid ? u1 : 0.f;
-            sm[L::SC + rho * L::BP + 2 * lane] = valid ? v0 : 0.f;
-            sm[L::SC + rho * L::BP + 2 * lane + 1] = valid ? v1 : 0.f;
+        if (pl < L::N2P) {
+            sm[L::SB + rho * L::BP + 2 * pl] = valid ? u0 : 0.f;
+            sm[L::SB + rho * L::BP + 2 * pl + 1] = valid ? u1 : 0.f;
+            sm[L::SC + rho * L::BP + 2 * pl] = valid ? v0 : 0.f;
+            sm[L::SC + rho * L::BP + 2 * pl + 1] = valid ? v1 : 0.f;
         }
     }
     __syncthreads();
@@ -1297,14 +1324,17 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     }
     // ------------------------------------------------ un-rotation and norm backward of each B and C row
     {
-        // raw B and C rows of this wave (rows wv + 8 m) and the angles, loaded together
-        ET rr[8][2][2];
-        bool ro[8];
+        // raw B and C rows of this wave, loaded together
+        using RP = RowPass<N2P>;
+        constexpr int NM = RP::NM;
+        const int pl = RP::pair();
+        ET rr[NM][2][2];
+        bool ro[NM];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int rho = wv + 8 * m, k = rho / R, r = rho - k * R;
-            ro[m] = k < Qt && k < Tv && lane < N2;
-            const int64_t o = (bth0 + (int64_t)k * H) * N * R + (int64_t)(2 * lane) * R + r;
+        for (int m = 0; m < NM; ++m) {
+            const int rho = RP::row(wv, m), k = rho / R, r = rho - k * R;
+            ro[m] = k < Qt && k < Tv && pl < N2;
+            const int64_t o = (bth0 + (int64_t)k * H) * N * R + (int64_t)(2 * pl) * R + r;
             rr[m][0][0] = ld_raw((const ET *)p.Bm, o, ro[m]);
             rr[m][0][1] = ld_raw((const ET *)p.Bm, o + R, ro[m]);
             rr[m][1][0] = ld_raw((const ET *)p.Cm, o, ro[m]);
@@ -1339,31 +1369,32 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         }
         __syncthreads();
         const bool norm = (p.flags & kFlagNorm) != 0;
-        float ga[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this wave's gain sums (lane = pair)
-        float ba[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this wave's bias sums (rank wv % R)
+        float ga[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this lane's gain sums (pair pl)
+        float ba[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this lane's bias sums (rank wv % R)
         const float invN = 1.f / (float)N;
         const float *phi = sm + L::PH;
         float gn[2][2];
         {
             const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
-            const bool okb = lane < N2 && p.bnw, okc = lane < N2 && p.cnw;
-            gn[0][0] = ld_raw(bnp, 2 * lane, okb);
-            gn[0][1] = ld_raw(bnp, 2 * lane + 1, okb);
-            gn[1][0] = ld_raw(cnp, 2 * lane, okc);
-            gn[1][1] = ld_raw(cnp, 2 * lane + 1, okc);
+            const bool okb = pl < N2 && p.bnw, okc = pl < N2 && p.cnw;
+            gn[0][0] = ld_raw(bnp, 2 * pl, okb);
+            gn[0][1] = ld_raw(bnp, 2 * pl + 1, okb);
+            gn[1][0] = ld_raw(cnp, 2 * pl, okc);
+            gn[1][1] = ld_raw(cnp, 2 * pl + 1, okc);
             gn[0][0] = okb ? gn[0][0] : 1.f;
             gn[0][1] = okb ? gn[0][1] : 1.f;
             gn[1][0] = okc ? gn[1][0] : 1.f;
             gn[1][1] = okc ? gn[1][1] : 1.f;
         }
-        const int lp = lane < N2P ? lane : 0;  // clamped pair for the LDS reads
-        const bool lv = lane < N2;
+        const int lp = pl < N2P ? pl : 0;  // clamped pair for the LDS reads
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int rho = wv + 8 * m, k = rho / R;
-            if (k >= Qt || k >= Tv) continue;  // uniform per wave
+        for (int m = 0; m < NM; ++m) {
+            const int rho = RP::row(wv, m), k = rho / R;
+            const bool rok = k < Qt && k < Tv;
+            if (__ballot(rok) == 0) continue;  // neither row of the wave is in the chunk
+            const bool lv = rok && pl < N2;
             float sn, cn;
-            fast_sincos(phi[k * N2P + lp], sn, cn);
+            fast_sincos(phi[(rok ? k : 0) * N2P + lp], sn, cn);
 #pragma unroll
             for (int side = 0; side < 2; ++side) {
                 float *rows = side == 0 ? sB : sC;
@@ -1374,8 +1405,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
                 float o0 = d0, o1 = d1;
                 if (norm) {
                     const float rs = L::KEEP ? sm[L::RS + 64 * side + rho]
-                                             : rsqrtf(wave_sum(v0 * v0 + v1 * v1) * invN + p.eps);
-                    const float dot = wave_sum(d0 * g0 * v0 + d1 * g1 * v1);
+                                             : rsqrtf(RP::sum(v0 * v0 + v1 * v1) * invN + p.eps);
+                    const float dot = RP::sum(d0 * g0 * v0 + d1 * g1 * v1);
                     const float f = dot * rs * rs * rs * invN;
                     o0 = d0 * g0 * rs - f * v0;
                     o1 = d1 * g1 * rs - f * v1;
@@ -1385,19 +1416,27 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
                 ba[side][0] += d0;
                 ba[side][1] += d1;
                 if (lv) {
-                    rows[rho * BP + 2 * lane] = o0;
-                    rows[rho * BP + 2 * lane + 1] = o1;
+                    rows[rho * BP + 2 * pl] = o0;
+                    rows[rho * BP + 2 * pl + 1] = o1;
                 }
             }
         }
-        if (lane < NPAD / 2)
+        // both halves of the wave hold sums for the same pairs (ranks agree when R divides 8)
+#pragma unroll
+        for (int side = 0; side < 2; ++side)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                ga[side][j] += RP::other(ga[side][j]);
+                ba[side][j] += RP::other(ba[side][j]);
+            }
+        if (RP::half() == 0 && pl < NPAD / 2)
 #pragma unroll
             for (int side = 0; side < 2; ++side) {
-                acc[(wv * 2 + side) * NPAD + 2 * lane] = ga[side][0];
-                acc[(wv * 2 + side) * NPAD + 2 * lane + 1] = ga[side][1];
+                acc[(wv * 2 + side) * NPAD + 2 * pl] = ga[side][0];
+                acc[(wv * 2 + side) * NPAD + 2 * pl + 1] = ga[side][1];
                 if (rdiv) {
-                    acc[16 * NPAD + (wv * 2 + side) * NPAD + 2 * lane] = ba[side][0];
-                    acc[16 * NPAD + (wv * 2 + side) * NPAD + 2 * lane + 1] = ba[side][1];
+                    acc[16 * NPAD + (wv * 2 + side) * NPAD + 2 * pl] = ba[side][0];
+                    acc[16 * NPAD + (wv * 2 + side) * NPAD + 2 * pl + 1] = ba[side][1];
                 }
             }
     }
