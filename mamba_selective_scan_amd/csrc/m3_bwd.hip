@@ -182,7 +182,11 @@ struct CL {
     static constexpr int AT = CE + 64;              // [2][64] C~ . (state term of dC~) per row
     static constexpr int KS = AT + 128;             // [2][64] B~ . (state term of dB~ / kappa) per row
     static constexpr int MS = KS + 128;             // misc
-    static constexpr int TOTAL = MS + 32;
+    // [8 waves][4 tiles][64 lanes][4] exchange of the s-oriented triangle's G and dY X^T tiles
+    // between the two waves of a row tile (gradient kernel, when it fits)
+    static constexpr int XC = MS + 32;
+    static constexpr bool XCH = GRAD && (XC + kWaves * 4 * 256) * 4 <= 160 * 1024;
+    static constexpr int TOTAL = XC + (XCH ? kWaves * 4 * 256 : 0);
     static_assert(32 * NPAD <= 2 * kRows * XP, "bias and gain sums must fit over the x and dy rows");
     static_assert(kRows * N2P <= 2 * kRows * XP, "angle terms must fit over the x and dy rows");
     static_assert(kWaves * 64 <= SLAB, "angle-sum scratch must fit in the slab area");
@@ -904,31 +908,75 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         const float cs_s = rcs(s), kap_s = rkap(s);
         const int tok_s = rtok(s);
         float ce = 0.f;
+        // G^T and (dY X^T)^T tiles of this row tile: with the exchange area, wave hf = 0 computes
+        // the G tiles and wave hf = 1 the dY X^T tiles, and each reads the other's from LDS;
+        // otherwise both waves compute both
+        f32x4_t mine[4];
+        if constexpr (L::XCH) {
+            float *xc = sm + L::XC;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                mine[a] = zero4();
+                if (a < amin) continue;
+                if (hf == 0) {
+#pragma unroll
+                    for (int kc = 0; kc < NPAD / 32; ++kc) {
+                        float av[8], bv[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            av[j] = sC[(16 * a + l16) * BP + 32 * kc + 8 * g + j];
+                            bv[j] = sB[s * BP + 32 * kc + 8 * g + j];
+                        }
+                        mine[a] = mma8(av, bv, mine[a]);
+                    }
+                } else {
+#pragma unroll
+                    for (int kc = 0; kc < PPAD / 32; ++kc) {
+                        float av[8], bv[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            av[j] = sY[(16 * a + l16) * XP + 32 * kc + 8 * g + j];
+                            bv[j] = sX[s * XP + 32 * kc + 8 * g + j];
+                        }
+                        mine[a] = mma8(av, bv, mine[a]);
+                    }
+                }
+                *(f32x4_t *)(xc + ((wv * 4 + a) * 64 + lane) * 4) = mine[a];
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             P1s[a] = P2s[a] = zero4();
             float rw[4] = {0.f, 0.f, 0.f, 0.f}, rd[4] = {0.f, 0.f, 0.f, 0.f};
             if (a >= amin) {
                 f32x4_t ga = zero4(), da = zero4();
+                if constexpr (L::XCH) {
+                    // the partner wave (same row tile, other half) is wave 7 - wv
+                    const f32x4_t theirs = *(const f32x4_t *)(sm + L::XC + (((kWaves - 1 - wv) * 4 + a) * 64 + lane) * 4);
+                    ga = hf == 0 ? mine[a] : theirs;
+                    da = hf == 0 ? theirs : mine[a];
+                } else {
 #pragma unroll
-                for (int kc = 0; kc < NPAD / 32; ++kc) {
-                    float av[8], bv[8];
+                    for (int kc = 0; kc < NPAD / 32; ++kc) {
+                        float av[8], bv[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        av[j] = sC[(16 * a + l16) * BP + 32 * kc + 8 * g + j];
-                        bv[j] = sB[s * BP + 32 * kc + 8 * g + j];
+                        for (int j = 0; j < 8; ++j) {
+                            av[j] = sC[(16 * a + l16) * BP + 32 * kc + 8 * g + j];
+                            bv[j] = sB[s * BP + 32 * kc + 8 * g + j];
+                        }
+                        ga = mma8(av, bv, ga);
                     }
-                    ga = mma8(av, bv, ga);
-                }
 #pragma unroll
-                for (int kc = 0; kc < PPAD / 32; ++kc) {
-                    float av[8], bv[8];
+                    for (int kc = 0; kc < PPAD / 32; ++kc) {
+                        float av[8], bv[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        av[j] = sY[(16 * a + l16) * XP + 32 * kc + 8 * g + j];
-                        bv[j] = sX[s * XP + 32 * kc + 8 * g + j];
+                        for (int j = 0; j < 8; ++j) {
+                            av[j] = sY[(16 * a + l16) * XP + 32 * kc + 8 * g + j];
+                            bv[j] = sX[s * XP + 32 * kc + 8 * g + j];
+                        }
+                        da = mma8(av, bv, da);
                     }
-                    da = mma8(av, bv, da);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
