@@ -161,17 +161,18 @@ __device__ __forceinline__ float eta_at(const BwdParams &p, int64_t b, int h, in
 // LDS layout of the chunk kernels (floats).  GRAD: the gradient kernel's layout, which keeps
 // the chunk's running angles (PH) and the rows' norm factors (RS) for the norm backward when
 // they fit beside the rest; otherwise the angles share the slab area and are computed again.
-template <int NPAD, int PPAD, bool GRAD = false>
+// SPLIT (chunk-state kernel): one B~/C~ tile and one x/dy tile, staged one side at a time.
+template <int NPAD, int PPAD, bool GRAD = false, bool SPLIT = false>
 struct CL {
     static constexpr int BP = NPAD + 1, XP = PPAD + 1, N2P = NPAD / 2;
-    static constexpr int SB = 0;                    // [64][BP] B~ rows (then dB~)
-    static constexpr int SC = SB + kRows * BP;      // [64][BP] C~ rows (then dC~)
-    static constexpr int SX = SC + kRows * BP;      // [64][XP] x rows
-    static constexpr int SY = SX + kRows * XP;      // [64][XP] gated dy rows
-    static constexpr int SS = SY + kRows * XP;      // state slab [32][XP]
+    static constexpr int SB = 0;                                  // [64][BP] B~ rows (then dB~)
+    static constexpr int SC = SPLIT ? SB : SB + kRows * BP;       // [64][BP] C~ rows (then dC~)
+    static constexpr int SX = SC + kRows * BP;                    // [64][XP] x rows
+    static constexpr int SY = SPLIT ? SX : SX + kRows * XP;       // [64][XP] gated dy rows
+    static constexpr int SS = SY + kRows * XP;                    // state slab [32][XP]
     static constexpr int REST = 3 * 64 + 6 * 64 + 8 * 64 + 64 + 128 + 128 + 32;
     static constexpr bool KEEP = GRAD && (SS + 32 * XP + kRows * N2P + 128 + REST) * 4 <= 160 * 1024;
-    static constexpr int SLAB = KEEP ? 32 * XP : (32 * XP > kRows * N2P ? 32 * XP : kRows * N2P);
+    static constexpr int SLAB = !GRAD ? kRows * N2P : KEEP ? 32 * XP : (32 * XP > kRows * N2P ? 32 * XP : kRows * N2P);
     static constexpr int PH = KEEP ? SS + SLAB : SS;  // [64][N2P] running angles of the chunk
     static constexpr int RS = PH + kRows * N2P;     // [2][64] norm factors of the B and C rows (KEEP)
     static constexpr int TK = KEEP ? RS + 128 : SS + SLAB;  // per token: cs, kappa, gamma
@@ -187,9 +188,10 @@ struct CL {
     static constexpr int XC = MS + 32;
     static constexpr bool XCH = GRAD && (XC + kWaves * 4 * 256) * 4 <= 160 * 1024;
     static constexpr int TOTAL = XC + (XCH ? kWaves * 4 * 256 : 0);
-    static_assert(32 * NPAD <= 2 * kRows * XP, "bias and gain sums must fit over the x and dy rows");
-    static_assert(kRows * N2P <= 2 * kRows * XP, "angle terms must fit over the x and dy rows");
-    static_assert(kWaves * 64 <= SLAB, "angle-sum scratch must fit in the slab area");
+    static_assert(!GRAD || 32 * NPAD <= 2 * kRows * XP, "bias and gain sums must fit over the x and dy rows");
+    static_assert(!GRAD || kRows * N2P <= 2 * kRows * XP, "angle terms must fit over the x and dy rows");
+    static_assert(!GRAD || kWaves * 64 <= SLAB, "angle-sum scratch must fit in the slab area");
+    static_assert(!(GRAD && SPLIT), "the gradient kernel needs every tile");
     static_assert(TOTAL * 4 <= 160 * 1024, "LDS");
 };
 
@@ -268,10 +270,14 @@ __device__ __forceinline__ float vec_elem(const u32x4_t &v, int j) {
 // run of x, dy, z, B and C and each token's angles are read as whole vectors (one or two per
 // thread), unpacked into the LDS tiles, and the B and C rows are then normalised and rotated
 // in place.  Needs P R and N R multiples of 16 / sizeof(element) and nr a multiple of 4.
-template <class Io, int NPAD, int PPAD, bool SCALED>
+// SIDES: 3 stages both sides; 1 (B~ and x, with the per-token scalars, angles and row tables)
+// and then 2 (C~ and gated dy, reusing those) stage one side at a time into the shared tiles
+// of the split layout.
+template <class Io, int NPAD, int PPAD, bool SCALED, int SIDES = 3>
 __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, int h, int64_t t0, int Tv) {
     using ET = typename Io::T;
-    using L = CL<NPAD, PPAD, !SCALED>;
+    using L = CL<NPAD, PPAD, !SCALED, SIDES != 3>;
+    constexpr bool DOB = (SIDES & 1) != 0, DOC = (SIDES & 2) != 0;
     constexpr int E = 16 / Io::bytes;
     constexpr int QX = (kRows * PPAD / E + kThreads - 1) / kThreads;
     constexpr int QB = (kRows * NPAD / E + kThreads - 1) / kThreads;
@@ -330,18 +336,18 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
     for (int row = wv; row < kRows; row += kWaves) {
         for (int col = lane; col < L::XP; col += 64)
             if (row >= rows || col >= P) {
-                sm[L::SX + row * L::XP + col] = 0.f;
-                sm[L::SY + row * L::XP + col] = 0.f;
+                if (DOB) sm[L::SX + row * L::XP + col] = 0.f;
+                if (DOC) sm[L::SY + row * L::XP + col] = 0.f;
             }
         for (int col = lane; col < L::BP; col += 64)
             if (row >= rows || col >= N) {
-                sm[L::SB + row * L::BP + col] = 0.f;
-                sm[L::SC + row * L::BP + col] = 0.f;
+                if (DOB) sm[L::SB + row * L::BP + col] = 0.f;
+                if (DOC) sm[L::SC + row * L::BP + col] = 0.f;
             }
-        if (lane < L::N2P && (row >= Tv || lane >= NR)) phi[row * L::N2P + lane] = 0.f;
+        if (DOB && lane < L::N2P && (row >= Tv || lane >= NR)) phi[row * L::N2P + lane] = 0.f;
     }
     // ---- per-token scalars (wave 0; lane = token of the chunk)
-    if (tid < 64) {
+    if (DOB && tid < 64) {
         float la = 0.f, kap = 0.f, gam = 0.f;
         if (k0 < Tv) {
             float dt = dtr, lam = lmr, dn = dtn, ln = lmn;
@@ -374,10 +380,10 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         for (int j = 0; j < E; ++j) {
             const float xf = vec_elem<Io>(xv[q], j);
             float yf = vec_elem<Io>(yv[q], j);
-            if (p.z) yf *= silu_f(vec_elem<Io>(zv[q], j));
-            sm[L::SX + (k * R + r) * L::XP + pc] = xf;
-            sm[L::SY + (k * R + r) * L::XP + pc] = yf;
-            dDp += xf * yf;
+            if (DOC && p.z) yf *= silu_f(vec_elem<Io>(zv[q], j));
+            if (DOB) sm[L::SX + (k * R + r) * L::XP + pc] = xf;
+            if (DOC) sm[L::SY + (k * R + r) * L::XP + pc] = yf;
+            if (DOB && DOC) dDp += xf * yf;
             if (++r == R) {
                 r = 0;
                 ++pc;
@@ -391,8 +397,8 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         int n = (v * E) / R, r = v * E - n * R;
 #pragma unroll
         for (int j = 0; j < E; ++j) {
-            sm[L::SB + (k * R + r) * L::BP + n] = vec_elem<Io>(bv[q], j);
-            sm[L::SC + (k * R + r) * L::BP + n] = vec_elem<Io>(cv[q], j);
+            if (DOB) sm[L::SB + (k * R + r) * L::BP + n] = vec_elem<Io>(bv[q], j);
+            if (DOC) sm[L::SC + (k * R + r) * L::BP + n] = vec_elem<Io>(cv[q], j);
             if (++r == R) {
                 r = 0;
                 ++n;
@@ -402,13 +408,14 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
         const int e = tid + kThreads * q, k = vt > 0 ? e / vt : 0, v = e - k * vt;
-        if (vt == 0 || e >= Tv * vt) continue;
+        if (!DOB || vt == 0 || e >= Tv * vt) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j) phi[k * L::N2P + 4 * v + j] = __uint_as_float(tv[q][j]);
     }
-    angle_scan_lds<L::N2P>(phi, sm + L::RW);  // (its barriers publish every tile and tk)
+    if constexpr (DOB) angle_scan_lds<L::N2P>(phi, sm + L::RW);  // (its barriers publish every tile and tk)
+    else __syncthreads();                                          // (the tiles; tk and rt are staged)
     const float cs_end = tk[Tv - 1];
-    if (tid < kRows) {
+    if (DOB && tid < kRows) {
         const int rho = tid, k = rho / R;
         const bool valid = k < Qt && k < Tv;
         const float cs = valid ? tk[k] : cs_end;
@@ -432,16 +439,16 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
     for (int m = 0; m < RP::NM; ++m) {
         const int rho = RP::row(wv, m), k = rho / R, r = rho - k * R;
         const bool valid = k < Qt && k < Tv && pl < N2;
-        float b0 = sm[L::SB + rho * L::BP + 2 * lp], b1 = sm[L::SB + rho * L::BP + 2 * lp + 1];
-        float c0 = sm[L::SC + rho * L::BP + 2 * lp], c1 = sm[L::SC + rho * L::BP + 2 * lp + 1];
+        float b0 = DOB ? sm[L::SB + rho * L::BP + 2 * lp] : 0.f, b1 = DOB ? sm[L::SB + rho * L::BP + 2 * lp + 1] : 0.f;
+        float c0 = DOC ? sm[L::SC + rho * L::BP + 2 * lp] : 0.f, c1 = DOC ? sm[L::SC + rho * L::BP + 2 * lp + 1] : 0.f;
         b0 = valid ? b0 : 0.f;
         b1 = valid ? b1 : 0.f;
         c0 = valid ? c0 : 0.f;
         c1 = valid ? c1 : 0.f;
         float sb = 1.f, sc = 1.f;
         if (norm) {
-            sb = rsqrtf(RP::sum(b0 * b0 + b1 * b1) * invN + p.eps);
-            sc = rsqrtf(RP::sum(c0 * c0 + c1 * c1) * invN + p.eps);
+            if (DOB) sb = rsqrtf(RP::sum(b0 * b0 + b1 * b1) * invN + p.eps);
+            if (DOC) sc = rsqrtf(RP::sum(c0 * c0 + c1 * c1) * invN + p.eps);
             if (L::KEEP && pl == 0) {
                 sm[L::RS + rho] = sb;
                 sm[L::RS + 64 + rho] = sc;
@@ -450,10 +457,14 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         float bi0 = bw0, bi1 = bw1, ci0 = cw0, ci1 = cw1;
         if (!rdiv) {
             const int64_t ob = ((int64_t)h * R + r) * N + 2 * pl;
-            bi0 = ld_raw(bbp, ob, valid && p.bbias);
-            bi1 = ld_raw(bbp, ob + 1, valid && p.bbias);
-            ci0 = ld_raw(cbp, ob, valid && p.cbias);
-            ci1 = ld_raw(cbp, ob + 1, valid && p.cbias);
+            if (DOB) {
+                bi0 = ld_raw(bbp, ob, valid && p.bbias);
+                bi1 = ld_raw(bbp, ob + 1, valid && p.bbias);
+            }
+            if (DOC) {
+                ci0 = ld_raw(cbp, ob, valid && p.cbias);
+                ci1 = ld_raw(cbp, ob + 1, valid && p.cbias);
+            }
         }
         bi0 = p.bbias ? bi0 : 0.f;
         bi1 = p.bbias ? bi1 : 0.f;
@@ -473,10 +484,14 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         const float u0 = fb * (cn * b0 - sn * b1), u1 = fb * (sn * b0 + cn * b1);
         const float v0 = fc * (cn * c0 - sn * c1), v1 = fc * (sn * c0 + cn * c1);
         if (pl < L::N2P) {
-            sm[L::SB + rho * L::BP + 2 * pl] = valid ? u0 : 0.f;
-            sm[L::SB + rho * L::BP + 2 * pl + 1] = valid ? u1 : 0.f;
-            sm[L::SC + rho * L::BP + 2 * pl] = valid ? v0 : 0.f;
-            sm[L::SC + rho * L::BP + 2 * pl + 1] = valid ? v1 : 0.f;
+            if (DOB) {
+                sm[L::SB + rho * L::BP + 2 * pl] = valid ? u0 : 0.f;
+                sm[L::SB + rho * L::BP + 2 * pl + 1] = valid ? u1 : 0.f;
+            }
+            if (DOC) {
+                sm[L::SC + rho * L::BP + 2 * pl] = valid ? v0 : 0.f;
+                sm[L::SC + rho * L::BP + 2 * pl + 1] = valid ? v1 : 0.f;
+            }
         }
     }
     __syncthreads();
@@ -486,11 +501,12 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
 // Stage one chunk: per-token scalars, normalised + biased + rotated B and C rows (scaled by
 // e^(cs_end - cs) kappa and e^cs when SCALED), x and gated dy rows, zero padding.  Every
 // global load of the chunk is issued before the first use.
-// Returns (per thread) its part of sum(dy_gated * x).
-template <class Io, int NPAD, int PPAD, bool SCALED>
+// Returns (per thread) its part of sum(dy_gated * x).  SIDES as in chunk_prologue_vec.
+template <class Io, int NPAD, int PPAD, bool SCALED, int SIDES = 3>
 __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h, int64_t t0, int Tv) {
     using ET = typename Io::T;
-    using L = CL<NPAD, PPAD, !SCALED>;
+    using L = CL<NPAD, PPAD, !SCALED, SIDES != 3>;
+    constexpr bool DOB = (SIDES & 1) != 0, DOC = (SIDES & 2) != 0;
     constexpr int QX = kRows * PPAD / kThreads;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int N = p.N, P = p.P, R = p.R, N2 = N / 2;
@@ -568,7 +584,7 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         }
     }
     // ---- per-token scalars (wave 0; lane = token of the chunk)
-    if (tid < 64) {
+    if (DOB && tid < 64) {
         float la = 0.f, kap = 0.f, gam = 0.f;
         if (k0 < Tv) {
             float dt = dtr, lam = lmr, dn = dtn, ln = lmn;
@@ -598,19 +614,20 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         if (e >= nx) continue;
         const int k = e / (PPAD * R), rem = e - k * PPAD * R, pc = rem / R, r = rem - pc * R;
         const float xv = raw_f<Io>(xr[q], xo[q]), yv = raw_f<Io>(yr[q], xo[q]);
-        const float y = p.z ? yv * silu_f(raw_f<Io>(zr[q], xo[q])) : yv;
-        sm[L::SX + (k * R + r) * L::XP + pc] = xv;
-        sm[L::SY + (k * R + r) * L::XP + pc] = y;
-        dDp += xv * y;
+        const float y = (DOC && p.z) ? yv * silu_f(raw_f<Io>(zr[q], xo[q])) : yv;
+        if (DOB) sm[L::SX + (k * R + r) * L::XP + pc] = xv;
+        if (DOC) sm[L::SY + (k * R + r) * L::XP + pc] = y;
+        if (DOB && DOC) dDp += xv * y;
     }
     for (int e = tid; e < (kRows - Qt * R) * L::XP; e += kThreads) {
-        sm[L::SX + Qt * R * L::XP + e] = 0.f;
-        sm[L::SY + Qt * R * L::XP + e] = 0.f;
+        if (DOB) sm[L::SX + Qt * R * L::XP + e] = 0.f;
+        if (DOC) sm[L::SY + Qt * R * L::XP + e] = 0.f;
     }
-    angle_scan<L::N2P>(ang, sm + L::PH, sm + L::RW);  // (its barriers publish tk)
+    if constexpr (DOB) angle_scan<L::N2P>(ang, sm + L::PH, sm + L::RW);  // (its barriers publish tk)
+    else __syncthreads();
     const float cs_end = tk[Tv - 1];
     // per-row tables
-    if (tid < kRows) {
+    if (DOB && tid < kRows) {
         const int rho = tid, k = rho / R;
         const bool valid = k < Qt && k < Tv;
         const float cs = valid ? tk[k] : cs_end;
@@ -635,8 +652,8 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         const int kc = k < kRows ? k : 0;
         float sb = 1.f, sc = 1.f;
         if (norm) {
-            sb = rsqrtf(RP::sum(rb[m][0] * rb[m][0] + rb[m][1] * rb[m][1]) * invN + p.eps);
-            sc = rsqrtf(RP::sum(rc[m][0] * rc[m][0] + rc[m][1] * rc[m][1]) * invN + p.eps);
+            if (DOB) sb = rsqrtf(RP::sum(rb[m][0] * rb[m][0] + rb[m][1] * rb[m][1]) * invN + p.eps);
+            if (DOC) sc = rsqrtf(RP::sum(rc[m][0] * rc[m][0] + rc[m][1] * rc[m][1]) * invN + p.eps);
             if (L::KEEP && pl == 0) {
                 sm[L::RS + rho] = sb;
                 sm[L::RS + 64 + rho] = sc;
@@ -656,10 +673,14 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         const float u0 = fb * (cn * b0 - sn * b1), u1 = fb * (sn * b0 + cn * b1);
         const float v0 = fc * (cn * c0 - sn * c1), v1 = fc * (sn * c0 + cn * c1);
         if (pl < L::N2P) {
-            sm[L::SB + rho * L::BP + 2 * pl] = valid ? u0 : 0.f;
-            sm[L::SB + rho * L::BP + 2 * pl + 1] = valid ? u1 : 0.f;
-            sm[L::SC + rho * L::BP + 2 * pl] = valid ? v0 : 0.f;
-            sm[L::SC + rho * L::BP + 2 * pl + 1] = valid ? v1 : 0.f;
+            if (DOB) {
+                sm[L::SB + rho * L::BP + 2 * pl] = valid ? u0 : 0.f;
+                sm[L::SB + rho * L::BP + 2 * pl + 1] = valid ? u1 : 0.f;
+            }
+            if (DOC) {
+                sm[L::SC + rho * L::BP + 2 * pl] = valid ? v0 : 0.f;
+                sm[L::SC + rho * L::BP + 2 * pl + 1] = valid ? v1 : 0.f;
+            }
         }
     }
     __syncthreads();
@@ -681,9 +702,20 @@ __device__ __forceinline__ float block_sum(float v, float *scratch) {
 }  // namespace
 
 // ---------------------------------------------------------------- per-chunk state sums
+// On the 16-byte load path, a layout that leaves room for only one workgroup per compute unit
+// stages one side at a time (B~ and x, then C~ and dy) when that makes room for two; the
+// register budget then follows two workgroups per unit (the launch bound counts waves per SIMD).
+template <int NPAD, int PPAD, bool VEC>
+constexpr bool state_split() {
+    return VEC && CL<NPAD, PPAD>::TOTAL * 4 * 2 > 160 * 1024 && CL<NPAD, PPAD, false, true>::TOTAL * 4 * 2 <= 160 * 1024;
+}
+template <int NPAD, int PPAD, bool VEC>
+constexpr int state_min_waves_per_simd() { return state_split<NPAD, PPAD, VEC>() ? 2 * kThreads / 256 : 1; }
+
 template <class Io, int NPAD, int PPAD, bool VEC>
-__global__ __launch_bounds__(kThreads) void bwd_chunk_state_kernel(BwdParams p) {
-    using L = CL<NPAD, PPAD>;
+__global__ __launch_bounds__(kThreads, (state_min_waves_per_simd<NPAD, PPAD, VEC>())) void bwd_chunk_state_kernel(BwdParams p) {
+    constexpr bool SPLIT = state_split<NPAD, PPAD, VEC>();
+    using L = CL<NPAD, PPAD, false, SPLIT>;
     constexpr int NT = NPAD / 16, PT = PPAD / 16;
     extern __shared__ __attribute__((aligned(16))) float sm[];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, l16 = lane & 15;
@@ -695,31 +727,46 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_state_kernel(BwdParams p) 
     const int Qt = kRows / p.R;
     const int64_t t0 = (int64_t)c * Qt;
     const int Tv = (int)min((int64_t)Qt, p.T - t0);
-    if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
-    else chunk_prologue<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
     const int64_t cidx = bh * nck + c;
-    for (int q = wv; q < 2 * NT * PT; q += kWaves) {
-        const int which = q / (NT * PT), rem = q - which * NT * PT, a = rem / PT, bq = rem - a * PT;
-        const float *Ao = sm + (which ? L::SC : L::SB), *Bo = sm + (which ? L::SY : L::SX);
-        f32x4_t acc = zero4();
+    // S (which 0) = sum over rows of B~ x^T, U (which 1) = sum of C~ dy^T: this wave's 16x16 tiles
+    auto products = [&](int which, int q0, int q1) {
+        for (int q = q0 + wv; q < q1; q += kWaves) {
+            const int rem = q - which * NT * PT, a = rem / PT, bq = rem - a * PT;
+            const float *Ao = sm + (which ? L::SC : L::SB), *Bo = sm + (which ? L::SY : L::SX);
+            f32x4_t acc = zero4();
 #pragma unroll
-        for (int kc = 0; kc < kRows / 32; ++kc) {
-            float av[8], bv[8];
+            for (int kc = 0; kc < kRows / 32; ++kc) {
+                float av[8], bv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int s = 32 * kc + 8 * g + j;
-                av[j] = Ao[s * L::BP + 16 * a + l16];
-                bv[j] = Bo[s * L::XP + 16 * bq + l16];
+                for (int j = 0; j < 8; ++j) {
+                    const int s = 32 * kc + 8 * g + j;
+                    av[j] = Ao[s * L::BP + 16 * a + l16];
+                    bv[j] = Bo[s * L::XP + 16 * bq + l16];
+                }
+                acc = mma8(av, bv, acc);
             }
-            acc = mma8(av, bv, acc);
-        }
-        float *dst = (which ? p.Ust : p.Sst) + cidx * N * (int64_t)P;
-        const int pc = 16 * bq + l16;
+            float *dst = (which ? p.Ust : p.Sst) + cidx * N * (int64_t)P;
+            const int pc = 16 * bq + l16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = 16 * a + 4 * g + i;
-            if (n < N && pc < P) dst[(int64_t)n * P + pc] = acc[i];
+            for (int i = 0; i < 4; ++i) {
+                const int n = 16 * a + 4 * g + i;
+                if (n < N && pc < P) dst[(int64_t)n * P + pc] = acc[i];
+            }
         }
+    };
+    if constexpr (SPLIT) {
+        if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true, 1>(p, sm, b, h, t0, Tv);
+        else chunk_prologue<Io, NPAD, PPAD, true, 1>(p, sm, b, h, t0, Tv);
+        products(0, 0, NT * PT);
+        __syncthreads();  // the shared tiles are restaged for the C side
+        if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true, 2>(p, sm, b, h, t0, Tv);
+        else chunk_prologue<Io, NPAD, PPAD, true, 2>(p, sm, b, h, t0, Tv);
+        products(1, NT * PT, 2 * NT * PT);
+    } else {
+        if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
+        else chunk_prologue<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
+        products(0, 0, NT * PT);
+        products(1, NT * PT, 2 * NT * PT);
     }
     if (tid < N2) p.phic[cidx * N2 + tid] = sm[L::PH + (Tv - 1) * L::N2P + tid];
     if (tid == 0) p.lsum[cidx] = sm[L::TK + Tv - 1];
@@ -1798,12 +1845,12 @@ __global__ __launch_bounds__(256) void bwd_empty_kernel(BwdParams p) {
 
 namespace {
 
-template <int NPAD, int PPAD, bool GRAD>
-constexpr size_t chunk_lds() { return sizeof(float) * CL<NPAD, PPAD, GRAD>::TOTAL; }
+template <int NPAD, int PPAD, bool GRAD, bool VEC = false>
+constexpr size_t chunk_lds() { return sizeof(float) * CL<NPAD, PPAD, GRAD, !GRAD && state_split<NPAD, PPAD, VEC>()>::TOTAL; }
 
 template <class Io, int NPAD, int PPAD, bool VEC>
 hipError_t launch_chunks_v(const BwdParams &p, hipStream_t st) {
-    const size_t lds = chunk_lds<NPAD, PPAD, false>(), ldg = chunk_lds<NPAD, PPAD, true>();
+    const size_t lds = chunk_lds<NPAD, PPAD, false, VEC>(), ldg = chunk_lds<NPAD, PPAD, true>();
     const dim3 grid((unsigned)(p.B * p.H * p.nck)), blk(kThreads);
     hipError_t e;
     if ((e = hipFuncSetAttribute((const void *)bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC>,

@@ -134,6 +134,8 @@ def test_bwd_tiny_f32():
     (33, 16, 16, 8, "f32"),      # MIMO R 8 (8 tokens per chunk)
     (70, 128, 32, 1, "bf16"),    # P 128 with N 32
     (45, 24, 40, 5, "f32"),      # MIMO R 5, N and P not multiples of 16
+    (90, 128, 64, 1, "f32"),     # chunk states staged one side at a time (P 128)
+    (75, 48, 128, 2, "f32"),     # the same with N 128, MIMO R 2
 ])
 def test_bwd_shapes(T, P, N, R, io):
     run_case(custom(batch=2, seqlen=T, nheads=2, headdim=P, dstate=N, rank=R, io=io, seed=T + N + R))
