@@ -922,22 +922,36 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     const int64_t cidx = bh * nck + c;
     const bool last = c == nck - 1;
     const float *Gend = p.Ust + cidx * N * (int64_t)P, *Hst = p.Sst + cidx * N * (int64_t)P;
-    // the first state slab, early
-    float stg[SQ];
-    auto load_slab = [&](const float *src, int ns) {
+    // State slabs (32 state rows of the adjoint after the chunk and of the state before it) go
+    // through registers into LDS.  The first is loaded before the staging; when the registers
+    // allow, every other slab is loaded right after it (in flight during the triangles),
+    // otherwise one slab ahead inside the slab loop.  Raw values; masked where they are used.
+    constexpr bool PFA = 2 * NS * SQ <= 32 && !(PPAD == 128 && NPAD >= 64);
+    float stg[PFA ? 2 * NS : 1][SQ];
+    auto slab_ok = [&](int ns, int q) {
+        const int e = tid + kThreads * q, row = e / PPAD, col = e - row * PPAD;
+        return 32 * ns + row < N && col < P;
+    };
+    auto load_slab = [&](float (&dst)[SQ], const float *src, int ns) {
 #pragma unroll
         for (int q = 0; q < SQ; ++q) {
-            const int e = tid + kThreads * q, row = e / PPAD, col = e - row * PPAD, n = 32 * ns + row;
-            const bool ok = n < N && col < P;
-            const float v = ld_raw(src, (int64_t)n * P + col, ok);
-            stg[q] = ok ? v : 0.f;
+            const int e = tid + kThreads * q, row = e / PPAD, col = e - row * PPAD;
+            dst[q] = ld_raw(src, (int64_t)(32 * ns + row) * P + col, slab_ok(ns, q));
         }
     };
-    load_slab(Gend, 0);
+    load_slab(stg[0], Gend, 0);
     // (a run-time choice here: with both staging variants in one kernel the register
     // allocation of the matrix phases comes out better than with either alone)
     const float dDp = p.vec ? chunk_prologue_vec<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv)
                             : chunk_prologue<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv);
+    if constexpr (PFA) {
+        load_slab(stg[1], Hst, 0);
+#pragma unroll
+        for (int ns = 1; ns < NS; ++ns) {
+            load_slab(stg[2 * ns], Gend, ns);
+            load_slab(stg[2 * ns + 1], Hst, ns);
+        }
+    }
     float *sB = sm + L::SB, *sC = sm + L::SC, *sX = sm + L::SX, *sY = sm + L::SY, *sS = sm + L::SS;
     const float *rt = sm + L::RT;
     auto rcs = [&](int r) { return rt[r]; };
@@ -1185,11 +1199,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
 #pragma unroll
         for (int q = 0; q < SQ; ++q) {
             const int e = tid + kThreads * q, row = e / PPAD, col = e - row * PPAD;
-            sS[row * XP + col] = stg[q];
-            gk[q] = stg[q];
+            const float v = slab_ok(ns, q) ? stg[PFA ? 2 * ns : 0][q] : 0.f;
+            sS[row * XP + col] = v;
+            gk[q] = v;
         }
         __syncthreads();
-        load_slab(Hst, ns);
+        if constexpr (!PFA) load_slab(stg[0], Hst, ns);
 #pragma unroll
         for (int q = 0; q < PH; ++q) {
             const int bq = hf * PH + q;
@@ -1217,11 +1232,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
 #pragma unroll
         for (int q = 0; q < SQ; ++q) {
             const int e = tid + kThreads * q, row = e / PPAD, col = e - row * PPAD;
-            sS[row * XP + col] = stg[q];
-            hdot += gk[q] * stg[q];
+            const float v = slab_ok(ns, q) ? stg[PFA ? 2 * ns + 1 : 0][q] : 0.f;
+            sS[row * XP + col] = v;
+            hdot += gk[q] * v;
         }
         __syncthreads();
-        if (ns + 1 < NS) load_slab(Gend, ns + 1);
+        if constexpr (!PFA) {
+            if (ns + 1 < NS) load_slab(stg[0], Gend, ns + 1);
+        }
         accCi[ns] = zero4();
 #pragma unroll
         for (int kc = 0; kc < PPAD / 32; ++kc) {
