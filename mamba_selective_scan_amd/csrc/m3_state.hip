@@ -51,6 +51,16 @@ __device__ __forceinline__ void store_y(const StepParams &p, int64_t off, float 
     if (p.z) v *= silu_f(Io::ld((const ET *)p.z + off));
     Io::st((ET *)p.y + off, v);
 }
+// Load of base[off] when ok, else of base[0] (base must be a valid array): the value is
+// selected afterwards, so that a run of such loads is in flight before the first use.
+template <class T>
+__device__ __forceinline__ T ld_sel(const T *base, int64_t off, bool ok) { return base[ok ? off : 0]; }
+template <class Io>
+__device__ __forceinline__ float to_f(typename Io::T v) {
+    if constexpr (Io::bytes == 2) return bf2f(v);
+    else return v;
+}
+
 // One workgroup per (head, batch).  The step is the recurrence itself for one
 // token (torchmamba "Quickstart": step(u_t, cache)):
 //     Theta <- Theta + theta;  B~, C~ = Rot(Theta)(norm(B) + bias), ...
@@ -225,8 +235,9 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
 // Rank-1 decode step (P a multiple of 4).  B~ and C~ are formed by one wave each (lane n
 // holds component n, and n + 64 when N > 64): a wave reduction for the norm and a swap
 // between neighbouring lanes for the rotation of pair (2i, 2i + 1).  A third wave stages
-// x and the carried x.  The step then needs two workgroup barriers, and each thread's rows
-// of h are requested before anything else.
+// x and the carried x, a fourth computes the step's coefficients.  The step then needs two
+// workgroup barriers, each thread's rows of h are requested before anything else, and each
+// wave issues all of its loads before the first use.
 template <class Io>
 __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
     using ET = typename Io::T;
@@ -258,17 +269,36 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
     float *s_x = s_pb + NA;       // [P] x
     float *s_px = s_x + PA;       // [P] previous x
     float *s_ang = s_px + PA;     // [N/2] new angle
-    float *s_red = s_ang + N2A;   // [NG][P] partial outputs
+    float *s_cf = s_ang + N2A;    // [4] alpha, beta, gamma
+    float *s_red = s_cf + 4;      // [NG][P] partial outputs
     const bool bcnorm = (p.flags & kFlagNorm) != 0;
+    // Every load of a wave is issued before its first use (absent elements load offset 0 of a
+    // valid array and are replaced afterwards): wave 0 stages B~ (and swaps prev_B), wave 1
+    // C~, wave 2 x (and swaps prev_x), wave 3 the step's coefficients.
     if (wave < 2) {
         const ET *src = (const ET *)(wave == 0 ? p.Bm : p.Cm) + bh * N;
         const float *gain = wave == 0 ? p.bnw : p.cnw;
         const float *bias = wave == 0 ? p.bbias : p.cbias;
+        const bool hg = bcnorm && gain != nullptr, hb = bias != nullptr;
+        const float *gp = hg ? gain : p.dt, *bp = hb ? bias + (int64_t)h * N : p.dt;
+        const float *ap = p.ang ? p.ang : p.dt, *tp = p.theta ? p.theta : p.dt;
+        ET raw[2];
+        float gv[2], bv[2], av[2], tv[2], pbv[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int n = lane + 64 * k, i = n >> 1;
+            const bool in = n < N, ir = in && i < p.nr;
+            raw[k] = ld_sel(src, n, in);
+            gv[k] = ld_sel(gp, n, in && hg);
+            bv[k] = ld_sel(bp, n, in && hb);
+            av[k] = ld_sel(ap, bh * p.nr + i, ir);
+            tv[k] = ld_sel(tp, bh * p.nr + i, ir);
+            pbv[k] = ld_sel(p.pB, bh * N + n, in && wave == 0);
+        }
         float v[2], ss = 0.f;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int n = lane + 64 * k;
-            v[k] = n < N ? Io::ld(src + n) : 0.f;
+            v[k] = lane + 64 * k < N ? to_f<Io>(raw[k]) : 0.f;
             ss += v[k] * v[k];
         }
 #pragma unroll
@@ -279,17 +309,17 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
             const int n = lane + 64 * k;
             const bool in = n < N;
             float u = v[k] * rs;
-            if (in && bcnorm && gain) u *= gain[n];
-            if (in && bias) u += bias[(int64_t)h * N + n];
+            if (in && hg) u *= gv[k];
+            if (in && hb) u += bv[k];
             // the pair's angle Theta + theta (the stored angle is kept in [0, 2 pi))
             const int i = n >> 1;
-            const double a = (in && i < p.nr) ? wrap_2pi((double)p.ang[bh * p.nr + i] + (double)p.theta[bh * p.nr + i]) : 0.0;
+            const double a = (in && i < p.nr) ? wrap_2pi((double)av[k] + (double)tv[k]) : 0.0;
             const f32x2_t sc = sincos_acc((float)a);  // (sin, cos)
             const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(u), 0xB1, 0xF, 0xF, false));
             const float out = (n & 1) ? other * sc[0] + u * sc[1] : u * sc[1] - other * sc[0];
             if (!in) continue;
             if (wave == 0) {
-                s_pb[n] = p.pB[bh * N + n];
+                s_pb[n] = pbv[k];
                 p.pB[bh * N + n] = out;
                 s_bt[n] = out;
                 if ((n & 1) == 0) s_ang[i] = (float)a;
@@ -300,17 +330,25 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
     } else if (wave == 2) {
         const ET *xg = (const ET *)p.x + bh * P;
         for (int pc = lane; pc < P; pc += 64) {
-            const float xv = Io::ld(xg + pc);
+            const float xv = Io::ld(xg + pc), pxv = p.px[bh * P + pc];
             s_x[pc] = xv;
-            s_px[pc] = p.px[bh * P + pc];
+            s_px[pc] = pxv;
             p.px[bh * P + pc] = xv;
         }
+    } else if (lane == 0) {
+        float alpha, beta, gamma;
+        step_coeffs(p, bh, h, alpha, beta, gamma);
+        s_cf[0] = alpha;
+        s_cf[1] = beta;
+        s_cf[2] = gamma;
     }
+    // the gate input of this thread's first output element
+    const ET *zb = (const ET *)(p.z ? p.z : p.x);
+    const ET zr = ld_sel(zb, bh * P + tid, p.z != nullptr && tid < P);
     __syncthreads();
     if (tid < p.nr) p.ang[bh * p.nr + tid] = s_ang[tid];
 
-    float alpha, beta, gamma;
-    step_coeffs(p, bh, h, alpha, beta, gamma);
+    const float alpha = s_cf[0], beta = s_cf[1], gamma = s_cf[2];
     if (upd) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         f32x4_t xv4 = *(const f32x4_t *)(s_x + pg * 4), pxv4 = *(const f32x4_t *)(s_px + pg * 4);
@@ -337,7 +375,9 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
     for (int e = tid; e < P; e += 256) {
         float sacc = 0.f;
         for (int k2 = 0; k2 < NG; ++k2) sacc += s_red[k2 * P + e];
-        store_y<Io>(p, bh * P + e, sacc + Dh * s_x[e]);
+        float v = sacc + Dh * s_x[e];
+        if (p.z) v *= silu_f(e == tid ? to_f<Io>(zr) : Io::ld(zb + bh * P + e));
+        Io::st((ET *)p.y + bh * P + e, v);
     }
 }
 
@@ -350,7 +390,7 @@ hipError_t launch_step(bool bf16, const StepParams &p, hipStream_t stream) {
     if (p.R == 1 && p.P % 4 == 0 && !(p.flags & kFlagHalfSplit)) {  // adjacent pairs across neighbouring lanes
         const int NG = 256 / (p.P / 4);
         const int NA = (p.N + 3) & ~3, PA = (p.P + 3) & ~3, N2A = (p.N / 2 + 3) & ~3;
-        const size_t lds = sizeof(float) * (size_t)(3 * NA + 2 * PA + N2A + NG * p.P);
+        const size_t lds = sizeof(float) * (size_t)(3 * NA + 2 * PA + N2A + 4 + NG * p.P);
         dim3 grid((unsigned)p.H, (unsigned)p.B);
         if (bf16) hipLaunchKernelGGL((step_kernel_r1<IoBF16>), grid, dim3(256), lds, stream, p);
         else hipLaunchKernelGGL((step_kernel_r1<IoF32>), grid, dim3(256), lds, stream, p);
