@@ -237,7 +237,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
 // between neighbouring lanes for the rotation of pair (2i, 2i + 1).  A third wave stages
 // x and the carried x, a fourth computes the step's coefficients.  The step then needs two
 // workgroup barriers, each thread's rows of h are requested before anything else, and each
-// wave issues all of its loads before the first use.
+// wave issues all of its loads before the first use.  The state rows are read and written
+// with the non-temporal hint (each is touched once per step; measured about 2% faster).
 template <class Io>
 __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
     using ET = typename Io::T;
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int n = n0 + u * NG;
-            if (upd && n < N) hv[u] = *(const f32x4_t *)(hst + (int64_t)n * P + pg * 4);
+            if (upd && n < N) hv[u] = __builtin_nontemporal_load((const f32x4_t *)(hst + (int64_t)n * P + pg * 4));
         }
     };
     load_rows(ng);
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
                     hn[j] = alpha * hv[u][j] + pb * pxv4[j] + bt * xv4[j];
                     acc[j] += hn[j] * ct;
                 }
-                *(f32x4_t *)(hst + (int64_t)n * P + pg * 4) = hn;
+                __builtin_nontemporal_store(hn, (f32x4_t *)(hst + (int64_t)n * P + pg * 4));
             }
         }
         *(f32x4_t *)(s_red + ng * P + pg * 4) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
