@@ -1752,11 +1752,23 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(BwdParams p) {
     const int64_t T = p.T, H = p.H, t0 = (int64_t)c * Qt;
     const int Tv = (int)min((int64_t)Qt, T - t0);
     const int64_t cidx = bh * nck + c;
-    if (p.dtheta)
-        for (int e = tid; e < Tv * NR; e += 256) {
-            const int k = e / NR, i = e - k * NR;
-            p.dtheta[((b * T + t0 + k) * H + h) * (int64_t)NR + i] += p.tot[cidx * N2 + i];
+    if (p.dtheta) {
+        if ((NR & 3) == 0 && (N2 & 3) == 0) {
+            // 16-byte read-modify-write of each token's angle gradients (rows of NR floats;
+            // the row starts and the per-chunk totals are 16-byte aligned)
+            const int nv = NR / 4;
+            for (int e = tid; e < Tv * nv; e += 256) {
+                const int k = e / nv, i = 4 * (e - k * nv);
+                f32x4_t *d = (f32x4_t *)(p.dtheta + ((b * T + t0 + k) * H + h) * (int64_t)NR + i);
+                *d += *(const f32x4_t *)(p.tot + cidx * N2 + i);
+            }
+        } else {
+            for (int e = tid; e < Tv * NR; e += 256) {
+                const int k = e / NR, i = e - k * NR;
+                p.dtheta[((b * T + t0 + k) * H + h) * (int64_t)NR + i] += p.tot[cidx * N2 + i];
+            }
         }
+    }
     float aA = 0.f, aB = 0.f;
     if (tid < Tv) {
         const int64_t t = t0 + tid, bth = (b * T + t) * H + h;
