@@ -126,12 +126,14 @@ Plan plan_of(const m3_shape *s) {
     if (pl.bps < 1) pl.bps = 1;
     pl.nseg = pl.nblk > 0 ? (pl.nblk + pl.bps - 1) / pl.bps : 1;
     // state sub-segments over the blocks of segments 0 .. nseg-2: halve them (while the
-    // length stays a whole number of blocks) until about three state workgroups per unit
-    // (only with long segments: splitting then pays for the extra prefix launch; otherwise
-    // one sub-segment per segment and the output kernel folds the aggregates itself)
+    // length stays a whole number of blocks) until about three state workgroups per unit,
+    // six with ranks above 1 (measured faster there) (only with long segments: splitting
+    // then pays for the extra prefix launch; otherwise one sub-segment per segment and the
+    // output kernel folds the aggregates itself)
     pl.sbps = pl.bps;
+    const int64_t sub_wgs = s->rank > 1 ? 1536 : 768;
     if (pl.bps >= 8 && pl.nseg > 1)
-        while ((pl.sbps % 2) == 0 && BH * (pl.nseg - 1) * (pl.bps / pl.sbps) < 768 &&
+        while ((pl.sbps % 2) == 0 && BH * (pl.nseg - 1) * (pl.bps / pl.sbps) < sub_wgs &&
                (pl.nseg - 1) * (pl.bps / pl.sbps) < 32)
             pl.sbps /= 2;
     pl.nsub = (pl.nseg - 1) * (pl.bps / pl.sbps);
