@@ -176,9 +176,15 @@ __device__ __forceinline__ int tr_off(int col, int row) {
 // Offset of (row, col) in the y staging plane [row][PP] (rank-1 and general paths):
 // columns XOR-swizzled in groups of 16 by bits 2.. of the row, so that the four
 // 4-row groups written by one instruction use different banks.
-// Offset of (p, row) in the X^T plane [p][row] (pitch RPP).
+// Offset of (p, row) in the X^T plane [p][row] (pitch RPP).  On the rank-1 16-byte path the
+// row index is XOR-swizzled by bits 3..5 of p, as in the (w B~)^T plane: the staging writes
+// one token's 8 consecutive p at once from 8 lanes per token, which without the swizzle all
+// fall into one LDS bank; aligned groups of 8 (and 4) rows stay contiguous for the operand reads.
 template <class Cfg>
-__device__ __forceinline__ int xt_off(int col, int row) { return col * Cfg::RPP + row; }
+__device__ __forceinline__ int xt_off(int col, int row) {
+    if constexpr (Cfg::VEC) return col * Cfg::RPP + (row ^ (((col >> 3) & 7) << 3));
+    else return col * Cfg::RPP + row;
+}
 template <class Cfg>
 __device__ __forceinline__ int ys_off(int row, int col) {
     return row * Cfg::PP + (col ^ (((row >> 2) & (Cfg::PP / 16 - 1)) << 4));
