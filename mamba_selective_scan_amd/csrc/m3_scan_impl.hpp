@@ -87,12 +87,14 @@ __device__ __forceinline__ int row_tile() { return threadIdx.x >> 6; }
 //              (n, rank) / (p, rank) interleaved rows, regrouped per rank through LDS.
 constexpr int kModeGen = 0, kModeVec = 1, kModeMimo = 2;
 
-template <class Io, int NP_, int PP_, int MODE_>
+// SWZ_: XOR-swizzled X^T plane on the rank-1 16-byte path (see xt_off).
+template <class Io, int NP_, int PP_, int MODE_, bool SWZ_ = true>
 struct SegCfg {
     using ET = typename Io::T;
     static constexpr bool BF = std::is_same<Io, IoBF16>::value;
     static constexpr bool VEC = MODE_ == kModeVec;
     static constexpr bool MV = MODE_ == kModeMimo;
+    static constexpr bool XSWZ = SWZ_ && VEC;
     static_assert(!MV || BF, "the interleaved-rank load path is bf16 only");
     static constexpr bool PACKED = (VEC || MV) && BF;  // raw B/C held as packed bf16 words
     static constexpr int NP = NP_, PP = PP_;
@@ -176,13 +178,15 @@ __device__ __forceinline__ int tr_off(int col, int row) {
 // Offset of (row, col) in the y staging plane [row][PP] (rank-1 and general paths):
 // columns XOR-swizzled in groups of 16 by bits 2.. of the row, so that the four
 // 4-row groups written by one instruction use different banks.
-// Offset of (p, row) in the X^T plane [p][row] (pitch RPP).  On the rank-1 16-byte path the
-// row index is XOR-swizzled by bits 3..5 of p, as in the (w B~)^T plane: the staging writes
-// one token's 8 consecutive p at once from 8 lanes per token, which without the swizzle all
-// fall into one LDS bank; aligned groups of 8 (and 4) rows stay contiguous for the operand reads.
+// Offset of (p, row) in the X^T plane [p][row] (pitch RPP).  With XSWZ (rank-1 16-byte path)
+// the row index is XOR-swizzled by bits 3..5 of p, as in the (w B~)^T plane: the staging
+// writes one token's 8 consecutive p at once from 8 lanes per token, which without the
+// swizzle all fall into one LDS bank; aligned groups of 8 (and 4) rows stay contiguous for
+// the operand reads.  The gated output kernel keeps the plain layout (the swizzled addresses
+// cost it more register spills than the conflicts they remove: 66 -> 74 us).
 template <class Cfg>
 __device__ __forceinline__ int xt_off(int col, int row) {
-    if constexpr (Cfg::VEC) return col * Cfg::RPP + (row ^ (((col >> 3) & 7) << 3));
+    if constexpr (Cfg::XSWZ) return col * Cfg::RPP + (row ^ (((col >> 3) & 7) << 3));
     else return col * Cfg::RPP + row;
 }
 template <class Cfg>
@@ -1159,7 +1163,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
 // SIMD), so such variants may use the whole register file.
 template <class Io, int NP, int PP, int MODE, bool GATE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1 : 2, NP > 64 ? 1 : 2))) void seg_output_kernel(ScanParams p) {
-    using Cfg = SegCfg<Io, NP, PP, MODE>;
+    using Cfg = SegCfg<Io, NP, PP, MODE, !GATE>;
     constexpr bool VEC = Cfg::VEC;
     using ET = typename Io::T;
     using Frag = typename std::conditional<Cfg::BF, FragHL, FragF>::type;
