@@ -238,6 +238,15 @@ def test_split_schedule_half_split(R, P, N, io):
     check_state(state, f_ref, io)
 
 
+@pytest.mark.parametrize("opts,nr", [(("rope", "atok", "softplus", "sigmoid", "gate"), 16), (("half",), None)])
+def test_options_full_workload(opts, nr):
+    """The headline workload (batch 4, T 2048, 16 heads, P = N = 64, bf16) with the option sets
+    bench.py times: every canonical-block option (16 of 32 pairs rotated), and the half-split
+    pairing; y and the final state against the oracle."""
+    from synth import WORKLOADS
+    run_scan(WORKLOADS[1], set(opts), nr=nr)
+
+
 def test_option_errors_raise():
     import torch
     m3 = _m3()

@@ -179,6 +179,14 @@ def test_bwd_empty_sequence():
     assert float(g["D"].abs().sum()) == 0.0 and float(g["A"].abs().sum()) == 0.0
 
 
+@pytest.mark.parametrize("opts", [("rope", "atok", "act", "gate"), ("half",)])
+def test_bwd_full_workload_options(opts):
+    """Gradients at the headline workload's full size with every canonical-block option (16 of
+    32 pairs rotated) and with the half-split pairing, against the oracle's reverse sweep."""
+    from synth import WORKLOADS
+    run_case(WORKLOADS[1], opts=opts, nr=16 if "rope" in opts else None)
+
+
 @pytest.mark.parametrize("k", [1, 2, 3])
 def test_bwd_full_workloads(k):
     """The bench workloads at full size (SISO config, MIMO rank 4, the 16384-token N 128 one):
