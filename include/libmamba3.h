@@ -113,8 +113,11 @@ typedef struct {
     int32_t headdim; /* P, 1 .. 128 */
     int32_t dstate;  /* N, even, 2 .. 128 */
     int32_t rank;    /* R, 1 .. 8 (1 for m3_scan_siso) */
-    int32_t chunk;   /* tokens per chunk, one of 16, 32, 64, 128 (the result does not depend on it);
-                        for rank R the chunk holds chunk*R (token, rank) rows, at most 128 */
+    int32_t chunk;   /* requested tokens per chunk, one of 16, 32, 64, 128 with chunk*R <= 128 (the
+                        result does not depend on it).  It is an upper bound: the scan kernels work
+                        on blocks of at most 64 (token, rank) rows, so a chunk is processed as
+                        min(chunk, 64 / R) tokens (chunk 128 runs as 64-token blocks, and rank R
+                        as blocks of 64 / R tokens); the gradient call always uses 64 / R */
     int32_t io;      /* m3_dtype */
     uint32_t flags;  /* M3_FLAG_* */
     float norm_eps;  /* RMSNorm epsilon (1e-5 is the usual value) */
@@ -141,7 +144,8 @@ typedef struct {
     float *angle;  /* [B, H, NR] cumulative angle Theta of the last token, kept in [0, 2 pi) */
 } m3_state;
 
-/* Bytes of workspace m3_scan_siso / m3_scan_mimo need for this shape (0 when T == 0). */
+/* Bytes of workspace m3_scan_siso / m3_scan_mimo need for this shape (0 when T == 0 or B == 0,
+ * also with M3_FLAG_HALF_SPLIT: such a call only copies the state).  0 for an invalid shape. */
 size_t m3_scan_workspace_bytes(const m3_shape *shape);
 
 /*

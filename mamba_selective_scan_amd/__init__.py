@@ -13,6 +13,7 @@ RuntimeError is raised.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -128,6 +129,16 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _alloc_on(stream):
+    """Context under which a call's outputs and workspace are allocated: the stream the
+    kernels run on.  The caching allocator then reuses a block freed here (the workspace,
+    released when the call returns) only for later work ordered on that same stream, never
+    while the kernels may still read or write it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
+
+
 def _shape_of(x, B, chunk, bcnorm, eps, mimo, opts):
     io = {torch.float32: M3_F32, torch.bfloat16: M3_BF16}.get(x.dtype)
     if io is None:
@@ -222,23 +233,24 @@ def _scan(mimo, x, B, C, dt, lam, theta, A, D, *, chunk=64, bcnorm=True, eps=1e-
     _need(x, "x", x.dtype, x.device)
     inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
                   dt_bias, z)
-    if y is None:
-        y = torch.empty_like(x)
-    else:
-        _need(y, "y", x.dtype, x.device, tuple(x.shape))
-    if final is True:
-        final = new_state(s.batch, s.nheads, s.headdim, s.dstate, s.rank, x.device, _rotated(s))
-    st_in = _state(s, init, x.device, "init")
-    st_out = _state(s, final, x.device, "final")
-    need = int(lib.m3_scan_workspace_bytes(ctypes.byref(s)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    _need(workspace, "workspace", torch.uint8, x.device)
-    f = lib.m3_scan_mimo if mimo else lib.m3_scan_siso
-    rc = f(ctypes.byref(s), ctypes.byref(inp), _ptr(y),
-           ctypes.byref(st_in) if st_in is not None else None,
-           ctypes.byref(st_out) if st_out is not None else None,
-           _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+    with _alloc_on(stream):
+        if y is None:
+            y = torch.empty_like(x)
+        else:
+            _need(y, "y", x.dtype, x.device, tuple(x.shape))
+        if final is True:
+            final = new_state(s.batch, s.nheads, s.headdim, s.dstate, s.rank, x.device, _rotated(s))
+        st_in = _state(s, init, x.device, "init")
+        st_out = _state(s, final, x.device, "final")
+        need = int(lib.m3_scan_workspace_bytes(ctypes.byref(s)))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        _need(workspace, "workspace", torch.uint8, x.device)
+        f = lib.m3_scan_mimo if mimo else lib.m3_scan_siso
+        rc = f(ctypes.byref(s), ctypes.byref(inp), _ptr(y),
+               ctypes.byref(st_in) if st_in is not None else None,
+               ctypes.byref(st_out) if st_out is not None else None,
+               _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
     _check(rc, "m3_scan_mimo" if mimo else "m3_scan_siso")
     return (y, final) if final is not None else y
 
@@ -275,10 +287,11 @@ def m3_step(x, B, C, dt, lam, theta, A, D, state, *, bcnorm=True, eps=1e-5, b_no
     _need(x, "x", x.dtype, x.device)
     inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
                   dt_bias, z)
-    if y is None:
-        y = torch.empty_like(x)
-    else:
-        _need(y, "y", x.dtype, x.device, tuple(x.shape))
+    with _alloc_on(stream):
+        if y is None:
+            y = torch.empty_like(x)
+        else:
+            _need(y, "y", x.dtype, x.device, tuple(x.shape))
     st = _state(s, state, x.device, "state")
     rc = lib.m3_step(ctypes.byref(s), ctypes.byref(inp), _ptr(y), ctypes.byref(st), _stream(stream))
     _check(rc, "m3_step")
@@ -311,6 +324,13 @@ def m3_scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5, b_n
     _need(dy, "dy", x.dtype, x.device, tuple(x.shape))
     dev, f32 = x.device, torch.float32
     H, N, R = s.nheads, s.dstate, s.rank
+    with _alloc_on(stream):
+        return _bwd_call(lib, s, inp, x, B, C, dt, lam, theta, A, D, dy, z, init, dfinal, workspace, stream,
+                         dev, f32, H, N, R)
+
+
+def _bwd_call(lib, s, inp, x, B, C, dt, lam, theta, A, D, dy, z, init, dfinal, workspace, stream, dev, f32,
+              H, N, R):
     g = dict(x=torch.empty_like(x), B=torch.empty_like(B), C=torch.empty_like(C),
              dt=torch.empty_like(dt), lam=torch.empty_like(lam), theta=torch.empty_like(theta),
              A=torch.empty_like(A), D=torch.empty_like(D),

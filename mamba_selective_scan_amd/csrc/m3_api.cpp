@@ -150,8 +150,10 @@ Plan plan_of(const m3_shape *s) {
     return pl;
 }
 
-m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_state *init,
-                    m3_state *fin, void *ws, size_t ws_bytes, void *stream, bool mimo) {
+// Every argument check of a scan call but the workspace size (the half-split path runs these
+// before its first permutation launch).
+m3_status validate_scan(const m3_shape *s, const m3_inputs *in, const void *y, const m3_state *init,
+                        const m3_state *fin, const void *ws, bool mimo) {
     m3_status rc = check_shape(s, false);
     if (rc != M3_OK) return rc;
     if (!mimo && s->rank != 1) return M3_EINVAL;
@@ -165,9 +167,18 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     const bool bf = s->io == M3_BF16;
     if (m3::seg_kernel_lds_bytes(true, bf, ts) > 160 * 1024 || m3::seg_kernel_lds_bytes(false, bf, ts) > 160 * 1024)
         return M3_EUNSUPPORTED;
+    if (!aligned16(ws)) return M3_EINVAL;
+    return M3_OK;
+}
+
+m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_state *init,
+                    m3_state *fin, void *ws, size_t ws_bytes, void *stream, bool mimo) {
+    m3_status rc = validate_scan(s, in, y, init, fin, ws, mimo);
+    if (rc != M3_OK) return rc;
+    const TileShape ts = tile_of(s);
+    const bool bf = s->io == M3_BF16;
     const Plan pl = plan_of(s);
     if (pl.total > 0 && (!ws || ws_bytes < pl.total)) return M3_EWORKSPACE;
-    if (!aligned16(ws)) return M3_EINVAL;
 
     ScanParams p;
     std::memset(&p, 0, sizeof p);
@@ -269,8 +280,9 @@ BwdPlan bwd_plan_of(const m3_shape *s) {
     return pl;
 }
 
-m3_status bwd_impl(const m3_shape *s, const m3_inputs *in, const void *dy, const m3_state *init,
-                   const m3_state *dfin, m3_grads *g, m3_state *dinit, void *ws, size_t ws_bytes, void *stream) {
+// Every argument check of a gradient call but the workspace size.
+m3_status validate_bwd(const m3_shape *s, const m3_inputs *in, const void *dy, const m3_state *init,
+                       const m3_state *dfin, const m3_grads *g, const m3_state *dinit, const void *ws) {
     m3_status rc = check_shape(s, false);
     if (rc != M3_OK) return rc;
     const int nr = rotated_pairs(s);
@@ -286,9 +298,17 @@ m3_status bwd_impl(const m3_shape *s, const m3_inputs *in, const void *dy, const
                           g->dc_norm_w, g->db_bias, g->dc_bias, g->ddt_bias, g->dz};
     for (const void *q : ptrs)
         if (!aligned16(q)) return M3_EINVAL;
+    if (!aligned16(ws)) return M3_EINVAL;
+    return M3_OK;
+}
+
+m3_status bwd_impl(const m3_shape *s, const m3_inputs *in, const void *dy, const m3_state *init,
+                   const m3_state *dfin, m3_grads *g, m3_state *dinit, void *ws, size_t ws_bytes, void *stream) {
+    m3_status rc = validate_bwd(s, in, dy, init, dfin, g, dinit, ws);
+    if (rc != M3_OK) return rc;
+    const int nr = rotated_pairs(s);
     const BwdPlan pl = bwd_plan_of(s);
     if (pl.total > 0 && (!ws || ws_bytes < pl.total)) return M3_EWORKSPACE;
-    if (!aligned16(ws)) return M3_EINVAL;
     if (s->batch == 0) return M3_OK;
     m3::BwdParams p;
     std::memset(&p, 0, sizeof p);
@@ -407,15 +427,19 @@ HsLayout hs_layout(const m3_shape *s, bool bwd) {
     return l;
 }
 
+// A call with no tokens (or no batch) only copies the state, which does not depend on the
+// pairing: no workspace, also with the half-split pairing.
+bool no_tokens(const m3_shape *s) { return s->seqlen == 0 || s->batch == 0; }
+
 size_t scan_ws_bytes(const m3_shape *s) {
-    if (!(s->flags & M3_FLAG_HALF_SPLIT)) return plan_of(s).total;
+    if (!(s->flags & M3_FLAG_HALF_SPLIT) || no_tokens(s)) return plan_of(s).total;
     m3_shape s2 = *s;
     s2.flags &= ~M3_FLAG_HALF_SPLIT;
     return align_up(plan_of(&s2).total) + hs_layout(s, false).total;
 }
 
 size_t bwd_ws_bytes(const m3_shape *s) {
-    if (!(s->flags & M3_FLAG_HALF_SPLIT)) return bwd_plan_of(s).total;
+    if (!(s->flags & M3_FLAG_HALF_SPLIT) || no_tokens(s)) return bwd_plan_of(s).total;
     m3_shape s2 = *s;
     s2.flags &= ~M3_FLAG_HALF_SPLIT;
     return align_up(bwd_plan_of(&s2).total) + hs_layout(s, true).total;
@@ -444,19 +468,19 @@ struct HsPerm {
 
 m3_status scan_half_split(const m3_shape *s, const m3_inputs *in, void *y, const m3_state *init, m3_state *fin,
                           void *ws, size_t ws_bytes, void *stream, bool mimo) {
-    m3_status rc = check_shape(s, false);
+    m3_status rc = validate_scan(s, in, y, init, fin, ws, mimo);
     if (rc != M3_OK) return rc;
-    const int nr = rotated_pairs(s);
-    if ((rc = check_inputs(in, s->seqlen > 0 && s->batch > 0, nr)) != M3_OK) return rc;
-    if ((rc = check_state(init, false, nr)) != M3_OK) return rc;
-    if ((rc = check_state(fin, false, nr)) != M3_OK) return rc;
-    if (s->batch == 0) return M3_OK;
+    if (no_tokens(s)) {
+        // only the state is copied (element by element): the pairing does not matter
+        m3_shape s1 = *s;
+        s1.flags &= ~M3_FLAG_HALF_SPLIT;
+        return scan_impl(&s1, in, y, init, fin, ws, ws_bytes, stream, mimo);
+    }
     m3_shape s2 = *s;
     s2.flags &= ~M3_FLAG_HALF_SPLIT;
     const size_t base = align_up(plan_of(&s2).total);
     HsPerm hp{s, nullptr, hs_layout(s, false), reinterpret_cast<hipStream_t>(stream)};
     if (!ws || ws_bytes < base + hp.hl.total) return M3_EWORKSPACE;
-    if (!aligned16(ws)) return M3_EINVAL;
     hp.w = static_cast<char *>(ws) + base;
     const int64_t BTH = s->batch * s->seqlen * (int64_t)s->nheads, BH = s->batch * (int64_t)s->nheads;
     const int R = s->rank, P = s->headdim, H = s->nheads, es = s->io == M3_BF16 ? 2 : 4;
@@ -493,21 +517,19 @@ m3_status scan_half_split(const m3_shape *s, const m3_inputs *in, void *y, const
 m3_status bwd_half_split(const m3_shape *s, const m3_inputs *in, const void *dy, const m3_state *init,
                          const m3_state *dfin, m3_grads *g, m3_state *dinit, void *ws, size_t ws_bytes,
                          void *stream) {
-    m3_status rc = check_shape(s, false);
+    m3_status rc = validate_bwd(s, in, dy, init, dfin, g, dinit, ws);
     if (rc != M3_OK) return rc;
-    const int nr = rotated_pairs(s);
-    if ((rc = check_inputs(in, s->seqlen > 0 && s->batch > 0, nr)) != M3_OK) return rc;
-    if ((rc = check_state(init, false, nr)) != M3_OK) return rc;
-    if ((rc = check_state(dfin, false, nr)) != M3_OK) return rc;
-    if ((rc = check_state(dinit, false, nr)) != M3_OK) return rc;
-    if (!g) return M3_EINVAL;
-    if (s->batch == 0) return M3_OK;
+    if (no_tokens(s)) {
+        // the gradients pass through element by element: the pairing does not matter
+        m3_shape s1 = *s;
+        s1.flags &= ~M3_FLAG_HALF_SPLIT;
+        return bwd_impl(&s1, in, dy, init, dfin, g, dinit, ws, ws_bytes, stream);
+    }
     m3_shape s2 = *s;
     s2.flags &= ~M3_FLAG_HALF_SPLIT;
     const size_t base = align_up(bwd_plan_of(&s2).total);
     HsPerm hp{s, nullptr, hs_layout(s, true), reinterpret_cast<hipStream_t>(stream)};
     if (!ws || ws_bytes < base + hp.hl.total) return M3_EWORKSPACE;
-    if (!aligned16(ws)) return M3_EINVAL;
     hp.w = static_cast<char *>(ws) + base;
     const int64_t BTH = s->batch * s->seqlen * (int64_t)s->nheads, BH = s->batch * (int64_t)s->nheads;
     const int R = s->rank, P = s->headdim, H = s->nheads, es = s->io == M3_BF16 ? 2 : 4;

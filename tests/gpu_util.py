@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import math
+import os
 import sys
 
 import numpy as np
@@ -20,6 +21,16 @@ BF16_HALF_ULP = 2.0 ** -8
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+# Achieved errors of every compared output, kept for the summary printed at the end of the
+# session: (test id, quantity, raw max|err|/rms, compute error or None).
+RECORDS = []
+
+
+def record(quantity, raw, comp=None):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    RECORDS.append((test, quantity, float(raw), None if comp is None else float(comp)))
 
 
 def to_dev(inp: dict, io: str, device="cuda"):

@@ -177,3 +177,46 @@ def test_status_strings():
                       (4, "M3_EHIP")):
         assert m3.m3_status_str(code).startswith(tag)
     assert "unknown" in m3.m3_status_str(99)
+
+
+def test_half_split_checks_before_any_launch():
+    """A half-split call permutes B, C and the state into the workspace before the scan
+    kernels run; every argument check (output pointer, workspace alignment, the gate's
+    gradient) comes before the first of those launches, so on this GPU-less host a bad
+    argument reports M3_EINVAL, not a launch failure."""
+    m3, lib = _lib()
+    sh = _shape(m3, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_HALF_SPLIT, seqlen=64)
+    assert _call_scan(m3, lib, sh, y=False) == 1                      # no output
+    _, ptrs = _fake_inputs(m3)
+    inp = m3._Inputs(**ptrs)
+    mis = ctypes.c_void_p(ptrs["x"].value + 8)
+    big = m3.m3_scan_workspace_bytes(sh) + 4096
+    rc = lib.m3_scan_siso(ctypes.byref(sh), ctypes.byref(inp), ptrs["x"], None, None, mis,
+                          ctypes.c_size_t(big), None)
+    assert rc == 1                                                    # misaligned workspace
+    # a gated gradient call without dz
+    ptrs_z = dict(ptrs, z=ptrs["x"])
+    inz = m3._Inputs(**ptrs_z)
+    gr = m3._Grads(dx=ptrs["x"])
+    bws = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(sh)) + 4096
+    rc = lib.m3_scan_bwd(ctypes.byref(sh), ctypes.byref(inz), ptrs["x"], None, None, ctypes.byref(gr), None,
+                         ptrs["x"], ctypes.c_size_t(bws), None)
+    assert rc == 1
+
+
+def test_half_split_empty_needs_no_workspace():
+    """With no tokens (or no batch) a call only copies the state, whatever the pairing: the
+    workspace size is 0 for the scans and the gradient call."""
+    m3, lib = _lib()
+    for kw in (dict(seqlen=0), dict(batch=0)):
+        sh = _shape(m3, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_HALF_SPLIT, **kw)
+        assert lib.m3_scan_workspace_bytes(ctypes.byref(sh)) == 0
+        assert lib.m3_scan_bwd_workspace_bytes(ctypes.byref(sh)) == 0
+        s = _shape(m3, **kw)
+        assert lib.m3_scan_workspace_bytes(ctypes.byref(s)) == 0
+    # B == 0 with no workspace at all succeeds without touching the device
+    sh = _shape(m3, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_HALF_SPLIT, batch=0)
+    _, ptrs = _fake_inputs(m3)
+    inp = m3._Inputs(**ptrs)
+    assert lib.m3_scan_siso(ctypes.byref(sh), ctypes.byref(inp), ptrs["x"], None, None, None,
+                            ctypes.c_size_t(0), None) == 0

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from synth import custom, make_block_inputs, make_inputs, make_norm_params, make_state
-from tests.gpu_util import angle_err, err_metrics, gate, log, state_to_dev, to_np
+from tests.gpu_util import angle_err, err_metrics, gate, log, record, state_to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,7 @@ def to_gpu(data, g_kw, io):
 def check(name, y_gpu, y_ref, io):
     raw, comp = err_metrics(to_np(y_gpu), y_ref, io)
     log(f"  {name}: raw max|err|/rms = {raw:.3e}, compute err = {comp:.3e} (gate {gate(io):.0e})")
+    record(name, raw, comp if io == "bf16" else None)
     assert comp <= gate(io), f"{name}: {comp:.3e}"
 
 
@@ -81,11 +82,13 @@ def check_state(fin_gpu, fin_ref, io):
     for k in ("h", "prev_B", "prev_x"):
         raw, _ = err_metrics(to_np(fin_gpu[k]), fin_ref[k], "f32")
         log(f"  final {k}: max|err|/rms = {raw:.3e}")
+        record(f"final {k}", raw)
         assert raw <= (1e-4 if io == "f32" else 2e-3), k
     assert fin_gpu["angle"].shape == fin_ref["angle"].shape
     if fin_ref["angle"].size:
         ae = angle_err(to_np(fin_gpu["angle"]), fin_ref["angle"])
         log(f"  final angle: max wrapped err/rms = {ae:.3e}")
+        record("final angle (wrapped)", ae)
         assert ae <= 1e-4
 
 
@@ -238,6 +241,7 @@ def test_split_schedule_half_split(R, P, N, io):
     check_state(state, f_ref, io)
 
 
+@pytest.mark.fullsize
 @pytest.mark.parametrize("opts,nr", [(("rope", "atok", "softplus", "sigmoid", "gate"), 16), (("half",), None)])
 def test_options_full_workload(opts, nr):
     """The headline workload (batch 4, T 2048, 16 heads, P = N = 64, bf16) with the option sets

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from synth import custom, make_block_inputs, make_inputs, make_norm_params, make_state
-from tests.gpu_util import log
+from tests.gpu_util import log, record
 
 pytestmark = pytest.mark.gpu
 
@@ -106,11 +106,13 @@ def run_case(w, *, opts=(), nr=None, init=True, dfinal=True, npar=True, bcnorm=T
         got = g[k].float().cpu().numpy()
         e = _err(got, ref[k], w.io == "bf16" and k in ("x", "B", "C", "z"))
         log(f"  d{k}: {e:.3e}")
+        record(f"d{k}", e)
         if not e <= GATE:
             bad.append((k, e))
     for k in ("h", "prev_B", "prev_x", "angle"):
         e = _err(g["init"][k].cpu().numpy(), ref["init"][k], False)
         log(f"  dinit.{k}: {e:.3e}")
+        record(f"dinit.{k}", e)
         if not e <= GATE:
             bad.append(("init." + k, e))
     assert not bad, bad
@@ -179,6 +181,7 @@ def test_bwd_empty_sequence():
     assert float(g["D"].abs().sum()) == 0.0 and float(g["A"].abs().sum()) == 0.0
 
 
+@pytest.mark.fullsize
 @pytest.mark.parametrize("opts", [("rope", "atok", "act", "gate"), ("half",)])
 def test_bwd_full_workload_options(opts):
     """Gradients at the headline workload's full size with every canonical-block option (16 of
@@ -187,6 +190,7 @@ def test_bwd_full_workload_options(opts):
     run_case(WORKLOADS[1], opts=opts, nr=16 if "rope" in opts else None)
 
 
+@pytest.mark.fullsize
 @pytest.mark.parametrize("k", [1, 2, 3])
 def test_bwd_full_workloads(k):
     """The bench workloads at full size (SISO config, MIMO rank 4, the 16384-token N 128 one):
@@ -221,11 +225,13 @@ def test_bwd_full_workloads(k):
     for name in ("x", "B", "C", "dt", "lam", "theta", "A", "D", "b_bias", "c_bias", "b_norm_w", "c_norm_w"):
         e = _err(g[name].float().cpu().numpy(), ref[name], w.io == "bf16" and name in ("x", "B", "C"))
         log(f"  d{name}: {e:.3e}")
+        record(f"d{name}", e)
         if not e <= GATE:
             bad.append((name, e))
     for name in ("h", "prev_B", "prev_x", "angle"):
         e = _err(g["init"][name].cpu().numpy(), ref["init"][name], False)
         log(f"  dinit.{name}: {e:.3e}")
+        record(f"dinit.{name}", e)
         if not e <= GATE:
             bad.append(("init." + name, e))
     assert not bad, bad
