@@ -224,6 +224,26 @@ m3_status m3_scan_bwd(const m3_shape *shape, const m3_inputs *in, const void *dy
                       const m3_state *dfinal, m3_grads *grads, m3_state *dinit, void *ws, size_t ws_bytes,
                       void *stream);
 
+/*
+ * Allocation-free variant of m3_scan_mimo (any rank R >= 1; R == 1 is the SISO scan), for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * m3_scan_mimo, but no workspace argument: the workspace is the library's own static
+ * device array of M3_STATIC_SCRATCH_BYTES bytes (one per GPU, held from the library's
+ * first call on that GPU until the process ends; its address is looked up once per device).
+ * The call allocates nothing and frees nothing.
+ *   - A shape whose m3_scan_workspace_bytes() exceeds M3_STATIC_SCRATCH_BYTES gives
+ *     M3_EWORKSPACE (64 MiB holds e.g. batch 4 x T 2048 x 16 heads at P = N = 64 with any
+ *     rank up to 4, and T 16384 x 32 heads at N 128).
+ *   - Every call on a GPU shares that GPU's one scratch array: two calls that may overlap in
+ *     time on the same GPU (different streams, or different host threads without ordering)
+ *     race on it and give wrong results.  Order them on one stream.  The scratch needs no
+ *     clearing (its contents on entry do not matter).
+ */
+#define M3_STATIC_SCRATCH_BYTES (64u << 20)
+m3_status m3_scan_noalloc(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,
+                          m3_state *final, void *stream);
+
 /* Static description of a status code. */
 const char *m3_status_str(m3_status status);
 

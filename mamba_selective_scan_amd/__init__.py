@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["m3_scan_siso", "m3_scan_mimo", "m3_step", "m3_scan_bwd", "m3_scan_workspace_bytes",
+__all__ = ["m3_scan_siso", "m3_scan_mimo", "m3_step", "m3_scan_bwd", "m3_scan_noalloc", "m3_scan_workspace_bytes",
            "m3_scan_bwd_workspace_bytes",
            "m3_status_str", "Shape", "M3_F32", "M3_BF16", "M3_FLAG_BCNORM", "M3_FLAG_PARTIAL_ROPE",
            "M3_FLAG_A_PER_TOKEN", "M3_FLAG_DT_SOFTPLUS", "M3_FLAG_LAM_SIGMOID", "M3_FLAG_HALF_SPLIT", "lib_path",
@@ -32,6 +32,7 @@ M3_FLAG_A_PER_TOKEN = 1 << 2
 M3_FLAG_DT_SOFTPLUS = 1 << 3
 M3_FLAG_LAM_SIGMOID = 1 << 4
 M3_FLAG_HALF_SPLIT = 1 << 5
+M3_STATIC_SCRATCH_BYTES = 64 << 20
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmamba3.so")
 
@@ -80,6 +81,9 @@ def load():
             f.argtypes = [P(Shape), P(_Inputs), ctypes.c_void_p, P(_State), P(_State),
                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
             f.restype = ctypes.c_int
+        lib.m3_scan_noalloc.argtypes = [P(Shape), P(_Inputs), ctypes.c_void_p, P(_State), P(_State),
+                                        ctypes.c_void_p]
+        lib.m3_scan_noalloc.restype = ctypes.c_int
         lib.m3_step.argtypes = [P(Shape), P(_Inputs), ctypes.c_void_p, P(_State), ctypes.c_void_p]
         lib.m3_step.restype = ctypes.c_int
         lib.m3_scan_bwd_workspace_bytes.argtypes = [P(Shape)]
@@ -252,6 +256,35 @@ def _scan(mimo, x, B, C, dt, lam, theta, A, D, *, chunk=64, bcnorm=True, eps=1e-
                ctypes.byref(st_out) if st_out is not None else None,
                _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
     _check(rc, "m3_scan_mimo" if mimo else "m3_scan_siso")
+    return (y, final) if final is not None else y
+
+
+def m3_scan_noalloc(x, B, C, dt, lam, theta, A, D, *, y, chunk=64, bcnorm=True, eps=1e-5,
+                    b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, init=None, final=None,
+                    stream=None, rope_pairs=None, dt_softplus=False, dt_bias=None, lam_sigmoid=False,
+                    z=None, half_split=False):
+    """The allocation-free scan (any rank: x [B,T,H,P] is rank 1, [B,T,H,P,R] rank R) with the
+    library's static scratch as workspace.  The caller passes the output ``y`` and, to get the
+    final state, ``final`` (a state dict as from ``new_state``); nothing is allocated here or
+    in the library, so the call may run under HIP graph capture."""
+    lib = load()
+    mimo = x.dim() == 5
+    s = _shape_of(x, B, chunk, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A, dt_softplus=dt_softplus,
+                                                        lam_sigmoid=lam_sigmoid, half_split=half_split))
+    _need(x, "x", x.dtype, x.device)
+    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo, dt_bias, z)
+    _need(y, "y", x.dtype, x.device, tuple(x.shape))
+    st_in = _state(s, init, x.device, "init")
+    st_out = _state(s, final, x.device, "final")
+    rc = lib.m3_scan_noalloc(ctypes.byref(s), ctypes.byref(inp), _ptr(y),
+                             ctypes.byref(st_in) if st_in is not None else None,
+                             ctypes.byref(st_out) if st_out is not None else None, _stream(stream))
+    if rc == 3:
+        need = int(lib.m3_scan_workspace_bytes(ctypes.byref(s)))
+        raise RuntimeError(f"m3_scan_noalloc: this shape needs {need} bytes of workspace, more than the "
+                           f"library's static scratch ({M3_STATIC_SCRATCH_BYTES} bytes); use m3_scan_mimo "
+                           "with a workspace")
+    _check(rc, "m3_scan_noalloc")
     return (y, final) if final is not None else y
 
 

@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/libmamba3.h"
 #include "m3_internal.hpp"
@@ -584,9 +585,46 @@ m3_status bwd_half_split(const m3_shape *s, const m3_inputs *in, const void *dy,
     return hp.e == hipSuccess ? M3_OK : M3_EHIP;
 }
 
+// ---------------------------------------------------------------- library-owned scratch
+// The workspace of m3_scan_noalloc: a file-scope device array, one copy per GPU, held by the
+// loaded code object until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[M3_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch (looked up on the device's first call), or NULL.
+void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+m3_status m3_scan_noalloc(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,
+                          m3_state *final, void *stream) {
+    // every argument check first, with the scratch standing in for the workspace
+    m3_status rc = validate_scan(shape, in, y, init, final, nullptr, true);
+    if (rc != M3_OK) return rc;
+    if (scan_ws_bytes(shape) > (size_t)M3_STATIC_SCRATCH_BYTES) return M3_EWORKSPACE;
+    void *ws = device_scratch();
+    if (!ws) return M3_EHIP;
+    if (shape->flags & M3_FLAG_HALF_SPLIT)
+        return scan_half_split(shape, in, y, init, final, ws, M3_STATIC_SCRATCH_BYTES, stream, true);
+    return scan_impl(shape, in, y, init, final, ws, M3_STATIC_SCRATCH_BYTES, stream, true);
+}
 
 size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape) {
     if (!shape || shape->seqlen < 0 || shape->batch < 0 || shape->nheads < 1 || shape->headdim < 1 ||

@@ -220,3 +220,20 @@ def test_half_split_empty_needs_no_workspace():
     inp = m3._Inputs(**ptrs)
     assert lib.m3_scan_siso(ctypes.byref(sh), ctypes.byref(inp), ptrs["x"], None, None, None,
                             ctypes.c_size_t(0), None) == 0
+
+
+def test_noalloc_rejects_shapes_beyond_static_scratch():
+    """m3_scan_noalloc checks every argument, then that the shape's workspace fits the
+    library's static scratch, before touching the device (this host has none)."""
+    m3, lib = _lib()
+    _, ptrs = _fake_inputs(m3)
+    inp = m3._Inputs(**ptrs)
+    # the half-split pairing puts permuted copies of B and C into the workspace: 2 x 67 MB here
+    big = _shape(m3, batch=16, seqlen=4096, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_HALF_SPLIT)
+    assert m3.m3_scan_workspace_bytes(big) > m3.M3_STATIC_SCRATCH_BYTES
+    assert lib.m3_scan_noalloc(ctypes.byref(big), ctypes.byref(inp), ptrs["x"], None, None, None) == 3
+    assert lib.m3_scan_noalloc(ctypes.byref(_shape(m3, dstate=63)), ctypes.byref(inp), ptrs["x"], None, None,
+                               None) == 1
+    assert lib.m3_scan_noalloc(ctypes.byref(_shape(m3)), ctypes.byref(inp), None, None, None, None) == 1
+    text = open(HEADER).read()
+    assert f"#define M3_STATIC_SCRATCH_BYTES (64u << 20)" in text and m3.M3_STATIC_SCRATCH_BYTES == 64 << 20
