@@ -88,6 +88,37 @@ __device__ __forceinline__ f32x4_t mma(const FragF &a, const FragF &b, f32x4_t c
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- fp16 operands
+// A single fp16 operand (8 halves per lane, same lane layout as the bf16 MFMA).  Used for the
+// normalised, rotated B~ and C~ and for the carried state H, each held within the fp16 range
+// by a power-of-two scale that the caller undoes after the product (scales are exact).
+struct FragH { u32x4_t v; };
+__device__ __forceinline__ f32x4_t mfma_h(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                  c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma(const FragH &a, const FragH &b, f32x4_t c) { return mfma_h(a.v, b.v, c); }
+// two floats -> packed fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+// acc + the squares of the two bf16 halves of w (one v_dot2 instruction)
+__device__ __forceinline__ float sumsq2_bf16(uint32_t w, float acc) {
+    const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w);
+    return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+// 2^(k - e) and 2^(e - k) for the exponent e of m (m = f 2^e, f in [0.5, 1)): a power of two
+// that maps m into [2^(k-1), 2^k), and its inverse; (1, 1) for m == 0 or a non-finite m
+template <int K>
+__device__ __forceinline__ void pow2_scale(float m, float &s, float &inv) {
+    const int e = __builtin_amdgcn_frexp_expf(m);
+    const bool ok = m > 0.f && m < 3.0e38f;
+    s = ok ? __builtin_ldexpf(1.f, K - e) : 1.f;
+    inv = ok ? __builtin_ldexpf(1.f, e - K) : 1.f;
+}
 
 // two floats -> packed bf16 words hi = rne(v), lo = rne(v - hi) (one v_cvt_pk_bf16_f32 each)
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {

@@ -76,8 +76,9 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// The 16-row tile of a block that this wave owns.
-__device__ __forceinline__ int row_tile() { return threadIdx.x >> 6; }
+// The 16-row tile of a block that this wave owns (wave-uniform: held in a scalar register, so
+// that loops and branches on it are scalar).
+__device__ __forceinline__ int row_tile() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Load paths (the MODE of a kernel variant):
 //   kModeGen : any rank, any even N, any P; element loads.
@@ -105,6 +106,16 @@ struct SegCfg {
     static constexpr int TPW = (PT * NT + 3) / 4;  // state tiles per wave
     static constexpr int ES = BF ? 2 : 4;          // bytes per operand element per plane
     static constexpr int NPL = BF ? 2 : 1;         // planes: (hi, lo) or (fp32)
+    // bf16 I/O: B~, C~ and H are single fp16 operands (power-of-two scaled); (w B~)^T, G o L
+    // and X stay bf16 hi/lo (X exact).  The interleaved-rank path stages raw B and C in two
+    // planes of the B~ area, so that area keeps two planes there.
+    static constexpr bool F16 = BF;
+    static constexpr int NPL_BT = F16 ? (MV ? 2 : 1) : NPL;
+    static constexpr int NPL_HT = F16 ? 1 : NPL;
+    // Column-owned outputs (rank-1 bf16 path with 64 columns): wave w computes Y^T for columns
+    // 16w .. 16w + 15 and every row of the block, from the state columns it holds and from
+    // G o L tiles computed once (spread evenly over the waves) and shared through LDS.
+    static constexpr bool COL = VEC && F16 && PP == 64;
     static constexpr int PADE = BF ? 8 : 4;        // 16 bytes of padding per row
     static constexpr int OPP = NP + PADE;          // pitch of [row][n] and [p][n]
     static constexpr int RPP = ROWS + PADE;        // pitch of [p][row] and [n][row]
@@ -124,23 +135,29 @@ struct SegCfg {
     static constexpr size_t BT_PLANE = (size_t)ROWS * OPP;  // elements per plane
     static constexpr size_t WB_PLANE = (size_t)NP * RPP;
     static constexpr size_t HT_PLANE = (size_t)PP * OPP;
-    static constexpr size_t L_BT = al(BT_PLANE * ES * NPL);
+    static constexpr size_t L_BT = al(BT_PLANE * ES * NPL_BT);
     static constexpr size_t L_WB = al(WB_PLANE * ES * NPL);
     static constexpr size_t L_XT = al((size_t)PP * RPP * ES);
-    static constexpr size_t L_HT = al(HT_PLANE * ES * NPL);
-    static constexpr size_t L_Y = al((size_t)ROWS * PP * sizeof(ET));
+    static constexpr size_t L_HT = COL ? 0 : al(HT_PLANE * ES * NPL_HT);
+    static constexpr size_t L_Y = COL ? 0 : al((size_t)ROWS * PP * sizeof(ET));
+    // COL: the C~ plane [row][n] (fp16) and the G o L planes [t][s] (bf16 hi, lo)
+    static constexpr size_t L_CT = COL ? al(BT_PLANE * 2) : 0;
+    static constexpr size_t GL_PLANE = (size_t)ROWS * RPP;
+    static constexpr size_t L_GL = COL ? al(GL_PLANE * 2 * 2) : 0;
     // angles: the general path keeps a table [token][pair]; the SISO path only tile totals [4][pair]
     static constexpr size_t L_PHI = al(VEC ? (size_t)4 * (NP / 2) * 4 : (size_t)TOKS * PHP * 4);
-    // scalars: cs, scale, gamma, w, exp(cs) [ROWS]; scan scratch [256 + 8];
-    // per pair: block angle total, its cos and sin; per pair (double): running angle base
-    static constexpr size_t L_SC0 = al((5 * ROWS + 264 + 3 * (NP / 2)) * 4);
+    // scalars: per pair (cos, sin) of the block angle total [NP/2][2] (padded pairs (1, 0));
+    // cs, scale, gamma, w, exp(cs), u (factored mask) [ROWS]; inverse row scales of B~ and
+    // C~ [2][ROWS]; scan scratch [256 + 8]; per pair the block angle total; per wave the
+    // largest |H|; per pair (double): running angle base
+    static constexpr size_t L_SC0 = al((NP + 8 * ROWS + 264 + NP / 2 + 4) * 4);
     static constexpr size_t L_SC = L_SC0 + (size_t)(NP / 2) * 8;
     // MV state kernel: raw B regrouped per rank, [row][n] (the output kernel uses the B~ planes)
     static constexpr size_t L_RAW = MV ? al((size_t)ROWS * OPP * 2) : 0;
     // rank-1 path: norm gains and this head's biases for B and C, [4][NP] (1 and 0 when absent)
     static constexpr size_t L_AFF = VEC ? al((size_t)4 * NP * 4) : 0;
     static constexpr size_t STATE_BYTES = L_WB + L_XT + L_PHI + L_SC + L_RAW + L_AFF;
-    static constexpr size_t OUTPUT_BYTES = L_BT + L_WB + L_XT + L_HT + L_Y + L_PHI + L_SC + L_AFF;
+    static constexpr size_t OUTPUT_BYTES = L_BT + L_CT + L_GL + L_WB + L_XT + L_HT + L_Y + L_PHI + L_SC + L_AFF;
 };
 
 // Raw inputs of one block, prefetched into registers.  With VEC the words are
@@ -206,12 +223,18 @@ __device__ __forceinline__ BlockGeo block_geo(const ScanParams &p, int blk) {
 // LDS carve-up
 template <class Cfg, bool OUT>
 struct Smem {
-    unsigned char *bt, *wb, *xt, *ht, *ys, *phi, *raw;
-    float *cs, *scale, *gam, *w, *ecs, *tmp, *pend, *cph, *sph, *aff;
+    unsigned char *bt, *ct, *gl, *wb, *xt, *ht, *ys, *phi, *raw;
+    float *csr, *cs, *scale, *gam, *w, *ecs, *u, *isr, *tmp, *pend, *hmax, *aff;
     double *base;
     __device__ __forceinline__ explicit Smem(unsigned char *s) {
         unsigned char *q = s;
-        if (OUT) { bt = q; q += Cfg::L_BT; } else { bt = nullptr; }
+        if (OUT) {
+            bt = q; q += Cfg::L_BT;
+            ct = q; q += Cfg::L_CT;
+            gl = q; q += Cfg::L_GL;
+        } else {
+            bt = ct = gl = nullptr;
+        }
         wb = q; q += Cfg::L_WB;
         xt = q; q += Cfg::L_XT;
         if (OUT) { ht = q; q += Cfg::L_HT; ys = q; q += Cfg::L_Y; } else { ht = nullptr; ys = nullptr; }
@@ -219,9 +242,11 @@ struct Smem {
         raw = nullptr;
         if (!OUT && Cfg::MV) { raw = q; q += Cfg::L_RAW; }
         float *f = (float *)q;
-        cs = f; scale = cs + Cfg::ROWS; gam = scale + Cfg::ROWS; w = gam + Cfg::ROWS; ecs = w + Cfg::ROWS;
-        tmp = ecs + Cfg::ROWS;
-        pend = tmp + 264; cph = pend + Cfg::NP / 2; sph = cph + Cfg::NP / 2;
+        csr = f;  // 16-byte aligned: (cos, sin) of pairs 2k, 2k + 1 are one f32x4
+        cs = csr + Cfg::NP; scale = cs + Cfg::ROWS; gam = scale + Cfg::ROWS; w = gam + Cfg::ROWS;
+        ecs = w + Cfg::ROWS; u = ecs + Cfg::ROWS; isr = u + Cfg::ROWS;
+        tmp = isr + 2 * Cfg::ROWS;
+        pend = tmp + 264; hmax = pend + Cfg::NP / 2;
         base = (double *)(q + Cfg::L_SC0);
         aff = (float *)(q + Cfg::L_SC);
     }
@@ -252,6 +277,7 @@ struct WgCtx {
     int sx, sbc, sth, sdt;     // token strides in elements: H*P*R, H*N*R, H*nr, H
     float invN, eps;
     bool bcnorm, affine;
+    bool rowscale;  // fp16 B~ / C~ rows get a power-of-two scale each (no norm, or gains / biases)
 };
 
 __device__ __forceinline__ int tok_of(int row, const WgCtx &c) {
@@ -259,7 +285,12 @@ __device__ __forceinline__ int tok_of(int row, const WgCtx &c) {
 }
 
 // Issue the global loads of one block (nothing is converted so the loads stay in flight).
-template <class Io, class Cfg, bool WANT_C>
+// PART selects what: kLoadXs = x, dt, lambda (and the per-token A), consumed by the staging of
+// scalars and X^T; kLoadBc = B, C and theta, consumed by the prologue.  The rank-1 path issues
+// the two parts at different points (each as soon as its registers are free); the other
+// paths load everything with kLoadXs.
+constexpr int kLoadXs = 1, kLoadBc = 2, kLoadAll = 3;
+template <class Io, int PART = kLoadAll, class Cfg, bool WANT_C>
 __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const ScanParams &p, const WgCtx &c,
                                            const BlockGeo &g) {
     using ET = typename Io::T;
@@ -274,6 +305,7 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
         // SISO, N and P multiples of 8: row == token, 8 consecutive n per (lane, k step).
         // Uniform 64-bit block bases plus 32-bit per-lane byte offsets.
         const bool rv = row < g.Tv;
+        if constexpr ((PART & kLoadBc) != 0) {
         const char *bbase = (const char *)c.Bb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
         const char *cbase = (const char *)c.Cb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
         const char *tbase = (const char *)c.thb + (int64_t)g.t0 * c.sth * 4;
@@ -302,6 +334,8 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
 #pragma unroll
             for (int k = 0; k < 4; ++k) rb.th[kk * 4 + k] = tv[k];
         }
+        }
+        if constexpr ((PART & kLoadXs) != 0) {
         const char *xbase = (const char *)c.xb + (int64_t)g.t0 * c.sx * (int64_t)sizeof(ET);
 #pragma unroll
         for (int m = 0; m < Cfg::XN / 4; ++m) {
@@ -313,6 +347,9 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
 #pragma unroll
             for (int k = 0; k < 4; ++k) rb.x[m * 4 + k] = v[k];
         }
+        }
+    } else if constexpr ((PART & kLoadXs) == 0) {
+        // other paths: everything is loaded with the first part
     } else if constexpr (Cfg::MV) {
         // rank R in {2, 4, 8}: one token's B (C) is N*R contiguous values, n major, rank
         // minor; x is P*R.  16-byte vectors over every (token, vector) slot of the block;
@@ -390,7 +427,7 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
             rb.th[m] = (tr < g.Tv && pc < p.nr) ? p.theta[((b * T + g.t0 + tr) * H + h) * (int64_t)p.nr + pc] : 0.f;
         }
     }
-    if (wave == 0) {
+    if ((PART & kLoadXs) != 0 && wave == 0) {
         rb.dt = rb.lam = rb.dtn = rb.lamn = rb.av = 0.f;
         const float *db = c.dtb + (int64_t)g.t0 * c.sdt, *lb = c.lamb + (int64_t)g.t0 * c.sdt;
         const uint32_t o = (uint32_t)lane * (uint32_t)c.sdt;
@@ -585,6 +622,13 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
         sm.gam[lane] = ga;
         sm.ecs[lane] = __expf(cs);
         sm.w[lane] = __expf(cs_end - cs) * sc;
+        if constexpr (Cfg::VEC) {
+            // factored decay of the strictly causal tiles (s in an earlier 16-row tile than t):
+            // exp(cs_t - cs_s) scale_s = exp(cs_t - cs_ref) * u_s, u_s = exp(cs_ref - cs_s) scale_s,
+            // cs_ref the running sum at the last row of s's tile (both factors <= 1: cs falls)
+            const float cref = __shfl(cs, lane | 15, 64);
+            sm.u[lane] = __expf(cref - cs) * sc;
+        }
     }
     if constexpr (Cfg::VEC) {
         float *tt = (float *)sm.phi;  // [4 tiles][NP/2]
@@ -634,17 +678,19 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
         for (int m = 0; m < Cfg::XN / 4; ++m) {
             const int e = tid + 256 * m;
             const int xr = e / (Cfg::PP / Cfg::XW), pc = (e % (Cfg::PP / Cfg::XW)) * Cfg::XW;
+            // the XW columns pc .. pc + XW - 1 (pc a multiple of XW <= 8) share their swizzle:
+            // one base address, constant offsets
             if constexpr (Cfg::BF) {
-                uint16_t *xt = (uint16_t *)sm.xt;
+                uint16_t *xt = (uint16_t *)sm.xt + xt_off<Cfg>(pc, xr);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    xt[xt_off<Cfg>(pc + 2 * k, xr)] = (uint16_t)(rb.x[m * 4 + k] & 0xffffu);
-                    xt[xt_off<Cfg>(pc + 2 * k + 1, xr)] = (uint16_t)(rb.x[m * 4 + k] >> 16);
+                    xt[(2 * k) * Cfg::RPP] = (uint16_t)(rb.x[m * 4 + k] & 0xffffu);
+                    xt[(2 * k + 1) * Cfg::RPP] = (uint16_t)(rb.x[m * 4 + k] >> 16);
                 }
             } else {
-                float *xt = (float *)sm.xt;
+                float *xt = (float *)sm.xt + xt_off<Cfg>(pc, xr);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) xt[xt_off<Cfg>(pc + k, xr)] = __uint_as_float(rb.x[m * 4 + k]);
+                for (int k = 0; k < 4; ++k) xt[k * Cfg::RPP] = __uint_as_float(rb.x[m * 4 + k]);
             }
         }
     } else {
@@ -705,21 +751,32 @@ __device__ __forceinline__ void block_angle_totals(const Sm &sm, const ScanParam
         } else {
             a = ((const float *)sm.phi)[(g.Tv - 1) * Cfg::PHP + tid];
         }
-        float s, c;
-        { const f32x2_t sc_ = sincos_acc(a); s = sc_[0]; c = sc_[1]; }
+        const f32x2_t sc_ = sincos_acc(a);
         sm.pend[tid] = a;
-        sm.cph[tid] = c;
-        sm.sph[tid] = s;
+        *(f32x2_t *)(sm.csr + 2 * tid) = f32x2_t{sc_[1], sc_[0]};
     }
 }
 
-// Stage 3: B~ (and C~) for the rows this lane owns.  Writes B~ [row][n] (output
-// mode) and (w B~)^T [n][row] planes to LDS; returns C~ fragments.
+// (cos, sin) of the padded pairs N/2 .. NP/2 - 1: (1, 0), never rewritten (their state rows are 0)
+template <class Cfg, class Sm>
+__device__ __forceinline__ void init_pad_pairs(const Sm &sm, const ScanParams &p) {
+    const int tid = threadIdx.x;
+    if (tid >= p.N / 2 && tid < Cfg::NP / 2) *(f32x2_t *)(sm.csr + 2 * tid) = f32x2_t{1.f, 0.f};
+}
+
+// Stage 3: B~ (and C~) for the rows this lane owns: norm, gains and biases, rotation by the
+// block-local angle.  Writes (w B~)^T [n][row] to LDS (bf16 hi/lo, or fp32) and, in output
+// mode, B~ [row][n] (fp16 times the row scale, or fp32) and returns the C~ fragments (fp16
+// times the row scale, or fp32); the inverse row scales go to sm.isr when c.rowscale.  With
+// `final_row` (the call's last block, in the workgroup that writes the final state) the lanes
+// of the last token's rows also write that token's B~, rotated into the global frame, to the
+// final state's prev_B.
 template <class Io, class Cfg, bool WANT_C, class Frag, class Sm>
 __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, const Sm &sm, const ScanParams &p,
-                                               const WgCtx &c, const BlockGeo &g, Frag (&ct)[Cfg::KS]) {
+                                               const WgCtx &c, const BlockGeo &g, Frag (&ct)[Cfg::KS],
+                                               bool final_row) {
     constexpr int KS = Cfg::KS;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int l16 = lane & 15, gq = lane >> 4;
     const int N = p.N;
     const int R = Cfg::VEC ? 1 : c.R;
@@ -754,15 +811,26 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
             }
     }
     float ssb = 0.f, ssc = 0.f;
+    if constexpr (Cfg::PACKED) {
+        // packed bf16 pairs: one dot2 per two squares
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        float vb[8], vc[8];
-        raw8<Cfg>(bw[kk], vb);
-        if constexpr (WANT_C) raw8<Cfg>(cw[kk], vc);
+        for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ssb = fmaf(vb[j], vb[j], ssb);
-            if constexpr (WANT_C) ssc = fmaf(vc[j], vc[j], ssc);
+            for (int k = 0; k < 4; ++k) {
+                ssb = sumsq2_bf16(bw[kk][k], ssb);
+                if constexpr (WANT_C) ssc = sumsq2_bf16(cw[kk][k], ssc);
+            }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            float vb[8], vc[8];
+            raw8<Cfg>(bw[kk], vb);
+            if constexpr (WANT_C) raw8<Cfg>(cw[kk], vc);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                ssb = fmaf(vb[j], vb[j], ssb);
+                if constexpr (WANT_C) ssc = fmaf(vc[j], vc[j], ssc);
+            }
         }
     }
     ssb += __shfl_xor(ssb, 16, 64);
@@ -775,25 +843,19 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
     const float rsb = rv ? (c.bcnorm ? __builtin_amdgcn_rsqf(fmaf(ssb, c.invN, c.eps)) : 1.f) : 0.f;
     const float rsc = rv ? (c.bcnorm ? __builtin_amdgcn_rsqf(fmaf(ssc, c.invN, c.eps)) : 1.f) : 0.f;
     const float wt = sm.w[tok];  // zero past the block end
-    // angle offsets of the earlier 16-row tiles (SISO path)
+    // angle offsets of the earlier 16-row tiles (SISO path; the tile index is wave-uniform)
     f32x4_t phoff[KS];
     if constexpr (Cfg::VEC) {
         const float *tt = (const float *)sm.phi;
         const int rtile = row_tile();
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < KS; ++kk) phoff[kk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int w2 = 0; w2 < rtile; ++w2)
 #pragma unroll
-            for (int w2 = 0; w2 < 3; ++w2) {
-                const f32x4_t t4 = *(const f32x4_t *)(tt + w2 * (Cfg::NP / 2) + kk * 16 + 4 * gq);
-                if (w2 < rtile) o += t4;
-            }
-            phoff[kk] = o;
-        }
+            for (int kk = 0; kk < KS; ++kk) phoff[kk] += *(const f32x4_t *)(tt + w2 * (Cfg::NP / 2) + kk * 16 + 4 * gq);
     }
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        float vb[8], vc[8];
+    // normalised values with gains and biases of one k step (8 components of the row)
+    auto prep = [&](int kk, float (&vb)[8], float (&vc)[8]) {
         raw8<Cfg>(bw[kk], vb);
         if constexpr (WANT_C) raw8<Cfg>(cw[kk], vc);
 #pragma unroll
@@ -839,6 +901,42 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
                 }
             }
         }
+    };
+    // fp16 row scales: a power of two that maps the row's largest |component| into [2^11, 2^12)
+    // (a rotated component is at most sqrt(2) times that); 1 for normalised rows without gains
+    // or biases, whose components are at most sqrt(N)
+    float sgb = 1.f, sgc = 1.f;
+    if constexpr (Cfg::F16 && WANT_C) {
+        if (c.rowscale) {
+            float mb = 0.f, mc = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                float vb[8], vc[8];
+                prep(kk, vb, vc);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    mb = fmaxf(mb, fabsf(vb[j]));
+                    mc = fmaxf(mc, fabsf(vc[j]));
+                }
+            }
+            mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+            mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+            mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
+            mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+            float ib, ic;
+            pow2_scale<12>(mb, sgb, ib);
+            pow2_scale<12>(mc, sgc, ic);
+            if (gq == 0) {
+                sm.isr[row] = ib;
+                sm.isr[Cfg::ROWS + row] = ic;
+            }
+        }
+    }
+    const bool last_tok = final_row && rv && tok == g.Tv - 1;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        float vb[8], vc[8];
+        prep(kk, vb, vc);
         float ob[8], oc[8];
 #pragma unroll
         for (int jp = 0; jp < 4; ++jp) {
@@ -857,73 +955,60 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
                 oc[2 * jp + 1] = uc * sn + vcc * cn;
             }
         }
+        if (last_tok) {
+            // the carried B~ of the call's last token: from the block frame to the global frame
+            // (the running angle at this block's start)
+#pragma unroll
+            for (int jp = 0; jp < 4; ++jp) {
+                const int n = kk * 32 + 8 * gq + 2 * jp;
+                if (n < N) {
+                    float sn, cn;
+                    fast_sincos((float)wrap_2pi(sm.base[n / 2]), sn, cn);
+                    const float u = ob[2 * jp], v = ob[2 * jp + 1];
+                    p.pB1[(c.bh * N + n) * R + r] = u * cn - v * sn;
+                    p.pB1[(c.bh * N + n + 1) * R + r] = u * sn + v * cn;
+                }
+            }
+        }
+        // the 8 components n0 .. n0 + 7 share their swizzle in the (w B~)^T plane
+        const int n0 = kk * 32 + 8 * gq;
         if constexpr (Cfg::BF) {
             uint32_t wh[4], wl[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) split2(ob[2 * k] * wt, ob[2 * k + 1] * wt, wh[k], wl[k]);
             if constexpr (WANT_C) {
-                uint32_t bh_[4], bl_[4], ch[4], cl[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    split2(ob[2 * k], ob[2 * k + 1], bh_[k], bl_[k]);
-                    split2(oc[2 * k], oc[2 * k + 1], ch[k], cl[k]);
-                }
-                const int off = row * Cfg::OPP + kk * 32 + 8 * gq;
-                uint16_t *bt = (uint16_t *)sm.bt;
-                *(u32x4_t *)(bt + off) = u32x4_t{bh_[0], bh_[1], bh_[2], bh_[3]};
-                *(u32x4_t *)(bt + Cfg::BT_PLANE + off) = u32x4_t{bl_[0], bl_[1], bl_[2], bl_[3]};
-                ct[kk].hi = u32x4_t{ch[0], ch[1], ch[2], ch[3]};
-                ct[kk].lo = u32x4_t{cl[0], cl[1], cl[2], cl[3]};
+                const int off = row * Cfg::OPP + n0;
+                *(u32x4_t *)((uint16_t *)sm.bt + off) =
+                    u32x4_t{pack_f16(ob[0] * sgb, ob[1] * sgb), pack_f16(ob[2] * sgb, ob[3] * sgb),
+                            pack_f16(ob[4] * sgb, ob[5] * sgb), pack_f16(ob[6] * sgb, ob[7] * sgb)};
+                const u32x4_t cw4 = {pack_f16(oc[0] * sgc, oc[1] * sgc), pack_f16(oc[2] * sgc, oc[3] * sgc),
+                                     pack_f16(oc[4] * sgc, oc[5] * sgc), pack_f16(oc[6] * sgc, oc[7] * sgc)};
+                if constexpr (Cfg::COL) *(u32x4_t *)((uint16_t *)sm.ct + off) = cw4;  // read by every wave
+                else ct[kk].v = cw4;
             }
-            uint16_t *wb = (uint16_t *)sm.wb;
+            uint16_t *wb = (uint16_t *)sm.wb + tr_off<Cfg>(n0, row);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int n = kk * 32 + 8 * gq + 2 * k;
-                wb[tr_off<Cfg>(n, row)] = (uint16_t)(wh[k] & 0xffffu);
-                wb[tr_off<Cfg>(n + 1, row)] = (uint16_t)(wh[k] >> 16);
-                wb[Cfg::WB_PLANE + tr_off<Cfg>(n, row)] = (uint16_t)(wl[k] & 0xffffu);
-                wb[Cfg::WB_PLANE + tr_off<Cfg>(n + 1, row)] = (uint16_t)(wl[k] >> 16);
+                wb[(2 * k) * Cfg::RPP] = (uint16_t)(wh[k] & 0xffffu);
+                wb[(2 * k + 1) * Cfg::RPP] = (uint16_t)(wh[k] >> 16);
+                wb[Cfg::WB_PLANE + (2 * k) * Cfg::RPP] = (uint16_t)(wl[k] & 0xffffu);
+                wb[Cfg::WB_PLANE + (2 * k + 1) * Cfg::RPP] = (uint16_t)(wl[k] >> 16);
             }
         } else {
             if constexpr (WANT_C) {
-                const int off = row * Cfg::OPP + kk * 32 + 8 * gq;
+                const int off = row * Cfg::OPP + n0;
                 float *bt = (float *)sm.bt;
                 *(f32x4_t *)(bt + off) = f32x4_t{ob[0], ob[1], ob[2], ob[3]};
                 *(f32x4_t *)(bt + off + 4) = f32x4_t{ob[4], ob[5], ob[6], ob[7]};
 #pragma unroll
                 for (int j = 0; j < 8; ++j) ct[kk].v[j] = oc[j];
             }
-            float *wb = (float *)sm.wb;
+            float *wb = (float *)sm.wb + tr_off<Cfg>(n0, row);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wb[tr_off<Cfg>(kk * 32 + 8 * gq + j, row)] = ob[j] * wt;
+            for (int j = 0; j < 8; ++j) wb[j * Cfg::RPP] = ob[j] * wt;
         }
     }
-}
-
-// Carried B~ of the call's last token: read back from the B~ plane of the last
-// block and rotated from the block frame to the global frame (block base angle).
-template <class Cfg, class Sm>
-__device__ __forceinline__ void write_final_prev_b(const Sm &sm, const ScanParams &p, const WgCtx &c,
-                                                   const BlockGeo &g) {
-    const int N = p.N, N2 = p.N / 2, R = c.R;
-    const int lrow0 = (g.Tv - 1) * R;
-    for (int e = threadIdx.x; e < N2 * R; e += 256) {
-        const int i = e / R, r = e - i * R, n = 2 * i;
-        const int off = (lrow0 + r) * Cfg::OPP + n;
-        float u, v;
-        if constexpr (Cfg::BF) {
-            const uint16_t *bt = (const uint16_t *)sm.bt;
-            u = bf2f(bt[off]) + bf2f(bt[Cfg::BT_PLANE + off]);
-            v = bf2f(bt[off + 1]) + bf2f(bt[Cfg::BT_PLANE + off + 1]);
-        } else {
-            u = ((const float *)sm.bt)[off];
-            v = ((const float *)sm.bt)[off + 1];
-        }
-        float sn, cn;
-        fast_sincos((float)wrap_2pi(sm.base[i]), sn, cn);
-        p.pB1[(c.bh * N + n) * R + r] = u * cn - v * sn;
-        p.pB1[(c.bh * N + n + 1) * R + r] = u * sn + v * cn;
-    }
+    (void)tid;
 }
 
 // State tiles of this wave: tile e = wave + 4m -> (nt = e / PT, pt = e % PT);
@@ -983,7 +1068,7 @@ __device__ __forceinline__ void rot_neg(f32x4_t &v, float c0, float s0, float c1
 // Carry update:  H <- Rot(-Phi) (decay H + S), with the matrix cores adding S
 // into the decayed state in place.
 template <class Cfg, class Sm>
-__device__ __forceinline__ void carry_block(const Sm &sm, f32x4_t (&hs)[Cfg::TPW], float decay, int N2) {
+__device__ __forceinline__ void carry_block(const Sm &sm, f32x4_t (&hs)[Cfg::TPW], float decay) {
     const int gq = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int m = 0; m < Cfg::TPW; ++m) hs[m] *= decay;
@@ -992,33 +1077,62 @@ __device__ __forceinline__ void carry_block(const Sm &sm, f32x4_t (&hs)[Cfg::TPW
     for (int m = 0; m < Cfg::TPW; ++m) {
         int nt, pt;
         if (!state_tile<Cfg>(m, nt, pt)) continue;
-        const int pr = (nt * 16 + 4 * gq) >> 1;  // pairs pr, pr + 1
-        // padded pairs (n >= N) carry zeros; their angle entries are never written
-        const float c0 = pr < N2 ? sm.cph[pr] : 1.f, s0 = pr < N2 ? sm.sph[pr] : 0.f;
-        const float c1 = pr + 1 < N2 ? sm.cph[pr + 1] : 1.f, s1 = pr + 1 < N2 ? sm.sph[pr + 1] : 0.f;
-        rot_neg(hs[m], c0, s0, c1, s1);
+        const int pr = (nt * 16 + 4 * gq) >> 1;  // pairs pr, pr + 1 (pr even)
+        const f32x4_t cs4 = *(const f32x4_t *)(sm.csr + 2 * pr);
+        rot_neg(hs[m], cs4[0], cs4[1], cs4[2], cs4[3]);
     }
 }
 
-// H fragments -> H^T [p][n] planes in LDS (hi/lo or fp32); 4 consecutive n per lane
+// H fragments -> the H^T [p][n] plane in LDS, 4 consecutive n per lane: fp16 times a power of
+// two that maps the block's largest |H| (the maxima the waves left in sm.hmax) into
+// [2^13, 2^14), or fp32.  Returns the inverse of that scale (1 for fp32).
 template <class Cfg, class Sm>
-__device__ __forceinline__ void write_ht(const Sm &sm, const f32x4_t (&hs)[Cfg::TPW]) {
+__device__ __forceinline__ float write_ht(const Sm &sm, const f32x4_t (&hs)[Cfg::TPW]) {
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15, gq = lane >> 4;
+    float sc = 1.f, inv = 1.f;
+    if constexpr (Cfg::F16) {
+        const f32x4_t m4 = *(const f32x4_t *)sm.hmax;
+        pow2_scale<14>(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])), sc, inv);
+    }
 #pragma unroll
     for (int m = 0; m < Cfg::TPW; ++m) {
         int nt, pt;
         if (!state_tile<Cfg>(m, nt, pt)) continue;
         const int off = (pt * 16 + l16) * Cfg::OPP + nt * 16 + 4 * gq;
-        if constexpr (Cfg::BF) {
-            uint32_t h0, l0, h1, l1;
-            split2(hs[m][0], hs[m][1], h0, l0);
-            split2(hs[m][2], hs[m][3], h1, l1);
-            *(u32x2_t *)((uint16_t *)sm.ht + off) = u32x2_t{h0, h1};
-            *(u32x2_t *)((uint16_t *)sm.ht + Cfg::HT_PLANE + off) = u32x2_t{l0, l1};
+        if constexpr (Cfg::F16) {
+            *(u32x2_t *)((uint16_t *)sm.ht + off) =
+                u32x2_t{pack_f16(hs[m][0] * sc, hs[m][1] * sc), pack_f16(hs[m][2] * sc, hs[m][3] * sc)};
         } else {
             *(f32x4_t *)((float *)sm.ht + off) = hs[m];
         }
+    }
+    return inv;
+}
+
+// Largest |component| over the 64 lanes of a wave (values >= 0; every lane active): inclusive
+// max inside rows of 16, then across rows as in wave_incl_scan; lane 63's value, broadcast.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// This wave's largest |H| -> sm.hmax[wave], read by every wave's next write_ht (fp16 path).
+template <class Cfg, class Sm>
+__device__ __forceinline__ void publish_hmax(const Sm &sm, const f32x4_t (&hs)[Cfg::TPW]) {
+    if constexpr (Cfg::F16) {
+        float m = 0.f;
+#pragma unroll
+        for (int k = 0; k < Cfg::TPW; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(hs[k][i]));
+        m = wave_max_nonneg(m);
+        if ((threadIdx.x & 63) == 0) sm.hmax[threadIdx.x >> 6] = m;
     }
 }
 
@@ -1069,6 +1183,8 @@ __device__ __forceinline__ WgCtx make_ctx(const ScanParams &p, int nsegk, int bp
     c.eps = p.eps;
     c.bcnorm = (p.flags & kFlagNorm) != 0;
     c.affine = (c.bcnorm && (p.bnw || p.cnw)) || p.bbias || p.cbias;
+    // normalised rows without gains or biases have |components| <= sqrt(N) <= 11.4: fp16 as is
+    c.rowscale = Cfg::F16 && !(c.bcnorm && !c.affine);
     return c;
 }
 
@@ -1095,7 +1211,7 @@ template <class Io, int NP, int PP, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) void seg_state_kernel(ScanParams p) {
     using Cfg = SegCfg<Io, NP, PP, MODE>;
     constexpr bool VEC = Cfg::VEC;
-    using Frag = typename std::conditional<Cfg::BF, FragHL, FragF>::type;
+    using Frag = typename std::conditional<Cfg::BF, FragH, FragF>::type;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const Smem<Cfg, false> sm(smem);
     const WgCtx c = make_ctx<Cfg>(p, p.nsub, p.sbps);  // c.seg: the state sub-segment
@@ -1107,6 +1223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
 #pragma unroll
     for (int m = 0; m < Cfg::TPW; ++m) sagg[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (tid < N2) sm.base[tid] = 0.0;
+    init_pad_pairs<Cfg>(sm, p);
     float lsum = 0.f;
     Frag ct_unused[Cfg::KS];
 
@@ -1118,14 +1235,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
     for (int blk = c.blk0; blk < c.blk1; ++blk) {
         lds_barrier();  // previous block's readers of the LDS planes are done
         stage_scalars_x<Io>(rb, sm, p, c, g);
+        const BlockGeo gn = block_geo(p, blk + 1);
+        if constexpr (VEC) {
+            if (blk + 1 < c.blk1) load_block<Io, kLoadXs>(rb, p, c, gn);  // x, dt, lambda: consumed
+        }
         if constexpr (!VEC) stage_angles_table<Cfg>(sm, p, g);
         block_angle_totals<Cfg>(sm, p, g);
-        stage_prologue<Io>(rb, sm, p, c, g, ct_unused);
-        const BlockGeo gn = block_geo(p, blk + 1);
-        if (blk + 1 < c.blk1) load_block<Io>(rb, p, c, gn);
+        stage_prologue<Io>(rb, sm, p, c, g, ct_unused, false);
+        if (blk + 1 < c.blk1) load_block<Io, VEC ? kLoadBc : kLoadAll>(rb, p, c, gn);
         lds_barrier();
         const float cs_end = sm.cs[Cfg::ROWS - 1];
-        carry_block<Cfg>(sm, sagg, __expf(cs_end), N2);
+        carry_block<Cfg>(sm, sagg, __expf(cs_end));
         if constexpr (Cfg::MV) {
             if (blk + 1 < c.blk1) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.raw, nullptr, c);
         }
@@ -1154,6 +1274,187 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
     }
 }
 
+// ============================================================ column-owned outputs
+// (rank-1 bf16 path with 64 columns per workgroup)
+//
+// The G o L tiles of a block (t tile T >= s tile S, 16 x 16 each) are computed once, spread over
+// the waves so that each does about the same work (a diagonal tile, with the full mask, costs
+// more than a strictly causal one, whose decay factors), masked, with D on the diagonal (so
+// that Y_intra includes D x), and written to the G o L planes [t][s] as bf16 hi / lo.  Tiles
+// above the diagonal that share a 32-wide k step with causal ones ((0, 1) and (2, 3)) stay 0.
+// Wave w then computes Y^T for its 16 columns p = 16w .. 16w + 15 and every row:
+//     Y^T = diag-scaled (H^T C~^T) + X^T (G o L)^T
+// H^T from the state columns the wave itself holds (fp16 with a per-wave power-of-two scale),
+// C~^T and (G o L)^T from LDS; a result fragment holds 4 consecutive columns of one row, stored
+// to y as 8 bytes.
+// Tiles of wave w (nibble q; 15 = none): w0 (0,0) (3,3); w1 (1,1) (2,2); w2 (1,0) (2,0) (3,0);
+// w3 (2,1) (3,1) (3,2).
+__device__ __forceinline__ void gl_tile(int w, int q, int &T, int &S) {
+    const unsigned tt_ = w == 0 ? 0xF30u : w == 1 ? 0xF21u : w == 2 ? 0x321u : 0x332u;
+    const unsigned ss_ = w == 0 ? 0xF30u : w == 1 ? 0xF21u : w == 2 ? 0x000u : 0x211u;
+    T = (int)((tt_ >> (4 * q)) & 15u);
+    S = (int)((ss_ >> (4 * q)) & 15u);
+}
+
+// Gate input z in the column-owned epilogue's mapping: for each 16-row tile T, columns
+// 16w + 4g .. 16w + 4g + 3 of row 16T + l16 (8 bytes).
+struct RawZCol {
+    u32x2_t w[4];
+};
+template <class Io>
+__device__ __forceinline__ void load_z_col(RawZCol &rz, const ScanParams &p, const WgCtx &c, const BlockGeo &g) {
+    using ET = typename Io::T;
+    const int lane = threadIdx.x & 63, l16 = lane & 15, gq = lane >> 4;
+    const int pc = row_tile() * 16 + 4 * gq;
+    const ET *zb = (const ET *)p.z + ((c.b * p.T + g.t0) * p.H + c.h) * (int64_t)p.P + c.p0;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+        const int t = T * 16 + l16;
+        u32x2_t v = {0u, 0u};
+        if (t < g.Tv && pc < c.Pw) v = *(const u32x2_t *)(zb + (int64_t)t * c.sx + pc);
+        rz.w[T] = v;
+    }
+}
+
+// The zero tiles (0, 1) and (2, 3) of both G o L planes (written once per workgroup).
+template <class Cfg, class Sm>
+__device__ __forceinline__ void init_gl_zero_tiles(const Sm &sm) {
+    const int tid = threadIdx.x;  // 256 threads: (plane, tile, row, 4-column group) -> 2 x 2 x 16 x 4
+    const int pl = tid >> 7, tl = (tid >> 6) & 1, r = (tid >> 2) & 15, cg = tid & 3;
+    const int T = tl ? 2 : 0, S = tl ? 3 : 1;
+    uint16_t *gp = (uint16_t *)sm.gl + pl * Cfg::GL_PLANE;
+    *(u32x2_t *)(gp + (T * 16 + r) * Cfg::RPP + S * 16 + 4 * cg) = u32x2_t{0u, 0u};
+}
+
+template <class Io, class Cfg, bool GATE, class Sm>
+__device__ __forceinline__ void col_outputs(const Sm &sm, const ScanParams &p, const WgCtx &c, const BlockGeo &g,
+                                            const f32x4_t (&hs)[Cfg::TPW], const RawZCol &rz) {
+    using ET = typename Io::T;
+    constexpr int KS = Cfg::KS, OPP = Cfg::OPP, RPP = Cfg::RPP;
+    const int lane = threadIdx.x & 63, l16 = lane & 15, gq = lane >> 4;
+    const int w = row_tile();
+    const uint16_t *bt = (const uint16_t *)sm.bt, *ctp = (const uint16_t *)sm.ct;
+    uint16_t *glh = (uint16_t *)sm.gl, *gll = glh + Cfg::GL_PLANE;
+    const float Dh = p.D[c.h];
+    // ---- this wave's G o L tiles
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        int T, S;
+        gl_tile(w, q, T, S);
+        if (T == 15) break;
+        f32x4_t gv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const FragH a{*(const u32x4_t *)(bt + (S * 16 + l16) * OPP + kk * 32 + 8 * gq)};
+            const FragH b{*(const u32x4_t *)(ctp + (T * 16 + l16) * OPP + kk * 32 + 8 * gq)};
+            gv = mma(a, b, gv);
+        }
+        const int trow = T * 16 + l16, sb = S * 16 + 4 * gq;  // slot i: G[t = trow][s = sb + i]
+        if (c.rowscale) gv *= *(const f32x4_t *)(sm.isr + sb) * sm.isr[Cfg::ROWS + trow];
+        const float cs_t = sm.cs[trow];
+        float mv[4];
+        if (S < T) {
+            // strictly causal tile: exp(cs_t - cs_ref) u_s
+            const f32x4_t us = *(const f32x4_t *)(sm.u + sb);
+            const float et = __expf(cs_t - sm.cs[S * 16 + 15]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mv[i] = gv[i] * (et * us[i]);
+        } else {
+            const f32x4_t css = *(const f32x4_t *)(sm.cs + sb);
+            const f32x4_t scs = *(const f32x4_t *)(sm.scale + sb);
+            const float g_t = sm.gam[trow];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = sb + i;
+                mv[i] = s < trow ? gv[i] * (__expf(cs_t - css[i]) * scs[i]) : (s == trow ? fmaf(gv[i], g_t, Dh) : 0.f);
+            }
+        }
+        uint32_t h0, l0, h1, l1;
+        split2(mv[0], mv[1], h0, l0);
+        split2(mv[2], mv[3], h1, l1);
+        const int off = trow * RPP + sb;
+        *(u32x2_t *)(glh + off) = u32x2_t{h0, h1};
+        *(u32x2_t *)(gll + off) = u32x2_t{l0, l1};
+    }
+    lds_barrier();
+    // ---- H^T of this wave's columns as fp16 A operands: k step mm covers state tiles 2mm, 2mm+1
+    // (slot j < 4: n = 32mm + 4g + j; j >= 4: n = 32mm + 16 + 4g + j - 4)
+    float hsc, hinv;
+    {
+        float m = 0.f;
+#pragma unroll
+        for (int k = 0; k < Cfg::TPW; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(hs[k][i]));
+        pow2_scale<14>(wave_max_nonneg(m), hsc, hinv);
+    }
+    u32x4_t ha[KS];
+#pragma unroll
+    for (int mm = 0; mm < KS; ++mm)
+        ha[mm] = u32x4_t{pack_f16(hs[2 * mm][0] * hsc, hs[2 * mm][1] * hsc), pack_f16(hs[2 * mm][2] * hsc, hs[2 * mm][3] * hsc),
+                         pack_f16(hs[2 * mm + 1][0] * hsc, hs[2 * mm + 1][1] * hsc),
+                         pack_f16(hs[2 * mm + 1][2] * hsc, hs[2 * mm + 1][3] * hsc)};
+    // X^T of this wave's columns (exact bf16): p = 16w + l16, s = 32kk + 8g .. + 7
+    u32x4_t xa[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) xa[kk] = *(const u32x4_t *)((const uint16_t *)sm.xt + xt_off<Cfg>(w * 16 + l16, kk * 32 + 8 * gq));
+    const int pc = w * 16 + 4 * gq;
+    // two row tiles at a time: every LDS operand of the pair is requested before its products
+#pragma unroll
+    for (int T0 = 0; T0 < 4; T0 += 2) {
+        u32x4_t cb[2][KS];
+        FragHL gb[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = (T0 + u) * 16 + l16;
+#pragma unroll
+            for (int mm = 0; mm < KS; ++mm) {
+                const u32x2_t b0 = *(const u32x2_t *)(ctp + t * OPP + mm * 32 + 4 * gq);
+                const u32x2_t b1 = *(const u32x2_t *)(ctp + t * OPP + mm * 32 + 16 + 4 * gq);
+                cb[u][mm] = u32x4_t{b0[0], b0[1], b1[0], b1[1]};
+            }
+#pragma unroll
+            for (int kk = 0; kk <= (T0 >> 1); ++kk) {
+                gb[u][kk].hi = *(const u32x4_t *)(glh + t * RPP + kk * 32 + 8 * gq);
+                gb[u][kk].lo = *(const u32x4_t *)(gll + t * RPP + kk * 32 + 8 * gq);
+            }
+        }
+        f32x4_t acc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mm = 0; mm < KS; ++mm) acc[u] = mfma_h(ha[mm], cb[u][mm], acc[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = (T0 + u) * 16 + l16;
+            float f = sm.ecs[t] * hinv;  // exp(cs_t) and the inverse scales of H and of the C~ row
+            if (c.rowscale) f *= sm.isr[Cfg::ROWS + t];
+            acc[u] *= f;
+        }
+#pragma unroll
+        for (int kk = 0; kk <= (T0 >> 1); ++kk)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) acc[u] = mma(xa[kk], gb[u][kk], acc[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int T = T0 + u, t = T * 16 + l16;
+            // epilogue: the gate, one rounding, 4 consecutive columns of row t
+            float yv[4] = {acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
+            if constexpr (GATE) {
+                const u32x2_t zw = rz.w[T];
+                const float zv[4] = {__uint_as_float(zw[0] << 16), __uint_as_float(zw[0] & 0xffff0000u),
+                                     __uint_as_float(zw[1] << 16), __uint_as_float(zw[1] & 0xffff0000u)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) yv[i] *= silu_f(zv[i]);
+            }
+            if (t < g.Tv && pc < c.Pw)
+                *(u32x2_t *)((ET *)c.yb + (g.t0 + t) * c.sx + pc) = u32x2_t{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])};
+        }
+    }
+}
+
 // ============================================================ output kernel
 // With N above 64 the LDS planes allow one workgroup per compute unit (one wave per
 // SIMD), so such variants may use the whole register file.
@@ -1162,7 +1463,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     using Cfg = SegCfg<Io, NP, PP, MODE, !GATE>;
     constexpr bool VEC = Cfg::VEC;
     using ET = typename Io::T;
-    using Frag = typename std::conditional<Cfg::BF, FragHL, FragF>::type;
+    using Frag = typename std::conditional<Cfg::BF, FragH, FragF>::type;
     constexpr int KS = Cfg::KS, PT = Cfg::PT, TPW = Cfg::TPW;
     constexpr int OPP = Cfg::OPP, RPP = Cfg::RPP;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1177,10 +1478,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
 
     // prefetch the first block while the incoming state is assembled
     stage_affine<Cfg>(sm, p, c);
+    init_pad_pairs<Cfg>(sm, p);
     RawBlock<Cfg, true> rb;
     RawZ<Cfg> rz;
+    RawZCol rzc;
     BlockGeo g = block_geo(p, c.blk0);
-    if constexpr (GATE) load_z<Io>(rz, p, c, g);
+    if constexpr (GATE) {
+        if constexpr (Cfg::COL) load_z_col<Io>(rzc, p, c, g);
+        else load_z<Io>(rz, p, c, g);
+    }
+    if constexpr (Cfg::COL) init_gl_zero_tiles<Cfg>(sm);
     load_block<Io>(rb, p, c, g);
 
     // ---- incoming state H (this wave's state fragments) and, for the final state, the
@@ -1248,7 +1555,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             // fold the earlier segments: H <- Rot(-Phi_s) (exp(l_s) H) + S_s (the aggregate is
             // already in its segment's end frame).  FB segments at a time, so that their loads are
             // in flight together; slots past the last segment reload it and are not applied.
-            constexpr int FB = TPW <= 2 ? 4 : (TPW <= 4 ? 2 : 1);
+            constexpr int FB = TPW <= 4 ? 4 : 2;
             const int64_t q = bh * p.ncg + c.cg;
             for (int s0 = 0; s0 < c.seg; s0 += FB) {
                 f32x4_t sv[FB][TPW], cs[FB][TPW];
@@ -1297,19 +1604,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         }
     }
 
+    if constexpr (!Cfg::COL) publish_hmax<Cfg>(sm, hs);  // the incoming state's magnitude, for its fp16 scale
     Frag ct[KS];
     for (int blk = c.blk0; blk < c.blk1; ++blk) {
         lds_barrier();  // every wave is done with the previous block's LDS planes
-        if constexpr (GATE) stage_z<Cfg>(rz, sm, c);  // read by the epilogue after two more barriers
-        write_ht<Cfg>(sm, hs);  // the state entering this block (read after two more barriers)
+        float inv_hs = 1.f;
+        if constexpr (!Cfg::COL) {
+            if constexpr (GATE) stage_z<Cfg>(rz, sm, c);  // read by the epilogue after two more barriers
+            inv_hs = write_ht<Cfg>(sm, hs);  // the state entering this block (read after two more barriers)
+        }
         if constexpr (Cfg::MV) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.bt, (uint16_t *)sm.bt + Cfg::BT_PLANE, c);
         stage_scalars_x<Io>(rb, sm, p, c, g);
+        const BlockGeo gn = block_geo(p, blk + 1);
+        if constexpr (VEC) {
+            // the next block's x, dt, lambda as soon as this block's are staged
+            if (blk + 1 < c.blk1) load_block<Io, kLoadXs>(rb, p, c, gn);
+        }
         if constexpr (!VEC) stage_angles_table<Cfg>(sm, p, g);
         block_angle_totals<Cfg>(sm, p, g);
-        stage_prologue<Io>(rb, sm, p, c, g, ct);
-        const BlockGeo gn = block_geo(p, blk + 1);
+        stage_prologue<Io>(rb, sm, p, c, g, ct, want_final && c.cg == 0 && blk == c.blk1 - 1);
+        if constexpr (VEC) {
+            // and its B, C, theta once the prologue has consumed this block's
+            if (blk + 1 < c.blk1) load_block<Io, kLoadBc>(rb, p, c, gn);
+        }
         lds_barrier();
 
+        if constexpr (Cfg::COL) {
+            col_outputs<Io, Cfg, GATE>(sm, p, c, g, hs, rzc);
+            if constexpr (GATE) {
+                if (blk + 1 < c.blk1) load_z_col<Io>(rzc, p, c, gn);
+            }
+        } else {
         // ---- outputs for this wave's 16 rows
         const int tt = row_tile();
         const int row0 = tt * 16 + 4 * gq;  // result rows row0 .. row0 + 3 of this lane
@@ -1322,10 +1647,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int ho = (pt * 16 + l16) * OPP + kk * 32 + 8 * gq;
-                if constexpr (Cfg::BF) {
-                    FragHL hf;
-                    hf.hi = *(const u32x4_t *)((const uint16_t *)sm.ht + ho);
-                    hf.lo = *(const u32x4_t *)((const uint16_t *)sm.ht + Cfg::HT_PLANE + ho);
+                if constexpr (Cfg::F16) {
+                    const FragH hf{*(const u32x4_t *)((const uint16_t *)sm.ht + ho)};
                     yacc[pt] = mma(ct[kk], hf, yacc[pt]);
                 } else {
                     FragF hf;
@@ -1338,6 +1661,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             }
         }
         {
+            // exp(cs_t), times the inverse scales of H and of the C~ rows (fp16 operands)
             f32x4_t ecs4;
             if constexpr (VEC) {
                 ecs4 = *(const f32x4_t *)(sm.ecs + row0);
@@ -1345,12 +1669,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ecs4[i] = sm.ecs[tok_of(row0 + i, c)];
             }
+            ecs4 *= inv_hs;
+            if (c.rowscale) ecs4 *= *(const f32x4_t *)(sm.isr + Cfg::ROWS + row0);
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) yacc[pt] *= ecs4;
         }
         const int trow = tt * 16 + l16;  // this lane's t-row in the G^T fragments
         const int ttok = VEC ? trow : tok_of(trow, c);
         const float cs_t = sm.cs[ttok], g_t = sm.gam[ttok];
+        const float isc_t = c.rowscale ? sm.isr[Cfg::ROWS + trow] : 1.f;  // inverse scale of C~ row t
         int smax = tt;
         if constexpr (!VEC) {
             // with R not dividing 16 the rows of the tile's last token may spill into the next tile
@@ -1365,18 +1692,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             for (int kk = 0; kk < KS; ++kk) {
                 const int o0 = (st0 * 16 + l16) * OPP + kk * 32 + 8 * gq;
                 const int o1 = (st1 * 16 + l16) * OPP + kk * 32 + 8 * gq;
-                if constexpr (Cfg::BF) {
+                if constexpr (Cfg::F16) {
                     const uint16_t *bt = (const uint16_t *)sm.bt;
-                    FragHL a0;
-                    a0.hi = *(const u32x4_t *)(bt + o0);
-                    a0.lo = *(const u32x4_t *)(bt + Cfg::BT_PLANE + o0);
-                    g0 = mma(a0, ct[kk], g0);
-                    if (has1) {
-                        FragHL a1;
-                        a1.hi = *(const u32x4_t *)(bt + o1);
-                        a1.lo = *(const u32x4_t *)(bt + Cfg::BT_PLANE + o1);
-                        g1 = mma(a1, ct[kk], g1);
-                    }
+                    g0 = mma(FragH{*(const u32x4_t *)(bt + o0)}, ct[kk], g0);
+                    if (has1) g1 = mma(FragH{*(const u32x4_t *)(bt + o1)}, ct[kk], g1);
                 } else {
                     const float *bt = (const float *)sm.bt;
                     FragF a0;
@@ -1397,14 +1716,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             float mv[8];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int sb = (half ? st1 : st0) * 16 + 4 * gq;
-                const f32x4_t gv = half ? g1 : g0;
+                const int st = half ? st1 : st0;
+                const int sb = st * 16 + 4 * gq;
+                f32x4_t gv = half ? g1 : g0;
                 if (half && !has1) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) mv[4 + i] = 0.f;
                     continue;
                 }
+                if (c.rowscale) gv *= *(const f32x4_t *)(sm.isr + sb) * isc_t;  // undo the fp16 row scales
                 if constexpr (VEC) {
+                    if (st < tt) {
+                        // a strictly earlier s tile: the factored decay exp(cs_t - cs_ref) u_s
+                        const f32x4_t us = *(const f32x4_t *)(sm.u + sb);
+                        const float et = __expf(cs_t - sm.cs[st * 16 + 15]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) mv[half * 4 + i] = gv[i] * (et * us[i]);
+                        continue;
+                    }
                     const f32x4_t css = *(const f32x4_t *)(sm.cs + sb);
                     const f32x4_t scs = *(const f32x4_t *)(sm.scale + sb);
 #pragma unroll
@@ -1423,7 +1752,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                     }
                 }
             }
-            Frag mf;
+            // G o L as the A operand of Y_intra: bf16 hi/lo (X is exact bf16) or fp32
+            typename std::conditional<Cfg::BF, FragHL, FragF>::type mf;
             if constexpr (Cfg::BF) mf = make_hl(mv);
             else mf = make_f(mv);
 #pragma unroll
@@ -1518,13 +1848,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 }
             }
         }
-        const float cs_end = sm.cs[Cfg::ROWS - 1];
-        // the next block's raw inputs, issued once this block's outputs are staged (they
-        // overlap the stores and the carry).  Issued right after the prologue instead, they
-        // stay live through the matrix phases; measured 1-3% slower.
+        // the next block's gate input (and, on the element and interleaved-rank paths, its
+        // raw inputs), issued once this block's outputs are staged (they overlap the stores
+        // and the carry)
         if (blk + 1 < c.blk1) {
             if constexpr (GATE) load_z<Io>(rz, p, c, gn);
-            load_block<Io>(rb, p, c, gn);
+            if constexpr (!VEC) load_block<Io>(rb, p, c, gn);
         }
         // ---- y: this wave's rows, staged in its own part of the staging area (LDS
         // operations of one wave complete in order), stored as 16-byte vectors
@@ -1561,8 +1890,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 }
             }
         }
+        }  // row-owned outputs
         // ---- carry to the next block (H^T is rewritten after the next top barrier)
-        carry_block<Cfg>(sm, hs, __expf(cs_end), N2);
+        const float cs_end = sm.cs[Cfg::ROWS - 1];
+        carry_block<Cfg>(sm, hs, __expf(cs_end));
+        if constexpr (!Cfg::COL) publish_hmax<Cfg>(sm, hs);
         // running angle at the next block's start (the last block's start angle is kept
         // for the carried B~ below)
         if (tid < N2 && blk + 1 < c.blk1) sm.base[tid] += (double)sm.pend[tid];
@@ -1572,7 +1904,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         // The last block's B~ (B~ planes), x (X^T plane) and angle total are still in LDS.
         const BlockGeo gl = block_geo(p, c.blk1 - 1);
         lds_barrier();
-        if (c.cg == 0) write_final_prev_b<Cfg>(sm, p, c, gl);
         {
             // carried x of the last token
             const int lrow0 = (gl.Tv - 1) * R;
