@@ -38,6 +38,7 @@ class _Args(ctypes.Structure):
         ("rope_pairs", ctypes.c_int32), ("a_per_token", ctypes.c_int32),
         ("dt_softplus", ctypes.c_int32), ("lam_sigmoid", ctypes.c_int32),
         ("dt_bias", _dp), ("z", _dp), ("half_split", ctypes.c_int32),
+        ("mimo_x", _dp), ("mimo_z", _dp), ("mimo_o", _dp),
     ]
 
 
@@ -91,7 +92,8 @@ def _ptr(a):
 def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
          b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None,
          init=None, nthreads=None, mutation=0, rope_pairs=None,
-         dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None, half_split=False):
+         dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None, half_split=False,
+         mimo_x=None, mimo_z=None, mimo_o=None):
     """Run the sequential fp64 loop.
 
     Shapes: x [Bt,T,H,P] (or [Bt,T,H,P,R]), B/C [Bt,T,H,N] (or [...,N,R]),
@@ -104,15 +106,22 @@ def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
     with silu(z); ``half_split`` pairs components (i, i + N/2) instead of
     (2i, 2i + 1).
 
-    Returns (y, final) with y shaped like x (float64) and final a dict of
-    float64 arrays h, prev_B, prev_x, angle (angle is the unreduced running
-    sum).
+    MIMO projections by learned per-rank vectors, each [H, R, P]: ``mimo_x``
+    (x is then rank-free [Bt,T,H,P] and the scan reads x * mimo_x[h, r]),
+    ``mimo_z`` (z rank-free, the gate reads z * mimo_z[h, r]), ``mimo_o`` (y is
+    the rank contraction sum_r mimo_o[h, r] * y_r, shaped [Bt,T,H,P]).
+
+    Returns (y, final) with y shaped like x (the rank-expanded x with mimo_x,
+    the contracted [Bt,T,H,P] with mimo_o; float64) and final a dict of float64
+    arrays h, prev_B, prev_x, angle (angle is the unreduced running sum;
+    prev_x holds the expanded x).
     """
     x = _f64(x)
-    mimo = x.ndim == 5
-    Bsz, T, H, P = x.shape[:4]
-    R = x.shape[4] if mimo else 1
     Bm, Cm = _f64(B), _f64(C)
+    Bsz, T, H, P = x.shape[:4]
+    R = Bm.shape[4] if Bm.ndim == 5 else 1
+    if mimo_x is None and x.ndim == 5 and x.shape[4] != R:
+        raise ValueError("oracle: x and B must have the same rank")
     N = Bm.shape[3]
     keep = [x, Bm, Cm]
     a = _Args()
@@ -135,16 +144,22 @@ def scan(x, B, C, dt, lam, theta, A, D, *, bcnorm=True, eps=1e-5,
     a.dt_softplus, a.lam_sigmoid = int(bool(dt_softplus)), int(bool(lam_sigmoid))
     if NR > 0 and np.shape(theta)[-1] != NR:
         raise ValueError("oracle: theta must hold rope_pairs angles per token")
-    if z is not None and np.shape(z) != x.shape:
-        raise ValueError("oracle: z must be shaped like x")
+    yr_shape = (Bsz, T, H, P) + ((R,) if R > 1 or x.ndim == 5 else ())  # per-rank outputs
+    zs = (Bsz, T, H, P) if mimo_z is not None else yr_shape
+    if z is not None and np.shape(z) != zs:
+        raise ValueError(f"oracle: z must be shaped {zs}")
+    for name, arr in (("mimo_x", mimo_x), ("mimo_z", mimo_z), ("mimo_o", mimo_o)):
+        if arr is not None and np.shape(arr) != (H, R, P):
+            raise ValueError(f"oracle: {name} must be [H, R, P]")
     for name, arr in (("dt", dt), ("lam", lam), ("theta", theta if NR > 0 else None), ("A", A),
                       ("D", D), ("b_norm_w", b_norm_w), ("c_norm_w", c_norm_w),
-                      ("b_bias", b_bias), ("c_bias", c_bias), ("dt_bias", dt_bias), ("z", z)):
+                      ("b_bias", b_bias), ("c_bias", c_bias), ("dt_bias", dt_bias), ("z", z),
+                      ("mimo_x", mimo_x), ("mimo_z", mimo_z), ("mimo_o", mimo_o)):
         put(name, arr)
     init = init or {}
     for name, key in (("h0", "h"), ("pB0", "prev_B"), ("px0", "prev_x"), ("ang0", "angle")):
         put(name, init.get(key))
-    y = np.zeros(x.shape, dtype=np.float64)
+    y = np.zeros((Bsz, T, H, P) if mimo_o is not None else yr_shape, dtype=np.float64)
     fin = dict(h=np.zeros((Bsz, H, N, P)), prev_B=np.zeros((Bsz, H, N, R)),
                prev_x=np.zeros((Bsz, H, P, R)), angle=np.zeros((Bsz, H, NR)))
     a.y = _ptr(y)

@@ -59,6 +59,15 @@
  *  - Output gate: y_t = (C_t^T h_t + D x_t) * silu(z_t), silu(v) = v sigmoid(v),
  *    z laid out like y.  dotLLM PR #136, "Stage C" (SelectiveScan -> D skip
  *    -> silu(z) gate).
+ *  - MIMO projections by learned per-rank vectors (torchmamba "Math notes",
+ *    MIMO paragraph: per-head x / y / z expanded by a learned vector, D P + P R
+ *    parameters rather than D P R; dotLLM PR #136, "What's deferred",
+ *    MIMO-in-Block: mimo_x / mimo_z projections and the post-scan rank
+ *    contraction): with mimo_x the input x is rank-free [.., P] and the scan
+ *    reads x_r = x * mimo_x[h, r, :]; with mimo_z the gate reads
+ *    z_r = z * mimo_z[h, r, :]; with mimo_o the output is the rank
+ *    contraction y = sum_r mimo_o[h, r, :] * y_r of the gated per-rank
+ *    outputs.  The carried previous x holds the expanded x_r.
  *
  * Layouts (row-major, last index fastest):
  *   x, y, z [B, T, H, P, R]   B, C [B, T, H, N, R]     dt, lam [B, T, H]
@@ -129,6 +138,7 @@ static void run_sequence(const m3o_args *a, int64_t b, int h) {
     const int NR = a->rope_pairs; /* rotated pairs */
     double *ang = calloc((size_t)(N2 > 0 ? N2 : 1), sizeof(double)); /* pairs >= NR stay 0 */
     double *col = calloc((size_t)N, sizeof(double));
+    double *xe = calloc((size_t)P * R, sizeof(double));        /* expanded x_t [P][R] */
     const int64_t bh = b * H + h;
     if (a->h0) memcpy(st, a->h0 + bh * N * P, sizeof(double) * N * P);
     if (a->pB0) memcpy(pB, a->pB0 + bh * N * R, sizeof(double) * N * R);
@@ -167,7 +177,13 @@ static void run_sequence(const m3o_args *a, int64_t b, int h) {
         double gamma = lam * dt;
         if (a->mutation == 1) beta = dt * (1.0 - lam); /* planted: beta without alpha */
         if (a->mutation == 5) { double tmp = beta; beta = gamma; gamma = tmp; } /* planted: swapped */
+        /* x_t per rank: given, or expanded from the rank-free x by the learned vectors */
         const double *xt = a->x + bth * P * R;
+        if (a->mimo_x) {
+            for (int p = 0; p < P; ++p)
+                for (int r = 0; r < R; ++r) xe[p * R + r] = a->x[bth * P + p] * a->mimo_x[((int64_t)h * R + r) * P + p];
+            xt = xe;
+        }
         /* state update */
         for (int n = 0; n < N; ++n) {
             for (int p = 0; p < P; ++p) {
@@ -181,19 +197,23 @@ static void run_sequence(const m3o_args *a, int64_t b, int h) {
                 st[n * P + p] = alpha * st[n * P + p] + beta * prev_term + gamma * cur_term;
             }
         }
-        /* output: y_t[:, r] = h^T C~_t[:, r] + D x_t[:, r] */
-        double *yt = a->y + bth * P * R;
+        /* output: y_t[:, r] = h^T C~_t[:, r] + D x_t[:, r] (gated), or its rank contraction */
+        double *yt = a->y + bth * P * (a->mimo_o ? 1 : R);
         for (int p = 0; p < P; ++p) {
+            double ysum = 0.0;
             for (int r = 0; r < R; ++r) {
                 double acc = 0.0;
                 for (int n = 0; n < N; ++n) acc += st[n * P + p] * Ct[n * R + r];
                 double v = acc + a->D[h] * xt[p * R + r];
                 if (a->z) {
-                    const double zv = a->z[bth * P * R + p * R + r];
+                    const double zv = a->mimo_z ? a->z[bth * P + p] * a->mimo_z[((int64_t)h * R + r) * P + p]
+                                                : a->z[bth * P * R + p * R + r];
                     v *= a->mutation == 8 ? sigmoid(zv) : zv * sigmoid(zv); /* planted (8): sigmoid gate */
                 }
-                yt[p * R + r] = v;
+                if (a->mimo_o) ysum += a->mimo_o[((int64_t)h * R + r) * P + p] * v;
+                else yt[p * R + r] = v;
             }
+            if (a->mimo_o) yt[p] = ysum;
         }
         memcpy(pB, Bt, sizeof(double) * N * R);
         for (int i = 0; i < P * R; ++i) px[i] = xt[i];
@@ -202,7 +222,7 @@ static void run_sequence(const m3o_args *a, int64_t b, int h) {
     if (a->pB1) memcpy(a->pB1 + bh * N * R, pB, sizeof(double) * N * R);
     if (a->px1) memcpy(a->px1 + bh * P * R, px, sizeof(double) * P * R);
     if (a->ang1) memcpy(a->ang1 + bh * NR, ang, sizeof(double) * NR);
-    free(st); free(pB); free(px); free(Bt); free(Ct); free(ang); free(col);
+    free(st); free(pB); free(px); free(Bt); free(Ct); free(ang); free(col); free(xe);
 }
 
 typedef struct { const m3o_args *a; int64_t begin, end; } work_t;

@@ -32,6 +32,11 @@ typedef struct {
     const double *dt_bias; /* [H] or NULL (= 0) */
     const double *z;       /* gate input laid out like y, or NULL (no gate) */
     int32_t half_split;    /* 1: pair i is components (i, i + N/2); 0: (2i, 2i + 1) */
+    /* MIMO projections by learned per-rank vectors [H, R, P] (NULL = absent):
+     *   mimo_x: x is [B, T, H, P] and the scan reads x_r[p] = x[p] mimo_x[h, r, p];
+     *   mimo_z: z is [B, T, H, P] and the gate reads z_r[p] = z[p] mimo_z[h, r, p];
+     *   mimo_o: y is [B, T, H, P] = sum_r mimo_o[h, r, p] y_r[p] (y_r after the gate). */
+    const double *mimo_x, *mimo_z, *mimo_o;
 } m3o_args;
 
 int m3o_scan(const m3o_args *a);
