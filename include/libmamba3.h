@@ -135,6 +135,33 @@ typedef struct {
     const float *b_bias, *c_bias;     /* [H, R, N] or NULL */
     const float *dt_bias;             /* [H] or NULL; read only with M3_FLAG_DT_SOFTPLUS */
     const void *z;                    /* gate input laid out like y (io dtype), or NULL: no gate */
+    /*
+     * MIMO projections by learned per-rank vectors, each [H, R, P] float32, or NULL (absent).
+     * torchmamba README, "Math notes", MIMO paragraph (per-head x / y / z expanded by a learned
+     * vector: D P + P R parameters rather than D P R); dotLLM PR #136, "What's deferred"
+     * (MIMO-in-Block: mimo_x / mimo_z projections and the post-scan rank contraction).
+     * m3_scan_mimo, m3_scan_noalloc and m3_step only (M3_EINVAL for m3_scan_siso); the
+     * gradient call rejects them (M3_EUNSUPPORTED).
+     *   mimo_x: x is rank-free [B, T, H, P]; the scan reads x_r[p] = x[p] mimo_x[h, r, p]
+     *           (on the bf16 path x_r is formed in fp32 and rounded once to bf16, as an
+     *           unexpanded x arrives; the carried prev_x holds x_r in fp32).
+     *   mimo_z: z is rank-free [B, T, H, P]; the gate reads z_r[p] = z[p] mimo_z[h, r, p]
+     *           (requires z).
+     *   mimo_o: y is [B, T, H, P] = sum_r mimo_o[h, r, p] y_r[p] of the gated per-rank
+     *           outputs, rounded once.
+     */
+    const float *mimo_x, *mimo_z, *mimo_o;
+    /*
+     * Row strides, in elements, between consecutive tokens (rows b*T + t) of inputs that are
+     * slices of a wider buffer, such as the in_proj output [B, T, d_in_proj] of the block
+     * (dotLLM PR #136, "Stage C": in_proj GEMM -> split -> ...); 0 = contiguous.  Within a row
+     * each tensor keeps its layout above ([H, P(, R)], [H, N(, R)], [H], [H, NR]); a stride
+     * must be 0 or at least the row's length and below 2^24.  A_stride applies to a per-token
+     * A.  Rows whose byte stride is not a multiple of 16 are read element by element.  The
+     * gradient call and the half-split pairing of B and C need contiguous inputs
+     * (M3_EUNSUPPORTED otherwise).  y is always contiguous.
+     */
+    int64_t x_stride, B_stride, C_stride, dt_stride, lam_stride, theta_stride, A_stride, z_stride;
 } m3_inputs;
 
 typedef struct {

@@ -46,10 +46,15 @@ class Shape(ctypes.Structure):
                 ("rope_pairs", ctypes.c_int32)]
 
 
+_ROW_STRIDED = ("x", "B", "C", "dt", "lam", "theta", "A", "z")
+
+
 class _Inputs(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("x", "Bm", "Cm", "dt", "lam", "theta", "A", "D",
-                 "b_norm_w", "c_norm_w", "b_bias", "c_bias", "dt_bias", "z")]
+    _fields_ = ([(n, ctypes.c_void_p) for n in
+                 ("x", "Bm", "Cm", "dt", "lam", "theta", "A", "D",
+                  "b_norm_w", "c_norm_w", "b_bias", "c_bias", "dt_bias", "z",
+                  "mimo_x", "mimo_z", "mimo_o")] +
+                [(n + "_stride", ctypes.c_int64) for n in _ROW_STRIDED])
 
 
 class _State(ctypes.Structure):
@@ -111,20 +116,42 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t, name, dtype, device, shape=None):
+def _need(t, name, dtype, device, shape=None, rows=False):
+    """Check a tensor argument.  With ``rows`` the tensor [B, T, ...] may be a slice of a wider
+    buffer: each token's row is contiguous and rows b*T + t are a fixed stride apart; the row
+    stride in elements is returned (0 when contiguous)."""
     if t is None:
-        return None
+        return None if not rows else 0
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.device != device:
         raise ValueError(f"{name} must be on {device}, got {t.device}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-    return t
+    if t.is_contiguous():
+        return 0 if rows else t
+    if rows and t.dim() >= 3:
+        rs = _row_stride(t)
+        if rs is not None:
+            return rs
+        raise ValueError(f"{name}: each token's row must be contiguous, rows evenly spaced")
+    raise ValueError(f"{name} must be contiguous")
+
+
+def _row_stride(t):
+    """Elements between consecutive token rows of [B, T, ...] with contiguous rows, or None."""
+    Bsz, T = t.shape[0], t.shape[1]
+    inner = 1
+    for d in range(t.dim() - 1, 1, -1):
+        if t.shape[d] != 1 and t.stride(d) != inner:
+            return None
+        inner *= t.shape[d]
+    rs = t.stride(1) if T > 1 else (t.stride(0) if Bsz > 1 else inner)
+    if T > 1 and Bsz > 1 and t.stride(0) != rs * T:
+        return None
+    return rs if rs >= inner else None
 
 
 def _stream(stream):
@@ -148,9 +175,17 @@ def _shape_of(x, B, chunk, bcnorm, eps, mimo, opts):
     if io is None:
         raise TypeError("x must be float32 or bfloat16")
     if mimo:
-        if x.dim() != 5:
-            raise ValueError("MIMO x must be [B, T, H, P, R]")
-        Bsz, T, H, P, R = x.shape
+        if B.dim() != 5:
+            raise ValueError("MIMO B must be [B, T, H, N, R]")
+        R = B.shape[4]
+        if opts.get("mimo_x") is not None:
+            if x.dim() != 4:
+                raise ValueError("x must be [B, T, H, P] with mimo_x")
+            Bsz, T, H, P = x.shape
+        else:
+            if x.dim() != 5:
+                raise ValueError("MIMO x must be [B, T, H, P, R]")
+            Bsz, T, H, P, R = x.shape
         N = B.shape[3]
     else:
         if x.dim() != 4:
@@ -178,29 +213,48 @@ def _rotated(s: Shape) -> int:
     return s.rope_pairs if s.flags & M3_FLAG_PARTIAL_ROPE else s.dstate // 2
 
 
+def _y_shape(s: Shape, mimo, mimo_o=None):
+    """Shape of y: [B, T, H, P], with a trailing R for a MIMO call without mimo_o."""
+    return (s.batch, s.seqlen, s.nheads, s.headdim) + ((s.rank,) if mimo and mimo_o is None else ())
+
+
 def _inputs(s: Shape, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
-            dt_bias=None, z=None):
+            dt_bias=None, z=None, mimo_x=None, mimo_z=None, mimo_o=None, strided=True):
+    """The C input block.  x, B, C, dt, lam, theta, a per-token A and z may be row-strided
+    slices (see ``_need``) unless ``strided`` is False."""
     dev, io_t = x.device, x.dtype
     f32 = torch.float32
-    bs = (s.batch, s.seqlen, s.nheads, s.dstate) + ((s.rank,) if mimo else ())
-    _need(B, "B", io_t, dev, bs)
-    _need(C, "C", io_t, dev, bs)
-    _need(dt, "dt", f32, dev, (s.batch, s.seqlen, s.nheads))
-    _need(lam, "lam", f32, dev, (s.batch, s.seqlen, s.nheads))
-    _need(theta, "theta", f32, dev, (s.batch, s.seqlen, s.nheads, _rotated(s)))
+    bt = (s.batch, s.seqlen, s.nheads)
+    bs = bt + (s.dstate,) + ((s.rank,) if mimo else ())
+    rank_free = (s.batch, s.seqlen, s.nheads, s.headdim)
+    full = rank_free + ((s.rank,) if mimo else ())
+    proj = (s.nheads, s.rank, s.headdim)
+    st = {}
+    st["x"] = _need(x, "x", io_t, dev, rank_free if mimo_x is not None else full, rows=True)
+    st["B"] = _need(B, "B", io_t, dev, bs, rows=True)
+    st["C"] = _need(C, "C", io_t, dev, bs, rows=True)
+    st["dt"] = _need(dt, "dt", f32, dev, bt, rows=True)
+    st["lam"] = _need(lam, "lam", f32, dev, bt, rows=True)
+    st["theta"] = _need(theta, "theta", f32, dev, bt + (_rotated(s),), rows=True)
     if s.flags & M3_FLAG_A_PER_TOKEN:
-        _need(A, "A", f32, dev, (s.batch, s.seqlen, s.nheads))
+        st["A"] = _need(A, "A", f32, dev, bt, rows=True)
     else:
         _need(A, "A", f32, dev, (s.nheads,))
+        st["A"] = 0
     _need(D, "D", f32, dev, (s.nheads,))
     _need(dt_bias, "dt_bias", f32, dev, (s.nheads,))
-    _need(z, "z", io_t, dev, tuple(x.shape))
+    st["z"] = _need(z, "z", io_t, dev, rank_free if mimo_z is not None else full, rows=True)
     _need(b_norm_w, "b_norm_w", f32, dev, (s.dstate,))
     _need(c_norm_w, "c_norm_w", f32, dev, (s.dstate,))
     _need(b_bias, "b_bias", f32, dev, (s.nheads, s.rank, s.dstate))
     _need(c_bias, "c_bias", f32, dev, (s.nheads, s.rank, s.dstate))
+    for t, name in ((mimo_x, "mimo_x"), (mimo_z, "mimo_z"), (mimo_o, "mimo_o")):
+        _need(t, name, f32, dev, proj)
+    if not strided and any(v != 0 for v in st.values()):
+        raise ValueError("this call takes contiguous inputs")
     return _Inputs(*(_ptr(t) for t in (x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w,
-                                        b_bias, c_bias, dt_bias, z)))
+                                        b_bias, c_bias, dt_bias, z, mimo_x, mimo_z, mimo_o)),
+                   *(int(st[k]) for k in _ROW_STRIDED))
 
 
 def new_state(batch, nheads, headdim, dstate, rank=1, device="cuda", rope_pairs=None):
@@ -230,18 +284,19 @@ def m3_scan_workspace_bytes(shape: Shape) -> int:
 def _scan(mimo, x, B, C, dt, lam, theta, A, D, *, chunk=64, bcnorm=True, eps=1e-5,
           b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, init=None, final=None,
           y=None, workspace=None, stream=None, rope_pairs=None, dt_softplus=False, dt_bias=None,
-          lam_sigmoid=False, z=None, half_split=False):
+          lam_sigmoid=False, z=None, half_split=False, mimo_x=None, mimo_z=None, mimo_o=None):
     lib = load()
     s = _shape_of(x, B, chunk, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A, dt_softplus=dt_softplus,
-                                                        lam_sigmoid=lam_sigmoid, half_split=half_split))
-    _need(x, "x", x.dtype, x.device)
+                                                        lam_sigmoid=lam_sigmoid, half_split=half_split,
+                                                        mimo_x=mimo_x))
     inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
-                  dt_bias, z)
+                  dt_bias, z, mimo_x, mimo_z, mimo_o)
+    ys = _y_shape(s, mimo, mimo_o)
     with _alloc_on(stream):
         if y is None:
-            y = torch.empty_like(x)
+            y = torch.empty(ys, dtype=x.dtype, device=x.device)
         else:
-            _need(y, "y", x.dtype, x.device, tuple(x.shape))
+            _need(y, "y", x.dtype, x.device, ys)
         if final is True:
             final = new_state(s.batch, s.nheads, s.headdim, s.dstate, s.rank, x.device, _rotated(s))
         st_in = _state(s, init, x.device, "init")
@@ -262,18 +317,19 @@ def _scan(mimo, x, B, C, dt, lam, theta, A, D, *, chunk=64, bcnorm=True, eps=1e-
 def m3_scan_noalloc(x, B, C, dt, lam, theta, A, D, *, y, chunk=64, bcnorm=True, eps=1e-5,
                     b_norm_w=None, c_norm_w=None, b_bias=None, c_bias=None, init=None, final=None,
                     stream=None, rope_pairs=None, dt_softplus=False, dt_bias=None, lam_sigmoid=False,
-                    z=None, half_split=False):
-    """The allocation-free scan (any rank: x [B,T,H,P] is rank 1, [B,T,H,P,R] rank R) with the
+                    z=None, half_split=False, mimo_x=None, mimo_z=None, mimo_o=None):
+    """The allocation-free scan (any rank: B [B,T,H,N] is rank 1, [B,T,H,N,R] rank R) with the
     library's static scratch as workspace.  The caller passes the output ``y`` and, to get the
     final state, ``final`` (a state dict as from ``new_state``); nothing is allocated here or
     in the library, so the call may run under HIP graph capture."""
     lib = load()
-    mimo = x.dim() == 5
+    mimo = B.dim() == 5
     s = _shape_of(x, B, chunk, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A, dt_softplus=dt_softplus,
-                                                        lam_sigmoid=lam_sigmoid, half_split=half_split))
-    _need(x, "x", x.dtype, x.device)
-    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo, dt_bias, z)
-    _need(y, "y", x.dtype, x.device, tuple(x.shape))
+                                                        lam_sigmoid=lam_sigmoid, half_split=half_split,
+                                                        mimo_x=mimo_x))
+    inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo, dt_bias, z,
+                  mimo_x, mimo_z, mimo_o)
+    _need(y, "y", x.dtype, x.device, _y_shape(s, mimo, mimo_o))
     st_in = _state(s, init, x.device, "init")
     st_out = _state(s, final, x.device, "final")
     rc = lib.m3_scan_noalloc(ctypes.byref(s), ctypes.byref(inp), _ptr(y),
@@ -300,31 +356,40 @@ def m3_scan_siso(x, B, C, dt, lam, theta, A, D, **kw):
 
 
 def m3_scan_mimo(x, B, C, dt, lam, theta, A, D, **kw):
-    """Rank-R MIMO chunked scan.  x [B,T,H,P,R], B/C [B,T,H,N,R]; ``chunk`` counts tokens."""
+    """Rank-R MIMO chunked scan.  x [B,T,H,P,R], B/C [B,T,H,N,R]; ``chunk`` counts tokens.
+
+    MIMO projections by learned per-rank vectors [H, R, P] (float32): ``mimo_x`` (x is then
+    [B,T,H,P] and rank r reads x * mimo_x[:, r]), ``mimo_z`` (z is [B,T,H,P], expanded the same
+    way) and ``mimo_o`` (y is [B,T,H,P] = sum_r mimo_o[:, r] * y_r).  x, B, C, dt, lam, theta,
+    a per-token A and z may be row-strided slices of a wider buffer (e.g. the block's in_proj
+    output): each token's row contiguous, rows evenly spaced."""
     return _scan(True, x, B, C, dt, lam, theta, A, D, **kw)
 
 
 def m3_step(x, B, C, dt, lam, theta, A, D, state, *, bcnorm=True, eps=1e-5, b_norm_w=None,
             c_norm_w=None, b_bias=None, c_bias=None, y=None, stream=None, rope_pairs=None,
-            dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None, half_split=False):
+            dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None, half_split=False,
+            mimo_x=None, mimo_z=None, mimo_o=None):
     """One decode step (T == 1) that updates ``state`` in place; returns y.
 
     x [B,1,H,P] (or [B,1,H,P,R]), B/C [B,1,H,N(,R)], dt/lam [B,1,H], theta [B,1,H,N/2]
-    (the same options as the scans; a per-token A is [B,1,H])."""
+    (the same options as the scans, MIMO projections and row-strided inputs included; a
+    per-token A is [B,1,H])."""
     lib = load()
-    mimo = x.dim() == 5
+    mimo = B.dim() == 5
     s = _shape_of(x, B, 16, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A, dt_softplus=dt_softplus,
-                                                     lam_sigmoid=lam_sigmoid, half_split=half_split))
+                                                     lam_sigmoid=lam_sigmoid, half_split=half_split,
+                                                     mimo_x=mimo_x))
     if s.seqlen != 1:
         raise ValueError("m3_step takes exactly one token (T == 1)")
-    _need(x, "x", x.dtype, x.device)
     inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
-                  dt_bias, z)
+                  dt_bias, z, mimo_x, mimo_z, mimo_o)
+    ys = _y_shape(s, mimo, mimo_o)
     with _alloc_on(stream):
         if y is None:
-            y = torch.empty_like(x)
+            y = torch.empty(ys, dtype=x.dtype, device=x.device)
         else:
-            _need(y, "y", x.dtype, x.device, tuple(x.shape))
+            _need(y, "y", x.dtype, x.device, ys)
     st = _state(s, state, x.device, "state")
     rc = lib.m3_step(ctypes.byref(s), ctypes.byref(inp), _ptr(y), ctypes.byref(st), _stream(stream))
     _check(rc, "m3_step")
@@ -351,9 +416,8 @@ def m3_scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5, b_n
     mimo = x.dim() == 5
     s = _shape_of(x, B, 16, bcnorm, eps, mimo, dict(rope_pairs=rope_pairs, A=A, dt_softplus=dt_softplus,
                                                      lam_sigmoid=lam_sigmoid, half_split=half_split))
-    _need(x, "x", x.dtype, x.device)
     inp = _inputs(s, x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias, c_bias, mimo,
-                  dt_bias, z)
+                  dt_bias, z, strided=False)
     _need(dy, "dy", x.dtype, x.device, tuple(x.shape))
     dev, f32 = x.device, torch.float32
     H, N, R = s.nheads, s.dstate, s.rank

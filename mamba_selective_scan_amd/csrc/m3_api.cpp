@@ -83,6 +83,44 @@ m3_status check_state(const m3_state *st, bool required, int nr) {
     return M3_OK;
 }
 
+// Effective row strides (elements between tokens b*T + t) of x, B, C, dt, lambda, theta, A,
+// z and y: the caller's, or the contiguous row length for 0.  A stride shorter than its row
+// gives M3_EINVAL, one of 2^24 or more M3_EUNSUPPORTED.
+enum { kRsX, kRsB, kRsC, kRsDt, kRsLam, kRsTh, kRsA, kRsZ, kRsY, kRsCount };
+struct RowStrides {
+    int64_t v[kRsCount];
+    bool contiguous_bc;  // B and C are contiguous [B, T, H, N, R]
+    bool any;            // a caller stride differs from the contiguous one
+};
+m3_status row_strides(const m3_shape *s, const m3_inputs *in, RowStrides &rs) {
+    const int64_t H = s->nheads, P = s->headdim, N = s->dstate, R = s->rank;
+    const int64_t nr = rotated_pairs(s);
+    const int64_t rx = in->mimo_x ? 1 : R, rz = in->mimo_z ? 1 : R, ry = in->mimo_o ? 1 : R;
+    const int64_t row[kRsCount] = {H * P * rx, H * N * R, H * N * R, H, H, H * nr, H, H * P * rz, H * P * ry};
+    const int64_t given[kRsCount] = {in->x_stride, in->B_stride, in->C_stride, in->dt_stride, in->lam_stride,
+                                     in->theta_stride, in->A_stride, in->z_stride, 0};
+    rs.any = false;
+    for (int k = 0; k < kRsCount; ++k) {
+        const int64_t g = given[k];
+        if (g < 0 || (g != 0 && g < row[k])) return M3_EINVAL;
+        if (g >= (int64_t)1 << 24) return M3_EUNSUPPORTED;
+        rs.v[k] = g ? g : row[k];
+        if (rs.v[k] != row[k]) rs.any = true;
+    }
+    rs.contiguous_bc = rs.v[kRsB] == row[kRsB] && rs.v[kRsC] == row[kRsC];
+    return M3_OK;
+}
+
+// Checks of the MIMO projection vectors: only with a rank (MIMO or step call), mimo_z only
+// with a gate input, 16-byte aligned.
+m3_status check_mimo_proj(const m3_inputs *in, bool rank_call) {
+    if (!in->mimo_x && !in->mimo_z && !in->mimo_o) return M3_OK;
+    if (!rank_call) return M3_EINVAL;
+    if (in->mimo_z && !in->z) return M3_EINVAL;
+    if (!aligned16(in->mimo_x) || !aligned16(in->mimo_z) || !aligned16(in->mimo_o)) return M3_EINVAL;
+    return M3_OK;
+}
+
 // Blocks, segments and workspace of one scan.
 struct Plan {
     int TB, nblk, nseg, bps, ncg, nsub, sbps;
@@ -98,6 +136,23 @@ TileShape tile_of(const m3_shape *s) {
     // the rank-1 path loads the angles of four pairs per 16-byte access
     if (v8 && s->rank == 1 && rotated_pairs(s) % 4 == 0) ts.mode = m3::kTileVec;
     else if (v8 && s->io == M3_BF16 && (s->rank == 2 || s->rank == 4 || s->rank == 8)) ts.mode = m3::kTileMimo;
+    return ts;
+}
+
+// The kernel variant a call runs: the shape's, except that row strides whose byte size is not
+// a multiple of 16, B and C rows of different strides, or the MIMO projections at rank 1, need
+// the element-load path, and the interleaved-rank path needs 16-byte rows of its (possibly
+// rank-free) x and z.  (The plan's segments follow the shape's variant, so the workspace size
+// depends on the shape alone.)
+TileShape kernel_tile(const m3_shape *s, const m3_inputs *in, const RowStrides &rs) {
+    TileShape ts = tile_of(s);
+    const int es = s->io == M3_BF16 ? 2 : 4;
+    auto a16 = [&](int k) { return (rs.v[k] * es) % 16 == 0; };
+    const bool rows16 = a16(kRsX) && a16(kRsB) && rs.v[kRsC] == rs.v[kRsB] && (!in->z || a16(kRsZ));
+    const bool proj = in->mimo_x || in->mimo_z || in->mimo_o;
+    if (ts.mode == m3::kTileVec && (proj || !rows16 || rs.v[kRsTh] % 4 != 0)) ts.mode = m3::kTileGen;
+    if (ts.mode == m3::kTileMimo && !rows16) ts.mode = m3::kTileGen;
+    ts.pj = proj;
     return ts;
 }
 
@@ -164,7 +219,11 @@ m3_status validate_scan(const m3_shape *s, const m3_inputs *in, const void *y, c
     if ((rc = check_state(fin, false, rotated_pairs(s))) != M3_OK) return rc;
     if (s->seqlen > 0 && s->batch > 0 && !y) return M3_EINVAL;
     if (!aligned16(y)) return M3_EINVAL;
-    const TileShape ts = tile_of(s);
+    if ((rc = check_mimo_proj(in, mimo)) != M3_OK) return rc;
+    RowStrides rs;
+    if ((rc = row_strides(s, in, rs)) != M3_OK) return rc;
+    if ((s->flags & M3_FLAG_HALF_SPLIT) && !rs.contiguous_bc) return M3_EUNSUPPORTED;
+    const TileShape ts = kernel_tile(s, in, rs);
     const bool bf = s->io == M3_BF16;
     if (m3::seg_kernel_lds_bytes(true, bf, ts) > 160 * 1024 || m3::seg_kernel_lds_bytes(false, bf, ts) > 160 * 1024)
         return M3_EUNSUPPORTED;
@@ -176,7 +235,9 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
                     m3_state *fin, void *ws, size_t ws_bytes, void *stream, bool mimo) {
     m3_status rc = validate_scan(s, in, y, init, fin, ws, mimo);
     if (rc != M3_OK) return rc;
-    const TileShape ts = tile_of(s);
+    RowStrides rs;
+    row_strides(s, in, rs);
+    const TileShape ts = kernel_tile(s, in, rs);
     const bool bf = s->io == M3_BF16;
     const Plan pl = plan_of(s);
     if (pl.total > 0 && (!ws || ws_bytes < pl.total)) return M3_EWORKSPACE;
@@ -213,6 +274,18 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     p.cnw = in->c_norm_w;
     p.bbias = in->b_bias;
     p.cbias = in->c_bias;
+    p.mx = in->mimo_x;
+    p.mz = in->mimo_z;
+    p.mo = in->mimo_o;
+    p.rsx = rs.v[kRsX];
+    p.rsb = rs.v[kRsB];
+    p.rsc = rs.v[kRsC];
+    p.rsdt = rs.v[kRsDt];
+    p.rslam = rs.v[kRsLam];
+    p.rsth = rs.v[kRsTh];
+    p.rsa = rs.v[kRsA];
+    p.rsz = rs.v[kRsZ];
+    p.rsy = rs.v[kRsY];
     p.y = y;
     if (init) {
         p.h0 = init->h;
@@ -300,6 +373,9 @@ m3_status validate_bwd(const m3_shape *s, const m3_inputs *in, const void *dy, c
     for (const void *q : ptrs)
         if (!aligned16(q)) return M3_EINVAL;
     if (!aligned16(ws)) return M3_EINVAL;
+    RowStrides rs;
+    if ((rc = row_strides(s, in, rs)) != M3_OK) return rc;
+    if (rs.any || in->mimo_x || in->mimo_z || in->mimo_o) return M3_EUNSUPPORTED;
     return M3_OK;
 }
 
@@ -675,6 +751,9 @@ m3_status m3_step(const m3_shape *s, const m3_inputs *in, void *y, m3_state *sta
     if ((rc = check_state(state, true, rotated_pairs(s))) != M3_OK) return rc;
     if (s->batch > 0 && !y) return M3_EINVAL;
     if (!aligned16(y)) return M3_EINVAL;
+    if ((rc = check_mimo_proj(in, true)) != M3_OK) return rc;
+    RowStrides rs;
+    if ((rc = row_strides(s, in, rs)) != M3_OK) return rc;
     if (s->batch == 0) return M3_OK;
     StepParams p;
     std::memset(&p, 0, sizeof p);
@@ -700,6 +779,18 @@ m3_status m3_step(const m3_shape *s, const m3_inputs *in, void *y, m3_state *sta
     p.cnw = in->c_norm_w;
     p.bbias = in->b_bias;
     p.cbias = in->c_bias;
+    p.mx = in->mimo_x;
+    p.mz = in->mimo_z;
+    p.mo = in->mimo_o;
+    p.rsx = rs.v[kRsX];
+    p.rsb = rs.v[kRsB];
+    p.rsc = rs.v[kRsC];
+    p.rsdt = rs.v[kRsDt];
+    p.rslam = rs.v[kRsLam];
+    p.rsth = rs.v[kRsTh];
+    p.rsa = rs.v[kRsA];
+    p.rsz = rs.v[kRsZ];
+    p.rsy = rs.v[kRsY];
     p.y = y;
     p.h = state->h;
     p.pB = state->prev_B;
@@ -714,7 +805,7 @@ const char *m3_status_str(m3_status status) {
     switch (status) {
         case M3_OK: return "M3_OK: success";
         case M3_EINVAL: return "M3_EINVAL: invalid argument (NULL pointer, bad size, odd N, rank < 1, unknown flag, rope_pairs outside 0..N/2 or misaligned pointer)";
-        case M3_EUNSUPPORTED: return "M3_EUNSUPPORTED: size outside the supported range (N, P <= 128, R <= 8, chunk in {16,32,64,128}, chunk*R <= 128)";
+        case M3_EUNSUPPORTED: return "M3_EUNSUPPORTED: size or option outside the supported range (N, P <= 128, R <= 8, chunk in {16,32,64,128}, chunk*R <= 128, row strides below 2^24; the gradient call needs contiguous inputs without MIMO projections)";
         case M3_EWORKSPACE: return "M3_EWORKSPACE: workspace missing or smaller than m3_scan_workspace_bytes()";
         case M3_EHIP: return "M3_EHIP: a HIP launch failed";
     }

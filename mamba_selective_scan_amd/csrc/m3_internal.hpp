@@ -33,7 +33,11 @@ struct ScanParams {
     const float *dt, *lam, *theta, *A, *D;  // A: [H], or [B, T, H] with kFlagAPerToken
     const float *bnw, *cnw, *bbias, *cbias;
     const float *dtbias;  // [H] or NULL (read with kFlagDtSoftplus)
-    const void *z;        // gate input laid out like y, or NULL
+    const void *z;        // gate input laid out like y (rank-free with mz), or NULL
+    const float *mx, *mz, *mo;  // MIMO projection vectors [H, R, P], or NULL
+    // row strides (elements between tokens b*T + t), never 0: x, B, C, dt, lambda, theta,
+    // A (per token), z, y
+    int64_t rsx, rsb, rsc, rsdt, rslam, rsth, rsa, rsz, rsy;
     void *y;
     // carried state
     const float *h0, *pB0, *px0, *ang0;  // initial (NULL = zeros)
@@ -63,6 +67,8 @@ struct StepParams {
     const float *bnw, *cnw, *bbias, *cbias;
     const float *dtbias;
     const void *z;
+    const float *mx, *mz, *mo;  // MIMO projection vectors [H, R, P], or NULL
+    int64_t rsx, rsb, rsc, rsdt, rslam, rsth, rsa, rsz, rsy;  // row strides (one token: row = b)
     void *y;
     float *h, *pB, *px, *ang;
 };
@@ -123,6 +129,7 @@ struct TileShape {
     int mode;  // kTileVec: rank 1 with N % 8 == 0 and P % 8 == 0 (16-byte accesses);
                // kTileMimo: bf16, rank 2, 4 or 8, N % 8 == 0, P % 8 == 0 (16-byte accesses);
                // kTileGen: anything else (element accesses)
+    bool pj = false;  // the call has MIMO projections: the kernels that read them (not kTileVec)
 };
 
 hipError_t launch_seg_state(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t stream);

@@ -89,12 +89,16 @@ __device__ __forceinline__ int row_tile() { return __builtin_amdgcn_readfirstlan
 constexpr int kModeGen = 0, kModeVec = 1, kModeMimo = 2;
 
 // SWZ_: XOR-swizzled X^T plane on the rank-1 16-byte path (see xt_off).
-template <class Io, int NP_, int PP_, int MODE_, bool SWZ_ = true>
+// PJ_: the variant that reads the MIMO projections (mimo_x, mimo_z, mimo_o) when given; the
+// kernels without it never test for them (element and interleaved-rank paths only).
+template <class Io, int NP_, int PP_, int MODE_, bool SWZ_ = true, bool PJ_ = false>
 struct SegCfg {
     using ET = typename Io::T;
     static constexpr bool BF = std::is_same<Io, IoBF16>::value;
     static constexpr bool VEC = MODE_ == kModeVec;
     static constexpr bool MV = MODE_ == kModeMimo;
+    static constexpr bool PJ = PJ_;
+    static_assert(!PJ || !VEC, "the rank-1 16-byte path takes no projections");
     static constexpr bool XSWZ = SWZ_ && VEC;
     static_assert(!MV || BF, "the interleaved-rank load path is bf16 only");
     static constexpr bool PACKED = (VEC || MV) && BF;  // raw B/C held as packed bf16 words
@@ -139,7 +143,9 @@ struct SegCfg {
     static constexpr size_t L_WB = al(WB_PLANE * ES * NPL);
     static constexpr size_t L_XT = al((size_t)PP * RPP * ES);
     static constexpr size_t L_HT = COL ? 0 : al(HT_PLANE * ES * NPL_HT);
-    static constexpr size_t L_Y = COL ? 0 : al((size_t)ROWS * PP * sizeof(ET));
+    // y staging: the per-wave rows in the io type; fp32 in the projection variant, whose rank
+    // contraction (mimo_o) sums fp32 per-rank terms there
+    static constexpr size_t L_Y = COL ? 0 : al((size_t)ROWS * PP * (PJ ? 4 : sizeof(ET)));
     // COL: the C~ plane [row][n] (fp16) and the G o L planes [t][s] (bf16 hi, lo)
     static constexpr size_t L_CT = COL ? al(BT_PLANE * 2) : 0;
     static constexpr size_t GL_PLANE = (size_t)ROWS * RPP;
@@ -252,10 +258,10 @@ struct Smem {
     }
 };
 
-// eta_{-1} = dt_0 (1 - lambda_0) of the call's first token (index g0 of [B, T, H]) after the
-// optional input activations: the weight of the carried previous B~ x^T in the first state.
-__device__ __forceinline__ float eta_first(const ScanParams &p, int64_t g0, int h) {
-    float dt = p.dt[g0], lam = p.lam[g0];
+// eta_{-1} = dt_0 (1 - lambda_0) of the call's first token of batch b after the optional input
+// activations: the weight of the carried previous B~ x^T in the first state.
+__device__ __forceinline__ float eta_first(const ScanParams &p, int64_t b, int h) {
+    float dt = p.dt[b * p.T * p.rsdt + h], lam = p.lam[b * p.T * p.rslam + h];
     if (p.flags & kFlagDtSoftplus) dt = softplus_f(dt + (p.dtbias ? p.dtbias[h] : 0.f));
     if (p.flags & kFlagLamSigmoid) lam = sigmoid_f(lam);
     return dt * (1.f - lam);
@@ -271,10 +277,13 @@ struct WgCtx {
     int h, cg, seg, p0, Pw, blk0, blk1;
     int R;      // rank (compile-time 1 on the SISO path)
     float invR; // 1 / R, to turn rows into tokens without an integer divide
+    int Rx, Rz, Ry;             // ranks of x, z, y in memory: 1 when rank-free (MIMO projections)
     const void *xb, *Bb, *Cb;  // x, B, C at (b, token 0, h) (x offset by the column group)
-    const float *thb, *dtb, *lamb;
+    const float *thb, *dtb, *lamb, *ab;  // theta, dt, lambda, per-token A at (b, token 0, h)
+    const void *zb;            // z at (b, token 0, h), offset by the column group
     void *yb;
-    int sx, sbc, sth, sdt;     // token strides in elements: H*P*R, H*N*R, H*nr, H
+    // row strides (elements between tokens) of x, B, C, theta, dt, lambda, A, z, y
+    int sx, sb, sc, sth, sdt, slam, sa, sz, sy;
     float invN, eps;
     bool bcnorm, affine;
     bool rowscale;  // fp16 B~ / C~ rows get a power-of-two scale each (no norm, or gains / biases)
@@ -306,10 +315,11 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
         // Uniform 64-bit block bases plus 32-bit per-lane byte offsets.
         const bool rv = row < g.Tv;
         if constexpr ((PART & kLoadBc) != 0) {
-        const char *bbase = (const char *)c.Bb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
-        const char *cbase = (const char *)c.Cb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
+        // (B and C share their row stride on the 16-byte paths)
+        const char *bbase = (const char *)c.Bb + (int64_t)g.t0 * c.sb * (int64_t)sizeof(ET);
+        const char *cbase = (const char *)c.Cb + (int64_t)g.t0 * c.sb * (int64_t)sizeof(ET);
         const char *tbase = (const char *)c.thb + (int64_t)g.t0 * c.sth * 4;
-        const uint32_t boff = (uint32_t)row * (uint32_t)(c.sbc * sizeof(ET)) + (uint32_t)(8 * gq * sizeof(ET));
+        const uint32_t boff = (uint32_t)row * (uint32_t)(c.sb * sizeof(ET)) + (uint32_t)(8 * gq * sizeof(ET));
         const uint32_t toff = (uint32_t)row * (uint32_t)(c.sth * 4) + (uint32_t)(16 * gq);
 #pragma unroll
         for (int kk = 0; kk < Cfg::KS; ++kk) {
@@ -356,17 +366,20 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
         // slots past the block end or the padded n / p range load zeros.
         const int R = c.R;
         const int Tv = g.Tv;
-        const int vpt = (Cfg::NP * R) >> 3, xvpt = (Cfg::PP * R) >> 3;
+        // x holds P values per token when rank-free (MIMO projection of x), P R otherwise
+        const int Rx = Cfg::PJ ? c.Rx : R;
+        const int vpt = (Cfg::NP * R) >> 3, xvpt = (Cfg::PP * Rx) >> 3;
         const float ivpt = 1.f / (float)vpt, ixvpt = 1.f / (float)xvpt;
-        const char *bbase = (const char *)c.Bb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
-        const char *cbase = (const char *)c.Cb + (int64_t)g.t0 * c.sbc * (int64_t)sizeof(ET);
+        // (B and C share their row stride on the 16-byte paths)
+        const char *bbase = (const char *)c.Bb + (int64_t)g.t0 * c.sb * (int64_t)sizeof(ET);
+        const char *cbase = (const char *)c.Cb + (int64_t)g.t0 * c.sb * (int64_t)sizeof(ET);
 #pragma unroll
         for (int m = 0; m < Cfg::NBV; ++m) {
             const int v = tid + 256 * m;
             const int tok = (int)(((float)v + 0.5f) * ivpt), o = v - tok * vpt;
             u32x4_t vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
             if (tok < Tv && o * 8 < N * R) {
-                const uint32_t off = (uint32_t)tok * (uint32_t)(c.sbc * sizeof(ET)) + (uint32_t)(o * 16);
+                const uint32_t off = (uint32_t)tok * (uint32_t)(c.sb * sizeof(ET)) + (uint32_t)(o * 16);
                 vb = *(const u32x4_t *)(bbase + off);
                 if constexpr (WANT_C) vc = *(const u32x4_t *)(cbase + off);
             }
@@ -382,7 +395,7 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
             const int v = tid + 256 * m;
             const int tok = (int)(((float)v + 0.5f) * ixvpt), o = v - tok * xvpt;
             u32x4_t vx = {0u, 0u, 0u, 0u};
-            if (tok < Tv && o * 8 < c.Pw * R)
+            if (tok < Tv && o * 8 < c.Pw * Rx)
                 vx = *(const u32x4_t *)(xbase + (uint32_t)tok * (uint32_t)(c.sx * sizeof(ET)) + (uint32_t)(o * 16));
 #pragma unroll
             for (int k = 0; k < 4; ++k) rb.x[m * 4 + k] = vx[k];
@@ -391,23 +404,23 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
         for (int m = 0; m < Cfg::TN; ++m) {
             const int e = tid + 256 * m;
             const int tr = e / (Cfg::NP / 2), pc = e - tr * (Cfg::NP / 2);
-            rb.th[m] = (tr < Tv && pc < p.nr) ? p.theta[((b * T + g.t0 + tr) * H + h) * (int64_t)p.nr + pc] : 0.f;
+            rb.th[m] = (tr < Tv && pc < p.nr) ? c.thb[(int64_t)(g.t0 + tr) * c.sth + pc] : 0.f;
         }
     } else {
         // general layout (rank R, any even N, any P): element loads
         const int R = c.R;
         const int tok = tok_of(row, c), r = row - tok * R;
         const bool rv = tok < g.Tv;
-        const int64_t base = ((b * T + g.t0 + tok) * H + h) * (int64_t)N * R + r;
+        const ET *bp = (const ET *)c.Bb + (int64_t)(g.t0 + tok) * c.sb + r;
+        const ET *cp = (const ET *)c.Cb + (int64_t)(g.t0 + tok) * c.sc + r;
 #pragma unroll
         for (int kk = 0; kk < Cfg::KS; ++kk) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int n = kk * 32 + 8 * gq + j;
                 const bool ok = rv && n < N;
-                rb.b[kk][j] = __float_as_uint(ok ? Io::ld((const ET *)p.Bm + base + (int64_t)n * R) : 0.f);
-                if constexpr (WANT_C)
-                    rb.c[kk][j] = __float_as_uint(ok ? Io::ld((const ET *)p.Cm + base + (int64_t)n * R) : 0.f);
+                rb.b[kk][j] = __float_as_uint(ok ? Io::ld(bp + (int64_t)n * R) : 0.f);
+                if constexpr (WANT_C) rb.c[kk][j] = __float_as_uint(ok ? Io::ld(cp + (int64_t)n * R) : 0.f);
             }
         }
 #pragma unroll
@@ -416,28 +429,33 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
             const int xrow = e / Cfg::PP, pc = e - xrow * Cfg::PP;
             const int xt = tok_of(xrow, c), xrk = xrow - xt * R;
             float v = 0.f;
-            if (xt < g.Tv && pc < c.Pw)
-                v = Io::ld((const ET *)p.x + ((b * T + g.t0 + xt) * H + h) * (int64_t)P * R + (int64_t)(c.p0 + pc) * R + xrk);
+            if (xt < g.Tv && pc < c.Pw) {
+                if (Cfg::PJ && p.mx)  // rank-free x expanded by the learned vector of rank xrk
+                    v = Io::ld((const ET *)c.xb + (int64_t)(g.t0 + xt) * c.sx + pc) *
+                        p.mx[((int64_t)h * R + xrk) * P + c.p0 + pc];
+                else
+                    v = Io::ld((const ET *)c.xb + (int64_t)(g.t0 + xt) * c.sx + (int64_t)pc * R + xrk);
+            }
             rb.x[m] = __float_as_uint(v);
         }
 #pragma unroll
         for (int m = 0; m < Cfg::TN; ++m) {
             const int e = tid + 256 * m;
             const int tr = e / (Cfg::NP / 2), pc = e - tr * (Cfg::NP / 2);
-            rb.th[m] = (tr < g.Tv && pc < p.nr) ? p.theta[((b * T + g.t0 + tr) * H + h) * (int64_t)p.nr + pc] : 0.f;
+            rb.th[m] = (tr < g.Tv && pc < p.nr) ? c.thb[(int64_t)(g.t0 + tr) * c.sth + pc] : 0.f;
         }
     }
     if ((PART & kLoadXs) != 0 && wave == 0) {
         rb.dt = rb.lam = rb.dtn = rb.lamn = rb.av = 0.f;
-        const float *db = c.dtb + (int64_t)g.t0 * c.sdt, *lb = c.lamb + (int64_t)g.t0 * c.sdt;
-        const uint32_t o = (uint32_t)lane * (uint32_t)c.sdt;
+        const float *db = c.dtb + (int64_t)g.t0 * c.sdt, *lb = c.lamb + (int64_t)g.t0 * c.slam;
+        const uint32_t od = (uint32_t)lane * (uint32_t)c.sdt, ol = (uint32_t)lane * (uint32_t)c.slam;
         if (lane < g.Tv) {
-            rb.dt = db[o];
-            rb.lam = lb[o];
-            if (p.flags & kFlagAPerToken) rb.av = (p.A + (c.b * T + g.t0) * H + h)[o];
+            rb.dt = db[od];
+            rb.lam = lb[ol];
+            if (p.flags & kFlagAPerToken) rb.av = c.ab[(int64_t)(g.t0 + lane) * c.sa];
             if (g.t0 + lane + 1 < T) {
-                rb.dtn = db[o + c.sdt];
-                rb.lamn = lb[o + c.sdt];
+                rb.dtn = db[od + c.sdt];
+                rb.lamn = lb[ol + c.slam];
             }
         }
     }
@@ -454,14 +472,14 @@ __device__ __forceinline__ void load_z(RawZ<Cfg> &rz, const ScanParams &p, const
     const int tid = threadIdx.x;
     const int R = c.R;
     // z at (b, token t0, h), offset by the column group like x
-    const ET *zb = (const ET *)p.z + ((c.b * p.T + g.t0) * p.H + c.h) * (int64_t)p.P * R + (int64_t)c.p0 * R;
+    const ET *zb = (const ET *)c.zb + (int64_t)g.t0 * c.sz;
     if constexpr (Cfg::VEC) {
 #pragma unroll
         for (int m = 0; m < Cfg::XN / 4; ++m) {
             const int e = tid + 256 * m;
             const int zr = e / (Cfg::PP / Cfg::XW), pc = (e % (Cfg::PP / Cfg::XW)) * Cfg::XW;
             u32x4_t v = {0u, 0u, 0u, 0u};
-            if (zr < g.Tv && pc < c.Pw) v = *(const u32x4_t *)(zb + (int64_t)zr * c.sx + pc);
+            if (zr < g.Tv && pc < c.Pw) v = *(const u32x4_t *)(zb + (int64_t)zr * c.sz + pc);
 #pragma unroll
             for (int k = 0; k < 4; ++k) rz.w[m * 4 + k] = v[k];
         }
@@ -473,7 +491,7 @@ __device__ __forceinline__ void load_z(RawZ<Cfg> &rz, const ScanParams &p, const
             const int v = tid + 256 * m;
             const int tok = (int)(((float)v + 0.5f) * ixvpt), o = v - tok * xvpt;
             u32x4_t vz = {0u, 0u, 0u, 0u};
-            if (tok < g.Tv && o * 8 < c.Pw * R) vz = *(const u32x4_t *)(zb + (int64_t)tok * c.sx + o * 8);
+            if (tok < g.Tv && o * 8 < c.Pw * R) vz = *(const u32x4_t *)(zb + (int64_t)tok * c.sz + o * 8);
 #pragma unroll
             for (int k = 0; k < 4; ++k) rz.w[m * 4 + k] = vz[k];
         }
@@ -484,7 +502,7 @@ __device__ __forceinline__ void load_z(RawZ<Cfg> &rz, const ScanParams &p, const
             const int zrow = e / Cfg::PP, pc = e - zrow * Cfg::PP;
             const int zt = tok_of(zrow, c), zrk = zrow - zt * R;
             float v = 0.f;
-            if (zt < g.Tv && pc < c.Pw) v = Io::ld(zb + (int64_t)zt * c.sx + (int64_t)pc * R + zrk);
+            if (zt < g.Tv && pc < c.Pw) v = Io::ld(zb + (int64_t)zt * c.sz + (int64_t)pc * R + zrk);
             rz.w[m] = __float_as_uint(v);
         }
     }
@@ -651,11 +669,34 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
     }
     // x -> X^T [p][row]
     if constexpr (Cfg::MV) {
-        // one vector holds 8 / R columns x R ranks: R consecutive rows of each column
         const int R = c.R;
+        uint16_t *xt = (uint16_t *)sm.xt;
+        if (Cfg::PJ && p.mx) {
+            // rank-free x: one vector holds 8 columns of a token; rank r of column q takes
+            // x[q] mimo_x[h, r, q], rounded once to bf16, in the R consecutive rows of the token
+            const int xvpt = Cfg::PP >> 3;
+            const float ixvpt = 1.f / (float)xvpt;
+            const float *mxh = p.mx + (int64_t)c.h * R * p.P + c.p0;
+#pragma unroll
+            for (int m = 0; m < Cfg::NXV; ++m) {
+                const int v = tid + 256 * m;
+                const int tok = (int)(((float)v + 0.5f) * ixvpt), o = v - tok * xvpt;
+                if (tok * R >= Cfg::ROWS) continue;
+                const int q0 = o * 8;
+                const bool live = q0 < c.Pw;  // columns past the group width hold zeros
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t w = rb.x[m * 4 + (i >> 1)];
+                    const float xv = __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+                    uint16_t *dst = xt + xt_off<Cfg>(q0 + i, tok * R);
+                    for (int r = 0; r < R; ++r)
+                        dst[r] = (uint16_t)f2bf(live ? xv * mxh[(int64_t)r * p.P + q0 + i] : 0.f);
+                }
+            }
+        } else {
+        // one vector holds 8 / R columns x R ranks: R consecutive rows of each column
         const int xvpt = (Cfg::PP * R) >> 3;
         const float ixvpt = 1.f / (float)xvpt;
-        uint16_t *xt = (uint16_t *)sm.xt;
 #pragma unroll
         for (int m = 0; m < Cfg::NXV; ++m) {
             const int v = tid + 256 * m;
@@ -672,6 +713,7 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
             } else {
                 *(u32x4_t *)(xt + xt_off<Cfg>(p0, row0)) = u32x4_t{rb.x[m * 4], rb.x[m * 4 + 1], rb.x[m * 4 + 2], rb.x[m * 4 + 3]};
             }
+        }
         }
     } else if constexpr (Cfg::VEC) {
 #pragma unroll
@@ -1167,18 +1209,28 @@ __device__ __forceinline__ WgCtx make_ctx(const ScanParams &p, int nsegk, int bp
     c.R = Cfg::VEC ? 1 : p.R;
     c.invR = 1.f / (float)c.R;
     using ET = typename Cfg::ET;
-    const int64_t tok0 = c.b * p.T * p.H + c.h;  // (b, token 0, h)
-    c.sx = p.H * p.P * c.R;
-    c.sbc = p.H * p.N * c.R;
-    c.sth = p.H * p.nr;
-    c.sdt = p.H;
-    c.xb = (const ET *)p.x + tok0 * p.P * c.R + (int64_t)c.p0 * c.R;
-    c.Bb = (const ET *)p.Bm + tok0 * p.N * c.R;
-    c.Cb = (const ET *)p.Cm + tok0 * p.N * c.R;
-    c.thb = p.theta + tok0 * p.nr;
-    c.dtb = p.dt + tok0;
-    c.lamb = p.lam + tok0;
-    c.yb = (ET *)p.y + tok0 * p.P * c.R + (int64_t)c.p0 * c.R;
+    const int64_t row0 = c.b * p.T;  // row of (b, token 0)
+    c.Rx = p.mx ? 1 : c.R;
+    c.Rz = p.mz ? 1 : c.R;
+    c.Ry = p.mo ? 1 : c.R;
+    c.sx = (int)p.rsx;
+    c.sb = (int)p.rsb;
+    c.sc = (int)p.rsc;
+    c.sth = (int)p.rsth;
+    c.sdt = (int)p.rsdt;
+    c.slam = (int)p.rslam;
+    c.sa = (int)p.rsa;
+    c.sz = (int)p.rsz;
+    c.sy = (int)p.rsy;
+    c.xb = (const ET *)p.x + row0 * p.rsx + ((int64_t)c.h * p.P + c.p0) * c.Rx;
+    c.Bb = (const ET *)p.Bm + row0 * p.rsb + (int64_t)c.h * p.N * c.R;
+    c.Cb = (const ET *)p.Cm + row0 * p.rsc + (int64_t)c.h * p.N * c.R;
+    c.thb = p.theta + row0 * p.rsth + (int64_t)c.h * p.nr;
+    c.dtb = p.dt + row0 * p.rsdt + c.h;
+    c.lamb = p.lam + row0 * p.rslam + c.h;
+    c.ab = p.A + row0 * p.rsa + c.h;
+    c.zb = (const ET *)p.z + row0 * p.rsz + ((int64_t)c.h * p.P + c.p0) * c.Rz;
+    c.yb = (ET *)p.y + row0 * p.rsy + ((int64_t)c.h * p.P + c.p0) * c.Ry;
     c.invN = 1.f / (float)p.N;
     c.eps = p.eps;
     c.bcnorm = (p.flags & kFlagNorm) != 0;
@@ -1207,9 +1259,9 @@ __device__ __forceinline__ void stage_affine(const Sm &sm, const ScanParams &p, 
 }
 
 // ============================================================ state kernel
-template <class Io, int NP, int PP, int MODE>
+template <class Io, int NP, int PP, int MODE, bool PJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) void seg_state_kernel(ScanParams p) {
-    using Cfg = SegCfg<Io, NP, PP, MODE>;
+    using Cfg = SegCfg<Io, NP, PP, MODE, true, PJ>;
     constexpr bool VEC = Cfg::VEC;
     using Frag = typename std::conditional<Cfg::BF, FragH, FragF>::type;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1306,12 +1358,12 @@ __device__ __forceinline__ void load_z_col(RawZCol &rz, const ScanParams &p, con
     using ET = typename Io::T;
     const int lane = threadIdx.x & 63, l16 = lane & 15, gq = lane >> 4;
     const int pc = row_tile() * 16 + 4 * gq;
-    const ET *zb = (const ET *)p.z + ((c.b * p.T + g.t0) * p.H + c.h) * (int64_t)p.P + c.p0;
+    const ET *zb = (const ET *)c.zb + (int64_t)g.t0 * c.sz;
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
         const int t = T * 16 + l16;
         u32x2_t v = {0u, 0u};
-        if (t < g.Tv && pc < c.Pw) v = *(const u32x2_t *)(zb + (int64_t)t * c.sx + pc);
+        if (t < g.Tv && pc < c.Pw) v = *(const u32x2_t *)(zb + (int64_t)t * c.sz + pc);
         rz.w[T] = v;
     }
 }
@@ -1450,7 +1502,7 @@ __device__ __forceinline__ void col_outputs(const Sm &sm, const ScanParams &p, c
                 for (int i = 0; i < 4; ++i) yv[i] *= silu_f(zv[i]);
             }
             if (t < g.Tv && pc < c.Pw)
-                *(u32x2_t *)((ET *)c.yb + (g.t0 + t) * c.sx + pc) = u32x2_t{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])};
+                *(u32x2_t *)((ET *)c.yb + (g.t0 + t) * c.sy + pc) = u32x2_t{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])};
         }
     }
 }
@@ -1458,9 +1510,9 @@ __device__ __forceinline__ void col_outputs(const Sm &sm, const ScanParams &p, c
 // ============================================================ output kernel
 // With N above 64 the LDS planes allow one workgroup per compute unit (one wave per
 // SIMD), so such variants may use the whole register file.
-template <class Io, int NP, int PP, int MODE, bool GATE>
+template <class Io, int NP, int PP, int MODE, bool GATE, bool PJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1 : 2, NP > 64 ? 1 : 2))) void seg_output_kernel(ScanParams p) {
-    using Cfg = SegCfg<Io, NP, PP, MODE, !GATE>;
+    using Cfg = SegCfg<Io, NP, PP, MODE, !GATE, PJ>;
     constexpr bool VEC = Cfg::VEC;
     using ET = typename Io::T;
     using Frag = typename std::conditional<Cfg::BF, FragH, FragF>::type;
@@ -1483,9 +1535,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     RawZ<Cfg> rz;
     RawZCol rzc;
     BlockGeo g = block_geo(p, c.blk0);
+    // With a MIMO projection of z or y the epilogue reads z from memory itself (the y staging
+    // area then holds fp32 per-rank outputs); otherwise z is prefetched into that area.
+    const bool proj_o = Cfg::PJ && p.mo;
+    const bool zpre = GATE && !(Cfg::PJ && (p.mz || p.mo));
     if constexpr (GATE) {
         if constexpr (Cfg::COL) load_z_col<Io>(rzc, p, c, g);
-        else load_z<Io>(rz, p, c, g);
+        else if (zpre) load_z<Io>(rz, p, c, g);
     }
     if constexpr (Cfg::COL) init_gl_zero_tiles<Cfg>(sm);
     load_block<Io>(rb, p, c, g);
@@ -1520,8 +1576,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         }
     } else {
         {
-            const int64_t g0 = (c.b * p.T) * p.H + c.h;  // token 0 of the call
-            const float eta0 = (p.pB0 && p.px0) ? eta_first(p, g0, c.h) : 0.f;
+            const float eta0 = (p.pB0 && p.px0) ? eta_first(p, c.b, c.h) : 0.f;
 #pragma unroll
             for (int m = 0; m < TPW; ++m) {
                 hs[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1610,7 +1665,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         lds_barrier();  // every wave is done with the previous block's LDS planes
         float inv_hs = 1.f;
         if constexpr (!Cfg::COL) {
-            if constexpr (GATE) stage_z<Cfg>(rz, sm, c);  // read by the epilogue after two more barriers
+            if (zpre) stage_z<Cfg>(rz, sm, c);  // read by the epilogue after two more barriers
             inv_hs = write_ht<Cfg>(sm, hs);  // the state entering this block (read after two more barriers)
         }
         if constexpr (Cfg::MV) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.bt, (uint16_t *)sm.bt + Cfg::BT_PLANE, c);
@@ -1801,7 +1856,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 float yv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) yv[i] = yacc[pt][i] + Dh * xv[i];
-                if constexpr (GATE) {
+                if (GATE && !zpre) {
+                    // z read from memory: rank-free and expanded by mimo_z[h, r, :], or per rank
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tk = tok_of(row0 + i, c), r = row0 + i - tk * R;
+                        float zv = 0.f;
+                        if (tk < g.Tv && pc < c.Pw) {
+                            const ET *zr = (const ET *)c.zb + (int64_t)(g.t0 + tk) * c.sz;
+                            zv = p.mz ? Io::ld(zr + pc) * p.mz[((int64_t)c.h * R + r) * p.P + c.p0 + pc]
+                                      : Io::ld(zr + (int64_t)pc * R + r);
+                        }
+                        yv[i] *= silu_f(zv);
+                    }
+                } else if constexpr (GATE) {
                     // z of these outputs, staged at the positions their y values take
                     float zv[4];
                     if constexpr (Cfg::MV) {
@@ -1825,7 +1893,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
 #pragma unroll
                     for (int i = 0; i < 4; ++i) yv[i] *= silu_f(zv[i]);
                 }
-                if constexpr (Cfg::MV) {
+                if (proj_o) {
+                    // per-rank outputs in fp32, [row][p], for the rank contraction below
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ((float *)sm.ys)[(row0 + i) * PP + pc] = yv[i];
+                } else if constexpr (Cfg::MV) {
                     // staged in the global order [token][p][rank]
                     const uint32_t w01 = pack_bf16(yv[0], yv[1]), w23 = pack_bf16(yv[2], yv[3]);
                     if (R == 2) {
@@ -1852,11 +1924,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         // raw inputs), issued once this block's outputs are staged (they overlap the stores
         // and the carry)
         if (blk + 1 < c.blk1) {
-            if constexpr (GATE) load_z<Io>(rz, p, c, gn);
+            if (zpre) load_z<Io>(rz, p, c, gn);
             if constexpr (!VEC) load_block<Io>(rb, p, c, gn);
         }
         // ---- y: this wave's rows, staged in its own part of the staging area (LDS
         // operations of one wave complete in order), stored as 16-byte vectors
+        if (proj_o) {
+            // y[t, q] = sum_r mimo_o[h, r, q] y_r[t, q]: a token's ranks may lie in the rows
+            // of two waves, so the whole block's staging is read after a barrier
+            lds_barrier();
+            const float *ysf = (const float *)sm.ys;
+            const float *moh = p.mo + (int64_t)c.h * R * p.P + c.p0;
+            for (int e = tid; e < g.Tv * PP; e += 256) {
+                const int tk = e / PP, q = e - tk * PP;
+                if (q >= c.Pw) continue;
+                float acc = 0.f;
+                for (int r = 0; r < R; ++r) acc += moh[(int64_t)r * p.P + q] * ysf[(tk * R + r) * PP + q];
+                Io::st((ET *)c.yb + (g.t0 + tk) * c.sy + q, acc);
+            }
+        } else {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
         __builtin_amdgcn_wave_barrier();
         {
@@ -1871,7 +1957,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                     const int e = lane + 64 * m;
                     const int tk = tk0 + (int)(((float)e + 0.5f) * iy), o = e - (tk - tk0) * yvpt;
                     if (tk < g.Tv && o * 8 < c.Pw * R)
-                        *(u32x4_t *)((ET *)c.yb + (g.t0 + tk) * c.sx + o * 8) = *(const u32x4_t *)(ys + tk * PP * R + o * 8);
+                        *(u32x4_t *)((ET *)c.yb + (g.t0 + tk) * c.sy + o * 8) = *(const u32x4_t *)(ys + tk * PP * R + o * 8);
                 }
             } else if constexpr (VEC) {
 #pragma unroll
@@ -1879,16 +1965,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                     const int e = lane + 64 * m;
                     const int yr = tt * 16 + e / (PP / Cfg::XW), pc = (e % (PP / Cfg::XW)) * Cfg::XW;
                     if (yr < Rv && pc < c.Pw)
-                        *(u32x4_t *)((ET *)c.yb + (g.t0 + yr) * c.sx + pc) = *(const u32x4_t *)(ys + ys_off<Cfg>(yr, pc));
+                        *(u32x4_t *)((ET *)c.yb + (g.t0 + yr) * c.sy + pc) = *(const u32x4_t *)(ys + ys_off<Cfg>(yr, pc));
                 }
             } else {
                 for (int e = lane; e < 16 * PP; e += 64) {
                     const int yr = tt * 16 + e / PP, pc = e - (e / PP) * PP;
                     if (yr >= Rv || pc >= c.Pw) continue;
                     const int tok = tok_of(yr, c), r = yr - tok * R;
-                    ((ET *)c.yb)[(g.t0 + tok) * c.sx + (int64_t)pc * R + r] = ys[ys_off<Cfg>(yr, pc)];
+                    ((ET *)c.yb)[(g.t0 + tok) * c.sy + (int64_t)pc * R + r] = ys[ys_off<Cfg>(yr, pc)];
                 }
             }
+        }
         }
         }  // row-owned outputs
         // ---- carry to the next block (H^T is rewritten after the next top barrier)
@@ -1966,8 +2053,7 @@ __global__ __launch_bounds__(256) void seg_prefix_kernel(ScanParams p) {
         const int pp = pt * 16 + l16;
         f32x4_t H = {0.f, 0.f, 0.f, 0.f};
         if (p.h0 || (p.pB0 && p.px0)) {
-            const int64_t g0 = (b * p.T) * p.H + h;  // token 0 of the call
-            const float eta0 = (p.pB0 && p.px0) ? eta_first(p, g0, h) : 0.f;
+            const float eta0 = (p.pB0 && p.px0) ? eta_first(p, b, h) : 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int nn = nt * 16 + 4 * gq + i;
@@ -2028,18 +2114,18 @@ static hipError_t set_lds(K kern, size_t bytes) {
     return hipSuccess;
 }
 
-template <class Io, int NP, int PP, int MODE>
-static hipError_t launch_seg_t(bool output, const ScanParams &p, hipStream_t st) {
-    using Cfg = SegCfg<Io, NP, PP, MODE>;
+template <class Io, int NP, int PP, int MODE, bool PJ>
+static hipError_t launch_seg_pj(bool output, const ScanParams &p, hipStream_t st) {
+    using Cfg = SegCfg<Io, NP, PP, MODE, true, PJ>;
     if (output) {
         // variant with the silu(z) output gate when z is given
-        auto kern = p.z ? seg_output_kernel<Io, NP, PP, MODE, true> : seg_output_kernel<Io, NP, PP, MODE, false>;
+        auto kern = p.z ? seg_output_kernel<Io, NP, PP, MODE, true, PJ> : seg_output_kernel<Io, NP, PP, MODE, false, PJ>;
         hipError_t e = set_lds(kern, Cfg::OUTPUT_BYTES);
         if (e != hipSuccess) return e;
         const int64_t nwg = p.B * p.H * (int64_t)p.ncg * p.nseg;
         hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), Cfg::OUTPUT_BYTES, st, p);
     } else {
-        auto kern = seg_state_kernel<Io, NP, PP, MODE>;
+        auto kern = seg_state_kernel<Io, NP, PP, MODE, PJ>;
         hipError_t e = set_lds(kern, Cfg::STATE_BYTES);
         if (e != hipSuccess) return e;
         const int64_t nwg = p.B * p.H * (int64_t)p.ncg * p.nsub;
@@ -2047,6 +2133,24 @@ static hipError_t launch_seg_t(bool output, const ScanParams &p, hipStream_t st)
         hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), Cfg::STATE_BYTES, st, p);
     }
     return hipGetLastError();
+}
+
+// the projection variant when the call has MIMO projections (never on the rank-1 16-byte path)
+template <class Io, int NP, int PP, int MODE>
+static hipError_t launch_seg_t(bool output, const TileShape &ts, const ScanParams &p, hipStream_t st) {
+    if constexpr (MODE != kModeVec) {
+        if (ts.pj) return launch_seg_pj<Io, NP, PP, MODE, true>(output, p, st);
+    } else {
+        if (ts.pj) return hipErrorInvalidValue;
+    }
+    return launch_seg_pj<Io, NP, PP, MODE, false>(output, p, st);
+}
+template <class Io, int NP, int PP, int MODE>
+static size_t seg_bytes_t(bool output, const TileShape &ts) {
+    using Cfg = SegCfg<Io, NP, PP, MODE>;
+    using CfgP = SegCfg<Io, NP, PP, MODE, true, MODE != kModeVec>;
+    if (ts.pj) return output ? CfgP::OUTPUT_BYTES : CfgP::STATE_BYTES;
+    return output ? Cfg::OUTPUT_BYTES : Cfg::STATE_BYTES;
 }
 
 #define M3_SHAPES(X, Io, MODE) \
@@ -2063,9 +2167,8 @@ static hipError_t launch_seg_t(bool output, const ScanParams &p, hipStream_t st)
         return 0;                                                                                     \
     }
 #define M3_LAUNCH_CASE(IoT, NPV, PPV, V) \
-    if (ts.np == NPV && ts.pp == PPV) return launch_seg_t<IoT, NPV, PPV, V>(output, p, st);
-#define M3_BYTES_CASE(IoT, NPV, PPV, V)                                                                 \
-    if (ts.np == NPV && ts.pp == PPV)                                                                   \
-        return output ? SegCfg<IoT, NPV, PPV, V>::OUTPUT_BYTES : SegCfg<IoT, NPV, PPV, V>::STATE_BYTES;
+    if (ts.np == NPV && ts.pp == PPV) return launch_seg_t<IoT, NPV, PPV, V>(output, ts, p, st);
+#define M3_BYTES_CASE(IoT, NPV, PPV, V) \
+    if (ts.np == NPV && ts.pp == PPV) return seg_bytes_t<IoT, NPV, PPV, V>(output, ts);
 
 }  // namespace m3

@@ -33,23 +33,23 @@ hipError_t launch_fill_state(const ScanParams &p, hipStream_t stream) {
 // ---------------------------------------------------------------- decode step
 // alpha, beta, gamma of the step's token: dt and lambda through the optional input
 // activations, A per head or (one token) per (batch, head).
-__device__ __forceinline__ void step_coeffs(const StepParams &p, int64_t bh, int h, float &alpha, float &beta,
+__device__ __forceinline__ void step_coeffs(const StepParams &p, int64_t b, int h, float &alpha, float &beta,
                                             float &gamma) {
-    float dt = p.dt[bh], lam = p.lam[bh];
+    float dt = p.dt[b * p.rsdt + h], lam = p.lam[b * p.rslam + h];
     if (p.flags & kFlagDtSoftplus) dt = softplus_f(dt + (p.dtbias ? p.dtbias[h] : 0.f));
     if (p.flags & kFlagLamSigmoid) lam = sigmoid_f(lam);
-    const float A = (p.flags & kFlagAPerToken) ? p.A[bh] : p.A[h];
+    const float A = (p.flags & kFlagAPerToken) ? p.A[b * p.rsa + h] : p.A[h];
     alpha = __expf(dt * A);
     beta = alpha * dt * (1.f - lam);
     gamma = lam * dt;
 }
 
-// y of one output element with the optional gate y * silu(z).
+// A value rounded to the io type (bf16 inputs formed in fp32, such as x expanded by mimo_x,
+// are rounded once, as the scan rounds them).
 template <class Io>
-__device__ __forceinline__ void store_y(const StepParams &p, int64_t off, float v) {
-    using ET = typename Io::T;
-    if (p.z) v *= silu_f(Io::ld((const ET *)p.z + off));
-    Io::st((ET *)p.y + off, v);
+__device__ __forceinline__ float round_io(float v) {
+    if constexpr (Io::bytes == 2) return bf2f(f2bf(v));
+    else return v;
 }
 // Load of base[off] when ok, else of base[0] (base must be a valid array): the value is
 // selected afterwards, so that a run of such loads is in flight before the first use.
@@ -114,22 +114,29 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     float *s_rs = s_sin + N2;      // [2][R] norm factors (B then C)
     float *s_red = s_rs + 2 * R;   // [NG][P][R] partial outputs
 
-    const ET *xg = (const ET *)p.x + bh * P * R;
-    const ET *bg = (const ET *)p.Bm + bh * N * R;
-    const ET *cg = (const ET *)p.Cm + bh * N * R;
+    // the token's rows (row b of each input; strided slices allowed), at head h
+    const ET *xg = (const ET *)p.x + b * p.rsx + (int64_t)h * P * (p.mx ? 1 : R);
+    const ET *bg = (const ET *)p.Bm + b * p.rsb + (int64_t)h * N * R;
+    const ET *cg = (const ET *)p.Cm + b * p.rsc + (int64_t)h * N * R;
     for (int e = tid; e < N * R; e += 256) {
         s_bt[e] = Io::ld(bg + e);
         s_ct[e] = Io::ld(cg + e);
         s_pb[e] = p.pB[bh * N * R + e];
     }
     for (int e = tid; e < P * R; e += 256) {
-        s_x[e] = Io::ld(xg + e);
+        if (p.mx) {  // rank-free x expanded by the learned vector of rank r
+            const int pc = e / R, r = e - pc * R;
+            s_x[e] = round_io<Io>(Io::ld(xg + pc) * p.mx[((int64_t)h * R + r) * P + pc]);
+        } else {
+            s_x[e] = Io::ld(xg + e);
+        }
         s_px[e] = p.px[bh * P * R + e];
     }
     for (int i = tid; i < N2; i += 256) {
         float sn = 0.f, cn = 1.f;  // pairs past nr do not rotate
         if (i < p.nr) {
-            const double th = wrap_2pi((double)p.ang[bh * p.nr + i] + (double)p.theta[bh * p.nr + i]);
+            const double th =
+                wrap_2pi((double)p.ang[bh * p.nr + i] + (double)p.theta[b * p.rsth + (int64_t)h * p.nr + i]);
             sincosf((float)th, &sn, &cn);
             p.ang[bh * p.nr + i] = (float)th;
         }
@@ -180,7 +187,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     for (int e = tid; e < P * R; e += 256) p.px[bh * P * R + e] = s_x[e];
 
     float alpha, beta, gamma;
-    step_coeffs(p, bh, h, alpha, beta, gamma);
+    step_coeffs(p, b, h, alpha, beta, gamma);
 
     float acc[VEC][RMAX];
 #pragma unroll
@@ -224,10 +231,28 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     }
     __syncthreads();
     const float Dh = p.D[h];
-    for (int e = tid; e < P * R; e += 256) {
+    const ET *zg = p.z ? (const ET *)p.z + b * p.rsz + (int64_t)h * P * (p.mz ? 1 : R) : nullptr;
+    ET *yg = (ET *)p.y + b * p.rsy + (int64_t)h * P * (p.mo ? 1 : R);
+    // output (pc, r) with the optional gate y * silu(z_r)
+    auto y_of = [&](int pc, int r) {
+        const int e = pc * R + r;
         float s = 0.f;
         for (int k = 0; k < NG; ++k) s += s_red[k * P * R + e];
-        store_y<Io>(p, bh * P * R + e, s + Dh * s_x[e]);
+        float v = s + Dh * s_x[e];
+        if (zg) {
+            const float zv = p.mz ? Io::ld(zg + pc) * p.mz[((int64_t)h * R + r) * P + pc] : Io::ld(zg + e);
+            v *= silu_f(zv);
+        }
+        return v;
+    };
+    if (p.mo) {  // rank contraction y[pc] = sum_r mimo_o[h, r, pc] y_r[pc]
+        for (int pc = tid; pc < P; pc += 256) {
+            float acc_o = 0.f;
+            for (int r = 0; r < R; ++r) acc_o += p.mo[((int64_t)h * R + r) * P + pc] * y_of(pc, r);
+            Io::st(yg + pc, acc_o);
+        }
+    } else {
+        for (int e = tid; e < P * R; e += 256) Io::st(yg + e, y_of(e / R, e % R));
     }
     (void)lane;
 }
@@ -277,12 +302,14 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
     // valid array and are replaced afterwards): wave 0 stages B~ (and swaps prev_B), wave 1
     // C~, wave 2 x (and swaps prev_x), wave 3 the step's coefficients.
     if (wave < 2) {
-        const ET *src = (const ET *)(wave == 0 ? p.Bm : p.Cm) + bh * N;
+        const ET *src = wave == 0 ? (const ET *)p.Bm + b * p.rsb + (int64_t)h * N : (const ET *)p.Cm + b * p.rsc + (int64_t)h * N;
         const float *gain = wave == 0 ? p.bnw : p.cnw;
         const float *bias = wave == 0 ? p.bbias : p.cbias;
         const bool hg = bcnorm && gain != nullptr, hb = bias != nullptr;
         const float *gp = hg ? gain : p.dt, *bp = hb ? bias + (int64_t)h * N : p.dt;
-        const float *ap = p.ang ? p.ang : p.dt, *tp = p.theta ? p.theta : p.dt;
+        // angle and increment of this (batch, head), rebased so that pair i is at offset i
+        const bool rot = p.nr > 0 && p.ang && p.theta;
+        const float *ap = rot ? p.ang + bh * p.nr : p.dt, *tp = rot ? p.theta + b * p.rsth + (int64_t)h * p.nr : p.dt;
         ET raw[2];
         float gv[2], bv[2], av[2], tv[2], pbv[2];
 #pragma unroll
@@ -292,8 +319,8 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
             raw[k] = ld_sel(src, n, in);
             gv[k] = ld_sel(gp, n, in && hg);
             bv[k] = ld_sel(bp, n, in && hb);
-            av[k] = ld_sel(ap, bh * p.nr + i, ir);
-            tv[k] = ld_sel(tp, bh * p.nr + i, ir);
+            av[k] = ld_sel(ap, i, ir);
+            tv[k] = ld_sel(tp, i, ir);
             pbv[k] = ld_sel(p.pB, bh * N + n, in && wave == 0);
         }
         float v[2], ss = 0.f;
@@ -329,7 +356,7 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
             }
         }
     } else if (wave == 2) {
-        const ET *xg = (const ET *)p.x + bh * P;
+        const ET *xg = (const ET *)p.x + b * p.rsx + (int64_t)h * P;
         for (int pc = lane; pc < P; pc += 64) {
             const float xv = Io::ld(xg + pc), pxv = p.px[bh * P + pc];
             s_x[pc] = xv;
@@ -338,14 +365,14 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
         }
     } else if (lane == 0) {
         float alpha, beta, gamma;
-        step_coeffs(p, bh, h, alpha, beta, gamma);
+        step_coeffs(p, b, h, alpha, beta, gamma);
         s_cf[0] = alpha;
         s_cf[1] = beta;
         s_cf[2] = gamma;
     }
     // the gate input of this thread's first output element
-    const ET *zb = (const ET *)(p.z ? p.z : p.x);
-    const ET zr = ld_sel(zb, bh * P + tid, p.z != nullptr && tid < P);
+    const ET *zb = p.z ? (const ET *)p.z + b * p.rsz + (int64_t)h * P : (const ET *)p.x;
+    const ET zr = ld_sel(zb, tid, p.z != nullptr && tid < P);
     __syncthreads();
     if (tid < p.nr) p.ang[bh * p.nr + tid] = s_ang[tid];
 
@@ -377,8 +404,8 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
         float sacc = 0.f;
         for (int k2 = 0; k2 < NG; ++k2) sacc += s_red[k2 * P + e];
         float v = sacc + Dh * s_x[e];
-        if (p.z) v *= silu_f(e == tid ? to_f<Io>(zr) : Io::ld(zb + bh * P + e));
-        Io::st((ET *)p.y + bh * P + e, v);
+        if (p.z) v *= silu_f(e == tid ? to_f<Io>(zr) : Io::ld(zb + e));
+        Io::st((ET *)p.y + b * p.rsy + (int64_t)h * P + e, v);
     }
 }
 
@@ -388,7 +415,8 @@ static size_t step_lds_bytes(const StepParams &p, int vec) {
 }
 
 hipError_t launch_step(bool bf16, const StepParams &p, hipStream_t stream) {
-    if (p.R == 1 && p.P % 4 == 0 && !(p.flags & kFlagHalfSplit)) {  // adjacent pairs across neighbouring lanes
+    // rank 1 with adjacent pairs (swapped between neighbouring lanes) and no MIMO projection
+    if (p.R == 1 && p.P % 4 == 0 && !(p.flags & kFlagHalfSplit) && !p.mx && !p.mz && !p.mo) {
         const int NG = 256 / (p.P / 4);
         const int NA = (p.N + 3) & ~3, PA = (p.P + 3) & ~3, N2A = (p.N / 2 + 3) & ~3;
         const size_t lds = sizeof(float) * (size_t)(3 * NA + 2 * PA + N2A + 4 + NG * p.P);

@@ -174,3 +174,27 @@ def make_block_inputs(w: Workload, *, rope_pairs: int | None = None, batch: int 
     if w.io == "bf16":
         z = bf16_round(z)
     return dict(dt_raw=dt_raw, dt_bias=dt_bias, lam_raw=lam_raw, A_tok=A_tok, z=z, theta_p=theta_p)
+
+
+def make_mimo_proj(w: Workload, *, batch: int | None = None, seqlen: int | None = None,
+                   seed: int | None = None) -> dict:
+    """Rank-free x and z and the MIMO projection vectors, drawn after ``make_inputs``' recipe.
+
+    One more ``default_rng(seed + 104729)`` stream, in this order:
+
+        x_free ~ N(0, 1)          [B, T, H, P]   (read as x_r = x_free * mimo_x[h, r])
+        z_free ~ N(0, 1)          [B, T, H, P]   (read as z_r = z_free * mimo_z[h, r])
+        mimo_x, mimo_z, mimo_o ~ U(-1.5, 1.5)   [H, R, P] each
+
+    x_free and z_free are bf16-rounded for bf16 workloads; the vectors stay float32.
+    """
+    Bsz = w.batch if batch is None else batch
+    T = w.seqlen if seqlen is None else seqlen
+    H, P, R = w.nheads, w.headdim, w.rank
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 104729)
+    x_free = rng.standard_normal((Bsz, T, H, P), dtype=np.float32)
+    z_free = rng.standard_normal((Bsz, T, H, P), dtype=np.float32)
+    vec = {k: rng.uniform(-1.5, 1.5, (H, R, P)).astype(np.float32) for k in ("mimo_x", "mimo_z", "mimo_o")}
+    if w.io == "bf16":
+        x_free, z_free = bf16_round(x_free), bf16_round(z_free)
+    return dict(x_free=x_free, z_free=z_free, **vec)

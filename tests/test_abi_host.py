@@ -237,3 +237,99 @@ def test_noalloc_rejects_shapes_beyond_static_scratch():
     assert lib.m3_scan_noalloc(ctypes.byref(_shape(m3)), ctypes.byref(inp), None, None, None, None) == 1
     text = open(HEADER).read()
     assert f"#define M3_STATIC_SCRATCH_BYTES (64u << 20)" in text and m3.M3_STATIC_SCRATCH_BYTES == 64 << 20
+
+
+def test_projection_and_stride_checks():
+    """MIMO projections and row strides are checked before any launch: a projection on the
+    SISO entry point, mimo_z without a gate input or a misaligned vector is M3_EINVAL; a row
+    stride shorter than its row M3_EINVAL, one of 2^24 or more M3_EUNSUPPORTED; strided B or C
+    with the half-split pairing, and strides or projections on the gradient call, are
+    M3_EUNSUPPORTED.  Valid strides pass every check (the call then stops at the short
+    workspace, M3_EWORKSPACE)."""
+    m3, lib = _lib()
+    _, ptrs = _fake_inputs(m3)
+    mis = ctypes.c_void_p(ptrs["x"].value + 4)
+    s1 = _shape(m3)
+    s4 = _shape(m3, rank=4, chunk=16)
+    assert _call_scan(m3, lib, s1, inp_over={"mimo_x": ptrs["x"]}) == 1
+    assert _call_scan(m3, lib, s4, inp_over={"mimo_z": ptrs["x"]}, mimo=True) == 1
+    assert _call_scan(m3, lib, s4, inp_over={"mimo_z": ptrs["x"], "z": ptrs["x"]}, mimo=True, ws_bytes=100) == 3
+    assert _call_scan(m3, lib, s4, inp_over={"mimo_o": mis}, mimo=True) == 1
+    assert _call_scan(m3, lib, s4, inp_over={"mimo_x": ptrs["x"], "mimo_o": ptrs["x"]}, mimo=True,
+                      ws_bytes=100) == 3
+    H, P, N = s1.nheads, s1.headdim, s1.dstate
+    assert _call_scan(m3, lib, s1, inp_over={"x_stride": H * P - 1}) == 1
+    assert _call_scan(m3, lib, s1, inp_over={"theta_stride": H * N // 2 - 4}) == 1
+    assert _call_scan(m3, lib, s1, inp_over={"dt_stride": 1 << 24}) == 2
+    assert _call_scan(m3, lib, s1, inp_over={"z_stride": -1}) == 1
+    ok = {"x_stride": 2 * H * P + 8, "B_stride": 2 * H * P + 8, "C_stride": 2 * H * P + 8, "dt_stride": H + 3,
+          "lam_stride": H + 3, "theta_stride": H * N // 2 + 1, "z_stride": 2 * H * P + 8}
+    assert _call_scan(m3, lib, s1, inp_over=ok, ws_bytes=100) == 3
+    # a MIMO call's rank-free x (mimo_x) has rows of H * P: a stride of H * P is valid there
+    assert _call_scan(m3, lib, s4, inp_over={"mimo_x": ptrs["x"], "x_stride": H * P}, mimo=True, ws_bytes=100) == 3
+    assert _call_scan(m3, lib, s4, inp_over={"x_stride": H * P}, mimo=True) == 1
+    sh = _shape(m3, flags=m3.M3_FLAG_BCNORM | m3.M3_FLAG_HALF_SPLIT)
+    assert _call_scan(m3, lib, sh, inp_over={"C_stride": H * N + 8}) == 2
+    assert _call_scan(m3, lib, sh, inp_over={"x_stride": H * P + 8}, ws_bytes=100) == 3
+    gr = m3._Grads(dx=ptrs["x"])
+    bws = lib.m3_scan_bwd_workspace_bytes(ctypes.byref(s1)) + 4096
+    for over in ({"x_stride": H * P + 8}, {"dt_stride": H + 1}):
+        inp = m3._Inputs(**dict(ptrs, **over))
+        rc = lib.m3_scan_bwd(ctypes.byref(s1), ctypes.byref(inp), ptrs["x"], None, None, ctypes.byref(gr), None,
+                             ptrs["x"], ctypes.c_size_t(bws), None)
+        assert rc == 2, over
+    inp = m3._Inputs(**dict(ptrs, mimo_x=ptrs["x"]))
+    rc = lib.m3_scan_bwd(ctypes.byref(s4), ctypes.byref(inp), ptrs["x"], None, None, ctypes.byref(gr), None,
+                         ptrs["x"], ctypes.c_size_t(lib.m3_scan_bwd_workspace_bytes(ctypes.byref(s4)) + 4096), None)
+    assert rc == 2
+    # the decode step: a short stride, and mimo_z without z
+    st = m3._State(h=ptrs["x"], prev_B=ptrs["x"], prev_x=ptrs["x"], angle=ptrs["x"])
+    s1t = _shape(m3, seqlen=1)
+    inp = m3._Inputs(**dict(ptrs, B_stride=N - 2))
+    assert lib.m3_step(ctypes.byref(s1t), ctypes.byref(inp), ptrs["x"], ctypes.byref(st), None) == 1
+    inp = m3._Inputs(**dict(ptrs, mimo_z=ptrs["x"]))
+    s4t = _shape(m3, seqlen=1, rank=4)
+    assert lib.m3_step(ctypes.byref(s4t), ctypes.byref(inp), ptrs["x"], ctypes.byref(st), None) == 1
+
+
+def test_binding_row_strides():
+    """The binding passes a slice of a wider buffer (contiguous token rows, evenly spaced) as
+    a pointer and a row stride, and refuses other non-contiguous layouts (host tensors only;
+    nothing is launched)."""
+    import torch
+    m3, _ = _lib()
+    Bsz, T, H, P = 2, 5, 3, 4
+    buf = torch.zeros(Bsz, T, 2 * H * P + 6)
+    x = buf[:, :, H * P:2 * H * P].unflatten(-1, (H, P))
+    assert m3._need(x, "x", torch.float32, x.device, (Bsz, T, H, P), rows=True) == 2 * H * P + 6
+    assert m3._need(x.contiguous(), "x", torch.float32, x.device, (Bsz, T, H, P), rows=True) == 0
+    one = buf[:, :1, :H * P].unflatten(-1, (H, P))  # one token: rows b are a batch stride apart
+    assert m3._need(one, "x", torch.float32, x.device, (Bsz, 1, H, P), rows=True) == T * (2 * H * P + 6)
+    with pytest.raises(ValueError):
+        m3._need(x.transpose(2, 3), "x", torch.float32, x.device, None, rows=True)   # rows not contiguous
+    with pytest.raises(ValueError):
+        m3._need(buf[:, ::2, :H * P].unflatten(-1, (H, P))[:, :, :, :2], "x", torch.float32, x.device, None,
+                 rows=True)
+    with pytest.raises(ValueError):
+        m3._need(x, "x", torch.float32, x.device, (Bsz, T, H, P))   # rows=False: contiguous only
+    # batch rows not T row strides apart
+    wide = torch.zeros(Bsz, T + 1, H * P)[:, :T].unflatten(-1, (H, P))
+    assert m3._row_stride(wide) is None
+
+
+def test_binding_gradient_call_takes_contiguous_inputs():
+    """The gradient call's input block refuses row-strided slices (host tensors; nothing runs)."""
+    import torch
+    m3, _ = _lib()
+    Bsz, T, H, P, N = 1, 4, 2, 8, 8
+    s = m3.Shape(Bsz, T, H, P, N, 1, 16, m3.M3_F32, m3.M3_FLAG_BCNORM, 1e-5)
+    f = lambda *sh: torch.zeros(sh)
+    args = dict(x=f(Bsz, T, H, P), B=f(Bsz, T, H, N), C=f(Bsz, T, H, N), dt=f(Bsz, T, H), lam=f(Bsz, T, H),
+                theta=f(Bsz, T, H, N // 2), A=f(H), D=f(H))
+    pos = lambda a: [a[k] for k in ("x", "B", "C", "dt", "lam", "theta", "A", "D")]
+    inp = m3._inputs(s, *pos(args), None, None, None, None, False, strided=False)
+    assert inp.x_stride == 0 and inp.dt_stride == 0
+    args["dt"] = f(Bsz, T, H + 2)[:, :, :H]
+    assert m3._inputs(s, *pos(args), None, None, None, None, False).dt_stride == H + 2
+    with pytest.raises(ValueError):
+        m3._inputs(s, *pos(args), None, None, None, None, False, strided=False)
