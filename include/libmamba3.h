@@ -271,6 +271,18 @@ m3_status m3_scan_bwd(const m3_shape *shape, const m3_inputs *in, const void *dy
 m3_status m3_scan_noalloc(const m3_shape *shape, const m3_inputs *in, void *y, const m3_state *init,
                           m3_state *final, void *stream);
 
+/*
+ * Device-side checks of a debug build (the library compiled with -DM3_DEBUG:
+ * libmamba3_debug.so; for developers of the kernels, not for normal use).  In such a build
+ * every kernel checks its block, segment and output indices against the call's sizes; a
+ * failed check does not fault the device but counts itself and records its source line.
+ * This call synchronises the current device, returns the number of failed checks since the
+ * last call in *failed and the largest failing source line in *line (either may be NULL),
+ * and clears both.  M3_EUNSUPPORTED in a release build (nothing is checked there);
+ * M3_EHIP when the device cannot be read.
+ */
+m3_status m3_debug_checks(uint32_t *failed, uint32_t *line);
+
 /* Static description of a status code. */
 const char *m3_status_str(m3_status status);
 

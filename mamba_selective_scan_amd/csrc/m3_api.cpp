@@ -21,6 +21,28 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ---------------------------------------------------------------- debug builds
+// With -DM3_DEBUG every kernel gets the device address of two words per GPU that its failed
+// checks update (count, largest failing source line); m3_debug_checks reads and clears them.
+#ifdef M3_DEBUG
+static __device__ unsigned int dbg_words[2];
+std::mutex g_dbg_mu;
+unsigned int *g_dbg_ptr[64];
+unsigned int *debug_words() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(g_dbg_mu);
+    if (!g_dbg_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(dbg_words)) != hipSuccess) return nullptr;
+        g_dbg_ptr[dev] = static_cast<unsigned int *>(p);
+    }
+    return g_dbg_ptr[dev];
+}
+#else
+unsigned int *debug_words() { return nullptr; }
+#endif
+
 static_assert(M3_FLAG_BCNORM == m3::kFlagNorm && M3_FLAG_PARTIAL_ROPE == m3::kFlagPartialRope &&
                   M3_FLAG_A_PER_TOKEN == m3::kFlagAPerToken && M3_FLAG_DT_SOFTPLUS == m3::kFlagDtSoftplus &&
                   M3_FLAG_LAM_SIGMOID == m3::kFlagLamSigmoid && M3_FLAG_HALF_SPLIT == m3::kFlagHalfSplit,
@@ -244,6 +266,7 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
 
     ScanParams p;
     std::memset(&p, 0, sizeof p);
+    p.dbg = debug_words();
     p.B = s->batch;
     p.T = s->seqlen;
     p.H = s->nheads;
@@ -389,6 +412,7 @@ m3_status bwd_impl(const m3_shape *s, const m3_inputs *in, const void *dy, const
     if (s->batch == 0) return M3_OK;
     m3::BwdParams p;
     std::memset(&p, 0, sizeof p);
+    p.dbg = debug_words();
     p.B = s->batch;
     p.T = s->seqlen;
     p.H = s->nheads;
@@ -757,6 +781,7 @@ m3_status m3_step(const m3_shape *s, const m3_inputs *in, void *y, m3_state *sta
     if (s->batch == 0) return M3_OK;
     StepParams p;
     std::memset(&p, 0, sizeof p);
+    p.dbg = debug_words();
     p.B = s->batch;
     p.H = s->nheads;
     p.P = s->headdim;
@@ -801,8 +826,30 @@ m3_status m3_step(const m3_shape *s, const m3_inputs *in, void *y, m3_state *sta
                : M3_EHIP;
 }
 
+m3_status m3_debug_checks(uint32_t *failed, uint32_t *line) {
+#ifdef M3_DEBUG
+    unsigned int *d = debug_words();
+    if (!d) return M3_EHIP;
+    unsigned int h[2] = {0u, 0u};
+    const unsigned int zero[2] = {0u, 0u};
+    if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(h, d, sizeof h, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(d, zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
+        return M3_EHIP;
+    if (failed) *failed = h[0];
+    if (line) *line = h[1];
+    return M3_OK;
+#else
+    (void)failed;
+    (void)line;
+    return M3_EUNSUPPORTED;
+#endif
+}
+
 const char *m3_status_str(m3_status status) {
-    switch (status) {
+    // a C caller may pass any int; read it as one (an out-of-range enum value is undefined in C++)
+    int code;
+    std::memcpy(&code, &status, sizeof code);
+    switch (code) {
         case M3_OK: return "M3_OK: success";
         case M3_EINVAL: return "M3_EINVAL: invalid argument (NULL pointer, bad size, odd N, rank < 1, unknown flag, rope_pairs outside 0..N/2 or misaligned pointer)";
         case M3_EUNSUPPORTED: return "M3_EUNSUPPORTED: size or option outside the supported range (N, P <= 128, R <= 8, chunk in {16,32,64,128}, chunk*R <= 128, row strides below 2^24; the gradient call needs contiguous inputs without MIMO projections)";

@@ -722,6 +722,7 @@ __global__ __launch_bounds__(kThreads, (state_min_waves_per_simd<NPAD, PPAD, VEC
     const int nck = p.nck, N = p.N, P = p.P, N2 = N / 2;
     const int64_t bh = blockIdx.x / nck;
     const int c = (int)(blockIdx.x - bh * nck);
+    M3_DCHECK(p, bh < p.B * p.H && c < nck && (int64_t)c * (kRows / p.R) < p.T);
     const int64_t b = bh / p.H;
     const int h = (int)(bh - b * p.H);
     const int Qt = kRows / p.R;
@@ -920,6 +921,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     const int64_t t0 = (int64_t)c * Qt;
     const int Tv = (int)min((int64_t)Qt, T - t0);
     const int64_t cidx = bh * nck + c;
+    M3_DCHECK(p, bh < p.B * p.H && c < nck && Tv >= 1 && Tv <= Qt && t0 + Tv <= T);
     const bool last = c == nck - 1;
     const float *Gend = p.Ust + cidx * N * (int64_t)P, *Hst = p.Sst + cidx * N * (int64_t)P;
     // State slabs (32 state rows of the adjoint after the chunk and of the state before it) go
@@ -1650,6 +1652,7 @@ __global__ __launch_bounds__(256) void bwd_init_kernel(BwdParams p) {
     const int64_t b = bh / p.H;
     const int h = (int)(bh - b * p.H);
     const int N = p.N, P = p.P, R = p.R, N2 = N / 2, NR = p.nr, nck = p.nck;
+    M3_DCHECK(p, bh < p.B * p.H);
     const int64_t T = p.T;
     const float *G0 = p.G0w + bh * N * (int64_t)P;
     if (p.dh0)
@@ -1749,6 +1752,7 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(BwdParams p) {
     const int64_t b = bh / p.H;
     const int h = (int)(bh - b * p.H);
     const int Qt = kRows / p.R;
+    M3_DCHECK(p, bh < p.B * p.H && c < nck && (int64_t)c * Qt < p.T);
     const int64_t T = p.T, H = p.H, t0 = (int64_t)c * Qt;
     const int Tv = (int)min((int64_t)Qt, T - t0);
     const int64_t cidx = bh * nck + c;

@@ -13,6 +13,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Debug builds (-DM3_DEBUG): device-side bounds and plan checks.  A failed check does not
+// trap: it counts itself and records its source line in two words that the host reads back
+// (m3_debug_checks), so a bad index is reported without faulting the device.  Release builds
+// compile the checks out.
+#ifdef M3_DEBUG
+#define M3_DCHECK(p, cond)                                   \
+    do {                                                     \
+        if (!(cond) && (p).dbg) {                            \
+            atomicAdd((p).dbg, 1u);                          \
+            atomicMax((p).dbg + 1, (unsigned int)__LINE__);  \
+        }                                                    \
+    } while (0)
+#else
+#define M3_DCHECK(p, cond) \
+    do {                   \
+    } while (0)
+#endif
+
 namespace m3 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

@@ -54,6 +54,7 @@ struct ScanParams {
     // per output segment, written by the prefix kernel (NULL when it does not run):
     float *Hin;   // [B*H*ncg][nseg][NP*PP] incoming state in the frame of the segment's first
                   //   block, fragment order
+    unsigned int *dbg;  // debug builds: [count of failed device checks, largest failing line]
 };
 
 struct StepParams {
@@ -71,6 +72,7 @@ struct StepParams {
     int64_t rsx, rsb, rsc, rsdt, rslam, rsth, rsa, rsz, rsy;  // row strides (one token: row = b)
     void *y;
     float *h, *pB, *px, *ang;
+    unsigned int *dbg;  // debug builds: failed device checks (as ScanParams::dbg)
 };
 
 // Gradients of a scan (reverse-mode), chunk by chunk: 64 (token, rank) rows per chunk,
@@ -112,6 +114,7 @@ struct BwdParams {
     float *dsc;    // [BH][T][3]      d log alpha, d gamma, d eta per token
     float *deta0;  // [BH]            d eta of the initial state
     float *part;   // [BH][nck][pw]   parameter partial sums
+    unsigned int *dbg;  // debug builds: failed device checks (as ScanParams::dbg)
 };
 hipError_t launch_bwd(bool bf16, const BwdParams &p, hipStream_t stream);
 

@@ -1237,6 +1237,8 @@ __device__ __forceinline__ WgCtx make_ctx(const ScanParams &p, int nsegk, int bp
     c.affine = (c.bcnorm && (p.bnw || p.cnw)) || p.bbias || p.cbias;
     // normalised rows without gains or biases have |components| <= sqrt(N) <= 11.4: fp16 as is
     c.rowscale = Cfg::F16 && !(c.bcnorm && !c.affine);
+    M3_DCHECK(p, c.b < p.B && c.h < p.H && c.cg < p.ncg && c.seg < nsegk && c.blk0 < c.blk1 &&
+                     c.blk1 <= p.nblk && c.Pw >= 1 && c.p0 + c.Pw <= p.P);
     return c;
 }
 
@@ -1285,6 +1287,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
     load_block<Io>(rb, p, c, g);
     if constexpr (Cfg::MV) stage_raw_bc<Cfg>(rb, (uint16_t *)sm.raw, nullptr, c);
     for (int blk = c.blk0; blk < c.blk1; ++blk) {
+        M3_DCHECK(p, g.t0 == (int64_t)blk * p.TB && g.Tv >= 1 && g.Tv <= p.TB && g.t0 + g.Tv <= p.T);
         lds_barrier();  // previous block's readers of the LDS planes are done
         stage_scalars_x<Io>(rb, sm, p, c, g);
         const BlockGeo gn = block_geo(p, blk + 1);
@@ -1308,6 +1311,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
     // segment aggregate -> workspace, in fragment order (one 16-byte store per tile and lane)
     const int wave = tid >> 6;
     const int64_t bs = c.bh * p.nsub + c.seg;
+    M3_DCHECK(p, c.seg < p.nsub && p.Sagg && p.lseg && p.pseg && p.cseg);
     float *Sg = p.Sagg + ((c.bh * p.ncg + c.cg) * p.nsub + c.seg) * (int64_t)(NP * PP);
 #pragma unroll
     for (int m = 0; m < Cfg::TPW; ++m) {
@@ -1501,6 +1505,7 @@ __device__ __forceinline__ void col_outputs(const Sm &sm, const ScanParams &p, c
 #pragma unroll
                 for (int i = 0; i < 4; ++i) yv[i] *= silu_f(zv[i]);
             }
+            M3_DCHECK(p, !(t < g.Tv && pc < c.Pw) || (g.t0 + t < p.T && c.p0 + pc + 4 <= p.P));
             if (t < g.Tv && pc < c.Pw)
                 *(u32x2_t *)((ET *)c.yb + (g.t0 + t) * c.sy + pc) = u32x2_t{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])};
         }
@@ -1552,6 +1557,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     // state sub-segment per output segment)
     f32x4_t hs[TPW];
     if (p.Hin) {
+        M3_DCHECK(p, c.seg < p.nseg);
         const float *Hg = p.Hin + ((bh * p.ncg + c.cg) * p.nseg + c.seg) * (int64_t)(NP * PP);
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
@@ -1662,6 +1668,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
     if constexpr (!Cfg::COL) publish_hmax<Cfg>(sm, hs);  // the incoming state's magnitude, for its fp16 scale
     Frag ct[KS];
     for (int blk = c.blk0; blk < c.blk1; ++blk) {
+        M3_DCHECK(p, g.t0 == (int64_t)blk * p.TB && g.Tv >= 1 && g.Tv <= p.TB && g.t0 + g.Tv <= p.T);
         lds_barrier();  // every wave is done with the previous block's LDS planes
         float inv_hs = 1.f;
         if constexpr (!Cfg::COL) {
@@ -1940,6 +1947,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 if (q >= c.Pw) continue;
                 float acc = 0.f;
                 for (int r = 0; r < R; ++r) acc += moh[(int64_t)r * p.P + q] * ysf[(tk * R + r) * PP + q];
+                M3_DCHECK(p, g.t0 + tk < p.T && c.p0 + q < p.P);
                 Io::st((ET *)c.yb + (g.t0 + tk) * c.sy + q, acc);
             }
         } else {
@@ -1956,6 +1964,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 for (int m = 0; m < 16 * PP / 8 / 64; ++m) {
                     const int e = lane + 64 * m;
                     const int tk = tk0 + (int)(((float)e + 0.5f) * iy), o = e - (tk - tk0) * yvpt;
+                    M3_DCHECK(p, !(tk < g.Tv && o * 8 < c.Pw * R) || (g.t0 + tk < p.T && c.p0 * R + o * 8 + 8 <= p.P * R));
                     if (tk < g.Tv && o * 8 < c.Pw * R)
                         *(u32x4_t *)((ET *)c.yb + (g.t0 + tk) * c.sy + o * 8) = *(const u32x4_t *)(ys + tk * PP * R + o * 8);
                 }
@@ -1964,6 +1973,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 for (int m = 0; m < 16 * PP / Cfg::XW / 64; ++m) {
                     const int e = lane + 64 * m;
                     const int yr = tt * 16 + e / (PP / Cfg::XW), pc = (e % (PP / Cfg::XW)) * Cfg::XW;
+                    M3_DCHECK(p, !(yr < Rv && pc < c.Pw) || (g.t0 + yr < p.T && c.p0 + pc + Cfg::XW <= p.P));
                     if (yr < Rv && pc < c.Pw)
                         *(u32x4_t *)((ET *)c.yb + (g.t0 + yr) * c.sy + pc) = *(const u32x4_t *)(ys + ys_off<Cfg>(yr, pc));
                 }
@@ -1972,6 +1982,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                     const int yr = tt * 16 + e / PP, pc = e - (e / PP) * PP;
                     if (yr >= Rv || pc >= c.Pw) continue;
                     const int tok = tok_of(yr, c), r = yr - tok * R;
+                    M3_DCHECK(p, g.t0 + tok < p.T && r >= 0 && r < R && c.p0 + pc < p.P);
                     ((ET *)c.yb)[(g.t0 + tok) * c.sy + (int64_t)pc * R + r] = ys[ys_off<Cfg>(yr, pc)];
                 }
             }
@@ -1999,6 +2010,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 float xv;
                 if constexpr (Cfg::BF) xv = bf2f(((const uint16_t *)sm.xt)[xt_off<Cfg>(pc, lrow0 + r)]);
                 else xv = ((const float *)sm.xt)[xt_off<Cfg>(pc, lrow0 + r)];
+                M3_DCHECK(p, c.p0 + pc < P && lrow0 + r < Cfg::ROWS);
                 p.px1[(bh * P + c.p0 + pc) * R + r] = xv;
             }
         }
@@ -2047,6 +2059,7 @@ __global__ __launch_bounds__(256) void seg_prefix_kernel(ScanParams p) {
     const int N = p.N, P = p.P, N2 = N / 2, R = p.R;
     const int p0 = cg * PP, Pw = min(PP, P - p0);
     const int kps = p.bps / p.sbps;  // state sub-segments per output segment
+    M3_DCHECK(p, bh < p.B * p.H && cg < p.ncg && Pw >= 1 && p.Hin && kps * p.sbps == p.bps);
     if (idx < per_q) {
         const int e = idx >> 6, lane = idx & 63;
         const int nt = e / PT, pt = e - nt * PT, gq = lane >> 4, l16 = lane & 15;

@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     const int N = p.N, P = p.P, R = RMAX == 1 ? 1 : p.R, N2 = N / 2;
     const int64_t bh = b * p.H + h;  // == (b, t=0, h) since T = 1
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    M3_DCHECK(p, b < p.B && h < p.H && R <= RMAX && P % VEC == 0 && 256 / (P / VEC) >= 1);
 
     // state update mapping: thread = (group of VEC columns, n group)
     const int PG = P / VEC;
@@ -273,6 +274,7 @@ __global__ __launch_bounds__(256) void step_kernel_r1(StepParams p) {
     const int N = p.N, P = p.P, N2 = N / 2;
     const int64_t bh = b * p.H + h;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    M3_DCHECK(p, b < p.B && h < p.H && p.R == 1 && P % 4 == 0 && N <= 128);
     const int PG = P / 4, NG = 256 / PG;
     const int pg = tid % PG, ng = tid / PG;
     const bool upd = ng < NG;

@@ -71,7 +71,9 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        _lib = ctypes.CDLL(build())
+        # M3_ORACLE_LIB: an alternative build of the same sources (the sanitizer build of the
+        # tests); the default is the in-tree -O2 build
+        _lib = ctypes.CDLL(os.environ.get("M3_ORACLE_LIB") or build())
         _lib.m3o_scan.argtypes = [ctypes.POINTER(_Args)]
         _lib.m3o_scan.restype = ctypes.c_int
         _lib.m3o_scan_bwd.argtypes = [ctypes.POINTER(_BwdArgs)]

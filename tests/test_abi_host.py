@@ -333,3 +333,11 @@ def test_binding_gradient_call_takes_contiguous_inputs():
     assert m3._inputs(s, *pos(args), None, None, None, None, False).dt_stride == H + 2
     with pytest.raises(ValueError):
         m3._inputs(s, *pos(args), None, None, None, None, False, strided=False)
+
+
+def test_debug_checks_unsupported_in_release_build():
+    """m3_debug_checks reads the device-side check counters of a -DM3_DEBUG build; the release
+    library checks nothing and says so (M3_EUNSUPPORTED) without touching a device."""
+    m3, lib = _lib()
+    lib.m3_debug_checks.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.m3_debug_checks(None, None) == 2
