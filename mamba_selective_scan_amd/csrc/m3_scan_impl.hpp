@@ -782,10 +782,10 @@ __device__ __forceinline__ void stage_angles_table(const Sm &sm, const ScanParam
 // Block angle totals per pair (and their cos/sin) for the carry.  Reads the
 // angle data of stage 1/2; the results are consumed after a later barrier.
 template <class Cfg, class Sm>
-__device__ __forceinline__ void block_angle_totals(const Sm &sm, const ScanParams &p, const BlockGeo &g) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void block_angle_totals(const Sm &sm, const ScanParams &p, const BlockGeo &g, int wave0 = 0) {
+    const int tid = threadIdx.x - 64 * wave0;  // pairs on the lanes of wave `wave0`
     const int N2 = p.N / 2;
-    if (tid < N2) {
+    if (tid >= 0 && tid < N2) {
         float a;
         if constexpr (Cfg::VEC) {
             const float *tt = (const float *)sm.phi;
@@ -1432,6 +1432,9 @@ __device__ __forceinline__ void col_outputs(const Sm &sm, const ScanParams &p, c
         *(u32x2_t *)(glh + off) = u32x2_t{h0, h1};
         *(u32x2_t *)(gll + off) = u32x2_t{l0, l1};
     }
+    // the block's angle totals and their (cos, sin) for the carry, on the wave with three
+    // strictly causal tiles (no per-element decays): it has slack before this barrier
+    if (w == 2) block_angle_totals<Cfg>(sm, p, g, 2);
     lds_barrier();
     // ---- H^T of this wave's columns as fp16 A operands: k step mm covers state tiles 2mm, 2mm+1
     // (slot j < 4: n = 32mm + 4g + j; j >= 4: n = 32mm + 16 + 4g + j - 4)
@@ -1683,7 +1686,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
             if (blk + 1 < c.blk1) load_block<Io, kLoadXs>(rb, p, c, gn);
         }
         if constexpr (!VEC) stage_angles_table<Cfg>(sm, p, g);
-        block_angle_totals<Cfg>(sm, p, g);
+        // (column-owned outputs: on wave 2, which has slack before col_outputs' barrier)
+        if constexpr (!Cfg::COL) block_angle_totals<Cfg>(sm, p, g);
         stage_prologue<Io>(rb, sm, p, c, g, ct, want_final && c.cg == 0 && blk == c.blk1 - 1);
         if constexpr (VEC) {
             // and its B, C, theta once the prologue has consumed this block's
