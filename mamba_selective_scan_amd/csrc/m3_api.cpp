@@ -175,6 +175,8 @@ TileShape kernel_tile(const m3_shape *s, const m3_inputs *in, const RowStrides &
     if (ts.mode == m3::kTileVec && (proj || !rows16 || rs.v[kRsTh] % 4 != 0)) ts.mode = m3::kTileGen;
     if (ts.mode == m3::kTileMimo && !rows16) ts.mode = m3::kTileGen;
     ts.pj = proj;
+    // reached with the flag only through the native half-split path (native_half_split)
+    ts.hs = (s->flags & M3_FLAG_HALF_SPLIT) != 0 && ts.mode == m3::kTileVec;
     return ts;
 }
 
@@ -338,6 +340,7 @@ m3_status scan_impl(const m3_shape *s, const m3_inputs *in, void *y, const m3_st
     // incoming states per segment from the prefix kernel when the state is split finer than
     // the segments; otherwise the output kernel assembles them itself
     const bool prefix = p.sbps < p.bps;
+    if (ts.hs && prefix) return M3_EINVAL;  // (native_half_split excludes it)
     p.Hin = prefix ? reinterpret_cast<float *>(base + pl.Hin) : nullptr;
     if (p.nsub > 0 && m3::launch_seg_state(bf, ts, p, st) != hipSuccess) return M3_EHIP;
     if (prefix && m3::launch_seg_prefix(ts, p, st) != hipSuccess) return M3_EHIP;
@@ -567,6 +570,20 @@ struct HsPerm {
     }
 };
 
+// The rank-1 16-byte kernels pair (i, i + N/2) themselves when N fills their tile (64 or 128)
+// and no prefix pass runs (the prefix kernel's fold keeps adjacent pairs); every other call
+// with the half-split pairing runs on N-permuted copies.
+bool native_half_split(const m3_shape *s, const m3_inputs *in) {
+    const TileShape t = tile_of(s);
+    if (t.mode != m3::kTileVec || s->dstate != t.np || t.np < 64) return false;
+    const Plan pl = plan_of(s);
+    if (pl.sbps < pl.bps) return false;
+    RowStrides rs;
+    if (row_strides(s, in, rs) != M3_OK) return false;
+    const TileShape k = kernel_tile(s, in, rs);
+    return k.mode == m3::kTileVec && !k.pj;
+}
+
 m3_status scan_half_split(const m3_shape *s, const m3_inputs *in, void *y, const m3_state *init, m3_state *fin,
                           void *ws, size_t ws_bytes, void *stream, bool mimo) {
     m3_status rc = validate_scan(s, in, y, init, fin, ws, mimo);
@@ -577,6 +594,10 @@ m3_status scan_half_split(const m3_shape *s, const m3_inputs *in, void *y, const
         s1.flags &= ~M3_FLAG_HALF_SPLIT;
         return scan_impl(&s1, in, y, init, fin, ws, ws_bytes, stream, mimo);
     }
+    // (the workspace is always the size m3_scan_workspace_bytes reports for the shape, which
+    // holds the permuted copies whichever path runs)
+    if (!ws || ws_bytes < scan_ws_bytes(s)) return M3_EWORKSPACE;
+    if (native_half_split(s, in)) return scan_impl(s, in, y, init, fin, ws, ws_bytes, stream, mimo);
     m3_shape s2 = *s;
     s2.flags &= ~M3_FLAG_HALF_SPLIT;
     const size_t base = align_up(plan_of(&s2).total);

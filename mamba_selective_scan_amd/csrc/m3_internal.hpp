@@ -133,6 +133,7 @@ struct TileShape {
                // kTileMimo: bf16, rank 2, 4 or 8, N % 8 == 0, P % 8 == 0 (16-byte accesses);
                // kTileGen: anything else (element accesses)
     bool pj = false;  // the call has MIMO projections: the kernels that read them (not kTileVec)
+    bool hs = false;  // half-split pairing in the kernels (kTileVec with N = np >= 64, no prefix pass)
 };
 
 hipError_t launch_seg_state(bool bf16, const TileShape &ts, const ScanParams &p, hipStream_t stream);

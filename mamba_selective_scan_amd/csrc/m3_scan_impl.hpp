@@ -91,7 +91,10 @@ constexpr int kModeGen = 0, kModeVec = 1, kModeMimo = 2;
 // SWZ_: XOR-swizzled X^T plane on the rank-1 16-byte path (see xt_off).
 // PJ_: the variant that reads the MIMO projections (mimo_x, mimo_z, mimo_o) when given; the
 // kernels without it never test for them (element and interleaved-rank paths only).
-template <class Io, int NP_, int PP_, int MODE_, bool SWZ_ = true, bool PJ_ = false>
+// HS_: the half-split rotation pairing (pair i = components (i, i + N/2)) natively, on the rank-1
+// 16-byte path with N = NP (64 or 128): component kk*32 + 8g + j of a lane pairs with the same
+// slot of step kk + KS/2 in the same lane, and state tile m (rows below N/2) with tile m + HSM.
+template <class Io, int NP_, int PP_, int MODE_, bool SWZ_ = true, bool PJ_ = false, bool HS_ = false>
 struct SegCfg {
     using ET = typename Io::T;
     static constexpr bool BF = std::is_same<Io, IoBF16>::value;
@@ -99,6 +102,8 @@ struct SegCfg {
     static constexpr bool MV = MODE_ == kModeMimo;
     static constexpr bool PJ = PJ_;
     static_assert(!PJ || !VEC, "the rank-1 16-byte path takes no projections");
+    static constexpr bool HS = HS_;
+    static_assert(!HS || (VEC && NP_ >= 64), "native half-split pairing: rank-1 16-byte path, N >= 64");
     static constexpr bool XSWZ = SWZ_ && VEC;
     static_assert(!MV || BF, "the interleaved-rank load path is bf16 only");
     static constexpr bool PACKED = (VEC || MV) && BF;  // raw B/C held as packed bf16 words
@@ -108,6 +113,7 @@ struct SegCfg {
     static constexpr int PT = PP / 16;  // p tiles
     static constexpr int NT = NP / 16;  // n tiles
     static constexpr int TPW = (PT * NT + 3) / 4;  // state tiles per wave
+    static constexpr int HSM = (NT / 2) * PT / 4;  // half-split: partner of state tile m < HSM
     static constexpr int ES = BF ? 2 : 4;          // bytes per operand element per plane
     static constexpr int NPL = BF ? 2 : 1;         // planes: (hi, lo) or (fp32)
     // bf16 I/O: B~, C~ and H are single fp16 operands (power-of-two scaled); (w B~)^T, G o L
@@ -211,6 +217,15 @@ __device__ __forceinline__ int xt_off(int col, int row) {
 template <class Cfg>
 __device__ __forceinline__ int ys_off(int row, int col) {
     return row * Cfg::PP + (col ^ (((row >> 2) & (Cfg::PP / 16 - 1)) << 4));
+}
+
+// First of the four rotation pairs of angle group q (0 .. KS-1) of lane group g: the pairs of the
+// components kk*32 + 8g .. + 7 of k step kk = q (adjacent pairing), or, half-split, the
+// components of k step q / 2 (which pair with step q / 2 + KS / 2), half q % 2 of them.
+template <class Cfg>
+__device__ __forceinline__ int pair_off(int q, int g) {
+    if constexpr (Cfg::HS) return (q >> 1) * 32 + 8 * g + 4 * (q & 1);
+    else return q * 16 + 4 * g;
 }
 
 struct BlockGeo {
@@ -320,7 +335,7 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
         const char *cbase = (const char *)c.Cb + (int64_t)g.t0 * c.sb * (int64_t)sizeof(ET);
         const char *tbase = (const char *)c.thb + (int64_t)g.t0 * c.sth * 4;
         const uint32_t boff = (uint32_t)row * (uint32_t)(c.sb * sizeof(ET)) + (uint32_t)(8 * gq * sizeof(ET));
-        const uint32_t toff = (uint32_t)row * (uint32_t)(c.sth * 4) + (uint32_t)(16 * gq);
+        const uint32_t toff = (uint32_t)row * (uint32_t)(c.sth * 4);
 #pragma unroll
         for (int kk = 0; kk < Cfg::KS; ++kk) {
             const bool ok = rv && kk * 32 + 8 * gq < N;
@@ -340,7 +355,8 @@ __device__ __forceinline__ void load_block(RawBlock<Cfg, WANT_C> &rb, const Scan
             }
             // angles of this lane's pairs: kk*16 + 4g + 0..3 (all four rotate or none: nr % 4 == 0)
             f32x4_t tv = {0.f, 0.f, 0.f, 0.f};
-            if (ok && kk * 16 + 4 * gq < p.nr) tv = *(const f32x4_t *)(tbase + toff + kk * 64);
+            const int po = pair_off<Cfg>(kk, gq);
+            if (ok && po < p.nr) tv = *(const f32x4_t *)(tbase + toff + (uint32_t)(po * 4));
 #pragma unroll
             for (int k = 0; k < 4; ++k) rb.th[kk * 4 + k] = tv[k];
         }
@@ -656,7 +672,7 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
             const int gq = lane >> 4;
 #pragma unroll
             for (int kk = 0; kk < Cfg::KS; ++kk)
-                *(f32x4_t *)(tt + row_tile() * (Cfg::NP / 2) + kk * 16 + 4 * gq) =
+                *(f32x4_t *)(tt + row_tile() * (Cfg::NP / 2) + pair_off<Cfg>(kk, gq)) =
                     f32x4_t{rb.th[kk * 4], rb.th[kk * 4 + 1], rb.th[kk * 4 + 2], rb.th[kk * 4 + 3]};
         }
     } else {
@@ -894,7 +910,7 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
         for (int kk = 0; kk < KS; ++kk) phoff[kk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int w2 = 0; w2 < rtile; ++w2)
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) phoff[kk] += *(const f32x4_t *)(tt + w2 * (Cfg::NP / 2) + kk * 16 + 4 * gq);
+            for (int kk = 0; kk < KS; ++kk) phoff[kk] += *(const f32x4_t *)(tt + w2 * (Cfg::NP / 2) + pair_off<Cfg>(kk, gq));
     }
     // normalised values with gains and biases of one k step (8 components of the row)
     auto prep = [&](int kk, float (&vb)[8], float (&vc)[8]) {
@@ -975,43 +991,9 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
         }
     }
     const bool last_tok = final_row && rv && tok == g.Tv - 1;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        float vb[8], vc[8];
-        prep(kk, vb, vc);
-        float ob[8], oc[8];
-#pragma unroll
-        for (int jp = 0; jp < 4; ++jp) {
-            const int n = kk * 32 + 8 * gq + 2 * jp;
-            float ang;
-            if constexpr (Cfg::VEC) ang = rb.th[kk * 4 + jp] + phoff[kk][jp];
-            else ang = (rv && n < N) ? ((const float *)sm.phi)[tok * Cfg::PHP + n / 2] : 0.f;
-            float sn, cn;
-            fast_sincos(ang, sn, cn);
-            const float u = vb[2 * jp], v = vb[2 * jp + 1];
-            ob[2 * jp] = u * cn - v * sn;
-            ob[2 * jp + 1] = u * sn + v * cn;
-            if constexpr (WANT_C) {
-                const float uc = vc[2 * jp], vcc = vc[2 * jp + 1];
-                oc[2 * jp] = uc * cn - vcc * sn;
-                oc[2 * jp + 1] = uc * sn + vcc * cn;
-            }
-        }
-        if (last_tok) {
-            // the carried B~ of the call's last token: from the block frame to the global frame
-            // (the running angle at this block's start)
-#pragma unroll
-            for (int jp = 0; jp < 4; ++jp) {
-                const int n = kk * 32 + 8 * gq + 2 * jp;
-                if (n < N) {
-                    float sn, cn;
-                    fast_sincos((float)wrap_2pi(sm.base[n / 2]), sn, cn);
-                    const float u = ob[2 * jp], v = ob[2 * jp + 1];
-                    p.pB1[(c.bh * N + n) * R + r] = u * cn - v * sn;
-                    p.pB1[(c.bh * N + n + 1) * R + r] = u * sn + v * cn;
-                }
-            }
-        }
+    // the rotated B~ (ob) and C~ (oc) components kk*32 + 8g .. + 7 of this row -> the B~, C~ and
+    // (w B~)^T planes (and, off the column-owned path, the C~ fragment of step kk)
+    auto write_planes = [&](int kk, const float (&ob)[8], const float (&oc)[8]) {
         // the 8 components n0 .. n0 + 7 share their swizzle in the (w B~)^T plane
         const int n0 = kk * 32 + 8 * gq;
         if constexpr (Cfg::BF) {
@@ -1048,6 +1030,85 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
             float *wb = (float *)sm.wb + tr_off<Cfg>(n0, row);
 #pragma unroll
             for (int j = 0; j < 8; ++j) wb[j * Cfg::RPP] = ob[j] * wt;
+        }
+    };
+    if constexpr (Cfg::HS) {
+        // half-split pairing: component n = k2*32 + 8g + j (step k2 < KS/2) pairs with n + N/2
+        // (step k2 + KS/2, same slot); pair n's angle is in angle group 2 k2 + j / 4
+#pragma unroll
+        for (int k2 = 0; k2 < KS / 2; ++k2) {
+            float vb0[8], vc0[8], vb1[8], vc1[8];
+            prep(k2, vb0, vc0);
+            prep(k2 + KS / 2, vb1, vc1);
+            float ob0[8], oc0[8], ob1[8], oc1[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int q = 2 * k2 + (j >> 2);
+                float sn, cn;
+                fast_sincos(rb.th[q * 4 + (j & 3)] + phoff[q][j & 3], sn, cn);
+                const float u = vb0[j], v = vb1[j];
+                ob0[j] = u * cn - v * sn;
+                ob1[j] = u * sn + v * cn;
+                if constexpr (WANT_C) {
+                    const float uc = vc0[j], vcc = vc1[j];
+                    oc0[j] = uc * cn - vcc * sn;
+                    oc1[j] = uc * sn + vcc * cn;
+                }
+            }
+            if (last_tok) {
+                // the carried B~ of the call's last token, rotated into the global frame
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int n = k2 * 32 + 8 * gq + j;
+                    float sn, cn;
+                    fast_sincos((float)wrap_2pi(sm.base[n]), sn, cn);
+                    const float u = ob0[j], v = ob1[j];
+                    p.pB1[(c.bh * N + n) * R + r] = u * cn - v * sn;
+                    p.pB1[(c.bh * N + n + N / 2) * R + r] = u * sn + v * cn;
+                }
+            }
+            write_planes(k2, ob0, oc0);
+            write_planes(k2 + KS / 2, ob1, oc1);
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            float vb[8], vc[8];
+            prep(kk, vb, vc);
+            float ob[8], oc[8];
+#pragma unroll
+            for (int jp = 0; jp < 4; ++jp) {
+                const int n = kk * 32 + 8 * gq + 2 * jp;
+                float ang;
+                if constexpr (Cfg::VEC) ang = rb.th[kk * 4 + jp] + phoff[kk][jp];
+                else ang = (rv && n < N) ? ((const float *)sm.phi)[tok * Cfg::PHP + n / 2] : 0.f;
+                float sn, cn;
+                fast_sincos(ang, sn, cn);
+                const float u = vb[2 * jp], v = vb[2 * jp + 1];
+                ob[2 * jp] = u * cn - v * sn;
+                ob[2 * jp + 1] = u * sn + v * cn;
+                if constexpr (WANT_C) {
+                    const float uc = vc[2 * jp], vcc = vc[2 * jp + 1];
+                    oc[2 * jp] = uc * cn - vcc * sn;
+                    oc[2 * jp + 1] = uc * sn + vcc * cn;
+                }
+            }
+            if (last_tok) {
+                // the carried B~ of the call's last token: from the block frame to the global frame
+                // (the running angle at this block's start)
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp) {
+                    const int n = kk * 32 + 8 * gq + 2 * jp;
+                    if (n < N) {
+                        float sn, cn;
+                        fast_sincos((float)wrap_2pi(sm.base[n / 2]), sn, cn);
+                        const float u = ob[2 * jp], v = ob[2 * jp + 1];
+                        p.pB1[(c.bh * N + n) * R + r] = u * cn - v * sn;
+                        p.pB1[(c.bh * N + n + 1) * R + r] = u * sn + v * cn;
+                    }
+                }
+            }
+            write_planes(kk, ob, oc);
         }
     }
     (void)tid;
@@ -1106,6 +1167,17 @@ __device__ __forceinline__ void rot_neg(f32x4_t &v, float c0, float s0, float c1
     v[2] = u1 * c1 + v1 * s1;
     v[3] = -u1 * s1 + v1 * c1;
 }
+// Half-split pairing: slot i of a (row n) pairs with slot i of b (row n + N/2); rotation by
+// -angle_i with (cos, sin) of pairs n .. n+3 in (cs01, cs23) = (c0, s0, c1, s1), (c2, s2, c3, s3).
+__device__ __forceinline__ void rot_neg_hs(f32x4_t &a, f32x4_t &b, const f32x4_t &cs01, const f32x4_t &cs23) {
+    const float cc[4] = {cs01[0], cs01[2], cs23[0], cs23[2]}, ss[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float u = a[i], v = b[i];
+        a[i] = u * cc[i] + v * ss[i];
+        b[i] = -u * ss[i] + v * cc[i];
+    }
+}
 
 // Carry update:  H <- Rot(-Phi) (decay H + S), with the matrix cores adding S
 // into the decayed state in place.
@@ -1115,13 +1187,24 @@ __device__ __forceinline__ void carry_block(const Sm &sm, f32x4_t (&hs)[Cfg::TPW
 #pragma unroll
     for (int m = 0; m < Cfg::TPW; ++m) hs[m] *= decay;
     mfma_state<Cfg>(sm, hs);
+    if constexpr (Cfg::HS) {
 #pragma unroll
-    for (int m = 0; m < Cfg::TPW; ++m) {
-        int nt, pt;
-        if (!state_tile<Cfg>(m, nt, pt)) continue;
-        const int pr = (nt * 16 + 4 * gq) >> 1;  // pairs pr, pr + 1 (pr even)
-        const f32x4_t cs4 = *(const f32x4_t *)(sm.csr + 2 * pr);
-        rot_neg(hs[m], cs4[0], cs4[1], cs4[2], cs4[3]);
+        for (int m = 0; m < Cfg::HSM; ++m) {
+            int nt, pt;
+            state_tile<Cfg>(m, nt, pt);
+            const int n0 = nt * 16 + 4 * gq;  // pairs n0 .. n0 + 3 (rows n0 + i and n0 + i + N/2)
+            const f32x4_t cs01 = *(const f32x4_t *)(sm.csr + 2 * n0), cs23 = *(const f32x4_t *)(sm.csr + 2 * n0 + 4);
+            rot_neg_hs(hs[m], hs[m + Cfg::HSM], cs01, cs23);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < Cfg::TPW; ++m) {
+            int nt, pt;
+            if (!state_tile<Cfg>(m, nt, pt)) continue;
+            const int pr = (nt * 16 + 4 * gq) >> 1;  // pairs pr, pr + 1 (pr even)
+            const f32x4_t cs4 = *(const f32x4_t *)(sm.csr + 2 * pr);
+            rot_neg(hs[m], cs4[0], cs4[1], cs4[2], cs4[3]);
+        }
     }
 }
 
@@ -1261,9 +1344,9 @@ __device__ __forceinline__ void stage_affine(const Sm &sm, const ScanParams &p, 
 }
 
 // ============================================================ state kernel
-template <class Io, int NP, int PP, int MODE, bool PJ>
+template <class Io, int NP, int PP, int MODE, bool PJ, bool HS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) void seg_state_kernel(ScanParams p) {
-    using Cfg = SegCfg<Io, NP, PP, MODE, true, PJ>;
+    using Cfg = SegCfg<Io, NP, PP, MODE, true, PJ, HS>;
     constexpr bool VEC = Cfg::VEC;
     using Frag = typename std::conditional<Cfg::BF, FragH, FragF>::type;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1518,9 +1601,9 @@ __device__ __forceinline__ void col_outputs(const Sm &sm, const ScanParams &p, c
 // ============================================================ output kernel
 // With N above 64 the LDS planes allow one workgroup per compute unit (one wave per
 // SIMD), so such variants may use the whole register file.
-template <class Io, int NP, int PP, int MODE, bool GATE, bool PJ>
+template <class Io, int NP, int PP, int MODE, bool GATE, bool PJ, bool HS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1 : 2, NP > 64 ? 1 : 2))) void seg_output_kernel(ScanParams p) {
-    using Cfg = SegCfg<Io, NP, PP, MODE, !GATE, PJ>;
+    using Cfg = SegCfg<Io, NP, PP, MODE, !GATE, PJ, HS>;
     constexpr bool VEC = Cfg::VEC;
     using ET = typename Io::T;
     using Frag = typename std::conditional<Cfg::BF, FragH, FragF>::type;
@@ -1607,13 +1690,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                     }
                     hs[m][i] = v;
                 }
-                if (p.ang0) {
+                if (!Cfg::HS && p.ang0) {
                     // rotate by -Theta_init
                     const int pr = (nt * 16 + 4 * gq) >> 1;
                     float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
                     if (pr < p.nr) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * p.nr + pr])); s0 = sc_[0]; c0 = sc_[1]; }
                     if (pr + 1 < p.nr) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi((double)p.ang0[bh * p.nr + pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
                     rot_neg(hs[m], c0, s0, c1, s1);
+                }
+            }
+            if (Cfg::HS && p.ang0) {
+                // rotate by -Theta_init (half-split: rows n and n + N/2 of pair n)
+#pragma unroll
+                for (int m = 0; m < Cfg::HSM; ++m) {
+                    int nt, pt;
+                    state_tile<Cfg>(m, nt, pt);
+                    const int n0 = nt * 16 + 4 * gq;
+                    float cs[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float sn = 0.f, cn = 1.f;
+                        if (n0 + i < p.nr) fast_sincos((float)wrap_2pi((double)p.ang0[bh * p.nr + n0 + i]), sn, cn);
+                        cs[2 * i] = cn;
+                        cs[2 * i + 1] = sn;
+                    }
+                    rot_neg_hs(hs[m], hs[m + Cfg::HSM], f32x4_t{cs[0], cs[1], cs[2], cs[3]},
+                               f32x4_t{cs[4], cs[5], cs[6], cs[7]});
                 }
             }
             // fold the earlier segments: H <- Rot(-Phi_s) (exp(l_s) H) + S_s (the aggregate is
@@ -1635,21 +1737,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                         int nt, pt;
                         if (!state_tile<Cfg>(m, nt, pt)) continue;
                         sv[k][m] = *(const f32x4_t *)(Sg + ((size_t)(wave + 4 * m) * 64 + lane) * 4);
-                        // (cos, sin) of pairs nt*8 + 2*gq and the next one
-                        cs[k][m] = *(const f32x4_t *)(p.cseg + (bs * p.np2 + nt * 8 + 2 * gq) * 2);
+                        if constexpr (Cfg::HS) {
+                            // (cos, sin) of pairs n0 .. n0 + 3 (tile m < HSM), in slots m and m + HSM
+                            if (m < Cfg::HSM) {
+                                const float *cp = p.cseg + (bs * p.np2 + nt * 16 + 4 * gq) * 2;
+                                cs[k][m] = *(const f32x4_t *)cp;
+                                cs[k][m + Cfg::HSM] = *(const f32x4_t *)(cp + 4);
+                            }
+                        } else {
+                            // (cos, sin) of pairs nt*8 + 2*gq and the next one
+                            cs[k][m] = *(const f32x4_t *)(p.cseg + (bs * p.np2 + nt * 8 + 2 * gq) * 2);
+                        }
                     }
                 }
 #pragma unroll
                 for (int k = 0; k < FB; ++k) {
                     if (s0 + k >= c.seg) break;
                     const float dec = __expf(lg[k]);
+                    if constexpr (Cfg::HS) {
 #pragma unroll
-                    for (int m = 0; m < TPW; ++m) {
-                        int nt, pt;
-                        if (!state_tile<Cfg>(m, nt, pt)) continue;
-                        f32x4_t a = dec * hs[m];
-                        rot_neg(a, cs[k][m][0], cs[k][m][1], cs[k][m][2], cs[k][m][3]);
-                        hs[m] = a + sv[k][m];
+                        for (int m = 0; m < Cfg::HSM; ++m) {
+                            f32x4_t a = dec * hs[m], b = dec * hs[m + Cfg::HSM];
+                            rot_neg_hs(a, b, cs[k][m], cs[k][m + Cfg::HSM]);
+                            hs[m] = a + sv[k][m];
+                            hs[m + Cfg::HSM] = b + sv[k][m + Cfg::HSM];
+                        }
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < TPW; ++m) {
+                            int nt, pt;
+                            if (!state_tile<Cfg>(m, nt, pt)) continue;
+                            f32x4_t a = dec * hs[m];
+                            rot_neg(a, cs[k][m][0], cs[k][m][1], cs[k][m][2], cs[k][m][3]);
+                            hs[m] = a + sv[k][m];
+                        }
                     }
                 }
             }
@@ -2022,17 +2143,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
         if (tid < N2) sm.base[tid] += (double)sm.pend[tid];
         lds_barrier();  // final base angles visible
         // final state in the global frame: Rot(Theta_final) H
+        f32x4_t hf[TPW];
+        if constexpr (Cfg::HS) {
+#pragma unroll
+            for (int m = 0; m < Cfg::HSM; ++m) {
+                int nt, pt;
+                state_tile<Cfg>(m, nt, pt);
+                const int n0 = nt * 16 + 4 * gq;
+                float cs[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x2_t sc_ = sincos_acc((float)wrap_2pi(sm.base[n0 + i]));
+                    cs[2 * i] = sc_[1];
+                    cs[2 * i + 1] = -sc_[0];  // rotation by +Theta
+                }
+                hf[m] = hs[m];
+                hf[m + Cfg::HSM] = hs[m + Cfg::HSM];
+                rot_neg_hs(hf[m], hf[m + Cfg::HSM], f32x4_t{cs[0], cs[1], cs[2], cs[3]}, f32x4_t{cs[4], cs[5], cs[6], cs[7]});
+            }
+        }
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             int nt, pt;
             if (!state_tile<Cfg>(m, nt, pt)) continue;
             const int pp = pt * 16 + l16;
-            const int pr = (nt * 16 + 4 * gq) >> 1;
-            float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
-            if (pr < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi(sm.base[pr])); s0 = sc_[0]; c0 = sc_[1]; }
-            if (pr + 1 < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi(sm.base[pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
-            f32x4_t a = hs[m];
-            rot_neg(a, c0, -s0, c1, -s1);  // rotation by +Theta
+            f32x4_t a;
+            if constexpr (Cfg::HS) {
+                a = hf[m];
+            } else {
+                const int pr = (nt * 16 + 4 * gq) >> 1;
+                float s0 = 0.f, c0 = 1.f, s1 = 0.f, c1 = 1.f;
+                if (pr < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi(sm.base[pr])); s0 = sc_[0]; c0 = sc_[1]; }
+                if (pr + 1 < N2) { const f32x2_t sc_ = sincos_acc((float)wrap_2pi(sm.base[pr + 1])); s1 = sc_[0]; c1 = sc_[1]; }
+                a = hs[m];
+                rot_neg(a, c0, -s0, c1, -s1);  // rotation by +Theta
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int nn = nt * 16 + 4 * gq + i;
@@ -2131,18 +2276,18 @@ static hipError_t set_lds(K kern, size_t bytes) {
     return hipSuccess;
 }
 
-template <class Io, int NP, int PP, int MODE, bool PJ>
+template <class Io, int NP, int PP, int MODE, bool PJ, bool HS = false>
 static hipError_t launch_seg_pj(bool output, const ScanParams &p, hipStream_t st) {
-    using Cfg = SegCfg<Io, NP, PP, MODE, true, PJ>;
+    using Cfg = SegCfg<Io, NP, PP, MODE, true, PJ, HS>;
     if (output) {
         // variant with the silu(z) output gate when z is given
-        auto kern = p.z ? seg_output_kernel<Io, NP, PP, MODE, true, PJ> : seg_output_kernel<Io, NP, PP, MODE, false, PJ>;
+        auto kern = p.z ? seg_output_kernel<Io, NP, PP, MODE, true, PJ, HS> : seg_output_kernel<Io, NP, PP, MODE, false, PJ, HS>;
         hipError_t e = set_lds(kern, Cfg::OUTPUT_BYTES);
         if (e != hipSuccess) return e;
         const int64_t nwg = p.B * p.H * (int64_t)p.ncg * p.nseg;
         hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(256), Cfg::OUTPUT_BYTES, st, p);
     } else {
-        auto kern = seg_state_kernel<Io, NP, PP, MODE, PJ>;
+        auto kern = seg_state_kernel<Io, NP, PP, MODE, PJ, HS>;
         hipError_t e = set_lds(kern, Cfg::STATE_BYTES);
         if (e != hipSuccess) return e;
         const int64_t nwg = p.B * p.H * (int64_t)p.ncg * p.nsub;
@@ -2153,12 +2298,18 @@ static hipError_t launch_seg_pj(bool output, const ScanParams &p, hipStream_t st
 }
 
 // the projection variant when the call has MIMO projections (never on the rank-1 16-byte path)
+// the half-split variant (rank-1 16-byte path with N = NP >= 64 only)
 template <class Io, int NP, int PP, int MODE>
 static hipError_t launch_seg_t(bool output, const TileShape &ts, const ScanParams &p, hipStream_t st) {
     if constexpr (MODE != kModeVec) {
+        if (ts.hs) return hipErrorInvalidValue;
         if (ts.pj) return launch_seg_pj<Io, NP, PP, MODE, true>(output, p, st);
     } else {
         if (ts.pj) return hipErrorInvalidValue;
+        if (ts.hs) {
+            if constexpr (NP >= 64) return launch_seg_pj<Io, NP, PP, MODE, false, true>(output, p, st);
+            else return hipErrorInvalidValue;
+        }
     }
     return launch_seg_pj<Io, NP, PP, MODE, false>(output, p, st);
 }

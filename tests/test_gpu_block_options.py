@@ -159,10 +159,23 @@ def test_all_options_long_segments(io):
     (40, 32, 16, 3, 16, "f32", ("half", "gate")),             # element-path MIMO
 ])
 def test_half_split(T, P, N, R, Q, io, opts):
-    """Rotation pairs (i, i + N/2): the scans run on N-permuted copies; states in and out in
-    the caller's (half-split) layout."""
+    """Rotation pairs (i, i + N/2): natively on the rank-1 16-byte path with N = 64 or 128
+    (rows 1 and 2), on N-permuted copies otherwise; states in and out in the caller's
+    (half-split) layout."""
     w = custom(batch=2, seqlen=T, nheads=2, headdim=P, dstate=N, rank=R, chunk=Q, io=io, seed=T + 7)
     run_scan(w, set(opts), nr=N // 4 if "rope" in opts else None)
+
+
+@pytest.mark.parametrize("T,Q,io,opts", [
+    (2048, 16, "bf16", ("half",)),                 # long segments: the prefix pass, permuted copies
+    (700, 32, "f32", ("half", "rope", "gate")),    # native pairing over several segments, P 32 tiles
+])
+def test_half_split_segments(T, Q, io, opts):
+    """Half-split pairing over many blocks: the native kernels' carried, folded and final
+    states, and the permuted-copy path where the prefix pass runs."""
+    w = custom(batch=1, seqlen=T, nheads=2, headdim=32 if io == "f32" else 64, dstate=64, rank=1, chunk=Q, io=io,
+               seed=T + Q)
+    run_scan(w, set(opts), nr=8 if "rope" in opts else None)
 
 
 # ---------------------------------------------------------------- decode step and streaming
