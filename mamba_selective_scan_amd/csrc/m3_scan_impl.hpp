@@ -1450,7 +1450,7 @@ __device__ __forceinline__ void load_z_col(RawZCol &rz, const ScanParams &p, con
     for (int T = 0; T < 4; ++T) {
         const int t = T * 16 + l16;
         u32x2_t v = {0u, 0u};
-        if (t < g.Tv && pc < c.Pw) v = *(const u32x2_t *)(zb + (int64_t)t * c.sz + pc);
+        if (t < g.Tv && pc < c.Pw) v = *(const u32x2_t *)(zb + (uint32_t)(t * c.sz + pc));
         rz.w[T] = v;
     }
 }
@@ -1541,6 +1541,7 @@ __device__ __forceinline__ void col_outputs(const Sm &sm, const ScanParams &p, c
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) xa[kk] = *(const u32x4_t *)((const uint16_t *)sm.xt + xt_off<Cfg>(w * 16 + l16, kk * 32 + 8 * gq));
     const int pc = w * 16 + 4 * gq;
+    ET *const yblk = (ET *)c.yb + g.t0 * c.sy;  // this block's first output row (row offsets fit 32 bits)
     // two row tiles at a time: every LDS operand of the pair is requested before its products
 #pragma unroll
     for (int T0 = 0; T0 < 4; T0 += 2) {
@@ -1593,7 +1594,7 @@ __device__ __forceinline__ void col_outputs(const Sm &sm, const ScanParams &p, c
             }
             M3_DCHECK(p, !(t < g.Tv && pc < c.Pw) || (g.t0 + t < p.T && c.p0 + pc + 4 <= p.P));
             if (t < g.Tv && pc < c.Pw)
-                *(u32x2_t *)((ET *)c.yb + (g.t0 + t) * c.sy + pc) = u32x2_t{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])};
+                *(u32x2_t *)(yblk + (uint32_t)(t * c.sy + pc)) = u32x2_t{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])};
         }
     }
 }
