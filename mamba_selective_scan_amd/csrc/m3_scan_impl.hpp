@@ -1720,46 +1720,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                 }
             }
             // fold the earlier segments: H <- Rot(-Phi_s) (exp(l_s) H) + S_s (the aggregate is
-            // already in its segment's end frame).  FB segments at a time, so that their loads are
-            // in flight together; slots past the last segment reload it and are not applied.
-            constexpr int FB = TPW <= 4 ? 4 : 2;
+            // already in its segment's end frame).  FB segments at a time: each wave loads its
+            // tiles of all FB aggregates at once (slots past the last segment reload it and are
+            // not applied), while the workgroup stages the FB segments' (cos, sin) per pair and
+            // decays in LDS (the B~ plane, free until the first block's prologue), so that one
+            // round trip to memory serves up to FB segments.
+            constexpr int FB = TPW <= 2 ? 16 : TPW <= 4 ? 8 : 4;
+            static_assert((FB * NP + FB) * sizeof(float) <= Cfg::L_BT, "fold tables exceed the B~ plane");
             const int64_t q = bh * p.ncg + c.cg;
+            float *fcs = (float *)sm.bt;              // [FB][np2][2] (cos, sin)
+            float *flg = fcs + FB * Cfg::NP;          // [FB] decay log
             for (int s0 = 0; s0 < c.seg; s0 += FB) {
-                f32x4_t sv[FB][TPW], cs[FB][TPW];
-                float lg[FB];
+                const int nk = min(FB, c.seg - s0);
+                f32x4_t sv[FB][TPW];
 #pragma unroll
                 for (int k = 0; k < FB; ++k) {
                     const int s2 = min(s0 + k, c.seg - 1);
-                    const int64_t bs = bh * p.nsub + s2;
-                    lg[k] = p.lseg[bs];
                     const float *Sg = p.Sagg + (q * p.nsub + s2) * (int64_t)(NP * PP);
 #pragma unroll
                     for (int m = 0; m < TPW; ++m) {
                         int nt, pt;
                         if (!state_tile<Cfg>(m, nt, pt)) continue;
                         sv[k][m] = *(const f32x4_t *)(Sg + ((size_t)(wave + 4 * m) * 64 + lane) * 4);
-                        if constexpr (Cfg::HS) {
-                            // (cos, sin) of pairs n0 .. n0 + 3 (tile m < HSM), in slots m and m + HSM
-                            if (m < Cfg::HSM) {
-                                const float *cp = p.cseg + (bs * p.np2 + nt * 16 + 4 * gq) * 2;
-                                cs[k][m] = *(const f32x4_t *)cp;
-                                cs[k][m + Cfg::HSM] = *(const f32x4_t *)(cp + 4);
-                            }
-                        } else {
-                            // (cos, sin) of pairs nt*8 + 2*gq and the next one
-                            cs[k][m] = *(const f32x4_t *)(p.cseg + (bs * p.np2 + nt * 8 + 2 * gq) * 2);
-                        }
                     }
                 }
+                {
+                    // the nk segments' (cos, sin) tables are contiguous: [nk][np2][2] floats
+                    const float *cb = p.cseg + (bh * p.nsub + s0) * (int64_t)p.np2 * 2;
+                    const int nv = nk * p.np2 / 2;  // float4s
+                    M3_DCHECK(p, p.np2 <= Cfg::NP / 2 && nv * 4 <= FB * Cfg::NP);
+                    for (int v = tid; v < nv; v += 256) *(f32x4_t *)(fcs + 4 * v) = *(const f32x4_t *)(cb + 4 * v);
+                    if (tid < nk) flg[tid] = p.lseg[bh * p.nsub + s0 + tid];
+                }
+                lds_barrier();
 #pragma unroll
                 for (int k = 0; k < FB; ++k) {
-                    if (s0 + k >= c.seg) break;
-                    const float dec = __expf(lg[k]);
+                    if (k >= nk) break;
+                    const float dec = __expf(flg[k]);
+                    const float *ck = fcs + k * p.np2 * 2;
                     if constexpr (Cfg::HS) {
 #pragma unroll
                         for (int m = 0; m < Cfg::HSM; ++m) {
+                            int nt, pt;
+                            state_tile<Cfg>(m, nt, pt);
+                            // (cos, sin) of pairs n0 .. n0 + 3 (tile m < HSM) pair rows m and m + HSM
+                            const float *cp = ck + (nt * 16 + 4 * gq) * 2;
                             f32x4_t a = dec * hs[m], b = dec * hs[m + Cfg::HSM];
-                            rot_neg_hs(a, b, cs[k][m], cs[k][m + Cfg::HSM]);
+                            rot_neg_hs(a, b, *(const f32x4_t *)cp, *(const f32x4_t *)(cp + 4));
                             hs[m] = a + sv[k][m];
                             hs[m + Cfg::HSM] = b + sv[k][m + Cfg::HSM];
                         }
@@ -1768,12 +1775,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NP > 64 ? 1
                         for (int m = 0; m < TPW; ++m) {
                             int nt, pt;
                             if (!state_tile<Cfg>(m, nt, pt)) continue;
+                            // (cos, sin) of pairs nt*8 + 2*gq and the next one
+                            const f32x4_t cs4 = *(const f32x4_t *)(ck + (nt * 8 + 2 * gq) * 2);
                             f32x4_t a = dec * hs[m];
-                            rot_neg(a, cs[k][m][0], cs[k][m][1], cs[k][m][2], cs[k][m][3]);
+                            rot_neg(a, cs4[0], cs4[1], cs4[2], cs4[3]);
                             hs[m] = a + sv[k][m];
                         }
                     }
                 }
+                if (s0 + FB < c.seg) lds_barrier();  // the next round rewrites the tables
             }
             if (tid < N2) {
                 double a = init_angle(p, bh, tid);
