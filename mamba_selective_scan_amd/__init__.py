@@ -403,14 +403,15 @@ def m3_scan_bwd_workspace_bytes(shape: Shape) -> int:
 def m3_scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5, b_norm_w=None,
                 c_norm_w=None, b_bias=None, c_bias=None, init=None, dfinal=None, rope_pairs=None,
                 dt_softplus=False, dt_bias=None, lam_sigmoid=False, z=None, workspace=None,
-                stream=None, half_split=False):
+                stream=None, half_split=False, init_grad=True):
     """Gradients of m3_scan_siso / m3_scan_mimo (SISO when x is 4-D) given ``dy``.
 
     ``init`` is the forward call's initial state and ``dfinal`` the gradients of its final
     state (dicts h, prev_B, prev_x, angle; either may be None).  Returns a dict of tensors
     shaped like the inputs: x, B, C, dt, lam, theta, A, D, b_norm_w, c_norm_w, b_bias
     ([H, R, N]), c_bias, dt_bias, z (gated calls) and init (a dict of the initial state's
-    gradients).  Parameter gradients are sums over batch and tokens.
+    gradients, or None with ``init_grad=False``, which also skips their kernel when no initial
+    state is given).  Parameter gradients are sums over batch and tokens.
     """
     lib = load()
     mimo = x.dim() == 5
@@ -423,11 +424,11 @@ def m3_scan_bwd(x, B, C, dt, lam, theta, A, D, dy, *, bcnorm=True, eps=1e-5, b_n
     H, N, R = s.nheads, s.dstate, s.rank
     with _alloc_on(stream):
         return _bwd_call(lib, s, inp, x, B, C, dt, lam, theta, A, D, dy, z, init, dfinal, workspace, stream,
-                         dev, f32, H, N, R)
+                         dev, f32, H, N, R, init_grad)
 
 
 def _bwd_call(lib, s, inp, x, B, C, dt, lam, theta, A, D, dy, z, init, dfinal, workspace, stream, dev, f32,
-              H, N, R):
+              H, N, R, init_grad=True):
     g = dict(x=torch.empty_like(x), B=torch.empty_like(B), C=torch.empty_like(C),
              dt=torch.empty_like(dt), lam=torch.empty_like(lam), theta=torch.empty_like(theta),
              A=torch.empty_like(A), D=torch.empty_like(D),
@@ -440,7 +441,7 @@ def _bwd_call(lib, s, inp, x, B, C, dt, lam, theta, A, D, dy, z, init, dfinal, w
                                          "c_norm_w", "b_bias", "c_bias", "dt_bias", "z")))
     st_in = _state(s, init, dev, "init")
     st_df = _state(s, dfinal, dev, "dfinal")
-    dinit = new_state(s.batch, s.nheads, s.headdim, s.dstate, s.rank, dev, _rotated(s))
+    dinit = new_state(s.batch, s.nheads, s.headdim, s.dstate, s.rank, dev, _rotated(s)) if init_grad else None
     st_di = _state(s, dinit, dev, "dinit")
     need = int(lib.m3_scan_bwd_workspace_bytes(ctypes.byref(s)))
     if workspace is None:
@@ -449,7 +450,7 @@ def _bwd_call(lib, s, inp, x, B, C, dt, lam, theta, A, D, dy, z, init, dfinal, w
     rc = lib.m3_scan_bwd(ctypes.byref(s), ctypes.byref(inp), _ptr(dy),
                          ctypes.byref(st_in) if st_in is not None else None,
                          ctypes.byref(st_df) if st_df is not None else None,
-                         ctypes.byref(gr), ctypes.byref(st_di), _ptr(workspace),
+                         ctypes.byref(gr), ctypes.byref(st_di) if st_di is not None else None, _ptr(workspace),
                          ctypes.c_size_t(workspace.numel()), _stream(stream))
     _check(rc, "m3_scan_bwd")
     g["init"] = dinit

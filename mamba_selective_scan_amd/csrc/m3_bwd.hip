@@ -775,8 +775,11 @@ __global__ __launch_bounds__(kThreads, (state_min_waves_per_simd<NPAD, PPAD, VEC
 
 // ---------------------------------------------------------------- state passes over the chunks
 // blockIdx.y 0: states before each chunk (in place of S); 1: adjoints after each chunk (in
-// place of U) and the initial state's adjoint.  Thread: (sequence, pair, column).
+// place of U) and the initial state's adjoint.  Thread: (sequence, pair, column).  Each
+// thread's chain over the chunks is serial; the loads of KQ chunks are issued together (8 or
+// 16 measured slower at T 16384: the registers they take halve the waves in flight).
 __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
+    constexpr int KQ = 4;
     const int N = p.N, P = p.P, N2 = N / 2, NR = p.nr, R = p.R, nck = p.nck;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= p.B * p.H * N2 * (int64_t)P) return;
@@ -812,10 +815,10 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
             g1 = v;
         }
         float *S = p.Sst + bh * nck * NP + (int64_t)(2 * i) * P + pc;
-        for (int c0 = 0; c0 < nck; c0 += 4) {
-            float s0[4], s1[4], dec[4], ph[4];
+        for (int c0 = 0; c0 < nck; c0 += KQ) {
+            float s0[KQ], s1[KQ], dec[KQ], ph[KQ];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < KQ; ++q) {
                 const int ck = c0 + q;
                 s0[q] = s1[q] = ph[q] = dec[q] = 0.f;
                 if (ck < nck) {
@@ -826,22 +829,23 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
                 }
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < KQ; ++q) {
                 const int ck = c0 + q;
-                if (ck >= nck) break;
-                S[ck * NP] = g0;
-                S[ck * NP + P] = g1;
-                const float d = __expf(dec[q]);
-                const float u = d * g0 + s0[q], v = d * g1 + s1[q];
-                if (ck == nck - 1) {  // state after the last chunk, in its frame
-                    p.hfin[(bh * N + 2 * i) * P + pc] = u;
-                    p.hfin[(bh * N + 2 * i + 1) * P + pc] = v;
-                    break;
+                if (ck < nck) {
+                    S[ck * NP] = g0;
+                    S[ck * NP + P] = g1;
+                    const float d = __expf(dec[q]);
+                    const float u = d * g0 + s0[q], v = d * g1 + s1[q];
+                    if (ck == nck - 1) {  // state after the last chunk, in its frame
+                        p.hfin[(bh * N + 2 * i) * P + pc] = u;
+                        p.hfin[(bh * N + 2 * i + 1) * P + pc] = v;
+                    } else {
+                        float s, c;
+                        fast_sincos(ph[q], s, c);
+                        g0 = c * u + s * v;
+                        g1 = -s * u + c * v;
+                    }
                 }
-                float s, c;
-                fast_sincos(ph[q], s, c);
-                g0 = c * u + s * v;
-                g1 = -s * u + c * v;
             }
         }
         return;
@@ -849,7 +853,13 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
     // reverse: the frame of the last chunk is the angle before it
     double th = (rot && p.ang0) ? (double)p.ang0[bh * NR + i] : 0.0;
     if (rot)
-        for (int ck = 0; ck + 1 < nck; ++ck) th += (double)p.phic[(bh * nck + ck) * N2 + i];
+        for (int c0 = 0; c0 + 1 < nck; c0 += KQ) {
+            float v[KQ];  // KQ independent loads in flight, summed in chunk order
+#pragma unroll
+            for (int q = 0; q < KQ; ++q) v[q] = c0 + q + 1 < nck ? p.phic[(bh * nck + c0 + q) * N2 + i] : 0.f;
+#pragma unroll
+            for (int q = 0; q < KQ; ++q) th += (double)v[q];
+        }
     const float thl = rot ? (float)wrap_2pi(th) : 0.f;
     if (pc == 0) p.thst[bh * N2 + i] = thl;
     float gb0 = 0.f, gb1 = 0.f;
@@ -861,10 +871,10 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
         gb1 = -s * d0 + c * d1;
     }
     float *U = p.Ust + bh * nck * NP + (int64_t)(2 * i) * P + pc;
-    for (int c0 = nck - 1; c0 >= 0; c0 -= 4) {
-        float u0[4], u1[4], dec[4], ph[4];
+    for (int c0 = nck - 1; c0 >= 0; c0 -= KQ) {
+        float u0[KQ], u1[KQ], dec[KQ], ph[KQ];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < KQ; ++q) {
             const int ck = c0 - q;
             u0[q] = u1[q] = ph[q] = dec[q] = 0.f;
             if (ck >= 0) {
@@ -875,17 +885,18 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
             }
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < KQ; ++q) {
             const int ck = c0 - q;
-            if (ck < 0) break;
-            U[ck * NP] = gb0;
-            U[ck * NP + P] = gb1;
-            const float d = __expf(dec[q]);
-            const float a = d * gb0 + u0[q], v = d * gb1 + u1[q];
-            float s, c;
-            fast_sincos(ph[q], s, c);
-            gb0 = c * a - s * v;
-            gb1 = s * a + c * v;
+            if (ck >= 0) {
+                U[ck * NP] = gb0;
+                U[ck * NP + P] = gb1;
+                const float d = __expf(dec[q]);
+                const float a = d * gb0 + u0[q], v = d * gb1 + u1[q];
+                float s, c;
+                fast_sincos(ph[q], s, c);
+                gb0 = c * a - s * v;
+                gb1 = s * a + c * v;
+            }
         }
     }
     // adjoint of the state before the first chunk, in the global frame
@@ -1777,7 +1788,8 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(BwdParams p) {
     if (tid < Tv) {
         const int64_t t = t0 + tid, bth = (b * T + t) * H + h;
         const float *d = p.dsc + (bh * T + t) * 3;
-        const float dprev = t == 0 ? p.deta0[bh] : p.dsc[(bh * T + t - 1) * 3 + 2];
+        // (deta0 is NULL when no initial state enters: its eta weight has no gradient)
+        const float dprev = t == 0 ? (p.deta0 ? p.deta0[bh] : 0.f) : p.dsc[(bh * T + t - 1) * 3 + 2];
         float dt, lam, dsp, dsg;
         act_scalars(p, bth, h, dt, lam, dsp, dsg);
         const float Av = (p.flags & kFlagAPerToken) ? p.A[bth] : p.A[h];
@@ -1934,9 +1946,17 @@ hipError_t launch_bwd(bool bf16, const BwdParams &p, hipStream_t st) {
     if (e != hipSuccess) return e;
     const unsigned nbh = (unsigned)(p.B * p.H);
     hipLaunchKernelGGL(bwd_angle_suffix_kernel, dim3(nbh), dim3(kThreads), 0, st, p);
-    if (bf16) hipLaunchKernelGGL(bwd_init_kernel<IoBF16>, dim3(nbh), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL(bwd_init_kernel<IoF32>, dim3(nbh), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(bwd_token_kernel, dim3((unsigned)(nbh * p.nck)), dim3(256), 0, st, p);
+    // The initial-state kernel has work only when an initial state enters (its eta-weighted
+    // prev_B prev_x^T term feeds d dt and d lambda of the first token) or a gradient of the
+    // initial state is requested; otherwise the token kernel takes that term as zero.
+    BwdParams pt = p;
+    if (p.dh0 || p.dpB0 || p.dpx0 || p.dang0 || (p.pB0 && p.px0)) {
+        if (bf16) hipLaunchKernelGGL(bwd_init_kernel<IoBF16>, dim3(nbh), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL(bwd_init_kernel<IoF32>, dim3(nbh), dim3(256), 0, st, p);
+    } else {
+        pt.deta0 = nullptr;
+    }
+    hipLaunchKernelGGL(bwd_token_kernel, dim3((unsigned)(nbh * p.nck)), dim3(256), 0, st, pt);
     const int total = 3 * p.H + 2 * p.N + 2 * p.H * p.R * p.N;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)total), dim3(256), 0, st, p);
     return hipGetLastError();

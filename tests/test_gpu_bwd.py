@@ -181,6 +181,33 @@ def test_bwd_empty_sequence():
     assert float(g["D"].abs().sum()) == 0.0 and float(g["A"].abs().sum()) == 0.0
 
 
+@pytest.mark.parametrize("with_init", [False, True])
+def test_bwd_without_initial_state_gradients(with_init):
+    """dinit = NULL (init_grad=False) leaves every other gradient bit-identical; without an
+    initial state the initial-state kernel is skipped and its eta term taken as zero."""
+    import torch
+    m3 = _m3()
+    w = custom(batch=2, seqlen=150, nheads=3, headdim=32, dstate=32, io="bf16", seed=31)
+    log(f"case bwd init_grad=False with_init={with_init} {w}")
+    inp = make_inputs(w)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in inp.items()}
+    for k in ("x", "B", "C"):
+        dev[k] = dev[k].to(torch.bfloat16)
+    kw = {}
+    if with_init:
+        kw["init"] = {k: torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).cuda()
+                      for k, v in make_state(w, scale=0.5).items()}
+    dy = torch.randn(dev["x"].shape, device="cuda").to(torch.bfloat16)
+    args = (dev["x"], dev["B"], dev["C"], dev["dt"], dev["lam"], dev["theta"], dev["A"], dev["D"], dy)
+    ga = m3.m3_scan_bwd(*args, **kw)
+    gb = m3.m3_scan_bwd(*args, init_grad=False, **kw)
+    torch.cuda.synchronize()
+    assert gb["init"] is None
+    for k, v in ga.items():
+        if isinstance(v, torch.Tensor):
+            assert torch.equal(v, gb[k]), k
+
+
 @pytest.mark.fullsize
 @pytest.mark.parametrize("opts", [("rope", "atok", "act", "gate"), ("half",)])
 def test_bwd_full_workload_options(opts):
