@@ -425,6 +425,7 @@ m3_status bwd_impl(const m3_shape *s, const m3_inputs *in, const void *dy, const
     p.flags = s->flags;
     p.eps = s->norm_eps;
     p.nr = nr;
+    p.hs = (s->flags & M3_FLAG_HALF_SPLIT) ? 1 : 0;  // (reached with the flag only through native_half_split_bwd)
     p.x = in->x;
     p.Bm = in->Bm;
     p.Cm = in->Cm;
@@ -636,6 +637,11 @@ m3_status scan_half_split(const m3_shape *s, const m3_inputs *in, void *y, const
     return hp.e == hipSuccess ? M3_OK : M3_EHIP;
 }
 
+// The gradient kernels pair (i, i + N/2) themselves when N is 64 or 128 (the two columns of a
+// pair then sit in one lane of the chunk kernel's per-column passes); other sizes run on
+// N-permuted copies.
+bool native_half_split_bwd(const m3_shape *s) { return s->dstate == 64 || s->dstate == 128; }
+
 m3_status bwd_half_split(const m3_shape *s, const m3_inputs *in, const void *dy, const m3_state *init,
                          const m3_state *dfin, m3_grads *g, m3_state *dinit, void *ws, size_t ws_bytes,
                          void *stream) {
@@ -647,6 +653,10 @@ m3_status bwd_half_split(const m3_shape *s, const m3_inputs *in, const void *dy,
         s1.flags &= ~M3_FLAG_HALF_SPLIT;
         return bwd_impl(&s1, in, dy, init, dfin, g, dinit, ws, ws_bytes, stream);
     }
+    // (the workspace is always the size m3_scan_bwd_workspace_bytes reports for the shape,
+    // which holds the permuted copies whichever path runs)
+    if (!ws || ws_bytes < bwd_ws_bytes(s)) return M3_EWORKSPACE;
+    if (native_half_split_bwd(s)) return bwd_impl(s, in, dy, init, dfin, g, dinit, ws, ws_bytes, stream);
     m3_shape s2 = *s;
     s2.flags &= ~M3_FLAG_HALF_SPLIT;
     const size_t base = align_up(bwd_plan_of(&s2).total);

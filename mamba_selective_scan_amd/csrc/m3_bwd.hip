@@ -162,6 +162,25 @@ __device__ __forceinline__ float eta_at(const BwdParams &p, int64_t b, int h, in
 // the chunk's running angles (PH) and the rows' norm factors (RS) for the norm backward when
 // they fit beside the rest; otherwise the angles share the slab area and are computed again.
 // SPLIT (chunk-state kernel): one B~/C~ tile and one x/dy tile, staged one side at a time.
+// Columns of rotation pair i (i < NPAD / 2): (2i, 2i + 1); with the half-split pairing
+// (i, i + N/2) for i < N/2, and the padding columns N + 2(i - N/2) and the next beyond, so that
+// every lane of a pair-per-lane pass owns two columns of its own.
+__device__ __forceinline__ int pn0(const BwdParams &p, int i) {
+    const int h = p.N >> 1;
+    return !p.hs ? 2 * i : (i < h ? i : p.N + 2 * (i - h));
+}
+__device__ __forceinline__ int pn1(const BwdParams &p, int i) {
+    const int h = p.N >> 1;
+    return !p.hs ? 2 * i + 1 : (i < h ? i + h : p.N + 2 * (i - h) + 1);
+}
+
+// The same map in the chunk kernels, where the half-split pairing (HS) needs N = NPAD: pair i
+// is (2i, 2i + 1), or (i, i + NPAD/2), at compile time.
+template <bool HS, int NPAD>
+__device__ __forceinline__ constexpr int pc0(int i) { return HS ? i : 2 * i; }
+template <bool HS, int NPAD>
+__device__ __forceinline__ constexpr int pc1(int i) { return HS ? i + NPAD / 2 : 2 * i + 1; }
+
 template <int NPAD, int PPAD, bool GRAD = false, bool SPLIT = false>
 struct CL {
     static constexpr int BP = NPAD + 1, XP = PPAD + 1, N2P = NPAD / 2;
@@ -273,7 +292,7 @@ __device__ __forceinline__ float vec_elem(const u32x4_t &v, int j) {
 // SIDES: 3 stages both sides; 1 (B~ and x, with the per-token scalars, angles and row tables)
 // and then 2 (C~ and gated dy, reusing those) stage one side at a time into the shared tiles
 // of the split layout.
-template <class Io, int NPAD, int PPAD, bool SCALED, int SIDES = 3>
+template <class Io, int NPAD, int PPAD, bool SCALED, int SIDES = 3, bool HS = false>
 __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, int h, int64_t t0, int Tv) {
     using ET = typename Io::T;
     using L = CL<NPAD, PPAD, !SCALED, SIDES != 3>;
@@ -325,13 +344,14 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
     const int pl = RP::pair();
     const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
     const bool okg = pl < N2;
-    float gb0 = ld_raw(bnp, 2 * pl, okg && p.bnw), gb1 = ld_raw(bnp, 2 * pl + 1, okg && p.bnw);
-    float gc0 = ld_raw(cnp, 2 * pl, okg && p.cnw), gc1 = ld_raw(cnp, 2 * pl + 1, okg && p.cnw);
+    const int q0 = pc0<HS, NPAD>(pl), q1 = pc1<HS, NPAD>(pl);  // this lane's two columns
+    float gb0 = ld_raw(bnp, q0, okg && p.bnw), gb1 = ld_raw(bnp, q1, okg && p.bnw);
+    float gc0 = ld_raw(cnp, q0, okg && p.cnw), gc1 = ld_raw(cnp, q1, okg && p.cnw);
     const bool rdiv = (8 % R) == 0;
     const float *bbp = p.bbias ? p.bbias : p.dt, *cbp = p.cbias ? p.cbias : p.dt;
-    const int64_t obw = ((int64_t)h * R + (wv % R)) * N + 2 * pl;
-    float bw0 = ld_raw(bbp, obw, okg && rdiv && p.bbias), bw1 = ld_raw(bbp, obw + 1, okg && rdiv && p.bbias);
-    float cw0 = ld_raw(cbp, obw, okg && rdiv && p.cbias), cw1 = ld_raw(cbp, obw + 1, okg && rdiv && p.cbias);
+    const int64_t obw = ((int64_t)h * R + (wv % R)) * N;
+    float bw0 = ld_raw(bbp, obw + q0, okg && rdiv && p.bbias), bw1 = ld_raw(bbp, obw + q1, okg && rdiv && p.bbias);
+    float cw0 = ld_raw(cbp, obw + q0, okg && rdiv && p.cbias), cw1 = ld_raw(cbp, obw + q1, okg && rdiv && p.cbias);
     // ---- zero padding of the tiles (disjoint from the loaded elements)
     for (int row = wv; row < kRows; row += kWaves) {
         for (int col = lane; col < L::XP; col += 64)
@@ -435,12 +455,13 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
     gc0 = okg && p.cnw ? gc0 : 1.f;
     gc1 = okg && p.cnw ? gc1 : 1.f;
     const int lp = pl < L::N2P ? pl : 0;
+    const int l0 = pc0<HS, NPAD>(lp), l1 = pc1<HS, NPAD>(lp);  // the clamped pair's columns, for the LDS reads
 #pragma unroll
     for (int m = 0; m < RP::NM; ++m) {
         const int rho = RP::row(wv, m), k = rho / R, r = rho - k * R;
         const bool valid = k < Qt && k < Tv && pl < N2;
-        float b0 = DOB ? sm[L::SB + rho * L::BP + 2 * lp] : 0.f, b1 = DOB ? sm[L::SB + rho * L::BP + 2 * lp + 1] : 0.f;
-        float c0 = DOC ? sm[L::SC + rho * L::BP + 2 * lp] : 0.f, c1 = DOC ? sm[L::SC + rho * L::BP + 2 * lp + 1] : 0.f;
+        float b0 = DOB ? sm[L::SB + rho * L::BP + l0] : 0.f, b1 = DOB ? sm[L::SB + rho * L::BP + l1] : 0.f;
+        float c0 = DOC ? sm[L::SC + rho * L::BP + l0] : 0.f, c1 = DOC ? sm[L::SC + rho * L::BP + l1] : 0.f;
         b0 = valid ? b0 : 0.f;
         b1 = valid ? b1 : 0.f;
         c0 = valid ? c0 : 0.f;
@@ -456,14 +477,14 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         }
         float bi0 = bw0, bi1 = bw1, ci0 = cw0, ci1 = cw1;
         if (!rdiv) {
-            const int64_t ob = ((int64_t)h * R + r) * N + 2 * pl;
+            const int64_t ob = ((int64_t)h * R + r) * N;
             if (DOB) {
-                bi0 = ld_raw(bbp, ob, valid && p.bbias);
-                bi1 = ld_raw(bbp, ob + 1, valid && p.bbias);
+                bi0 = ld_raw(bbp, ob + q0, valid && p.bbias);
+                bi1 = ld_raw(bbp, ob + q1, valid && p.bbias);
             }
             if (DOC) {
-                ci0 = ld_raw(cbp, ob, valid && p.cbias);
-                ci1 = ld_raw(cbp, ob + 1, valid && p.cbias);
+                ci0 = ld_raw(cbp, ob + q0, valid && p.cbias);
+                ci1 = ld_raw(cbp, ob + q1, valid && p.cbias);
             }
         }
         bi0 = p.bbias ? bi0 : 0.f;
@@ -485,12 +506,12 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
         const float v0 = fc * (cn * c0 - sn * c1), v1 = fc * (sn * c0 + cn * c1);
         if (pl < L::N2P) {
             if (DOB) {
-                sm[L::SB + rho * L::BP + 2 * pl] = valid ? u0 : 0.f;
-                sm[L::SB + rho * L::BP + 2 * pl + 1] = valid ? u1 : 0.f;
+                sm[L::SB + rho * L::BP + q0] = valid ? u0 : 0.f;
+                sm[L::SB + rho * L::BP + q1] = valid ? u1 : 0.f;
             }
             if (DOC) {
-                sm[L::SC + rho * L::BP + 2 * pl] = valid ? v0 : 0.f;
-                sm[L::SC + rho * L::BP + 2 * pl + 1] = valid ? v1 : 0.f;
+                sm[L::SC + rho * L::BP + q0] = valid ? v0 : 0.f;
+                sm[L::SC + rho * L::BP + q1] = valid ? v1 : 0.f;
             }
         }
     }
@@ -502,7 +523,7 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
 // e^(cs_end - cs) kappa and e^cs when SCALED), x and gated dy rows, zero padding.  Every
 // global load of the chunk is issued before the first use.
 // Returns (per thread) its part of sum(dy_gated * x).  SIDES as in chunk_prologue_vec.
-template <class Io, int NPAD, int PPAD, bool SCALED, int SIDES = 3>
+template <class Io, int NPAD, int PPAD, bool SCALED, int SIDES = 3, bool HS = false>
 __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h, int64_t t0, int Tv) {
     using ET = typename Io::T;
     using L = CL<NPAD, PPAD, !SCALED, SIDES != 3>;
@@ -539,6 +560,7 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
     using RP = RowPass<L::N2P>;
     constexpr int NM = RP::NM;
     const int pl = RP::pair();
+    const int q0 = pc0<HS, NPAD>(pl), q1 = pc1<HS, NPAD>(pl);  // this lane's two columns
     ET rbr[NM][2], rcr[NM][2];
     float bb[NM][2], cb[NM][2];
     bool ro[NM];
@@ -547,21 +569,21 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
     for (int m = 0; m < NM; ++m) {
         const int rho = RP::row(wv, m), k = rho / R, r = rho - k * R;
         ro[m] = k < Qt && k < Tv && pl < N2;
-        const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)N * R + (int64_t)(2 * pl) * R + r;
-        rbr[m][0] = ld_raw((const ET *)p.Bm, o, ro[m]);
-        rbr[m][1] = ld_raw((const ET *)p.Bm, o + R, ro[m]);
-        rcr[m][0] = ld_raw((const ET *)p.Cm, o, ro[m]);
-        rcr[m][1] = ld_raw((const ET *)p.Cm, o + R, ro[m]);
-        const int64_t ob = ((int64_t)h * R + r) * N + 2 * pl;
-        bb[m][0] = ld_raw(bbp, ob, ro[m] && p.bbias);
-        bb[m][1] = ld_raw(bbp, ob + 1, ro[m] && p.bbias);
-        cb[m][0] = ld_raw(cbp, ob, ro[m] && p.cbias);
-        cb[m][1] = ld_raw(cbp, ob + 1, ro[m] && p.cbias);
+        const int64_t o = ((b * T + t0 + k) * H + h) * (int64_t)N * R + r;
+        rbr[m][0] = ld_raw((const ET *)p.Bm, o + (int64_t)q0 * R, ro[m]);
+        rbr[m][1] = ld_raw((const ET *)p.Bm, o + (int64_t)q1 * R, ro[m]);
+        rcr[m][0] = ld_raw((const ET *)p.Cm, o + (int64_t)q0 * R, ro[m]);
+        rcr[m][1] = ld_raw((const ET *)p.Cm, o + (int64_t)q1 * R, ro[m]);
+        const int64_t ob = ((int64_t)h * R + r) * N;
+        bb[m][0] = ld_raw(bbp, ob + q0, ro[m] && p.bbias);
+        bb[m][1] = ld_raw(bbp, ob + q1, ro[m] && p.bbias);
+        cb[m][0] = ld_raw(cbp, ob + q0, ro[m] && p.cbias);
+        cb[m][1] = ld_raw(cbp, ob + q1, ro[m] && p.cbias);
     }
     const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
     const bool okg = pl < N2;
-    float gb0 = ld_raw(bnp, 2 * pl, okg && p.bnw), gb1 = ld_raw(bnp, 2 * pl + 1, okg && p.bnw);
-    float gc0 = ld_raw(cnp, 2 * pl, okg && p.cnw), gc1 = ld_raw(cnp, 2 * pl + 1, okg && p.cnw);
+    float gb0 = ld_raw(bnp, q0, okg && p.bnw), gb1 = ld_raw(bnp, q1, okg && p.bnw);
+    float gc0 = ld_raw(cnp, q0, okg && p.cnw), gc1 = ld_raw(cnp, q1, okg && p.cnw);
     // ---- values (after every load is in flight)
     dtr = okt ? dtr : 0.f;
     lmr = okt ? lmr : 0.f;
@@ -674,12 +696,12 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
         const float v0 = fc * (cn * c0 - sn * c1), v1 = fc * (sn * c0 + cn * c1);
         if (pl < L::N2P) {
             if (DOB) {
-                sm[L::SB + rho * L::BP + 2 * pl] = valid ? u0 : 0.f;
-                sm[L::SB + rho * L::BP + 2 * pl + 1] = valid ? u1 : 0.f;
+                sm[L::SB + rho * L::BP + q0] = valid ? u0 : 0.f;
+                sm[L::SB + rho * L::BP + q1] = valid ? u1 : 0.f;
             }
             if (DOC) {
-                sm[L::SC + rho * L::BP + 2 * pl] = valid ? v0 : 0.f;
-                sm[L::SC + rho * L::BP + 2 * pl + 1] = valid ? v1 : 0.f;
+                sm[L::SC + rho * L::BP + q0] = valid ? v0 : 0.f;
+                sm[L::SC + rho * L::BP + q1] = valid ? v1 : 0.f;
             }
         }
     }
@@ -712,7 +734,7 @@ constexpr bool state_split() {
 template <int NPAD, int PPAD, bool VEC>
 constexpr int state_min_waves_per_simd() { return state_split<NPAD, PPAD, VEC>() ? 2 * kThreads / 256 : 1; }
 
-template <class Io, int NPAD, int PPAD, bool VEC>
+template <class Io, int NPAD, int PPAD, bool VEC, bool HS = false>
 __global__ __launch_bounds__(kThreads, (state_min_waves_per_simd<NPAD, PPAD, VEC>())) void bwd_chunk_state_kernel(BwdParams p) {
     constexpr bool SPLIT = state_split<NPAD, PPAD, VEC>();
     using L = CL<NPAD, PPAD, false, SPLIT>;
@@ -756,16 +778,16 @@ __global__ __launch_bounds__(kThreads, (state_min_waves_per_simd<NPAD, PPAD, VEC
         }
     };
     if constexpr (SPLIT) {
-        if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true, 1>(p, sm, b, h, t0, Tv);
-        else chunk_prologue<Io, NPAD, PPAD, true, 1>(p, sm, b, h, t0, Tv);
+        if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true, 1, HS>(p, sm, b, h, t0, Tv);
+        else chunk_prologue<Io, NPAD, PPAD, true, 1, HS>(p, sm, b, h, t0, Tv);
         products(0, 0, NT * PT);
         __syncthreads();  // the shared tiles are restaged for the C side
-        if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true, 2>(p, sm, b, h, t0, Tv);
-        else chunk_prologue<Io, NPAD, PPAD, true, 2>(p, sm, b, h, t0, Tv);
+        if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true, 2, HS>(p, sm, b, h, t0, Tv);
+        else chunk_prologue<Io, NPAD, PPAD, true, 2, HS>(p, sm, b, h, t0, Tv);
         products(1, NT * PT, 2 * NT * PT);
     } else {
-        if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
-        else chunk_prologue<Io, NPAD, PPAD, true>(p, sm, b, h, t0, Tv);
+        if constexpr (VEC) chunk_prologue_vec<Io, NPAD, PPAD, true, 3, HS>(p, sm, b, h, t0, Tv);
+        else chunk_prologue<Io, NPAD, PPAD, true, 3, HS>(p, sm, b, h, t0, Tv);
         products(0, 0, NT * PT);
         products(1, NT * PT, 2 * NT * PT);
     }
@@ -790,19 +812,21 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
     const int h = (int)(bh - b * p.H);
     const bool rot = i < NR;
     const int64_t NP = (int64_t)N * P;
+    const int n0 = pn0(p, i), n1 = pn1(p, i);        // the pair's two state rows
+    const int64_t dr = (int64_t)(n1 - n0) * P;        // from the first row to the second
     if (blockIdx.y == 0) {
         float g0 = 0.f, g1 = 0.f;
         if (p.h0) {
-            g0 = p.h0[(bh * N + 2 * i) * P + pc];
-            g1 = p.h0[(bh * N + 2 * i + 1) * P + pc];
+            g0 = p.h0[(bh * N + n0) * P + pc];
+            g1 = p.h0[(bh * N + n1) * P + pc];
         }
         if (p.pB0 && p.px0) {
             const float eta = eta_at(p, b, h, -1);
             float a0 = 0.f, a1 = 0.f;
             for (int r = 0; r < R; ++r) {
                 const float xv = p.px0[(bh * P + pc) * R + r];
-                a0 += p.pB0[(bh * N + 2 * i) * R + r] * xv;
-                a1 += p.pB0[(bh * N + 2 * i + 1) * R + r] * xv;
+                a0 += p.pB0[(bh * N + n0) * R + r] * xv;
+                a1 += p.pB0[(bh * N + n1) * R + r] * xv;
             }
             g0 += eta * a0;
             g1 += eta * a1;
@@ -814,7 +838,7 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
             g0 = u;
             g1 = v;
         }
-        float *S = p.Sst + bh * nck * NP + (int64_t)(2 * i) * P + pc;
+        float *S = p.Sst + bh * nck * NP + (int64_t)n0 * P + pc;
         for (int c0 = 0; c0 < nck; c0 += KQ) {
             float s0[KQ], s1[KQ], dec[KQ], ph[KQ];
 #pragma unroll
@@ -823,7 +847,7 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
                 s0[q] = s1[q] = ph[q] = dec[q] = 0.f;
                 if (ck < nck) {
                     s0[q] = S[ck * NP];
-                    s1[q] = S[ck * NP + P];
+                    s1[q] = S[ck * NP + dr];
                     dec[q] = p.lsum[bh * nck + ck];
                     ph[q] = rot ? p.phic[(bh * nck + ck) * N2 + i] : 0.f;
                 }
@@ -833,12 +857,12 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
                 const int ck = c0 + q;
                 if (ck < nck) {
                     S[ck * NP] = g0;
-                    S[ck * NP + P] = g1;
+                    S[ck * NP + dr] = g1;
                     const float d = __expf(dec[q]);
                     const float u = d * g0 + s0[q], v = d * g1 + s1[q];
                     if (ck == nck - 1) {  // state after the last chunk, in its frame
-                        p.hfin[(bh * N + 2 * i) * P + pc] = u;
-                        p.hfin[(bh * N + 2 * i + 1) * P + pc] = v;
+                        p.hfin[(bh * N + n0) * P + pc] = u;
+                        p.hfin[(bh * N + n1) * P + pc] = v;
                     } else {
                         float s, c;
                         fast_sincos(ph[q], s, c);
@@ -864,13 +888,13 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
     if (pc == 0) p.thst[bh * N2 + i] = thl;
     float gb0 = 0.f, gb1 = 0.f;
     if (p.dh1) {
-        const float d0 = p.dh1[(bh * N + 2 * i) * P + pc], d1 = p.dh1[(bh * N + 2 * i + 1) * P + pc];
+        const float d0 = p.dh1[(bh * N + n0) * P + pc], d1 = p.dh1[(bh * N + n1) * P + pc];
         float s = 0.f, c = 1.f;
         if (rot) fast_sincos(thl, s, c);
         gb0 = c * d0 + s * d1;
         gb1 = -s * d0 + c * d1;
     }
-    float *U = p.Ust + bh * nck * NP + (int64_t)(2 * i) * P + pc;
+    float *U = p.Ust + bh * nck * NP + (int64_t)n0 * P + pc;
     for (int c0 = nck - 1; c0 >= 0; c0 -= KQ) {
         float u0[KQ], u1[KQ], dec[KQ], ph[KQ];
 #pragma unroll
@@ -879,7 +903,7 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
             u0[q] = u1[q] = ph[q] = dec[q] = 0.f;
             if (ck >= 0) {
                 u0[q] = U[ck * NP];
-                u1[q] = U[ck * NP + P];
+                u1[q] = U[ck * NP + dr];
                 dec[q] = p.lsum[bh * nck + ck];
                 ph[q] = (rot && ck > 0) ? p.phic[(bh * nck + ck - 1) * N2 + i] : 0.f;
             }
@@ -889,7 +913,7 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
             const int ck = c0 - q;
             if (ck >= 0) {
                 U[ck * NP] = gb0;
-                U[ck * NP + P] = gb1;
+                U[ck * NP + dr] = gb1;
                 const float d = __expf(dec[q]);
                 const float a = d * gb0 + u0[q], v = d * gb1 + u1[q];
                 float s, c;
@@ -902,12 +926,14 @@ __global__ __launch_bounds__(256) void bwd_state_pass_kernel(BwdParams p) {
     // adjoint of the state before the first chunk, in the global frame
     float s = 0.f, c = 1.f;
     if (rot && p.ang0) fast_sincos((float)wrap_2pi((double)p.ang0[bh * NR + i]), s, c);
-    p.G0w[(bh * N + 2 * i) * P + pc] = c * gb0 - s * gb1;
-    p.G0w[(bh * N + 2 * i + 1) * P + pc] = s * gb0 + c * gb1;
+    p.G0w[(bh * N + n0) * P + pc] = c * gb0 - s * gb1;
+    p.G0w[(bh * N + n1) * P + pc] = s * gb0 + c * gb1;
 }
 
 // ---------------------------------------------------------------- per-chunk gradients
-template <class Io, int NPAD, int PPAD>
+// HS: the half-split pairing (p.hs, N = NPAD of 64 or 128), compiled separately so that the
+// adjacent pairing's per-column angle terms keep their lane-pair form.
+template <class Io, int NPAD, int PPAD, bool HS = false>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     using ET = typename Io::T;
     using L = CL<NPAD, PPAD, true>;
@@ -955,8 +981,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
     load_slab(stg[0], Gend, 0);
     // (a run-time choice here: with both staging variants in one kernel the register
     // allocation of the matrix phases comes out better than with either alone)
-    const float dDp = p.vec ? chunk_prologue_vec<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv)
-                            : chunk_prologue<Io, NPAD, PPAD, false>(p, sm, b, h, t0, Tv);
+    const float dDp = p.vec ? chunk_prologue_vec<Io, NPAD, PPAD, false, 3, HS>(p, sm, b, h, t0, Tv)
+                            : chunk_prologue<Io, NPAD, PPAD, false, 3, HS>(p, sm, b, h, t0, Tv);
     if constexpr (PFA) {
         load_slab(stg[1], Hst, 0);
 #pragma unroll
@@ -1327,8 +1353,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
 #pragma unroll
         for (int ns = 0; ns < NH; ++ns) {
             const int n = 16 * (2 * ns + hf) + l16;
-            const bool odd = (n & 1) != 0;
-            const int i2 = n >> 1;
+            // component (odd) and pair (i2) of column n, and the pair's other column; with the
+            // half-split pairing (N = NPAD of 64 or 128) the other column n +- N/2 is in this
+            // lane's slot ns +- NH/2
+            const bool odd = HS ? n >= N2 : (n & 1) != 0;
+            const int i2 = HS ? (odd ? n - N2 : n) : n >> 1;
+            const int nx = HS ? (odd ? n - N2 : n + N2) : n ^ 1;
             float thc = 1.f, ths = 0.f;
             if (last && p.dpB1 && n < N && i2 < NR) fast_sincos(p.thst[bh * N2 + i2], ths, thc);
 #pragma unroll
@@ -1337,7 +1367,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
                 const float z = rdec(row) * accZ[ns][i];
                 float db = accB[ns][i] + rkap(row) * z;
                 if (last && k == Tv - 1 && p.dpB1 && n < N) {
-                    const float d0 = p.dpB1[(bh * N + 2 * i2) * R + r], d1 = p.dpB1[(bh * N + 2 * i2 + 1) * R + r];
+                    const float d0 = p.dpB1[(bh * N + pc0<HS, NPAD>(i2)) * R + r], d1 = p.dpB1[(bh * N + pc1<HS, NPAD>(i2)) * R + r];
                     db += odd ? (-ths * d0 + thc * d1) : (thc * d0 + ths * d1);
                 }
                 const float ci = recs(row) * accCi[ns][i];
@@ -1346,13 +1376,24 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
                 ksum[i] += bn * z;
                 asum[i] += cn * ci;
                 // <d, J v> over the pair: component 0 pairs with -v1, component 1 with v0
-                const float bo = sB[row * BP + (n ^ 1)], co = sC[row * BP + (n ^ 1)];
+                const float bo = sB[row * BP + nx], co = sC[row * BP + nx];
                 float term = odd ? (db * bo + dc * co) : -(db * bo + dc * co);
-                term += dpp_f<0xB1>(term);
+                if constexpr (!HS) term += dpp_f<0xB1>(term);  // adjacent pairs: the other column is lane ^ 1
                 dph[ns][i] = term;
                 accB[ns][i] = db;
                 accC[ns][i] = dc;
             }
+        }
+        if constexpr (HS) {
+            // half-split pairs: the two columns' terms are in slots ns and ns + NH/2
+#pragma unroll
+            for (int ns = 0; ns < NH / 2; ++ns)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float t = dph[ns][i] + dph[ns + NH / 2][i];
+                    dph[ns][i] = t;
+                    dph[ns + NH / 2][i] = t;
+                }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1373,7 +1414,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * w + 4 * g + i;
-            if (!(n & 1)) dphi[row * N2P + (n >> 1)] = (n >> 1) < NR ? dph[ns][i] : 0.f;
+            if constexpr (HS) {
+                if (n < N2) dphi[row * N2P + n] = n < NR ? dph[ns][i] : 0.f;
+            } else if (!(n & 1)) {
+                dphi[row * N2P + (n >> 1)] = (n >> 1) < NR ? dph[ns][i] : 0.f;
+            }
             sB[row * BP + n] = accB[ns][i];
             sC[row * BP + n] = accC[ns][i];
         }
@@ -1454,17 +1499,18 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         using RP = RowPass<N2P>;
         constexpr int NM = RP::NM;
         const int pl = RP::pair();
+        const int q0 = pc0<HS, NPAD>(pl), q1 = pc1<HS, NPAD>(pl);  // this lane's two columns
         ET rr[NM][2][2];
         bool ro[NM];
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             const int rho = RP::row(wv, m), k = rho / R, r = rho - k * R;
             ro[m] = k < Qt && k < Tv && pl < N2;
-            const int64_t o = (bth0 + (int64_t)k * H) * N * R + (int64_t)(2 * pl) * R + r;
-            rr[m][0][0] = ld_raw((const ET *)p.Bm, o, ro[m]);
-            rr[m][0][1] = ld_raw((const ET *)p.Bm, o + R, ro[m]);
-            rr[m][1][0] = ld_raw((const ET *)p.Cm, o, ro[m]);
-            rr[m][1][1] = ld_raw((const ET *)p.Cm, o + R, ro[m]);
+            const int64_t o = (bth0 + (int64_t)k * H) * N * R + r;
+            rr[m][0][0] = ld_raw((const ET *)p.Bm, o + (int64_t)q0 * R, ro[m]);
+            rr[m][0][1] = ld_raw((const ET *)p.Bm, o + (int64_t)q1 * R, ro[m]);
+            rr[m][1][0] = ld_raw((const ET *)p.Cm, o + (int64_t)q0 * R, ro[m]);
+            rr[m][1][1] = ld_raw((const ET *)p.Cm, o + (int64_t)q1 * R, ro[m]);
         }
         if constexpr (!L::KEEP) {
             AngleTile<N2P> ang;
@@ -1486,12 +1532,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
             for (int k = 0; k < Tv; ++k) {
                 float sn, cn;
                 fast_sincos(sm[L::PH + k * N2P + i], sn, cn);
-                const float e0 = rows[(k * R + r) * BP + 2 * i], e1 = rows[(k * R + r) * BP + 2 * i + 1];
+                const float e0 = rows[(k * R + r) * BP + pc0<HS, NPAD>(i)], e1 = rows[(k * R + r) * BP + pc1<HS, NPAD>(i)];
                 a0 += cn * e0 + sn * e1;
                 a1 += -sn * e0 + cn * e1;
             }
-            acc[16 * NPAD + (side * R + r) * NPAD + 2 * i] = a0;
-            acc[16 * NPAD + (side * R + r) * NPAD + 2 * i + 1] = a1;
+            acc[16 * NPAD + (side * R + r) * NPAD + pc0<HS, NPAD>(i)] = a0;
+            acc[16 * NPAD + (side * R + r) * NPAD + pc1<HS, NPAD>(i)] = a1;
         }
         __syncthreads();
         const bool norm = (p.flags & kFlagNorm) != 0;
@@ -1503,16 +1549,17 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         {
             const float *bnp = p.bnw ? p.bnw : p.dt, *cnp = p.cnw ? p.cnw : p.dt;
             const bool okb = pl < N2 && p.bnw, okc = pl < N2 && p.cnw;
-            gn[0][0] = ld_raw(bnp, 2 * pl, okb);
-            gn[0][1] = ld_raw(bnp, 2 * pl + 1, okb);
-            gn[1][0] = ld_raw(cnp, 2 * pl, okc);
-            gn[1][1] = ld_raw(cnp, 2 * pl + 1, okc);
+            gn[0][0] = ld_raw(bnp, q0, okb);
+            gn[0][1] = ld_raw(bnp, q1, okb);
+            gn[1][0] = ld_raw(cnp, q0, okc);
+            gn[1][1] = ld_raw(cnp, q1, okc);
             gn[0][0] = okb ? gn[0][0] : 1.f;
             gn[0][1] = okb ? gn[0][1] : 1.f;
             gn[1][0] = okc ? gn[1][0] : 1.f;
             gn[1][1] = okc ? gn[1][1] : 1.f;
         }
         const int lp = pl < N2P ? pl : 0;  // clamped pair for the LDS reads
+        const int l0 = pc0<HS, NPAD>(lp), l1 = pc1<HS, NPAD>(lp);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             const int rho = RP::row(wv, m), k = rho / R;
@@ -1526,7 +1573,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
                 float *rows = side == 0 ? sB : sC;
                 const float v0 = raw_f<Io>(rr[m][side][0], ro[m]), v1 = raw_f<Io>(rr[m][side][1], ro[m]);
                 const float g0 = gn[side][0], g1 = gn[side][1];
-                const float e0 = rows[rho * BP + 2 * lp], e1 = rows[rho * BP + 2 * lp + 1];
+                const float e0 = rows[rho * BP + l0], e1 = rows[rho * BP + l1];
                 const float d0 = lv ? cn * e0 + sn * e1 : 0.f, d1 = lv ? -sn * e0 + cn * e1 : 0.f;
                 float o0 = d0, o1 = d1;
                 if (norm) {
@@ -1542,8 +1589,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
                 ba[side][0] += d0;
                 ba[side][1] += d1;
                 if (lv) {
-                    rows[rho * BP + 2 * pl] = o0;
-                    rows[rho * BP + 2 * pl + 1] = o1;
+                    rows[rho * BP + q0] = o0;
+                    rows[rho * BP + q1] = o1;
                 }
             }
         }
@@ -1558,11 +1605,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         if (RP::half() == 0 && pl < NPAD / 2)
 #pragma unroll
             for (int side = 0; side < 2; ++side) {
-                acc[(wv * 2 + side) * NPAD + 2 * pl] = ga[side][0];
-                acc[(wv * 2 + side) * NPAD + 2 * pl + 1] = ga[side][1];
+                acc[(wv * 2 + side) * NPAD + q0] = ga[side][0];
+                acc[(wv * 2 + side) * NPAD + q1] = ga[side][1];
                 if (rdiv) {
-                    acc[16 * NPAD + (wv * 2 + side) * NPAD + 2 * pl] = ba[side][0];
-                    acc[16 * NPAD + (wv * 2 + side) * NPAD + 2 * pl + 1] = ba[side][1];
+                    acc[16 * NPAD + (wv * 2 + side) * NPAD + q0] = ba[side][0];
+                    acc[16 * NPAD + (wv * 2 + side) * NPAD + q1] = ba[side][1];
                 }
             }
     }
@@ -1690,11 +1737,11 @@ __global__ __launch_bounds__(256) void bwd_init_kernel(BwdParams p) {
     // initial angle: wave wv sums its share of the columns per pair (lane = pair)
     float a = 0.f;
     if (lane < NR) {
-        const int i = lane;
+        const int i = lane, n0 = pn0(p, i), n1 = pn1(p, i);
         const float *Gl = p.Ust + (bh * nck + nck - 1) * N * (int64_t)P;  // adjoint after the last chunk
         const float *Hf = p.hfin + bh * N * (int64_t)P;                     // state after it, same frame
         for (int pc = wv; pc < P; pc += 4) {
-            const int64_t o0 = (int64_t)(2 * i) * P + pc, o1 = o0 + P;
+            const int64_t o0 = (int64_t)n0 * P + pc, o1 = (int64_t)n1 * P + pc;
             a += -Gl[o0] * Hf[o1] + Gl[o1] * Hf[o0];
             if (p.h0) a -= -G0[o0] * p.h0[bh * N * (int64_t)P + o1] + G0[o1] * p.h0[bh * N * (int64_t)P + o0];
         }
@@ -1705,12 +1752,12 @@ __global__ __launch_bounds__(256) void bwd_init_kernel(BwdParams p) {
                 if (p.px0)
                     for (int pc = 0; pc < P; ++pc) {
                         const float xv = p.px0[(bh * P + pc) * R + r];
-                        d0 += G0[(int64_t)(2 * i) * P + pc] * xv;
-                        d1 += G0[(int64_t)(2 * i + 1) * P + pc] * xv;
+                        d0 += G0[(int64_t)n0 * P + pc] * xv;
+                        d1 += G0[(int64_t)n1 * P + pc] * xv;
                     }
                 d0 *= eta;
                 d1 *= eta;
-                a -= -d0 * p.pB0[(bh * N + 2 * i + 1) * R + r] + d1 * p.pB0[(bh * N + 2 * i) * R + r];
+                a -= -d0 * p.pB0[(bh * N + n1) * R + r] + d1 * p.pB0[(bh * N + n0) * R + r];
             }
         }
     }
@@ -1722,23 +1769,24 @@ __global__ __launch_bounds__(256) void bwd_init_kernel(BwdParams p) {
             const ET *raw = (const ET *)p.Bm + bth * N * R + r;
             const bool norm = (p.flags & kFlagNorm) != 0;
             float v0 = 0.f, v1 = 0.f;
+            const int n0 = pn0(p, lane), n1 = pn1(p, lane);  // lane = pair
             if (lane < N2) {
-                v0 = Io::ld(raw + (int64_t)(2 * lane) * R);
-                v1 = Io::ld(raw + (int64_t)(2 * lane + 1) * R);
+                v0 = Io::ld(raw + (int64_t)n0 * R);
+                v1 = Io::ld(raw + (int64_t)n1 * R);
             }
             const float rs = norm ? rsqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)N + p.eps) : 1.f;
             if (lane < NR) {
                 const int i = lane;
-                float b0 = norm ? v0 * rs * (p.bnw ? p.bnw[2 * i] : 1.f) : v0;
-                float b1 = norm ? v1 * rs * (p.bnw ? p.bnw[2 * i + 1] : 1.f) : v1;
+                float b0 = norm ? v0 * rs * (p.bnw ? p.bnw[n0] : 1.f) : v0;
+                float b1 = norm ? v1 * rs * (p.bnw ? p.bnw[n1] : 1.f) : v1;
                 if (p.bbias) {
-                    b0 += p.bbias[((int64_t)h * R + r) * N + 2 * i];
-                    b1 += p.bbias[((int64_t)h * R + r) * N + 2 * i + 1];
+                    b0 += p.bbias[((int64_t)h * R + r) * N + n0];
+                    b1 += p.bbias[((int64_t)h * R + r) * N + n1];
                 }
                 const float th = (float)wrap_2pi((double)p.thst[bh * N2 + i] + (double)p.phic[(bh * nck + nck - 1) * N2 + i]);
                 float sn, cn;
                 fast_sincos(th, sn, cn);
-                const float e0 = p.dpB1[(bh * N + 2 * i) * R + r], e1 = p.dpB1[(bh * N + 2 * i + 1) * R + r];
+                const float e0 = p.dpB1[(bh * N + n0) * R + r], e1 = p.dpB1[(bh * N + n1) * R + r];
                 const float f0 = cn * e0 + sn * e1, f1 = -sn * e0 + cn * e1;
                 a += -f0 * b1 + f1 * b0;
             }
@@ -1898,17 +1946,23 @@ template <class Io, int NPAD, int PPAD, bool VEC>
 hipError_t launch_chunks_v(const BwdParams &p, hipStream_t st) {
     const size_t lds = chunk_lds<NPAD, PPAD, false, VEC>(), ldg = chunk_lds<NPAD, PPAD, true>();
     const dim3 grid((unsigned)(p.B * p.H * p.nck)), blk(kThreads);
+    // the half-split pairing in the chunk kernels needs N = NPAD of 64 or 128
+    if (p.hs && (NPAD < 64 || p.N != NPAD)) return hipErrorInvalidValue;
+    constexpr bool HSOK = NPAD >= 64;  // (no half-split variants below 64)
+    const bool hs = HSOK && p.hs;
+    const void *sk = hs ? (const void *)bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC, HSOK>
+                        : (const void *)bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC, false>;
+    const void *gk = hs ? (const void *)bwd_chunk_grad_kernel<Io, NPAD, PPAD, HSOK>
+                        : (const void *)bwd_chunk_grad_kernel<Io, NPAD, PPAD, false>;
     hipError_t e;
-    if ((e = hipFuncSetAttribute((const void *)bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-        return e;
-    if ((e = hipFuncSetAttribute((const void *)bwd_chunk_grad_kernel<Io, NPAD, PPAD>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldg)) != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC>), grid, blk, lds, st, p);
+    if ((e = hipFuncSetAttribute(sk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute(gk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldg)) != hipSuccess) return e;
+    if (hs) hipLaunchKernelGGL((bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC, HSOK>), grid, blk, lds, st, p);
+    else hipLaunchKernelGGL((bwd_chunk_state_kernel<Io, NPAD, PPAD, VEC, false>), grid, blk, lds, st, p);
     const int64_t ne = p.B * p.H * (p.N / 2) * (int64_t)p.P;
     hipLaunchKernelGGL(bwd_state_pass_kernel, dim3((unsigned)((ne + 255) / 256), 2), dim3(256), 0, st, p);
-    hipLaunchKernelGGL((bwd_chunk_grad_kernel<Io, NPAD, PPAD>), grid, blk, ldg, st, p);
+    if (hs) hipLaunchKernelGGL((bwd_chunk_grad_kernel<Io, NPAD, PPAD, HSOK>), grid, blk, ldg, st, p);
+    else hipLaunchKernelGGL((bwd_chunk_grad_kernel<Io, NPAD, PPAD, false>), grid, blk, ldg, st, p);
     return hipGetLastError();
 }
 

@@ -83,6 +83,7 @@ struct BwdParams {
     uint32_t flags;
     float eps;
     int nr;
+    int hs;  // pairs (i, i + N/2) (the half-split pairing, N 64 or 128) instead of (2i, 2i + 1)
     // forward inputs (as for ScanParams)
     const void *x, *Bm, *Cm;
     const float *dt, *lam, *theta, *A, *D;
