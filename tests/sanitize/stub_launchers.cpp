@@ -98,6 +98,10 @@ hipError_t launch_bwd(bool, const BwdParams &p, hipStream_t) {
         return hipSuccess;
     }
     if ((int64_t)p.nck * (64 / p.R) < p.T) fail("bwd plan");
+    // the half-split pairing reaches the kernels exactly at N = 64 or 128 (other sizes run on
+    // N-permuted copies with the flag cleared)
+    const bool hsflag = (p.flags & kFlagHalfSplit) != 0;
+    if (hsflag != (p.hs != 0) || (p.hs && p.N != 64 && p.N != 128)) fail("bwd half-split pairing");
     in_ws(p.Sst, C * N * P * 4, "Sst");
     in_ws(p.Ust, C * N * P * 4, "Ust");
     in_ws(p.lsum, C * 4, "lsum");
