@@ -47,10 +47,13 @@
  *                         state's rows) instead of (2i, 2i + 1): the rotate-half layout of
  *                         the canonical block.  torchmamba "Math notes" (RoPE trick on pairs
  *                         of state components); the pages leave the pairing layout open and
- *                         the two differ only by a permutation of N.  The scans and the
- *                         gradient call permute B, C, gains, biases and the state rows into
- *                         the workspace (larger workspace, one extra pass over B and C);
- *                         the decode step pairs natively.
+ *                         the two differ only by a permutation of N.  The decode step,
+ *                         the rank-1 scans at N = 64 or 128 whose state is not split finer
+ *                         than their output segments, and the gradient call at N = 64 or
+ *                         128 pair natively; other calls permute B, C, gains, biases and
+ *                         the state rows into the workspace (one extra pass over B and C).
+ *                         The workspace size reported for the flag holds those copies
+ *                         whichever route a call takes.
  *
  * Layouts: row-major, contiguous, last index fastest.
  *   x, y, z [B, T, H, P]        MIMO: [B, T, H, P, R]       io dtype
