@@ -149,11 +149,19 @@ def test_bwd_all_options(R):
     run_case(w, opts=("rope", "atok", "act", "gate"), nr=8)
 
 
-@pytest.mark.parametrize("R,io,opts", [(1, "bf16", ("half",)), (2, "f32", ("half", "rope", "atok", "act", "gate"))])
-def test_bwd_half_split(R, io, opts):
-    """Gradients with the half-split pairing (N-permuted copies in the workspace)."""
-    w = custom(batch=2, seqlen=90, nheads=2, headdim=32, dstate=32, rank=R, io=io, seed=29 + R)
-    run_case(w, opts=opts, nr=8 if "rope" in opts else None)
+@pytest.mark.parametrize("R,N,P,io,opts", [
+    (1, 32, 32, "bf16", ("half",)),                                 # N 32: N-permuted copies
+    (2, 32, 32, "f32", ("half", "rope", "atok", "act", "gate")),    # N 32: N-permuted copies
+    (1, 64, 32, "bf16", ("half",)),                                 # N 64: pairs in the kernels
+    (2, 64, 48, "f32", ("half", "rope", "atok", "act", "gate")),    # N 64, rank 2, every option
+    (1, 128, 64, "bf16", ("half", "rope")),                         # N 128, partial rotation
+    (3, 128, 24, "f32", ("half",)),                                 # N 128, rank 3 (element loads)
+])
+def test_bwd_half_split(R, N, P, io, opts):
+    """Gradients with the half-split pairing: paired in the kernels at N = 64 or 128, through
+    N-permuted copies in the workspace otherwise."""
+    w = custom(batch=2, seqlen=90, nheads=2, headdim=P, dstate=N, rank=R, io=io, seed=29 + R + N)
+    run_case(w, opts=opts, nr=(N // 4 if N >= 64 else 8) if "rope" in opts else None)
 
 
 def test_bwd_norm_off_no_state():
