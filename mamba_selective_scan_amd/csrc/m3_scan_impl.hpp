@@ -69,6 +69,24 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
     return v;
 }
 
+// Sum and maximum over the four 16-lane rows of a wave, returned to every lane.  With both
+// operands the same value, permlane16_swap hands each lane the value of the same lane in the
+// neighbouring row (rows 0-1, 2-3) and permlane32_swap that of the other half: the xor-16 /
+// xor-32 butterfly in two VALU exchanges instead of two LDS permutes, with the same bits (each
+// step adds or compares the same two values on both lanes of a pair).
+__device__ __forceinline__ float rows_sum4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // LDS-only workgroup barrier (global memory needs no ordering between the waves here)
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -896,12 +914,8 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
             }
         }
     }
-    ssb += __shfl_xor(ssb, 16, 64);
-    ssb += __shfl_xor(ssb, 32, 64);
-    if constexpr (WANT_C) {
-        ssc += __shfl_xor(ssc, 16, 64);
-        ssc += __shfl_xor(ssc, 32, 64);
-    }
+    ssb = rows_sum4(ssb);
+    if constexpr (WANT_C) ssc = rows_sum4(ssc);
     // norm factors; rows past the block end are zero
     const float rsb = rv ? (c.bcnorm ? __builtin_amdgcn_rsqf(fmaf(ssb, c.invN, c.eps)) : 1.f) : 0.f;
     const float rsc = rv ? (c.bcnorm ? __builtin_amdgcn_rsqf(fmaf(ssc, c.invN, c.eps)) : 1.f) : 0.f;
@@ -982,10 +996,8 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
                     mc = fmaxf(mc, fabsf(vc[j]));
                 }
             }
-            mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-            mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-            mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
-            mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+            mb = rows_max4(mb);
+            mc = rows_max4(mc);
             float ib, ic;
             pow2_scale<12>(mb, sgb, ib);
             pow2_scale<12>(mc, sgc, ic);
