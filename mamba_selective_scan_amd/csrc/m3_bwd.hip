@@ -64,12 +64,6 @@ __device__ __forceinline__ float row_sum16(float v) {
     v += dpp_f<0x140>(v);  // row_mirror
     return v;
 }
-// sum over the four rows of a wave (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float rows_sum4(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
 // sum over the wave, returned to every lane: row sums, then rows 0+1 and 2+3 (row_bcast:15
 // into rows 1 and 3), then all four (row_bcast:31 into rows 2 and 3); lane 63 holds the total
 __device__ __forceinline__ float wave_sum(float v) {
@@ -98,18 +92,16 @@ struct RowPass {
     __device__ static int row(int wv, int m) { return wv + 8 * (HV ? 2 * m + half() : m); }
     __device__ static float sum(float v) { return HV ? half_sum(v) : wave_sum(v); }
     // the other half's value of v (0 when a row of the wave takes every lane)
-    __device__ static float other(float v) { return HV ? __shfl_xor(v, 32, 64) : 0.f; }
-};
-// inclusive prefix sum over the 64 lanes of a wave (all lanes active)
-__device__ __forceinline__ float wave_scan_incl(float v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float u = __shfl_up(v, d, 64);
-        if (lane >= d) v += u;
+    __device__ static float other(float v) {
+        if constexpr (HV) {
+            // permlane32_swap of v with itself: [0] holds lane l & 31's value, [1] lane (l & 31) + 32's
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+            return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+        } else {
+            return 0.f;
+        }
     }
-    return v;
-}
+};
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 // Branch-free loads: an absent element is loaded from offset 0 and replaced by 0 afterwards,
@@ -384,7 +376,7 @@ __device__ float chunk_prologue_vec(const BwdParams &p, float *sm, int64_t b, in
             gam = lam * dt;
             kap = gam + (okn ? dn * (1.f - ln) : 0.f);
         }
-        const float cs = wave_scan_incl(la);
+        const float cs = wave_incl_scan(la);
         tk[k0] = cs;
         tk[64 + k0] = kap;
         tk[128 + k0] = gam;
@@ -623,7 +615,7 @@ __device__ float chunk_prologue(const BwdParams &p, float *sm, int64_t b, int h,
             gam = lam * dt;
             kap = gam + (t0 + k0 + 1 < T ? dn * (1.f - ln) : 0.f);
         }
-        const float cs = wave_scan_incl(la);
+        const float cs = wave_incl_scan(la);
         tk[k0] = cs;
         tk[64 + k0] = kap;
         tk[128 + k0] = gam;
@@ -1441,21 +1433,28 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_grad_kernel(BwdParams p) {
         }
         const float btot = wave_sum(bst);
         float dcs = 0.f, dk = 0.f, dgd = 0.f;
-        for (int r = 0; r < R; ++r) {
-            const int src = min(k * R + r, 63);
-            const float a0 = __shfl(dcs_r, src, 64), a1 = __shfl(dk_r, src, 64), a2 = __shfl(dgd_r, src, 64);
-            if (k * R + r < 64) {
-                dcs += a0;
-                dk += a1;
-                dgd += a2;
+        if (R == 1) {
+            // one row per token: the row of token k is lane k
+            dcs = dcs_r;
+            dk = dk_r;
+            dgd = dgd_r;
+        } else {
+            for (int r = 0; r < R; ++r) {
+                const int src = min(k * R + r, 63);
+                const float a0 = __shfl(dcs_r, src, 64), a1 = __shfl(dk_r, src, 64), a2 = __shfl(dgd_r, src, 64);
+                if (k * R + r < 64) {
+                    dcs += a0;
+                    dk += a1;
+                    dgd += a2;
+                }
             }
         }
         if (k >= Tv) dcs = dk = dgd = 0.f;
         // the chunk's last token: e^cs_end <Gb, H> and the state terms of every row
         if (k == Tv - 1) dcs += __expf(sm[L::TK + Tv - 1]) * hd + btot;
         // d log alpha_k = sum over the chunk's tokens >= k
-        const float incl = wave_scan_incl(dcs);
-        const float tot = __shfl(incl, 63, 64);
+        const float incl = wave_incl_scan(dcs);
+        const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
         const float dla = tot - incl + dcs;
         if (k < Tv) {
             float *d = p.dsc + ((bh * T) + t0 + k) * 3;

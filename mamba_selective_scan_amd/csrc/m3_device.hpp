@@ -194,6 +194,49 @@ __device__ __forceinline__ f32x2_t sincos_acc(float a) {
     return f32x2_t{s, c};
 }
 
+// ---------------------------------------------------------------- cross-lane scans and reductions
+// v + (value of the lane K to the left inside its row of 16 lanes, or 0)
+template <int K>
+__device__ __forceinline__ float add_row_shr(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + K, 0xF, 0xF, true));
+}
+// inclusive add-scan over the 16 lanes of each DPP row
+__device__ __forceinline__ float row_incl_scan(float v) {
+    v = add_row_shr<1>(v);
+    v = add_row_shr<2>(v);
+    v = add_row_shr<4>(v);
+    v = add_row_shr<8>(v);
+    return v;
+}
+
+// inclusive add-scan of 64 lanes (every lane of the wave must be active): scans
+// inside the rows of 16, then row 0's total is broadcast into row 1 (and row 2's
+// into row 3), then row 1's running total into rows 2 and 3
+__device__ __forceinline__ float wave_incl_scan(float v) {
+    v = row_incl_scan(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+
+// Sum and maximum over the four 16-lane rows of a wave, returned to every lane.  With both
+// operands the same value, permlane16_swap hands each lane the value of the same lane in the
+// neighbouring row (rows 0-1, 2-3) and permlane32_swap that of the other half: the xor-16 /
+// xor-32 butterfly in two VALU exchanges instead of two LDS permutes, with the same bits (each
+// step adds or compares the same two values on both lanes of a pair).
+__device__ __forceinline__ float rows_sum4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max4(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // ---------------------------------------------------------------- block activations
 // Input activations of the canonical block: dt = softplus(raw + bias) in the
 // overflow-safe form max(v, 0) + log1p(exp(-|v|)); lambda = sigmoid(raw) (reciprocal
