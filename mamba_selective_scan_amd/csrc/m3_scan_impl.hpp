@@ -977,11 +977,20 @@ __device__ __forceinline__ void stage_prologue(const RawBlock<Cfg, WANT_C> &rb, 
             for (int k = 0; k < 4; ++k) split2(ob[2 * k] * wt, ob[2 * k + 1] * wt, wh[k], wl[k]);
             if constexpr (WANT_C) {
                 const int off = row * Cfg::OPP + n0;
-                *(u32x4_t *)((uint16_t *)sm.bt + off) =
-                    u32x4_t{pack_f16(ob[0] * sgb, ob[1] * sgb), pack_f16(ob[2] * sgb, ob[3] * sgb),
-                            pack_f16(ob[4] * sgb, ob[5] * sgb), pack_f16(ob[6] * sgb, ob[7] * sgb)};
-                const u32x4_t cw4 = {pack_f16(oc[0] * sgc, oc[1] * sgc), pack_f16(oc[2] * sgc, oc[3] * sgc),
-                                     pack_f16(oc[4] * sgc, oc[5] * sgc), pack_f16(oc[6] * sgc, oc[7] * sgc)};
+                u32x4_t bw4, cw4;
+                // (the N = 128 variants, at the whole register file, keep the one multiplying path:
+                // the branch measured slower there)
+                if (Cfg::NP > 64 || c.rowscale) {
+                    bw4 = u32x4_t{pack_f16(ob[0] * sgb, ob[1] * sgb), pack_f16(ob[2] * sgb, ob[3] * sgb),
+                                  pack_f16(ob[4] * sgb, ob[5] * sgb), pack_f16(ob[6] * sgb, ob[7] * sgb)};
+                    cw4 = u32x4_t{pack_f16(oc[0] * sgc, oc[1] * sgc), pack_f16(oc[2] * sgc, oc[3] * sgc),
+                                  pack_f16(oc[4] * sgc, oc[5] * sgc), pack_f16(oc[6] * sgc, oc[7] * sgc)};
+                } else {
+                    // unit row scales (normalised rows without gains or biases): no multiplies
+                    bw4 = u32x4_t{pack_f16(ob[0], ob[1]), pack_f16(ob[2], ob[3]), pack_f16(ob[4], ob[5]), pack_f16(ob[6], ob[7])};
+                    cw4 = u32x4_t{pack_f16(oc[0], oc[1]), pack_f16(oc[2], oc[3]), pack_f16(oc[4], oc[5]), pack_f16(oc[6], oc[7])};
+                }
+                *(u32x4_t *)((uint16_t *)sm.bt + off) = bw4;
                 if constexpr (Cfg::COL) *(u32x4_t *)((uint16_t *)sm.ct + off) = cw4;  // read by every wave
                 else ct[kk].v = cw4;
             }
