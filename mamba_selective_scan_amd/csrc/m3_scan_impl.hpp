@@ -612,6 +612,9 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
     const int tid = ltid(), lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15;
     if (wave == 0) {
+        // the workgroup's other waves wait at the barrier below for this chain: it takes issue
+        // priority over the co-resident workgroup's waves until its results are written
+        __builtin_amdgcn_s_setprio(2);
         // log alpha, gamma, eta (next token's dt (1 - lambda); 0 after the last token), scale;
         // dt and lambda through the optional input activations, tokens past the end stay 0
         float dt = rb.dt, lam = rb.lam, dtn = rb.dtn, lamn = rb.lamn;
@@ -644,6 +647,7 @@ __device__ __forceinline__ void stage_scalars_x(RawBlock<Cfg, WANT_C> &rb, const
             const float cref = __shfl(cs, lane | 15, 64);
             sm.u[lane] = __expf(cref - cs) * sc;
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     if constexpr (Cfg::VEC) {
         float *tt = (float *)sm.phi;  // [4 tiles][NP/2]
